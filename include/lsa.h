@@ -1,0 +1,222 @@
+/*
+ * lsa.h — C ABI of the Latent Sparse Attention (LSA) layer hot path on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (zhichai.net explainer "卡片柜", ch.2–ch.4; diosapp.com.cn LSA
+ * tutorial, section 二):
+ *   key side   — every key is projected to a 64-d latent and L2-normalised,
+ *                4 consecutive latents are pooled into one entry, each block
+ *                of 512 entries is clustered once with Ward's method into
+ *                buckets of mean 8 / max 16 entries, and the normalised bucket
+ *                means ("cards") form the bucket cache; optionally a complete
+ *                binary tree of merged buckets is kept above the leaves.
+ *   query side — the query is projected the same way, every visible card is
+ *                scored (max over the query heads of a GQA group), the best
+ *                buckets are expanded into k long-range token indices, and
+ *                exact softmax attention runs over sinks + local window +
+ *                those tokens.
+ *
+ * Three calls follow that problem statement:
+ *   lsa_build_buckets(K)              -> cache
+ *   lsa_select(Q, cache)              -> long-range indices
+ *   lsa_sparse_attend(Q, K, V, idx)   -> O
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates or frees device memory and keeps no device
+ *     state between calls.  Pointers must be 16-byte aligned.
+ *   - Work is enqueued on the given HIP stream (a hipStream_t passed as
+ *     void*; NULL = the default stream) and is asynchronous: a call returns
+ *     once its kernels are queued, never synchronises the host with the
+ *     device, and so may be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is queued; on any
+ *     error nothing is written and a status other than LSA_OK is returned
+ *     (lsa_last_error() then holds a per-thread message).  Faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Layouts are row-major and contiguous:
+ *       K, V   [B, H_kv, t_cap, d]   (a pooled entry's 4 keys are 4*d
+ *                                      consecutive elements)
+ *       Q, O   [B, n_q, H_q, d]
+ *       W_k, W_q [d, 64]
+ *       q_pos  [B, n_q] int64, absolute position of each query
+ *       lr_idx [B, n_q, H_kv, k] int32, lr_cnt [B, n_q, H_kv] int32
+ *     Query head h reads KV head h / G, G = H_q / H_kv.
+ *   - Token geometry of a query at position t, with T tokens bucketed
+ *     (n_blocks = T / 2048 full blocks; a trailing partial block is not
+ *     bucketed):  nvis = min(t / 2048, n_blocks) blocks are selectable;
+ *     sinks = [0, min(n_sinks, t+1)); local window = [l0, t] with
+ *     l0 = max(0, min(t - window + 1, 2048 * nvis)), i.e. the last `window`
+ *     tokens widened back to the first token that is not selectable.
+ *     The long-range list holds only tokens outside sinks and window.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_ABI_VERSION 1
+
+#define LSA_LATENT_DIM 64         /* latent width (ch.2: 64-d index space) */
+#define LSA_POOL 4                /* keys pooled per entry (ch.2)            */
+#define LSA_BLOCK_ENTRIES 512     /* entries per Ward block (ch.2)           */
+#define LSA_BLOCK_TOKENS 2048     /* = LSA_POOL * LSA_BLOCK_ENTRIES          */
+#define LSA_MEAN_BUCKET 8         /* mean entries per bucket (ch.2)          */
+#define LSA_MAX_BUCKET 16         /* max entries per bucket (ch.2)           */
+#define LSA_LEAVES_PER_BLOCK 64   /* = 512 / 8 buckets per full block        */
+#define LSA_MAX_GROUP 8           /* largest supported G = H_q / H_kv        */
+#define LSA_MAX_K 4096            /* largest k short of "every eligible token" */
+#define LSA_MAX_BEAM 64           /* largest tree beam width                 */
+
+typedef enum lsa_status {
+    LSA_OK = 0,
+    LSA_ERR_INVALID_ARG = 1,  /* NULL pointer, negative size, unknown enum value     */
+    LSA_ERR_SHAPE = 2,        /* unsupported d / latent / pool / block / bucket / G  */
+    LSA_ERR_DTYPE = 3,        /* dtype not LSA_F32 or LSA_BF16                       */
+    LSA_ERR_ALIGN = 4,        /* a pointer not 16-byte aligned                       */
+    LSA_ERR_WORKSPACE = 5,    /* cache or workspace smaller than the size query says */
+    LSA_ERR_CAPACITY = 6,     /* T > t_max or T > t_cap, k or beam out of range      */
+    LSA_ERR_HIP = 7,          /* a HIP launch returned an error                      */
+    LSA_ERR_UNSUPPORTED = 8   /* e.g. tree search on a cache built without a tree    */
+} lsa_status;
+
+typedef enum lsa_dtype { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
+
+typedef enum lsa_search { LSA_SEARCH_FLAT = 0, LSA_SEARCH_TREE = 1 } lsa_search;
+
+/* How lsa_select finds the top buckets of a flat search.  Every strategy
+ * returns identical results; they differ only in speed. */
+typedef enum lsa_strategy {
+    LSA_STRATEGY_AUTO = 0,         /* fused for many queries, materialised for few       */
+    LSA_STRATEGY_FUSED = 1,        /* two MFMA scoring passes: a per-query bound from
+                                      per-block maxima, then candidates above the bound  */
+    LSA_STRATEGY_MATERIALIZED = 2  /* every score written to the workspace, then an exact
+                                      radix select (decode: few queries, many buckets)   */
+} lsa_strategy;
+
+/* Shape of the layer.  latent_dim, pool, block_entries, mean_bucket and
+ * max_bucket must equal the LSA_* constants above (the method's values);
+ * they are spelled out so a caller states them and a mismatch is caught. */
+typedef struct lsa_layout {
+    int32_t head_dim;       /* d: 64 or 128                                        */
+    int32_t latent_dim;     /* 64                                                  */
+    int32_t n_kv_heads;     /* H_kv >= 1                                           */
+    int32_t n_q_heads;      /* H_q, a multiple of H_kv, G = H_q / H_kv in 1..8     */
+    int32_t pool;           /* 4                                                   */
+    int32_t block_entries;  /* 512                                                 */
+    int32_t mean_bucket;    /* 8                                                   */
+    int32_t max_bucket;     /* 16                                                  */
+    int32_t dtype;          /* lsa_dtype of K, V, Q, O, W and the stored centroids */
+    int32_t build_tree;     /* 1: also keep the binary tree of merged buckets      */
+} lsa_layout;
+
+/* Query-side parameters (ch.3: k long-range keys, sinks, local window; ch.4:
+ * tree beam). */
+typedef struct lsa_select_cfg {
+    int32_t k;         /* long-range budget: 0..LSA_MAX_K, or >= T (take every eligible token) */
+    int32_t n_sinks;   /* >= 0                                                          */
+    int32_t window;    /* >= 1                                                          */
+    int32_t search;    /* lsa_search                                                    */
+    int32_t beam;      /* tree only: 1..LSA_MAX_BEAM                                    */
+    int32_t strategy;  /* lsa_strategy (flat search only)                               */
+} lsa_select_cfg;
+
+/* Byte offsets of the cache regions, for inspection (tests, tools).  Per
+ * (b, g): cent [leaves_max, 64] (dtype), sums [leaves_max, 64] fp32,
+ * meta [leaves_max] uint32 (bits 0-7 = entries in the bucket, bits 8-17 =
+ * offset of its first member in the block's member list), members
+ * [n_blocks_max, 512] uint16 (each block's entry indices grouped by bucket,
+ * ascending inside a bucket), entry_leaf [n_blocks_max, 512] uint8 (bucket
+ * rank of every entry), tree_cent / tree_sums [nodes_max, 64] for the tree
+ * levels above the leaves (level l >= 1 starts at node level_off[l]). */
+typedef struct lsa_cache_info {
+    int64_t n_blocks_max;
+    int64_t leaves_max;
+    int64_t nodes_max;
+    int64_t n_blocks;          /* for the T passed to lsa_cache_describe */
+    int64_t n_leaves;
+    int32_t n_levels;          /* tree levels including the leaves (1 + ceil(log2 n_leaves)) */
+    int32_t elt_bytes;         /* 2 (bf16) or 4 (fp32) */
+    int64_t level_off[40];     /* node offset of tree level l (l >= 1); level_size below */
+    int64_t level_size[40];
+    size_t off_cent, off_sums, off_meta, off_members, off_entry_leaf, off_tree_cent, off_tree_sums;
+    size_t stride_cent, stride_sums, stride_meta, stride_members, stride_entry_leaf,
+           stride_tree_cent, stride_tree_sums;   /* bytes between consecutive (b, g) */
+    size_t total_bytes;
+} lsa_cache_info;
+
+/* Bytes of a bucket cache for `batch` sequences of up to t_max tokens.
+ * Host only; no device work. */
+lsa_status lsa_cache_bytes(const lsa_layout* layout, int64_t batch, int64_t t_max, size_t* bytes);
+
+/* Region offsets of such a cache when T tokens are bucketed. Host only. */
+lsa_status lsa_cache_describe(const lsa_layout* layout, int64_t batch, int64_t t_max, int64_t T,
+                              lsa_cache_info* info);
+
+/* Key side (ch.2; ch.4 for the tree).  For every sequence b < batch and KV
+ * head g, and every full 2048-token block of the first T tokens: project
+ * each key with W_k (64-d), L2-normalise, pool 4 -> 1, run capped Ward down
+ * to 64 buckets (<= 16 entries each, ties to the lowest cluster-id pair) and
+ * store each bucket's fp32 member sum, its centroid (sum / ||sum||, rounded
+ * to nearest even in the dtype), size and members.  With
+ * layout->build_tree, also the tree levels (node sum = sum of its children,
+ * centroid likewise).  K: [batch, H_kv, t_cap, d] in layout->dtype, T <= t_cap,
+ * T <= t_max; cache: cache_bytes >= lsa_cache_bytes(layout, batch, t_max).
+ * The cache is then read-only for the other calls. */
+lsa_status lsa_build_buckets(const lsa_layout* layout, const void* K, int64_t batch, int64_t t_cap,
+                             int64_t T, const void* W_k, void* cache, size_t cache_bytes,
+                             int64_t t_max, void* stream);
+
+/* Workspace bytes lsa_select needs for this many queries. Host only. */
+lsa_status lsa_select_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg,
+                                      int64_t batch, int64_t n_q, int64_t t_max, size_t* bytes);
+
+/* Query side selection (ch.3 flat search, ch.4 tree search).  For each
+ * (b, i, g): q_hat_h = round(normalise(Q[b,i,h] W_q)) for the G heads of
+ * group g; score(x) = max_h <q_hat_h, c_x> over the visible buckets x
+ * (blocks < nvis; tree: visible nodes on the beam); buckets ranked by
+ * (score desc, bucket id asc) are taken whole until k eligible tokens
+ * (tokens outside sinks and window), the last one giving its lowest-index
+ * eligible tokens.  Writes lr_idx[b,i,g,:] ascending, padded with -1, and
+ * lr_cnt[b,i,g] = min(k, eligible tokens of the visible buckets).  A query
+ * position outside [0, t_cap) of the K/V it will attend is not checked here;
+ * positions < 0 give lr_cnt = -1.  T is the number of bucketed tokens the
+ * cache was built with. */
+lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache,
+                      size_t cache_bytes, int64_t t_max, int64_t T, const void* Q,
+                      const int64_t* q_pos, int64_t batch, int64_t n_q, const void* W_q,
+                      int32_t* lr_idx, int32_t* lr_cnt, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Workspace bytes lsa_sparse_attend needs (split-key partial results). */
+lsa_status lsa_attend_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg,
+                                      int64_t batch, int64_t n_q, size_t* bytes);
+
+/* Exact attention over the selected keys (diosapp section 二:
+ * softmax(q K[keys]^T / sqrt(d)) V[keys]).  For each (b, i, h):
+ * O[b,i,h] = sum_{j in S} softmax_j(scale * <Q[b,i,h], K[b,g,j]>) V[b,g,j]
+ * over S = sinks U [l0, t] U lr_idx[b,i,g,:lr_cnt], fp32 softmax with the
+ * running max subtracted, O written in the dtype.  K, V: [batch, H_kv,
+ * t_cap, d] with every position <= t valid; T = tokens bucketed (fixes the
+ * geometry exactly as in lsa_select).  Rows with lr_cnt < 0 are written as
+ * zeros. */
+lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* Q,
+                             const void* K, const void* V, int64_t t_cap, int64_t T,
+                             const int64_t* q_pos, int64_t batch, int64_t n_q,
+                             const int32_t* lr_idx, const int32_t* lr_cnt, float scale, void* O,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable status name; detail of the last failed call on this thread. */
+const char* lsa_status_string(lsa_status status);
+const char* lsa_last_error(void);
+int32_t lsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

@@ -99,8 +99,11 @@ def key_latents(Kg: np.ndarray, W: np.ndarray) -> np.ndarray:
 
 def pooled_entries(u: np.ndarray) -> np.ndarray:
     """e_i = mean of u_{4i}..u_{4i+3}; a trailing partial group is dropped (ch.2)."""
+    u = np.asarray(u, np.float64)
     n = len(u) // POOL
-    return np.asarray(u[: n * POOL], np.float64).reshape(n, POOL, -1).mean(axis=1)
+    if n == 0:
+        return np.zeros((0, u.shape[1] if u.ndim == 2 else 0))
+    return u[: n * POOL].reshape(n, POOL, -1).mean(axis=1)
 
 
 def _ward_pair_cost(size_a, mu_a, sizes, mus):

@@ -1,0 +1,204 @@
+"""Latent Sparse Attention (LSA) layer hot path for AMD Instinct MI355X.
+
+Thin Python binding over liblsa.so (include/lsa.h).  The three calls follow
+the method's problem statement (zhichai.net explainer "卡片柜", ch.2-ch.4):
+
+    cache = build_buckets(K, W_k)                   # key side
+    lr_idx, lr_cnt = select(Q, cache, q_pos, ...)   # query side selection
+    O = sparse_attend(Q, K, V, q_pos, lr_idx, lr_cnt, ...)
+
+Tensors live on the GPU (torch is used for device memory and the current
+stream only); every step runs in the library's HIP kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (LsaError, Layout, SelectCfg, CacheInfo, LSA_BF16, LSA_F32, LSA_SEARCH_FLAT, LSA_SEARCH_TREE,
+                   LSA_STRATEGY_AUTO, LSA_STRATEGY_FUSED, LSA_STRATEGY_MATERIALIZED)
+
+__all__ = ["build_buckets", "select", "sparse_attend", "LsaCache", "LsaError", "make_layout", "select_cfg",
+           "library_path"]
+
+_STRATEGIES = {"auto": LSA_STRATEGY_AUTO, "fused": LSA_STRATEGY_FUSED, "materialized": LSA_STRATEGY_MATERIALIZED}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return LSA_BF16
+    if dt == torch.float32:
+        return LSA_F32
+    raise LsaError(3, f"unsupported dtype {dt}")
+
+
+def make_layout(head_dim: int, n_kv_heads: int, n_q_heads: int, dtype: torch.dtype, build_tree: bool = False) -> Layout:
+    return Layout(head_dim, _lib.LATENT_DIM, n_kv_heads, n_q_heads, _lib.POOL, _lib.BLOCK_ENTRIES,
+                  _lib.MEAN_BUCKET, _lib.MAX_BUCKET, _dtype_code(dtype), 1 if build_tree else 0)
+
+
+def select_cfg(k: int, n_sinks: int, window: int, search: str = "flat", beam: int = 0,
+               strategy: str = "auto") -> SelectCfg:
+    return SelectCfg(k, n_sinks, window, LSA_SEARCH_TREE if search == "tree" else LSA_SEARCH_FLAT, beam,
+                     _STRATEGIES[strategy])
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+@dataclasses.dataclass
+class LsaCache:
+    """A bucket cache: an opaque device buffer plus the shape it was built for."""
+
+    buf: torch.Tensor          # uint8 device buffer
+    layout: Layout
+    batch: int
+    t_max: int
+    T: int                     # tokens bucketed
+
+    def info(self) -> CacheInfo:
+        info = CacheInfo()
+        _lib.check(_lib.lib().lsa_cache_describe(ctypes.byref(self.layout), self.batch, self.t_max, self.T,
+                                                 ctypes.byref(info)))
+        return info
+
+    # ---- read-only views of the regions (inspection and tests)
+    def _region(self, off, stride, count, dtype, shape):
+        ebytes = torch.empty(0, dtype=dtype).element_size()
+        HB = self.batch * self.layout.n_kv_heads
+        raw = self.buf[off: off + stride * HB].view(HB, stride)[:, : count * ebytes]
+        return raw.contiguous().view(dtype).view(self.batch, self.layout.n_kv_heads, *shape)
+
+    def centroids(self) -> torch.Tensor:
+        i = self.info()
+        dt = torch.bfloat16 if self.layout.dtype == LSA_BF16 else torch.float32
+        return self._region(i.off_cent, i.stride_cent, i.n_leaves * 64, dt, (i.n_leaves, 64))
+
+    def sums(self) -> torch.Tensor:
+        i = self.info()
+        return self._region(i.off_sums, i.stride_sums, i.n_leaves * 64, torch.float32, (i.n_leaves, 64))
+
+    def meta(self) -> torch.Tensor:
+        i = self.info()
+        return self._region(i.off_meta, i.stride_meta, i.n_leaves, torch.int32, (i.n_leaves,))
+
+    def members(self) -> torch.Tensor:
+        i = self.info()
+        return self._region(i.off_members, i.stride_members, i.n_blocks * 512, torch.int16, (i.n_blocks, 512))
+
+    def entry_leaf(self) -> torch.Tensor:
+        i = self.info()
+        return self._region(i.off_entry_leaf, i.stride_entry_leaf, i.n_blocks * 512, torch.uint8, (i.n_blocks, 512))
+
+    def tree_level(self, lev: int):
+        """(centroids, sums) of tree level lev (0 = leaves)."""
+        if lev == 0:
+            return self.centroids(), self.sums()
+        i = self.info()
+        n, off = i.level_size[lev], i.level_off[lev]
+        dt = torch.bfloat16 if self.layout.dtype == LSA_BF16 else torch.float32
+        c = self._region(i.off_tree_cent, i.stride_tree_cent, i.nodes_max * 64, dt, (i.nodes_max, 64))
+        s = self._region(i.off_tree_sums, i.stride_tree_sums, i.nodes_max * 64, torch.float32, (i.nodes_max, 64))
+        return c[:, :, off: off + n], s[:, :, off: off + n]
+
+
+def build_buckets(K: torch.Tensor, W_k: torch.Tensor, T: Optional[int] = None, t_max: Optional[int] = None,
+                  build_tree: bool = False, n_q_heads: Optional[int] = None, cache: Optional[torch.Tensor] = None):
+    """Key side: latent, normalise, pool, Ward per 512-entry block -> LsaCache.
+
+    K: [B, H_kv, t_cap, d] (bf16 or fp32, contiguous, on the GPU); W_k: [d, 64].
+    """
+    assert K.is_cuda and K.is_contiguous() and W_k.is_contiguous()
+    B, H_kv, t_cap, d = K.shape
+    T = t_cap if T is None else T
+    t_max = T if t_max is None else t_max
+    layout = make_layout(d, H_kv, n_q_heads or H_kv, K.dtype, build_tree)
+    L = _lib.lib()
+    nbytes = ctypes.c_size_t()
+    _lib.check(L.lsa_cache_bytes(ctypes.byref(layout), B, t_max, ctypes.byref(nbytes)))
+    if cache is None:
+        cache = torch.empty(nbytes.value, dtype=torch.uint8, device=K.device)
+    _lib.check(L.lsa_build_buckets(ctypes.byref(layout), _ptr(K), B, t_cap, T, _ptr(W_k), _ptr(cache),
+                                   cache.numel(), t_max, _stream(K.device)))
+    return LsaCache(cache, layout, B, t_max, T)
+
+
+def select_workspace_bytes(cache: LsaCache, cfg: SelectCfg, n_q: int, n_q_heads: int) -> int:
+    layout = Layout.from_buffer_copy(cache.layout)
+    layout.n_q_heads = n_q_heads
+    n = ctypes.c_size_t()
+    _lib.check(_lib.lib().lsa_select_workspace_bytes(ctypes.byref(layout), ctypes.byref(cfg), cache.batch, n_q,
+                                                     cache.t_max, ctypes.byref(n)))
+    return n.value
+
+
+def select(Q: torch.Tensor, cache: LsaCache, q_pos: torch.Tensor, W_q: torch.Tensor, k: int, n_sinks: int,
+           window: int, search: str = "flat", beam: int = 0, strategy: str = "auto",
+           workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None):
+    """Query side: score buckets, pick the top ones, expand to k tokens.
+
+    Q: [B, n_q, H_q, d]; q_pos: int64 [B, n_q] on the GPU.  Returns
+    (lr_idx int32 [B, n_q, H_kv, k] ascending, -1 padded; lr_cnt int32 [B, n_q, H_kv]).
+    """
+    assert Q.is_cuda and Q.is_contiguous() and q_pos.dtype == torch.int64 and q_pos.is_contiguous()
+    B, n_q, H_q, d = Q.shape
+    layout = Layout.from_buffer_copy(cache.layout)
+    layout.n_q_heads = H_q
+    cfg = select_cfg(k, n_sinks, window, search, beam, strategy)
+    L = _lib.lib()
+    H_kv = layout.n_kv_heads
+    if out is None:
+        lr_idx = torch.empty(B, n_q, H_kv, k, dtype=torch.int32, device=Q.device)
+        lr_cnt = torch.empty(B, n_q, H_kv, dtype=torch.int32, device=Q.device)
+    else:
+        lr_idx, lr_cnt = out
+    n = ctypes.c_size_t()
+    _lib.check(L.lsa_select_workspace_bytes(ctypes.byref(layout), ctypes.byref(cfg), B, n_q, cache.t_max,
+                                            ctypes.byref(n)))
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=Q.device)
+    _lib.check(L.lsa_select(ctypes.byref(layout), ctypes.byref(cfg), _ptr(cache.buf), cache.buf.numel(),
+                            cache.t_max, cache.T, _ptr(Q), _ptr(q_pos), B, n_q, _ptr(W_q),
+                            _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt), _ptr(workspace),
+                            workspace.numel(), _stream(Q.device)))
+    return lr_idx, lr_cnt
+
+
+def sparse_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torch.Tensor, lr_idx: torch.Tensor,
+                  lr_cnt: torch.Tensor, T: int, k: int, n_sinks: int, window: int, scale: Optional[float] = None,
+                  O: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Exact attention over sinks + window + selected tokens -> O [B, n_q, H_q, d]."""
+    assert Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()
+    B, n_q, H_q, d = Q.shape
+    _, H_kv, t_cap, _ = K.shape
+    layout = make_layout(d, H_kv, H_q, Q.dtype)
+    cfg = select_cfg(k, n_sinks, window)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if O is None:
+        O = torch.empty_like(Q)
+    L = _lib.lib()
+    n = ctypes.c_size_t()
+    _lib.check(L.lsa_attend_workspace_bytes(ctypes.byref(layout), ctypes.byref(cfg), B, n_q, ctypes.byref(n)))
+    if n.value > 0 and (workspace is None or workspace.numel() < n.value):
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=Q.device)
+    _lib.check(L.lsa_sparse_attend(ctypes.byref(layout), ctypes.byref(cfg), _ptr(Q), _ptr(K), _ptr(V), t_cap, T,
+                                   _ptr(q_pos), B, n_q, _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt),
+                                   ctypes.c_float(scale), _ptr(O), _ptr(workspace) if n.value > 0 else ctypes.c_void_p(0),
+                                   workspace.numel() if (workspace is not None and n.value > 0) else 0,
+                                   _stream(Q.device)))
+    return O

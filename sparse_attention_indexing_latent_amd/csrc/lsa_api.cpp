@@ -1,0 +1,431 @@
+// C ABI of the LSA hot path: argument validation, cache and workspace
+// layouts, and kernel launches on the caller's stream.  See include/lsa.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/lsa.h"
+#include "lsa_launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+lsa_status fail(lsa_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+lsa_status ok() {
+    g_err.clear();
+    return LSA_OK;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+lsa_status check_layout(const lsa_layout* L) {
+    if (!L) return fail(LSA_ERR_INVALID_ARG, "layout is NULL");
+    if (L->latent_dim != LSA_LATENT_DIM) return fail(LSA_ERR_SHAPE, "latent_dim must be %d", LSA_LATENT_DIM);
+    if (L->pool != LSA_POOL) return fail(LSA_ERR_SHAPE, "pool must be %d", LSA_POOL);
+    if (L->block_entries != LSA_BLOCK_ENTRIES) return fail(LSA_ERR_SHAPE, "block_entries must be %d", LSA_BLOCK_ENTRIES);
+    if (L->mean_bucket != LSA_MEAN_BUCKET) return fail(LSA_ERR_SHAPE, "mean_bucket must be %d", LSA_MEAN_BUCKET);
+    if (L->max_bucket != LSA_MAX_BUCKET) return fail(LSA_ERR_SHAPE, "max_bucket must be %d", LSA_MAX_BUCKET);
+    if (L->head_dim != 64 && L->head_dim != 128) return fail(LSA_ERR_SHAPE, "head_dim must be 64 or 128, got %d", L->head_dim);
+    if (L->n_kv_heads < 1 || L->n_q_heads < 1) return fail(LSA_ERR_SHAPE, "head counts must be >= 1");
+    if (L->n_q_heads % L->n_kv_heads != 0) return fail(LSA_ERR_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
+    if (L->n_q_heads / L->n_kv_heads > LSA_MAX_GROUP)
+        return fail(LSA_ERR_SHAPE, "group size %d exceeds %d", L->n_q_heads / L->n_kv_heads, LSA_MAX_GROUP);
+    if (L->dtype != LSA_F32 && L->dtype != LSA_BF16) return fail(LSA_ERR_DTYPE, "dtype must be LSA_F32 or LSA_BF16");
+    if (L->build_tree != 0 && L->build_tree != 1) return fail(LSA_ERR_INVALID_ARG, "build_tree must be 0 or 1");
+    return LSA_OK;
+}
+
+struct CacheGeom {
+    int64_t nbm, nlm, nnm;
+    int64_t n_blocks, n_leaves;
+    int32_t n_levels;
+    int32_t elt;
+    int64_t level_off[lsa::kMaxLevels];
+    int64_t level_size[lsa::kMaxLevels];
+    size_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums;   // bytes per (b, g)
+    size_t off_cent, off_sums, off_meta, off_members, off_eleaf, off_tcent, off_tsums, total;
+};
+
+int64_t tree_nodes_above(int64_t nl) {
+    int64_t tot = 0;
+    while (nl > 1) {
+        nl = (nl + 1) / 2;
+        tot += nl;
+    }
+    return tot;
+}
+
+void cache_geom(const lsa_layout* L, int64_t B, int64_t t_max, int64_t T, CacheGeom& c) {
+    memset(&c, 0, sizeof(c));
+    c.elt = L->dtype == LSA_BF16 ? 2 : 4;
+    c.nbm = t_max / LSA_BLOCK_TOKENS;
+    c.nlm = c.nbm * LSA_LEAVES_PER_BLOCK;
+    c.nnm = L->build_tree ? tree_nodes_above(c.nlm) : 0;
+    c.n_blocks = T / LSA_BLOCK_TOKENS;
+    c.n_leaves = c.n_blocks * LSA_LEAVES_PER_BLOCK;
+    if (c.n_leaves > 0) {
+        int64_t nl = c.n_leaves, off = 0;
+        int lev = 0;
+        c.level_size[0] = nl;
+        c.level_off[0] = 0;
+        while (nl > 1 && lev + 1 < lsa::kMaxLevels) {
+            nl = (nl + 1) / 2;
+            ++lev;
+            c.level_off[lev] = off;
+            c.level_size[lev] = nl;
+            off += nl;
+        }
+        c.n_levels = lev + 1;
+    }
+    const int64_t HB = B * L->n_kv_heads;
+    c.s_cent = align256((size_t)c.nlm * LSA_LATENT_DIM * c.elt);
+    c.s_sums = align256((size_t)c.nlm * LSA_LATENT_DIM * 4);
+    c.s_meta = align256((size_t)c.nlm * 4);
+    c.s_members = align256((size_t)c.nbm * LSA_BLOCK_ENTRIES * 2);
+    c.s_eleaf = align256((size_t)c.nbm * LSA_BLOCK_ENTRIES);
+    c.s_tcent = align256((size_t)c.nnm * LSA_LATENT_DIM * c.elt);
+    c.s_tsums = align256((size_t)c.nnm * LSA_LATENT_DIM * 4);
+    size_t o = 0;
+    c.off_cent = o;    o += c.s_cent * HB;
+    c.off_sums = o;    o += c.s_sums * HB;
+    c.off_meta = o;    o += c.s_meta * HB;
+    c.off_members = o; o += c.s_members * HB;
+    c.off_eleaf = o;   o += c.s_eleaf * HB;
+    c.off_tcent = o;   o += c.s_tcent * HB;
+    c.off_tsums = o;   o += c.s_tsums * HB;
+    c.total = o > 0 ? o : 256;
+}
+
+lsa::CacheView make_view(const CacheGeom& c, void* cache, bool bf16) {
+    lsa::CacheView v;
+    memset(&v, 0, sizeof(v));
+    char* base = static_cast<char*>(cache);
+    v.cent = base + c.off_cent;
+    v.sums = reinterpret_cast<float*>(base + c.off_sums);
+    v.meta = reinterpret_cast<uint32_t*>(base + c.off_meta);
+    v.members = reinterpret_cast<uint16_t*>(base + c.off_members);
+    v.eleaf = reinterpret_cast<uint8_t*>(base + c.off_eleaf);
+    v.tcent = base + c.off_tcent;
+    v.tsums = reinterpret_cast<float*>(base + c.off_tsums);
+    v.s_cent = (int64_t)(c.s_cent / c.elt);
+    v.s_sums = (int64_t)(c.s_sums / 4);
+    v.s_meta = (int64_t)(c.s_meta / 4);
+    v.s_members = (int64_t)(c.s_members / 2);
+    v.s_eleaf = (int64_t)c.s_eleaf;
+    v.s_tcent = (int64_t)(c.s_tcent / c.elt);
+    v.s_tsums = (int64_t)(c.s_tsums / 4);
+    v.n_blocks = (int32_t)c.n_blocks;
+    v.n_leaves = (int32_t)c.n_leaves;
+    v.n_levels = c.n_levels;
+    v.bf16 = bf16 ? 1 : 0;
+    for (int i = 0; i < lsa::kMaxLevels; ++i) {
+        v.level_off[i] = c.level_off[i];
+        v.level_size[i] = c.level_size[i];
+    }
+    return v;
+}
+
+lsa_status check_cfg(const lsa_select_cfg* C, int64_t T) {
+    if (!C) return fail(LSA_ERR_INVALID_ARG, "select cfg is NULL");
+    if (C->k < 0 || C->n_sinks < 0) return fail(LSA_ERR_INVALID_ARG, "k and n_sinks must be >= 0");
+    if (C->window < 1) return fail(LSA_ERR_INVALID_ARG, "window must be >= 1");
+    if (C->search != LSA_SEARCH_FLAT && C->search != LSA_SEARCH_TREE) return fail(LSA_ERR_INVALID_ARG, "unknown search");
+    if (C->strategy < LSA_STRATEGY_AUTO || C->strategy > LSA_STRATEGY_MATERIALIZED)
+        return fail(LSA_ERR_INVALID_ARG, "unknown strategy");
+    if (C->k > LSA_MAX_K && (int64_t)C->k < T)
+        return fail(LSA_ERR_CAPACITY, "k=%d exceeds %d and is below the %lld bucketed tokens", C->k, LSA_MAX_K,
+                    (long long)T);
+    if (C->search == LSA_SEARCH_TREE && (C->beam < 1 || C->beam > LSA_MAX_BEAM))
+        return fail(LSA_ERR_CAPACITY, "beam must be in 1..%d", LSA_MAX_BEAM);
+    return LSA_OK;
+}
+
+struct SelectWs {
+    size_t off_qhat, off_tau, off_cnt, off_counters, off_cand, off_fb, off_scores, total;
+    int64_t score_stride;
+    int fb_slots;
+    int strategy;
+};
+
+constexpr int kFallbackSlots = 256;
+
+int resolve_strategy(const lsa_select_cfg* C, int64_t units) {
+    if (C->search == LSA_SEARCH_TREE) return -1;
+    if (C->strategy != LSA_STRATEGY_AUTO) return C->strategy;
+    return units <= 4096 ? LSA_STRATEGY_MATERIALIZED : LSA_STRATEGY_FUSED;
+}
+
+void select_ws(const lsa_layout* L, const lsa_select_cfg* C, int64_t B, int64_t n_q, int64_t t_max, SelectWs& w) {
+    memset(&w, 0, sizeof(w));
+    const int64_t units = B * n_q * L->n_kv_heads;
+    const int elt = L->dtype == LSA_BF16 ? 2 : 4;
+    const int64_t nlm = (t_max / LSA_BLOCK_TOKENS) * LSA_LEAVES_PER_BLOCK;
+    w.strategy = resolve_strategy(C, units);
+    w.score_stride = (nlm + 63) & ~(int64_t)63;
+    size_t o = 0;
+    w.off_qhat = o;     o = align256(o + (size_t)(B * n_q * L->n_q_heads) * LSA_LATENT_DIM * elt);
+    w.off_counters = o; o = align256(o + 64);
+    w.off_tau = o;      o = align256(o + (size_t)units * 4);
+    w.off_cnt = o;      o = align256(o + (size_t)units * 4);
+    if (w.strategy == LSA_STRATEGY_FUSED) {
+        w.off_cand = o; o = align256(o + (size_t)units * lsa::kCandCap * 8);
+        w.off_fb = o;   o = align256(o + (size_t)units * 4);
+        w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
+        w.off_scores = o; o = align256(o + (size_t)w.fb_slots * w.score_stride * 4);
+    } else if (w.strategy == LSA_STRATEGY_MATERIALIZED) {
+        w.off_scores = o; o = align256(o + (size_t)units * w.score_stride * 4);
+    }
+    w.total = o;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lsa_abi_version(void) { return LSA_ABI_VERSION; }
+
+const char* lsa_status_string(lsa_status s) {
+    switch (s) {
+        case LSA_OK: return "LSA_OK";
+        case LSA_ERR_INVALID_ARG: return "LSA_ERR_INVALID_ARG";
+        case LSA_ERR_SHAPE: return "LSA_ERR_SHAPE";
+        case LSA_ERR_DTYPE: return "LSA_ERR_DTYPE";
+        case LSA_ERR_ALIGN: return "LSA_ERR_ALIGN";
+        case LSA_ERR_WORKSPACE: return "LSA_ERR_WORKSPACE";
+        case LSA_ERR_CAPACITY: return "LSA_ERR_CAPACITY";
+        case LSA_ERR_HIP: return "LSA_ERR_HIP";
+        case LSA_ERR_UNSUPPORTED: return "LSA_ERR_UNSUPPORTED";
+    }
+    return "LSA_ERR_UNKNOWN";
+}
+
+const char* lsa_last_error(void) { return g_err.c_str(); }
+
+lsa_status lsa_cache_bytes(const lsa_layout* layout, int64_t batch, int64_t t_max, size_t* bytes) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
+    if (batch < 0 || t_max < 0) return fail(LSA_ERR_INVALID_ARG, "batch and t_max must be >= 0");
+    CacheGeom c;
+    cache_geom(layout, batch, t_max, t_max, c);
+    *bytes = c.total;
+    return ok();
+}
+
+lsa_status lsa_cache_describe(const lsa_layout* layout, int64_t batch, int64_t t_max, int64_t T,
+                              lsa_cache_info* info) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (!info) return fail(LSA_ERR_INVALID_ARG, "info is NULL");
+    if (batch < 0 || t_max < 0 || T < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (T > t_max) return fail(LSA_ERR_CAPACITY, "T=%lld exceeds t_max=%lld", (long long)T, (long long)t_max);
+    CacheGeom c;
+    cache_geom(layout, batch, t_max, T, c);
+    memset(info, 0, sizeof(*info));
+    info->n_blocks_max = c.nbm;
+    info->leaves_max = c.nlm;
+    info->nodes_max = c.nnm;
+    info->n_blocks = c.n_blocks;
+    info->n_leaves = c.n_leaves;
+    info->n_levels = c.n_levels;
+    info->elt_bytes = c.elt;
+    for (int i = 0; i < 40 && i < lsa::kMaxLevels; ++i) {
+        info->level_off[i] = c.level_off[i];
+        info->level_size[i] = c.level_size[i];
+    }
+    info->off_cent = c.off_cent;
+    info->off_sums = c.off_sums;
+    info->off_meta = c.off_meta;
+    info->off_members = c.off_members;
+    info->off_entry_leaf = c.off_eleaf;
+    info->off_tree_cent = c.off_tcent;
+    info->off_tree_sums = c.off_tsums;
+    info->stride_cent = c.s_cent;
+    info->stride_sums = c.s_sums;
+    info->stride_meta = c.s_meta;
+    info->stride_members = c.s_members;
+    info->stride_entry_leaf = c.s_eleaf;
+    info->stride_tree_cent = c.s_tcent;
+    info->stride_tree_sums = c.s_tsums;
+    info->total_bytes = c.total;
+    return ok();
+}
+
+lsa_status lsa_build_buckets(const lsa_layout* layout, const void* K, int64_t batch, int64_t t_cap, int64_t T,
+                             const void* W_k, void* cache, size_t cache_bytes, int64_t t_max, void* stream) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (batch < 0 || t_cap < 0 || T < 0 || t_max < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (T > t_cap) return fail(LSA_ERR_CAPACITY, "T=%lld exceeds t_cap=%lld", (long long)T, (long long)t_cap);
+    if (T > t_max) return fail(LSA_ERR_CAPACITY, "T=%lld exceeds t_max=%lld", (long long)T, (long long)t_max);
+    if (!K || !W_k || !cache) return fail(LSA_ERR_INVALID_ARG, "K, W_k and cache must be non-NULL");
+    if (misaligned(K) || misaligned(W_k) || misaligned(cache)) return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
+    CacheGeom c;
+    cache_geom(layout, batch, t_max, T, c);
+    if (cache_bytes < c.total)
+        return fail(LSA_ERR_WORKSPACE, "cache has %zu bytes, needs %zu", cache_bytes, c.total);
+    if (batch == 0 || c.n_blocks == 0) return ok();
+    const bool bf16 = layout->dtype == LSA_BF16;
+    lsa::CacheView v = make_view(c, cache, bf16);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = lsa::launch_build(v, K, bf16, t_cap, layout->head_dim, (int)batch, layout->n_kv_heads, W_k, st);
+    if (e == hipSuccess && layout->build_tree) e = lsa::launch_tree(v, (int)batch, layout->n_kv_heads, st);
+    if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+lsa_status lsa_select_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg, int64_t batch,
+                                      int64_t n_q, int64_t t_max, size_t* bytes) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (!cfg || !bytes) return fail(LSA_ERR_INVALID_ARG, "cfg and bytes must be non-NULL");
+    if (batch < 0 || n_q < 0 || t_max < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    s = check_cfg(cfg, t_max);
+    if (s) return s;
+    SelectWs w;
+    select_ws(layout, cfg, batch, n_q, t_max, w);
+    *bytes = w.total;
+    return ok();
+}
+
+lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache, size_t cache_bytes,
+                      int64_t t_max, int64_t T, const void* Q, const int64_t* q_pos, int64_t batch, int64_t n_q,
+                      const void* W_q, int32_t* lr_idx, int32_t* lr_cnt, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (batch < 0 || n_q < 0 || T < 0 || t_max < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (T > t_max) return fail(LSA_ERR_CAPACITY, "T=%lld exceeds t_max=%lld", (long long)T, (long long)t_max);
+    s = check_cfg(cfg, T);
+    if (s) return s;
+    if (cfg->search == LSA_SEARCH_TREE && !layout->build_tree)
+        return fail(LSA_ERR_UNSUPPORTED, "tree search needs a cache built with build_tree = 1");
+    const int64_t units = batch * n_q * layout->n_kv_heads;
+    if (units == 0) return ok();
+    if (!cache || !Q || !q_pos || !W_q || !lr_cnt || (!lr_idx && cfg->k > 0) || !workspace)
+        return fail(LSA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (misaligned(cache) || misaligned(Q) || misaligned(q_pos) || misaligned(W_q) || misaligned(lr_cnt) ||
+        (lr_idx && misaligned(lr_idx)) || misaligned(workspace))
+        return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
+    CacheGeom c;
+    cache_geom(layout, batch, t_max, T, c);
+    if (cache_bytes < c.total) return fail(LSA_ERR_WORKSPACE, "cache has %zu bytes, needs %zu", cache_bytes, c.total);
+    SelectWs w;
+    select_ws(layout, cfg, batch, n_q, t_max, w);
+    if (workspace_bytes < w.total)
+        return fail(LSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+    const bool bf16 = layout->dtype == LSA_BF16;
+    lsa::CacheView v = make_view(c, const_cast<void*>(cache), bf16);
+    char* wb = static_cast<char*>(workspace);
+    lsa::SelectBuffers sb;
+    sb.qhat = wb + w.off_qhat;
+    sb.tau = reinterpret_cast<float*>(wb + w.off_tau);
+    sb.cnt = reinterpret_cast<int*>(wb + w.off_cnt);
+    sb.counters = reinterpret_cast<int*>(wb + w.off_counters);
+    sb.cand = reinterpret_cast<uint64_t*>(wb + w.off_cand);
+    sb.fb_list = reinterpret_cast<int*>(wb + w.off_fb);
+    sb.scores = reinterpret_cast<float*>(wb + w.off_scores);
+    sb.score_stride = w.score_stride;
+    sb.fb_slots = w.fb_slots;
+    lsa::SelArgs sa;
+    sa.k = cfg->k;
+    sa.n_sinks = cfg->n_sinks;
+    sa.window = cfg->window;
+    sa.beam = cfg->beam;
+    sa.H_q = layout->n_q_heads;
+    sa.H_kv = layout->n_kv_heads;
+    sa.G = layout->n_q_heads / layout->n_kv_heads;
+    sa.n_q = n_q;
+    sa.n_units = units;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* lr = lr_idx ? lr_idx : lr_cnt;  // k == 0: rows are empty, never written
+    hipError_t e = lsa::launch_qlatent(Q, W_q, bf16, layout->head_dim, batch * n_q * layout->n_q_heads, sb.qhat,
+                                       sb.counters, st);
+    if (e == hipSuccess) {
+        if (cfg->search == LSA_SEARCH_TREE)
+            e = lsa::launch_select_tree(v, bf16, q_pos, sa, sb, lr, lr_cnt, st);
+        else if (w.strategy == LSA_STRATEGY_FUSED)
+            e = lsa::launch_select_fused(v, bf16, q_pos, sa, (int)batch, sb, lr, lr_cnt, st);
+        else
+            e = lsa::launch_select_materialized(v, bf16, q_pos, sa, sb, lr, lr_cnt, st);
+    }
+    if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+lsa_status lsa_attend_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg, int64_t batch,
+                                      int64_t n_q, size_t* bytes) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (!cfg || !bytes) return fail(LSA_ERR_INVALID_ARG, "cfg and bytes must be non-NULL");
+    if (batch < 0 || n_q < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    const int64_t units = batch * n_q * layout->n_kv_heads;
+    const int splits = lsa::attend_splits(units, cfg->window, cfg->k);
+    const int G = layout->n_q_heads / layout->n_kv_heads;
+    *bytes = splits > 1 ? align256((size_t)units * splits * G * (layout->head_dim + 2) * 4) : 0;
+    return ok();
+}
+
+lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* Q, const void* K,
+                             const void* V, int64_t t_cap, int64_t T, const int64_t* q_pos, int64_t batch,
+                             int64_t n_q, const int32_t* lr_idx, const int32_t* lr_cnt, float scale, void* O,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (!cfg) return fail(LSA_ERR_INVALID_ARG, "cfg is NULL");
+    if (batch < 0 || n_q < 0 || t_cap < 0 || T < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (cfg->k < 0 || cfg->n_sinks < 0 || cfg->window < 1) return fail(LSA_ERR_INVALID_ARG, "bad k / n_sinks / window");
+    if (T > t_cap) return fail(LSA_ERR_CAPACITY, "T=%lld exceeds t_cap=%lld", (long long)T, (long long)t_cap);
+    if (!std::isfinite(scale)) return fail(LSA_ERR_INVALID_ARG, "scale must be finite");
+    const int64_t units = batch * n_q * layout->n_kv_heads;
+    if (units == 0) return ok();
+    if (!Q || !K || !V || !q_pos || !lr_cnt || (!lr_idx && cfg->k > 0) || !O)
+        return fail(LSA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(q_pos) || misaligned(lr_cnt) ||
+        (lr_idx && misaligned(lr_idx)) || misaligned(O))
+        return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int splits = lsa::attend_splits(units, cfg->window, cfg->k);
+    const int G = layout->n_q_heads / layout->n_kv_heads;
+    const size_t need = splits > 1 ? align256((size_t)units * splits * G * (layout->head_dim + 2) * 4) : 0;
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(LSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (need > 0 && misaligned(workspace)) return fail(LSA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    lsa::AttArgs aa;
+    aa.n_q = n_q;
+    aa.n_units = units;
+    aa.t_cap = t_cap;
+    aa.B = (int32_t)batch;
+    aa.H_kv = layout->n_kv_heads;
+    aa.H_q = layout->n_q_heads;
+    aa.G = G;
+    aa.n_sinks = cfg->n_sinks;
+    aa.window = cfg->window;
+    aa.n_blocks = (int32_t)(T / LSA_BLOCK_TOKENS);
+    aa.k = cfg->k;
+    aa.splits = splits;
+    aa.scale = scale;
+    hipError_t e = lsa::launch_attend(Q, K, V, q_pos, lr_idx ? lr_idx : lr_cnt, lr_cnt, aa, layout->head_dim,
+                                      layout->dtype == LSA_BF16, O, static_cast<float*>(workspace),
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

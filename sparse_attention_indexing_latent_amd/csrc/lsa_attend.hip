@@ -1,0 +1,408 @@
+// Exact softmax attention over the selected keys on gfx950.
+//
+// Method: diosapp.com.cn LSA tutorial, section 二 (pseudocode: output =
+// softmax(q K[keys]^T / sqrt(d)) V[keys]); zhichai.net explainer "卡片柜",
+// ch.3 (keys = sinks + recent window + the selected long-range tokens; the
+// attention itself is unchanged, only the keys it reads).
+//
+// One wave per (query, KV head) — or per slice of its key list when few
+// queries must fill the chip (decode), followed by a log-sum-exp combine.
+// The G query heads of the group share the key list, so they form the N = 16
+// columns of the MFMAs.  Per 32 gathered keys:
+//   S^T = K Q^T        two 16x16x32 bf16 MFMA tiles per 8-dim k-step,
+//   online softmax     fp32, max subtracted, per head,
+//   V^T                V rows pass through a 16x16x16 MFMA with the
+//                      identity as B, which hands each lane 4 consecutive
+//                      keys of one head dimension (the k-layout PV needs),
+//   O^T += V^T P^T     16x16x32 bf16 MFMAs, P rounded to bf16.
+// Every lane loads contiguous 64-byte pieces of K/V rows (4 lanes per
+// 256-byte row), so each gathered row is one fully used 256-byte segment.
+
+#include "lsa_launch.hpp"
+
+namespace lsa {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Unit order inside the kernel: KV head slowest, then sequence, then query,
+// so neighbouring waves (and, after the XCD remap, one XCD) handle
+// neighbouring queries of one head and share their local windows in L2.
+struct AUnit {
+    int64_t b, i, g, u;
+};
+__device__ __forceinline__ AUnit aunit_of(int64_t uu, const AttArgs& aa) {
+    AUnit r;
+    const int64_t per_g = (int64_t)aa.B * aa.n_q;
+    r.g = uu / per_g;
+    const int64_t rem = uu % per_g;
+    r.b = rem / aa.n_q;
+    r.i = rem % aa.n_q;
+    r.u = (r.b * aa.n_q + r.i) * aa.H_kv + r.g;
+    return r;
+}
+
+// Map the hardware workgroup id (dispatched round-robin over the 8 XCDs) to a
+// logical id so that consecutive logical ids run on the same XCD.
+__device__ __forceinline__ int64_t xcd_logical(int64_t bid, int64_t nwg_padded) {
+    const int64_t per = nwg_padded / 8;
+    return (bid % 8) * per + bid / 8;
+}
+
+struct KeyList {
+    int64_t ns, nl, l0, nS;
+    const int32_t* lr;
+    __device__ __forceinline__ int64_t at(int64_t j) const {
+        if (j < ns) return j;
+        if (j < ns + nl) return l0 + (j - ns);
+        return (int64_t)lr[j - ns - nl];
+    }
+};
+
+__device__ __forceinline__ KeyList key_list(int64_t t, const AttArgs& aa, const int32_t* lr_row, int32_t cnt) {
+    const Geom q = query_geom(t, aa.n_blocks, aa.n_sinks, aa.window);
+    KeyList kl;
+    kl.ns = q.sink_end < q.l0 ? q.sink_end : q.l0;
+    kl.l0 = q.l0;
+    kl.nl = t - q.l0 + 1;
+    kl.lr = lr_row;
+    kl.nS = kl.ns + kl.nl + (cnt > 0 ? cnt : 0);
+    return kl;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attend_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ V,
+                                                          const int64_t* __restrict__ q_pos,
+                                                          const int32_t* __restrict__ lr_idx,
+                                                          const int32_t* __restrict__ lr_cnt, AttArgs aa,
+                                                          uint16_t* __restrict__ O, float* __restrict__ part,
+                                                          int64_t nwg_padded) {
+    constexpr int DPL = D / 4;   // head dims per lane group (lane (r, h) owns [DPL h, DPL h + DPL))
+    constexpr int KS = DPL / 8;  // 8-element k-steps per lane for QK
+    constexpr int NC = DPL / 4;  // 4-dim chunks for the transpose and PV
+    const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4;
+    const int64_t logical = xcd_logical(blockIdx.x, nwg_padded);
+    const int64_t w_id = logical * 4 + wid;
+    if (w_id >= aa.n_units * aa.splits) return;
+    const int64_t uu = w_id / aa.splits;
+    const int s = (int)(w_id % aa.splits);
+    const AUnit un = aunit_of(uu, aa);
+    const int64_t t = q_pos[un.b * aa.n_q + un.i];
+    const int32_t cnt = lr_cnt[un.u];
+    const int n = r;  // head column of the C layouts
+    const int64_t orow = ((un.b * aa.n_q + un.i) * aa.H_q + un.g * aa.G + n) * D;
+
+    f32x4 acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kNegInf, l_run = 0.f;
+
+    if (t >= 0 && cnt >= 0) {
+        const KeyList kl = key_list(t, aa, lr_idx + un.u * aa.k, cnt);
+        int64_t chunk = (kl.nS + aa.splits - 1) / aa.splits;
+        chunk = (chunk + 31) & ~(int64_t)31;
+        const int64_t j0 = (int64_t)s * chunk;
+        const int64_t j1 = j0 + chunk < kl.nS ? j0 + chunk : kl.nS;
+
+        // B operand of S^T = K Q^T: head n, dims DPL h + 8 ks + [0, 8)
+        uint4 qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[ks] = uint4{0, 0, 0, 0};
+            if (n < aa.G) qf[ks] = *reinterpret_cast<const uint4*>(Q + orow + DPL * h + 8 * ks);
+        }
+        // identity B for the transposing MFMA: lane (col n, k-group h) holds I[4h + j][n]
+        s16x4 ident;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ident[j] = (4 * h + j == n) ? (short)0x3F80 : (short)0;
+
+        const int64_t bg = un.b * aa.H_kv + un.g;
+        const uint16_t* Kbg = K + bg * aa.t_cap * D;
+        const uint16_t* Vbg = V + bg * aa.t_cap * D;
+
+        for (int64_t j = j0; j < j1; j += 32) {
+            const int64_t ja = j + r, jb = j + 16 + r;
+            int64_t ta = ja < j1 ? kl.at(ja) : -1, tb = jb < j1 ? kl.at(jb) : -1;
+            // a key outside [0, t] (malformed list) is never read and never scored
+            const bool va = ta >= 0 && ta <= t, vb = tb >= 0 && tb <= t;
+            ta = va ? ta : 0;
+            tb = vb ? tb : 0;
+            uint4 ka[KS], kb[KS], xa[KS], xb[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                ka[ks] = va ? *reinterpret_cast<const uint4*>(Kbg + ta * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
+                kb[ks] = vb ? *reinterpret_cast<const uint4*>(Kbg + tb * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
+                xa[ks] = va ? *reinterpret_cast<const uint4*>(Vbg + ta * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
+                xb[ks] = vb ? *reinterpret_cast<const uint4*>(Vbg + tb * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
+            }
+            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), as_bf16x8(qf[ks]), sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), as_bf16x8(qf[ks]), sb, 0, 0, 0);
+            }
+            // rows of sa: keys j + 4h + v; rows of sb: keys j + 16 + 4h + v
+            float pa[4], pb[4];
+            float mx = kNegInf;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t ra = j + 4 * h + v, rb = j + 16 + 4 * h + v;
+                const int64_t ua = ra < j1 ? kl.at(ra) : -1, ub = rb < j1 ? kl.at(rb) : -1;
+                pa[v] = (ua >= 0 && ua <= t) ? sa[v] * aa.scale : kNegInf;
+                pb[v] = (ub >= 0 && ub <= t) ? sb[v] * aa.scale : kNegInf;
+                mx = fmaxf(mx, fmaxf(pa[v], pb[v]));
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            if (m_new == kNegInf) continue;   // every key of this tile is masked
+            const float alpha = __expf(m_run - m_new);
+            m_run = m_new;
+            uint32_t pk[4];
+            float psum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; v += 2) {
+                const uint16_t a0 = f32_to_bf16(__expf(pa[v] - m_new)), a1 = f32_to_bf16(__expf(pa[v + 1] - m_new));
+                const uint16_t b0 = f32_to_bf16(__expf(pb[v] - m_new)), b1 = f32_to_bf16(__expf(pb[v + 1] - m_new));
+                psum += bf16_to_f32(a0) + bf16_to_f32(a1) + bf16_to_f32(b0) + bf16_to_f32(b1);
+                pk[v / 2] = (uint32_t)a0 | ((uint32_t)a1 << 16);
+                pk[2 + v / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+            }
+            l_run = l_run * alpha + psum;
+            const bf16x8 pfrag = as_bf16x8(uint4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                // chunk c: lane (r, h) contributes V[key r][DPL h + 4c + 0..3]
+                const uint32_t* wa = reinterpret_cast<const uint32_t*>(&xa[c / 2]);
+                const uint32_t* wb = reinterpret_cast<const uint32_t*>(&xb[c / 2]);
+                const int o = (c & 1) * 2;
+                const s16x4 va4 = __builtin_bit_cast(s16x4, u32x2{wa[o], wa[o + 1]});
+                const s16x4 vb4 = __builtin_bit_cast(s16x4, u32x2{wb[o], wb[o + 1]});
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 ta4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, ident, z, 0, 0, 0);
+                const f32x4 tb4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb4, ident, z, 0, 0, 0);
+                // lane (n, h): V[key 4h+v][dim(c, n)] and V[key 16+4h+v][dim(c, n)], exact in fp32
+                uint32_t vt[4];
+                vt[0] = (__float_as_uint(ta4[0]) >> 16) | (__float_as_uint(ta4[1]) & 0xFFFF0000u);
+                vt[1] = (__float_as_uint(ta4[2]) >> 16) | (__float_as_uint(ta4[3]) & 0xFFFF0000u);
+                vt[2] = (__float_as_uint(tb4[0]) >> 16) | (__float_as_uint(tb4[1]) & 0xFFFF0000u);
+                vt[3] = (__float_as_uint(tb4[2]) >> 16) | (__float_as_uint(tb4[3]) & 0xFFFF0000u);
+                acc[c] *= alpha;
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uint4{vt[0], vt[1], vt[2], vt[3]}), pfrag,
+                                                                 acc[c], 0, 0, 0);
+            }
+        }
+    }
+    // acc[c][v] = unnormalised O[head n][DPL h + 4c + v]
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (aa.splits == 1) {
+        if (n < aa.G) {
+            const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+            uint32_t w[DPL / 2];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                w[2 * c] = (uint32_t)f32_to_bf16(acc[c][0] * inv) | ((uint32_t)f32_to_bf16(acc[c][1] * inv) << 16);
+                w[2 * c + 1] = (uint32_t)f32_to_bf16(acc[c][2] * inv) | ((uint32_t)f32_to_bf16(acc[c][3] * inv) << 16);
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < DPL / 8; ++q4)
+                *reinterpret_cast<uint4*>(O + orow + DPL * h + 8 * q4) =
+                    uint4{w[4 * q4], w[4 * q4 + 1], w[4 * q4 + 2], w[4 * q4 + 3]};
+        }
+    } else if (n < aa.G) {
+        float* pp = part + ((un.u * aa.splits + s) * aa.G + n) * (D + 2);
+        if (h == 0) {
+            pp[0] = m_run;
+            pp[1] = l_run;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pp[2 + DPL * h + 4 * c + v] = acc[c][v];
+    }
+}
+
+// fp32 path: plain fp32 arithmetic (lanes over keys for the scores, lanes
+// over head dims for PV).
+__global__ __launch_bounds__(256) void attend_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                         const float* __restrict__ V,
+                                                         const int64_t* __restrict__ q_pos,
+                                                         const int32_t* __restrict__ lr_idx,
+                                                         const int32_t* __restrict__ lr_cnt, AttArgs aa, int D,
+                                                         float* __restrict__ O, float* __restrict__ part,
+                                                         int64_t nwg_padded) {
+    __shared__ float qs[4][kMaxGroup][128];
+    __shared__ float ps[4][64][kMaxGroup];
+    __shared__ int64_t ts[4][64];
+    const int l = lane_id(), wid = threadIdx.x >> 6;
+    const int64_t logical = xcd_logical(blockIdx.x, nwg_padded);
+    const int64_t w_id = logical * 4 + wid;
+    if (w_id >= aa.n_units * aa.splits) return;
+    const int64_t uu = w_id / aa.splits;
+    const int s = (int)(w_id % aa.splits);
+    const AUnit un = aunit_of(uu, aa);
+    const int64_t t = q_pos[un.b * aa.n_q + un.i];
+    const int32_t cnt = lr_cnt[un.u];
+    const int G = aa.G;
+    const int64_t qrow0 = ((un.b * aa.n_q + un.i) * aa.H_q + un.g * G) * D;
+    float m_run[kMaxGroup], l_run[kMaxGroup], acc[kMaxGroup][2];
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+        m_run[hh] = kNegInf;
+        l_run[hh] = 0.f;
+        acc[hh][0] = acc[hh][1] = 0.f;
+    }
+    if (t >= 0 && cnt >= 0) {
+        for (int hh = 0; hh < G; ++hh)
+            for (int dd = l; dd < D; dd += 64) qs[wid][hh][dd] = Q[qrow0 + (int64_t)hh * D + dd];
+        __builtin_amdgcn_wave_barrier();
+        const KeyList kl = key_list(t, aa, lr_idx + un.u * aa.k, cnt);
+        int64_t chunk = (kl.nS + aa.splits - 1) / aa.splits;
+        chunk = (chunk + 31) & ~(int64_t)31;
+        const int64_t j0 = (int64_t)s * chunk;
+        const int64_t j1 = j0 + chunk < kl.nS ? j0 + chunk : kl.nS;
+        const int64_t bg = un.b * aa.H_kv + un.g;
+        const float* Kbg = K + bg * aa.t_cap * D;
+        const float* Vbg = V + bg * aa.t_cap * D;
+        for (int64_t j = j0; j < j1; j += 64) {
+            int64_t tk = j + l < j1 ? kl.at(j + l) : -1;
+            const bool ok = tk >= 0 && tk <= t;
+            tk = ok ? tk : 0;
+            ts[wid][l] = tk;
+            float sc[kMaxGroup];
+            for (int hh = 0; hh < G; ++hh) {
+                float a = 0.f;
+                for (int dd = 0; dd < D; ++dd) a = fmaf(qs[wid][hh][dd], Kbg[tk * D + dd], a);
+                sc[hh] = ok ? a * aa.scale : kNegInf;
+            }
+            for (int hh = 0; hh < G; ++hh) {
+                const float m_new = fmaxf(m_run[hh], wave_max(sc[hh]));
+                const float alpha = m_new == kNegInf ? 1.f : expf(m_run[hh] - m_new);
+                const float p = (ok && m_new > kNegInf) ? expf(sc[hh] - m_new) : 0.f;
+                l_run[hh] = l_run[hh] * alpha + wave_sum(p);
+                m_run[hh] = m_new;
+                acc[hh][0] *= alpha;
+                acc[hh][1] *= alpha;
+                ps[wid][l][hh] = p;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int nk = (int)((j1 - j) < 64 ? (j1 - j) : 64);
+            for (int jj = 0; jj < nk; ++jj) {
+                const int64_t tt = ts[wid][jj];
+                const float v0 = l < D ? Vbg[tt * D + l] : 0.f;
+                const float v1 = l + 64 < D ? Vbg[tt * D + l + 64] : 0.f;
+                for (int hh = 0; hh < G; ++hh) {
+                    const float p = ps[wid][jj][hh];
+                    acc[hh][0] = fmaf(p, v0, acc[hh][0]);
+                    acc[hh][1] = fmaf(p, v1, acc[hh][1]);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+    for (int hh = 0; hh < G; ++hh) {
+        if (aa.splits == 1) {
+            const float inv = l_run[hh] > 0.f ? 1.0f / l_run[hh] : 0.f;
+            if (l < D) O[qrow0 + (int64_t)hh * D + l] = acc[hh][0] * inv;
+            if (l + 64 < D) O[qrow0 + (int64_t)hh * D + l + 64] = acc[hh][1] * inv;
+        } else {
+            float* pp = part + ((un.u * aa.splits + s) * G + hh) * (D + 2);
+            if (l == 0) {
+                pp[0] = m_run[hh];
+                pp[1] = l_run[hh];
+            }
+            if (l < D) pp[2 + l] = acc[hh][0];
+            if (l + 64 < D) pp[2 + l + 64] = acc[hh][1];
+        }
+    }
+}
+
+// Log-sum-exp combine of the split partials: one wave per (unit, head).
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, AttArgs aa, int D, int out_bf16,
+                                                      void* O) {
+    const int l = lane_id(), wid = threadIdx.x >> 6;
+    const int64_t w_id = (int64_t)blockIdx.x * 4 + wid;
+    if (w_id >= aa.n_units * aa.G) return;
+    const int64_t u = w_id / aa.G;
+    const int hh = (int)(w_id % aa.G);
+    float m = kNegInf;
+    for (int s = 0; s < aa.splits; ++s) m = fmaxf(m, part[((u * aa.splits + s) * aa.G + hh) * (D + 2)]);
+    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+    if (m > kNegInf) {
+        for (int s = 0; s < aa.splits; ++s) {
+            const float* pp = part + ((u * aa.splits + s) * aa.G + hh) * (D + 2);
+            const float ms = pp[0];
+            if (!(ms > kNegInf)) continue;
+            const float e = __expf(ms - m);
+            lsum += pp[1] * e;
+            if (l < D) o0 += pp[2 + l] * e;
+            if (l + 64 < D) o1 += pp[2 + l + 64] * e;
+        }
+    }
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    const int64_t g = u % aa.H_kv;
+    const int64_t bi = u / aa.H_kv;
+    const int64_t orow = (bi * aa.H_q + g * aa.G + hh) * D;
+    if (out_bf16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(O);
+        if (l < D) o[orow + l] = f32_to_bf16(o0 * inv);
+        if (l + 64 < D) o[orow + l + 64] = f32_to_bf16(o1 * inv);
+    } else {
+        float* o = reinterpret_cast<float*>(O);
+        if (l < D) o[orow + l] = o0 * inv;
+        if (l + 64 < D) o[orow + l + 64] = o1 * inv;
+    }
+}
+
+}  // namespace
+
+int attend_splits(int64_t n_units, int window, int k) {
+    if (n_units >= 8192) return 1;
+    const int64_t keys = (int64_t)window + kBlockTokens + k + 64;
+    int64_t want = (8192 + n_units - 1) / n_units;
+    const int64_t maxs = (keys + 255) / 256;
+    if (want > maxs) want = maxs;
+    if (want < 1) want = 1;
+    if (want > 64) want = 64;
+    return (int)want;
+}
+
+hipError_t launch_attend(const void* Q, const void* K, const void* V, const int64_t* q_pos, const int32_t* lr_idx,
+                         const int32_t* lr_cnt, const AttArgs& aa, int D, bool bf16, void* O, float* part,
+                         hipStream_t st) {
+    const int64_t waves = aa.n_units * aa.splits;
+    int64_t nwg = (waves + 3) / 4;
+    nwg = (nwg + 7) & ~(int64_t)7;
+    if (bf16) {
+        if (D == 128)
+            hipLaunchKernelGGL(attend_bf16_kernel<128>, dim3((unsigned)nwg), dim3(256), 0, st,
+                               static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                               static_cast<const uint16_t*>(V), q_pos, lr_idx, lr_cnt, aa, static_cast<uint16_t*>(O),
+                               part, nwg);
+        else
+            hipLaunchKernelGGL(attend_bf16_kernel<64>, dim3((unsigned)nwg), dim3(256), 0, st,
+                               static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                               static_cast<const uint16_t*>(V), q_pos, lr_idx, lr_cnt, aa, static_cast<uint16_t*>(O),
+                               part, nwg);
+    } else {
+        hipLaunchKernelGGL(attend_f32_kernel, dim3((unsigned)nwg), dim3(256), 0, st, static_cast<const float*>(Q),
+                           static_cast<const float*>(K), static_cast<const float*>(V), q_pos, lr_idx, lr_cnt, aa, D,
+                           static_cast<float*>(O), part, nwg);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || aa.splits == 1) return e;
+    const int64_t cw = aa.n_units * aa.G;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((cw + 3) / 4)), dim3(256), 0, st, part, aa, D, bf16 ? 1 : 0, O);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -1,0 +1,326 @@
+// Key side of LSA on gfx950: latent projection, L2 normalisation, 4-key
+// pooling and capped Ward clustering per 512-entry block, then the centroids
+// and the binary tree of merged buckets.
+//
+// Method: zhichai.net explainer "卡片柜", ch.2 (project to 64-d, normalise,
+// pool 4 keys, Ward inside each 512-entry block to buckets of mean 8 / max
+// 16, normalised bucket mean as the card) and ch.4 (complete binary tree,
+// node centroid = mean of all keys below).
+//
+// One workgroup of 512 threads clusters one block; thread i owns entry i and,
+// while it is alive, the cluster whose smallest member is i (its id).  Each
+// thread keeps its cluster mean (64 fp32) in registers together with its
+// nearest allowed partner among larger ids (nn, delta).  A merge step is a
+// workgroup argmin over (delta, id, nn) — the lowest (id_A, id_B) wins ties —
+// followed by recomputing, from broadcast means, the partner of the merged
+// cluster and of every cluster whose partner was A or B; every other
+// cluster only compares its partner with the merged cluster.  This is the
+// same greedy decision sequence as rescanning all pairs every step.
+
+#include "lsa_launch.hpp"
+
+namespace lsa {
+
+namespace {
+
+constexpr int kWardThreads = 512;
+constexpr int kRows = 16;             // broadcast rows per recompute round
+constexpr float kInf = __builtin_huge_valf();
+
+__device__ __forceinline__ uint64_t pair_key(float d, int id, int nn) {
+    return ((uint64_t)__float_as_uint(d) << 32) | ((uint64_t)id << 16) | (uint64_t)nn;
+}
+
+template <typename TIN>
+__global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restrict__ K, int64_t t_cap, int d,
+                                                            int H_kv, const TIN* __restrict__ W, CacheView cv) {
+    const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t bg = (int64_t)b * H_kv + g;
+
+    __shared__ __align__(16) float Wsh[128 * kLatent];     // projection (phase 1) / entry chunks (phase 2 init)
+    __shared__ __align__(16) float rowv[kRows][kLatent];   // broadcast means
+    __shared__ int row_id[kRows], row_n[kRows];
+    __shared__ uint64_t red[8];
+    __shared__ uint64_t red2[8][kRows];
+    __shared__ __align__(16) float sBmu[kLatent];
+    __shared__ int sBn, nrows;
+    __shared__ short lab[kWardThreads];
+    __shared__ short rank_of[kWardThreads];
+    __shared__ int size_by_rank[kLeavesPerBlock];
+    __shared__ int wcnt[8];
+
+    // ---------------- phase 1: pooled entry e_i = mean of the 4 unit latents
+    for (int i = tid; i < d * kLatent; i += kWardThreads) Wsh[i] = load_f32(W + i);
+    __syncthreads();
+    float mu[kLatent];
+#pragma unroll
+    for (int c = 0; c < kLatent; ++c) mu[c] = 0.f;
+    const int64_t tok0 = (int64_t)blk * kBlockTokens + (int64_t)kPool * tid;
+    const TIN* kr = K + (bg * t_cap + tok0) * d;
+    for (int j = 0; j < kPool; ++j) {
+        float z[kLatent];
+#pragma unroll
+        for (int c = 0; c < kLatent; ++c) z[c] = 0.f;
+        const TIN* row = kr + (int64_t)j * d;
+        for (int dd = 0; dd < d; ++dd) {
+            const float kv = load_f32(row + dd);
+            const float4* wr = reinterpret_cast<const float4*>(Wsh + dd * kLatent);
+#pragma unroll
+            for (int c4 = 0; c4 < kLatent / 4; ++c4) {
+                const float4 w = wr[c4];
+                z[4 * c4 + 0] = fmaf(kv, w.x, z[4 * c4 + 0]);
+                z[4 * c4 + 1] = fmaf(kv, w.y, z[4 * c4 + 1]);
+                z[4 * c4 + 2] = fmaf(kv, w.z, z[4 * c4 + 2]);
+                z[4 * c4 + 3] = fmaf(kv, w.w, z[4 * c4 + 3]);
+            }
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < kLatent; ++c) ss = fmaf(z[c], z[c], ss);
+        const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+#pragma unroll
+        for (int c = 0; c < kLatent; ++c) mu[c] = fmaf(z[c], inv, mu[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < kLatent; ++c) mu[c] *= 0.25f;
+
+    // ---------------- phase 2: capped Ward
+    int n = 1;
+    bool act = true;
+    lab[tid] = (short)tid;
+    float nd = kInf;
+    int nn = -1;
+    // initial partners: singletons, delta = |e_i - e_j|^2 / 2 over j > i
+    for (int c0 = 0; c0 < kWardThreads; c0 += 32) {
+        __syncthreads();
+        if (tid >= c0 && tid < c0 + 32) {
+#pragma unroll
+            for (int c = 0; c < kLatent; ++c) Wsh[(tid - c0) * kLatent + c] = mu[c];
+        }
+        __syncthreads();
+        if (c0 + 31 > tid) {
+            for (int jj = 0; jj < 32; ++jj) {
+                const int j = c0 + jj;
+                if (j <= tid) continue;
+                const float4* er = reinterpret_cast<const float4*>(Wsh + jj * kLatent);
+                float dist = 0.f;
+#pragma unroll
+                for (int c4 = 0; c4 < kLatent / 4; ++c4) {
+                    const float4 e = er[c4];
+                    float t0 = mu[4 * c4 + 0] - e.x, t1 = mu[4 * c4 + 1] - e.y;
+                    float t2 = mu[4 * c4 + 2] - e.z, t3 = mu[4 * c4 + 3] - e.w;
+                    dist = fmaf(t0, t0, dist);
+                    dist = fmaf(t1, t1, dist);
+                    dist = fmaf(t2, t2, dist);
+                    dist = fmaf(t3, t3, dist);
+                }
+                const float dl = 0.5f * dist;
+                if (dl < nd) {
+                    nd = dl;
+                    nn = j;
+                }
+            }
+        }
+    }
+
+    const int n_merge = kBlockEntries - kLeavesPerBlock;
+    for (int step = 0; step < n_merge; ++step) {
+        uint64_t key = (act && nn >= 0) ? pair_key(nd, tid, nn) : ~0ull;
+        key = wave_min_u64(key);
+        if (lane == 0) red[wid] = key;
+        if (tid == 0) nrows = 1;
+        __syncthreads();
+        key = red[0];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) key = red[w] < key ? red[w] : key;
+        if (key == ~0ull) break;  // no allowed pair: impossible before 64 clusters remain
+        const int A = (int)((key >> 16) & 0xFFFF), B = (int)(key & 0xFFFF);
+        bool redo = act && tid != A && tid != B && (nn == A || nn == B);
+        if (tid == B) {
+#pragma unroll
+            for (int c = 0; c < kLatent; ++c) sBmu[c] = mu[c];
+            sBn = n;
+            act = false;
+            nn = -1;
+            nd = kInf;
+        }
+        __syncthreads();
+        if (tid == A) {
+            const float fa = (float)n, fb = (float)sBn, inv = 1.0f / (float)(n + sBn);
+#pragma unroll
+            for (int c = 0; c < kLatent; ++c) {
+                mu[c] = (fa * mu[c] + fb * sBmu[c]) * inv;
+                rowv[0][c] = mu[c];
+            }
+            n += sBn;
+            row_id[0] = A;
+            row_n[0] = n;
+            // its partner is recomputed from scratch below
+            nn = -1;
+            nd = kInf;
+        }
+        if (lab[tid] == B) lab[tid] = (short)A;
+
+        bool first = true;
+        while (true) {
+            if (!first) {
+                if (tid == 0) nrows = 0;
+                __syncthreads();
+            }
+            if (redo) {
+                const int s = atomicAdd(&nrows, 1);
+                if (s < kRows) {
+#pragma unroll
+                    for (int c = 0; c < kLatent; ++c) rowv[s][c] = mu[c];
+                    row_id[s] = tid;
+                    row_n[s] = n;
+                    redo = false;
+                }
+            }
+            __syncthreads();
+            const int nr = nrows < kRows ? nrows : kRows;
+            for (int r = 0; r < nr; ++r) {
+                const int Kr = row_id[r], nK = row_n[r];
+                const bool ok = act && tid != Kr && (nK + n <= kMaxBucket);
+                float dl = kInf;
+                if (ok) {
+                    const float4* rv = reinterpret_cast<const float4*>(rowv[r]);
+                    float dist = 0.f;
+#pragma unroll
+                    for (int c4 = 0; c4 < kLatent / 4; ++c4) {
+                        const float4 e = rv[c4];
+                        float t0 = mu[4 * c4 + 0] - e.x, t1 = mu[4 * c4 + 1] - e.y;
+                        float t2 = mu[4 * c4 + 2] - e.z, t3 = mu[4 * c4 + 3] - e.w;
+                        dist = fmaf(t0, t0, dist);
+                        dist = fmaf(t1, t1, dist);
+                        dist = fmaf(t2, t2, dist);
+                        dist = fmaf(t3, t3, dist);
+                    }
+                    dl = ((float)(nK * n) / (float)(nK + n)) * dist;
+                }
+                // clusters with smaller ids only compare their partner with the merged one
+                if (first && r == 0 && ok && tid < Kr && !(nn == A || nn == B)) {
+                    if (dl < nd || (dl == nd && Kr < nn)) {
+                        nd = dl;
+                        nn = Kr;
+                    }
+                }
+                uint64_t k2 = (ok && tid > Kr) ? (((uint64_t)__float_as_uint(dl) << 32) | (uint64_t)tid) : ~0ull;
+                k2 = wave_min_u64(k2);
+                if (lane == 0) red2[wid][r] = k2;
+            }
+            __syncthreads();
+            for (int r = 0; r < nr; ++r) {
+                if (tid == row_id[r]) {
+                    uint64_t k = red2[0][r];
+#pragma unroll
+                    for (int w = 1; w < 8; ++w) k = red2[w][r] < k ? red2[w][r] : k;
+                    if (k == ~0ull) {
+                        nn = -1;
+                        nd = kInf;
+                    } else {
+                        nn = (int)(k & 0xFFFF);
+                        nd = __uint_as_float((uint32_t)(k >> 32));
+                    }
+                }
+            }
+            first = false;
+            if (!__syncthreads_or(redo ? 1 : 0)) break;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- phase 3: leaves of this block, ordered by id
+    const uint64_t bal = __ballot(act);
+    if (lane == 0) wcnt[wid] = __popcll(bal);
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wid; ++w) base += wcnt[w];
+    const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
+    rank_of[tid] = act ? (short)rank : (short)-1;
+    if (act) size_by_rank[rank] = n;
+    __syncthreads();
+    cv.eleaf[bg * cv.s_eleaf + (int64_t)blk * kBlockEntries + tid] = (uint8_t)rank_of[lab[tid]];
+    if (act) {
+        int off = 0;
+        for (int r = 0; r < rank; ++r) off += size_by_rank[r];
+        const int64_t leaf = (int64_t)blk * kLeavesPerBlock + rank;
+        float* srow = cv.sums + bg * cv.s_sums + leaf * kLatent;
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < kLatent; ++c) {
+            srow[c] = mu[c] * (float)n;
+            ss = fmaf(mu[c], mu[c], ss);
+        }
+        const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+        if (cv.bf16) {
+            uint16_t* crow = reinterpret_cast<uint16_t*>(cv.cent) + bg * cv.s_cent + leaf * kLatent;
+#pragma unroll
+            for (int c = 0; c < kLatent; ++c) crow[c] = f32_to_bf16(mu[c] * inv);
+        } else {
+            float* crow = reinterpret_cast<float*>(cv.cent) + bg * cv.s_cent + leaf * kLatent;
+#pragma unroll
+            for (int c = 0; c < kLatent; ++c) crow[c] = mu[c] * inv;
+        }
+        cv.meta[bg * cv.s_meta + leaf] = (uint32_t)n | ((uint32_t)off << 8);
+        uint16_t* mem = cv.members + bg * cv.s_members + (int64_t)blk * kBlockEntries + off;
+        int cnt = 0;
+        for (int j = tid; j < kWardThreads && cnt < n; ++j)
+            if (lab[j] == tid) mem[cnt++] = (uint16_t)j;
+    }
+}
+
+// One wave per tree node: sum of the two children (an odd last node has
+// one), its norm, and the rounded centroid (ch.4: node centroid = mean of
+// every key below it; the normalisation makes mean and sum equivalent).
+__global__ __launch_bounds__(256) void tree_level_kernel(CacheView cv, int lev, int64_t n_child, int64_t n_par) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int64_t node = (int64_t)blockIdx.x * 4 + wid;
+    if (node >= n_par) return;
+    const int64_t bg = blockIdx.y;
+    const float* cs = lev == 1 ? cv.sums + bg * cv.s_sums
+                               : cv.tsums + bg * cv.s_tsums + cv.level_off[lev - 1] * kLatent;
+    const int64_t c0 = 2 * node, c1 = c0 + 1;
+    float s = cs[c0 * kLatent + lane];
+    if (c1 < n_child) s += cs[c1 * kLatent + lane];
+    const int64_t o = (cv.level_off[lev] + node) * kLatent + lane;
+    cv.tsums[bg * cv.s_tsums + o] = s;
+    const float ss = wave_sum(s * s);
+    const float v = ss > 0.f ? s * (1.0f / sqrtf(ss)) : 0.f;
+    if (cv.bf16)
+        reinterpret_cast<uint16_t*>(cv.tcent)[bg * cv.s_tcent + o] = f32_to_bf16(v);
+    else
+        reinterpret_cast<float*>(cv.tcent)[bg * cv.s_tcent + o] = v;
+}
+
+}  // namespace
+
+hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
+                        const void* W, hipStream_t st) {
+    if (cv.n_blocks > 0) {
+        dim3 grid(cv.n_blocks, H_kv, B);
+        if (bf16)
+            hipLaunchKernelGGL(ward_kernel<uint16_t>, grid, dim3(kWardThreads), 0, st,
+                               static_cast<const uint16_t*>(K), t_cap, d, H_kv, static_cast<const uint16_t*>(W), cv);
+        else
+            hipLaunchKernelGGL(ward_kernel<float>, grid, dim3(kWardThreads), 0, st, static_cast<const float*>(K),
+                               t_cap, d, H_kv, static_cast<const float*>(W), cv);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_tree(const CacheView& cv, int B, int H_kv, hipStream_t st) {
+    for (int lev = 1; lev < cv.n_levels; ++lev) {
+        const int64_t n_child = cv.level_size[lev - 1], n_par = cv.level_size[lev];
+        dim3 grid((unsigned)((n_par + 3) / 4), (unsigned)(B * H_kv));
+        hipLaunchKernelGGL(tree_level_kernel, grid, dim3(256), 0, st, cv, lev, n_child, n_par);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace lsa

@@ -1,0 +1,171 @@
+// Shared device-side definitions of the LSA HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lsa.h"
+
+namespace lsa {
+
+constexpr int kLatent = LSA_LATENT_DIM;           // 64
+constexpr int kPool = LSA_POOL;                   // 4
+constexpr int kBlockEntries = LSA_BLOCK_ENTRIES;  // 512
+constexpr int kBlockTokens = LSA_BLOCK_TOKENS;    // 2048
+constexpr int kLeavesPerBlock = LSA_LEAVES_PER_BLOCK;
+constexpr int kMaxBucket = LSA_MAX_BUCKET;
+constexpr int kMaxGroup = LSA_MAX_GROUP;
+constexpr int kMaxLevels = 40;
+constexpr int kCandCap = 512;      // candidates per (query, KV head) in the fused flat search
+constexpr int kFullTake = 0xFFFF;  // "every eligible token of this bucket"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- cache view
+// Device pointers of one bucket cache; strides are element counts between
+// consecutive (b, g) slices.
+struct CacheView {
+    void* cent;            // [B, H_kv, leaves_max, 64]  dtype
+    float* sums;           // [B, H_kv, leaves_max, 64]  fp32
+    uint32_t* meta;        // [B, H_kv, leaves_max]      size | first-member offset << 8
+    uint16_t* members;     // [B, H_kv, n_blocks_max, 512]
+    uint8_t* eleaf;        // [B, H_kv, n_blocks_max, 512]
+    void* tcent;           // [B, H_kv, nodes_max, 64]   dtype (tree levels >= 1)
+    float* tsums;          // [B, H_kv, nodes_max, 64]
+    int64_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums;
+    int32_t n_blocks;      // full blocks bucketed
+    int32_t n_leaves;
+    int32_t n_levels;
+    int32_t bf16;          // centroid storage dtype
+    int64_t level_off[kMaxLevels];
+    int64_t level_size[kMaxLevels];
+};
+
+// ---------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// Monotone map float -> uint32 (larger float -> larger key); -0 folded into +0.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+    uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_key_inv(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+// Ranking key of a bucket: score descending, then id ascending.
+__device__ __forceinline__ uint64_t rank_key(float score, uint32_t id) {
+    return ((uint64_t)ord_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint32_t rank_key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu); }
+
+// ---------------------------------------------------------------- wave helpers (wave64)
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl_xor(lo, o);
+    hi = __shfl_xor(hi, o);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl(lo, src);
+    hi = __shfl(hi, src);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        uint64_t w = shfl_xor_u64(v, o);
+        v = w < v ? w : v;
+    }
+    return v;
+}
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int w = __shfl_up(v, o);
+        if (l >= o) v += w;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------- query geometry
+// nvis selectable blocks, sinks [0, sink_end), local window [l0, t];
+// eligible long-range tokens are [sink_end, l0).
+struct Geom {
+    int64_t t;
+    int32_t nvis;
+    int64_t sink_end;
+    int64_t l0;
+};
+__device__ __forceinline__ Geom query_geom(int64_t t, int32_t n_blocks, int32_t n_sinks, int32_t window) {
+    Geom G;
+    G.t = t;
+    int64_t bq = t / kBlockTokens;
+    G.nvis = (int32_t)(bq < n_blocks ? bq : n_blocks);
+    G.sink_end = (int64_t)n_sinks < t + 1 ? (int64_t)n_sinks : t + 1;
+    int64_t lw = t - (int64_t)window + 1;
+    int64_t lb = (int64_t)kBlockTokens * G.nvis;
+    int64_t l0 = lw < lb ? lw : lb;
+    G.l0 = l0 > 0 ? l0 : 0;
+    return G;
+}
+
+// Eligible tokens of one bucket: its tokens in [sink_end, l0).
+__device__ __forceinline__ int leaf_weight(const CacheView& cv, int64_t bg, uint32_t leaf, const Geom& q) {
+    const int blk = leaf / kLeavesPerBlock;
+    const int64_t lo = (int64_t)blk * kBlockTokens, hi = lo + kBlockTokens;
+    const uint32_t m = cv.meta[bg * cv.s_meta + leaf];
+    const int sz = m & 0xFF;
+    if (lo >= q.sink_end && hi <= q.l0) return kPool * sz;
+    if (hi <= q.sink_end || lo >= q.l0) return 0;
+    const uint16_t* mem = cv.members + bg * cv.s_members + (int64_t)blk * kBlockEntries + ((m >> 8) & 0x3FF);
+    int w = 0;
+    for (int e = 0; e < sz; ++e) {
+        int64_t t0 = lo + (int64_t)mem[e] * kPool;
+#pragma unroll
+        for (int j = 0; j < kPool; ++j) w += (t0 + j >= q.sink_end && t0 + j < q.l0) ? 1 : 0;
+    }
+    return w;
+}
+
+}  // namespace lsa

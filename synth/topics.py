@@ -33,6 +33,7 @@ import hashlib
 import math
 from typing import Optional
 
+import numpy as np
 import torch
 
 KAPPA = 20.0
@@ -259,7 +260,10 @@ def random_lr_lists(cfg: LayerConfig, q_pos: torch.Tensor, seed: int = 0, n_bloc
     idx = torch.full((B, n_q, cfg.H_kv, max(k, 1)), -1, dtype=torch.int32)
     cnt = torch.zeros(B, n_q, cfg.H_kv, dtype=torch.int32)
     nb_all = cfg.T // 2048 if n_blocks is None else n_blocks
-    gen = _gen("cpu", seed, cfg.cid, "randlr")
+    digest = hashlib.sha256(repr((seed, cfg.cid, "randlr")).encode()).digest()
+    rng = np.random.default_rng(int.from_bytes(digest[:8], "little"))
+    idx_np = idx.numpy()
+    cnt_np = cnt.numpy()
     for b in range(B):
         for i in range(n_q):
             t = int(q_pos[b, i])
@@ -271,8 +275,7 @@ def random_lr_lists(cfg: LayerConfig, q_pos: torch.Tensor, seed: int = 0, n_bloc
                 want = min(k, int(span * fill))
                 if want <= 0:
                     continue
-                pick = torch.randperm(span, generator=gen)[:want] + lo
-                pick, _ = torch.sort(pick)
-                idx[b, i, g, :want] = pick.to(torch.int32)
-                cnt[b, i, g] = want
+                pick = np.sort(rng.choice(span, size=want, replace=False)) + lo
+                idx_np[b, i, g, :want] = pick
+                cnt_np[b, i, g] = want
     return idx[..., :k] if k > 0 else idx[..., :0], cnt
