@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the LSA layer hot path on one MI355X.
+
+Default workload: one bf16 prefill layer at T = 1,048,576 (8 KV / 40 query
+heads, head_dim 128, 4096-topic mixture, k = 2048, 4 sinks, window 1024,
+flat search).  One step = build_buckets over all keys + select and
+sparse_attend for every query (in chunks of 65,536 queries), with K, V, Q
+and W already resident in HBM.  Also measured: the decode step at 1M context
+(16 sequences, one query each) and, with --config 5, the 10M-token tree
+prefill.
+
+Prints one JSON line (metric, value in tokens/s, roofline of the dominant
+kernel measured with HIP events on the launch stream, and the CPU oracle
+baseline timed on a bounded sample).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_attention_indexing_latent_amd as lsa  # noqa: E402
+from synth import decode_inputs, get_config, layer_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+CHUNK = 65536
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on the current (launch) stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def span(self):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        self.pairs.append((s, e))
+        return e
+
+    def total_ms(self):
+        return sum(s.elapsed_time(e) for s, e in self.pairs)
+
+    def count(self):
+        return len(self.pairs)
+
+
+def prefill_step(cfg, G, ws, timers=None, tree=False, O=None):
+    """One pass of the whole hot path over one layer."""
+    tm = timers
+    if tm:
+        e = tm["build"].span()
+    cache = lsa.build_buckets(G["K"], G["W"], n_q_heads=cfg.H_q, build_tree=tree, cache=ws.get("cache"))
+    ws["cache"] = cache.buf
+    if tm:
+        e.record()
+    n_q = G["Q"].shape[1]
+    for i0 in range(0, n_q, CHUNK):
+        i1 = min(n_q, i0 + CHUNK)
+        Qc = G["Q"][:, i0:i1]
+        qp = G["q_pos"][:, i0:i1]
+        if tm:
+            e = tm["select"].span()
+        lr, cnt = lsa.select(Qc, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window,
+                             search="tree" if tree else "flat", beam=cfg.beam, workspace=ws.get("sel"),
+                             out=(ws["lr"][:, : i1 - i0], ws["cnt"][:, : i1 - i0]))
+        if tm:
+            e.record()
+            e = tm["attend"].span()
+        lsa.sparse_attend(Qc, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window,
+                          O=O[:, i0:i1])
+        if tm:
+            e.record()
+        if "cnt_sum" in ws:
+            ws["cnt_sum"] += int(cnt.clamp_min(0).sum().item())
+    return cache
+
+
+def selected_bytes(cfg, n_q_total, lr_total, q_pos_all):
+    """Algorithmic bytes of the gather attention over all queries: every key
+    and value row of S = sinks + window + long-range list, plus Q read and O
+    written.  (Keys are read once per (query, KV head).)"""
+    t = q_pos_all.double()
+    nvis = torch.clamp(torch.div(t, 2048, rounding_mode="floor"), max=cfg.T // 2048)
+    l0 = torch.clamp(torch.minimum(t - cfg.window + 1, 2048 * nvis), min=0)
+    sink_end = torch.clamp(torch.full_like(t, cfg.n_sinks), max=t + 1)
+    n_local = (t - l0 + 1) + torch.minimum(sink_end, l0)
+    keys = float(n_local.sum().item()) * cfg.H_kv + lr_total
+    row = cfg.d * 2
+    return keys * 2 * row + 2 * n_q_total * cfg.H_q * row
+
+
+def cpu_baseline(cfg, inp_cpu, budget_s=25.0):
+    """Oracle timed on this host: Ward on sampled blocks and select + attend
+    for sampled queries against the oracle's own cache of those blocks; the
+    full-layer time is projected from the measured per-unit costs."""
+    import oracle as O
+
+    cores = len(os.sched_getaffinity(0))
+    procs = max(1, min(cores, 16))
+    nb = 16
+    K = [inp_cpu["K"][0, g, : nb * 2048].double().numpy() for g in range(cfg.H_kv)]
+    W = inp_cpu["W"].double().numpy()
+    e = [O.pooled_entries(O.key_latents(K[g], W)) for g in range(1)]
+    blocks = [e[0][b * 512:(b + 1) * 512] for b in range(nb)]
+    t0 = time.perf_counter()
+    clusters = O.ward_blocks(blocks, processes=procs)
+    t_ward = time.perf_counter() - t0
+    per_block = t_ward * procs / nb                      # single-core seconds per block
+    cache = O.build_head_cache(K[0], W, cfg.dtype, T=nb * 2048, clusters=clusters)
+    Q = inp_cpu["Q"][0]
+    Kg, Vg = K[0], inp_cpu["V"][0, 0, : nb * 2048].double().numpy()
+    rng = np.random.default_rng(0)
+    ts = rng.integers((nb - 1) * 2048, nb * 2048, 24)
+    scale = 1 / math.sqrt(cfg.d)
+    t0 = time.perf_counter()
+    for t in ts:
+        qg = Q[int(t), : cfg.G].double().numpy()
+        lr, _ = O.select_flat(O.query_latent(qg, W, cfg.dtype), cache, int(t), cfg.k, cfg.n_sinks, cfg.window)
+        O.attend(qg, Kg, Vg, int(t), lr, cfg.n_sinks, cfg.window, cache["n_blocks"], scale)
+    per_unit = (time.perf_counter() - t0) / len(ts)      # at (nb-1)*64 visible buckets
+    # projection: selection cost grows with the visible buckets, the rest is per unit
+    leaves_sample = (nb - 1) * 64
+    mean_leaves = 64 * (cfg.T // 2048 - 1) / 2
+    full_s = (cfg.T // 2048) * cfg.H_kv * per_block + cfg.T * cfg.H_kv * per_unit * max(1.0, mean_leaves / leaves_sample)
+    full_s /= procs
+    return dict(value=cfg.T / full_s, unit="tokens/s", cores=procs, kind="oracle",
+                sample=(f"oracle Ward on {nb} blocks of KV head 0 ({t_ward:.1f}s on {procs} processes) and "
+                        f"select+attend for {len(ts)} (query, KV head) units at {leaves_sample} visible buckets "
+                        f"({per_unit * len(ts):.1f}s, 1 process); full 1-layer time projected as "
+                        f"blocks*H_kv*t_block + T*H_kv*t_unit*(mean visible buckets / sampled), divided by "
+                        f"{procs} processes"))
+
+
+def traffic_for(kernel_src: str, key: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(key)
+    except Exception:
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    return rec.get("bytes_per_launch") if rec.get("source_sha256") == h else None
+
+
+def run_prefill(args, cid):
+    cfg = get_config(cid)
+    dev = torch.device("cuda:0")
+    log(f"generating {cfg.name} on the GPU")
+    inp = layer_inputs(cfg, seed=0, device=dev)
+    G = {k: inp[k].contiguous() for k in ("K", "V", "W", "Q", "q_pos")}
+    torch.cuda.synchronize()
+    n_q = G["Q"].shape[1]
+    ws = {"lr": torch.empty(1, CHUNK, cfg.H_kv, cfg.k, dtype=torch.int32, device=dev),
+          "cnt": torch.empty(1, CHUNK, cfg.H_kv, dtype=torch.int32, device=dev)}
+    tree = cfg.search == "tree"
+    O = torch.empty_like(G["Q"])
+    # workspace sized for the largest chunk
+    cache0 = lsa.build_buckets(G["K"], G["W"], n_q_heads=cfg.H_q, build_tree=tree)
+    nbytes = lsa.select_workspace_bytes(cache0, lsa.select_cfg(cfg.k, cfg.n_sinks, cfg.window,
+                                                               "tree" if tree else "flat", cfg.beam),
+                                        min(CHUNK, n_q), cfg.H_q)
+    ws["sel"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws["cache"] = cache0.buf
+    ws["cnt_sum"] = 0
+    log("warmup")
+    for _ in range(args.warmup):
+        ws["cnt_sum"] = 0
+        prefill_step(cfg, G, ws, O=O)
+    lr_total = ws.pop("cnt_sum") if args.warmup > 0 else None
+    torch.cuda.synchronize()
+    timers = {k: Timer() for k in ("build", "select", "attend")}
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        prefill_step(cfg, G, ws, timers, tree=tree, O=O)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if lr_total is None:
+        ws["cnt_sum"] = 0
+        prefill_step(cfg, G, ws, O=O)
+        lr_total = ws.pop("cnt_sum")
+    ms_step = wall * 1000 / args.steps
+    att_ms = timers["attend"].total_ms() / args.steps
+    n_att = timers["attend"].count() // args.steps
+    alg_bytes = selected_bytes(cfg, n_q, lr_total, G["q_pos"][0].cpu())
+    achieved = alg_bytes / (att_ms / 1e3) / 1e9
+    per_launch = alg_bytes / n_att
+    traffic = traffic_for(os.path.join(ROOT, "sparse_attention_indexing_latent_amd", "csrc", "lsa_attend.hip"),
+                          f"attend_{cfg.name}")
+    res = dict(
+        metric="1-layer LSA prefill tokens/s at 1M ctx (1 GPU)" if cid == 4 else f"1-layer LSA prefill tokens/s ({cfg.name})",
+        value=cfg.T / (ms_step / 1e3), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=ms_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic (seeded topic-mixture keys, random-init projection)",
+        config={"workload": cfg.name, "T": cfg.T, "H_kv": cfg.H_kv, "H_q": cfg.H_q, "head_dim": cfg.d,
+                "k": cfg.k, "n_sinks": cfg.n_sinks, "window": cfg.window, "search": cfg.search,
+                "beam": cfg.beam, "query_chunk": CHUNK},
+        breakdown_ms={"build_buckets": timers["build"].total_ms() / args.steps,
+                      "select": timers["select"].total_ms() / args.steps, "sparse_attend": att_ms},
+        roofline={"kernel": "attend_bf16_kernel<128>", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                  "traffic": traffic, "alg_bytes_per_launch": per_launch,
+                  "avg_launch_ms": att_ms / n_att, "launches_per_step": n_att},
+    )
+    return res, cfg, inp
+
+
+def run_decode(args):
+    cfg = get_config(3)
+    dev = torch.device("cuda:0")
+    log("generating decode-16x1m on the GPU")
+    inp = decode_inputs(cfg, seed=0, device=dev)
+    G = {k: inp[k].contiguous() for k in ("K", "V", "W", "Q", "q_pos")}
+    cache = lsa.build_buckets(G["K"], G["W"], T=cfg.T, n_q_heads=cfg.H_q)
+    newK = G["K"][:, :, cfg.T].clone()
+    newV = G["V"][:, :, cfg.T].clone()
+    ws = lsa.select_workspace_bytes(cache, lsa.select_cfg(cfg.k, cfg.n_sinks, cfg.window), 1, cfg.H_q)
+    wsel = torch.empty(ws, dtype=torch.uint8, device=dev)
+    lr = torch.empty(cfg.B, 1, cfg.H_kv, cfg.k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(cfg.B, 1, cfg.H_kv, dtype=torch.int32, device=dev)
+    O = torch.empty_like(G["Q"])
+
+    def step():
+        G["K"][:, :, cfg.T] = newK          # append the new token's key/value
+        G["V"][:, :, cfg.T] = newV
+        lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window, workspace=wsel,
+                   out=(lr, cnt))
+        lsa.sparse_attend(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    n = 50
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / n
+    # needle retrieved by every (sequence, KV head)?
+    lr_c, cnt_c = lr.cpu(), cnt.cpu()
+    found = sum(all(p + j in set(lr_c[b, 0, g, : cnt_c[b, 0, g]].tolist()) for j in range(4))
+                for b, p in enumerate(inp["needle_pos"]) for g in range(cfg.H_kv))
+    # algorithmic bytes of one step: every visible centroid once per (sequence, KV head) + gathered rows
+    nl = (cfg.T // 2048) * 64
+    cent_bytes = cfg.B * cfg.H_kv * nl * 64 * 2
+    gather = cfg.B * cfg.H_kv * (int(cnt_c.clamp_min(0).sum()) / (cfg.B * cfg.H_kv) + cfg.window + cfg.n_sinks) * 512
+    alg = cent_bytes + gather
+    return dict(queries_per_s=cfg.B / (ms / 1e3), ms_per_step=ms, needle_found=f"{found}/{cfg.B * cfg.H_kv}",
+                alg_bytes_per_step=alg, hbm_frac=(alg / (ms / 1e3) / 1e9) / HBM_PEAK_GBS)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=4, choices=[2, 4, 5])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the LSA path here has no multi-GPU sharding); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    res, cfg, inp = run_prefill(args, args.config)
+    log(f"prefill {res['value']:.0f} tokens/s, {res['ms_per_step']:.1f} ms/step")
+    del inp
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        try:
+            res["decode_1m"] = run_decode(args)
+            log(f"decode {res['decode_1m']}")
+        except torch.cuda.OutOfMemoryError as exc:  # pragma: no cover
+            res["decode_1m"] = {"error": str(exc)[:200]}
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cfg_cpu = get_config(args.config)
+        small = cfg_cpu.scaled(T=16 * 2048)
+        inp_cpu = layer_inputs(small, seed=0)
+        res["cpu_baseline"] = cpu_baseline(cfg_cpu, inp_cpu)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
