@@ -135,10 +135,6 @@ lsa::CacheView make_view(const CacheGeom& c, void* cache, bool bf16) {
     v.n_leaves = (int32_t)c.n_leaves;
     v.n_levels = c.n_levels;
     v.bf16 = bf16 ? 1 : 0;
-    for (int i = 0; i < lsa::kMaxLevels; ++i) {
-        v.level_off[i] = c.level_off[i];
-        v.level_size[i] = c.level_size[i];
-    }
     return v;
 }
 
@@ -286,7 +282,8 @@ lsa_status lsa_build_buckets(const lsa_layout* layout, const void* K, int64_t ba
     lsa::CacheView v = make_view(c, cache, bf16);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = lsa::launch_build(v, K, bf16, t_cap, layout->head_dim, (int)batch, layout->n_kv_heads, W_k, st);
-    if (e == hipSuccess && layout->build_tree) e = lsa::launch_tree(v, (int)batch, layout->n_kv_heads, st);
+    if (e == hipSuccess && layout->build_tree)
+        e = lsa::launch_tree(v, c.level_off, c.level_size, (int)batch, layout->n_kv_heads, st);
     if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }

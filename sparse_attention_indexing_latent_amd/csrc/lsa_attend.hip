@@ -73,8 +73,95 @@ __device__ __forceinline__ KeyList key_list(int64_t t, const AttArgs& aa, const 
     return kl;
 }
 
+// Token of position jr of the key list, or -1 past the end or when the
+// list holds an index outside [0, t] (never read, never scored).
+__device__ __forceinline__ int32_t tok_of(const KeyList& kl, int64_t jr, int64_t j1, int64_t t) {
+    if (jr >= j1) return -1;
+    const int64_t tk = kl.at(jr);
+    return (tk >= 0 && tk <= t) ? (int32_t)tk : -1;
+}
+
+// Lane (r, h) loads head dims [D/4 h, D/4 h + D/4) of the key and value rows.
 template <int D>
-__global__ __launch_bounds__(256) void attend_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__device__ __forceinline__ void load_rows(const uint16_t* Kbg, const uint16_t* Vbg, int32_t tk, int h, uint4* kr,
+                                          uint4* vr) {
+    constexpr int DPL = D / 4, KS = DPL / 8;
+    // branch-free: a masked row reads row 0 (always present); its score is
+    // -inf and its probability exactly 0, so it contributes nothing
+    const uint32_t row = tk >= 0 ? (uint32_t)tk : 0u;
+    const uint4* kp = reinterpret_cast<const uint4*>(Kbg + (size_t)row * D + DPL * h);
+    const uint4* vp = reinterpret_cast<const uint4*>(Vbg + (size_t)row * D + DPL * h);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kr[ks] = kp[ks];
+        vr[ks] = vp[ks];
+    }
+}
+
+// One tile of 32 keys: S^T = K Q^T, online softmax, V^T via the identity
+// MFMA, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void attend_tile(int32_t ta, int32_t tb, const uint4* ka, const uint4* kb, const uint4* xa,
+                                            const uint4* xb, const uint4* qf, const s16x4& ident, int h, float scale,
+                                            float& m_run, float& l_run, f32x4* acc) {
+    constexpr int KS = D / 32, NC = D / 16;
+    const uint64_t ma = __ballot(ta >= 0), mb = __ballot(tb >= 0);   // bit r: key row r of the tile is valid
+    if ((ma | mb) == 0ull) return;                                       // wave-uniform
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), as_bf16x8(qf[ks]), sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), as_bf16x8(qf[ks]), sb, 0, 0, 0);
+    }
+    // rows of sa: keys 4h + v of the tile; rows of sb: keys 16 + 4h + v
+    float pa[4], pb[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        pa[v] = ((ma >> (4 * h + v)) & 1ull) ? sa[v] * scale : kNegInf;
+        pb[v] = ((mb >> (4 * h + v)) & 1ull) ? sb[v] * scale : kNegInf;
+        mx = fmaxf(mx, fmaxf(pa[v], pb[v]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __expf(m_run - m_new);
+    m_run = m_new;
+    uint32_t pk[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; v += 2) {
+        const uint16_t a0 = f32_to_bf16(__expf(pa[v] - m_new)), a1 = f32_to_bf16(__expf(pa[v + 1] - m_new));
+        const uint16_t b0 = f32_to_bf16(__expf(pb[v] - m_new)), b1 = f32_to_bf16(__expf(pb[v + 1] - m_new));
+        psum += bf16_to_f32(a0) + bf16_to_f32(a1) + bf16_to_f32(b0) + bf16_to_f32(b1);
+        pk[v / 2] = (uint32_t)a0 | ((uint32_t)a1 << 16);
+        pk[2 + v / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+    }
+    l_run = l_run * alpha + psum;
+    const bf16x8 pfrag = as_bf16x8(uint4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        // chunk c: lane (r, h) contributes V[key r][D/4 h + 4c + 0..3]
+        const uint4 wa = xa[c / 2], wb = xb[c / 2];
+        const s16x4 va4 = __builtin_bit_cast(s16x4, (c & 1) ? u32x2{wa.z, wa.w} : u32x2{wa.x, wa.y});
+        const s16x4 vb4 = __builtin_bit_cast(s16x4, (c & 1) ? u32x2{wb.z, wb.w} : u32x2{wb.x, wb.y});
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 ta4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, ident, z, 0, 0, 0);
+        const f32x4 tb4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb4, ident, z, 0, 0, 0);
+        // lane (n, h): V[key 4h+v][dim(c, n)] and V[key 16+4h+v][dim(c, n)], exact in fp32
+        uint32_t vt[4];
+        vt[0] = (__float_as_uint(ta4[0]) >> 16) | (__float_as_uint(ta4[1]) & 0xFFFF0000u);
+        vt[1] = (__float_as_uint(ta4[2]) >> 16) | (__float_as_uint(ta4[3]) & 0xFFFF0000u);
+        vt[2] = (__float_as_uint(tb4[0]) >> 16) | (__float_as_uint(tb4[1]) & 0xFFFF0000u);
+        vt[3] = (__float_as_uint(tb4[2]) >> 16) | (__float_as_uint(tb4[3]) & 0xFFFF0000u);
+        acc[c] *= alpha;
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uint4{vt[0], vt[1], vt[2], vt[3]}), pfrag, acc[c],
+                                                         0, 0, 0);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
                                                           const int64_t* __restrict__ q_pos,
                                                           const int32_t* __restrict__ lr_idx,
@@ -124,77 +211,32 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(const uint16_t* __rest
         const uint16_t* Kbg = K + bg * aa.t_cap * D;
         const uint16_t* Vbg = V + bg * aa.t_cap * D;
 
-        for (int64_t j = j0; j < j1; j += 32) {
-            const int64_t ja = j + r, jb = j + 16 + r;
-            int64_t ta = ja < j1 ? kl.at(ja) : -1, tb = jb < j1 ? kl.at(jb) : -1;
-            // a key outside [0, t] (malformed list) is never read and never scored
-            const bool va = ta >= 0 && ta <= t, vb = tb >= 0 && tb <= t;
-            ta = va ? ta : 0;
-            tb = vb ? tb : 0;
-            uint4 ka[KS], kb[KS], xa[KS], xb[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                ka[ks] = va ? *reinterpret_cast<const uint4*>(Kbg + ta * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
-                kb[ks] = vb ? *reinterpret_cast<const uint4*>(Kbg + tb * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
-                xa[ks] = va ? *reinterpret_cast<const uint4*>(Vbg + ta * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
-                xb[ks] = vb ? *reinterpret_cast<const uint4*>(Vbg + tb * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
-            }
-            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), as_bf16x8(qf[ks]), sa, 0, 0, 0);
-                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), as_bf16x8(qf[ks]), sb, 0, 0, 0);
-            }
-            // rows of sa: keys j + 4h + v; rows of sb: keys j + 16 + 4h + v
-            float pa[4], pb[4];
-            float mx = kNegInf;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t ra = j + 4 * h + v, rb = j + 16 + 4 * h + v;
-                const int64_t ua = ra < j1 ? kl.at(ra) : -1, ub = rb < j1 ? kl.at(rb) : -1;
-                pa[v] = (ua >= 0 && ua <= t) ? sa[v] * aa.scale : kNegInf;
-                pb[v] = (ub >= 0 && ub <= t) ? sb[v] * aa.scale : kNegInf;
-                mx = fmaxf(mx, fmaxf(pa[v], pb[v]));
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            if (m_new == kNegInf) continue;   // every key of this tile is masked
-            const float alpha = __expf(m_run - m_new);
-            m_run = m_new;
-            uint32_t pk[4];
-            float psum = 0.f;
-#pragma unroll
-            for (int v = 0; v < 4; v += 2) {
-                const uint16_t a0 = f32_to_bf16(__expf(pa[v] - m_new)), a1 = f32_to_bf16(__expf(pa[v + 1] - m_new));
-                const uint16_t b0 = f32_to_bf16(__expf(pb[v] - m_new)), b1 = f32_to_bf16(__expf(pb[v + 1] - m_new));
-                psum += bf16_to_f32(a0) + bf16_to_f32(a1) + bf16_to_f32(b0) + bf16_to_f32(b1);
-                pk[v / 2] = (uint32_t)a0 | ((uint32_t)a1 << 16);
-                pk[2 + v / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
-            }
-            l_run = l_run * alpha + psum;
-            const bf16x8 pfrag = as_bf16x8(uint4{pk[0], pk[1], pk[2], pk[3]});
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                // chunk c: lane (r, h) contributes V[key r][DPL h + 4c + 0..3]
-                const uint32_t* wa = reinterpret_cast<const uint32_t*>(&xa[c / 2]);
-                const uint32_t* wb = reinterpret_cast<const uint32_t*>(&xb[c / 2]);
-                const int o = (c & 1) * 2;
-                const s16x4 va4 = __builtin_bit_cast(s16x4, u32x2{wa[o], wa[o + 1]});
-                const s16x4 vb4 = __builtin_bit_cast(s16x4, u32x2{wb[o], wb[o + 1]});
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 ta4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, ident, z, 0, 0, 0);
-                const f32x4 tb4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb4, ident, z, 0, 0, 0);
-                // lane (n, h): V[key 4h+v][dim(c, n)] and V[key 16+4h+v][dim(c, n)], exact in fp32
-                uint32_t vt[4];
-                vt[0] = (__float_as_uint(ta4[0]) >> 16) | (__float_as_uint(ta4[1]) & 0xFFFF0000u);
-                vt[1] = (__float_as_uint(ta4[2]) >> 16) | (__float_as_uint(ta4[3]) & 0xFFFF0000u);
-                vt[2] = (__float_as_uint(tb4[0]) >> 16) | (__float_as_uint(tb4[1]) & 0xFFFF0000u);
-                vt[3] = (__float_as_uint(tb4[2]) >> 16) | (__float_as_uint(tb4[3]) & 0xFFFF0000u);
-                acc[c] *= alpha;
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(uint4{vt[0], vt[1], vt[2], vt[3]}), pfrag,
-                                                                 acc[c], 0, 0, 0);
-            }
+        // Software pipeline: the K/V rows of tile j + 32 are in flight while
+        // tile j is computed, and the indices of tile j + 64 one step earlier.
+        // A key outside [0, t] (malformed list) is never read nor scored.
+        // Two register sets ping-pong: while one tile of 32 keys is computed
+        // the K/V rows of the next one are in flight, and the indices of the
+        // tile after that are fetched one step earlier still.
+        int32_t a_ta = tok_of(kl, j0 + r, j1, t), a_tb = tok_of(kl, j0 + 16 + r, j1, t);
+        int32_t b_ta = tok_of(kl, j0 + 32 + r, j1, t), b_tb = tok_of(kl, j0 + 48 + r, j1, t);
+        uint4 a_ka[KS], a_kb[KS], a_xa[KS], a_xb[KS];
+        uint4 b_ka[KS], b_kb[KS], b_xa[KS], b_xb[KS];
+        load_rows<D>(Kbg, Vbg, a_ta, h, a_ka, a_xa);
+        load_rows<D>(Kbg, Vbg, a_tb, h, a_kb, a_xb);
+        for (int64_t j = j0; j < j1; j += 64) {
+            load_rows<D>(Kbg, Vbg, b_ta, h, b_ka, b_xa);
+            load_rows<D>(Kbg, Vbg, b_tb, h, b_kb, b_xb);
+            const int32_t fa = tok_of(kl, j + 64 + r, j1, t), fb = tok_of(kl, j + 80 + r, j1, t);
+            attend_tile<D>(a_ta, a_tb, a_ka, a_kb, a_xa, a_xb, qf, ident, h, aa.scale, m_run, l_run, acc);
+            if (j + 32 >= j1) break;
+            a_ta = fa;
+            a_tb = fb;
+            load_rows<D>(Kbg, Vbg, a_ta, h, a_ka, a_xa);
+            load_rows<D>(Kbg, Vbg, a_tb, h, a_kb, a_xb);
+            const int32_t ga = tok_of(kl, j + 96 + r, j1, t), gb = tok_of(kl, j + 112 + r, j1, t);
+            attend_tile<D>(b_ta, b_tb, b_ka, b_kb, b_xa, b_xb, qf, ident, h, aa.scale, m_run, l_run, acc);
+            b_ta = ga;
+            b_tb = gb;
         }
     }
     // acc[c][v] = unnormalised O[head n][DPL h + 4c + v]

@@ -274,17 +274,17 @@ __global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restric
 // One wave per tree node: sum of the two children (an odd last node has
 // one), its norm, and the rounded centroid (ch.4: node centroid = mean of
 // every key below it; the normalisation makes mean and sum equivalent).
-__global__ __launch_bounds__(256) void tree_level_kernel(CacheView cv, int lev, int64_t n_child, int64_t n_par) {
+__global__ __launch_bounds__(256) void tree_level_kernel(CacheView cv, int lev, int64_t n_child, int64_t n_par,
+                                                         int64_t child_off, int64_t par_off) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int64_t node = (int64_t)blockIdx.x * 4 + wid;
     if (node >= n_par) return;
     const int64_t bg = blockIdx.y;
-    const float* cs = lev == 1 ? cv.sums + bg * cv.s_sums
-                               : cv.tsums + bg * cv.s_tsums + cv.level_off[lev - 1] * kLatent;
+    const float* cs = lev == 1 ? cv.sums + bg * cv.s_sums : cv.tsums + bg * cv.s_tsums + child_off * kLatent;
     const int64_t c0 = 2 * node, c1 = c0 + 1;
     float s = cs[c0 * kLatent + lane];
     if (c1 < n_child) s += cs[c1 * kLatent + lane];
-    const int64_t o = (cv.level_off[lev] + node) * kLatent + lane;
+    const int64_t o = (par_off + node) * kLatent + lane;
     cv.tsums[bg * cv.s_tsums + o] = s;
     const float ss = wave_sum(s * s);
     const float v = ss > 0.f ? s * (1.0f / sqrtf(ss)) : 0.f;
@@ -312,11 +312,13 @@ hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t
     return hipSuccess;
 }
 
-hipError_t launch_tree(const CacheView& cv, int B, int H_kv, hipStream_t st) {
+hipError_t launch_tree(const CacheView& cv, const int64_t* level_off, const int64_t* level_size, int B, int H_kv,
+                       hipStream_t st) {
     for (int lev = 1; lev < cv.n_levels; ++lev) {
-        const int64_t n_child = cv.level_size[lev - 1], n_par = cv.level_size[lev];
+        const int64_t n_child = level_size[lev - 1], n_par = level_size[lev];
         dim3 grid((unsigned)((n_par + 3) / 4), (unsigned)(B * H_kv));
-        hipLaunchKernelGGL(tree_level_kernel, grid, dim3(256), 0, st, cv, lev, n_child, n_par);
+        hipLaunchKernelGGL(tree_level_kernel, grid, dim3(256), 0, st, cv, lev, n_child, n_par, level_off[lev - 1],
+                           level_off[lev]);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -39,11 +39,20 @@ struct CacheView {
     int64_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums;
     int32_t n_blocks;      // full blocks bucketed
     int32_t n_leaves;
-    int32_t n_levels;
+    int32_t n_levels;      // tree levels including the leaves
     int32_t bf16;          // centroid storage dtype
-    int64_t level_off[kMaxLevels];
-    int64_t level_size[kMaxLevels];
 };
+
+// Tree level l >= 1 holds ceil(n_leaves / 2^l) nodes (pairing (2j, 2j+1) level
+// by level); levels are stored one after the other from level 1.
+__device__ __forceinline__ int64_t tree_level_size(int64_t n_leaves, int lev) {
+    return (n_leaves + ((int64_t)1 << lev) - 1) >> lev;
+}
+__device__ __forceinline__ int64_t tree_level_off(int64_t n_leaves, int lev) {
+    int64_t off = 0;
+    for (int i = 1; i < lev; ++i) off += tree_level_size(n_leaves, i);
+    return off;
+}
 
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }

@@ -44,7 +44,8 @@ struct AttArgs {
 
 hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
                         const void* W, hipStream_t st);
-hipError_t launch_tree(const CacheView& cv, int B, int H_kv, hipStream_t st);
+hipError_t launch_tree(const CacheView& cv, const int64_t* level_off, const int64_t* level_size, int B, int H_kv,
+                       hipStream_t st);
 hipError_t launch_qlatent(const void* Q, const void* W, bool bf16, int d, int64_t rows, void* qhat, int* counters,
                           hipStream_t st);
 hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa, int B,

@@ -90,6 +90,62 @@ __global__ __launch_bounds__(256) void qlatent_kernel(const TIN* __restrict__ Q,
     }
 }
 
+// bf16: 16 query rows per MFMA tile, Q [16 x d] . W [d x 64] as 4 column
+// tiles; lane (r, h) feeds head dims [d/4 h, d/4 h + d/4) of row r, the W
+// fragments use the same dim order and stay in registers for the whole
+// (persistent) workgroup.  The C layout gives lane (n, h) rows 4h..4h+3 of
+// latent column n of each tile; row norms are reduced over the 16 lanes of
+// a row group.
+template <int D>
+__global__ __launch_bounds__(256) void qlatent_bf16_kernel(const uint16_t* __restrict__ Q,
+                                                           const uint16_t* __restrict__ W, int64_t rows,
+                                                           uint16_t* __restrict__ qhat, int* counters) {
+    constexpr int DPL = D / 4, KS = DPL / 8;
+    if (blockIdx.x == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0;
+    const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4;
+    bf16x8 wf[4][KS];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint16_t e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = W[(DPL * h + 8 * ks + j) * kLatent + 16 * nt + r];
+            wf[nt][ks] = as_bf16x8(uint4{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16),
+                                         (uint32_t)e[4] | ((uint32_t)e[5] << 16), (uint32_t)e[6] | ((uint32_t)e[7] << 16)});
+        }
+    const int64_t ntile = (rows + 15) / 16;
+    for (int64_t tile = (int64_t)blockIdx.x * 4 + wid; tile < ntile; tile += (int64_t)gridDim.x * 4) {
+        const int64_t row = tile * 16 + r;
+        uint4 qa[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qa[ks] = row < rows ? *reinterpret_cast<const uint4*>(Q + row * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
+        f32x4 c[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            c[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), wf[nt][ks], c[nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float ss = c[0][v] * c[0][v] + c[1][v] * c[1][v] + c[2][v] * c[2][v] + c[3][v] * c[3][v];
+            ss += __shfl_xor(ss, 1);
+            ss += __shfl_xor(ss, 2);
+            ss += __shfl_xor(ss, 4);
+            ss += __shfl_xor(ss, 8);
+            const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+            const int64_t orow = tile * 16 + 4 * h + v;
+            if (orow < rows) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) qhat[orow * kLatent + 16 * nt + r] = f32_to_bf16(c[nt][v] * inv);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ scoring tiles
 // Scores of the 16 buckets x0..x0+15 against 16 query slots, max over the
 // group's heads.  Output (MFMA C layout): lane l holds buckets
@@ -161,13 +217,57 @@ __device__ __forceinline__ f32x4 score_tile_f32(const float* cent_bg, int64_t x0
 // ------------------------------------------------------------------ fused flat scan
 // PASS 0: per-query bound tau; PASS 1: candidates with score >= tau.
 // grid (ceil(n_q / 64), H_kv, B), 4 waves, wave w owns queries 16w..16w+15
-// of the tile; every wave scans all buckets visible to any of its queries.
+// of the tile; every wave scans all buckets visible to any of its queries,
+// with the centroid fragments of the next 16 buckets in flight while the
+// current ones are scored.
+//
+// The bound: a histogram over 256 score bins of width 1/128 accumulates
+// token weights that are certainly eligible (4 x size for buckets of blocks
+// inside [sink_end, l0), else 0).  While a wave sees at most
+// kPerLeafMaxLeaves buckets every bucket is binned; beyond that only each
+// block's best bucket (its score truncated downwards, packed with its size).
+// The bin where the weight from the top reaches k gives tau = its lower edge
+// minus 2^-16 (absorbs fp32 rounding of the binning): at least k eligible
+// tokens lie in buckets scoring >= tau, so the k-th token's bucket does too.
+constexpr int kPerLeafMaxLeaves = 96 * kLeavesPerBlock;
+constexpr int kHistStride = 257;   // padded: neighbouring queries fall in different banks
+
+__device__ __forceinline__ void load_cent_bf16(const uint16_t* cent_bg, int64_t x0, uint4& a0, uint4& a1) {
+    const int l = lane_id(), r = l & 15, h = l >> 4;
+    const uint4* p = reinterpret_cast<const uint4*>(cent_bg + (x0 + r) * kLatent + 16 * h);
+    a0 = p[0];
+    a1 = p[1];
+}
+
+__device__ __forceinline__ f32x4 mfma_tile_bf16(uint4 u0, uint4 u1, const QFragBF16& qf, int G) {
+    const bf16x8 a0 = as_bf16x8(u0), a1 = as_bf16x8(u1);
+    f32x4 best = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+        if (hh < G) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf.f[hh][0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf.f[hh][1], acc, 0, 0, 0);
+            best[0] = fmaxf(best[0], acc[0]);
+            best[1] = fmaxf(best[1], acc[1]);
+            best[2] = fmaxf(best[2], acc[2]);
+            best[3] = fmaxf(best[3], acc[3]);
+        }
+    }
+    return best;
+}
+
+__device__ __forceinline__ int score_bin(float s) {
+    int bin = (int)floorf((s + 1.0f) * 128.0f);
+    return bin < 0 ? 0 : (bin > 255 ? 255 : bin);
+}
+
 template <bool BF16, int PASS>
 __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const void* __restrict__ qhat,
                                                          const int64_t* __restrict__ q_pos, SelArgs sa,
                                                          float* __restrict__ tau, int* __restrict__ cnt,
                                                          uint64_t* __restrict__ cand) {
-    __shared__ uint32_t hist[PASS == 0 ? 4 : 1][16][256];
+    __shared__ uint32_t hist[PASS == 0 ? 4 * 16 * kHistStride : 1];
     __shared__ int lcnt[4][16];
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
     const int64_t b = blockIdx.z, g = blockIdx.y;
@@ -180,14 +280,16 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
     const int64_t bg = b * sa.H_kv + g;
     const int maxNLv = wave_max_i(NLv), minNLv = wave_min_i(NLv);
     const int64_t qrow = ((b * sa.n_q + i) * sa.H_q + g * sa.G) * kLatent;
+    const bool perleaf = maxNLv <= kPerLeafMaxLeaves;   // wave-uniform
 
     QFragBF16 qf;
     if constexpr (BF16) load_qfrag_bf16(qf, reinterpret_cast<const uint16_t*>(qhat) + (qv ? qrow : 0), qv, sa.G);
     const float* qf32 = reinterpret_cast<const float*>(qhat) + (qv ? qrow : 0);
 
+    uint32_t* myhist = hist + (PASS == 0 ? (wid * 16 + n) * kHistStride : 0);
     float tau_n = 0.f;
     if constexpr (PASS == 0) {
-        for (int j = l; j < 16 * 256; j += 64) (&hist[wid][0][0])[j] = 0u;
+        for (int j = l; j < 16 * kHistStride; j += 64) hist[wid * 16 * kHistStride + j] = 0u;
     } else {
         if (l < 16) lcnt[wid][l] = 0;
         tau_n = qv ? tau[u] : 0.f;
@@ -198,49 +300,61 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
     const float* cb32 = reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent;
     const uint32_t* meta = cv.meta + bg * cv.s_meta;
 
-    for (int blk = 0; blk * kLeavesPerBlock < maxNLv; ++blk) {
-        uint32_t bmax = 0;
+    uint4 na0 = {0, 0, 0, 0}, na1 = {0, 0, 0, 0}, nm = {0, 0, 0, 0};
+    if (maxNLv > 0) {
+        if constexpr (BF16) load_cent_bf16(cb16, 0, na0, na1);
+        if constexpr (PASS == 0) nm = *reinterpret_cast<const uint4*>(meta + 4 * h);
+    }
+    uint32_t bmax = 0;
+    for (int64_t x0 = 0; x0 < maxNLv; x0 += 16) {
+        const uint4 a0 = na0, a1 = na1, m4 = nm;
+        if (x0 + 16 < maxNLv) {
+            if constexpr (BF16) load_cent_bf16(cb16, x0 + 16, na0, na1);
+            if constexpr (PASS == 0) nm = *reinterpret_cast<const uint4*>(meta + x0 + 16 + 4 * h);
+        }
+        f32x4 vals;
+        if constexpr (BF16)
+            vals = mfma_tile_bf16(a0, a1, qf, sa.G);
+        else
+            vals = score_tile_f32(cb32, x0, qf32, qv, sa.G);
+        const int64_t xb = x0 + 4 * h;
+        const bool edge = x0 + 16 > minNLv;
+        const int64_t lo = (x0 / kLeavesPerBlock) * (int64_t)kBlockTokens;
+        if constexpr (PASS == 0) {
+            const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w};
+            const bool elig = qv && lo >= q.sink_end && lo + kBlockTokens <= q.l0;
+            if (perleaf) {
+                if (elig) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int64_t x0 = (int64_t)blk * kLeavesPerBlock + 16 * tt;
-            f32x4 vals;
-            if constexpr (BF16)
-                vals = score_tile_bf16(cb16, x0, qf, sa.G);
-            else
-                vals = score_tile_f32(cb32, x0, qf32, qv, sa.G);
-            const int64_t xb = x0 + 4 * h;
-            const bool edge = x0 + 16 > minNLv;
-            if constexpr (PASS == 0) {
-                const uint4 m4 = *reinterpret_cast<const uint4*>(meta + xb);
-                const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w};
+                    for (int v = 0; v < 4; ++v)
+                        if (!edge || (xb + v < NLv))
+                            atomicAdd(&myhist[score_bin(vals[v])], (uint32_t)kPool * (mm[v] & 0xFFu));
+                }
+            } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const uint32_t key = (__float_as_uint(vals[v] + 2.0f) & ~0xFu) | ((mm[v] & 0xFFu) - 1u);
                     const bool ok = !edge || (xb + v < NLv);
                     bmax = (ok && key > bmax) ? key : bmax;
                 }
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const bool pred = (!edge || (xb + v < NLv)) && qv && vals[v] >= tau_n;
-                    if (pred) {
-                        const int pos = atomicAdd(&lcnt[wid][n], 1);
-                        if (pos < kCandCap) cand[u * kCandCap + pos] = rank_key(vals[v], (uint32_t)(xb + v));
-                    }
+                if (((x0 / 16) & 3) == 3) {   // end of a cluster block: bin its best bucket
+                    uint32_t o = __shfl_xor(bmax, 16);
+                    bmax = o > bmax ? o : bmax;
+                    o = __shfl_xor(bmax, 32);
+                    bmax = o > bmax ? o : bmax;
+                    if (h == 0 && elig && bmax != 0u)
+                        myhist[score_bin(__uint_as_float(bmax & ~0xFu) - 2.0f)] += (uint32_t)kPool * ((bmax & 0xFu) + 1u);
+                    bmax = 0;
                 }
             }
-        }
-        if constexpr (PASS == 0) {
-            uint32_t o = __shfl_xor(bmax, 16);
-            bmax = o > bmax ? o : bmax;
-            o = __shfl_xor(bmax, 32);
-            bmax = o > bmax ? o : bmax;
-            const int64_t lo = (int64_t)blk * kBlockTokens;
-            if (h == 0 && qv && bmax != 0u && lo >= q.sink_end && lo + kBlockTokens <= q.l0) {
-                const float s = __uint_as_float(bmax & ~0xFu) - 2.0f;
-                int bin = (int)floorf((s + 1.0f) * 128.0f);
-                bin = bin < 0 ? 0 : (bin > 255 ? 255 : bin);
-                hist[wid][n][bin] += (uint32_t)kPool * ((bmax & 0xFu) + 1u);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bool pred = (!edge || (xb + v < NLv)) && qv && vals[v] >= tau_n;
+                if (pred) {
+                    const int pos = atomicAdd(&lcnt[wid][n], 1);
+                    if (pos < kCandCap) cand[u * kCandCap + pos] = rank_key(vals[v], (uint32_t)(xb + v));
+                }
             }
         }
     }
@@ -250,9 +364,9 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
             uint32_t cum = 0;
             float tv = kNegInf;
             for (int bin = 255; bin >= 1; --bin) {
-                cum += hist[wid][n][bin];
+                cum += myhist[bin];
                 if (cum >= (uint32_t)sa.k) {
-                    tv = (float)bin * (1.0f / 128.0f) - 1.0f;
+                    tv = (float)bin * (1.0f / 128.0f) - 1.0f - 1.52587890625e-05f;
                     break;
                 }
             }
@@ -265,7 +379,7 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
 
 // ------------------------------------------------------------------ wave-level finish
 // Bitonic sort of P (power of two) 64-bit keys in LDS, descending.
-__device__ void wave_sort_desc(uint64_t* a, int P) {
+__device__ __forceinline__ void wave_sort_desc(uint64_t* a, int P) {
     const int l = lane_id();
     for (int size = 2; size <= P; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -289,87 +403,204 @@ __device__ __forceinline__ int pow2_at_least(int n) {
     return p;
 }
 
-// Writes the tokens of the selected buckets in ascending order.  sel[] holds
-// (leaf << 16 | take) sorted by leaf; take = kFullTake or, for the single
-// boundary bucket, the count of its lowest eligible tokens.  tk[] is a
-// 64-entry scratch.  Returns the number of tokens written.
-__device__ int wave_expand(const uint64_t* sel, int nsel, const CacheView& cv, int64_t bg, const Geom& q,
-                           int32_t* out, int* tk) {
-    const int l = lane_id();
-    int count = 0;
-    int i = 0;
-    while (i < nsel) {
-        const uint32_t blk = (uint32_t)(sel[i] >> 16) / kLeavesPerBlock;
-        int j = i;
-        while (true) {
-            const int idx = j + l;
-            const bool same = idx < nsel && (uint32_t)(sel[idx] >> 16) / kLeavesPerBlock == blk;
-            const uint64_t bal = __ballot(same);
-            const int run = __popcll(bal);
-            j += run;
-            if (run < 64) break;
-        }
-        tk[l] = 0;
-        wave_sync();
-        for (int idx = i + l; idx < j; idx += 64) {
-            const uint64_t s = sel[idx];
-            tk[(uint32_t)(s >> 16) % kLeavesPerBlock] = (int)(s & 0xFFFF);
-        }
-        wave_sync();
-        const int my = tk[l];
-        const bool is_part = my != 0 && my != kFullTake;
-        const uint64_t pb = __ballot(is_part);
-        const int prank = pb ? __builtin_ctzll(pb) : -1;
-        const int quota = pb ? __shfl(my, prank) : 0;
+// A selected bucket: leaf id in bits 32..63, its member list (offset in the
+// block's member array in bits 15..24, entry count in bits 25..29), its
+// eligible tokens w in bits 8..14, bit 7 set when all of them are taken,
+// else bits 0..6 = how many of its lowest eligible tokens are taken (only
+// the boundary bucket).  Sorting the records ascending sorts them by leaf.
+__device__ __forceinline__ uint64_t pack_sel(uint32_t leaf, uint32_t meta, int w, bool full, int take) {
+    const uint64_t off = (meta >> 8) & 0x3FF, sz = meta & 0x1F;
+    return ((uint64_t)leaf << 32) | (sz << 25) | (off << 15) | ((uint64_t)(w & 0x7F) << 8) |
+           (full ? 0x80ull : (uint64_t)(take & 0x7F));
+}
+__device__ __forceinline__ int sel_off(uint64_t s) { return (int)((s >> 15) & 0x3FF); }
+__device__ __forceinline__ int sel_size(uint64_t s) { return (int)((s >> 25) & 0x1F); }
 
-        const uint64_t rk8 = *reinterpret_cast<const uint64_t*>(cv.eleaf + bg * cv.s_eleaf +
-                                                               (int64_t)blk * kBlockEntries + 8 * l);
-        const int64_t T0 = (int64_t)blk * kBlockTokens + 32 * l;
-        uint32_t emit = 0;   // bit (4e + jj) set when token T0 + 4e + jj is emitted
-        uint32_t part = 0;   // eligible tokens of the boundary bucket
-        int npart = 0;
+// The member entries of one bucket (<= 16, ascending) as 16-bit values in
+// registers: the aligned 48-byte window holding them is read with three
+// 16-byte loads.
+__device__ __forceinline__ void load_members(const uint16_t* blk_members, int off, uint16_t (&e)[16]) {
+    const int a = off & ~7;
+    const uint4* p = reinterpret_cast<const uint4*>(blk_members + a);
+    const uint4 w0 = p[0], w1 = p[1], w2 = (a + 16 < kBlockEntries) ? p[2] : uint4{0, 0, 0, 0};
+    const uint32_t w[12] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x, w2.y, w2.z, w2.w};
+    const int sh = off - a;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int rk = (int)((rk8 >> (8 * e)) & 0x3F);
-            const int take = tk[rk];
+    for (int j = 0; j < 16; ++j) {
+        const int k = j + sh;   // 0..22
+        uint32_t v = 0;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int64_t tok = T0 + 4 * e + jj;
-                const bool el = tok >= q.sink_end && tok < q.l0;
-                if (!el || take == 0) continue;
-                if (take == kFullTake) {
-                    emit |= 1u << (4 * e + jj);
-                } else {
-                    part |= 1u << (4 * e + jj);
-                    ++npart;
-                }
-            }
-        }
-        if (prank >= 0) {
-            const int pre = wave_incl_scan(npart) - npart;
-            int seen = pre;
-            for (int bit = 0; bit < 32; ++bit) {
-                if (part & (1u << bit)) {
-                    if (seen < quota) emit |= 1u << bit;
-                    ++seen;
-                }
-            }
-        }
-        const int ne = __popc(emit);
-        const int base = wave_incl_scan(ne) - ne;
-        int w = count + base;
-        for (int bit = 0; bit < 32; ++bit)
-            if (emit & (1u << bit)) out[w++] = (int32_t)(T0 + bit);
-        count += __shfl(base + ne, 63);
-        wave_sync();
-        i = j;
+        for (int kk = 0; kk < 24; ++kk)
+            if (kk == k) v = (w[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu;
+        e[j] = (uint16_t)v;
     }
-    return count;
+}
+__device__ __forceinline__ uint32_t sel_leaf(uint64_t s) { return (uint32_t)(s >> 32); }
+__device__ __forceinline__ bool sel_full(uint64_t s) { return (s & 0x80ull) != 0; }
+__device__ __forceinline__ int sel_count(uint64_t s) { return sel_full(s) ? (int)((s >> 8) & 0x7F) : (int)(s & 0x7F); }
+__device__ __forceinline__ uint32_t sel_block(uint64_t s) { return sel_leaf(s) / kLeavesPerBlock; }
+
+// Token-level expansion of one block (used when the block straddles the
+// sink or window edge, or holds the partially taken boundary bucket): lane l
+// owns entries l + 64 k (k = 0..7); for each k the 256 tokens are ordered by
+// (lane, token in entry), so output positions follow from ballots and
+// lane-prefix bit counts.  Writes the block's tokens ascending from out[0].
+__device__ __forceinline__ void expand_block_scan(uint32_t blk, const uint64_t* sel, int a, int b, const CacheView& cv,
+                                                  int64_t bg, const Geom& q, int32_t* out, int* tk) {
+    const int l = lane_id();
+    const uint64_t lt = (1ull << l) - 1ull;
+    tk[l] = 0;
+    wave_sync();
+    for (int idx = a + l; idx < b; idx += 64) {
+        const uint64_t sv = sel[idx];
+        tk[sel_leaf(sv) % kLeavesPerBlock] = sel_full(sv) ? kFullTake : (int)(sv & 0x7F);
+    }
+    wave_sync();
+    const int my = tk[l];
+    const uint64_t pb = __ballot(my != 0 && my != kFullTake);
+    const int quota = pb ? __shfl(my, __builtin_ctzll(pb)) : 0;
+    const uint8_t* row = cv.eleaf + bg * cv.s_eleaf + (int64_t)blk * kBlockEntries + l;
+    uint32_t rk[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rk[k] = row[64 * k];
+    const int64_t B0 = (int64_t)blk * kBlockTokens;
+    int pseen = 0, count = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int take = tk[rk[k] & 0x3F];
+        const int64_t t0 = B0 + (int64_t)kPool * (l + 64 * k);
+        bool full[4], part[4], emit[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int64_t tok = t0 + jj;
+            const bool el = take != 0 && tok >= q.sink_end && tok < q.l0;
+            full[jj] = el && take == kFullTake;
+            part[jj] = el && take != kFullTake;
+        }
+        int before = pseen, mine = 0;
+        uint64_t bp[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            bp[jj] = __ballot(part[jj]);
+            before += __popcll(bp[jj] & lt);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            emit[jj] = full[jj] || (part[jj] && before + mine < quota);
+            mine += part[jj] ? 1 : 0;
+            pseen += __popcll(bp[jj]);
+        }
+        uint64_t be[4];
+        int pos = count;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            be[jj] = __ballot(emit[jj]);
+            pos += __popcll(be[jj] & lt);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            if (emit[jj]) out[pos++] = (int32_t)(t0 + jj);
+            count += __popcll(be[jj]);
+        }
+    }
+    wave_sync();
+}
+
+// Writes the tokens of the selected buckets (sel[0..nsel), sorted by leaf id)
+// in ascending order and returns their number.  Each record's output offset
+// is the prefix of the records' token counts (records of one block are
+// contiguous, and a block's tokens precede the next block's).  In a block
+// lying inside [sink_end, l0) whose buckets are all fully taken, every
+// member entry contributes its 4 tokens at 4 x (its rank among the block's
+// selected entries); member lists are stored ascending, so a lone bucket's
+// rank is the member's position.  Other blocks use expand_block_scan.
+// base[] and spec[] are LDS scratch of at least nsel and 64 ints.
+__device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const CacheView& cv, int64_t bg,
+                                           const Geom& q, int32_t* out, int* tk, int* base, int* spec) {
+    const int l = lane_id();
+    int run = 0;
+    for (int c0 = 0; c0 < nsel; c0 += 64) {
+        const int i = c0 + l;
+        const int ci = i < nsel ? sel_count(sel[i]) : 0;
+        const int inc = wave_incl_scan(ci);
+        if (i < nsel) base[i] = run + inc - ci;
+        run += __shfl(inc, 63);
+    }
+    if (l == 0) spec[0] = 0;
+    wave_sync();
+    const uint16_t* mem_bg = cv.members + bg * cv.s_members;
+    for (int c0 = 0; c0 < nsel; c0 += 64) {
+        const int i = c0 + l;
+        if (i >= nsel) continue;
+        const uint64_t sv = sel[i];
+        const uint32_t blk = sel_block(sv);
+        int f = i, g = i;
+        while (f > 0 && sel_block(sel[f - 1]) == blk) --f;
+        while (g + 1 < nsel && sel_block(sel[g + 1]) == blk) ++g;
+        const int64_t lo = (int64_t)blk * kBlockTokens;
+        bool special = !(lo >= q.sink_end && lo + kBlockTokens <= q.l0);
+        for (int x = f; x <= g && !special; ++x) special = !sel_full(sel[x]);
+        if (special) {
+            if (i == f) {
+                const int slot = atomicAdd(&spec[0], 1);
+                if (slot < 63) spec[1 + slot] = i;
+            }
+            continue;
+        }
+        const int sz = sel_size(sv);
+        const uint16_t* blk_mem = mem_bg + (int64_t)blk * kBlockEntries;
+        uint16_t e[16];
+        load_members(blk_mem, sel_off(sv), e);
+        int rank[16];
+#pragma unroll
+        for (int jm = 0; jm < 16; ++jm) rank[jm] = jm;
+        for (int x = f; x <= g; ++x) {   // other selected buckets of this block (usually none)
+            if (x == i) continue;
+            const uint64_t sx = sel[x];
+            uint16_t ex[16];
+            load_members(blk_mem, sel_off(sx), ex);
+            const int szx = sel_size(sx);
+#pragma unroll
+            for (int y = 0; y < 16; ++y)
+#pragma unroll
+                for (int jm = 0; jm < 16; ++jm) rank[jm] += (y < szx && ex[y] < e[jm]) ? 1 : 0;
+        }
+        int32_t* o = out + base[f];
+#pragma unroll
+        for (int jm = 0; jm < 16; ++jm) {
+            if (jm < sz) {
+                const int32_t t0 = (int32_t)(lo + (int64_t)kPool * e[jm]);
+                int32_t* d = o + kPool * rank[jm];
+                d[0] = t0;
+                d[1] = t0 + 1;
+                d[2] = t0 + 2;
+                d[3] = t0 + 3;
+            }
+        }
+    }
+    wave_sync();
+    const int nspec = spec[0] < 63 ? spec[0] : 63;
+    for (int sidx = 0; sidx < nspec; ++sidx) {
+        const int f = spec[1 + sidx];
+        const uint32_t blk = sel_block(sel[f]);
+        int g = f;
+        while (true) {
+            const int idx = g + l;
+            const bool same = idx < nsel && sel_block(sel[idx]) == blk;
+            const int r = __popcll(__ballot(same));
+            g += r;
+            if (r < 64) break;
+        }
+        expand_block_scan(blk, sel, f, g, cv, bg, q, out + base[f], tk);
+    }
+    wave_sync();
+    return run;
 }
 
 // Walk keys[0..n) (sorted by rank), pick the buckets until k eligible
 // tokens, sort the picks by id into sel[] and expand.  Returns the count.
-__device__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, const CacheView& cv, int64_t bg,
+__device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, const CacheView& cv,
+                                                int64_t bg,
                                 const Geom& q, int k, int32_t* out) {
     const int l = lane_id();
     int have = 0, nsel = 0;
@@ -379,13 +610,13 @@ __device__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, c
         const bool in = r < n && keys[r] != 0ull;
         const uint32_t leaf = in ? rank_key_id(keys[r]) : 0u;
         const int w = in ? leaf_weight(cv, bg, leaf, q) : 0;
+        const uint32_t lmeta = in ? cv.meta[bg * cv.s_meta + leaf] : 0u;
         const int cum = wave_incl_scan(w) + have;
         const int before = cum - w;
         const bool take = w > 0 && before < k;
-        const int tk_n = take ? ((cum <= k) ? kFullTake : (k - before)) : 0;
         const uint64_t bal = __ballot(take);
         const int pos = __popcll(bal & ((1ull << l) - 1ull));
-        if (take) sel[nsel + pos] = ((uint64_t)leaf << 16) | (uint64_t)tk_n;
+        if (take) sel[nsel + pos] = pack_sel(leaf, lmeta, w, cum <= k, k - before);
         nsel += __popcll(bal);
         have = __shfl(cum, 63);
         if (have >= k) done = true;
@@ -400,16 +631,18 @@ __device__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, c
     wave_sort_desc(sel, P);
     for (int j = l; j < P; j += 64) sel[j] = ~sel[j];
     wave_sync();
-    return wave_expand(sel, nsel, cv, bg, q, out, tk);
+    // the rank keys are no longer needed: reuse them as the offset scratch
+    int* base = reinterpret_cast<int*>(keys);
+    return wave_expand(sel, nsel, cv, bg, q, out, tk, base, tk + 64);
 }
 
-__device__ void write_pad(int32_t* out, int from, int k) {
+__device__ __forceinline__ void write_pad(int32_t* out, int from, int k) {
     for (int j = from + lane_id(); j < k; j += 64) out[j] = -1;
 }
 
 // Handles the cases that need no ranking: invalid position (count -1), and
 // a budget covering every eligible token (the whole range [sink_end, l0)).
-__device__ bool trivial_unit(int64_t t, const Geom& q, int k, int32_t* out, int32_t* cnt_out) {
+__device__ __forceinline__ bool trivial_unit(int64_t t, const Geom& q, int k, int32_t* out, int32_t* cnt_out) {
     const int l = lane_id();
     if (t < 0) {
         write_pad(out, 0, k);
@@ -437,7 +670,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
                                                              int* counters, int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ uint64_t keys[4][kCandCap];
     __shared__ uint64_t sel[4][kCandCap];
-    __shared__ int tk[4][64];
+    __shared__ int tk[4][128];
     const int l = lane_id(), wid = threadIdx.x >> 6;
     const int64_t u = (int64_t)blockIdx.x * 4 + wid;
     if (u >= sa.n_units) return;
@@ -527,7 +760,8 @@ __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const v
                                                            int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ uint32_t hist[256];
     __shared__ uint64_t sel[kExactSel];
-    __shared__ int tk[64];
+    __shared__ int ebase[kExactSel];
+    __shared__ int tk[128];
     __shared__ int sh4[4];
     __shared__ uint32_t bc[4];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
@@ -612,19 +846,19 @@ __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const v
             const bool gt = w > 0 && key > kstar, eq = w > 0 && key == kstar;
             int eq_tot;
             const int eb = wg_excl_scan(eq ? w : 0, sh4, eq_tot) + eq_have;
-            int tkn = 0;
-            if (gt) tkn = kFullTake;
-            if (eq && eb < (int)target) tkn = (eb + w <= (int)target) ? kFullTake : ((int)target - eb);
+            const bool take_all = gt || (eq && eb + w <= (int)target);
+            const bool take_part = !take_all && eq && eb < (int)target;
             int s_tot;
-            const int pos = wg_excl_scan(tkn != 0 ? 1 : 0, sh4, s_tot);
-            if (tkn != 0 && nsel + pos < kExactSel) sel[nsel + pos] = ((uint64_t)x << 16) | (uint64_t)tkn;
+            const int pos = wg_excl_scan((take_all || take_part) ? 1 : 0, sh4, s_tot);
+            if ((take_all || take_part) && nsel + pos < kExactSel)
+                sel[nsel + pos] = pack_sel((uint32_t)x, cv.meta[bg * cv.s_meta + x], w, take_all, (int)target - eb);
             nsel += s_tot;
             eq_have += eq_tot;
         }
         __syncthreads();
         if (wid == 0) {
             const int ns = nsel < kExactSel ? nsel : kExactSel;
-            const int got = wave_expand(sel, ns, cv, bg, q, out, tk);
+            const int got = wave_expand(sel, ns, cv, bg, q, out, tk, ebase, tk + 64);
             write_pad(out, got, sa.k);
             if (l == 0) lr_cnt[u] = got;
         }
@@ -643,7 +877,7 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
     __shared__ uint64_t keys[4][2 * LSA_MAX_BEAM];
     __shared__ uint32_t front[4][LSA_MAX_BEAM];
     __shared__ uint64_t sel[4][2 * LSA_MAX_BEAM];
-    __shared__ int tk[4][64];
+    __shared__ int tk[4][128];
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
     const int64_t u = (int64_t)blockIdx.x * 4 + wid;
     if (u >= sa.n_units) return;
@@ -680,7 +914,8 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
     }
     wave_sync();
     for (int lev = top - 1; lev >= 0; --lev) {
-        const int64_t n_lev = cv.level_size[lev];
+        const int64_t n_lev = tree_level_size(cv.n_leaves, lev);
+        const int64_t lev_off = tree_level_off(cv.n_leaves, lev);
         const int64_t span = (int64_t)1 << lev;
         const int ncand = 2 * nf;
         const int ntiles = (ncand + 15) / 16;
@@ -698,7 +933,7 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
                     const uint16_t* base =
                         lev == 0 ? reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent + node * kLatent
                                  : reinterpret_cast<const uint16_t*>(cv.tcent) + bg * cv.s_tcent +
-                                       (cv.level_off[lev] + node) * kLatent;
+                                       (lev_off + node) * kLatent;
                     const uint4* p = reinterpret_cast<const uint4*>(base + 16 * h);
                     b0 = p[0];
                     b1 = p[1];
@@ -714,7 +949,7 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
                     const float* base = lev == 0 ? reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent +
                                                        node * kLatent
                                                  : reinterpret_cast<const float*>(cv.tcent) + bg * cv.s_tcent +
-                                                       (cv.level_off[lev] + node) * kLatent;
+                                                       (lev_off + node) * kLatent;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int hh = 4 * h + v;
@@ -755,10 +990,16 @@ hipError_t launch_qlatent(const void* Q, const void* W, bool bf16, int d, int64_
                           hipStream_t st) {
     int64_t need = (rows + 15) / 16;
     unsigned grid = (unsigned)(need < 2048 ? (need > 0 ? need : 1) : 2048);
-    if (bf16)
-        hipLaunchKernelGGL(qlatent_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
-                           static_cast<const uint16_t*>(W), d, rows, qhat, 1, counters);
-    else
+    if (bf16) {
+        const int64_t tiles = (rows + 15) / 16;
+        const unsigned g2 = (unsigned)((tiles + 3) / 4 < 1024 ? ((tiles + 3) / 4 > 0 ? (tiles + 3) / 4 : 1) : 1024);
+        if (d == 128)
+            hipLaunchKernelGGL(qlatent_bf16_kernel<128>, dim3(g2), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
+                               static_cast<const uint16_t*>(W), rows, static_cast<uint16_t*>(qhat), counters);
+        else
+            hipLaunchKernelGGL(qlatent_bf16_kernel<64>, dim3(g2), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
+                               static_cast<const uint16_t*>(W), rows, static_cast<uint16_t*>(qhat), counters);
+    } else
         hipLaunchKernelGGL(qlatent_kernel<float>, dim3(grid), dim3(256), 0, st, static_cast<const float*>(Q),
                            static_cast<const float*>(W), d, rows, qhat, 0, counters);
     return hipGetLastError();
