@@ -288,6 +288,8 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=[2, 4, 5])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run one plain 1 GiB device copy (a known-size kernel for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the LSA path here has no multi-GPU sharding); got --gpus {args.gpus}",
@@ -296,6 +298,13 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)            # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     res, cfg, inp = run_prefill(args, args.config)
     log(f"prefill {res['value']:.0f} tokens/s, {res['ms_per_step']:.1f} ms/step")
     del inp
