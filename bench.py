@@ -128,7 +128,8 @@ def cpu_baseline(cfg, inp_cpu, budget_s=25.0):
     clusters = O.ward_blocks(blocks, processes=procs)
     t_ward = time.perf_counter() - t0
     per_block = t_ward * procs / nb                      # single-core seconds per block
-    cache = O.build_head_cache(K[0], W, cfg.dtype, T=nb * 2048, clusters=clusters)
+    tree = cfg.search == "tree"
+    cache = O.build_head_cache(K[0], W, cfg.dtype, T=nb * 2048, clusters=clusters, tree=tree)
     Q = inp_cpu["Q"][0]
     Kg, Vg = K[0], inp_cpu["V"][0, 0, : nb * 2048].double().numpy()
     rng = np.random.default_rng(0)
@@ -137,18 +138,25 @@ def cpu_baseline(cfg, inp_cpu, budget_s=25.0):
     t0 = time.perf_counter()
     for t in ts:
         qg = Q[int(t), : cfg.G].double().numpy()
-        lr, _ = O.select_flat(O.query_latent(qg, W, cfg.dtype), cache, int(t), cfg.k, cfg.n_sinks, cfg.window)
+        qh = O.query_latent(qg, W, cfg.dtype)
+        if tree:
+            lr, _ = O.select_tree(qh, cache, int(t), cfg.k, cfg.n_sinks, cfg.window, cfg.beam)
+        else:
+            lr, _ = O.select_flat(qh, cache, int(t), cfg.k, cfg.n_sinks, cfg.window)
         O.attend(qg, Kg, Vg, int(t), lr, cfg.n_sinks, cfg.window, cache["n_blocks"], scale)
     per_unit = (time.perf_counter() - t0) / len(ts)      # at (nb-1)*64 visible buckets
-    # projection: selection cost grows with the visible buckets, the rest is per unit
+    # projection: flat selection cost grows with the visible buckets, tree
+    # selection with the depth; the rest is per unit
     leaves_sample = (nb - 1) * 64
     mean_leaves = 64 * (cfg.T // 2048 - 1) / 2
+    if tree:
+        leaves_sample, mean_leaves = math.log2(max(2, leaves_sample)), math.log2(max(2, mean_leaves))
     full_s = (cfg.T // 2048) * cfg.H_kv * per_block + cfg.T * cfg.H_kv * per_unit * max(1.0, mean_leaves / leaves_sample)
     full_s /= procs
     return dict(value=cfg.T / full_s, unit="tokens/s", cores=procs, kind="oracle",
                 sample=(f"the same topic-mixture recipe generated on the CPU at T={nb * 2048}: oracle Ward on its {nb} "
                         f"blocks of KV head 0 ({t_ward:.1f}s wall on {procs} processes) and "
-                        f"select+attend for {len(ts)} (query, KV head) units at {leaves_sample} visible buckets "
+                        f"select+attend for {len(ts)} (query, KV head) units at {(nb - 1) * 64} visible buckets "
                         f"({per_unit * len(ts):.1f}s, 1 process); full 1-layer time projected as "
                         f"blocks*H_kv*t_block + T*H_kv*t_unit*(mean visible buckets / sampled), divided by "
                         f"{procs} processes"))
@@ -174,7 +182,13 @@ def run_prefill(args, cid):
     cfg = get_config(cid)
     dev = torch.device("cuda:0")
     log(f"generating {cfg.name} on the GPU")
-    inp = layer_inputs(cfg, seed=0, device=dev)
+    # one spare K/V row at position T serves the decode step on the same cache
+    inp = layer_inputs(cfg, seed=0, device=dev, T_cap=cfg.T + 1)
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+    kn = torch.randn(cfg.B, cfg.H_kv, cfg.d, generator=g, device=dev)
+    inp["K"][:, :, cfg.T] = (kn / kn.norm(dim=-1, keepdim=True)).to(inp["K"].dtype)
+    inp["V"][:, :, cfg.T] = torch.randn(cfg.B, cfg.H_kv, cfg.d, generator=g, device=dev).to(inp["V"].dtype)
     G = {k: inp[k].contiguous() for k in ("K", "V", "W", "Q", "q_pos")}
     torch.cuda.synchronize()
     n_q = G["Q"].shape[1]
@@ -217,7 +231,7 @@ def run_prefill(args, cid):
     traffic = traffic_for(os.path.join(ROOT, "sparse_attention_indexing_latent_amd", "csrc", "lsa_attend.hip"),
                           f"attend_{cfg.name}")
     res = dict(
-        metric="1-layer LSA prefill tokens/s at 1M ctx (1 GPU)" if cid == 4 else f"1-layer LSA prefill tokens/s ({cfg.name})",
+        metric="1-layer LSA prefill tokens/s at 1M & 10M ctx; decode queries/s at 1M (1 GPU)",
         value=cfg.T / (ms_step / 1e3), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=ms_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
         data="synthetic (seeded topic-mixture keys, random-init projection)",
@@ -231,7 +245,44 @@ def run_prefill(args, cid):
                   "traffic": traffic, "alg_bytes_per_launch": per_launch,
                   "avg_launch_ms": att_ms / n_att, "launches_per_step": n_att},
     )
+    if cfg.decode_batch:
+        res["decode_shared"] = decode_on_cache(cfg, G, inp, ws["cache"], tree)
     return res, cfg, inp
+
+
+def decode_on_cache(cfg, G, inp, cache_buf, tree):
+    """decode_batch queries at position T on the layer's own cache (the new
+    token's K/V sits in row T)."""
+    from synth.topics import make_queries
+    dev = G["K"].device
+    nq = cfg.decode_batch
+    qp = torch.full((1, nq), cfg.T, dtype=torch.int64)
+    Q = make_queries(cfg, 7, inp["mu"], inp["topic"], qp, dev).contiguous()
+    qp = qp.to(dev)
+    layout = lsa.make_layout(cfg.d, cfg.H_kv, cfg.H_q, G["K"].dtype, tree)
+    cache = lsa.LsaCache(cache_buf, layout, 1, cfg.T, cfg.T)
+    lr = torch.empty(1, nq, cfg.H_kv, cfg.k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, nq, cfg.H_kv, dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    search = "tree" if tree else "flat"
+
+    def step():
+        lsa.select(Q, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window, search=search, beam=cfg.beam, out=(lr, cnt))
+        lsa.sparse_attend(Q, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    n = 20
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / n
+    return dict(queries_per_s=nq / (ms / 1e3), ms_per_step=ms, batch=nq, search=search, beam=cfg.beam,
+                mean_lr=float(cnt.float().mean()))
 
 
 def run_decode(args):
