@@ -250,6 +250,21 @@ def run_prefill(args, cid):
     return res, cfg, inp
 
 
+def kv_rows(K, T):
+    """Flat row index of position T for every (sequence, KV head) of K [B, H_kv, t_cap, d]."""
+    B, H, t_cap, _ = K.shape
+    return torch.arange(B * H, device=K.device) * t_cap + T
+
+
+def append_kv(G, rows, newK, newV):
+    """Write one new token's key/value rows: one index_copy_ per tensor (a
+    slice assignment into a >2^31-element tensor splits into one copy per
+    sequence)."""
+    d = G["K"].shape[-1]
+    G["K"].view(-1, d).index_copy_(0, rows, newK.reshape(-1, d))
+    G["V"].view(-1, d).index_copy_(0, rows, newV.reshape(-1, d))
+
+
 def decode_on_cache(cfg, G, inp, cache_buf, tree):
     """decode_batch queries at position T on the layer's own cache (the new
     token's K/V sits in row T)."""
@@ -265,8 +280,12 @@ def decode_on_cache(cfg, G, inp, cache_buf, tree):
     cnt = torch.empty(1, nq, cfg.H_kv, dtype=torch.int32, device=dev)
     O = torch.empty_like(Q)
     search = "tree" if tree else "flat"
+    newK = G["K"][:, :, cfg.T].clone()
+    newV = G["V"][:, :, cfg.T].clone()
+    rows = kv_rows(G["K"], cfg.T)
 
     def step():
+        append_kv(G, rows, newK, newV)
         lsa.select(Q, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window, search=search, beam=cfg.beam, out=(lr, cnt))
         lsa.sparse_attend(Q, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O)
 
@@ -294,6 +313,7 @@ def run_decode(args):
     cache = lsa.build_buckets(G["K"], G["W"], T=cfg.T, n_q_heads=cfg.H_q)
     newK = G["K"][:, :, cfg.T].clone()
     newV = G["V"][:, :, cfg.T].clone()
+    rows = kv_rows(G["K"], cfg.T)
     ws = lsa.select_workspace_bytes(cache, lsa.select_cfg(cfg.k, cfg.n_sinks, cfg.window), 1, cfg.H_q)
     wsel = torch.empty(ws, dtype=torch.uint8, device=dev)
     lr = torch.empty(cfg.B, 1, cfg.H_kv, cfg.k, dtype=torch.int32, device=dev)
@@ -301,8 +321,7 @@ def run_decode(args):
     O = torch.empty_like(G["Q"])
 
     def step():
-        G["K"][:, :, cfg.T] = newK          # append the new token's key/value
-        G["V"][:, :, cfg.T] = newV
+        append_kv(G, rows, newK, newV)      # append the new token's key/value at row T
         lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window, workspace=wsel,
                    out=(lr, cnt))
         lsa.sparse_attend(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O)

@@ -154,7 +154,7 @@ lsa_status check_cfg(const lsa_select_cfg* C, int64_t T) {
 }
 
 struct SelectWs {
-    size_t off_qhat, off_tau, off_cnt, off_counters, off_cand, off_fb, off_scores, total;
+    size_t off_qhat, off_tau, off_cnt, off_counters, off_cand, off_fb, off_scores, off_packed, total;
     int64_t score_stride;
     int fb_slots;
     int strategy;
@@ -186,7 +186,11 @@ void select_ws(const lsa_layout* L, const lsa_select_cfg* C, int64_t B, int64_t 
         w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
         w.off_scores = o; o = align256(o + (size_t)w.fb_slots * w.score_stride * 4);
     } else if (w.strategy == LSA_STRATEGY_MATERIALIZED) {
+        w.off_cand = o; o = align256(o + (size_t)units * lsa::kCandCap * 8);
+        w.off_fb = o;   o = align256(o + (size_t)units * 4);
+        w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
         w.off_scores = o; o = align256(o + (size_t)units * w.score_stride * 4);
+        w.off_packed = o; o = align256(o + (size_t)units * w.score_stride * 4);
     }
     w.total = o;
 }
@@ -339,6 +343,7 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     sb.cand = reinterpret_cast<uint64_t*>(wb + w.off_cand);
     sb.fb_list = reinterpret_cast<int*>(wb + w.off_fb);
     sb.scores = reinterpret_cast<float*>(wb + w.off_scores);
+    sb.packed = reinterpret_cast<uint32_t*>(wb + w.off_packed);
     sb.score_stride = w.score_stride;
     sb.fb_slots = w.fb_slots;
     lsa::SelArgs sa;

@@ -376,19 +376,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (w_id >= aa.n_units * aa.G) return;
     const int64_t u = w_id / aa.G;
     const int hh = (int)(w_id % aa.G);
-    float m = kNegInf;
-    for (int s = 0; s < aa.splits; ++s) m = fmaxf(m, part[((u * aa.splits + s) * aa.G + hh) * (D + 2)]);
-    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    if (m > kNegInf) {
-        for (int s = 0; s < aa.splits; ++s) {
-            const float* pp = part + ((u * aa.splits + s) * aa.G + hh) * (D + 2);
-            const float ms = pp[0];
-            if (!(ms > kNegInf)) continue;
-            const float e = __expf(ms - m);
-            lsum += pp[1] * e;
-            if (l < D) o0 += pp[2 + l] * e;
-            if (l + 64 < D) o1 += pp[2 + l + 64] * e;
-        }
+    // split s of this (unit, head) starts at p0 + s * ss; lane s holds its max and denominator (splits <= 64)
+    const int64_t ss = (int64_t)aa.G * (D + 2);
+    const float* p0 = part + (u * aa.splits * aa.G + hh) * (D + 2);
+    const float ms = l < aa.splits ? p0[l * ss] : kNegInf;
+    const float ls = l < aa.splits ? p0[l * ss + 1] : 0.f;
+    const float m = wave_max(ms);
+    const float e = ms > kNegInf ? __expf(ms - m) : 0.f;
+    const float lsum = wave_sum(ls * e);
+    float o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < aa.splits; ++s) {
+        const float es = __shfl(e, s);
+        const float* pp = p0 + s * ss + 2;
+        const float v0 = l < D ? pp[l] : 0.f, v1 = l + 64 < D ? pp[l + 64] : 0.f;
+        o0 += es != 0.f ? v0 * es : 0.f;   // a split that saw no key holds no partial output
+        o1 += es != 0.f ? v1 * es : 0.f;
     }
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     const int64_t g = u % aa.H_kv;

@@ -159,22 +159,52 @@ __device__ __forceinline__ Geom query_geom(int64_t t, int32_t n_blocks, int32_t 
     return G;
 }
 
-// Eligible tokens of one bucket: its tokens in [sink_end, l0).
-__device__ __forceinline__ int leaf_weight(const CacheView& cv, int64_t bg, uint32_t leaf, const Geom& q) {
+// The member entries of one bucket (<= 16, ascending, starting at entry
+// `off` of the block's member array) as 16-bit values in registers: the
+// aligned 48-byte window holding them is read with three 16-byte loads (none
+// past the block's 512 entries) and shifted into place.
+__device__ __forceinline__ void load_members(const uint16_t* blk_members, int off, uint16_t (&e)[16]) {
+    const int a = off & ~7;
+    const uint4* p = reinterpret_cast<const uint4*>(blk_members + a);
+    const uint4 z = {0, 0, 0, 0};
+    const uint4 w0 = p[0], w1 = (a + 8 < kBlockEntries) ? p[1] : z, w2 = (a + 16 < kBlockEntries) ? p[2] : z;
+    const uint32_t w[12] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x, w2.y, w2.z, w2.w};
+    const int sh = off - a;        // 0..7 entries
+    const int s2 = sh >> 1;        // whole 32-bit words to skip
+    uint32_t ww[9];
+#pragma unroll
+    for (int m = 0; m < 9; ++m)
+        ww[m] = s2 == 0 ? w[m] : (s2 == 1 ? w[m + 1] : (s2 == 2 ? w[m + 2] : w[m + 3]));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const uint32_t v = (sh & 1) ? __builtin_amdgcn_alignbit(ww[m + 1], ww[m], 16) : ww[m];
+        e[2 * m] = (uint16_t)(v & 0xFFFFu);
+        e[2 * m + 1] = (uint16_t)(v >> 16);
+    }
+}
+
+// Eligible tokens of one bucket: its tokens in [sink_end, l0).  m is the
+// bucket's meta word (size | first-member offset << 8).
+__device__ __forceinline__ int leaf_weight_m(const CacheView& cv, int64_t bg, uint32_t leaf, uint32_t m,
+                                             const Geom& q) {
     const int blk = leaf / kLeavesPerBlock;
     const int64_t lo = (int64_t)blk * kBlockTokens, hi = lo + kBlockTokens;
-    const uint32_t m = cv.meta[bg * cv.s_meta + leaf];
     const int sz = m & 0xFF;
     if (lo >= q.sink_end && hi <= q.l0) return kPool * sz;
     if (hi <= q.sink_end || lo >= q.l0) return 0;
-    const uint16_t* mem = cv.members + bg * cv.s_members + (int64_t)blk * kBlockEntries + ((m >> 8) & 0x3FF);
+    uint16_t e[16];
+    load_members(cv.members + bg * cv.s_members + (int64_t)blk * kBlockEntries, (m >> 8) & 0x3FF, e);
     int w = 0;
-    for (int e = 0; e < sz; ++e) {
-        int64_t t0 = lo + (int64_t)mem[e] * kPool;
 #pragma unroll
-        for (int j = 0; j < kPool; ++j) w += (t0 + j >= q.sink_end && t0 + j < q.l0) ? 1 : 0;
+    for (int j = 0; j < 16; ++j) {
+        const int64_t t0 = lo + (int64_t)e[j] * kPool;
+#pragma unroll
+        for (int jj = 0; jj < kPool; ++jj) w += (j < sz && t0 + jj >= q.sink_end && t0 + jj < q.l0) ? 1 : 0;
     }
     return w;
+}
+__device__ __forceinline__ int leaf_weight(const CacheView& cv, int64_t bg, uint32_t leaf, const Geom& q) {
+    return leaf_weight_m(cv, bg, leaf, cv.meta[bg * cv.s_meta + leaf], q);
 }
 
 }  // namespace lsa

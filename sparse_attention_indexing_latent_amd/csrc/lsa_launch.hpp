@@ -28,6 +28,7 @@ struct SelectBuffers {
     int* fb_list;
     int* counters;
     float* scores;
+    uint32_t* packed;      // materialised path: thr_key << 7 | eligible tokens, per leaf
     int64_t score_stride;
     int fb_slots;
 };

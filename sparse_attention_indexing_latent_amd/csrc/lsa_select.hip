@@ -378,23 +378,66 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
 }
 
 // ------------------------------------------------------------------ wave-level finish
-// Bitonic sort of P (power of two) 64-bit keys in LDS, descending.
-__device__ __forceinline__ void wave_sort_desc(uint64_t* a, int P) {
+// Bitonic sort, descending, of 64 N 64-bit keys held in registers: element
+// e = 64 i + lane is v[i].  Compare-exchanges across lanes use xor shuffles,
+// those across registers stay in the lane.
+template <int N>
+__device__ __forceinline__ void reg_sort_desc(uint64_t (&v)[N]) {
     const int l = lane_id();
-    for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+    for (int size = 2; size <= 64 * N; size <<= 1) {
+#pragma unroll
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int j = l; j < (P >> 1); j += 64) {
-                const int lo = 2 * stride * (j / stride) + (j % stride), hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint64_t x = a[lo], y = a[hi];
-                if (desc ? (x < y) : (x > y)) {
-                    a[lo] = y;
-                    a[hi] = x;
+            if (stride >= 64) {
+                const int rs = stride >> 6;
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    if (i & rs) continue;
+                    const bool desc = ((64 * i) & size) == 0;
+                    const uint64_t x = v[i], y = v[i | rs];
+                    const bool sw = desc ? (x < y) : (x > y);
+                    v[i] = sw ? y : x;
+                    v[i | rs] = sw ? x : y;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    const uint64_t y = shfl_xor_u64(v[i], stride);
+                    const bool desc = ((64 * i + l) & size) == 0;
+                    const bool lo = (l & stride) == 0;
+                    const uint64_t mx = v[i] > y ? v[i] : y, mn = v[i] > y ? y : v[i];
+                    v[i] = (lo == desc) ? mx : mn;
                 }
             }
-            wave_sync();
         }
     }
+}
+
+template <int N>
+__device__ __forceinline__ void wave_sort_desc_n(uint64_t* a, int P) {
+    const int l = lane_id();
+    uint64_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = (64 * i + l < P) ? a[64 * i + l] : 0ull;
+    reg_sort_desc<N>(v);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (64 * i + l < P) a[64 * i + l] = v[i];
+    wave_sync();
+}
+
+// Sorts a[0..P) (P a power of two, at most 512) descending in place.  Slots
+// past P are treated as zero keys, which sort after every other key.
+__device__ __forceinline__ void wave_sort_desc(uint64_t* a, int P) {
+    wave_sync();
+    if (P <= 64)
+        wave_sort_desc_n<1>(a, P);
+    else if (P <= 128)
+        wave_sort_desc_n<2>(a, P);
+    else if (P <= 256)
+        wave_sort_desc_n<4>(a, P);
+    else
+        wave_sort_desc_n<8>(a, P);
 }
 
 __device__ __forceinline__ int pow2_at_least(int n) {
@@ -416,25 +459,6 @@ __device__ __forceinline__ uint64_t pack_sel(uint32_t leaf, uint32_t meta, int w
 __device__ __forceinline__ int sel_off(uint64_t s) { return (int)((s >> 15) & 0x3FF); }
 __device__ __forceinline__ int sel_size(uint64_t s) { return (int)((s >> 25) & 0x1F); }
 
-// The member entries of one bucket (<= 16, ascending) as 16-bit values in
-// registers: the aligned 48-byte window holding them is read with three
-// 16-byte loads.
-__device__ __forceinline__ void load_members(const uint16_t* blk_members, int off, uint16_t (&e)[16]) {
-    const int a = off & ~7;
-    const uint4* p = reinterpret_cast<const uint4*>(blk_members + a);
-    const uint4 w0 = p[0], w1 = p[1], w2 = (a + 16 < kBlockEntries) ? p[2] : uint4{0, 0, 0, 0};
-    const uint32_t w[12] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w, w2.x, w2.y, w2.z, w2.w};
-    const int sh = off - a;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int k = j + sh;   // 0..22
-        uint32_t v = 0;
-#pragma unroll
-        for (int kk = 0; kk < 24; ++kk)
-            if (kk == k) v = (w[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu;
-        e[j] = (uint16_t)v;
-    }
-}
 __device__ __forceinline__ uint32_t sel_leaf(uint64_t s) { return (uint32_t)(s >> 32); }
 __device__ __forceinline__ bool sel_full(uint64_t s) { return (s & 0x80ull) != 0; }
 __device__ __forceinline__ int sel_count(uint64_t s) { return sel_full(s) ? (int)((s >> 8) & 0x7F) : (int)(s & 0x7F); }
@@ -514,9 +538,12 @@ __device__ __forceinline__ void expand_block_scan(uint32_t blk, const uint64_t* 
 // member entry contributes its 4 tokens at 4 x (its rank among the block's
 // selected entries); member lists are stored ascending, so a lone bucket's
 // rank is the member's position.  Other blocks use expand_block_scan.
-// base[] and spec[] are LDS scratch of at least nsel and 64 ints.
+// base[] and spec[] are LDS scratch of at least nsel and 64 ints; stage[]
+// holds the member lists of up to 64 records (64 x 16 entries) so that the
+// ranks within a block read other records' members from LDS.
 __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const CacheView& cv, int64_t bg,
-                                           const Geom& q, int32_t* out, int* tk, int* base, int* spec) {
+                                           const Geom& q, int32_t* out, int* tk, int* base, int* spec,
+                                           uint16_t* stage) {
     const int l = lane_id();
     int run = 0;
     for (int c0 = 0; c0 < nsel; c0 += 64) {
@@ -531,9 +558,21 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
     const uint16_t* mem_bg = cv.members + bg * cv.s_members;
     for (int c0 = 0; c0 < nsel; c0 += 64) {
         const int i = c0 + l;
-        if (i >= nsel) continue;
-        const uint64_t sv = sel[i];
+        const bool live = i < nsel;
+        const uint64_t sv = live ? sel[i] : 0ull;
         const uint32_t blk = sel_block(sv);
+        const uint16_t* blk_mem = mem_bg + (int64_t)blk * kBlockEntries;
+        uint16_t e[16];
+        if (live) load_members(blk_mem, sel_off(sv), e);
+        if (live) {
+            uint4* st = reinterpret_cast<uint4*>(stage + 16 * l);
+            st[0] = uint4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                          e[6] | ((uint32_t)e[7] << 16)};
+            st[1] = uint4{e[8] | ((uint32_t)e[9] << 16), e[10] | ((uint32_t)e[11] << 16),
+                          e[12] | ((uint32_t)e[13] << 16), e[14] | ((uint32_t)e[15] << 16)};
+        }
+        wave_sync();
+        if (live) {
         int f = i, g = i;
         while (f > 0 && sel_block(sel[f - 1]) == blk) --f;
         while (g + 1 < nsel && sel_block(sel[g + 1]) == blk) ++g;
@@ -545,20 +584,27 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
                 const int slot = atomicAdd(&spec[0], 1);
                 if (slot < 63) spec[1 + slot] = i;
             }
-            continue;
-        }
+        } else {
         const int sz = sel_size(sv);
-        const uint16_t* blk_mem = mem_bg + (int64_t)blk * kBlockEntries;
-        uint16_t e[16];
-        load_members(blk_mem, sel_off(sv), e);
         int rank[16];
 #pragma unroll
         for (int jm = 0; jm < 16; ++jm) rank[jm] = jm;
-        for (int x = f; x <= g; ++x) {   // other selected buckets of this block (usually none)
+        for (int x = f; x <= g; ++x) {   // other selected buckets of this block
             if (x == i) continue;
             const uint64_t sx = sel[x];
             uint16_t ex[16];
-            load_members(blk_mem, sel_off(sx), ex);
+            if (x >= c0 && x < c0 + 64) {
+                const uint4* st = reinterpret_cast<const uint4*>(stage + 16 * (x - c0));
+                const uint4 s0 = st[0], s1 = st[1];
+                const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    ex[2 * m] = (uint16_t)(sw[m] & 0xFFFFu);
+                    ex[2 * m + 1] = (uint16_t)(sw[m] >> 16);
+                }
+            } else {
+                load_members(blk_mem, sel_off(sx), ex);
+            }
             const int szx = sel_size(sx);
 #pragma unroll
             for (int y = 0; y < 16; ++y)
@@ -577,6 +623,9 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
                 d[3] = t0 + 3;
             }
         }
+        }
+        }
+        wave_sync();   // stage[] is rewritten by the next chunk
     }
     wave_sync();
     const int nspec = spec[0] < 63 ? spec[0] : 63;
@@ -599,9 +648,8 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
 
 // Walk keys[0..n) (sorted by rank), pick the buckets until k eligible
 // tokens, sort the picks by id into sel[] and expand.  Returns the count.
-__device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, const CacheView& cv,
-                                                int64_t bg,
-                                const Geom& q, int k, int32_t* out) {
+__device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, uint16_t* stage,
+                                                const CacheView& cv, int64_t bg, const Geom& q, int k, int32_t* out) {
     const int l = lane_id();
     int have = 0, nsel = 0;
     bool done = false;
@@ -633,7 +681,7 @@ __device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t*
     wave_sync();
     // the rank keys are no longer needed: reuse them as the offset scratch
     int* base = reinterpret_cast<int*>(keys);
-    return wave_expand(sel, nsel, cv, bg, q, out, tk, base, tk + 64);
+    return wave_expand(sel, nsel, cv, bg, q, out, tk, base, tk + 64, stage);
 }
 
 __device__ __forceinline__ void write_pad(int32_t* out, int from, int k) {
@@ -668,7 +716,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
                                                              const int* __restrict__ cnt,
                                                              const uint64_t* __restrict__ cand, int* fb_list,
                                                              int* counters, int32_t* lr_idx, int32_t* lr_cnt) {
-    __shared__ uint64_t keys[4][kCandCap];
+    __shared__ __align__(16) uint64_t keys[4][kCandCap];
     __shared__ uint64_t sel[4][kCandCap];
     __shared__ int tk[4][128];
     const int l = lane_id(), wid = threadIdx.x >> 6;
@@ -692,9 +740,37 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
     wave_sync();
     wave_sort_desc(keys[wid], P);
     const int64_t bg = un.b * sa.H_kv + un.g;
-    const int got = wave_walk_expand(keys[wid], c, sel[wid], tk[wid], cv, bg, q, sa.k, out);
+    // keys[] past its first 256 slots (the walk's offset scratch needs <= 512 ints) stages member lists
+    const int got = wave_walk_expand(keys[wid], c, sel[wid], tk[wid], reinterpret_cast<uint16_t*>(keys[wid] + 256), cv,
+                                     bg, q, sa.k, out);
     write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
+}
+
+// ------------------------------------------------------------------ threshold over materialised scores
+// Offset key of a score: monotone non-decreasing in the score and in
+// [0, 3 * 2^23) (s + 2 clamped to [0.5, 4)).  Equal keys need not mean equal
+// scores, so the key only bounds the candidate set; ranking uses the score.
+__device__ __forceinline__ uint32_t thr_key(float s) {
+    const float v = fminf(fmaxf(s + 2.0f, 0.5f), 3.99999976f);
+    return __float_as_uint(v) - 0x3F000000u;
+}
+
+// Packed leaf record of the materialised path: thr_key(score) << 7 | eligible
+// tokens of the leaf (<= 64).  m is the leaf's meta word.  Leaves of a block
+// that straddles an edge of [sink_end, l0) get weight 0 here and are patched
+// afterwards from their member lists (patch_straddling).
+__device__ __forceinline__ uint32_t pack_leaf(uint32_t x, uint32_t m, float score, const Geom& q) {
+    const int64_t lo = (int64_t)(x / kLeavesPerBlock) * kBlockTokens;
+    const int w = (lo >= q.sink_end && lo + kBlockTokens <= q.l0) ? kPool * (int)(m & 0xFFu) : 0;
+    return (thr_key(score) << 7) | (uint32_t)w;
+}
+
+// The (at most two) blocks that straddle an edge of [sink_end, l0).
+__device__ __forceinline__ void straddling_blocks(const Geom& q, int& b0, int& b1) {
+    b0 = (q.sink_end % kBlockTokens) ? (int)(q.sink_end / kBlockTokens) : -1;
+    b1 = (q.l0 % kBlockTokens) ? (int)(q.l0 / kBlockTokens) : -1;
+    if (b1 == b0) b1 = -1;
 }
 
 // ------------------------------------------------------------------ materialised scores
@@ -702,7 +778,8 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
 template <bool BF16>
 __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void* __restrict__ qhat,
                                                         const int64_t* __restrict__ q_pos, SelArgs sa,
-                                                        float* __restrict__ scores, int64_t score_stride) {
+                                                        float* __restrict__ scores, uint32_t* __restrict__ packed,
+                                                        int64_t score_stride) {
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
     const int64_t u = blockIdx.x;
     const Unit un = unit_of(u, sa);
@@ -715,19 +792,257 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
     const int t0 = blockIdx.y * per, t1 = min(ntiles, t0 + per);
     const int64_t bg = un.b * sa.H_kv + un.g;
     const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
-    QFragBF16 qf;
-    if constexpr (BF16) load_qfrag_bf16(qf, reinterpret_cast<const uint16_t*>(qhat) + qrow, n == 0, sa.G);
     const float* qf32 = reinterpret_cast<const float*>(qhat) + qrow;
     float* sc = scores + u * score_stride;
-    for (int tt = t0 + wid; tt < t1; tt += 4) {
-        const int64_t x0 = (int64_t)tt * 16;
-        f32x4 vals;
-        if constexpr (BF16)
-            vals = score_tile_bf16(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent, x0, qf, sa.G);
-        else
-            vals = score_tile_f32(reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent, x0, qf32, n == 0, sa.G);
-        if (n == 0) *reinterpret_cast<f32x4*>(sc + x0 + 4 * h) = vals;
+    uint32_t* pk = packed + u * score_stride;
+    const uint32_t* meta = cv.meta + bg * cv.s_meta;
+    // lanes n == 0 hold the scores of leaves x0 + 4h .. x0 + 4h + 3; they
+    // write them and the packed records (key, eligible tokens)
+    auto emit = [&](int64_t x0, const f32x4& vals, const uint4& m4) {
+        *reinterpret_cast<f32x4*>(sc + x0 + 4 * h) = vals;
+        const uint32_t xb = (uint32_t)(x0 + 4 * h);
+        uint4 r;
+        r.x = pack_leaf(xb, m4.x, vals[0], q);
+        r.y = pack_leaf(xb + 1, m4.y, vals[1], q);
+        r.z = pack_leaf(xb + 2, m4.z, vals[2], q);
+        r.w = pack_leaf(xb + 3, m4.w, vals[3], q);
+        *reinterpret_cast<uint4*>(pk + xb) = r;
+    };
+    if constexpr (BF16) {
+        // B operand: query head n of the group in column n (zero columns past G);
+        // the group max is taken across the 16 lanes of each row group
+        uint4 qa = {0, 0, 0, 0}, qc = {0, 0, 0, 0};
+        if (n < sa.G) {
+            const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(qhat) + qrow +
+                                                            n * kLatent + 16 * h);
+            qa = p[0];
+            qc = p[1];
+        }
+        const bf16x8 q0 = as_bf16x8(qa), q1 = as_bf16x8(qc);
+        // each wave takes 4 consecutive tiles and has all their loads in flight before the MFMAs
+        const uint16_t* cb = reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent;
+        for (int tt0 = t0 + 4 * wid; tt0 < t1; tt0 += 16) {
+            uint4 a[4][2], m4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (tt0 + j < t1) {
+                    load_cent_bf16(cb, (int64_t)(tt0 + j) * 16, a[j][0], a[j][1]);
+                    m4[j] = n == 0 ? *reinterpret_cast<const uint4*>(meta + (int64_t)(tt0 + j) * 16 + 4 * h)
+                                   : uint4{0, 0, 0, 0};
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (tt0 + j < t1) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j][0]), q0, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j][1]), q1, acc, 0, 0, 0);
+                    f32x4 vals;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = n < sa.G ? acc[v] : kNegInf;
+                        x = fmaxf(x, __shfl_xor(x, 1));
+                        x = fmaxf(x, __shfl_xor(x, 2));
+                        x = fmaxf(x, __shfl_xor(x, 4));
+                        x = fmaxf(x, __shfl_xor(x, 8));
+                        vals[v] = x;
+                    }
+                    if (n == 0) emit((int64_t)(tt0 + j) * 16, vals, m4[j]);
+                }
+            }
+        }
+    } else {
+        for (int tt = t0 + wid; tt < t1; tt += 4) {
+            const int64_t x0 = (int64_t)tt * 16;
+            const f32x4 vals =
+                score_tile_f32(reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent, x0, qf32, n == 0, sa.G);
+            if (n == 0) emit(x0, vals, *reinterpret_cast<const uint4*>(meta + x0 + 4 * h));
+        }
     }
+    // patch the straddling blocks' leaves of this workgroup's range
+    int sb0, sb1;
+    straddling_blocks(q, sb0, sb1);
+    if (sb0 < 0 && sb1 < 0) return;
+    __syncthreads();   // this workgroup's score writes are visible to all its threads
+    if (threadIdx.x < 2 * kLeavesPerBlock) {
+        const int blk = threadIdx.x < kLeavesPerBlock ? sb0 : sb1;
+        const int64_t x = (int64_t)blk * kLeavesPerBlock + threadIdx.x % kLeavesPerBlock;
+        if (blk >= 0 && x >= (int64_t)t0 * 16 && x < (int64_t)t1 * 16) {
+            const int w = leaf_weight(cv, bg, (uint32_t)x, q);
+            pk[x] = (thr_key(sc[x]) << 7) | (uint32_t)w;
+        }
+    }
+}
+
+constexpr int kThrThreads = 1024;
+constexpr int kThrBins = 3072;   // level 0: key >> 13
+constexpr int kThrGoal = 128;    // refine the bound while more leaves than this sit at or above it
+constexpr int kThrRegs = 32;     // leaves per thread held in registers (one chunk = 32768 leaves)
+
+__device__ __forceinline__ unsigned long long shfl_down_u64(unsigned long long v, int o) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl_down(lo, o);
+    hi = __shfl_down(hi, o);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// One workgroup per (query, KV head), over the packed records of its visible
+// leaves.  Finds a key bound L such that the leaves with key >= L hold at
+// least k eligible tokens while those with key above L's bin hold fewer, with
+// at most kCandCap leaves at or above L (weighted histograms of 3072, 2048 and
+// 4 bins, each refining the boundary bin of the one before); writes those
+// leaves' rank keys to cand in any order and their count to cnt.  A lower key
+// means a lower score, so every leaf below L ranks after every candidate, and
+// the walk in rank order ends among the candidates exactly where a walk over
+// all leaves ends.
+__global__ __launch_bounds__(kThrThreads) void threshold_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
+                                                                 SelArgs sa, const float* __restrict__ scores,
+                                                                 const uint32_t* __restrict__ packed,
+                                                                 int64_t score_stride, int* __restrict__ cnt,
+                                                                 uint64_t* __restrict__ cand) {
+    __shared__ unsigned long long hist[kThrBins];   // count << 32 | weight
+    __shared__ unsigned long long wtot[kThrThreads / 64];
+    __shared__ uint32_t bc[4];
+    __shared__ int ncand;
+    __shared__ uint32_t cid[kCandCap];
+    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
+    const int64_t u = blockIdx.x;
+    const Unit un = unit_of(u, sa);
+    const float* sc = scores + u * score_stride;
+    const uint32_t* pk = packed + u * score_stride;
+    // Records are handled in chunks of kThrRegs per thread, held in registers;
+    // with a single chunk its loads are issued before the query position is
+    // known (rows are written up to the visible leaves, read up to n_leaves
+    // and masked) and it stays resident.
+    constexpr int kChunk = kThrRegs * kThrThreads;
+    uint32_t rv[kThrRegs];
+#define LSA_THR_LOAD(c0, lim)                                   \
+    _Pragma("unroll") for (int j = 0; j < kThrRegs; ++j) {      \
+        const int x = (c0) + j * kThrThreads + tid;             \
+        rv[j] = x < (lim) ? pk[x] : 0u;                         \
+    }
+    const bool resident = cv.n_leaves <= kChunk;
+    if (resident) LSA_THR_LOAD(0, (int)cv.n_leaves)
+    const int64_t t = q_pos[un.b * sa.n_q + un.i];
+    const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
+    const int64_t total = q.l0 > q.sink_end ? q.l0 - q.sink_end : 0;
+    if (t < 0 || sa.k == 0 || (int64_t)sa.k >= total) {   // handled by the walk kernel without candidates
+        if (tid == 0) cnt[u] = 0;
+        return;
+    }
+    const int NLv = kLeavesPerBlock * q.nvis;
+    const int nchunks = (NLv + kChunk - 1) / kChunk;
+    if (resident) {
+#pragma unroll
+        for (int j = 0; j < kThrRegs; ++j)
+            if (j * kThrThreads + tid >= NLv) rv[j] = 0u;   // weight 0: never counted
+    }
+    uint32_t lo = 0, target = (uint32_t)sa.k, cabove = 0, lower = 0, flo = 0;
+    int shift = 13, nb = kThrBins;
+    bool overflow = false;
+    // Level -1 histograms only each thread's best leaf.  Those leaves are a
+    // subset of all leaves, so if the ones at or above bin F hold >= k tokens
+    // then so do all leaves at or above F, and the boundary bin is >= F: the
+    // level-0 histogram may skip every leaf below F (far fewer LDS atomics).
+    for (int level = -1; level < 3; ++level) {
+        for (int j = tid; j < nb; j += kThrThreads) hist[j] = 0ull;
+        __syncthreads();
+        const uint32_t hi = lo + ((uint32_t)nb << shift);
+        uint32_t best = 0;   // best record with a nonzero weight (records compare by key first)
+        for (int c = 0; c < nchunks; ++c) {
+            if (!resident) LSA_THR_LOAD(c * kChunk, NLv)
+#pragma unroll
+            for (int j = 0; j < kThrRegs; ++j) {
+                const uint32_t key = rv[j] >> 7, w = rv[j] & 0x7Fu;
+                if (level < 0) {
+                    if (w > 0 && rv[j] > best) best = rv[j];
+                } else if (w > 0 && key >= lo && key < hi && key >= flo) {
+                    atomicAdd(&hist[(key - lo) >> shift], (1ull << 32) | (unsigned long long)w);
+                }
+            }
+        }
+        if (level < 0 && best != 0u)
+            atomicAdd(&hist[(best >> 7) >> shift], (1ull << 32) | (unsigned long long)(best & 0x7Fu));
+        if (level < 0 && tid == 0) bc[0] = 0xFFFFFFFFu;   // stays so if the best leaves hold < k tokens
+        __syncthreads();
+        // thread tid owns bins [per * tid, per * tid + per); suffix sums run from the top bin down
+        const int per = (nb + kThrThreads - 1) / kThrThreads;
+        const int b0 = per * tid;
+        unsigned long long mine = 0ull;
+        for (int j = 0; j < per; ++j)
+            if (b0 + j < nb) mine += hist[b0 + j];
+        unsigned long long suf = mine;   // inclusive suffix within the wave (lanes >= l)
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long v = shfl_down_u64(suf, o);
+            if (l + o < 64) suf += v;
+        }
+        if (l == 0) wtot[wid] = suf;
+        __syncthreads();
+        unsigned long long above = suf - mine;   // bins of higher threads in this wave
+        for (int w2 = wid + 1; w2 < kThrThreads / 64; ++w2) above += wtot[w2];
+        // the boundary bin: weight above it < target <= weight above it + its own
+        for (int j = per - 1; j >= 0; --j) {
+            const int bin = b0 + j;
+            if (bin >= nb) continue;
+            const unsigned long long hv = hist[bin];
+            const uint32_t wa = (uint32_t)above, wb = (uint32_t)hv;
+            if (wa < target && target <= wa + wb) {
+                bc[0] = (uint32_t)bin;
+                bc[1] = target - wa;
+                bc[2] = (uint32_t)(above >> 32);
+                bc[3] = (uint32_t)(hv >> 32);
+            }
+            above += hv;
+        }
+        __syncthreads();
+        const uint32_t B = bc[0], rem = bc[1], cab = cabove + bc[2], cB = bc[3];
+        __syncthreads();
+        if (level < 0) {
+            flo = B == 0xFFFFFFFFu ? 0u : (B << shift);
+            continue;
+        }
+        if (cab + cB <= (uint32_t)(level == 2 ? kCandCap : kThrGoal)) {
+            lower = lo + (B << shift);
+            break;
+        }
+        if (level == 2) {
+            overflow = true;
+            break;
+        }
+        lo += B << shift;
+        target = rem;
+        cabove = cab;
+        shift = level == 0 ? 2 : 0;
+        nb = level == 0 ? 2048 : 4;
+    }
+    if (overflow) {   // too many leaves tie at the boundary key: the exact radix path takes the unit
+        if (tid == 0) cnt[u] = kCandCap + 1;
+        return;
+    }
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        if (!resident) LSA_THR_LOAD(c * kChunk, NLv)
+#pragma unroll
+        for (int j = 0; j < kThrRegs; ++j) {
+            const int x = c * kChunk + j * kThrThreads + tid;
+            const bool take = (rv[j] & 0x7Fu) != 0u && (rv[j] >> 7) >= lower;
+            const uint64_t bal = __ballot(take);
+            int base = 0;
+            if (l == 0 && bal) base = atomicAdd(&ncand, __popcll(bal));
+            base = __shfl(base, 0);
+            if (take) {
+                const int pos = base + __popcll(bal & ((1ull << l) - 1ull));
+                if (pos < kCandCap) cid[pos] = (uint32_t)x;
+            }
+        }
+    }
+    __syncthreads();
+    const int nc = ncand < kCandCap ? ncand : kCandCap;
+    if (tid < nc) cand[u * kCandCap + tid] = rank_key(sc[cid[tid]], cid[tid]);
+    if (tid == 0) cnt[u] = ncand;
+#undef LSA_THR_LOAD
 }
 
 // Workgroup-wide exclusive scan over 256 threads (4 waves).
@@ -751,17 +1066,19 @@ constexpr int kExactSel = LSA_MAX_K + 2 * kLeavesPerBlock;   // selected buckets
 
 // One workgroup per (query, KV head): weighted radix select of the boundary
 // key over materialised scores, then the selected buckets in id order.
-// With unit_list, loops over the fallback list and scores its units itself.
+// With unit_list, loops over the fallback list; with rescore, it scores each
+// unit itself into the row of its workgroup, else reads the unit's own row.
 template <bool BF16>
 __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const void* __restrict__ qhat,
                                                            const int64_t* __restrict__ q_pos, SelArgs sa,
                                                            const int* unit_list, const int* counters,
-                                                           float* scores, int64_t score_stride,
+                                                           float* scores, int64_t score_stride, int rescore,
                                                            int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ uint32_t hist[256];
     __shared__ uint64_t sel[kExactSel];
     __shared__ int ebase[kExactSel];
     __shared__ int tk[128];
+    __shared__ __align__(16) uint16_t stg[64 * 16];
     __shared__ int sh4[4];
     __shared__ uint32_t bc[4];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
@@ -780,8 +1097,8 @@ __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const v
         }
         const int NLv = kLeavesPerBlock * q.nvis;
         const int64_t bg = un.b * sa.H_kv + un.g;
-        float* sc = scores + (unit_list ? (int64_t)blockIdx.x : u) * score_stride;
-        if (unit_list) {
+        float* sc = scores + (rescore ? (int64_t)blockIdx.x : u) * score_stride;
+        if (rescore) {
             const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
             QFragBF16 qf;
             if constexpr (BF16) load_qfrag_bf16(qf, reinterpret_cast<const uint16_t*>(qhat) + qrow, n == 0, sa.G);
@@ -858,7 +1175,7 @@ __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const v
         __syncthreads();
         if (wid == 0) {
             const int ns = nsel < kExactSel ? nsel : kExactSel;
-            const int got = wave_expand(sel, ns, cv, bg, q, out, tk, ebase, tk + 64);
+            const int got = wave_expand(sel, ns, cv, bg, q, out, tk, ebase, tk + 64, stg);
             write_pad(out, got, sa.k);
             if (l == 0) lr_cnt[u] = got;
         }
@@ -878,6 +1195,7 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
     __shared__ uint32_t front[4][LSA_MAX_BEAM];
     __shared__ uint64_t sel[4][2 * LSA_MAX_BEAM];
     __shared__ int tk[4][128];
+    __shared__ __align__(16) uint16_t stg[4][64 * 16];
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
     const int64_t u = (int64_t)blockIdx.x * 4 + wid;
     if (u >= sa.n_units) return;
@@ -977,7 +1295,7 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
         for (int j = l; j < nf; j += 64) front[wid][j] = rank_key_id(keys[wid][j]);
         wave_sync();
     }
-    const int got = wave_walk_expand(keys[wid], nf, sel[wid], tk[wid], cv, bg, q, sa.k, out);
+    const int got = wave_walk_expand(keys[wid], nf, sel[wid], tk[wid], stg[wid], cv, bg, q, sa.k, out);
     write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
 }
@@ -1027,10 +1345,10 @@ hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_
     if (e != hipSuccess) return e;
     if (bf16)
         hipLaunchKernelGGL(exact_select_kernel<true>, dim3((unsigned)sb.fb_slots), dim3(256), 0, st, cv, sb.qhat, q_pos,
-                           sa, sb.fb_list, sb.counters, sb.scores, sb.score_stride, lr_idx, lr_cnt);
+                           sa, sb.fb_list, sb.counters, sb.scores, sb.score_stride, 1, lr_idx, lr_cnt);
     else
         hipLaunchKernelGGL(exact_select_kernel<false>, dim3((unsigned)sb.fb_slots), dim3(256), 0, st, cv, sb.qhat,
-                           q_pos, sa, sb.fb_list, sb.counters, sb.scores, sb.score_stride, lr_idx, lr_cnt);
+                           q_pos, sa, sb.fb_list, sb.counters, sb.scores, sb.score_stride, 1, lr_idx, lr_cnt);
     return hipGetLastError();
 }
 
@@ -1043,18 +1361,26 @@ hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int6
     dim3 grid((unsigned)sa.n_units, (unsigned)splits);
     if (bf16)
         hipLaunchKernelGGL(score_all_kernel<true>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, sb.scores,
-                           sb.score_stride);
+                           sb.packed, sb.score_stride);
     else
         hipLaunchKernelGGL(score_all_kernel<false>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, sb.scores,
-                           sb.score_stride);
+                           sb.packed, sb.score_stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)sa.n_units), dim3(kThrThreads), 0, st, cv, q_pos, sa, sb.scores,
+                       sb.packed, sb.score_stride, sb.cnt, sb.cand);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fused_finalize_kernel, dim3((unsigned)((sa.n_units + 3) / 4)), dim3(256), 0, st, cv, q_pos, sa,
+                       sb.cnt, sb.cand, sb.fb_list, sb.counters, lr_idx, lr_cnt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (bf16)
-        hipLaunchKernelGGL(exact_select_kernel<true>, dim3((unsigned)sa.n_units), dim3(256), 0, st, cv, sb.qhat, q_pos,
-                           sa, (const int*)nullptr, sb.counters, sb.scores, sb.score_stride, lr_idx, lr_cnt);
+        hipLaunchKernelGGL(exact_select_kernel<true>, dim3((unsigned)sb.fb_slots), dim3(256), 0, st, cv, sb.qhat, q_pos,
+                           sa, sb.fb_list, sb.counters, sb.scores, sb.score_stride, 0, lr_idx, lr_cnt);
     else
-        hipLaunchKernelGGL(exact_select_kernel<false>, dim3((unsigned)sa.n_units), dim3(256), 0, st, cv, sb.qhat,
-                           q_pos, sa, (const int*)nullptr, sb.counters, sb.scores, sb.score_stride, lr_idx, lr_cnt);
+        hipLaunchKernelGGL(exact_select_kernel<false>, dim3((unsigned)sb.fb_slots), dim3(256), 0, st, cv, sb.qhat,
+                           q_pos, sa, sb.fb_list, sb.counters, sb.scores, sb.score_stride, 0, lr_idx, lr_cnt);
     return hipGetLastError();
 }
 
