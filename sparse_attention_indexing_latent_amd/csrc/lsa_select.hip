@@ -426,6 +426,66 @@ __device__ __forceinline__ void wave_sort_desc_n(uint64_t* a, int P) {
     wave_sync();
 }
 
+template <int N>
+__device__ __forceinline__ void reg_sort_desc_u32(uint32_t (&v)[N]) {
+    const int l = lane_id();
+#pragma unroll
+    for (int size = 2; size <= 64 * N; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= 64) {
+                const int rs = stride >> 6;
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    if (i & rs) continue;
+                    const bool desc = ((64 * i) & size) == 0;
+                    const uint32_t x = v[i], y = v[i | rs];
+                    const bool sw = desc ? (x < y) : (x > y);
+                    v[i] = sw ? y : x;
+                    v[i | rs] = sw ? x : y;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    const uint32_t y = (uint32_t)__shfl_xor((int)v[i], stride);
+                    const bool desc = ((64 * i + l) & size) == 0;
+                    const bool lo = (l & stride) == 0;
+                    const uint32_t mx = v[i] > y ? v[i] : y, mn = v[i] > y ? y : v[i];
+                    v[i] = (lo == desc) ? mx : mn;
+                }
+            }
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wave_sort_desc_u32_n(uint32_t* a, int P) {
+    const int l = lane_id();
+    uint32_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = (64 * i + l < P) ? a[64 * i + l] : 0u;
+    reg_sort_desc_u32<N>(v);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (64 * i + l < P) a[64 * i + l] = v[i];
+    wave_sync();
+}
+
+// Sorts a[0..P) (P a power of two, at most 1024) of 32-bit keys descending.
+__device__ __forceinline__ void wave_sort_desc_u32(uint32_t* a, int P) {
+    wave_sync();
+    if (P <= 64)
+        wave_sort_desc_u32_n<1>(a, P);
+    else if (P <= 128)
+        wave_sort_desc_u32_n<2>(a, P);
+    else if (P <= 256)
+        wave_sort_desc_u32_n<4>(a, P);
+    else if (P <= 512)
+        wave_sort_desc_u32_n<8>(a, P);
+    else
+        wave_sort_desc_u32_n<16>(a, P);
+}
+
 // Sorts a[0..P) (P a power of two, at most 512) descending in place.  Slots
 // past P are treated as zero keys, which sort after every other key.
 __device__ __forceinline__ void wave_sort_desc(uint64_t* a, int P) {
@@ -530,107 +590,77 @@ __device__ __forceinline__ void expand_block_scan(uint32_t blk, const uint64_t* 
     wave_sync();
 }
 
+// Sum over records [a, b) of their taken token counts (wave-wide).
+__device__ __forceinline__ int records_tokens(const uint64_t* sel, int a, int b) {
+    int acc = 0;
+    for (int c0 = a; c0 < b; c0 += 64) {
+        const int i = c0 + lane_id();
+        acc += i < b ? sel_count(sel[i]) : 0;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    return acc;
+}
+
 // Writes the tokens of the selected buckets (sel[0..nsel), sorted by leaf id)
-// in ascending order and returns their number.  Each record's output offset
-// is the prefix of the records' token counts (records of one block are
-// contiguous, and a block's tokens precede the next block's).  In a block
-// lying inside [sink_end, l0) whose buckets are all fully taken, every
-// member entry contributes its 4 tokens at 4 x (its rank among the block's
-// selected entries); member lists are stored ascending, so a lone bucket's
-// rank is the member's position.  Other blocks use expand_block_scan.
-// base[] and spec[] are LDS scratch of at least nsel and 64 ints; stage[]
-// holds the member lists of up to 64 records (64 x 16 entries) so that the
-// ranks within a block read other records' members from LDS.
+// in ascending order and returns their number.  A block is "plain" when it
+// lies inside [sink_end, l0) and every selected bucket of it is taken whole;
+// the other (special) blocks, at most the two straddling an edge and the one
+// holding the partially taken bucket, go through expand_block_scan.  The
+// member entries of all plain buckets are gathered as (block, entry) keys,
+// sorted once, and entry number p of that order lands at 4 p plus the
+// tokens of the special blocks before its block.
+// LDS scratch: ent[] of at least k/4 keys, tk[] of 256 ints (tk[0..64) is
+// expand_block_scan's map, tk[64..) lists the special blocks).
 __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const CacheView& cv, int64_t bg,
-                                           const Geom& q, int32_t* out, int* tk, int* base, int* spec,
-                                           uint16_t* stage) {
+                                           const Geom& q, int32_t* out, int* tk, uint32_t* ent) {
     const int l = lane_id();
-    int run = 0;
+    int* spec_first = tk + 64;    // [0] = count, then first record of each special block
+    int* spec_tok = tk + 128;     // tokens of special block s
+    int* spec_blk = tk + 192;     // block id of special block s
+    // the block of the partially taken bucket (at most one), -1 if none
+    int part_blk = -1;
     for (int c0 = 0; c0 < nsel; c0 += 64) {
         const int i = c0 + l;
-        const int ci = i < nsel ? sel_count(sel[i]) : 0;
-        const int inc = wave_incl_scan(ci);
-        if (i < nsel) base[i] = run + inc - ci;
-        run += __shfl(inc, 63);
+        const uint64_t bal = __ballot(i < nsel && !sel_full(sel[i]));
+        if (bal) {
+            part_blk = (int)sel_block(sel[c0 + __builtin_ctzll(bal)]);
+            break;
+        }
     }
-    if (l == 0) spec[0] = 0;
+    if (l == 0) spec_first[0] = 0;
     wave_sync();
     const uint16_t* mem_bg = cv.members + bg * cv.s_members;
+    int nent = 0;
     for (int c0 = 0; c0 < nsel; c0 += 64) {
         const int i = c0 + l;
         const bool live = i < nsel;
         const uint64_t sv = live ? sel[i] : 0ull;
-        const uint32_t blk = sel_block(sv);
-        const uint16_t* blk_mem = mem_bg + (int64_t)blk * kBlockEntries;
-        uint16_t e[16];
-        if (live) load_members(blk_mem, sel_off(sv), e);
-        if (live) {
-            uint4* st = reinterpret_cast<uint4*>(stage + 16 * l);
-            st[0] = uint4{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
-                          e[6] | ((uint32_t)e[7] << 16)};
-            st[1] = uint4{e[8] | ((uint32_t)e[9] << 16), e[10] | ((uint32_t)e[11] << 16),
-                          e[12] | ((uint32_t)e[13] << 16), e[14] | ((uint32_t)e[15] << 16)};
-        }
-        wave_sync();
-        if (live) {
-        int f = i, g = i;
-        while (f > 0 && sel_block(sel[f - 1]) == blk) --f;
-        while (g + 1 < nsel && sel_block(sel[g + 1]) == blk) ++g;
+        const int blk = (int)sel_block(sv);
         const int64_t lo = (int64_t)blk * kBlockTokens;
-        bool special = !(lo >= q.sink_end && lo + kBlockTokens <= q.l0);
-        for (int x = f; x <= g && !special; ++x) special = !sel_full(sel[x]);
-        if (special) {
-            if (i == f) {
-                const int slot = atomicAdd(&spec[0], 1);
-                if (slot < 63) spec[1 + slot] = i;
-            }
-        } else {
-        const int sz = sel_size(sv);
-        int rank[16];
-#pragma unroll
-        for (int jm = 0; jm < 16; ++jm) rank[jm] = jm;
-        for (int x = f; x <= g; ++x) {   // other selected buckets of this block
-            if (x == i) continue;
-            const uint64_t sx = sel[x];
-            uint16_t ex[16];
-            if (x >= c0 && x < c0 + 64) {
-                const uint4* st = reinterpret_cast<const uint4*>(stage + 16 * (x - c0));
-                const uint4 s0 = st[0], s1 = st[1];
-                const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    ex[2 * m] = (uint16_t)(sw[m] & 0xFFFFu);
-                    ex[2 * m + 1] = (uint16_t)(sw[m] >> 16);
-                }
-            } else {
-                load_members(blk_mem, sel_off(sx), ex);
-            }
-            const int szx = sel_size(sx);
-#pragma unroll
-            for (int y = 0; y < 16; ++y)
-#pragma unroll
-                for (int jm = 0; jm < 16; ++jm) rank[jm] += (y < szx && ex[y] < e[jm]) ? 1 : 0;
+        const bool special = live && (!(lo >= q.sink_end && lo + kBlockTokens <= q.l0) || blk == part_blk);
+        const bool first = live && (i == 0 || (int)sel_block(sel[i - 1]) != blk);
+        if (special && first) {
+            const int slot = atomicAdd(&spec_first[0], 1);
+            if (slot < 63) spec_first[1 + slot] = i;
         }
-        int32_t* o = out + base[f];
+        const int sz = (live && !special) ? sel_size(sv) : 0;
+        const int incl = wave_incl_scan(sz);
+        const int pos = nent + incl - sz;
+        nent += __shfl(incl, 63);
+        if (sz > 0) {
+            uint16_t e[16];
+            load_members(mem_bg + (int64_t)blk * kBlockEntries, sel_off(sv), e);
 #pragma unroll
-        for (int jm = 0; jm < 16; ++jm) {
-            if (jm < sz) {
-                const int32_t t0 = (int32_t)(lo + (int64_t)kPool * e[jm]);
-                int32_t* d = o + kPool * rank[jm];
-                d[0] = t0;
-                d[1] = t0 + 1;
-                d[2] = t0 + 2;
-                d[3] = t0 + 3;
-            }
+            for (int jm = 0; jm < 16; ++jm)
+                if (jm < sz) ent[pos + jm] = ((uint32_t)blk << 9) | e[jm];
         }
-        }
-        }
-        wave_sync();   // stage[] is rewritten by the next chunk
     }
     wave_sync();
-    const int nspec = spec[0] < 63 ? spec[0] : 63;
+    const int nspec = spec_first[0] < 63 ? spec_first[0] : 63;
+    // special blocks: their record ranges, token counts and output offsets
     for (int sidx = 0; sidx < nspec; ++sidx) {
-        const int f = spec[1 + sidx];
+        const int f = spec_first[1 + sidx];
         const uint32_t blk = sel_block(sel[f]);
         int g = f;
         while (true) {
@@ -640,15 +670,53 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
             g += r;
             if (r < 64) break;
         }
-        expand_block_scan(blk, sel, f, g, cv, bg, q, out + base[f], tk);
+        const int tok = records_tokens(sel, f, g);
+        if (l == 0) {
+            spec_tok[sidx] = tok;
+            spec_blk[sidx] = (int)blk;
+        }
     }
     wave_sync();
-    return run;
+    // plain entries ascending by (block, entry): sort the complements descending
+    const int P = pow2_at_least(nent);
+    for (int j = l; j < P; j += 64) ent[j] = j < nent ? ~ent[j] : 0u;
+    wave_sync();
+    wave_sort_desc_u32(ent, P);
+    for (int p = l; p < nent; p += 64) {
+        const uint32_t key = ~ent[p];
+        const int blk = (int)(key >> 9);
+        int before = 0;
+        for (int sidx = 0; sidx < nspec; ++sidx) before += spec_blk[sidx] < blk ? spec_tok[sidx] : 0;
+        const int32_t t0 = (int32_t)((int64_t)blk * kBlockTokens + kPool * (int64_t)(key & 511u));
+        int32_t* d = out + kPool * p + before;
+        d[0] = t0;
+        d[1] = t0 + 1;
+        d[2] = t0 + 2;
+        d[3] = t0 + 3;
+    }
+    // special blocks at their offsets: tokens of plain entries and special blocks before them
+    const int total = records_tokens(sel, 0, nsel);
+    for (int sidx = 0; sidx < nspec; ++sidx) {
+        const int f = spec_first[1 + sidx];
+        const int blk = spec_blk[sidx];
+        int g = f;
+        while (true) {
+            const int idx = g + l;
+            const bool same = idx < nsel && (int)sel_block(sel[idx]) == blk;
+            const int r = __popcll(__ballot(same));
+            g += r;
+            if (r < 64) break;
+        }
+        const int off = records_tokens(sel, 0, f);
+        expand_block_scan((uint32_t)blk, sel, f, g, cv, bg, q, out + off, tk);
+    }
+    wave_sync();
+    return total;
 }
 
 // Walk keys[0..n) (sorted by rank), pick the buckets until k eligible
 // tokens, sort the picks by id into sel[] and expand.  Returns the count.
-__device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, uint16_t* stage,
+__device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, uint32_t* ent,
                                                 const CacheView& cv, int64_t bg, const Geom& q, int k, int32_t* out) {
     const int l = lane_id();
     int have = 0, nsel = 0;
@@ -679,9 +747,7 @@ __device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t*
     wave_sort_desc(sel, P);
     for (int j = l; j < P; j += 64) sel[j] = ~sel[j];
     wave_sync();
-    // the rank keys are no longer needed: reuse them as the offset scratch
-    int* base = reinterpret_cast<int*>(keys);
-    return wave_expand(sel, nsel, cv, bg, q, out, tk, base, tk + 64, stage);
+    return wave_expand(sel, nsel, cv, bg, q, out, tk, ent);
 }
 
 __device__ __forceinline__ void write_pad(int32_t* out, int from, int k) {
@@ -718,7 +784,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
                                                              int* counters, int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ __align__(16) uint64_t keys[4][kCandCap];
     __shared__ uint64_t sel[4][kCandCap];
-    __shared__ int tk[4][128];
+    __shared__ int tk[4][256];
     const int l = lane_id(), wid = threadIdx.x >> 6;
     const int64_t u = (int64_t)blockIdx.x * 4 + wid;
     if (u >= sa.n_units) return;
@@ -740,9 +806,9 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
     wave_sync();
     wave_sort_desc(keys[wid], P);
     const int64_t bg = un.b * sa.H_kv + un.g;
-    // keys[] past its first 256 slots (the walk's offset scratch needs <= 512 ints) stages member lists
-    const int got = wave_walk_expand(keys[wid], c, sel[wid], tk[wid], reinterpret_cast<uint16_t*>(keys[wid] + 256), cv,
-                                     bg, q, sa.k, out);
+    // the rank keys are dead once the walk is done: their space holds the entry keys (<= k / 4)
+    const int got = wave_walk_expand(keys[wid], c, sel[wid], tk[wid], reinterpret_cast<uint32_t*>(keys[wid]), cv, bg,
+                                     q, sa.k, out);
     write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
 }
@@ -1076,9 +1142,8 @@ __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const v
                                                            int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ uint32_t hist[256];
     __shared__ uint64_t sel[kExactSel];
-    __shared__ int ebase[kExactSel];
-    __shared__ int tk[128];
-    __shared__ __align__(16) uint16_t stg[64 * 16];
+    __shared__ uint32_t ebase[kExactSel];   // entry keys of the expansion (>= k / 4)
+    __shared__ int tk[256];
     __shared__ int sh4[4];
     __shared__ uint32_t bc[4];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
@@ -1175,7 +1240,7 @@ __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const v
         __syncthreads();
         if (wid == 0) {
             const int ns = nsel < kExactSel ? nsel : kExactSel;
-            const int got = wave_expand(sel, ns, cv, bg, q, out, tk, ebase, tk + 64, stg);
+            const int got = wave_expand(sel, ns, cv, bg, q, out, tk, ebase);
             write_pad(out, got, sa.k);
             if (l == 0) lr_cnt[u] = got;
         }
@@ -1194,8 +1259,8 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
     __shared__ uint64_t keys[4][2 * LSA_MAX_BEAM];
     __shared__ uint32_t front[4][LSA_MAX_BEAM];
     __shared__ uint64_t sel[4][2 * LSA_MAX_BEAM];
-    __shared__ int tk[4][128];
-    __shared__ __align__(16) uint16_t stg[4][64 * 16];
+    __shared__ int tk[4][256];
+    __shared__ uint32_t ent[4][LSA_MAX_K / kPool];
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
     const int64_t u = (int64_t)blockIdx.x * 4 + wid;
     if (u >= sa.n_units) return;
@@ -1295,7 +1360,7 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
         for (int j = l; j < nf; j += 64) front[wid][j] = rank_key_id(keys[wid][j]);
         wave_sync();
     }
-    const int got = wave_walk_expand(keys[wid], nf, sel[wid], tk[wid], stg[wid], cv, bg, q, sa.k, out);
+    const int got = wave_walk_expand(keys[wid], nf, sel[wid], tk[wid], ent[wid], cv, bg, q, sa.k, out);
     write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
 }
