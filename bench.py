@@ -283,25 +283,50 @@ def decode_on_cache(cfg, G, inp, cache_buf, tree):
     newK = G["K"][:, :, cfg.T].clone()
     newV = G["V"][:, :, cfg.T].clone()
     rows = kv_rows(G["K"], cfg.T)
+    scfg = lsa.select_cfg(cfg.k, cfg.n_sinks, cfg.window, search, cfg.beam)
+    wsel = torch.empty(lsa.select_workspace_bytes(cache, scfg, nq, cfg.H_q), dtype=torch.uint8, device=dev)
+    wat = torch.empty(max(1, lsa.attend_workspace_bytes(Q, cfg.H_kv, cfg.k, cfg.window)), dtype=torch.uint8,
+                      device=dev)
 
     def step():
         append_kv(G, rows, newK, newV)
-        lsa.select(Q, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window, search=search, beam=cfg.beam, out=(lr, cnt))
-        lsa.sparse_attend(Q, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O)
+        lsa.select(Q, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window, search=search, beam=cfg.beam, out=(lr, cnt),
+                   workspace=wsel)
+        lsa.sparse_attend(Q, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O, workspace=wat)
 
     for _ in range(3):
         step()
     torch.cuda.synchronize()
-    n = 20
+    ms = graph_replay_ms(step, (lr, cnt, O), 20)
+    return dict(queries_per_s=nq / (ms / 1e3), ms_per_step=ms, timing="hip graph replay", batch=nq, search=search,
+                beam=cfg.beam, mean_lr=float(cnt.float().mean()))
+
+
+def graph_replay_ms(step, outs, n):
+    """Capture one decode step into a HIP graph, check that replays reproduce
+    the eager step's outputs exactly (with eager work and synchronisations in
+    between), and return the mean time of n back-to-back replays in ms."""
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay differs from the eager decode step")
+        step()
+        torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(n):
-        step()
+        g.replay()
     e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / n
-    return dict(queries_per_s=nq / (ms / 1e3), ms_per_step=ms, batch=nq, search=search, beam=cfg.beam,
-                mean_lr=float(cnt.float().mean()))
+    return s.elapsed_time(e) / n
 
 
 def run_decode(args):
@@ -319,12 +344,15 @@ def run_decode(args):
     lr = torch.empty(cfg.B, 1, cfg.H_kv, cfg.k, dtype=torch.int32, device=dev)
     cnt = torch.empty(cfg.B, 1, cfg.H_kv, dtype=torch.int32, device=dev)
     O = torch.empty_like(G["Q"])
+    wat = torch.empty(max(1, lsa.attend_workspace_bytes(G["Q"], cfg.H_kv, cfg.k, cfg.window)), dtype=torch.uint8,
+                      device=dev)
 
     def step():
         append_kv(G, rows, newK, newV)      # append the new token's key/value at row T
         lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window, workspace=wsel,
                    out=(lr, cnt))
-        lsa.sparse_attend(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O)
+        lsa.sparse_attend(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O,
+                          workspace=wat)
 
     for _ in range(5):
         step()
@@ -336,7 +364,8 @@ def run_decode(args):
         step()
     e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / n
+    ms_eager = s.elapsed_time(e) / n
+    ms = graph_replay_ms(step, (lr, cnt, O), n)
     # needle retrieved by every (sequence, KV head)?
     lr_c, cnt_c = lr.cpu(), cnt.cpu()
     found = sum(all(p + j in set(lr_c[b, 0, g, : cnt_c[b, 0, g]].tolist()) for j in range(4))
@@ -346,7 +375,8 @@ def run_decode(args):
     cent_bytes = cfg.B * cfg.H_kv * nl * 64 * 2
     gather = cfg.B * cfg.H_kv * (int(cnt_c.clamp_min(0).sum()) / (cfg.B * cfg.H_kv) + cfg.window + cfg.n_sinks) * 512
     alg = cent_bytes + gather
-    return dict(queries_per_s=cfg.B / (ms / 1e3), ms_per_step=ms, needle_found=f"{found}/{cfg.B * cfg.H_kv}",
+    return dict(queries_per_s=cfg.B / (ms / 1e3), ms_per_step=ms, ms_per_step_eager=ms_eager, timing="hip graph replay",
+                needle_found=f"{found}/{cfg.B * cfg.H_kv}",
                 alg_bytes_per_step=alg, hbm_frac=(alg / (ms / 1e3) / 1e9) / HBM_PEAK_GBS)
 
 

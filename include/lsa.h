@@ -126,7 +126,9 @@ typedef struct lsa_select_cfg {
 } lsa_select_cfg;
 
 /* Byte offsets of the cache regions, for inspection (tests, tools).  Per
- * (b, g): cent [leaves_max, 64] (dtype), sums [leaves_max, 64] fp32,
+ * (b, g): cent [leaves_max, 64] (dtype; in bf16 stored in tiles of 16
+ * buckets: element d of bucket x at (x/16)*1024 + ((d/8)%2)*512 +
+ * (x%16 + 16*(d/16))*8 + d%8, the scoring operand order), sums [leaves_max, 64] fp32,
  * meta [leaves_max] uint32 (bits 0-7 = entries in the bucket, bits 8-17 =
  * offset of its first member in the block's member list), members
  * [n_blocks_max, 512] uint16 (each block's entry indices grouped by bucket,

@@ -25,7 +25,7 @@ from ._lib import (LsaError, Layout, SelectCfg, CacheInfo, LSA_BF16, LSA_F32, LS
                    LSA_STRATEGY_AUTO, LSA_STRATEGY_FUSED, LSA_STRATEGY_MATERIALIZED)
 
 __all__ = ["build_buckets", "select", "sparse_attend", "LsaCache", "LsaError", "make_layout", "select_cfg",
-           "library_path"]
+           "library_path", "select_workspace_bytes", "attend_workspace_bytes"]
 
 _STRATEGIES = {"auto": LSA_STRATEGY_AUTO, "fused": LSA_STRATEGY_FUSED, "materialized": LSA_STRATEGY_MATERIALIZED}
 
@@ -85,9 +85,14 @@ class LsaCache:
         return raw.contiguous().view(dtype).view(self.batch, self.layout.n_kv_heads, *shape)
 
     def centroids(self) -> torch.Tensor:
+        """[B, H_kv, n_leaves, 64] leaf centroids (bf16 storage is tile-swizzled: undone here)."""
         i = self.info()
-        dt = torch.bfloat16 if self.layout.dtype == LSA_BF16 else torch.float32
-        return self._region(i.off_cent, i.stride_cent, i.n_leaves * 64, dt, (i.n_leaves, 64))
+        if self.layout.dtype != LSA_BF16:
+            return self._region(i.off_cent, i.stride_cent, i.n_leaves * 64, torch.float32, (i.n_leaves, 64))
+        nt = i.n_leaves // 16
+        raw = self._region(i.off_cent, i.stride_cent, i.n_leaves * 64, torch.bfloat16, (nt, 2, 4, 16, 8))
+        # stored (tile, m, h, r, e) -> bucket 16 tile + r, dim 16 h + 8 m + e
+        return raw.permute(0, 1, 2, 5, 4, 3, 6).reshape(self.batch, self.layout.n_kv_heads, i.n_leaves, 64)
 
     def sums(self) -> torch.Tensor:
         i = self.info()
@@ -177,6 +182,16 @@ def select(Q: torch.Tensor, cache: LsaCache, q_pos: torch.Tensor, W_q: torch.Ten
                             _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt), _ptr(workspace),
                             workspace.numel(), _stream(Q.device)))
     return lr_idx, lr_cnt
+
+
+def attend_workspace_bytes(Q: torch.Tensor, H_kv: int, k: int, window: int) -> int:
+    """Bytes of the split-key workspace sparse_attend needs for Q [B, n_q, H_q, d] (0: none)."""
+    B, n_q, H_q, d = Q.shape
+    layout = make_layout(d, H_kv, H_q, Q.dtype)
+    n = ctypes.c_size_t()
+    _lib.check(_lib.lib().lsa_attend_workspace_bytes(ctypes.byref(layout), ctypes.byref(select_cfg(k, 0, window)),
+                                                     B, n_q, ctypes.byref(n)))
+    return n.value
 
 
 def sparse_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torch.Tensor, lr_idx: torch.Tensor,

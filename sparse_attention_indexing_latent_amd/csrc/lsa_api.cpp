@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -154,13 +156,32 @@ lsa_status check_cfg(const lsa_select_cfg* C, int64_t T) {
 }
 
 struct SelectWs {
-    size_t off_qhat, off_tau, off_cnt, off_counters, off_cand, off_fb, off_scores, off_packed, total;
+    size_t off_qhat, off_tau, off_cnt, off_counters, off_cand, off_fb, off_scores, zero_off, zero_bytes, total;
     int64_t score_stride;
     int fb_slots;
     int strategy;
 };
 
 constexpr int kFallbackSlots = 256;
+
+// Split-key attention workspace: fp32 partials (max, denominator, d values
+// per split and head), then one 64-bit arrival word per unit.
+size_t attend_part_bytes(int64_t units, int splits, int G, int d) {
+    return align256((size_t)units * splits * G * (d + 2) * 4);
+}
+size_t attend_ws_bytes(int64_t units, int splits, int G, int d) {
+    return splits > 1 ? attend_part_bytes(units, splits, G, d) + align256((size_t)units * 8) : 0;
+}
+
+// Tag that tells one attention call's arrival words from another's: a
+// process-wide counter, started from the clock so that words left by another
+// process in reused memory are unlikely to carry a live tag; 0 is skipped.
+uint32_t next_call_tag() {
+    static std::atomic<uint32_t> tag{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
+    uint32_t t = tag.fetch_add(1, std::memory_order_relaxed);
+    if (t == 0) t = tag.fetch_add(1, std::memory_order_relaxed);
+    return t;
+}
 
 int resolve_strategy(const lsa_select_cfg* C, int64_t units) {
     if (C->search == LSA_SEARCH_TREE) return -1;
@@ -186,11 +207,9 @@ void select_ws(const lsa_layout* L, const lsa_select_cfg* C, int64_t B, int64_t 
         w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
         w.off_scores = o; o = align256(o + (size_t)w.fb_slots * w.score_stride * 4);
     } else if (w.strategy == LSA_STRATEGY_MATERIALIZED) {
-        w.off_cand = o; o = align256(o + (size_t)units * lsa::kCandCap * 8);
         w.off_fb = o;   o = align256(o + (size_t)units * 4);
         w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
         w.off_scores = o; o = align256(o + (size_t)units * w.score_stride * 4);
-        w.off_packed = o; o = align256(o + (size_t)units * w.score_stride * 4);
     }
     w.total = o;
 }
@@ -343,7 +362,6 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     sb.cand = reinterpret_cast<uint64_t*>(wb + w.off_cand);
     sb.fb_list = reinterpret_cast<int*>(wb + w.off_fb);
     sb.scores = reinterpret_cast<float*>(wb + w.off_scores);
-    sb.packed = reinterpret_cast<uint32_t*>(wb + w.off_packed);
     sb.score_stride = w.score_stride;
     sb.fb_slots = w.fb_slots;
     lsa::SelArgs sa;
@@ -359,7 +377,7 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t* lr = lr_idx ? lr_idx : lr_cnt;  // k == 0: rows are empty, never written
     hipError_t e = lsa::launch_qlatent(Q, W_q, bf16, layout->head_dim, batch * n_q * layout->n_q_heads, sb.qhat,
-                                       sb.counters, st);
+                                       sb.counters, wb + w.zero_off, w.zero_bytes, st);
     if (e == hipSuccess) {
         if (cfg->search == LSA_SEARCH_TREE)
             e = lsa::launch_select_tree(v, bf16, q_pos, sa, sb, lr, lr_cnt, st);
@@ -379,9 +397,8 @@ lsa_status lsa_attend_workspace_bytes(const lsa_layout* layout, const lsa_select
     if (!cfg || !bytes) return fail(LSA_ERR_INVALID_ARG, "cfg and bytes must be non-NULL");
     if (batch < 0 || n_q < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
     const int64_t units = batch * n_q * layout->n_kv_heads;
-    const int splits = lsa::attend_splits(units, cfg->window, cfg->k);
-    const int G = layout->n_q_heads / layout->n_kv_heads;
-    *bytes = splits > 1 ? align256((size_t)units * splits * G * (layout->head_dim + 2) * 4) : 0;
+    *bytes = attend_ws_bytes(units, lsa::attend_splits(units, cfg->window, cfg->k),
+                             layout->n_q_heads / layout->n_kv_heads, layout->head_dim);
     return ok();
 }
 
@@ -405,7 +422,7 @@ lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg
         return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
     const int splits = lsa::attend_splits(units, cfg->window, cfg->k);
     const int G = layout->n_q_heads / layout->n_kv_heads;
-    const size_t need = splits > 1 ? align256((size_t)units * splits * G * (layout->head_dim + 2) * 4) : 0;
+    const size_t need = attend_ws_bytes(units, splits, G, layout->head_dim);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(LSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     if (need > 0 && misaligned(workspace)) return fail(LSA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -423,6 +440,10 @@ lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg
     aa.k = cfg->k;
     aa.splits = splits;
     aa.scale = scale;
+    aa.arrive = need > 0 ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) +
+                                                                 attend_part_bytes(units, splits, G, layout->head_dim))
+                         : nullptr;
+    aa.tag = next_call_tag();
     hipError_t e = lsa::launch_attend(Q, K, V, q_pos, lr_idx ? lr_idx : lr_cnt, lr_cnt, aa, layout->head_dim,
                                       layout->dtype == LSA_BF16, O, static_cast<float*>(workspace),
                                       static_cast<hipStream_t>(stream));

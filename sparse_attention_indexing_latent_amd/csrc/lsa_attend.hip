@@ -81,6 +81,90 @@ __device__ __forceinline__ int32_t tok_of(const KeyList& kl, int64_t jr, int64_t
     return (tk >= 0 && tk <= t) ? (int32_t)tk : -1;
 }
 
+// Log-sum-exp combine of the split partials of one unit (all G heads), by
+// one wave.  Lane s (< splits <= 64) holds split s's max and denominator of
+// every head; lane l then sums dims 2l, 2l + 1 over the splits, the loads of
+// 16 splits in flight at once (the partials come from other waves, so they
+// are read with coherent loads).
+__device__ __forceinline__ void combine_unit(const float* __restrict__ part, const AttArgs& aa, int D, int out_bf16,
+                                             void* O, int64_t u) {
+    const int l = lane_id();
+    const int G = aa.G, S = aa.splits;
+    const int64_t rec = D + 2;   // floats per (split, head): max, denominator, D values
+    const float* base = part + u * (int64_t)S * G * rec;
+    uint64_t ml[kMaxGroup];
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh)
+        ml[hh] = (hh < G && l < S) ? load_coherent_u64(base + ((int64_t)l * G + hh) * rec)
+                                   : pack_f32x2(kNegInf, 0.f);
+    const int64_t g = u % aa.H_kv, bi = u / aa.H_kv;
+    const bool active = 2 * l < D;
+    for (int hh = 0; hh < G; ++hh) {
+        const float ms = __uint_as_float((uint32_t)ml[hh]), ls = __uint_as_float((uint32_t)(ml[hh] >> 32));
+        const float m = wave_max(ms);
+        const float e = ms > kNegInf ? __expf(ms - m) : 0.f;
+        const float lsum = wave_sum(ls * e);
+        float o0 = 0.f, o1 = 0.f;
+        for (int s0 = 0; s0 < S; s0 += 16) {
+            uint64_t v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                v[j] = (s0 + j < S && active) ? load_coherent_u64(base + ((int64_t)(s0 + j) * G + hh) * rec + 2 + 2 * l)
+                                              : 0ull;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float es = __shfl(e, (s0 + j) & 63);
+                if (s0 + j < S && es != 0.f) {   // a split that saw no key holds no partial output
+                    o0 += __uint_as_float((uint32_t)v[j]) * es;
+                    o1 += __uint_as_float((uint32_t)(v[j] >> 32)) * es;
+                }
+            }
+        }
+        const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+        const int64_t orow = (bi * aa.H_q + g * G + hh) * D;
+        if (active) {
+            if (out_bf16) {
+                uint16_t* o = reinterpret_cast<uint16_t*>(O);
+                *reinterpret_cast<uint32_t*>(o + orow + 2 * l) =
+                    (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
+            } else {
+                float* o = reinterpret_cast<float*>(O);
+                *reinterpret_cast<uint64_t*>(o + orow + 2 * l) = pack_f32x2(o0 * inv, o1 * inv);
+            }
+        }
+    }
+}
+
+// Arrival of one split of a unit: returns true for the split that arrives
+// last.  The word holds (call tag << 32 | splits arrived so far); a word
+// carrying another call's tag counts as zero arrivals, and the last arrival
+// leaves (tag, 0), so every call leaves the words ready for the next one.
+// The CAS loop retries only while other splits update the word at the same
+// moment, so it ends after at most `splits` attempts.
+__device__ __forceinline__ bool split_arrive(unsigned long long* word, uint32_t tag, int splits) {
+    unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (true) {
+        const uint32_t seen = (uint32_t)(cur >> 32) == tag ? (uint32_t)cur : 0u;
+        const uint32_t now = seen + 1u;
+        const unsigned long long nv = ((unsigned long long)tag << 32) | (now == (uint32_t)splits ? 0u : now);
+        if (__hip_atomic_compare_exchange_strong(word, &cur, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return now == (uint32_t)splits;
+    }
+}
+
+// After a split wave has written its partials (coherent stores): the last
+// split of the unit combines all of the unit's heads.
+__device__ __forceinline__ void finish_split(const AttArgs& aa, const float* part, int D, int out_bf16, void* O,
+                                             int64_t u) {
+    wait_all_memory();   // this wave's partials are complete before it arrives
+    int last = 0;
+    if (lane_id() == 0) last = split_arrive(aa.arrive + u, aa.tag, aa.splits) ? 1 : 0;
+    last = __shfl(last, 0);
+    if (!last) return;
+    combine_unit(part, aa, D, out_bf16, O, u);
+}
+
 // Lane (r, h) loads head dims [D/4 h, D/4 h + D/4) of the key and value rows.
 template <int D>
 __device__ __forceinline__ void load_rows(const uint16_t* Kbg, const uint16_t* Vbg, int32_t tk, int h, uint4* kr,
@@ -179,7 +263,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int s = (int)(w_id % aa.splits);
     const AUnit un = aunit_of(uu, aa);
     const int64_t t = q_pos[un.b * aa.n_q + un.i];
-    const int32_t cnt = lr_cnt[un.u];
+    // a count above k (never written by the selection) is clamped: the list row holds k entries
+    const int32_t cnt = min(lr_cnt[un.u], aa.k);
     const int n = r;  // head column of the C layouts
     const int64_t orow = ((un.b * aa.n_q + un.i) * aa.H_q + un.g * aa.G + n) * D;
 
@@ -256,16 +341,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 *reinterpret_cast<uint4*>(O + orow + DPL * h + 8 * q4) =
                     uint4{w[4 * q4], w[4 * q4 + 1], w[4 * q4 + 2], w[4 * q4 + 3]};
         }
-    } else if (n < aa.G) {
-        float* pp = part + ((un.u * aa.splits + s) * aa.G + n) * (D + 2);
-        if (h == 0) {
-            pp[0] = m_run;
-            pp[1] = l_run;
+    } else {
+        if (n < aa.G) {
+            float* pp = part + ((un.u * aa.splits + s) * aa.G + n) * (D + 2);
+            if (h == 0) store_coherent_u64(pp, pack_f32x2(m_run, l_run));
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                store_coherent_u64(pp + 2 + DPL * h + 4 * c, pack_f32x2(acc[c][0], acc[c][1]));
+                store_coherent_u64(pp + 4 + DPL * h + 4 * c, pack_f32x2(acc[c][2], acc[c][3]));
+            }
         }
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) pp[2 + DPL * h + 4 * c + v] = acc[c][v];
+        finish_split(aa, part, D, 1, O, un.u);
     }
 }
 
@@ -289,7 +375,8 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const float* __restrict
     const int s = (int)(w_id % aa.splits);
     const AUnit un = aunit_of(uu, aa);
     const int64_t t = q_pos[un.b * aa.n_q + un.i];
-    const int32_t cnt = lr_cnt[un.u];
+    // a count above k (never written by the selection) is clamped: the list row holds k entries
+    const int32_t cnt = min(lr_cnt[un.u], aa.k);
     const int G = aa.G;
     const int64_t qrow0 = ((un.b * aa.n_q + un.i) * aa.H_q + un.g * G) * D;
     float m_run[kMaxGroup], l_run[kMaxGroup], acc[kMaxGroup][2];
@@ -358,63 +445,24 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const float* __restrict
             if (l + 64 < D) O[qrow0 + (int64_t)hh * D + l + 64] = acc[hh][1] * inv;
         } else {
             float* pp = part + ((un.u * aa.splits + s) * G + hh) * (D + 2);
-            if (l == 0) {
-                pp[0] = m_run[hh];
-                pp[1] = l_run[hh];
-            }
-            if (l < D) pp[2 + l] = acc[hh][0];
-            if (l + 64 < D) pp[2 + l + 64] = acc[hh][1];
+            if (l == 0) store_coherent_u64(pp, pack_f32x2(m_run[hh], l_run[hh]));
+            if (l < D) store_coherent_u32(pp + 2 + l, __float_as_uint(acc[hh][0]));
+            if (l + 64 < D) store_coherent_u32(pp + 2 + l + 64, __float_as_uint(acc[hh][1]));
         }
     }
-}
-
-// Log-sum-exp combine of the split partials: one wave per (unit, head).
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, AttArgs aa, int D, int out_bf16,
-                                                      void* O) {
-    const int l = lane_id(), wid = threadIdx.x >> 6;
-    const int64_t w_id = (int64_t)blockIdx.x * 4 + wid;
-    if (w_id >= aa.n_units * aa.G) return;
-    const int64_t u = w_id / aa.G;
-    const int hh = (int)(w_id % aa.G);
-    // split s of this (unit, head) starts at p0 + s * ss; lane s holds its max and denominator (splits <= 64)
-    const int64_t ss = (int64_t)aa.G * (D + 2);
-    const float* p0 = part + (u * aa.splits * aa.G + hh) * (D + 2);
-    const float ms = l < aa.splits ? p0[l * ss] : kNegInf;
-    const float ls = l < aa.splits ? p0[l * ss + 1] : 0.f;
-    const float m = wave_max(ms);
-    const float e = ms > kNegInf ? __expf(ms - m) : 0.f;
-    const float lsum = wave_sum(ls * e);
-    float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < aa.splits; ++s) {
-        const float es = __shfl(e, s);
-        const float* pp = p0 + s * ss + 2;
-        const float v0 = l < D ? pp[l] : 0.f, v1 = l + 64 < D ? pp[l + 64] : 0.f;
-        o0 += es != 0.f ? v0 * es : 0.f;   // a split that saw no key holds no partial output
-        o1 += es != 0.f ? v1 * es : 0.f;
-    }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    const int64_t g = u % aa.H_kv;
-    const int64_t bi = u / aa.H_kv;
-    const int64_t orow = (bi * aa.H_q + g * aa.G + hh) * D;
-    if (out_bf16) {
-        uint16_t* o = reinterpret_cast<uint16_t*>(O);
-        if (l < D) o[orow + l] = f32_to_bf16(o0 * inv);
-        if (l + 64 < D) o[orow + l + 64] = f32_to_bf16(o1 * inv);
-    } else {
-        float* o = reinterpret_cast<float*>(O);
-        if (l < D) o[orow + l] = o0 * inv;
-        if (l + 64 < D) o[orow + l + 64] = o1 * inv;
-    }
+    if (aa.splits > 1) finish_split(aa, part, D, 0, O, un.u);
 }
 
 }  // namespace
 
+// Key-list splits per (query, KV head): few units are spread over about one
+// wave per SIMD (1024 SIMDs), at least 128 keys each; more splits cost more
+// in arrivals and combining than they gain in parallel gathers.
 int attend_splits(int64_t n_units, int window, int k) {
-    if (n_units >= 8192) return 1;
+    if (n_units >= 1024) return 1;
     const int64_t keys = (int64_t)window + kBlockTokens + k + 64;
-    int64_t want = (8192 + n_units - 1) / n_units;
-    const int64_t maxs = (keys + 255) / 256;
+    int64_t want = 1024 / n_units;
+    const int64_t maxs = (keys + 127) / 128;
     if (want > maxs) want = maxs;
     if (want < 1) want = 1;
     if (want > 64) want = 64;
@@ -443,10 +491,6 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V, const int6
                            static_cast<const float*>(K), static_cast<const float*>(V), q_pos, lr_idx, lr_cnt, aa, D,
                            static_cast<float*>(O), part, nwg);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || aa.splits == 1) return e;
-    const int64_t cw = aa.n_units * aa.G;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((cw + 3) / 4)), dim3(256), 0, st, part, aa, D, bf16 ? 1 : 0, O);
     return hipGetLastError();
 }
 

@@ -254,10 +254,20 @@ __global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restric
             ss = fmaf(mu[c], mu[c], ss);
         }
         const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-        if (cv.bf16) {
-            uint16_t* crow = reinterpret_cast<uint16_t*>(cv.cent) + bg * cv.s_cent + leaf * kLatent;
+        if (cv.bf16) {   // tile-swizzled: eight 16-byte words (h, m) of 8 consecutive dims
+            uint4* cw = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(cv.cent) + bg * cv.s_cent);
 #pragma unroll
-            for (int c = 0; c < kLatent; ++c) crow[c] = f32_to_bf16(mu[c] * inv);
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int c = 16 * h + 8 * m;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = (uint32_t)f32_to_bf16(mu[c + 2 * e] * inv) |
+                               ((uint32_t)f32_to_bf16(mu[c + 2 * e + 1] * inv) << 16);
+                    cw[cent_tile_word(leaf, h, m)] = uint4{w[0], w[1], w[2], w[3]};
+                }
         } else {
             float* crow = reinterpret_cast<float*>(cv.cent) + bg * cv.s_cent + leaf * kLatent;
 #pragma unroll

@@ -43,6 +43,17 @@ struct CacheView {
     int32_t bf16;          // centroid storage dtype
 };
 
+// bf16 leaf centroids are stored in tiles of 16 buckets (2 KB, 1024
+// elements) in the operand order of the scoring MFMA: element dim of bucket
+// `leaf` sits at tile * 1024 + m * 512 + (r + 16 h) * 8 + e, with r = leaf %
+// 16, h = dim / 16, m = (dim / 8) % 2, e = dim % 8.  Lane l = r + 16 h of a
+// wave then reads its two 8-element k-steps of a tile as the 16-byte words
+// l and 64 + l, so each load instruction covers 1 KB contiguously.
+// (fp32 centroids and the tree levels above the leaves stay row-major.)
+__device__ __forceinline__ int64_t cent_tile_word(int64_t leaf, int h, int m) {
+    return (leaf >> 4) * 128 + m * 64 + (leaf & 15) + 16 * h;   // 16-byte word index
+}
+
 // Tree level l >= 1 holds ceil(n_leaves / 2^l) nodes (pairing (2j, 2j+1) level
 // by level); levels are stored one after the other from level 1.
 __device__ __forceinline__ int64_t tree_level_size(int64_t n_leaves, int lev) {
@@ -135,6 +146,39 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
         if (l >= o) v += w;
     }
     return v;
+}
+
+// ---------------------------------------------------------------- device-coherent accesses
+// Data one workgroup hands to another within a kernel goes through relaxed
+// agent-scope atomic stores and loads: on gfx950 they carry the system-
+// coherence bit, so they are visible across the XCDs' separate L2 caches
+// without the full L2 write-back and invalidate that an agent-scope fence
+// costs.  The writer waits for its stores to complete (s_waitcnt) before the
+// atomic that signals the reader; the reader's loads issue after it has seen
+// that atomic.
+__device__ __forceinline__ void store_coherent_u64(void* p, uint64_t v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent_u32(void* p, uint32_t v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent_u64(const void* p) {
+    return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent_u32(const void* p) {
+    return __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent_f32(const float* p) { return __uint_as_float(load_coherent_u32(p)); }
+__device__ __forceinline__ uint64_t pack_f32x2(float a, float b) {
+    return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+}
+// Wait until every memory access this wave issued has completed.
+__device__ __forceinline__ void wait_all_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // ---------------------------------------------------------------- query geometry

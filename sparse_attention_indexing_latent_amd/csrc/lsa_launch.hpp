@@ -28,7 +28,6 @@ struct SelectBuffers {
     int* fb_list;
     int* counters;
     float* scores;
-    uint32_t* packed;      // materialised path: thr_key << 7 | eligible tokens, per leaf
     int64_t score_stride;
     int fb_slots;
 };
@@ -41,6 +40,8 @@ struct AttArgs {
     int32_t n_sinks, window, n_blocks, k;
     int32_t splits;
     float scale;
+    unsigned long long* arrive;   // splits > 1: per-unit arrival words (tag << 32 | count)
+    uint32_t tag;                 // distinct per call
 };
 
 hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
@@ -48,7 +49,7 @@ hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t
 hipError_t launch_tree(const CacheView& cv, const int64_t* level_off, const int64_t* level_size, int B, int H_kv,
                        hipStream_t st);
 hipError_t launch_qlatent(const void* Q, const void* W, bool bf16, int d, int64_t rows, void* qhat, int* counters,
-                          hipStream_t st);
+                          void* zero, size_t zero_bytes, hipStream_t st);
 hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa, int B,
                                const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, hipStream_t st);
 hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa,

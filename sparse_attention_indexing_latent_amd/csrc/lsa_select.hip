@@ -54,14 +54,23 @@ __device__ __forceinline__ Unit unit_of(int64_t u, const SelArgs& sa) {
     return r;
 }
 
+// Grid-stride clear of zero_n 16-byte words (the per-call counters and
+// histograms of the materialised path; a kernel rather than a memset node).
+__device__ __forceinline__ void clear_words(uint4* zero, int64_t zero_n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < zero_n; i += (int64_t)gridDim.x * blockDim.x)
+        zero[i] = uint4{0u, 0u, 0u, 0u};
+}
+
 // ------------------------------------------------------------------ q latent
 // q_hat = round(normalise(q W)) per (b, i, h) row; one wave handles 4 rows,
 // lane c produces latent coordinate c.
 template <typename TIN>
 __global__ __launch_bounds__(256) void qlatent_kernel(const TIN* __restrict__ Q, const TIN* __restrict__ W, int d,
-                                                      int64_t rows, void* qhat, int out_bf16, int* counters) {
+                                                      int64_t rows, void* qhat, int out_bf16, int* counters,
+                                                      uint4* zero, int64_t zero_n) {
     __shared__ float Wsh[128 * kLatent];
     if (blockIdx.x == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0;
+    clear_words(zero, zero_n);
     for (int i = threadIdx.x; i < d * kLatent; i += 256) Wsh[i] = load_f32(W + i);
     __syncthreads();
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -99,9 +108,11 @@ __global__ __launch_bounds__(256) void qlatent_kernel(const TIN* __restrict__ Q,
 template <int D>
 __global__ __launch_bounds__(256) void qlatent_bf16_kernel(const uint16_t* __restrict__ Q,
                                                            const uint16_t* __restrict__ W, int64_t rows,
-                                                           uint16_t* __restrict__ qhat, int* counters) {
+                                                           uint16_t* __restrict__ qhat, int* counters,
+                                                           uint4* zero, int64_t zero_n) {
     constexpr int DPL = D / 4, KS = DPL / 8;
     if (blockIdx.x == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0;
+    clear_words(zero, zero_n);
     const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4;
     bf16x8 wf[4][KS];
 #pragma unroll
@@ -174,9 +185,9 @@ __device__ __forceinline__ void load_qfrag_bf16(QFragBF16& qf, const uint16_t* q
 }
 
 __device__ __forceinline__ f32x4 score_tile_bf16(const uint16_t* cent_bg, int64_t x0, const QFragBF16& qf, int G) {
-    const int l = lane_id(), r = l & 15, h = l >> 4;
-    const uint4* p = reinterpret_cast<const uint4*>(cent_bg + (x0 + r) * kLatent + 16 * h);
-    const bf16x8 a0 = as_bf16x8(p[0]), a1 = as_bf16x8(p[1]);
+    const int l = lane_id();
+    const uint4* p = reinterpret_cast<const uint4*>(cent_bg) + (x0 >> 4) * 128 + l;   // tile-swizzled storage
+    const bf16x8 a0 = as_bf16x8(p[0]), a1 = as_bf16x8(p[64]);
     f32x4 best = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int hh = 0; hh < kMaxGroup; ++hh) {
@@ -232,11 +243,13 @@ __device__ __forceinline__ f32x4 score_tile_f32(const float* cent_bg, int64_t x0
 constexpr int kPerLeafMaxLeaves = 96 * kLeavesPerBlock;
 constexpr int kHistStride = 257;   // padded: neighbouring queries fall in different banks
 
+// The A fragments of the tile of buckets x0..x0+15 (x0 a multiple of 16):
+// lane (r, h) gets dims [16h, 16h+8) and [16h+8, 16h+16) of bucket x0 + r,
+// one contiguous 1 KB read per fragment (tile-swizzled storage).
 __device__ __forceinline__ void load_cent_bf16(const uint16_t* cent_bg, int64_t x0, uint4& a0, uint4& a1) {
-    const int l = lane_id(), r = l & 15, h = l >> 4;
-    const uint4* p = reinterpret_cast<const uint4*>(cent_bg + (x0 + r) * kLatent + 16 * h);
+    const uint4* p = reinterpret_cast<const uint4*>(cent_bg) + (x0 >> 4) * 128 + lane_id();
     a0 = p[0];
-    a1 = p[1];
+    a1 = p[64];
 }
 
 __device__ __forceinline__ f32x4 mfma_tile_bf16(uint4 u0, uint4 u1, const QFragBF16& qf, int G) {
@@ -813,7 +826,30 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
     if (l == 0) lr_cnt[u] = got;
 }
 
-// ------------------------------------------------------------------ threshold over materialised scores
+// ------------------------------------------------------------------ materialised path
+// Few queries against many buckets (decode).  Two kernels:
+//
+// score_all_kernel, grid (units x splits), unit-major: every visible bucket
+// score of a (query, KV head), written to the workspace (fp32).  A pure
+// stream over the tile-swizzled centroids, up to 128 tiles per workgroup.
+//
+// score_select_kernel, one 1024-thread workgroup per unit, records held in
+// registers: packed record = offset key << 7 | eligible tokens per bucket
+// (the key is monotone in the score).  Finds a key bound L such that the
+// buckets keyed >= L hold at least k eligible tokens while those above L's
+// bin hold fewer, with at most kCandCap buckets at or above L (weighted
+// histograms of 3072, 2048 and 4 bins, each refining the boundary bin of the
+// one before), collects those buckets, and wave 0 ranks them by (score
+// desc, id asc), walks them to k tokens and expands.  Every bucket keyed
+// below L ranks after every collected one, so the walk ends exactly where a
+// walk over all buckets would.  Too many ties at L send the unit to the
+// exact radix path.
+constexpr int kScoreTiles = 128;  // tiles (16 buckets each) per scoring workgroup
+constexpr int kThrThreads = 1024;
+constexpr int kThrBins = 3072;    // level 0: key >> 13
+constexpr int kThrGoal = 128;     // refine the bound while more buckets than this sit at or above it
+constexpr int kThrRegs = 32;      // buckets per thread held in registers (one chunk = 32768 buckets)
+
 // Offset key of a score: monotone non-decreasing in the score and in
 // [0, 3 * 2^23) (s + 2 clamped to [0.5, 4)).  Equal keys need not mean equal
 // scores, so the key only bounds the candidate set; ranking uses the score.
@@ -822,14 +858,18 @@ __device__ __forceinline__ uint32_t thr_key(float s) {
     return __float_as_uint(v) - 0x3F000000u;
 }
 
-// Packed leaf record of the materialised path: thr_key(score) << 7 | eligible
-// tokens of the leaf (<= 64).  m is the leaf's meta word.  Leaves of a block
-// that straddles an edge of [sink_end, l0) get weight 0 here and are patched
-// afterwards from their member lists (patch_straddling).
-__device__ __forceinline__ uint32_t pack_leaf(uint32_t x, uint32_t m, float score, const Geom& q) {
-    const int64_t lo = (int64_t)(x / kLeavesPerBlock) * kBlockTokens;
-    const int w = (lo >= q.sink_end && lo + kBlockTokens <= q.l0) ? kPool * (int)(m & 0xFFu) : 0;
-    return (thr_key(score) << 7) | (uint32_t)w;
+__device__ __forceinline__ unsigned long long shfl_down_u64(unsigned long long v, int o) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl_down(lo, o);
+    hi = __shfl_down(hi, o);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Eligible tokens of a bucket whose block lies inside or outside [sink_end,
+// l0); a block straddling an edge (at most two) needs its member lists.
+__device__ __forceinline__ int leaf_weight_whole(uint32_t leaf, uint32_t m, const Geom& q) {
+    const int64_t lo = (int64_t)(leaf / kLeavesPerBlock) * kBlockTokens;
+    return (lo >= q.sink_end && lo + kBlockTokens <= q.l0) ? kPool * (int)(m & 0xFFu) : 0;
 }
 
 // The (at most two) blocks that straddle an edge of [sink_end, l0).
@@ -839,41 +879,30 @@ __device__ __forceinline__ void straddling_blocks(const Geom& q, int& b0, int& b
     if (b1 == b0) b1 = -1;
 }
 
-// ------------------------------------------------------------------ materialised scores
-// grid (n_units, splits): all visible bucket scores of one (query, KV head).
+// Needs no ranking: invalid position, k = 0, or k covering every eligible token.
+__device__ __forceinline__ bool unit_is_trivial(int64_t t, const Geom& q, int k) {
+    const int64_t total = q.l0 > q.sink_end ? q.l0 - q.sink_end : 0;
+    return t < 0 || k == 0 || (int64_t)k >= total;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void* __restrict__ qhat,
-                                                        const int64_t* __restrict__ q_pos, SelArgs sa,
-                                                        float* __restrict__ scores, uint32_t* __restrict__ packed,
-                                                        int64_t score_stride) {
+                                                        const int64_t* __restrict__ q_pos, SelArgs sa, int splits,
+                                                        float* __restrict__ scores, int64_t score_stride) {
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
-    const int64_t u = blockIdx.x;
+    const int64_t u = (int64_t)blockIdx.x / splits;
+    const int split = (int)((int64_t)blockIdx.x % splits);
     const Unit un = unit_of(u, sa);
     const int64_t t = q_pos[un.b * sa.n_q + un.i];
-    if (t < 0) return;
-    const Geom q = query_geom(t, cv.n_blocks, sa.n_sinks, sa.window);
-    const int NLv = kLeavesPerBlock * q.nvis;
-    const int ntiles = NLv / 16;
-    const int per = (ntiles + gridDim.y - 1) / gridDim.y;
-    const int t0 = blockIdx.y * per, t1 = min(ntiles, t0 + per);
+    const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
+    if (unit_is_trivial(t, q, sa.k)) return;
+    const int ntiles = kLeavesPerBlock * q.nvis / 16;
+    const int t0 = split * kScoreTiles, t1 = min(ntiles, t0 + kScoreTiles);
+    const int w0 = t0 + (kScoreTiles / 4) * wid, w1 = min(t1, w0 + kScoreTiles / 4);   // this wave's tiles
+    if (w0 >= w1) return;
     const int64_t bg = un.b * sa.H_kv + un.g;
     const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
-    const float* qf32 = reinterpret_cast<const float*>(qhat) + qrow;
     float* sc = scores + u * score_stride;
-    uint32_t* pk = packed + u * score_stride;
-    const uint32_t* meta = cv.meta + bg * cv.s_meta;
-    // lanes n == 0 hold the scores of leaves x0 + 4h .. x0 + 4h + 3; they
-    // write them and the packed records (key, eligible tokens)
-    auto emit = [&](int64_t x0, const f32x4& vals, const uint4& m4) {
-        *reinterpret_cast<f32x4*>(sc + x0 + 4 * h) = vals;
-        const uint32_t xb = (uint32_t)(x0 + 4 * h);
-        uint4 r;
-        r.x = pack_leaf(xb, m4.x, vals[0], q);
-        r.y = pack_leaf(xb + 1, m4.y, vals[1], q);
-        r.z = pack_leaf(xb + 2, m4.z, vals[2], q);
-        r.w = pack_leaf(xb + 3, m4.w, vals[3], q);
-        *reinterpret_cast<uint4*>(pk + xb) = r;
-    };
     if constexpr (BF16) {
         // B operand: query head n of the group in column n (zero columns past G);
         // the group max is taken across the 16 lanes of each row group
@@ -885,151 +914,149 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
             qc = p[1];
         }
         const bf16x8 q0 = as_bf16x8(qa), q1 = as_bf16x8(qc);
-        // each wave takes 4 consecutive tiles and has all their loads in flight before the MFMAs
         const uint16_t* cb = reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent;
-        for (int tt0 = t0 + 4 * wid; tt0 < t1; tt0 += 16) {
-            uint4 a[4][2], m4[4];
+        // batches of TPI tiles; the next batch's loads are in flight while one is scored
+        // (loads are unconditional, past the last tile they repeat it, so they stay in flight together)
+        constexpr int TPI = 4;
+        uint4 a[2][TPI][2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (tt0 + j < t1) {
-                    load_cent_bf16(cb, (int64_t)(tt0 + j) * 16, a[j][0], a[j][1]);
-                    m4[j] = n == 0 ? *reinterpret_cast<const uint4*>(meta + (int64_t)(tt0 + j) * 16 + 4 * h)
-                                   : uint4{0, 0, 0, 0};
-                }
-            }
+        for (int j = 0; j < TPI; ++j)
+            load_cent_bf16(cb, (int64_t)min(w0 + j, w1 - 1) * 16, a[0][j][0], a[0][j][1]);
+        for (int tt0 = w0; tt0 < w1; tt0 += 2 * TPI) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (tt0 + j < t1) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j][0]), q0, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[j][1]), q1, acc, 0, 0, 0);
-                    f32x4 vals;
+            for (int half = 0; half < 2; ++half) {
+                const int tb = tt0 + half * TPI;
+                if (tb >= w1) break;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float x = n < sa.G ? acc[v] : kNegInf;
-                        x = fmaxf(x, __shfl_xor(x, 1));
-                        x = fmaxf(x, __shfl_xor(x, 2));
-                        x = fmaxf(x, __shfl_xor(x, 4));
-                        x = fmaxf(x, __shfl_xor(x, 8));
-                        vals[v] = x;
+                for (int j = 0; j < TPI; ++j)
+                    load_cent_bf16(cb, (int64_t)min(tb + TPI + j, w1 - 1) * 16, a[half ^ 1][j][0], a[half ^ 1][j][1]);
+#pragma unroll
+                for (int j = 0; j < TPI; ++j) {
+                    if (tb + j < w1) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[half][j][0]), q0, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[half][j][1]), q1, acc, 0, 0, 0);
+                        f32x4 vals;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            float x = n < sa.G ? acc[v] : kNegInf;
+                            x = fmaxf(x, __shfl_xor(x, 1));
+                            x = fmaxf(x, __shfl_xor(x, 2));
+                            x = fmaxf(x, __shfl_xor(x, 4));
+                            x = fmaxf(x, __shfl_xor(x, 8));
+                            vals[v] = x;
+                        }
+                        if (n == 0) *reinterpret_cast<f32x4*>(sc + (int64_t)(tb + j) * 16 + 4 * h) = vals;
                     }
-                    if (n == 0) emit((int64_t)(tt0 + j) * 16, vals, m4[j]);
                 }
             }
         }
     } else {
-        for (int tt = t0 + wid; tt < t1; tt += 4) {
+        const float* qf32 = reinterpret_cast<const float*>(qhat) + qrow;
+        for (int tt = w0; tt < w1; ++tt) {
             const int64_t x0 = (int64_t)tt * 16;
             const f32x4 vals =
                 score_tile_f32(reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent, x0, qf32, n == 0, sa.G);
-            if (n == 0) emit(x0, vals, *reinterpret_cast<const uint4*>(meta + x0 + 4 * h));
-        }
-    }
-    // patch the straddling blocks' leaves of this workgroup's range
-    int sb0, sb1;
-    straddling_blocks(q, sb0, sb1);
-    if (sb0 < 0 && sb1 < 0) return;
-    __syncthreads();   // this workgroup's score writes are visible to all its threads
-    if (threadIdx.x < 2 * kLeavesPerBlock) {
-        const int blk = threadIdx.x < kLeavesPerBlock ? sb0 : sb1;
-        const int64_t x = (int64_t)blk * kLeavesPerBlock + threadIdx.x % kLeavesPerBlock;
-        if (blk >= 0 && x >= (int64_t)t0 * 16 && x < (int64_t)t1 * 16) {
-            const int w = leaf_weight(cv, bg, (uint32_t)x, q);
-            pk[x] = (thr_key(sc[x]) << 7) | (uint32_t)w;
+            if (n == 0) *reinterpret_cast<f32x4*>(sc + x0 + 4 * h) = vals;
         }
     }
 }
 
-constexpr int kThrThreads = 1024;
-constexpr int kThrBins = 3072;   // level 0: key >> 13
-constexpr int kThrGoal = 128;    // refine the bound while more leaves than this sit at or above it
-constexpr int kThrRegs = 32;     // leaves per thread held in registers (one chunk = 32768 leaves)
-
-__device__ __forceinline__ unsigned long long shfl_down_u64(unsigned long long v, int o) {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_down(lo, o);
-    hi = __shfl_down(hi, o);
-    return ((unsigned long long)hi << 32) | lo;
-}
-
-// One workgroup per (query, KV head), over the packed records of its visible
-// leaves.  Finds a key bound L such that the leaves with key >= L hold at
-// least k eligible tokens while those with key above L's bin hold fewer, with
-// at most kCandCap leaves at or above L (weighted histograms of 3072, 2048 and
-// 4 bins, each refining the boundary bin of the one before); writes those
-// leaves' rank keys to cand in any order and their count to cnt.  A lower key
-// means a lower score, so every leaf below L ranks after every candidate, and
-// the walk in rank order ends among the candidates exactly where a walk over
-// all leaves ends.
-__global__ __launch_bounds__(kThrThreads) void threshold_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
-                                                                 SelArgs sa, const float* __restrict__ scores,
-                                                                 const uint32_t* __restrict__ packed,
-                                                                 int64_t score_stride, int* __restrict__ cnt,
-                                                                 uint64_t* __restrict__ cand) {
-    __shared__ unsigned long long hist[kThrBins];   // count << 32 | weight
+template <bool BF16>
+__global__ __launch_bounds__(kThrThreads) void score_select_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
+                                                                    SelArgs sa, const float* __restrict__ scores,
+                                                                    int64_t score_stride, int* fb_list, int* counters,
+                                                                    int32_t* lr_idx, int32_t* lr_cnt) {
+    // LDS (153 KB): the packed records of up to 32768 buckets, the histogram
+    // (count << 32 | weight), and small scratch.  Once the candidates are
+    // collected, the record space holds the ranking scratch and the tokens.
+    __shared__ __align__(16) uint32_t rec[kThrRegs * kThrThreads];
+    __shared__ unsigned long long hist[kThrBins];
     __shared__ unsigned long long wtot[kThrThreads / 64];
     __shared__ uint32_t bc[4];
-    __shared__ int ncand;
-    __shared__ uint32_t cid[kCandCap];
+    __shared__ int ncand, fin[3];
+    __shared__ int tk[2 * kLeavesPerBlock];   // eligible tokens of the straddling blocks' buckets
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
     const int64_t u = blockIdx.x;
     const Unit un = unit_of(u, sa);
-    const float* sc = scores + u * score_stride;
-    const uint32_t* pk = packed + u * score_stride;
-    // Records are handled in chunks of kThrRegs per thread, held in registers;
-    // with a single chunk its loads are issued before the query position is
-    // known (rows are written up to the visible leaves, read up to n_leaves
-    // and masked) and it stays resident.
-    constexpr int kChunk = kThrRegs * kThrThreads;
-    uint32_t rv[kThrRegs];
-#define LSA_THR_LOAD(c0, lim)                                   \
-    _Pragma("unroll") for (int j = 0; j < kThrRegs; ++j) {      \
-        const int x = (c0) + j * kThrThreads + tid;             \
-        rv[j] = x < (lim) ? pk[x] : 0u;                         \
-    }
-    const bool resident = cv.n_leaves <= kChunk;
-    if (resident) LSA_THR_LOAD(0, (int)cv.n_leaves)
     const int64_t t = q_pos[un.b * sa.n_q + un.i];
     const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
-    const int64_t total = q.l0 > q.sink_end ? q.l0 - q.sink_end : 0;
-    if (t < 0 || sa.k == 0 || (int64_t)sa.k >= total) {   // handled by the walk kernel without candidates
-        if (tid == 0) cnt[u] = 0;
+    int32_t* out = lr_idx + u * sa.k;
+    if (unit_is_trivial(t, q, sa.k)) {
+        if (wid == 0) trivial_unit(t, q, sa.k, out, lr_cnt + u);
         return;
     }
+    const int64_t bg = un.b * sa.H_kv + un.g;
+    const float* sc = scores + u * score_stride;
+    const uint32_t* meta = cv.meta + bg * cv.s_meta;
     const int NLv = kLeavesPerBlock * q.nvis;
+    constexpr int kChunk = kThrRegs * kThrThreads;
     const int nchunks = (NLv + kChunk - 1) / kChunk;
-    if (resident) {
-#pragma unroll
-        for (int j = 0; j < kThrRegs; ++j)
-            if (j * kThrThreads + tid >= NLv) rv[j] = 0u;   // weight 0: never counted
+    // Eligible tokens of the buckets of the (at most two) blocks straddling an
+    // edge of [sink_end, l0), from their member lists, once.
+    int sb0, sb1;
+    straddling_blocks(q, sb0, sb1);
+    if (tid < 2 * kLeavesPerBlock) {
+        const int blk = tid < kLeavesPerBlock ? sb0 : sb1;
+        const int64_t x = (int64_t)blk * kLeavesPerBlock + tid % kLeavesPerBlock;
+        tk[tid] = (blk >= 0 && x < NLv) ? leaf_weight(cv, bg, (uint32_t)x, q) : 0;
     }
+    __syncthreads();
+    // Records of one chunk into LDS, eight at a time per thread with their
+    // score and meta loads in flight together (unconditional, clamped index).
+    auto load_chunk = [&](int c0) {
+        for (int j0 = 0; j0 < kThrRegs; j0 += 8) {
+            float s8[8];
+            uint32_t m8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int x = c0 + (j0 + j) * kThrThreads + tid;
+                const int xc = x < NLv ? x : NLv - 1;
+                s8[j] = sc[xc];
+                m8[j] = meta[xc];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int x = c0 + (j0 + j) * kThrThreads + tid;
+                const int blk = x / kLeavesPerBlock;
+                const int w = blk == sb0   ? tk[x % kLeavesPerBlock]
+                              : blk == sb1 ? tk[kLeavesPerBlock + x % kLeavesPerBlock]
+                                           : leaf_weight_whole((uint32_t)x, m8[j], q);
+                rec[(j0 + j) * kThrThreads + tid] = x < NLv ? (thr_key(s8[j]) << 7) | (uint32_t)w : 0u;
+            }
+        }
+        __syncthreads();
+    };
+    const bool resident = nchunks == 1;
+    if (resident) load_chunk(0);
     uint32_t lo = 0, target = (uint32_t)sa.k, cabove = 0, lower = 0, flo = 0;
     int shift = 13, nb = kThrBins;
     bool overflow = false;
-    // Level -1 histograms only each thread's best leaf.  Those leaves are a
-    // subset of all leaves, so if the ones at or above bin F hold >= k tokens
-    // then so do all leaves at or above F, and the boundary bin is >= F: the
-    // level-0 histogram may skip every leaf below F (far fewer LDS atomics).
+    // Level -1 histograms only each thread's best bucket.  Those are a subset
+    // of all buckets, so if the ones at or above bin F hold >= k tokens then so
+    // do all buckets at or above F, and the boundary bin is >= F: level 0 may
+    // skip every bucket below F (far fewer LDS atomics).
     for (int level = -1; level < 3; ++level) {
         for (int j = tid; j < nb; j += kThrThreads) hist[j] = 0ull;
         __syncthreads();
         const uint32_t hi = lo + ((uint32_t)nb << shift);
         uint32_t best = 0;   // best record with a nonzero weight (records compare by key first)
         for (int c = 0; c < nchunks; ++c) {
-            if (!resident) LSA_THR_LOAD(c * kChunk, NLv)
-#pragma unroll
+            if (!resident) load_chunk(c * kChunk);
             for (int j = 0; j < kThrRegs; ++j) {
-                const uint32_t key = rv[j] >> 7, w = rv[j] & 0x7Fu;
+                const uint32_t r = rec[j * kThrThreads + tid];
+                const uint32_t key = r >> 7, w = r & 0x7Fu;
                 if (level < 0) {
-                    if (w > 0 && rv[j] > best) best = rv[j];
+                    if (w > 0 && r > best) best = r;
                 } else if (w > 0 && key >= lo && key < hi && key >= flo) {
                     atomicAdd(&hist[(key - lo) >> shift], (1ull << 32) | (unsigned long long)w);
                 }
             }
+            if (!resident) __syncthreads();   // the chunk's records are overwritten next
         }
         if (level < 0 && best != 0u)
             atomicAdd(&hist[(best >> 7) >> shift], (1ull << 32) | (unsigned long long)(best & 0x7Fu));
-        if (level < 0 && tid == 0) bc[0] = 0xFFFFFFFFu;   // stays so if the best leaves hold < k tokens
+        if (level < 0 && tid == 0) bc[0] = 0xFFFFFFFFu;   // stays so if the best buckets hold < k tokens
         __syncthreads();
         // thread tid owns bins [per * tid, per * tid + per); suffix sums run from the top bin down
         const int per = (nb + kThrThreads - 1) / kThrThreads;
@@ -1068,6 +1095,10 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(CacheView cv, co
             flo = B == 0xFFFFFFFFu ? 0u : (B << shift);
             continue;
         }
+        if (B == 0xFFFFFFFFu) {   // cannot happen: the visible buckets hold every eligible token (> k)
+            overflow = true;
+            break;
+        }
         if (cab + cB <= (uint32_t)(level == 2 ? kCandCap : kThrGoal)) {
             lower = lo + (B << shift);
             break;
@@ -1082,18 +1113,22 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(CacheView cv, co
         shift = level == 0 ? 2 : 0;
         nb = level == 0 ? 2048 : 4;
     }
-    if (overflow) {   // too many leaves tie at the boundary key: the exact radix path takes the unit
-        if (tid == 0) cnt[u] = kCandCap + 1;
+    if (overflow) {   // too many buckets tie at the boundary key: the exact radix path takes the unit
+        if (tid == 0) {
+            const int pos = atomicAdd(&counters[0], 1);
+            fb_list[pos] = (int)u;
+        }
         return;
     }
+    uint32_t* cid = reinterpret_cast<uint32_t*>(hist);   // [kCandCap] candidate ids (the histogram is dead)
     if (tid == 0) ncand = 0;
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
-        if (!resident) LSA_THR_LOAD(c * kChunk, NLv)
-#pragma unroll
+        if (!resident) load_chunk(c * kChunk);
         for (int j = 0; j < kThrRegs; ++j) {
             const int x = c * kChunk + j * kThrThreads + tid;
-            const bool take = (rv[j] & 0x7Fu) != 0u && (rv[j] >> 7) >= lower;
+            const uint32_t r = rec[j * kThrThreads + tid];
+            const bool take = (r & 0x7Fu) != 0u && (r >> 7) >= lower;
             const uint64_t bal = __ballot(take);
             int base = 0;
             if (l == 0 && bal) base = atomicAdd(&ncand, __popcll(bal));
@@ -1103,12 +1138,111 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(CacheView cv, co
                 if (pos < kCandCap) cid[pos] = (uint32_t)x;
             }
         }
+        if (!resident) __syncthreads();
     }
     __syncthreads();
+    // the record space is dead: ranking scratch and the tokens
+    uint64_t* keys = reinterpret_cast<uint64_t*>(rec);       // [kCandCap]
+    uint32_t* cmeta = reinterpret_cast<uint32_t*>(keys + kCandCap);
+    int* cw = reinterpret_cast<int*>(cmeta + kCandCap);
+    int* coff = cw + kCandCap;
+    uint32_t* tok = reinterpret_cast<uint32_t*>(coff + kCandCap);   // [LSA_MAX_K]
+    static_assert(kCandCap * 20 + LSA_MAX_K * 4 <= kThrRegs * kThrThreads * 4, "ranking scratch fits the records");
+    // ---- rank the candidates (score desc, id asc)
     const int nc = ncand < kCandCap ? ncand : kCandCap;
-    if (tid < nc) cand[u * kCandCap + tid] = rank_key(sc[cid[tid]], cid[tid]);
-    if (tid == 0) cnt[u] = ncand;
-#undef LSA_THR_LOAD
+    const int P = pow2_at_least(nc);
+    for (int j = tid; j < P; j += kThrThreads) keys[j] = j < nc ? rank_key(sc[cid[j]], cid[j]) : 0ull;
+    __syncthreads();
+    if (wid == 0) wave_sort_desc(keys, P);
+    __syncthreads();
+    // ---- eligible tokens of each ranked candidate, then the buckets taken until k tokens
+    if (tid < nc) {
+        const uint32_t x = rank_key_id(keys[tid]);
+        const uint32_t m = meta[x];
+        const int blk = (int)(x / kLeavesPerBlock);
+        cmeta[tid] = m;
+        cw[tid] = blk == sb0 ? tk[x % kLeavesPerBlock]
+                  : blk == sb1 ? tk[kLeavesPerBlock + x % kLeavesPerBlock]
+                               : leaf_weight_whole(x, m, q);
+    }
+    __syncthreads();
+    if (wid == 0) {
+        int run = 0, ntake = nc, last = 0;
+        for (int c0 = 0; c0 < nc; c0 += 64) {
+            const int j = c0 + l;
+            const int w = j < nc ? cw[j] : 0;
+            const int incl = wave_incl_scan(w) + run;
+            if (j < nc) coff[j] = incl - w;
+            const uint64_t hit = __ballot(j < nc && w > 0 && incl >= sa.k && incl - w < sa.k);
+            if (hit) {
+                const int hl = __builtin_ctzll(hit);
+                ntake = c0 + hl + 1;
+                last = sa.k - __shfl(incl - w, hl);   // tokens the boundary bucket gives
+                break;
+            }
+            run = __shfl(incl, 63);
+        }
+        if (l == 0) {
+            fin[0] = ntake;
+            // total: k when the boundary was reached (always, the candidates hold >= k tokens)
+            fin[1] = ntake < nc || last > 0 ? sa.k : run;
+            fin[2] = last;
+        }
+    }
+    __syncthreads();
+    const int ntake = fin[0], total = fin[1], last = fin[2];
+    // ---- emit: bucket j by wave j % 16, lane l = member l / 4, token l % 4 (members ascending, so
+    // the lanes' eligible tokens are in ascending order and the boundary bucket keeps its lowest ones)
+    {
+        constexpr int NW = kThrThreads / 64, GB = 4;   // waves; buckets per wave whose member loads fly together
+        const uint16_t* mem_bg = cv.members + bg * cv.s_members;
+        const int e = l >> 2, jj = l & 3;
+        for (int j0 = wid; j0 < ntake; j0 += NW * GB) {
+            uint16_t mv[GB];
+#pragma unroll
+            for (int g = 0; g < GB; ++g) {
+                const int j = min(j0 + g * NW, ntake - 1);
+                const uint32_t m = cmeta[j];
+                const int sz = (int)(m & 0xFFu), off = (int)((m >> 8) & 0x3FFu);
+                const int64_t blk = rank_key_id(keys[j]) / kLeavesPerBlock;
+                mv[g] = mem_bg[blk * kBlockEntries + off + (e < sz ? e : 0)];
+            }
+#pragma unroll
+            for (int g = 0; g < GB; ++g) {
+                const int j = j0 + g * NW;
+                if (j >= ntake) break;
+                const uint32_t m = cmeta[j];
+                const int sz = (int)(m & 0xFFu);
+                const int64_t blk = rank_key_id(keys[j]) / kLeavesPerBlock;
+                const int64_t t0 = blk * kBlockTokens + (int64_t)kPool * mv[g] + jj;
+                const bool el = e < sz && t0 >= q.sink_end && t0 < q.l0;
+                const uint64_t bal = __ballot(el);
+                const int pos = __popcll(bal & ((1ull << l) - 1ull));
+                const int quota = (j == ntake - 1 && last > 0) ? last : 64;
+                if (el && pos < quota) tok[coff[j] + pos] = (uint32_t)t0;
+            }
+        }
+    }
+    // ---- sort the tokens ascending (bitonic over the next power of two, padded with ~0)
+    const int PT = pow2_at_least(total);
+    for (int j = total + tid; j < PT; j += kThrThreads) tok[j] = 0xFFFFFFFFu;
+    __syncthreads();
+    for (int size = 2; size <= PT; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < PT / 2; i += kThrThreads) {
+                const int a = 2 * i - (i & (stride - 1)), b = a + stride;
+                const uint32_t va = tok[a], vb = tok[b];
+                const bool up = (a & size) == 0;
+                if ((va > vb) == up) {
+                    tok[a] = vb;
+                    tok[b] = va;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int j = tid; j < sa.k; j += kThrThreads) out[j] = j < total ? (int32_t)tok[j] : -1;
+    if (tid == 0) lr_cnt[u] = total;
 }
 
 // Workgroup-wide exclusive scan over 256 threads (4 waves).
@@ -1313,13 +1447,18 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
             if constexpr (BF16) {
                 uint4 b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
                 if (node >= 0) {
-                    const uint16_t* base =
-                        lev == 0 ? reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent + node * kLatent
-                                 : reinterpret_cast<const uint16_t*>(cv.tcent) + bg * cv.s_tcent +
-                                       (lev_off + node) * kLatent;
-                    const uint4* p = reinterpret_cast<const uint4*>(base + 16 * h);
-                    b0 = p[0];
-                    b1 = p[1];
+                    if (lev == 0) {   // leaves: tile-swizzled storage
+                        const uint4* p =
+                            reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
+                        b0 = p[cent_tile_word(node, h, 0)];
+                        b1 = p[cent_tile_word(node, h, 1)];
+                    } else {
+                        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.tcent) +
+                                                                        bg * cv.s_tcent + (lev_off + node) * kLatent +
+                                                                        16 * h);
+                        b0 = p[0];
+                        b1 = p[1];
+                    }
                 }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, as_bf16x8(b0), acc, 0, 0, 0);
@@ -1370,21 +1509,28 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
 // ------------------------------------------------------------------ host launch
 
 hipError_t launch_qlatent(const void* Q, const void* W, bool bf16, int d, int64_t rows, void* qhat, int* counters,
-                          hipStream_t st) {
+                          void* zero, size_t zero_bytes, hipStream_t st) {
+    const int64_t zero_n = (int64_t)(zero_bytes / 16);
+    // enough workgroups that each thread clears at most ~8 words
+    const int64_t zg = (zero_n + 2047) / 2048;
+    const unsigned zgrid = (unsigned)(zg < 1024 ? zg : 1024);
     int64_t need = (rows + 15) / 16;
     unsigned grid = (unsigned)(need < 2048 ? (need > 0 ? need : 1) : 2048);
+    if (grid < zgrid) grid = zgrid;
+    uint4* z = static_cast<uint4*>(zero);
     if (bf16) {
         const int64_t tiles = (rows + 15) / 16;
-        const unsigned g2 = (unsigned)((tiles + 3) / 4 < 1024 ? ((tiles + 3) / 4 > 0 ? (tiles + 3) / 4 : 1) : 1024);
+        unsigned g2 = (unsigned)((tiles + 3) / 4 < 1024 ? ((tiles + 3) / 4 > 0 ? (tiles + 3) / 4 : 1) : 1024);
+        if (g2 < zgrid) g2 = zgrid;
         if (d == 128)
             hipLaunchKernelGGL(qlatent_bf16_kernel<128>, dim3(g2), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
-                               static_cast<const uint16_t*>(W), rows, static_cast<uint16_t*>(qhat), counters);
+                               static_cast<const uint16_t*>(W), rows, static_cast<uint16_t*>(qhat), counters, z, zero_n);
         else
             hipLaunchKernelGGL(qlatent_bf16_kernel<64>, dim3(g2), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
-                               static_cast<const uint16_t*>(W), rows, static_cast<uint16_t*>(qhat), counters);
+                               static_cast<const uint16_t*>(W), rows, static_cast<uint16_t*>(qhat), counters, z, zero_n);
     } else
         hipLaunchKernelGGL(qlatent_kernel<float>, dim3(grid), dim3(256), 0, st, static_cast<const float*>(Q),
-                           static_cast<const float*>(W), d, rows, qhat, 0, counters);
+                           static_cast<const float*>(W), d, rows, qhat, 0, counters, z, zero_n);
     return hipGetLastError();
 }
 
@@ -1420,24 +1566,22 @@ hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_
 hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa,
                                       const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, hipStream_t st) {
     const int64_t ntiles_max = (int64_t)cv.n_blocks * kLeavesPerBlock / 16;
-    int splits = (int)((ntiles_max + 63) / 64);
-    if (splits < 1) splits = 1;
-    if (splits > 64) splits = 64;
-    dim3 grid((unsigned)sa.n_units, (unsigned)splits);
+    const int splits = (int)((ntiles_max + kScoreTiles - 1) / kScoreTiles > 0 ? (ntiles_max + kScoreTiles - 1) / kScoreTiles : 1);
+    const dim3 grid((unsigned)(sa.n_units * splits));
     if (bf16)
-        hipLaunchKernelGGL(score_all_kernel<true>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, sb.scores,
-                           sb.packed, sb.score_stride);
+        hipLaunchKernelGGL(score_all_kernel<true>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits, sb.scores,
+                           sb.score_stride);
     else
-        hipLaunchKernelGGL(score_all_kernel<false>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, sb.scores,
-                           sb.packed, sb.score_stride);
+        hipLaunchKernelGGL(score_all_kernel<false>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits, sb.scores,
+                           sb.score_stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)sa.n_units), dim3(kThrThreads), 0, st, cv, q_pos, sa, sb.scores,
-                       sb.packed, sb.score_stride, sb.cnt, sb.cand);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fused_finalize_kernel, dim3((unsigned)((sa.n_units + 3) / 4)), dim3(256), 0, st, cv, q_pos, sa,
-                       sb.cnt, sb.cand, sb.fb_list, sb.counters, lr_idx, lr_cnt);
+    if (bf16)
+        hipLaunchKernelGGL(score_select_kernel<true>, dim3((unsigned)sa.n_units), dim3(kThrThreads), 0, st, cv, q_pos,
+                           sa, sb.scores, sb.score_stride, sb.fb_list, sb.counters, lr_idx, lr_cnt);
+    else
+        hipLaunchKernelGGL(score_select_kernel<false>, dim3((unsigned)sa.n_units), dim3(kThrThreads), 0, st, cv, q_pos,
+                           sa, sb.scores, sb.score_stride, sb.fb_list, sb.counters, lr_idx, lr_cnt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (bf16)
