@@ -165,20 +165,22 @@ __device__ __forceinline__ void finish_split(const AttArgs& aa, const float* par
     combine_unit(part, aa, D, out_bf16, O, u);
 }
 
-// Lane (r, h) loads head dims [D/4 h, D/4 h + D/4) of the key and value rows.
+// Lane (r, h) loads head dims 32 ks + 8 h + [0, 8) of the key and value rows,
+// ks < D/32: the four lanes of a row read 64 contiguous bytes per load
+// instruction, so one instruction covers 16 rows x 64 bytes.
 template <int D>
 __device__ __forceinline__ void load_rows(const uint16_t* Kbg, const uint16_t* Vbg, int32_t tk, int h, uint4* kr,
                                           uint4* vr) {
-    constexpr int DPL = D / 4, KS = DPL / 8;
+    constexpr int KS = D / 32;
     // branch-free: a masked row reads row 0 (always present); its score is
     // -inf and its probability exactly 0, so it contributes nothing
     const uint32_t row = tk >= 0 ? (uint32_t)tk : 0u;
-    const uint4* kp = reinterpret_cast<const uint4*>(Kbg + (size_t)row * D + DPL * h);
-    const uint4* vp = reinterpret_cast<const uint4*>(Vbg + (size_t)row * D + DPL * h);
+    const uint4* kp = reinterpret_cast<const uint4*>(Kbg + (size_t)row * D + 8 * h);
+    const uint4* vp = reinterpret_cast<const uint4*>(Vbg + (size_t)row * D + 8 * h);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        kr[ks] = kp[ks];
-        vr[ks] = vp[ks];
+        kr[ks] = kp[4 * ks];
+        vr[ks] = vp[4 * ks];
     }
 }
 
@@ -225,7 +227,7 @@ __device__ __forceinline__ void attend_tile(int32_t ta, int32_t tb, const uint4*
     const bf16x8 pfrag = as_bf16x8(uint4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        // chunk c: lane (r, h) contributes V[key r][D/4 h + 4c + 0..3]
+        // chunk c: lane (r, h) contributes V[key r][32 (c/2) + 8h + 4 (c%2) + 0..3]
         const uint4 wa = xa[c / 2], wb = xb[c / 2];
         const s16x4 va4 = __builtin_bit_cast(s16x4, (c & 1) ? u32x2{wa.z, wa.w} : u32x2{wa.x, wa.y});
         const s16x4 vb4 = __builtin_bit_cast(s16x4, (c & 1) ? u32x2{wb.z, wb.w} : u32x2{wb.x, wb.y});
@@ -252,9 +254,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                           const int32_t* __restrict__ lr_cnt, AttArgs aa,
                                                           uint16_t* __restrict__ O, float* __restrict__ part,
                                                           int64_t nwg_padded) {
-    constexpr int DPL = D / 4;   // head dims per lane group (lane (r, h) owns [DPL h, DPL h + DPL))
-    constexpr int KS = DPL / 8;  // 8-element k-steps per lane for QK
-    constexpr int NC = DPL / 4;  // 4-dim chunks for the transpose and PV
+    // lane (r, h) owns head dims 32 ks + 8 h + [0, 8), ks < KS (see load_rows)
+    constexpr int KS = D / 32;   // 8-element k-steps per lane for QK
+    constexpr int NC = 2 * KS;   // 4-dim chunks for the transpose and PV: chunk c = dims 32 (c/2) + 8h + 4 (c%2) + [0, 4)
     const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4;
     const int64_t logical = xcd_logical(blockIdx.x, nwg_padded);
     const int64_t w_id = logical * 4 + wid;
@@ -280,12 +282,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int64_t j0 = (int64_t)s * chunk;
         const int64_t j1 = j0 + chunk < kl.nS ? j0 + chunk : kl.nS;
 
-        // B operand of S^T = K Q^T: head n, dims DPL h + 8 ks + [0, 8)
+        // B operand of S^T = K Q^T: head n, dims 32 ks + 8 h + [0, 8)
         uint4 qf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             qf[ks] = uint4{0, 0, 0, 0};
-            if (n < aa.G) qf[ks] = *reinterpret_cast<const uint4*>(Q + orow + DPL * h + 8 * ks);
+            if (n < aa.G) qf[ks] = *reinterpret_cast<const uint4*>(Q + orow + 32 * ks + 8 * h);
         }
         // identity B for the transposing MFMA: lane (col n, k-group h) holds I[4h + j][n]
         s16x4 ident;
@@ -324,22 +326,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             b_tb = gb;
         }
     }
-    // acc[c][v] = unnormalised O[head n][DPL h + 4c + v]
+    // acc[c][v] = unnormalised O[head n][32 (c/2) + 8h + 4 (c%2) + v]
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     if (aa.splits == 1) {
         if (n < aa.G) {
             const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-            uint32_t w[DPL / 2];
+            uint32_t w[2 * NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 w[2 * c] = (uint32_t)f32_to_bf16(acc[c][0] * inv) | ((uint32_t)f32_to_bf16(acc[c][1] * inv) << 16);
                 w[2 * c + 1] = (uint32_t)f32_to_bf16(acc[c][2] * inv) | ((uint32_t)f32_to_bf16(acc[c][3] * inv) << 16);
             }
 #pragma unroll
-            for (int q4 = 0; q4 < DPL / 8; ++q4)
-                *reinterpret_cast<uint4*>(O + orow + DPL * h + 8 * q4) =
-                    uint4{w[4 * q4], w[4 * q4 + 1], w[4 * q4 + 2], w[4 * q4 + 3]};
+            for (int ks = 0; ks < KS; ++ks)   // dims 32 ks + 8h + [0, 8)
+                *reinterpret_cast<uint4*>(O + orow + 32 * ks + 8 * h) =
+                    uint4{w[4 * ks], w[4 * ks + 1], w[4 * ks + 2], w[4 * ks + 3]};
         }
     } else {
         if (n < aa.G) {
@@ -347,8 +349,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (h == 0) store_coherent_u64(pp, pack_f32x2(m_run, l_run));
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                store_coherent_u64(pp + 2 + DPL * h + 4 * c, pack_f32x2(acc[c][0], acc[c][1]));
-                store_coherent_u64(pp + 4 + DPL * h + 4 * c, pack_f32x2(acc[c][2], acc[c][3]));
+                const int d0 = 32 * (c / 2) + 8 * h + 4 * (c % 2);
+                store_coherent_u64(pp + 2 + d0, pack_f32x2(acc[c][0], acc[c][1]));
+                store_coherent_u64(pp + 4 + d0, pack_f32x2(acc[c][2], acc[c][3]));
             }
         }
         finish_split(aa, part, D, 1, O, un.u);

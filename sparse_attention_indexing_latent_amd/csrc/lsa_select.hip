@@ -844,11 +844,30 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
 // below L ranks after every collected one, so the walk ends exactly where a
 // walk over all buckets would.  Too many ties at L send the unit to the
 // exact radix path.
-constexpr int kScoreTiles = 128;  // tiles (16 buckets each) per scoring workgroup
+constexpr int kScoreTiles = 16;   // tiles (16 buckets each) per scoring workgroup: small workgroups overlap best
 constexpr int kThrThreads = 1024;
 constexpr int kThrBins = 3072;    // level 0: key >> 13
 constexpr int kThrGoal = 128;     // refine the bound while more buckets than this sit at or above it
-constexpr int kThrRegs = 32;      // buckets per thread held in registers (one chunk = 32768 buckets)
+constexpr int kThrRegs = 32;      // records per thread (one chunk = 32768 buckets)
+constexpr int kMaxBlockWords = 1024;   // blocks a unit may see: 64 x 1024 (2^27 tokens)
+constexpr int kMaskSlots = 384;        // distinct blocks among the taken buckets
+
+// Workgroup-wide exclusive scan over 1024 threads; tot = the sum.  scratch: 16 ints.
+__device__ __forceinline__ int wg1024_excl_scan(int v, int* scratch, int& tot) {
+    const int l = lane_id(), wid = threadIdx.x >> 6;
+    const int inc = wave_incl_scan(v);
+    if (l == 63) scratch[wid] = inc;
+    __syncthreads();
+    int base = 0;
+    tot = 0;
+    for (int w = 0; w < 16; ++w) {
+        const int s = scratch[w];
+        base += w < wid ? s : 0;
+        tot += s;
+    }
+    __syncthreads();
+    return base + inc - v;
+}
 
 // Offset key of a score: monotone non-decreasing in the score and in
 // [0, 3 * 2^23) (s + 2 clamped to [0.5, 4)).  Equal keys need not mean equal
@@ -973,6 +992,7 @@ __global__ __launch_bounds__(kThrThreads) void score_select_kernel(CacheView cv,
     __shared__ __align__(16) uint32_t rec[kThrRegs * kThrThreads];
     __shared__ unsigned long long hist[kThrBins];
     __shared__ unsigned long long wtot[kThrThreads / 64];
+    __shared__ int wtot32[kThrThreads / 64];
     __shared__ uint32_t bc[4];
     __shared__ int ncand, fin[3];
     __shared__ int tk[2 * kLeavesPerBlock];   // eligible tokens of the straddling blocks' buckets
@@ -1002,21 +1022,21 @@ __global__ __launch_bounds__(kThrThreads) void score_select_kernel(CacheView cv,
         tk[tid] = (blk >= 0 && x < NLv) ? leaf_weight(cv, bg, (uint32_t)x, q) : 0;
     }
     __syncthreads();
-    // Records of one chunk into LDS, eight at a time per thread with their
+    // Records of one chunk into LDS, 16 at a time per thread with their
     // score and meta loads in flight together (unconditional, clamped index).
     auto load_chunk = [&](int c0) {
-        for (int j0 = 0; j0 < kThrRegs; j0 += 8) {
-            float s8[8];
-            uint32_t m8[8];
+        for (int j0 = 0; j0 < kThrRegs; j0 += 16) {
+            float s8[16];
+            uint32_t m8[16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 16; ++j) {
                 const int x = c0 + (j0 + j) * kThrThreads + tid;
                 const int xc = x < NLv ? x : NLv - 1;
                 s8[j] = sc[xc];
                 m8[j] = meta[xc];
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 16; ++j) {
                 const int x = c0 + (j0 + j) * kThrThreads + tid;
                 const int blk = x / kLeavesPerBlock;
                 const int w = blk == sb0   ? tk[x % kLeavesPerBlock]
@@ -1142,12 +1162,16 @@ __global__ __launch_bounds__(kThrThreads) void score_select_kernel(CacheView cv,
     }
     __syncthreads();
     // the record space is dead: ranking scratch and the tokens
-    uint64_t* keys = reinterpret_cast<uint64_t*>(rec);       // [kCandCap]
-    uint32_t* cmeta = reinterpret_cast<uint32_t*>(keys + kCandCap);
-    int* cw = reinterpret_cast<int*>(cmeta + kCandCap);
-    int* coff = cw + kCandCap;
-    uint32_t* tok = reinterpret_cast<uint32_t*>(coff + kCandCap);   // [LSA_MAX_K]
-    static_assert(kCandCap * 20 + LSA_MAX_K * 4 <= kThrRegs * kThrThreads * 4, "ranking scratch fits the records");
+    uint64_t* keys = reinterpret_cast<uint64_t*>(rec);         // [kCandCap]
+    uint64_t* used = keys + kCandCap;                           // [kMaxBlockWords] blocks holding taken buckets
+    uint64_t* mask = used + kMaxBlockWords;                     // [kMaskSlots][32] token masks
+    uint32_t* cmeta = reinterpret_cast<uint32_t*>(mask + kMaskSlots * 32);   // [kCandCap]
+    int* cw = reinterpret_cast<int*>(cmeta + kCandCap);         // [kCandCap]
+    int* coff = cw + kCandCap;                                  // [kCandCap]
+    int* upre = coff + kCandCap;                                // [kMaxBlockWords]
+    int* slot_blk = upre + kMaxBlockWords;                      // [kMaskSlots]
+    static_assert(kCandCap * (8 + 12) + kMaxBlockWords * 12 + kMaskSlots * (256 + 4) <= kThrRegs * kThrThreads * 4,
+                  "ranking scratch fits the records' space");
     // ---- rank the candidates (score desc, id asc)
     const int nc = ncand < kCandCap ? ncand : kCandCap;
     const int P = pow2_at_least(nc);
@@ -1191,8 +1215,48 @@ __global__ __launch_bounds__(kThrThreads) void score_select_kernel(CacheView cv,
     }
     __syncthreads();
     const int ntake = fin[0], total = fin[1], last = fin[2];
-    // ---- emit: bucket j by wave j % 16, lane l = member l / 4, token l % 4 (members ascending, so
-    // the lanes' eligible tokens are in ascending order and the boundary bucket keeps its lowest ones)
+    // ---- tokens in ascending order through per-block token masks: the blocks of the taken buckets
+    // get slots in block order (a bitmap of used blocks and its prefix counts), every emitted token
+    // sets its bit in its block's 2048-bit mask, and a prefix count over the mask words places it.
+    const int nbw = (cv.n_blocks + 63) / 64;
+    if (nbw > kMaxBlockWords) {   // beyond the masks' reach: the exact radix path takes the unit
+        if (tid == 0) fb_list[atomicAdd(&counters[0], 1)] = (int)u;
+        return;
+    }
+    for (int w = tid; w < nbw; w += kThrThreads) used[w] = 0ull;
+    __syncthreads();
+    for (int j = tid; j < ntake; j += kThrThreads) {
+        const uint32_t blk = rank_key_id(keys[j]) / kLeavesPerBlock;
+        atomicOr(&used[blk / 64], 1ull << (blk % 64));
+    }
+    __syncthreads();
+    {
+        const int pc = tid < nbw ? __popcll(used[tid]) : 0;   // nbw <= kThrThreads
+        int tot;
+        const int ex = wg1024_excl_scan(pc, wtot32, tot);
+        if (tid < nbw) {
+            upre[tid] = ex;
+            uint64_t m = used[tid];
+            int r = ex;
+            while (m) {   // slot -> block
+                const int b = __builtin_ctzll(m);
+                m &= m - 1;
+                if (r < kMaskSlots) slot_blk[r] = tid * 64 + b;
+                ++r;
+            }
+        }
+        if (tid == 0) fin[0] = tot;
+    }
+    __syncthreads();
+    const int nslots = fin[0];
+    if (nslots > kMaskSlots) {
+        if (tid == 0) fb_list[atomicAdd(&counters[0], 1)] = (int)u;
+        return;
+    }
+    for (int w = tid; w < nslots * 32; w += kThrThreads) mask[w] = 0ull;
+    __syncthreads();
+    // emit: bucket j by wave j % 16, lane l = member l / 4, token l % 4 (members ascending, so the
+    // lanes' eligible tokens are in ascending order and the boundary bucket keeps its lowest ones)
     {
         constexpr int NW = kThrThreads / 64, GB = 4;   // waves; buckets per wave whose member loads fly together
         const uint16_t* mem_bg = cv.members + bg * cv.s_members;
@@ -1213,35 +1277,39 @@ __global__ __launch_bounds__(kThrThreads) void score_select_kernel(CacheView cv,
                 if (j >= ntake) break;
                 const uint32_t m = cmeta[j];
                 const int sz = (int)(m & 0xFFu);
-                const int64_t blk = rank_key_id(keys[j]) / kLeavesPerBlock;
-                const int64_t t0 = blk * kBlockTokens + (int64_t)kPool * mv[g] + jj;
+                const int blk = (int)(rank_key_id(keys[j]) / kLeavesPerBlock);
+                const int tb = kPool * mv[g] + jj;   // token offset in the block
+                const int64_t t0 = (int64_t)blk * kBlockTokens + tb;
                 const bool el = e < sz && t0 >= q.sink_end && t0 < q.l0;
                 const uint64_t bal = __ballot(el);
                 const int pos = __popcll(bal & ((1ull << l) - 1ull));
                 const int quota = (j == ntake - 1 && last > 0) ? last : 64;
-                if (el && pos < quota) tok[coff[j] + pos] = (uint32_t)t0;
-            }
-        }
-    }
-    // ---- sort the tokens ascending (bitonic over the next power of two, padded with ~0)
-    const int PT = pow2_at_least(total);
-    for (int j = total + tid; j < PT; j += kThrThreads) tok[j] = 0xFFFFFFFFu;
-    __syncthreads();
-    for (int size = 2; size <= PT; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < PT / 2; i += kThrThreads) {
-                const int a = 2 * i - (i & (stride - 1)), b = a + stride;
-                const uint32_t va = tok[a], vb = tok[b];
-                const bool up = (a & size) == 0;
-                if ((va > vb) == up) {
-                    tok[a] = vb;
-                    tok[b] = va;
+                if (el && pos < quota) {
+                    const int slot = upre[blk / 64] + __popcll(used[blk / 64] & ((1ull << (blk % 64)) - 1ull));
+                    atomicOr(&mask[slot * 32 + tb / 64], 1ull << (tb % 64));
                 }
             }
-            __syncthreads();
         }
     }
-    for (int j = tid; j < sa.k; j += kThrThreads) out[j] = j < total ? (int32_t)tok[j] : -1;
+    __syncthreads();
+    // thread tid owns mask words [per * tid, per * tid + per): its tokens follow those of lower words
+    {
+        const int nw = nslots * 32, per = (nw + kThrThreads - 1) / kThrThreads, w0 = per * tid;
+        int pc = 0;
+        for (int w = w0; w < w0 + per && w < nw; ++w) pc += __popcll(mask[w]);
+        int tot;
+        int pos = wg1024_excl_scan(pc, wtot32, tot);
+        for (int w = w0; w < w0 + per && w < nw; ++w) {
+            uint64_t m = mask[w];
+            const int32_t base = slot_blk[w / 32] * kBlockTokens + (w % 32) * 64;
+            while (m) {
+                const int b = __builtin_ctzll(m);
+                m &= m - 1;
+                out[pos++] = base + b;
+            }
+        }
+    }
+    for (int j = total + tid; j < sa.k; j += kThrThreads) out[j] = -1;
     if (tid == 0) lr_cnt[u] = total;
 }
 
@@ -1584,12 +1652,14 @@ hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int6
                            sa, sb.scores, sb.score_stride, sb.fb_list, sb.counters, lr_idx, lr_cnt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // the fallback list is almost always empty: a few workgroups loop over it (cheaper to launch)
+    const unsigned fb_grid = (unsigned)(sb.fb_slots < 8 ? sb.fb_slots : 8);
     if (bf16)
-        hipLaunchKernelGGL(exact_select_kernel<true>, dim3((unsigned)sb.fb_slots), dim3(256), 0, st, cv, sb.qhat, q_pos,
-                           sa, sb.fb_list, sb.counters, sb.scores, sb.score_stride, 0, lr_idx, lr_cnt);
+        hipLaunchKernelGGL(exact_select_kernel<true>, dim3(fb_grid), dim3(256), 0, st, cv, sb.qhat, q_pos, sa,
+                           sb.fb_list, sb.counters, sb.scores, sb.score_stride, 0, lr_idx, lr_cnt);
     else
-        hipLaunchKernelGGL(exact_select_kernel<false>, dim3((unsigned)sb.fb_slots), dim3(256), 0, st, cv, sb.qhat,
-                           q_pos, sa, sb.fb_list, sb.counters, sb.scores, sb.score_stride, 0, lr_idx, lr_cnt);
+        hipLaunchKernelGGL(exact_select_kernel<false>, dim3(fb_grid), dim3(256), 0, st, cv, sb.qhat, q_pos, sa,
+                           sb.fb_list, sb.counters, sb.scores, sb.score_stride, 0, lr_idx, lr_cnt);
     return hipGetLastError();
 }
 
