@@ -165,39 +165,77 @@ __device__ __forceinline__ void finish_split(const AttArgs& aa, const float* par
     combine_unit(part, aa, D, out_bf16, O, u);
 }
 
-// Lane (r, h) loads head dims 32 ks + 8 h + [0, 8) of the key and value rows,
-// ks < D/32: the four lanes of a row read 64 contiguous bytes per load
-// instruction, so one instruction covers 16 rows x 64 bytes.
+// One 32-key tile of K and V rows staged in LDS (per wave).  Rows are
+// loaded with whole-row coalescing: load instruction i brings rows RPI i ..
+// RPI i + RPI - 1 of the tile, lane l taking row RPI i + l / CPR, 16-byte
+// column l % CPR (each instruction covers RPI complete rows, 1 KB); the rows
+// are written to LDS in a swizzled layout and read back in the MFMA operand
+// layout (lane (r, h): row r, column 4 ks + h, i.e. head dims 32 ks + 8 h +
+// [0, 8)).  The swizzle (slot (j CPR/RPI + col) mod CPR inside the row, 16
+// bytes of padding per instruction group) keeps both the writes and the
+// 16-row reads free of bank conflicts for D = 128.
 template <int D>
-__device__ __forceinline__ void load_rows(const uint16_t* Kbg, const uint16_t* Vbg, int32_t tk, int h, uint4* kr,
-                                          uint4* vr) {
-    constexpr int KS = D / 32;
-    // branch-free: a masked row reads row 0 (always present); its score is
-    // -inf and its probability exactly 0, so it contributes nothing
-    const uint32_t row = tk >= 0 ? (uint32_t)tk : 0u;
-    const uint4* kp = reinterpret_cast<const uint4*>(Kbg + (size_t)row * D + 8 * h);
-    const uint4* vp = reinterpret_cast<const uint4*>(Vbg + (size_t)row * D + 8 * h);
+struct TileLds {
+    static constexpr int RPI = 512 / D;   // rows per load instruction
+    static constexpr int CPR = D / 8;     // 16-byte columns per row
+    static constexpr int NI = 32 / RPI;   // load instructions per tile and array
+    static constexpr int GB = 1024 + 16;  // bytes per instruction group, padded
+    static constexpr int ARR = NI * GB;   // bytes per array (K or V)
+    static constexpr int BYTES = 2 * ARR;
+    __device__ static __forceinline__ int off(int row, int col) {
+        const int i = row / RPI, j = row % RPI;
+        return i * GB + 16 * (CPR * j + ((j * (CPR / RPI) + col) % CPR));
+    }
+};
+
+// Global loads of one tile: lane l's row of instruction i is tile row
+// RPI i + l / CPR, whose token lane (row & 31) holds in `tok` (-1: masked; a
+// masked row reads row 0, always present, and gets probability exactly 0).
+// (native vector type: arrays of it stay in registers)
+template <int D>
+__device__ __forceinline__ void load_tile(const uint16_t* Kbg, const uint16_t* Vbg, int32_t tok, u32x4 (&kr)[TileLds<D>::NI],
+                                          u32x4 (&vr)[TileLds<D>::NI]) {
+    using TL = TileLds<D>;
+    const int l = lane_id();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        kr[ks] = kp[4 * ks];
-        vr[ks] = vp[4 * ks];
+    for (int i = 0; i < TL::NI; ++i) {
+        const int32_t tk = __shfl(tok, TL::RPI * i + l / TL::CPR);
+        const size_t row = tk >= 0 ? (size_t)tk : 0;
+        kr[i] = *reinterpret_cast<const u32x4*>(Kbg + row * D + 8 * (l % TL::CPR));
+        vr[i] = *reinterpret_cast<const u32x4*>(Vbg + row * D + 8 * (l % TL::CPR));
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const u32x4 (&kr)[TileLds<D>::NI], const u32x4 (&vr)[TileLds<D>::NI],
+                                           uint8_t* buf) {
+    using TL = TileLds<D>;
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < TL::NI; ++i) {
+        const int o = TL::off(TL::RPI * i + l / TL::CPR, l % TL::CPR);
+        *reinterpret_cast<u32x4*>(buf + o) = kr[i];
+        *reinterpret_cast<u32x4*>(buf + TL::ARR + o) = vr[i];
     }
 }
 
 // One tile of 32 keys: S^T = K Q^T, online softmax, V^T via the identity
 // MFMA, O^T += V^T P^T.
 template <int D>
-__device__ __forceinline__ void attend_tile(int32_t ta, int32_t tb, const uint4* ka, const uint4* kb, const uint4* xa,
-                                            const uint4* xb, const uint4* qf, const s16x4& ident, int h, float scale,
-                                            float& m_run, float& l_run, f32x4* acc) {
+__device__ __forceinline__ void attend_tile(uint64_t ma, uint64_t mb, const uint8_t* buf, int r, const uint4* qf,
+                                            const s16x4& ident, int h, float scale, float& m_run, float& l_run,
+                                            f32x4* acc) {
+    using TL = TileLds<D>;
     constexpr int KS = D / 32, NC = D / 16;
-    const uint64_t ma = __ballot(ta >= 0), mb = __ballot(tb >= 0);   // bit r: key row r of the tile is valid
-    if ((ma | mb) == 0ull) return;                                       // wave-uniform
+    // bit r of ma (mb): key row r (16 + r) of the tile is valid
+    if ((ma | mb) == 0ull) return;   // wave-uniform
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), as_bf16x8(qf[ks]), sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), as_bf16x8(qf[ks]), sb, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {   // K fragments: rows r and 16 + r, column 4 ks + h
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(buf + TL::off(r, 4 * ks + h));
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(buf + TL::off(16 + r, 4 * ks + h));
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, as_bf16x8(qf[ks]), sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, as_bf16x8(qf[ks]), sb, 0, 0, 0);
     }
     // rows of sa: keys 4h + v of the tile; rows of sb: keys 16 + 4h + v
     float pa[4], pb[4];
@@ -227,10 +265,11 @@ __device__ __forceinline__ void attend_tile(int32_t ta, int32_t tb, const uint4*
     const bf16x8 pfrag = as_bf16x8(uint4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        // chunk c: lane (r, h) contributes V[key r][32 (c/2) + 8h + 4 (c%2) + 0..3]
-        const uint4 wa = xa[c / 2], wb = xb[c / 2];
-        const s16x4 va4 = __builtin_bit_cast(s16x4, (c & 1) ? u32x2{wa.z, wa.w} : u32x2{wa.x, wa.y});
-        const s16x4 vb4 = __builtin_bit_cast(s16x4, (c & 1) ? u32x2{wb.z, wb.w} : u32x2{wb.x, wb.y});
+        // chunk c: lane (r, h) contributes V[key r][32 (c/2) + 8h + 4 (c%2) + 0..3]: 8 bytes of the
+        // V fragments of rows r and 16 + r, column 4 (c/2) + h
+        const int vo = TL::ARR + 8 * (c & 1);
+        const s16x4 va4 = *reinterpret_cast<const s16x4*>(buf + vo + TL::off(r, 4 * (c / 2) + h));
+        const s16x4 vb4 = *reinterpret_cast<const s16x4*>(buf + vo + TL::off(16 + r, 4 * (c / 2) + h));
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const f32x4 ta4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va4, ident, z, 0, 0, 0);
         const f32x4 tb4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb4, ident, z, 0, 0, 0);
@@ -254,7 +293,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                           const int32_t* __restrict__ lr_cnt, AttArgs aa,
                                                           uint16_t* __restrict__ O, float* __restrict__ part,
                                                           int64_t nwg_padded) {
-    // lane (r, h) owns head dims 32 ks + 8 h + [0, 8), ks < KS (see load_rows)
+    __shared__ __align__(16) uint8_t tile_lds[4 * TileLds<D>::BYTES];
+    // lane (r, h) owns head dims 32 ks + 8 h + [0, 8), ks < KS (see TileLds)
     constexpr int KS = D / 32;   // 8-element k-steps per lane for QK
     constexpr int NC = 2 * KS;   // 4-dim chunks for the transpose and PV: chunk c = dims 32 (c/2) + 8h + 4 (c%2) + [0, 4)
     const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4;
@@ -298,32 +338,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint16_t* Kbg = K + bg * aa.t_cap * D;
         const uint16_t* Vbg = V + bg * aa.t_cap * D;
 
-        // Software pipeline: the K/V rows of tile j + 32 are in flight while
-        // tile j is computed, and the indices of tile j + 64 one step earlier.
+        // Software pipeline over 32-key tiles: the rows of the next tile are in
+        // flight (registers) while the current one, staged through LDS, is
+        // computed; a tile's indices are fetched one step before its rows.
         // A key outside [0, t] (malformed list) is never read nor scored.
-        // Two register sets ping-pong: while one tile of 32 keys is computed
-        // the K/V rows of the next one are in flight, and the indices of the
-        // tile after that are fetched one step earlier still.
-        int32_t a_ta = tok_of(kl, j0 + r, j1, t), a_tb = tok_of(kl, j0 + 16 + r, j1, t);
-        int32_t b_ta = tok_of(kl, j0 + 32 + r, j1, t), b_tb = tok_of(kl, j0 + 48 + r, j1, t);
-        uint4 a_ka[KS], a_kb[KS], a_xa[KS], a_xb[KS];
-        uint4 b_ka[KS], b_kb[KS], b_xa[KS], b_xb[KS];
-        load_rows<D>(Kbg, Vbg, a_ta, h, a_ka, a_xa);
-        load_rows<D>(Kbg, Vbg, a_tb, h, a_kb, a_xb);
-        for (int64_t j = j0; j < j1; j += 64) {
-            load_rows<D>(Kbg, Vbg, b_ta, h, b_ka, b_xa);
-            load_rows<D>(Kbg, Vbg, b_tb, h, b_kb, b_xb);
-            const int32_t fa = tok_of(kl, j + 64 + r, j1, t), fb = tok_of(kl, j + 80 + r, j1, t);
-            attend_tile<D>(a_ta, a_tb, a_ka, a_kb, a_xa, a_xb, qf, ident, h, aa.scale, m_run, l_run, acc);
-            if (j + 32 >= j1) break;
-            a_ta = fa;
-            a_tb = fb;
-            load_rows<D>(Kbg, Vbg, a_ta, h, a_ka, a_xa);
-            load_rows<D>(Kbg, Vbg, a_tb, h, a_kb, a_xb);
-            const int32_t ga = tok_of(kl, j + 96 + r, j1, t), gb = tok_of(kl, j + 112 + r, j1, t);
-            attend_tile<D>(b_ta, b_tb, b_ka, b_kb, b_xa, b_xb, qf, ident, h, aa.scale, m_run, l_run, acc);
-            b_ta = ga;
-            b_tb = gb;
+        uint8_t* buf = tile_lds + wid * TileLds<D>::BYTES;
+        constexpr int NI = TileLds<D>::NI;
+        int32_t tok = tok_of(kl, j0 + (l & 31), j1, t);
+        u32x4 kR[NI], vR[NI];
+        load_tile<D>(Kbg, Vbg, tok, kR, vR);
+        for (int64_t j = j0; j < j1; j += 32) {
+            const int32_t nxt = tok_of(kl, j + 32 + (l & 31), j1, t);
+            const uint64_t vm = __ballot(tok >= 0);   // bit r: tile row r valid (lanes 32..63 repeat 0..31)
+            store_tile<D>(kR, vR, buf);
+            load_tile<D>(Kbg, Vbg, nxt, kR, vR);   // past the end: masked rows (row 0), never used
+            attend_tile<D>(vm & 0xFFFFull, (vm >> 16) & 0xFFFFull, buf, r, qf, ident, h, aa.scale, m_run, l_run, acc);
+            tok = nxt;
         }
     }
     // acc[c][v] = unnormalised O[head n][32 (c/2) + 8h + 4 (c%2) + v]

@@ -235,11 +235,11 @@ __device__ __forceinline__ f32x4 score_tile_f32(const float* cent_bg, int64_t x0
 // The bound: a histogram over 256 score bins of width 1/128 accumulates
 // token weights that are certainly eligible (4 x size for buckets of blocks
 // inside [sink_end, l0), else 0).  While a wave sees at most
-// kPerLeafMaxLeaves buckets every bucket is binned; beyond that only each
-// block's best bucket (its score truncated downwards, packed with its size).
-// The bin where the weight from the top reaches k gives tau = its lower edge
-// minus 2^-16 (absorbs fp32 rounding of the binning): at least k eligible
-// tokens lie in buckets scoring >= tau, so the k-th token's bucket does too.
+// kPerLeafMaxLeaves buckets every bucket is binned; beyond that the buckets
+// of every other block.  The bin where the weight from the top reaches k
+// gives tau = its lower edge minus 2^-16 (absorbs fp32 rounding of the
+// binning): at least k eligible tokens lie in buckets scoring >= tau, so the
+// k-th token's bucket does too.
 constexpr int kPerLeafMaxLeaves = 96 * kLeavesPerBlock;
 constexpr int kHistStride = 257;   // padded: neighbouring queries fall in different banks
 
@@ -313,30 +313,48 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
     const float* cb32 = reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent;
     const uint32_t* meta = cv.meta + bg * cv.s_meta;
 
-    uint4 na0 = {0, 0, 0, 0}, na1 = {0, 0, 0, 0}, nm = {0, 0, 0, 0};
-    if (maxNLv > 0) {
-        if constexpr (BF16) load_cent_bf16(cb16, 0, na0, na1);
-        if constexpr (PASS == 0) nm = *reinterpret_cast<const uint4*>(meta + 4 * h);
+    // Tiles visited: all of them, or in pass 0 with many visible buckets only
+    // those of every other block (a sample: its buckets above tau still hold
+    // >= k eligible tokens, so tau stays a valid bound, for half the work).
+    const bool sample = PASS == 0 && !perleaf;
+    const int ntl_all = maxNLv / 16;
+    const int ntl = sample ? 4 * ((ntl_all / 4 + 1) / 2) : ntl_all;
+    auto tile_x = [&](int idx) -> int64_t {
+        return sample ? (int64_t)(8 * (idx / 4) + (idx & 3)) * 16 : (int64_t)idx * 16;
+    };
+    // A ring of DEPTH tiles in flight: tile idx + DEPTH is loaded once tile idx is scored (loads are
+    // unconditional: past the last tile they repeat it, so they never serialise on a branch)
+    constexpr int DEPTH = 4;
+    uint4 ra[DEPTH][2], rm[DEPTH];
+    auto load_tile = [&](int idx, uint4 (&a)[2], uint4& m) {
+        const int64_t x = tile_x(idx < ntl ? idx : (ntl > 0 ? ntl - 1 : 0));
+        if constexpr (BF16) load_cent_bf16(cb16, x, a[0], a[1]);
+        if constexpr (PASS == 0) m = *reinterpret_cast<const uint4*>(meta + x + 4 * h);
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        ra[d][0] = ra[d][1] = rm[d] = uint4{0, 0, 0, 0};
+        if (ntl > 0) load_tile(d, ra[d], rm[d]);
     }
-    uint32_t bmax = 0;
-    for (int64_t x0 = 0; x0 < maxNLv; x0 += 16) {
-        const uint4 a0 = na0, a1 = na1, m4 = nm;
-        if (x0 + 16 < maxNLv) {
-            if constexpr (BF16) load_cent_bf16(cb16, x0 + 16, na0, na1);
-            if constexpr (PASS == 0) nm = *reinterpret_cast<const uint4*>(meta + x0 + 16 + 4 * h);
-        }
-        f32x4 vals;
-        if constexpr (BF16)
-            vals = mfma_tile_bf16(a0, a1, qf, sa.G);
-        else
-            vals = score_tile_f32(cb32, x0, qf32, qv, sa.G);
-        const int64_t xb = x0 + 4 * h;
-        const bool edge = x0 + 16 > minNLv;
-        const int64_t lo = (x0 / kLeavesPerBlock) * (int64_t)kBlockTokens;
-        if constexpr (PASS == 0) {
-            const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w};
-            const bool elig = qv && lo >= q.sink_end && lo + kBlockTokens <= q.l0;
-            if (perleaf) {
+    for (int i0 = 0; i0 < ntl; i0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int idx = i0 + d;
+            if (idx >= ntl) break;
+            const int64_t x0 = tile_x(idx);
+            f32x4 vals;
+            if constexpr (BF16)
+                vals = mfma_tile_bf16(ra[d][0], ra[d][1], qf, sa.G);
+            else
+                vals = score_tile_f32(cb32, x0, qf32, qv, sa.G);
+            const uint4 m4 = rm[d];
+            load_tile(idx + DEPTH, ra[d], rm[d]);
+            const int64_t xb = x0 + 4 * h;
+            const bool edge = x0 + 16 > minNLv;
+            const int64_t lo = (x0 / kLeavesPerBlock) * (int64_t)kBlockTokens;
+            if constexpr (PASS == 0) {
+                const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w};
+                const bool elig = qv && lo >= q.sink_end && lo + kBlockTokens <= q.l0;
                 if (elig) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
@@ -346,27 +364,11 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const uint32_t key = (__float_as_uint(vals[v] + 2.0f) & ~0xFu) | ((mm[v] & 0xFFu) - 1u);
-                    const bool ok = !edge || (xb + v < NLv);
-                    bmax = (ok && key > bmax) ? key : bmax;
-                }
-                if (((x0 / 16) & 3) == 3) {   // end of a cluster block: bin its best bucket
-                    uint32_t o = __shfl_xor(bmax, 16);
-                    bmax = o > bmax ? o : bmax;
-                    o = __shfl_xor(bmax, 32);
-                    bmax = o > bmax ? o : bmax;
-                    if (h == 0 && elig && bmax != 0u)
-                        myhist[score_bin(__uint_as_float(bmax & ~0xFu) - 2.0f)] += (uint32_t)kPool * ((bmax & 0xFu) + 1u);
-                    bmax = 0;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bool pred = (!edge || (xb + v < NLv)) && qv && vals[v] >= tau_n;
-                if (pred) {
-                    const int pos = atomicAdd(&lcnt[wid][n], 1);
-                    if (pos < kCandCap) cand[u * kCandCap + pos] = rank_key(vals[v], (uint32_t)(xb + v));
+                    const bool pred = (!edge || (xb + v < NLv)) && qv && vals[v] >= tau_n;
+                    if (pred) {
+                        const int pos = atomicAdd(&lcnt[wid][n], 1);
+                        if (pos < kCandCap) cand[u * kCandCap + pos] = rank_key(vals[v], (uint32_t)(xb + v));
+                    }
                 }
             }
         }
