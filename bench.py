@@ -111,55 +111,71 @@ def selected_bytes(cfg, n_q_total, lr_total, q_pos_all, tile=64):
     return keys * 2 * row + 2 * n_q_total * cfg.H_q * row
 
 
-def cpu_baseline(cfg, inp_cpu, budget_s=25.0):
-    """Oracle timed on this host: Ward on sampled blocks and select + attend
-    for sampled queries against the oracle's own cache of those blocks; the
-    full-layer time is projected from the measured per-unit costs."""
+_CPU_CTX = {}
+
+
+def _cpu_units(items):
+    """select + attend of the oracle for a list of (position, query rows) (one process, one BLAS thread)."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    c = _CPU_CTX
+    cfg, cache, Kg, Vg, W = c["cfg"], c["cache"], c["Kg"], c["Vg"], c["W"]
+    scale = 1 / math.sqrt(cfg.d)
+    with threadpool_limits(1):
+        for t, qg in items:
+            qh = O.query_latent(qg, W, cfg.dtype)
+            if cfg.search == "tree":
+                lr, _ = O.select_tree(qh, cache, int(t), cfg.k, cfg.n_sinks, cfg.window, cfg.beam)
+            else:
+                lr, _ = O.select_flat(qh, cache, int(t), cfg.k, cfg.n_sinks, cfg.window)
+            O.attend(qg, Kg, Vg, int(t), lr, cfg.n_sinks, cfg.window, cache["n_blocks"], scale)
+    return len(items)
+
+
+def cpu_baseline(cfg, inp_cpu, n_units=1500):
+    """Oracle timed on this host: Ward on every block of KV head 0 of a CPU-generated layer, and
+    select + attend for n_units (query, KV head) units against the oracle's own cache of those
+    blocks, both spread over one process per core; the full-layer time is projected from the
+    measured per-unit costs."""
     import oracle as O
 
     cores = len(os.sched_getaffinity(0))
     procs = max(1, min(cores, 16))
     nb = inp_cpu["K"].shape[2] // 2048
-    K = [inp_cpu["K"][0, 0, : nb * 2048].double().numpy()]
+    Kg = inp_cpu["K"][0, 0, : nb * 2048].double().numpy()
     W = inp_cpu["W"].double().numpy()
-    e = [O.pooled_entries(O.key_latents(K[0], W))]
-    blocks = [e[0][b * 512:(b + 1) * 512] for b in range(nb)]
+    e = O.pooled_entries(O.key_latents(Kg, W))
+    blocks = [e[b * 512:(b + 1) * 512] for b in range(nb)]
     t0 = time.perf_counter()
     clusters = O.ward_blocks(blocks, processes=procs)
     t_ward = time.perf_counter() - t0
-    per_block = t_ward * procs / nb                      # single-core seconds per block
     tree = cfg.search == "tree"
-    cache = O.build_head_cache(K[0], W, cfg.dtype, T=nb * 2048, clusters=clusters, tree=tree)
-    Q = inp_cpu["Q"][0]
-    Kg, Vg = K[0], inp_cpu["V"][0, 0, : nb * 2048].double().numpy()
+    cache = O.build_head_cache(Kg, W, cfg.dtype, T=nb * 2048, clusters=clusters, tree=tree)
+    _CPU_CTX.update(cfg=cfg, cache=cache, Kg=Kg, Vg=inp_cpu["V"][0, 0, : nb * 2048].double().numpy(), W=W)
     rng = np.random.default_rng(0)
-    ts = rng.integers((nb - 1) * 2048, nb * 2048, 200)
-    scale = 1 / math.sqrt(cfg.d)
+    ts = rng.integers((nb - 1) * 2048, nb * 2048, n_units)
+    items = [(int(t), inp_cpu["Q"][0, int(t), : cfg.G].double().numpy()) for t in ts]   # plain arrays before forking
+    parts = [items[i::procs] for i in range(procs)]
     t0 = time.perf_counter()
-    for t in ts:
-        qg = Q[int(t), : cfg.G].double().numpy()
-        qh = O.query_latent(qg, W, cfg.dtype)
-        if tree:
-            lr, _ = O.select_tree(qh, cache, int(t), cfg.k, cfg.n_sinks, cfg.window, cfg.beam)
-        else:
-            lr, _ = O.select_flat(qh, cache, int(t), cfg.k, cfg.n_sinks, cfg.window)
-        O.attend(qg, Kg, Vg, int(t), lr, cfg.n_sinks, cfg.window, cache["n_blocks"], scale)
-    per_unit = (time.perf_counter() - t0) / len(ts)      # at (nb-1)*64 visible buckets
-    # projection: flat selection cost grows with the visible buckets, tree
-    # selection with the depth; the rest is per unit
+    with mp.get_context("fork").Pool(procs) as pool:
+        pool.map(_cpu_units, parts)
+    t_units = time.perf_counter() - t0
+    # full-layer projection: Ward per block, and select + attend per (query, KV head) unit; flat
+    # selection cost grows with the visible buckets, tree selection with the depth
     leaves_sample = (nb - 1) * 64
     mean_leaves = 64 * (cfg.T // 2048 - 1) / 2
     if tree:
         leaves_sample, mean_leaves = math.log2(max(2, leaves_sample)), math.log2(max(2, mean_leaves))
-    full_s = (cfg.T // 2048) * cfg.H_kv * per_block + cfg.T * cfg.H_kv * per_unit * max(1.0, mean_leaves / leaves_sample)
-    full_s /= procs
+    wall_per_block = t_ward / nb                 # with procs processes
+    wall_per_unit = t_units / n_units
+    full_s = (cfg.T // 2048) * cfg.H_kv * wall_per_block + \
+        cfg.T * cfg.H_kv * wall_per_unit * max(1.0, mean_leaves / leaves_sample)
     return dict(value=cfg.T / full_s, unit="tokens/s", cores=procs, kind="oracle",
                 sample=(f"the same topic-mixture recipe generated on the CPU at T={nb * 2048}: oracle Ward on its {nb} "
-                        f"blocks of KV head 0 ({t_ward:.1f}s wall on {procs} processes) and "
-                        f"select+attend for {len(ts)} (query, KV head) units at {(nb - 1) * 64} visible buckets "
-                        f"({per_unit * len(ts):.1f}s, 1 process); full 1-layer time projected as "
-                        f"blocks*H_kv*t_block + T*H_kv*t_unit*(mean visible buckets / sampled), divided by "
-                        f"{procs} processes"))
+                        f"blocks of KV head 0 ({t_ward:.1f}s wall) and select+attend for {n_units} (query, KV head) "
+                        f"units at {(nb - 1) * 64} visible buckets ({t_units:.1f}s wall), each spread over {procs} "
+                        f"processes ({(t_ward + t_units) * procs:.0f} core-seconds); full 1-layer time projected as "
+                        f"blocks*H_kv*t_block + T*H_kv*t_unit*(mean visible buckets / sampled)"))
 
 
 def traffic_for(kernel_src: str, key: str):
