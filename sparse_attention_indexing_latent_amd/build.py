@@ -20,7 +20,9 @@ SOURCES = ["lsa_api.cpp", "lsa_build.hip", "lsa_select.hip", "lsa_attend.hip"]
 ARCH = os.environ.get("LSA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU forms are kept out of the generated code
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results in VGPRs: the VALU reads them without accvgpr moves
+         "-mllvm", "--amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

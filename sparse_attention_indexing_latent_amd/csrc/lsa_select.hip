@@ -392,6 +392,142 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
     }
 }
 
+// ------------------------------------------------------------------ candidate pass, LDS-staged (bf16)
+// Pass 1 of the fused flat scan with the centroid tiles shared through LDS:
+// a workgroup owns 128 queries of one KV head (32 per wave, as two 16-query
+// MFMA column groups), streams the visible tiles in chunks of 8 (16 KB,
+// double-buffered; each thread copies 64 B of a chunk, a ring one chunk
+// ahead) and every wave reads the operand fragments from LDS.  A fragment
+// read feeds 2 x G x 2 MFMAs, and the L2 traffic is a quarter of per-wave
+// loads.  Output as pass 1: every visible bucket scoring >= tau of its query
+// is appended (rank key) to the query's candidate list (capped at kCandCap,
+// the count is exact).
+constexpr int kScanQ = 128;         // queries per workgroup
+constexpr int kScanChunk = 8;       // tiles per staged chunk
+
+template <int G>
+__global__ __launch_bounds__(256) void scan_collect_kernel(CacheView cv, const uint16_t* __restrict__ qhat,
+                                                           const int64_t* __restrict__ q_pos, SelArgs sa,
+                                                           const float* __restrict__ tau, int* __restrict__ cnt,
+                                                           uint64_t* __restrict__ cand) {
+    __shared__ __align__(16) uint4 stage[2][kScanChunk * 128];   // 2 x 16 KB
+    __shared__ int lcnt[4][2][16];
+    __shared__ int wmax[4];
+    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
+    const int64_t b = blockIdx.z, g = blockIdx.y;
+    const int64_t bg = b * sa.H_kv + g;
+    // per column group cg: this lane's query (column n)
+    int64_t iq[2], u[2];
+    int NLv[2];
+    bool qv[2];
+    float tq[2];
+    bf16x8 qf[2][G][2];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+        iq[cg] = (int64_t)blockIdx.x * kScanQ + wid * 32 + cg * 16 + n;
+        qv[cg] = iq[cg] < sa.n_q;
+        const int64_t t = qv[cg] ? q_pos[b * sa.n_q + iq[cg]] : -1;
+        const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
+        NLv[cg] = t < 0 ? 0 : kLeavesPerBlock * q.nvis;
+        u[cg] = (b * sa.n_q + iq[cg]) * sa.H_kv + g;
+        tq[cg] = qv[cg] ? tau[u[cg]] : 0.f;
+        const int64_t qrow = ((b * sa.n_q + (qv[cg] ? iq[cg] : 0)) * sa.H_q + g * sa.G) * kLatent;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            uint4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+            if (qv[cg]) {
+                const uint4* p = reinterpret_cast<const uint4*>(qhat + qrow + hh * kLatent + 16 * h);
+                a = p[0];
+                c = p[1];
+            }
+            qf[cg][hh][0] = as_bf16x8(a);
+            qf[cg][hh][1] = as_bf16x8(c);
+        }
+    }
+    if (l < 32) lcnt[wid][l >> 4][l & 15] = 0;
+    // tiles visible to any query of the workgroup
+    const int wm = wave_max_i(max(NLv[0], NLv[1]));
+    if (l == 0) wmax[wid] = wm;
+    __syncthreads();
+    const int maxNLv = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const int ntl = maxNLv / 16;
+    const int nch = (ntl + kScanChunk - 1) / kScanChunk;
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
+    // staging: thread tid copies words tid + 256 j (j < 4) of a chunk; words past the last tile repeat it
+    u32x4 r0, r1, r2, r3;
+#define LSA_LOAD_CHUNK(c)                                                                                    \
+    {                                                                                                        \
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src);                                               \
+        r0 = s4[(int64_t)min((c) * kScanChunk + (tid) / 128, ntl - 1) * 128 + (tid & 127)];                  \
+        r1 = s4[(int64_t)min((c) * kScanChunk + (tid + 256) / 128, ntl - 1) * 128 + (tid & 127)];            \
+        r2 = s4[(int64_t)min((c) * kScanChunk + (tid + 512) / 128, ntl - 1) * 128 + (tid & 127)];            \
+        r3 = s4[(int64_t)min((c) * kScanChunk + (tid + 768) / 128, ntl - 1) * 128 + (tid & 127)];            \
+    }
+#define LSA_STORE_CHUNK(bf)                                                                                  \
+    {                                                                                                        \
+        u32x4* d4 = reinterpret_cast<u32x4*>(stage[bf]);                                                     \
+        d4[tid] = r0;                                                                                        \
+        d4[tid + 256] = r1;                                                                                  \
+        d4[tid + 512] = r2;                                                                                  \
+        d4[tid + 768] = r3;                                                                                  \
+    }
+    if (nch > 0) {
+        LSA_LOAD_CHUNK(0)
+        LSA_STORE_CHUNK(0)
+    }
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) LSA_LOAD_CHUNK(c + 1)
+        const uint4* sb = stage[c & 1];
+        const int tend = min(kScanChunk, ntl - c * kScanChunk);
+        for (int tt = 0; tt < tend; ++tt) {
+            const int x0 = (c * kScanChunk + tt) * 16;
+            const bf16x8 a0 = as_bf16x8(sb[tt * 128 + l]), a1 = as_bf16x8(sb[tt * 128 + 64 + l]);
+            const int xb = x0 + 4 * h;
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg) {
+                f32x4 best;
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[cg][hh][0], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[cg][hh][1], acc, 0, 0, 0);
+                    if (hh == 0) {
+                        best = acc;
+                    } else {
+                        best[0] = fmaxf(best[0], acc[0]);
+                        best[1] = fmaxf(best[1], acc[1]);
+                        best[2] = fmaxf(best[2], acc[2]);
+                        best[3] = fmaxf(best[3], acc[3]);
+                    }
+                }
+                // buckets of this lane's query at or above its bound (rare): one branch per group
+                const int lim = qv[cg] ? NLv[cg] - xb : 0;   // buckets xb + v with v < lim are visible
+                const uint32_t m = (best[0] >= tq[cg] && 0 < lim ? 1u : 0u) | (best[1] >= tq[cg] && 1 < lim ? 2u : 0u) |
+                                   (best[2] >= tq[cg] && 2 < lim ? 4u : 0u) | (best[3] >= tq[cg] && 3 < lim ? 8u : 0u);
+                if (m) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        if (m & (1u << v)) {
+                            const int pos = atomicAdd(&lcnt[wid][cg][n], 1);
+                            if (pos < kCandCap) cand[u[cg] * kCandCap + pos] = rank_key(best[v], (uint32_t)(xb + v));
+                        }
+                    }
+                }
+            }
+        }
+        if (c + 1 < nch) LSA_STORE_CHUNK((c + 1) & 1)
+        __syncthreads();
+    }
+#undef LSA_LOAD_CHUNK
+#undef LSA_STORE_CHUNK
+    if (h == 0) {
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg)
+            if (qv[cg]) cnt[u[cg]] = lcnt[wid][cg][n];
+    }
+}
+
 // ------------------------------------------------------------------ wave-level finish
 // Bitonic sort, descending, of 64 N 64-bit keys held in registers: element
 // e = 64 i + lane is v[i].  Compare-exchanges across lanes use xor shuffles,
@@ -1610,8 +1746,18 @@ hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_
     if (bf16) {
         hipLaunchKernelGGL((fused_scan_kernel<true, 0>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, sb.tau, sb.cnt,
                            sb.cand);
-        hipLaunchKernelGGL((fused_scan_kernel<true, 1>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, sb.tau, sb.cnt,
-                           sb.cand);
+        const dim3 g2((unsigned)((sa.n_q + kScanQ - 1) / kScanQ), (unsigned)sa.H_kv, (unsigned)B);
+        const uint16_t* qh = static_cast<const uint16_t*>(sb.qhat);
+        switch (sa.G) {
+#define LSA_SCAN_G(GG)                                                                                              \
+    case GG:                                                                                                        \
+        hipLaunchKernelGGL(scan_collect_kernel<GG>, g2, dim3(256), 0, st, cv, qh, q_pos, sa, sb.tau, sb.cnt, sb.cand); \
+        break;
+            LSA_SCAN_G(1) LSA_SCAN_G(2) LSA_SCAN_G(3) LSA_SCAN_G(4) LSA_SCAN_G(5) LSA_SCAN_G(6) LSA_SCAN_G(7)
+            LSA_SCAN_G(8)
+#undef LSA_SCAN_G
+            default: return hipErrorInvalidValue;
+        }
     } else {
         hipLaunchKernelGGL((fused_scan_kernel<false, 0>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, sb.tau,
                            sb.cnt, sb.cand);
