@@ -84,8 +84,12 @@ def prefill_step(cfg, G, ws, timers=None, tree=False, O=None):
         if tm:
             e.record()
             e = tm["attend"].span()
-        lsa.sparse_attend(Qc, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window,
-                          O=O[:, i0:i1])
+        if "bm" in ws:
+            lsa.sparse_attend_bucket_major(Qc, G["K"], G["V"], qp, lr, cnt, cache, cfg.k, cfg.n_sinks, cfg.window,
+                                           O=O[:, i0:i1], workspace=ws["bm"])
+        else:
+            lsa.sparse_attend(Qc, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window,
+                              O=O[:, i0:i1])
         if tm:
             e.record()
         if "cnt_sum" in ws:
@@ -219,6 +223,15 @@ def run_prefill(args, cid):
                                         min(CHUNK, n_q), cfg.H_q)
     ws["sel"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws["cache"] = cache0.buf
+    if args.attend == "bucket":
+        # passes of up to 16384 queries, fewer if free memory is short (workspace <= 40% of it)
+        free = torch.cuda.mem_get_info(dev)[0]
+        n_pass = 16384
+        while n_pass > 1024 and lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass) > 0.4 * free:
+            n_pass //= 2
+        ws["bm"] = torch.empty(lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass),
+                               dtype=torch.uint8, device=dev)
+        log(f"bucket-major attention, passes of {n_pass} queries, workspace {ws['bm'].numel() / 2**30:.1f} GiB")
     ws["cnt_sum"] = 0
     log("warmup")
     for _ in range(args.warmup):
@@ -253,7 +266,7 @@ def run_prefill(args, cid):
         data="synthetic (seeded topic-mixture keys, random-init projection)",
         config={"workload": cfg.name, "T": cfg.T, "H_kv": cfg.H_kv, "H_q": cfg.H_q, "head_dim": cfg.d,
                 "k": cfg.k, "n_sinks": cfg.n_sinks, "window": cfg.window, "search": cfg.search,
-                "beam": cfg.beam, "query_chunk": CHUNK},
+                "beam": cfg.beam, "query_chunk": CHUNK, "attention": args.attend},
         breakdown_ms={"build_buckets": timers["build"].total_ms() / args.steps,
                       "select": timers["select"].total_ms() / args.steps, "sparse_attend": att_ms},
         roofline={"kernel": "attend_bf16_kernel<128>", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -402,6 +415,8 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=4, choices=[2, 4, 5])
+    ap.add_argument("--attend", default="gather", choices=["gather", "bucket"],
+                    help="prefill attention: per-query gather, or bucket-major (each bucket's K/V read once per pass)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate", action="store_true",

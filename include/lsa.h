@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 1
+#define LSA_ABI_VERSION 2
 
 #define LSA_LATENT_DIM 64         /* latent width (ch.2: 64-d index space) */
 #define LSA_POOL 4                /* keys pooled per entry (ch.2)            */
@@ -134,7 +134,10 @@ typedef struct lsa_select_cfg {
  * [n_blocks_max, 512] uint16 (each block's entry indices grouped by bucket,
  * ascending inside a bucket), entry_leaf [n_blocks_max, 512] uint8 (bucket
  * rank of every entry), tree_cent / tree_sums [nodes_max, 64] for the tree
- * levels above the leaves (level l >= 1 starts at node level_off[l]). */
+ * levels above the leaves (level l >= 1 starts at node level_off[l]),
+ * entry_pos [n_blocks_max, 512] uint8 (position of every entry inside its
+ * bucket's member list, so token 4e + j of a bucket is its key number
+ * 4 * entry_pos[e] + j in member order). */
 typedef struct lsa_cache_info {
     int64_t n_blocks_max;
     int64_t leaves_max;
@@ -149,6 +152,7 @@ typedef struct lsa_cache_info {
     size_t stride_cent, stride_sums, stride_meta, stride_members, stride_entry_leaf,
            stride_tree_cent, stride_tree_sums;   /* bytes between consecutive (b, g) */
     size_t total_bytes;
+    size_t off_entry_pos, stride_entry_pos;
 } lsa_cache_info;
 
 /* Bytes of a bucket cache for `batch` sequences of up to t_max tokens.
@@ -211,6 +215,36 @@ lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg
                              const int64_t* q_pos, int64_t batch, int64_t n_q,
                              const int32_t* lr_idx, const int32_t* lr_cnt, float scale, void* O,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lsa_sparse_attend_bucket_major needs to process n_q_pass
+ * queries per sequence in one pass (a cache for t_max tokens).  Host only.
+ * Dominated by one fp32 partial per (query, KV head, bucket) pair: about
+ * 80 * G * (4 d + 8) bytes per (query, KV head). */
+lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg,
+                                                   int64_t batch, int64_t n_q_pass, int64_t t_max, size_t* bytes);
+
+/* The same attention as lsa_sparse_attend, computed bucket-major (diosapp
+ * section 二 for the attention; zhichai.net "卡片柜" ch.3 for the long-range
+ * keys being whole buckets): the (query, bucket) pairs of a pass of queries
+ * are grouped by bucket through the cache's entry_leaf / entry_pos maps, each
+ * bucket's keys and values are read once for every query that listed any of
+ * them, and the per-pair softmax partials are merged with the sinks + window
+ * part by a log-sum-exp combine.  Outputs equal lsa_sparse_attend's up to
+ * the order of the fp32 sums.  Arguments as for lsa_sparse_attend plus the
+ * cache (built with T tokens for t_max) and a workspace of at least
+ * lsa_attend_bucket_major_workspace_bytes(.., 1, ..); the call then runs
+ * ceil(n_q / P) passes, P the most queries the workspace holds.  A
+ * (query, KV head) whose list is not strictly ascending, holds a token outside
+ * [sink end, window start), touches more than 256 buckets, or finds the pass's
+ * pair pool full is gathered whole instead (same result, slower).  bf16 only
+ * (LSA_ERR_UNSUPPORTED otherwise); lr_idx rows must not be modified while
+ * the call's kernels run. */
+lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache,
+                                          size_t cache_bytes, int64_t t_max, const void* Q, const void* K,
+                                          const void* V, int64_t t_cap, int64_t T, const int64_t* q_pos,
+                                          int64_t batch, int64_t n_q, const int32_t* lr_idx, const int32_t* lr_cnt,
+                                          float scale, void* O, void* workspace, size_t workspace_bytes,
+                                          void* stream);
 
 /* Human-readable status name; detail of the last failed call on this thread. */
 const char* lsa_status_string(lsa_status status);

@@ -24,8 +24,9 @@ from . import _lib
 from ._lib import (LsaError, Layout, SelectCfg, CacheInfo, LSA_BF16, LSA_F32, LSA_SEARCH_FLAT, LSA_SEARCH_TREE,
                    LSA_STRATEGY_AUTO, LSA_STRATEGY_FUSED, LSA_STRATEGY_MATERIALIZED)
 
-__all__ = ["build_buckets", "select", "sparse_attend", "LsaCache", "LsaError", "make_layout", "select_cfg",
-           "library_path", "select_workspace_bytes", "attend_workspace_bytes"]
+__all__ = ["build_buckets", "select", "sparse_attend", "sparse_attend_bucket_major", "LsaCache", "LsaError",
+           "make_layout", "select_cfg", "library_path", "select_workspace_bytes", "attend_workspace_bytes",
+           "attend_bucket_major_workspace_bytes"]
 
 _STRATEGIES = {"auto": LSA_STRATEGY_AUTO, "fused": LSA_STRATEGY_FUSED, "materialized": LSA_STRATEGY_MATERIALIZED}
 
@@ -109,6 +110,11 @@ class LsaCache:
     def entry_leaf(self) -> torch.Tensor:
         i = self.info()
         return self._region(i.off_entry_leaf, i.stride_entry_leaf, i.n_blocks * 512, torch.uint8, (i.n_blocks, 512))
+
+    def entry_pos(self) -> torch.Tensor:
+        """[B, H_kv, n_blocks, 512] position of each entry inside its bucket's member list."""
+        i = self.info()
+        return self._region(i.off_entry_pos, i.stride_entry_pos, i.n_blocks * 512, torch.uint8, (i.n_blocks, 512))
 
     def tree_level(self, lev: int):
         """(centroids, sums) of tree level lev (0 = leaves)."""
@@ -216,4 +222,40 @@ def sparse_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torc
                                    ctypes.c_float(scale), _ptr(O), _ptr(workspace) if n.value > 0 else ctypes.c_void_p(0),
                                    workspace.numel() if (workspace is not None and n.value > 0) else 0,
                                    _stream(Q.device)))
+    return O
+
+
+def attend_bucket_major_workspace_bytes(cache: LsaCache, n_q_heads: int, head_dim: int, n_q_pass: int) -> int:
+    """Workspace bytes of one bucket-major pass over n_q_pass queries per sequence."""
+    layout = make_layout(head_dim, cache.layout.n_kv_heads, n_q_heads, torch.bfloat16)
+    n = ctypes.c_size_t()
+    _lib.check(_lib.lib().lsa_attend_bucket_major_workspace_bytes(ctypes.byref(layout),
+                                                                  ctypes.byref(select_cfg(0, 0, 1)), cache.batch,
+                                                                  n_q_pass, cache.t_max, ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attend_bucket_major(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torch.Tensor,
+                               lr_idx: torch.Tensor, lr_cnt: torch.Tensor, cache: LsaCache, k: int, n_sinks: int,
+                               window: int, scale: Optional[float] = None, O: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None, n_q_pass: int = 16384) -> torch.Tensor:
+    """sparse_attend computed bucket-major (bf16): same outputs, each bucket's K/V read once per pass.
+
+    Without a workspace, one for passes of min(n_q, n_q_pass) queries is allocated.
+    """
+    assert Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()
+    B, n_q, H_q, d = Q.shape
+    _, H_kv, t_cap, _ = K.shape
+    layout = make_layout(d, H_kv, H_q, Q.dtype)
+    cfg = select_cfg(k, n_sinks, window)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if O is None:
+        O = torch.empty_like(Q)
+    if workspace is None:
+        nbytes = attend_bucket_major_workspace_bytes(cache, H_q, d, max(1, min(n_q, n_q_pass)))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    _lib.check(_lib.lib().lsa_sparse_attend_bucket_major(
+        ctypes.byref(layout), ctypes.byref(cfg), _ptr(cache.buf), cache.buf.numel(), cache.t_max, _ptr(Q), _ptr(K),
+        _ptr(V), t_cap, cache.T, _ptr(q_pos), B, n_q, _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt),
+        ctypes.c_float(scale), _ptr(O), _ptr(workspace), workspace.numel(), _stream(Q.device)))
     return O

@@ -36,7 +36,8 @@ STATUS_NAMES = {
 # every symbol include/lsa.h declares
 EXPORTS = [
     "lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_select_workspace_bytes", "lsa_select",
-    "lsa_attend_workspace_bytes", "lsa_sparse_attend", "lsa_status_string", "lsa_last_error", "lsa_abi_version",
+    "lsa_attend_workspace_bytes", "lsa_sparse_attend", "lsa_attend_bucket_major_workspace_bytes",
+    "lsa_sparse_attend_bucket_major", "lsa_status_string", "lsa_last_error", "lsa_abi_version",
 ]
 
 
@@ -58,7 +59,7 @@ class CacheInfo(ctypes.Structure):
     ] + [(n, ctypes.c_size_t) for n in (
         "off_cent", "off_sums", "off_meta", "off_members", "off_entry_leaf", "off_tree_cent", "off_tree_sums",
         "stride_cent", "stride_sums", "stride_meta", "stride_members", "stride_entry_leaf", "stride_tree_cent",
-        "stride_tree_sums", "total_bytes")]
+        "stride_tree_sums", "total_bytes", "off_entry_pos", "stride_entry_pos")]
 
 
 class LsaError(RuntimeError):
@@ -88,8 +89,12 @@ def lib():
     L.lsa_attend_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, P(sz)]
     L.lsa_sparse_attend.argtypes = [P(Layout), P(SelectCfg), vp, vp, vp, i64, i64, vp, i64, i64, vp, vp,
                                     ctypes.c_float, vp, vp, sz, vp]
+    L.lsa_attend_bucket_major_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, i64, P(sz)]
+    L.lsa_sparse_attend_bucket_major.argtypes = [P(Layout), P(SelectCfg), vp, sz, i64, vp, vp, vp, i64, i64, vp,
+                                                 i64, i64, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     for name in ("lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_select_workspace_bytes",
-                 "lsa_select", "lsa_attend_workspace_bytes", "lsa_sparse_attend"):
+                 "lsa_select", "lsa_attend_workspace_bytes", "lsa_sparse_attend",
+                 "lsa_attend_bucket_major_workspace_bytes", "lsa_sparse_attend_bucket_major"):
         getattr(L, name).restype = ctypes.c_int
     L.lsa_status_string.argtypes = [ctypes.c_int]
     L.lsa_status_string.restype = ctypes.c_char_p

@@ -61,8 +61,8 @@ struct CacheGeom {
     int32_t elt;
     int64_t level_off[lsa::kMaxLevels];
     int64_t level_size[lsa::kMaxLevels];
-    size_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums;   // bytes per (b, g)
-    size_t off_cent, off_sums, off_meta, off_members, off_eleaf, off_tcent, off_tsums, total;
+    size_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos;   // bytes per (b, g)
+    size_t off_cent, off_sums, off_meta, off_members, off_eleaf, off_tcent, off_tsums, off_epos, total;
 };
 
 int64_t tree_nodes_above(int64_t nl) {
@@ -104,6 +104,7 @@ void cache_geom(const lsa_layout* L, int64_t B, int64_t t_max, int64_t T, CacheG
     c.s_eleaf = align256((size_t)c.nbm * LSA_BLOCK_ENTRIES);
     c.s_tcent = align256((size_t)c.nnm * LSA_LATENT_DIM * c.elt);
     c.s_tsums = align256((size_t)c.nnm * LSA_LATENT_DIM * 4);
+    c.s_epos = align256((size_t)c.nbm * LSA_BLOCK_ENTRIES);
     size_t o = 0;
     c.off_cent = o;    o += c.s_cent * HB;
     c.off_sums = o;    o += c.s_sums * HB;
@@ -112,6 +113,7 @@ void cache_geom(const lsa_layout* L, int64_t B, int64_t t_max, int64_t T, CacheG
     c.off_eleaf = o;   o += c.s_eleaf * HB;
     c.off_tcent = o;   o += c.s_tcent * HB;
     c.off_tsums = o;   o += c.s_tsums * HB;
+    c.off_epos = o;    o += c.s_epos * HB;
     c.total = o > 0 ? o : 256;
 }
 
@@ -126,6 +128,7 @@ lsa::CacheView make_view(const CacheGeom& c, void* cache, bool bf16) {
     v.eleaf = reinterpret_cast<uint8_t*>(base + c.off_eleaf);
     v.tcent = base + c.off_tcent;
     v.tsums = reinterpret_cast<float*>(base + c.off_tsums);
+    v.epos = reinterpret_cast<uint8_t*>(base + c.off_epos);
     v.s_cent = (int64_t)(c.s_cent / c.elt);
     v.s_sums = (int64_t)(c.s_sums / 4);
     v.s_meta = (int64_t)(c.s_meta / 4);
@@ -133,6 +136,7 @@ lsa::CacheView make_view(const CacheGeom& c, void* cache, bool bf16) {
     v.s_eleaf = (int64_t)c.s_eleaf;
     v.s_tcent = (int64_t)(c.s_tcent / c.elt);
     v.s_tsums = (int64_t)(c.s_tsums / 4);
+    v.s_epos = (int64_t)c.s_epos;
     v.n_blocks = (int32_t)c.n_blocks;
     v.n_leaves = (int32_t)c.n_leaves;
     v.n_levels = c.n_levels;
@@ -181,6 +185,48 @@ uint32_t next_call_tag() {
     uint32_t t = tag.fetch_add(1, std::memory_order_relaxed);
     if (t == 0) t = tag.fetch_add(1, std::memory_order_relaxed);
     return t;
+}
+
+// Workspace of one bucket-major pass over nqp queries per sequence: the
+// per-bin counts and offsets, the per-unit slot ranges, the pair records and
+// the fp32 partials (max and denominator, D values) of every pair slot.  The
+// pool holds kBmPoolPerUnit slots per unit on average (a unit takes one per
+// bucket it reads from, about k / 32 with buckets of 8 entries).
+constexpr int64_t kBmPoolPerUnit = 80;
+
+struct BmWs {
+    int64_t units, leaves_max, nbins, nbins_pad;
+    uint32_t pool_cap;
+    size_t off_lcnt, off_loff, off_ctot, off_csum, off_uoff, off_unp, off_runit, off_rbin, off_rrank, off_rmask,
+        off_sorted, off_po, off_pml, total;
+};
+
+void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) {
+    memset(&w, 0, sizeof(w));
+    const int64_t H_kv = L->n_kv_heads, G = L->n_q_heads / L->n_kv_heads, D = L->head_dim;
+    w.units = B * nqp * H_kv;
+    w.leaves_max = (t_max / LSA_BLOCK_TOKENS) * LSA_LEAVES_PER_BLOCK;
+    w.nbins = B * H_kv * w.leaves_max;
+    const int64_t nch = (w.nbins + lsa::kBmScanChunk - 1) / lsa::kBmScanChunk;
+    w.nbins_pad = (nch > 0 ? nch : 1) * lsa::kBmScanChunk;
+    int64_t pool = w.units * kBmPoolPerUnit;
+    if (pool > ((int64_t)1 << 31)) pool = (int64_t)1 << 31;
+    w.pool_cap = (uint32_t)pool;
+    size_t o = 0;
+    w.off_lcnt = o;   o = align256(o + (size_t)(w.nbins_pad + 1) * 4);
+    w.off_loff = o;   o = align256(o + (size_t)w.nbins_pad * 4);
+    w.off_ctot = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 4);
+    w.off_csum = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 4);
+    w.off_uoff = o;   o = align256(o + (size_t)w.units * 4);
+    w.off_unp = o;    o = align256(o + (size_t)w.units * 4);
+    w.off_runit = o;  o = align256(o + (size_t)pool * 4);
+    w.off_rbin = o;   o = align256(o + (size_t)pool * 4);
+    w.off_rrank = o;  o = align256(o + (size_t)pool * 4);
+    w.off_rmask = o;  o = align256(o + (size_t)pool * 8);
+    w.off_sorted = o; o = align256(o + (size_t)pool * 4);
+    w.off_po = o;     o = align256(o + (size_t)pool * G * D * 4);
+    w.off_pml = o;    o = align256(o + (size_t)pool * G * 8);
+    w.total = o;
 }
 
 int resolve_strategy(const lsa_select_cfg* C, int64_t units) {
@@ -284,6 +330,8 @@ lsa_status lsa_cache_describe(const lsa_layout* layout, int64_t batch, int64_t t
     info->stride_tree_cent = c.s_tcent;
     info->stride_tree_sums = c.s_tsums;
     info->total_bytes = c.total;
+    info->off_entry_pos = c.off_epos;
+    info->stride_entry_pos = c.s_epos;
     return ok();
 }
 
@@ -427,7 +475,10 @@ lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg
         return fail(LSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     if (need > 0 && misaligned(workspace)) return fail(LSA_ERR_ALIGN, "workspace must be 16-byte aligned");
     lsa::AttArgs aa;
+    memset(&aa, 0, sizeof(aa));
     aa.n_q = n_q;
+    aa.q0 = 0;
+    aa.nqp = n_q;
     aa.n_units = units;
     aa.t_cap = t_cap;
     aa.B = (int32_t)batch;
@@ -448,6 +499,112 @@ lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg
                                       layout->dtype == LSA_BF16, O, static_cast<float*>(workspace),
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg,
+                                                   int64_t batch, int64_t n_q_pass, int64_t t_max, size_t* bytes) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (!cfg || !bytes) return fail(LSA_ERR_INVALID_ARG, "cfg and bytes must be non-NULL");
+    if (batch < 0 || n_q_pass < 0 || t_max < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    BmWs w;
+    bm_ws(layout, batch, n_q_pass, t_max, w);
+    *bytes = w.total;
+    return ok();
+}
+
+lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache,
+                                          size_t cache_bytes, int64_t t_max, const void* Q, const void* K,
+                                          const void* V, int64_t t_cap, int64_t T, const int64_t* q_pos,
+                                          int64_t batch, int64_t n_q, const int32_t* lr_idx, const int32_t* lr_cnt,
+                                          float scale, void* O, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (!cfg) return fail(LSA_ERR_INVALID_ARG, "cfg is NULL");
+    if (layout->dtype != LSA_BF16) return fail(LSA_ERR_UNSUPPORTED, "bucket-major attention is bf16 only");
+    if (batch < 0 || n_q < 0 || t_cap < 0 || T < 0 || t_max < 0)
+        return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (cfg->k < 0 || cfg->n_sinks < 0 || cfg->window < 1) return fail(LSA_ERR_INVALID_ARG, "bad k / n_sinks / window");
+    if (T > t_cap) return fail(LSA_ERR_CAPACITY, "T=%lld exceeds t_cap=%lld", (long long)T, (long long)t_cap);
+    if (T > t_max) return fail(LSA_ERR_CAPACITY, "T=%lld exceeds t_max=%lld", (long long)T, (long long)t_max);
+    if (!std::isfinite(scale)) return fail(LSA_ERR_INVALID_ARG, "scale must be finite");
+    const int64_t units = batch * n_q * layout->n_kv_heads;
+    if (units == 0) return ok();
+    if (!cache || !Q || !K || !V || !q_pos || !lr_cnt || (!lr_idx && cfg->k > 0) || !O || !workspace)
+        return fail(LSA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (misaligned(cache) || misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(q_pos) ||
+        misaligned(lr_cnt) || (lr_idx && misaligned(lr_idx)) || misaligned(O) || misaligned(workspace))
+        return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
+    CacheGeom c;
+    cache_geom(layout, batch, t_max, T, c);
+    if (cache_bytes < c.total) return fail(LSA_ERR_WORKSPACE, "cache has %zu bytes, needs %zu", cache_bytes, c.total);
+    // queries per pass: the most the workspace holds (the size is increasing in the pass length)
+    BmWs w;
+    bm_ws(layout, batch, 1, t_max, w);
+    if (workspace_bytes < w.total)
+        return fail(LSA_ERR_WORKSPACE, "workspace has %zu bytes, needs at least %zu", workspace_bytes, w.total);
+    int64_t lo = 1, hi = n_q;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        bm_ws(layout, batch, mid, t_max, w);
+        if (w.total <= workspace_bytes) lo = mid; else hi = mid - 1;
+    }
+    const int64_t nqp_max = lo;
+    if (w.nbins > (int64_t)0xFFFFFFFF) return fail(LSA_ERR_CAPACITY, "too many buckets for one pass");
+    const int G = layout->n_q_heads / layout->n_kv_heads;
+    lsa::CacheView v = make_view(c, const_cast<void*>(cache), true);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* wb = static_cast<char*>(workspace);
+    for (int64_t q0 = 0; q0 < n_q; q0 += nqp_max) {
+        const int64_t nqp = n_q - q0 < nqp_max ? n_q - q0 : nqp_max;
+        bm_ws(layout, batch, nqp, t_max, w);
+        lsa::BmBuffers bm;
+        bm.leaves_max = w.leaves_max;
+        bm.nbins = w.nbins;
+        bm.nbins_pad = w.nbins_pad;
+        bm.pool_cap = w.pool_cap;
+        bm.lcnt = reinterpret_cast<uint32_t*>(wb + w.off_lcnt);
+        bm.loff = reinterpret_cast<uint32_t*>(wb + w.off_loff);
+        bm.ctot = reinterpret_cast<uint32_t*>(wb + w.off_ctot);
+        bm.csum = reinterpret_cast<uint32_t*>(wb + w.off_csum);
+        bm.unit_off = reinterpret_cast<uint32_t*>(wb + w.off_uoff);
+        bm.unit_np = reinterpret_cast<int32_t*>(wb + w.off_unp);
+        bm.rec_unit = reinterpret_cast<uint32_t*>(wb + w.off_runit);
+        bm.rec_bin = reinterpret_cast<uint32_t*>(wb + w.off_rbin);
+        bm.rec_rank = reinterpret_cast<uint32_t*>(wb + w.off_rrank);
+        bm.rec_mask = reinterpret_cast<unsigned long long*>(wb + w.off_rmask);
+        bm.sorted = reinterpret_cast<uint32_t*>(wb + w.off_sorted);
+        bm.po = reinterpret_cast<float*>(wb + w.off_po);
+        bm.pml = reinterpret_cast<float*>(wb + w.off_pml);
+        lsa::AttArgs aa;
+        memset(&aa, 0, sizeof(aa));
+        aa.n_q = n_q;
+        aa.q0 = q0;
+        aa.nqp = nqp;
+        aa.n_units = w.units;
+        aa.t_cap = t_cap;
+        aa.B = (int32_t)batch;
+        aa.H_kv = layout->n_kv_heads;
+        aa.H_q = layout->n_q_heads;
+        aa.G = G;
+        aa.n_sinks = cfg->n_sinks;
+        aa.window = cfg->window;
+        aa.n_blocks = (int32_t)(T / LSA_BLOCK_TOKENS);
+        aa.k = cfg->k;
+        aa.splits = 1;
+        aa.scale = scale;
+        aa.bm_off = bm.unit_off;
+        aa.bm_np = bm.unit_np;
+        aa.bm_po = bm.po;
+        aa.bm_ml = bm.pml;
+        const int32_t* lr = lr_idx ? lr_idx : lr_cnt;
+        hipError_t e = lsa::launch_bucket_partials(v, Q, K, V, q_pos, lr, lr_cnt, aa, bm, layout->head_dim, st);
+        if (e == hipSuccess)
+            e = lsa::launch_attend_local(Q, K, V, q_pos, lr, lr_cnt, aa, layout->head_dim, O, st);
+        if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    }
     return ok();
 }
 

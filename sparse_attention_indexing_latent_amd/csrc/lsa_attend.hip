@@ -31,18 +31,57 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 // Unit order inside the kernel: KV head slowest, then sequence, then query,
 // so neighbouring waves (and, after the XCD remap, one XCD) handle
 // neighbouring queries of one head and share their local windows in L2.
+// u indexes the call's [B, n_q, H_kv] arrays, l the launch's own [B, nqp,
+// H_kv] ones (the same when a launch covers every query).
 struct AUnit {
-    int64_t b, i, g, u;
+    int64_t b, i, g, u, l;
 };
 __device__ __forceinline__ AUnit aunit_of(int64_t uu, const AttArgs& aa) {
     AUnit r;
-    const int64_t per_g = (int64_t)aa.B * aa.n_q;
+    const int64_t per_g = (int64_t)aa.B * aa.nqp;
     r.g = uu / per_g;
     const int64_t rem = uu % per_g;
-    r.b = rem / aa.n_q;
-    r.i = rem % aa.n_q;
+    r.b = rem / aa.nqp;
+    const int64_t il = rem % aa.nqp;
+    r.i = aa.q0 + il;
     r.u = (r.b * aa.n_q + r.i) * aa.H_kv + r.g;
+    r.l = (r.b * aa.nqp + il) * aa.H_kv + r.g;
     return r;
+}
+
+// Log-sum-exp merge of a unit's bucket partials of head hh (of its group)
+// into this lane's running state (lane (n, h) holds dims 32 (c/2) + 8h +
+// 4 (c%2) + [0, 4) of acc[c]); partials are read four at a time, a missing
+// one (past the unit's count) reads the first slot again with weight 0.
+template <int D>
+__device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t ul, int npl, int hh, int h,
+                                                      float& m_run, float& l_run, f32x4* acc) {
+    constexpr int NC = D / 16;
+    const int64_t s0 = aa.bm_off[ul];
+    for (int s = 0; s < npl; s += 4) {
+        float2 ml[4];
+        f32x4 o[4][NC];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t slot = (s0 + (s + j < npl ? s + j : 0)) * aa.G + hh;
+            ml[j] = *reinterpret_cast<const float2*>(aa.bm_ml + slot * 2);
+            const float* po = aa.bm_po + slot * D;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                o[j][c] = *reinterpret_cast<const f32x4*>(po + 32 * (c / 2) + 8 * h + 4 * (c % 2));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float mj = s + j < npl ? ml[j].x : kNegInf;
+            const float M = fmaxf(m_run, mj);
+            const float a = m_run > kNegInf ? __expf(m_run - M) : 0.f;
+            const float b = mj > kNegInf ? __expf(mj - M) : 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c] = acc[c] * a + o[j][c] * b;
+            l_run = l_run * a + ml[j].y * b;
+            m_run = M;
+        }
+    }
 }
 
 // Map the hardware workgroup id (dispatched round-robin over the 8 XCDs) to a
@@ -220,15 +259,15 @@ __device__ __forceinline__ void store_tile(const u32x4 (&kr)[TileLds<D>::NI], co
 }
 
 // One tile of 32 keys: S^T = K Q^T, online softmax, V^T via the identity
-// MFMA, O^T += V^T P^T.
+// MFMA, O^T += V^T P^T.  Bit v of ok_a (ok_b): key row 4h + v (16 + 4h + v)
+// of the tile counts for this lane's column; a column that has seen no key
+// yet keeps m = -inf and l = 0.
 template <int D>
-__device__ __forceinline__ void attend_tile(uint64_t ma, uint64_t mb, const uint8_t* buf, int r, const uint4* qf,
+__device__ __forceinline__ void attend_tile(uint32_t ok_a, uint32_t ok_b, const uint8_t* buf, int r, const uint4* qf,
                                             const s16x4& ident, int h, float scale, float& m_run, float& l_run,
                                             f32x4* acc) {
     using TL = TileLds<D>;
     constexpr int KS = D / 32, NC = D / 16;
-    // bit r of ma (mb): key row r (16 + r) of the tile is valid
-    if ((ma | mb) == 0ull) return;   // wave-uniform
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {   // K fragments: rows r and 16 + r, column 4 ks + h
@@ -242,21 +281,22 @@ __device__ __forceinline__ void attend_tile(uint64_t ma, uint64_t mb, const uint
     float mx = kNegInf;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        pa[v] = ((ma >> (4 * h + v)) & 1ull) ? sa[v] * scale : kNegInf;
-        pb[v] = ((mb >> (4 * h + v)) & 1ull) ? sb[v] * scale : kNegInf;
+        pa[v] = ((ok_a >> v) & 1u) ? sa[v] * scale : kNegInf;
+        pb[v] = ((ok_b >> v) & 1u) ? sb[v] * scale : kNegInf;
         mx = fmaxf(mx, fmaxf(pa[v], pb[v]));
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __expf(m_run - m_new);
+    const float alpha = m_run > kNegInf ? __expf(m_run - m_new) : 0.f;
     m_run = m_new;
     uint32_t pk[4];
     float psum = 0.f;
+    auto pexp = [m_new](float x) { return x > kNegInf ? __expf(x - m_new) : 0.f; };
 #pragma unroll
     for (int v = 0; v < 4; v += 2) {
-        const uint16_t a0 = f32_to_bf16(__expf(pa[v] - m_new)), a1 = f32_to_bf16(__expf(pa[v + 1] - m_new));
-        const uint16_t b0 = f32_to_bf16(__expf(pb[v] - m_new)), b1 = f32_to_bf16(__expf(pb[v + 1] - m_new));
+        const uint16_t a0 = f32_to_bf16(pexp(pa[v])), a1 = f32_to_bf16(pexp(pa[v + 1]));
+        const uint16_t b0 = f32_to_bf16(pexp(pb[v])), b1 = f32_to_bf16(pexp(pb[v + 1]));
         psum += bf16_to_f32(a0) + bf16_to_f32(a1) + bf16_to_f32(b0) + bf16_to_f32(b1);
         pk[v / 2] = (uint32_t)a0 | ((uint32_t)a1 << 16);
         pk[2 + v / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
@@ -306,7 +346,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const AUnit un = aunit_of(uu, aa);
     const int64_t t = q_pos[un.b * aa.n_q + un.i];
     // a count above k (never written by the selection) is clamped: the list row holds k entries
-    const int32_t cnt = min(lr_cnt[un.u], aa.k);
+    int32_t cnt = min(lr_cnt[un.u], aa.k);
+    int32_t npl = 0;
+    if (aa.bm_np != nullptr) {
+        npl = aa.bm_np[un.l];
+        if (npl >= 0 && cnt > 0) cnt = 0;   // the long-range keys arrive as bucket partials
+    }
     const int n = r;  // head column of the C layouts
     const int64_t orow = ((un.b * aa.n_q + un.i) * aa.H_q + un.g * aa.G + n) * D;
 
@@ -352,13 +397,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const uint64_t vm = __ballot(tok >= 0);   // bit r: tile row r valid (lanes 32..63 repeat 0..31)
             store_tile<D>(kR, vR, buf);
             load_tile<D>(Kbg, Vbg, nxt, kR, vR);   // past the end: masked rows (row 0), never used
-            attend_tile<D>(vm & 0xFFFFull, (vm >> 16) & 0xFFFFull, buf, r, qf, ident, h, aa.scale, m_run, l_run, acc);
+            if ((vm & 0xFFFFFFFFull) != 0ull)
+                attend_tile<D>((uint32_t)(vm >> (4 * h)) & 0xFu, (uint32_t)(vm >> (16 + 4 * h)) & 0xFu, buf, r, qf,
+                               ident, h, aa.scale, m_run, l_run, acc);
             tok = nxt;
         }
     }
     // acc[c][v] = unnormalised O[head n][32 (c/2) + 8h + 4 (c%2) + v]
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+    if (npl > 0 && n < aa.G) merge_bucket_partials<D>(aa, un.l, npl, n, h, m_run, l_run, acc);
     if (aa.splits == 1) {
         if (n < aa.G) {
             const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
@@ -385,6 +433,155 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
         finish_split(aa, part, D, 1, O, un.u);
+    }
+}
+
+// Sinks + local window of the bucket-major path, then the merge of the
+// unit's bucket partials.  One wave per QW = 16 / G consecutive queries of a
+// KV head: column n of the MFMAs is query n / G, head n % G, so the window
+// keys the queries share are read once per wave instead of once per query.
+// The wave walks the keys in 32-key tiles aligned to multiples of 32 —
+// those covering [0, S1), S1 the largest sink end, then those covering the
+// rest of [kmin, kmax], the union of the windows — and a key counts for a
+// column when it is one of that query's sinks or inside its window, so no
+// key is counted twice.  A unit
+// whose list the bucket pass could not take (np = -1) has that list gathered
+// here, for its own columns only.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bm_local_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const int64_t* __restrict__ q_pos, const int32_t* __restrict__ lr_idx, const int32_t* __restrict__ lr_cnt,
+    AttArgs aa, uint16_t* __restrict__ O, int64_t nwg_padded) {
+    __shared__ __align__(16) uint8_t tile_lds[4 * TileLds<D>::BYTES];
+    constexpr int KS = D / 32, NC = 2 * KS, NI = TileLds<D>::NI;
+    const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4, n = r;
+    const int G = aa.G, QW = 16 / G;
+    const int64_t ntrip = (aa.nqp + QW - 1) / QW;
+    const int64_t per_g = (int64_t)aa.B * ntrip;
+    const int64_t w_id = xcd_logical(blockIdx.x, nwg_padded) * 4 + wid;
+    if (w_id >= (int64_t)aa.H_kv * per_g) return;
+    const int64_t g = w_id / per_g, rem = w_id % per_g, b = rem / ntrip, tr = rem % ntrip;
+    const int qi = n / G, hh = n % G;
+    const int64_t il = tr * QW + qi;
+    const bool colq = qi < QW && il < aa.nqp;
+    const int64_t i = aa.q0 + (colq ? il : 0);
+    const int64_t t = colq ? q_pos[b * aa.n_q + i] : -1;
+    const int64_t u = (b * aa.n_q + i) * aa.H_kv + g, ul = (b * aa.nqp + (colq ? il : 0)) * aa.H_kv + g;
+    const int32_t cnt = colq ? min(lr_cnt[u], aa.k) : -1;
+    const bool live = colq && t >= 0 && cnt >= 0;
+    const int32_t npl = live ? aa.bm_np[ul] : 0;
+    int64_t se = 0, l0 = INT64_MAX, te = -1;   // this column's sinks [0, se) and window [l0, te]
+    if (live) {
+        const Geom q = query_geom(t, aa.n_blocks, aa.n_sinks, aa.window);
+        se = q.sink_end < q.l0 ? q.sink_end : q.l0;
+        l0 = q.l0;
+        te = t;
+    }
+    const int64_t orow = ((b * aa.n_q + i) * aa.H_q + g * G + hh) * D;
+    uint4 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = uint4{0, 0, 0, 0};
+        if (live) qf[ks] = *reinterpret_cast<const uint4*>(Q + orow + 32 * ks + 8 * h);
+    }
+    s16x4 ident;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ident[j] = (4 * h + j == n) ? (short)0x3F80 : (short)0;
+    f32x4 acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kNegInf, l_run = 0.f;
+
+    int64_t S1 = se, kmin = l0, kmax = te;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        S1 = max(S1, (int64_t)__shfl_xor(S1, o));
+        kmin = min(kmin, (int64_t)__shfl_xor(kmin, o));
+        kmax = max(kmax, (int64_t)__shfl_xor(kmax, o));
+    }
+    const int64_t bg = b * aa.H_kv + g;
+    const uint16_t* Kbg = K + bg * aa.t_cap * D;
+    const uint16_t* Vbg = V + bg * aa.t_cap * D;
+    uint8_t* buf = tile_lds + wid * TileLds<D>::BYTES;
+    u32x4 kR[NI], vR[NI];
+    // 32-key tiles at multiples of 32: nt1 tiles from key 0 (the sinks), then
+    // from a2 = max(32 nt1, kmin rounded down) to kmax; a column's keys fall in
+    // the same tiles whichever queries share the wave, and a tile holding
+    // none of them leaves its state exactly as it was
+    const int64_t nt1 = (S1 + 31) / 32;
+    const int64_t kmin_al = kmin == INT64_MAX ? kmin : (kmin / 32) * 32;
+    const int64_t a2 = 32 * nt1 > kmin_al ? 32 * nt1 : kmin_al;
+    const int64_t nt2 = kmax >= a2 ? (kmax - a2 + 32) / 32 : 0;
+    const int64_t ntiles = nt1 + nt2;
+    auto tile_start = [&](int64_t x) { return x < nt1 ? 32 * x : a2 + 32 * (x - nt1); };
+    auto tile_end = [&](int64_t) { return kmax + 1; };   // no row past the last window is read
+    if (ntiles > 0) {
+        int64_t k0 = tile_start(0), ke = tile_end(0);
+        int32_t tok = k0 + (l & 31) < ke ? (int32_t)(k0 + (l & 31)) : -1;
+        load_tile<D>(Kbg, Vbg, tok, kR, vR);
+        for (int64_t x = 0; x < ntiles; ++x) {
+            const int64_t n0 = x + 1 < ntiles ? tile_start(x + 1) : 0, ne = x + 1 < ntiles ? tile_end(x + 1) : 0;
+            const int32_t nxt = n0 + (l & 31) < ne ? (int32_t)(n0 + (l & 31)) : -1;
+            store_tile<D>(kR, vR, buf);
+            load_tile<D>(Kbg, Vbg, nxt, kR, vR);
+            uint32_t va4 = 0, vb4 = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t ka = k0 + 4 * h + v, kb = k0 + 16 + 4 * h + v;
+                va4 |= (ka < ke && (ka < se || (ka >= l0 && ka <= te))) ? (1u << v) : 0u;
+                vb4 |= (kb < ke && (kb < se || (kb >= l0 && kb <= te))) ? (1u << v) : 0u;
+            }
+            if (__ballot((va4 | vb4) != 0u) != 0ull)
+                attend_tile<D>(va4, vb4, buf, r, qf, ident, h, aa.scale, m_run, l_run, acc);
+            k0 = n0;
+            ke = ne;
+        }
+    }
+    // long-range lists of the units the bucket pass left to the gather
+    const uint64_t fb = __ballot(npl < 0);
+    for (int q2 = 0; q2 < QW; ++q2) {
+        if (((fb >> (q2 * G)) & 1ull) == 0ull) continue;   // column q2 * G stands for its query
+        const int lane0 = q2 * G;
+        const int64_t u2 = __shfl(u, lane0);
+        const int64_t t2 = __shfl(t, lane0);
+        const int32_t c2 = __shfl(cnt, lane0);
+        const int32_t* lr = lr_idx + u2 * aa.k;
+        auto tok_at = [&](int64_t j) -> int32_t {
+            if (j >= c2) return -1;
+            const int32_t tk = lr[j];
+            return (tk >= 0 && tk <= t2) ? tk : -1;
+        };
+        int32_t tok = tok_at(l & 31);
+        load_tile<D>(Kbg, Vbg, tok, kR, vR);
+        for (int64_t j = 0; j < c2; j += 32) {
+            const int32_t nxt = tok_at(j + 32 + (l & 31));
+            const uint64_t vm = __ballot(tok >= 0);
+            store_tile<D>(kR, vR, buf);
+            load_tile<D>(Kbg, Vbg, nxt, kR, vR);
+            if ((vm & 0xFFFFFFFFull) != 0ull) {
+                const bool mine = qi == q2;
+                attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
+                               mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h, aa.scale,
+                               m_run, l_run, acc);
+            }
+            tok = nxt;
+        }
+    }
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (npl > 0) merge_bucket_partials<D>(aa, ul, npl, hh, h, m_run, l_run, acc);
+    if (colq) {
+        const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+        uint32_t w[2 * NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            w[2 * c] = (uint32_t)f32_to_bf16(acc[c][0] * inv) | ((uint32_t)f32_to_bf16(acc[c][1] * inv) << 16);
+            w[2 * c + 1] = (uint32_t)f32_to_bf16(acc[c][2] * inv) | ((uint32_t)f32_to_bf16(acc[c][3] * inv) << 16);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            *reinterpret_cast<uint4*>(O + orow + 32 * ks + 8 * h) =
+                uint4{w[4 * ks], w[4 * ks + 1], w[4 * ks + 2], w[4 * ks + 3]};
     }
 }
 
@@ -500,6 +697,24 @@ int attend_splits(int64_t n_units, int window, int k) {
     if (want < 1) want = 1;
     if (want > 64) want = 64;
     return (int)want;
+}
+
+hipError_t launch_attend_local(const void* Q, const void* K, const void* V, const int64_t* q_pos,
+                               const int32_t* lr_idx, const int32_t* lr_cnt, const AttArgs& aa, int D, void* O,
+                               hipStream_t st) {
+    const int QW = 16 / aa.G;
+    const int64_t waves = (int64_t)aa.H_kv * aa.B * ((aa.nqp + QW - 1) / QW);
+    int64_t nwg = (waves + 3) / 4;
+    nwg = (nwg + 7) & ~(int64_t)7;
+    if (D == 128)
+        hipLaunchKernelGGL(bm_local_kernel<128>, dim3((unsigned)nwg), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
+                           static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), q_pos, lr_idx, lr_cnt,
+                           aa, static_cast<uint16_t*>(O), nwg);
+    else
+        hipLaunchKernelGGL(bm_local_kernel<64>, dim3((unsigned)nwg), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
+                           static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), q_pos, lr_idx, lr_cnt,
+                           aa, static_cast<uint16_t*>(O), nwg);
+    return hipGetLastError();
 }
 
 hipError_t launch_attend(const void* Q, const void* K, const void* V, const int64_t* q_pos, const int32_t* lr_idx,

@@ -276,8 +276,12 @@ __global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restric
         cv.meta[bg * cv.s_meta + leaf] = (uint32_t)n | ((uint32_t)off << 8);
         uint16_t* mem = cv.members + bg * cv.s_members + (int64_t)blk * kBlockEntries + off;
         int cnt = 0;
+        uint8_t* pos = cv.epos + bg * cv.s_epos + (int64_t)blk * kBlockEntries;
         for (int j = tid; j < kWardThreads && cnt < n; ++j)
-            if (lab[j] == tid) mem[cnt++] = (uint16_t)j;
+            if (lab[j] == tid) {
+                pos[j] = (uint8_t)cnt;
+                mem[cnt++] = (uint16_t)j;
+            }
     }
 }
 

@@ -36,7 +36,8 @@ struct CacheView {
     uint8_t* eleaf;        // [B, H_kv, n_blocks_max, 512]
     void* tcent;           // [B, H_kv, nodes_max, 64]   dtype (tree levels >= 1)
     float* tsums;          // [B, H_kv, nodes_max, 64]
-    int64_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums;
+    uint8_t* epos;         // [B, H_kv, n_blocks_max, 512] position of each entry in its bucket's member list
+    int64_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos;
     int32_t n_blocks;      // full blocks bucketed
     int32_t n_leaves;
     int32_t n_levels;      // tree levels including the leaves

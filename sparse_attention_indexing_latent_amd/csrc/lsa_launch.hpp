@@ -34,7 +34,8 @@ struct SelectBuffers {
 
 struct AttArgs {
     int64_t n_q;
-    int64_t n_units;
+    int64_t q0, nqp;   // this launch covers queries [q0, q0 + nqp) of every sequence
+    int64_t n_units;   // B * nqp * H_kv
     int64_t t_cap;
     int32_t B, H_kv, H_q, G;
     int32_t n_sinks, window, n_blocks, k;
@@ -42,7 +43,38 @@ struct AttArgs {
     float scale;
     unsigned long long* arrive;   // splits > 1: per-unit arrival words (tag << 32 | count)
     uint32_t tag;                 // distinct per call
+    // bucket-major merge (null bm_np: plain gather of the long-range list)
+    const uint32_t* bm_off;       // [n_units] first partial slot of the unit
+    const int32_t* bm_np;         // [n_units] partials of the unit; -1: gather its list instead
+    const float* bm_po;           // [slots, G, D] unnormalised partial outputs
+    const float* bm_ml;           // [slots, G, 2] partial max and denominator
 };
+
+// Workspace of one bucket-major pass.  A "bin" is one bucket of one (b, g):
+// bin = (b * H_kv + g) * leaves_max + bucket id.  A pair is one (query, KV
+// head) unit together with one bucket it selected tokens from; pair slots
+// are handed out per unit from a pool of pool_cap.
+struct BmBuffers {
+    int64_t leaves_max;
+    int64_t nbins;             // B * H_kv * leaves_max
+    int64_t nbins_pad;         // nbins rounded up to the scan chunk
+    uint32_t pool_cap;
+    uint32_t* lcnt;            // [nbins_pad + 1] pairs per bin, then the pool cursor
+    uint32_t* loff;            // [nbins_pad] offset of the bin's pairs inside its scan chunk
+    uint32_t* ctot;            // [nbins_pad / chunk] pairs per scan chunk
+    uint32_t* csum;            // [nbins_pad / chunk] exclusive scan of ctot
+    uint32_t* unit_off;        // [n_units]
+    int32_t* unit_np;          // [n_units]
+    uint32_t* rec_unit;        // [pool_cap] local unit of the pair
+    uint32_t* rec_bin;         // [pool_cap]
+    uint32_t* rec_rank;        // [pool_cap] arrival rank inside the bin
+    unsigned long long* rec_mask;   // [pool_cap] bit j: key j of the bucket (member order) is selected
+    uint32_t* sorted;          // [pool_cap] pair slots grouped by bin
+    float* po;                 // [pool_cap, G, D]
+    float* pml;                // [pool_cap, G, 2]
+};
+constexpr int kBmScanChunk = 4096;   // bins per workgroup of the offset scan
+constexpr int kBmUnitCap = 256;      // most buckets one unit may take through the bucket-major path
 
 hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
                         const void* W, hipStream_t st);
@@ -60,5 +92,11 @@ int attend_splits(int64_t n_units, int window, int k);
 hipError_t launch_attend(const void* Q, const void* K, const void* V, const int64_t* q_pos, const int32_t* lr_idx,
                          const int32_t* lr_cnt, const AttArgs& aa, int D, bool bf16, void* O, float* part,
                          hipStream_t st);
+hipError_t launch_attend_local(const void* Q, const void* K, const void* V, const int64_t* q_pos,
+                               const int32_t* lr_idx, const int32_t* lr_cnt, const AttArgs& aa, int D, void* O,
+                               hipStream_t st);
+hipError_t launch_bucket_partials(const CacheView& cv, const void* Q, const void* K, const void* V,
+                                  const int64_t* q_pos, const int32_t* lr_idx, const int32_t* lr_cnt,
+                                  const AttArgs& aa, const BmBuffers& bm, int D, hipStream_t st);
 
 }  // namespace lsa

@@ -1,0 +1,226 @@
+"""Parity of the bucket-major attention call (lsa_sparse_attend_bucket_major)
+with the oracle and with the gather call, on a layer shaped like the 131k
+prefill (head_dim 128, GQA 10/2 heads, k = 2048, 4 sinks, window 1024) at
+T = 32768, plus batch / pass / fallback / edge cases."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_attention_indexing_latent_amd as lsa
+from synth import get_config, layer_inputs, random_lr_lists
+from tests.parity import lr_row, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def bm():
+    print("[bm] generating inputs", flush=True)
+    cfg = get_config(2, T=32768, H_kv=2, H_q=10, n_topics=64)
+    inp = layer_inputs(cfg, seed=3)
+    G = {k: inp[k].to(DEV).contiguous() for k in ("K", "V", "W", "Q", "q_pos")}
+    cache = lsa.build_buckets(G["K"], G["W"], n_q_heads=cfg.H_q)
+    lr, cnt = lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window)
+    torch.cuda.synchronize()
+    return dict(cfg=cfg, inp=inp, G=G, cache=cache, lr=lr, cnt=cnt,
+                Ks=[inp["K"][0, g].double().numpy() for g in range(cfg.H_kv)],
+                Vs=[inp["V"][0, g].double().numpy() for g in range(cfg.H_kv)], Q=inp["Q"][0].double().numpy())
+
+
+def _oracle_err(bm, Ob, lr, cnt, units, positions=None):
+    cfg = bm["cfg"]
+    scale = 1 / math.sqrt(cfg.d)
+    nb = cfg.T // 2048
+    err = 0.0
+    for i, g in units:
+        t = int(bm["inp"]["q_pos"][0, i]) if positions is None else int(positions[i])
+        qi = i if positions is None else int(positions[i])
+        row = lr_row(lr[0, i, g], int(cnt[0, i, g]))
+        ref = O.attend(bm["Q"][qi, g * cfg.G:(g + 1) * cfg.G], bm["Ks"][g], bm["Vs"][g], t, row, cfg.n_sinks,
+                       cfg.window, nb, scale)
+        err = max(err, float(np.max(np.abs(ref - Ob[0, i, g * cfg.G:(g + 1) * cfg.G]))))
+    return err
+
+
+def test_entry_pos_matches_member_lists(bm):
+    """Cache region entry_pos: position of every entry inside its bucket's (ascending) member list."""
+    cache = bm["cache"]
+    members = cache.members()[0].cpu().numpy().astype(np.int64) & 0xFFFF
+    meta = cache.meta()[0].cpu().numpy().astype(np.int64)
+    eleaf = cache.entry_leaf()[0].cpu().numpy()
+    epos = cache.entry_pos()[0].cpu().numpy()
+    for g in range(bm["cfg"].H_kv):
+        for blk in range(0, members.shape[1], 3):
+            seen = np.zeros(512, bool)
+            for r in range(64):
+                m = int(meta[g, blk * 64 + r])
+                size, off = m & 0xFF, (m >> 8) & 0x3FF
+                mem = members[g, blk, off: off + size]
+                assert np.all(np.diff(mem) > 0)
+                assert np.array_equal(epos[g, blk, mem], np.arange(size))
+                assert np.all(eleaf[g, blk, mem] == r)
+                seen[mem] = True
+            assert seen.all()
+
+
+def test_bucket_major_on_selection(bm):
+    """On the GPU's own selection: equal to the gather call within the bf16 bound, and to the oracle."""
+    cfg, G = bm["cfg"], bm["G"]
+    Og = lsa.sparse_attend(G["Q"], G["K"], G["V"], G["q_pos"], bm["lr"], bm["cnt"], cfg.T, cfg.k, cfg.n_sinks,
+                           cfg.window)
+    Ob = lsa.sparse_attend_bucket_major(G["Q"], G["K"], G["V"], G["q_pos"], bm["lr"], bm["cnt"], bm["cache"],
+                                        cfg.k, cfg.n_sinks, cfg.window)
+    torch.cuda.synchronize()
+    d_gather = float((Og.float() - Ob.float()).abs().max())
+    print(f"[bm] bucket-major vs gather max abs diff {d_gather:.3e}", flush=True)
+    assert d_gather <= tol_for("bf16")
+    rng = np.random.default_rng(11)
+    units = list(zip(rng.integers(0, cfg.T, 500).tolist(), rng.integers(0, cfg.H_kv, 500).tolist()))
+    err = _oracle_err(bm, Ob.double().cpu().numpy(), bm["lr"].cpu().numpy(), bm["cnt"].cpu().numpy(), units)
+    print(f"[bm] bucket-major vs oracle max abs err {err:.3e}", flush=True)
+    assert err <= tol_for("bf16")
+
+
+def test_bucket_major_passes_bit_identical(bm):
+    """Splitting the queries into passes changes nothing: each pair's partial and each unit's merge order
+    are independent of the pass."""
+    cfg, G = bm["cfg"], bm["G"]
+    args = (G["Q"], G["K"], G["V"], G["q_pos"], bm["lr"], bm["cnt"], bm["cache"], cfg.k, cfg.n_sinks, cfg.window)
+    one = lsa.sparse_attend_bucket_major(*args)
+    for n_pass in (1000, 7777):
+        ws = torch.empty(lsa.attend_bucket_major_workspace_bytes(bm["cache"], cfg.H_q, cfg.d, n_pass),
+                         dtype=torch.uint8, device=DEV)
+        many = lsa.sparse_attend_bucket_major(*args, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(one, many), n_pass
+
+
+def _entry_lists(cfg, q_pos, seed):
+    """Lists made of whole and cut entries spread over random buckets (arbitrary key masks)."""
+    rng = np.random.default_rng(seed)
+    n_q = q_pos.shape[1]
+    idx = np.full((1, n_q, cfg.H_kv, cfg.k), -1, np.int32)
+    cnt = np.zeros((1, n_q, cfg.H_kv), np.int32)
+    for i in range(n_q):
+        t = int(q_pos[0, i])
+        nvis = min(t // 2048, cfg.T // 2048)
+        l0 = max(0, min(t - cfg.window + 1, 2048 * nvis))
+        lo = min(cfg.n_sinks, t + 1)
+        if l0 - lo < 8:
+            continue
+        for g in range(cfg.H_kv):
+            m = int(rng.integers(1, 160))
+            ents = rng.integers(lo // 4, (l0 - 1) // 4 + 1, m)
+            toks = (ents[:, None] * 4 + np.arange(4)[None, :]).ravel()
+            keep = rng.random(toks.size) < 0.8
+            toks = np.unique(np.concatenate([toks[keep], rng.integers(lo, l0, 8)]))
+            toks = toks[(toks >= lo) & (toks < l0)][: cfg.k]
+            idx[0, i, g, :toks.size] = toks
+            cnt[0, i, g] = toks.size
+    return torch.from_numpy(idx), torch.from_numpy(cnt)
+
+
+def test_bucket_major_arbitrary_masks_and_fallback(bm):
+    """Lists that are no walk of the selection: partial buckets (bucket-major path) and lists touching
+    more than 256 buckets or holding a repeated token (gathered whole by the window kernel; equal to the
+    gather call up to the order of the softmax sums)."""
+    cfg, G = bm["cfg"], bm["G"]
+    sel = torch.arange(0, cfg.T, 8)
+    Qs = G["Q"][:, sel].contiguous()
+    qp = G["q_pos"][:, sel].contiguous()
+    qp_cpu = qp.cpu()
+    ia, ca = _entry_lists(cfg, qp_cpu, seed=5)
+    ib, cb = random_lr_lists(cfg, qp_cpu, seed=9, fill=0.3)
+    n_q = sel.numel()
+    mode = (np.arange(n_q)[:, None] + np.arange(cfg.H_kv)[None, :]) % 3
+    idx = torch.where(torch.from_numpy(mode == 0)[None, :, :, None], ia, ib).contiguous()
+    cnt = torch.where(torch.from_numpy(mode == 0)[None], ca, cb).contiguous()
+    # mode 2: a repeated token (not strictly ascending) where the list has two or more entries
+    for i in range(n_q):
+        for g in range(cfg.H_kv):
+            if mode[i, g] == 2 and int(cnt[0, i, g]) >= 2:
+                idx[0, i, g, 1] = idx[0, i, g, 0]
+    idx_d, cnt_d = idx.to(DEV), cnt.to(DEV)
+    Og = lsa.sparse_attend(Qs, G["K"], G["V"], qp, idx_d, cnt_d, cfg.T, cfg.k, cfg.n_sinks, cfg.window)
+    Ob = lsa.sparse_attend_bucket_major(Qs, G["K"], G["V"], qp, idx_d, cnt_d, bm["cache"], cfg.k, cfg.n_sinks,
+                                        cfg.window)
+    torch.cuda.synchronize()
+    Og, Ob = Og.cpu(), Ob.cpu()
+    # lists the bucket-major path must hand back to the gather kernel: a repeated token, or > 256 buckets
+    eleaf = bm["cache"].entry_leaf()[0].cpu().numpy().astype(np.int64)
+    n_fb = 0
+    for i in range(n_q):
+        for g in range(cfg.H_kv):
+            c = int(cnt[0, i, g])
+            row = idx[0, i, g, :c].numpy().astype(np.int64)
+            buckets = np.unique((row // 2048) * 64 + eleaf[g, row // 2048, (row // 4) % 512]) if c else row
+            if (mode[i, g] == 2 and c >= 2) or buckets.size > 256:
+                n_fb += 1
+                dd = float((Og[0, i, g * cfg.G:(g + 1) * cfg.G].float() -
+                            Ob[0, i, g * cfg.G:(g + 1) * cfg.G].float()).abs().max())
+                assert dd <= 4e-3, (i, g, dd)
+    print(f"[bm] {n_fb} gathered-whole units match the gather call", flush=True)
+    assert n_fb > n_q // 4
+    d = float((Og.float() - Ob.float()).abs().max())
+    print(f"[bm] arbitrary lists: bucket-major vs gather max abs diff {d:.3e}", flush=True)
+    assert d <= tol_for("bf16")
+    units = [(i, g) for i in range(0, n_q, 5) for g in range(cfg.H_kv) if mode[i, g] == 0]
+    err = _oracle_err(bm, Ob.double().numpy(), idx.numpy(), cnt.numpy(), units, positions=sel.numpy())
+    print(f"[bm] arbitrary lists vs oracle max abs err {err:.3e} over {len(units)} units", flush=True)
+    assert err <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("d,H_kv,H_q", [(128, 2, 16), (64, 1, 3), (128, 4, 4)])
+def test_bucket_major_batch_shapes_and_invalid_positions(d, H_kv, H_q):
+    """B = 2, GQA groups of 8 / 3 / 1 heads, d = 64 and 128, a position of -1, several passes."""
+    cfg = get_config(2, T=8192, B=2, H_kv=H_kv, H_q=H_q, d=d, n_topics=16, k=512, window=256)
+    qp = torch.arange(0, cfg.T, 5, dtype=torch.int64).repeat(2, 1)
+    qp[1, 3] = -1
+    inp = layer_inputs(cfg, seed=31, q_positions=qp)
+    G = {k: inp[k].to(DEV).contiguous() for k in ("K", "V", "W", "Q", "q_pos")}
+    cache = lsa.build_buckets(G["K"], G["W"], n_q_heads=cfg.H_q)
+    lr, cnt = lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window)
+    Og = lsa.sparse_attend(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window)
+    ws = torch.empty(lsa.attend_bucket_major_workspace_bytes(cache, cfg.H_q, cfg.d, 300), dtype=torch.uint8,
+                     device=DEV)
+    Ob = lsa.sparse_attend_bucket_major(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cache, cfg.k, cfg.n_sinks,
+                                        cfg.window, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((Ob[1, 3] == 0).all())
+    dmax = float((Og.float() - Ob.float()).abs().max())
+    assert dmax <= tol_for("bf16"), dmax
+    W = inp["W"].double().numpy()
+    scale = 1 / math.sqrt(cfg.d)
+    lr_c, cnt_c, Ob_c = lr.cpu().numpy(), cnt.cpu().numpy(), Ob.double().cpu().numpy()
+    err = 0.0
+    for b in range(2):
+        Kb = [inp["K"][b, g].double().numpy() for g in range(cfg.H_kv)]
+        Vb = [inp["V"][b, g].double().numpy() for g in range(cfg.H_kv)]
+        for i in range(0, qp.shape[1], 23):
+            t = int(qp[b, i])
+            if t < 0:
+                continue
+            for g in range(cfg.H_kv):
+                qg = inp["Q"][b, i, g * cfg.G:(g + 1) * cfg.G].double().numpy()
+                ref = O.attend(qg, Kb[g], Vb[g], t, lr_row(lr_c[b, i, g], int(cnt_c[b, i, g])), cfg.n_sinks,
+                               cfg.window, cfg.T // 2048, scale)
+                err = max(err, float(np.max(np.abs(ref - Ob_c[b, i, g * cfg.G:(g + 1) * cfg.G]))))
+    print(f"[bm] d={d} G={cfg.G}: vs gather {dmax:.3e}, vs oracle {err:.3e}", flush=True)
+    assert err <= tol_for("bf16")
+
+
+def test_bucket_major_rejects_fp32_and_small_workspace():
+    cfg = get_config(1, T=4096)
+    inp = layer_inputs(cfg, seed=4)
+    G = {k: inp[k].to(DEV).contiguous() for k in ("K", "V", "W", "Q", "q_pos")}
+    cache = lsa.build_buckets(G["K"], G["W"], n_q_heads=cfg.H_q)
+    lr, cnt = lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window)
+    with pytest.raises(lsa.LsaError) as e:
+        lsa.sparse_attend_bucket_major(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cache, cfg.k, cfg.n_sinks,
+                                       cfg.window)
+    assert e.value.status == 8
