@@ -197,8 +197,7 @@ constexpr int64_t kBmPoolPerUnit = 80;
 struct BmWs {
     int64_t units, leaves_max, nbins, nbins_pad;
     uint32_t pool_cap;
-    size_t off_lcnt, off_loff, off_ctot, off_csum, off_uoff, off_unp, off_runit, off_rbin, off_rrank, off_rmask,
-        off_sorted, off_po, off_pml, total;
+    size_t off_lcnt, off_loff, off_ctot, off_csum, off_uoff, off_unp, off_rec, off_srec, off_po, off_pml, total;
 };
 
 void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) {
@@ -219,11 +218,8 @@ void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) 
     w.off_csum = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 4);
     w.off_uoff = o;   o = align256(o + (size_t)w.units * 4);
     w.off_unp = o;    o = align256(o + (size_t)w.units * 4);
-    w.off_runit = o;  o = align256(o + (size_t)pool * 4);
-    w.off_rbin = o;   o = align256(o + (size_t)pool * 4);
-    w.off_rrank = o;  o = align256(o + (size_t)pool * 4);
-    w.off_rmask = o;  o = align256(o + (size_t)pool * 8);
-    w.off_sorted = o; o = align256(o + (size_t)pool * 4);
+    w.off_rec = o;    o = align256(o + (size_t)pool * 16);
+    w.off_srec = o;   o = align256(o + (size_t)pool * 16);
     w.off_po = o;     o = align256(o + (size_t)pool * G * D * 4);
     w.off_pml = o;    o = align256(o + (size_t)pool * G * 8);
     w.total = o;
@@ -571,11 +567,8 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         bm.csum = reinterpret_cast<uint32_t*>(wb + w.off_csum);
         bm.unit_off = reinterpret_cast<uint32_t*>(wb + w.off_uoff);
         bm.unit_np = reinterpret_cast<int32_t*>(wb + w.off_unp);
-        bm.rec_unit = reinterpret_cast<uint32_t*>(wb + w.off_runit);
-        bm.rec_bin = reinterpret_cast<uint32_t*>(wb + w.off_rbin);
-        bm.rec_rank = reinterpret_cast<uint32_t*>(wb + w.off_rrank);
-        bm.rec_mask = reinterpret_cast<unsigned long long*>(wb + w.off_rmask);
-        bm.sorted = reinterpret_cast<uint32_t*>(wb + w.off_sorted);
+        bm.rec = reinterpret_cast<lsa::u32x4*>(wb + w.off_rec);
+        bm.srec = reinterpret_cast<lsa::u32x4*>(wb + w.off_srec);
         bm.po = reinterpret_cast<float*>(wb + w.off_po);
         bm.pml = reinterpret_cast<float*>(wb + w.off_pml);
         lsa::AttArgs aa;

@@ -95,33 +95,55 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
         const uint8_t* ep = cv.epos + bg * cv.s_epos;
         int32_t prev = -1;
         int cur = -1;
-        for (int j0 = 0; j0 < cnt; j0 += 64) {
-            const int j = j0 + l;
-            const bool valid = j < cnt;
-            const int32_t tk = valid ? lr[j] : 0;
-            int32_t before = __shfl_up(tk, 1);
-            if (l == 0) before = prev;
-            // [sink end, window start) lies inside the bucketed blocks
-            const bool ok = !valid || (tk > before && (int64_t)tk >= q.sink_end && (int64_t)tk < q.l0);
-            if (__ballot(!ok) != 0ull) {
-                bad = true;
-                break;
+        // rounds of 16 groups of 64 listed tokens: every load of a round is
+        // issued before the groups are walked in order
+        constexpr int RG = 16;
+        for (int r0 = 0; r0 < cnt && !bad; r0 += 64 * RG) {
+            int32_t tkr[RG];
+            uint32_t inf[RG];   // bucket rank | key number << 8
+#pragma unroll
+            for (int m = 0; m < RG; ++m) {
+                const int j = r0 + 64 * m + l;
+                tkr[m] = j < cnt ? lr[j] : 0;
             }
-            prev = __shfl(tk, 63);   // read only when lane 63 was valid (a further group exists)
-            const int blk = tk / kBlockTokens;
-            const int64_t e = (int64_t)blk * kBlockEntries + ((tk / kPool) % kBlockEntries);
-            const int rank = valid ? (el[e] & (kLeavesPerBlock - 1)) : 0;
-            const int bit = valid ? kPool * ep[e] + (tk % kPool) : 0;
-            uint64_t pending = __ballot(valid);
-            while (pending != 0ull) {
-                const int cb = __shfl(blk, __builtin_ctzll(pending));
-                if (cb != cur) {
-                    if (cur >= 0) np = bm_flush(mk[wid], pl[wid], pm[wid], cur, np);
-                    cur = cb;
+#pragma unroll
+            for (int m = 0; m < RG; ++m) {
+                const int j = r0 + 64 * m + l;
+                const int32_t tk = tkr[m];
+                // a token outside the bucketed blocks is caught by the range check below; clamp the lookup
+                const int64_t tc = tk >= 0 && (int64_t)tk < (int64_t)aa.n_blocks * kBlockTokens ? tk : 0;
+                const int64_t e = (tc / kBlockTokens) * kBlockEntries + ((tc / kPool) % kBlockEntries);
+                inf[m] = 0u;
+                if (j < cnt) inf[m] = (uint32_t)(el[e] & (kLeavesPerBlock - 1)) | ((uint32_t)(kPool * ep[e] + (tc % kPool)) << 8);
+            }
+#pragma unroll
+            for (int m = 0; m < RG; ++m) {
+                const int j0 = r0 + 64 * m;
+                if (j0 >= cnt || bad) break;
+                const bool valid = j0 + l < cnt;
+                const int32_t tk = tkr[m];
+                int32_t before = __shfl_up(tk, 1);
+                if (l == 0) before = prev;
+                // [sink end, window start) lies inside the bucketed blocks
+                const bool ok = !valid || (tk > before && (int64_t)tk >= q.sink_end && (int64_t)tk < q.l0);
+                if (__ballot(!ok) != 0ull) {
+                    bad = true;
+                    break;
                 }
-                const uint64_t mine = __ballot(valid && blk == cb) & pending;
-                if ((mine >> l) & 1ull) atomicOr(&mk[wid][rank], 1ull << bit);
-                pending &= ~mine;
+                prev = __shfl(tk, 63);   // read only when lane 63 was valid (a further group exists)
+                const int blk = tk / kBlockTokens;
+                const int rank = (int)(inf[m] & 0xFFu), bit = (int)(inf[m] >> 8);
+                uint64_t pending = __ballot(valid);
+                while (pending != 0ull) {
+                    const int cb = __shfl(blk, __builtin_ctzll(pending));
+                    if (cb != cur) {
+                        if (cur >= 0) np = bm_flush(mk[wid], pl[wid], pm[wid], cur, np);
+                        cur = cb;
+                    }
+                    const uint64_t mine = __ballot(valid && blk == cb) & pending;
+                    if ((mine >> l) & 1ull) atomicOr(&mk[wid][rank], 1ull << bit);
+                    pending &= ~mine;
+                }
             }
         }
         if (!bad && cur >= 0) np = bm_flush(mk[wid], pl[wid], pm[wid], cur, np);
@@ -138,11 +160,8 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
         for (int idx = l; idx < np; idx += 64) {
             const uint32_t bin = (uint32_t)(bg * bm.leaves_max + pl[wid][idx]);
             const uint32_t rk = atomicAdd(bm.lcnt + bin, 1u);
-            const uint32_t p = base + (uint32_t)idx;
-            bm.rec_unit[p] = (uint32_t)ul;
-            bm.rec_bin[p] = bin;
-            bm.rec_rank[p] = rk;
-            bm.rec_mask[p] = pm[wid][idx];
+            const unsigned long long m = pm[wid][idx];
+            bm.rec[base + (uint32_t)idx] = u32x4{bin, rk, (uint32_t)m, (uint32_t)(m >> 32)};
         }
     }
     if (l == 0) {
@@ -211,7 +230,8 @@ __device__ __forceinline__ uint32_t bm_bin_start(const BmBuffers& bm, uint32_t b
     return bm.csum[bin / kBmScanChunk] + bm.loff[bin];
 }
 
-// One wave per local unit: its pair slots go to their bin's place.
+// One wave per local unit: its pair records go to their bin's place as
+// (unit, pair slot, key mask).
 __global__ __launch_bounds__(256) void bm_scatter_kernel(AttArgs aa, BmBuffers bm) {
     const int l = lane_id(), wid = threadIdx.x >> 6;
     const int64_t ul = (int64_t)blockIdx.x * 4 + wid;
@@ -221,8 +241,8 @@ __global__ __launch_bounds__(256) void bm_scatter_kernel(AttArgs aa, BmBuffers b
     const uint32_t base = bm.unit_off[ul];
     for (int idx = l; idx < np; idx += 64) {
         const uint32_t p = base + (uint32_t)idx;
-        const uint32_t bin = bm.rec_bin[p];
-        bm.sorted[bm_bin_start(bm, bin) + bm.rec_rank[p]] = p;
+        const u32x4 r = bm.rec[p];
+        bm.srec[bm_bin_start(bm, r[0]) + r[1]] = u32x4{(uint32_t)ul, p, r[2], r[3]};
     }
 }
 
@@ -316,27 +336,39 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
         __syncthreads();
         const int NT = (ntok + 15) / 16, NK = nrow / 32;
         const uint32_t ngroups = (npairs + GP - 1) / GP;
+        const int pi = n / G, hh = n % G;
+        // software pipeline over this wave's groups: the records two groups
+        // ahead and the Q rows one group ahead are in flight while a group
+        // is computed (a record with unit ~0: no pair in this column)
+#define LSA_BM_REC(GRP, R)                                                                  \
+    {                                                                                        \
+        const uint32_t pidx_ = (GRP) * GP + pi;                                              \
+        R = u32x4{~0u, 0u, 0u, 0u};                                                          \
+        if ((GRP) < ngroups && pi < GP && pidx_ < npairs) R = bm.srec[start + pidx_];        \
+    }
+#define LSA_BM_Q(R, QV)                                                                     \
+    {                                                                                        \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) QV[ks] = u32x4{0u, 0u, 0u, 0u};    \
+        if (R[0] != ~0u) {                                                                   \
+            const int64_t ul_ = R[0];                                                        \
+            const int64_t gq_ = ul_ % aa.H_kv, rq_ = ul_ / aa.H_kv;                          \
+            const int64_t bq_ = rq_ / aa.nqp, iq_ = aa.q0 + rq_ % aa.nqp;                    \
+            const uint16_t* qrow_ = Q + ((bq_ * aa.n_q + iq_) * aa.H_q + gq_ * G + hh) * D;  \
+            _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) QV[ks] =                       \
+                *reinterpret_cast<const u32x4*>(qrow_ + 32 * ks + 8 * h);                    \
+        }                                                                                    \
+    }
+        u32x4 rc, rn, qf[KS], qn[KS];
+        LSA_BM_REC(wid, rc)
+        LSA_BM_Q(rc, qf)
+        LSA_BM_REC(wid + 4, rn)
         for (uint32_t grp = wid; grp < ngroups; grp += 4) {
-            const int pi = n / G, hh = n % G;
-            const uint32_t pidx = grp * GP + pi;
-            const bool col = pi < GP && pidx < npairs;
-            uint32_t p = 0;
-            unsigned long long mask = 0ull;
-            u32x4 qf[KS];
-            int64_t ul = 0;
-            if (col) {
-                p = bm.sorted[start + pidx];
-                ul = bm.rec_unit[p];
-                mask = bm.rec_mask[p];
-            }
-            {
-                const int64_t gq = ul % aa.H_kv, rq = ul / aa.H_kv;
-                const int64_t bq = rq / aa.nqp, iq = aa.q0 + rq % aa.nqp;
-                const uint16_t* qrow = Q + ((bq * aa.n_q + iq) * aa.H_q + gq * G + hh) * D;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    qf[ks] = col ? *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * h) : u32x4{0u, 0u, 0u, 0u};
-            }
+            LSA_BM_Q(rn, qn)
+            u32x4 rnn;
+            LSA_BM_REC(grp + 8, rnn)
+            const bool col = rc[0] != ~0u;
+            const uint32_t p = rc[1];
+            const unsigned long long mask = col ? ((unsigned long long)rc[3] << 32) | rc[2] : 0ull;
             // S^T = K Q^T over the bucket's keys
             f32x4 s[4];
             float mx = kNegInf;
@@ -400,7 +432,13 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
                 for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * h) = acc[dt];
                 if (h == 0) *reinterpret_cast<float2*>(bm.pml + slot * 2) = float2{mx, psum};
             }
+            rc = rn;
+            rn = rnn;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
         }
+#undef LSA_BM_REC
+#undef LSA_BM_Q
     }
 }
 

@@ -65,11 +65,9 @@ struct BmBuffers {
     uint32_t* csum;            // [nbins_pad / chunk] exclusive scan of ctot
     uint32_t* unit_off;        // [n_units]
     int32_t* unit_np;          // [n_units]
-    uint32_t* rec_unit;        // [pool_cap] local unit of the pair
-    uint32_t* rec_bin;         // [pool_cap]
-    uint32_t* rec_rank;        // [pool_cap] arrival rank inside the bin
-    unsigned long long* rec_mask;   // [pool_cap] bit j: key j of the bucket (member order) is selected
-    uint32_t* sorted;          // [pool_cap] pair slots grouped by bin
+    u32x4* rec;                // [pool_cap] (bin, arrival rank in the bin, key mask lo, hi); mask bit j:
+                               //   key j of the bucket (member order) is listed
+    u32x4* srec;               // [pool_cap] grouped by bin: (local unit, pair slot, key mask lo, hi)
     float* po;                 // [pool_cap, G, D]
     float* pml;                // [pool_cap, G, 2]
 };
