@@ -224,9 +224,9 @@ def run_prefill(args, cid):
     ws["sel"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws["cache"] = cache0.buf
     if args.attend == "bucket":
-        # passes of up to 16384 queries, fewer if free memory is short (workspace <= 40% of it)
+        # passes of up to --bm-pass queries, fewer if free memory is short (workspace <= 40% of it)
         free = torch.cuda.mem_get_info(dev)[0]
-        n_pass = 16384
+        n_pass = args.bm_pass
         while n_pass > 1024 and lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass) > 0.4 * free:
             n_pass //= 2
         ws["bm"] = torch.empty(lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass),
@@ -417,6 +417,8 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=[2, 4, 5])
     ap.add_argument("--attend", default="gather", choices=["gather", "bucket"],
                     help="prefill attention: per-query gather, or bucket-major (each bucket's K/V read once per pass)")
+    ap.add_argument("--bm-pass", type=int, default=32768,
+                    help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate", action="store_true",

@@ -189,7 +189,8 @@ uint32_t next_call_tag() {
 
 // Workspace of one bucket-major pass over nqp queries per sequence: the
 // per-bin counts and offsets, the per-unit slot ranges, the pair records and
-// the fp32 partials (max and denominator, D values) of every pair slot.  The
+// the partials (fp32 max, denominator and scale; D fp16 values) of every
+// pair slot.  The
 // pool holds kBmPoolPerUnit slots per unit on average (a unit takes one per
 // bucket it reads from, about k / 32 with buckets of 8 entries).
 constexpr int64_t kBmPoolPerUnit = 80;
@@ -220,8 +221,8 @@ void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) 
     w.off_unp = o;    o = align256(o + (size_t)w.units * 4);
     w.off_rec = o;    o = align256(o + (size_t)pool * 16);
     w.off_srec = o;   o = align256(o + (size_t)pool * 16);
-    w.off_po = o;     o = align256(o + (size_t)pool * G * D * 4);
-    w.off_pml = o;    o = align256(o + (size_t)pool * G * 8);
+    w.off_po = o;     o = align256(o + (size_t)pool * G * D * 2);
+    w.off_pml = o;    o = align256(o + (size_t)pool * G * 16);
     w.total = o;
 }
 
@@ -569,7 +570,7 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         bm.unit_np = reinterpret_cast<int32_t*>(wb + w.off_unp);
         bm.rec = reinterpret_cast<lsa::u32x4*>(wb + w.off_rec);
         bm.srec = reinterpret_cast<lsa::u32x4*>(wb + w.off_srec);
-        bm.po = reinterpret_cast<float*>(wb + w.off_po);
+        bm.po = reinterpret_cast<uint16_t*>(wb + w.off_po);
         bm.pml = reinterpret_cast<float*>(wb + w.off_pml);
         lsa::AttArgs aa;
         memset(&aa, 0, sizeof(aa));

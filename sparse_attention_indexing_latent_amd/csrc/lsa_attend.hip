@@ -59,26 +59,33 @@ __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t
     constexpr int NC = D / 16;
     const int64_t s0 = aa.bm_off[ul];
     for (int s = 0; s < npl; s += 4) {
-        float2 ml[4];
-        f32x4 o[4][NC];
+        f32x4 ml[4];
+        u32x2 o[4][NC];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t slot = (s0 + (s + j < npl ? s + j : 0)) * aa.G + hh;
-            ml[j] = *reinterpret_cast<const float2*>(aa.bm_ml + slot * 2);
-            const float* po = aa.bm_po + slot * D;
+            ml[j] = *reinterpret_cast<const f32x4*>(aa.bm_ml + slot * 4);
+            const uint16_t* po = aa.bm_po + slot * D;
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                o[j][c] = *reinterpret_cast<const f32x4*>(po + 32 * (c / 2) + 8 * h + 4 * (c % 2));
+                o[j][c] = *reinterpret_cast<const u32x2*>(po + 32 * (c / 2) + 8 * h + 4 * (c % 2));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float mj = s + j < npl ? ml[j].x : kNegInf;
+            const float mj = s + j < npl ? ml[j][0] : kNegInf;
             const float M = fmaxf(m_run, mj);
             const float a = m_run > kNegInf ? __expf(m_run - M) : 0.f;
             const float b = mj > kNegInf ? __expf(mj - M) : 0.f;
+            const float bs = b * ml[j][2];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) acc[c] = acc[c] * a + o[j][c] * b;
-            l_run = l_run * a + ml[j].y * b;
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 oc = {(float)__builtin_bit_cast(_Float16, (uint16_t)(o[j][c][0] & 0xFFFFu)),
+                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(o[j][c][0] >> 16)),
+                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(o[j][c][1] & 0xFFFFu)),
+                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(o[j][c][1] >> 16))};
+                acc[c] = acc[c] * a + oc * bs;
+            }
+            l_run = l_run * a + ml[j][1] * b;
             m_run = M;
         }
     }

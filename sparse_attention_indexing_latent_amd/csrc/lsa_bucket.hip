@@ -9,8 +9,8 @@
 // gathering each query's keys (about 1 MiB of K/V per query and KV head),
 // the (query, bucket) pairs are grouped by bucket: a workgroup stages one
 // bucket's keys and values in LDS once and runs the MFMAs for every query
-// that picked it, leaving one fp32 partial (max, denominator, unnormalised
-// output per head) per pair.  The gather kernel then attends sinks + window
+// that picked it, leaving one partial (fp32 max and denominator, the
+// unnormalised output per head as fp16 times an fp32 scale) per pair.  The gather kernel then attends sinks + window
 // and merges the unit's partials with a log-sum-exp combine.  The result is
 // the same attention; only the order of the softmax sums differs.
 //
@@ -425,12 +425,28 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
                     }
                 }
             }
+            // the row's scale: its largest magnitude over the D dims (4 lanes of the column)
+            float amax = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(acc[dt][v]));
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
             if (col) {
                 const int64_t slot = (int64_t)p * G + hh;
-                float* po = bm.po + slot * D;
+                const float inv = amax > 0.f ? 1.0f / amax : 0.f;
+                uint16_t* po = bm.po + slot * D;
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * h) = acc[dt];
-                if (h == 0) *reinterpret_cast<float2*>(bm.pml + slot * 2) = float2{mx, psum};
+                for (int dt = 0; dt < NDT; ++dt) {
+                    uint32_t w2[2];
+#pragma unroll
+                    for (int v = 0; v < 4; v += 2)
+                        w2[v / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[dt][v] * inv)) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[dt][v + 1] * inv)) << 16);
+                    *reinterpret_cast<u32x2*>(po + 16 * dt + 4 * h) = u32x2{w2[0], w2[1]};
+                }
+                if (h == 0) *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx, psum, amax, 0.f};
             }
             rc = rn;
             rn = rnn;

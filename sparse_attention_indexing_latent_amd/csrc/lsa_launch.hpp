@@ -46,11 +46,14 @@ struct AttArgs {
     // bucket-major merge (null bm_np: plain gather of the long-range list)
     const uint32_t* bm_off;       // [n_units] first partial slot of the unit
     const int32_t* bm_np;         // [n_units] partials of the unit; -1: gather its list instead
-    const float* bm_po;           // [slots, G, D] unnormalised partial outputs
-    const float* bm_ml;           // [slots, G, 2] partial max and denominator
+    const uint16_t* bm_po;        // [slots, G, D] fp16: unnormalised partial output / its scale
+    const float* bm_ml;           // [slots, G, 4] partial max, denominator, scale (largest |output|), 0
 };
 
 // Workspace of one bucket-major pass.  A "bin" is one bucket of one (b, g):
+// (a pair's partial output row is kept as fp16 values in [-1, 1] times an
+// fp32 scale, the row's largest magnitude: half the bytes of fp32 with an
+// absolute rounding error of at most 2^-12 of that scale)
 // bin = (b * H_kv + g) * leaves_max + bucket id.  A pair is one (query, KV
 // head) unit together with one bucket it selected tokens from; pair slots
 // are handed out per unit from a pool of pool_cap.
@@ -68,8 +71,8 @@ struct BmBuffers {
     u32x4* rec;                // [pool_cap] (bin, arrival rank in the bin, key mask lo, hi); mask bit j:
                                //   key j of the bucket (member order) is listed
     u32x4* srec;               // [pool_cap] grouped by bin: (local unit, pair slot, key mask lo, hi)
-    float* po;                 // [pool_cap, G, D]
-    float* pml;                // [pool_cap, G, 2]
+    uint16_t* po;              // [pool_cap, G, D] fp16 partial outputs, divided by their scale
+    float* pml;                // [pool_cap, G, 4] (max, denominator, scale, 0)
 };
 constexpr int kBmScanChunk = 4096;   // bins per workgroup of the offset scan
 constexpr int kBmUnitCap = 256;      // most buckets one unit may take through the bucket-major path
