@@ -94,6 +94,8 @@ def prefill_step(cfg, G, ws, timers=None, tree=False, O=None):
             e.record()
         if "cnt_sum" in ws:
             ws["cnt_sum"] += int(cnt.clamp_min(0).sum().item())
+            if "bm" in ws:
+                ws["bm_bytes"] += bucket_major_bytes(cfg, lr, cnt, cache, ws["bm_pass"])
     return cache
 
 
@@ -113,6 +115,43 @@ def selected_bytes(cfg, n_q_total, lr_total, q_pos_all, tile=64):
     row = cfg.d * 2
     keys = local_rows * cfg.H_kv + lr_total
     return keys * 2 * row + 2 * n_q_total * cfg.H_q * row
+
+
+def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=8192):
+    """Algorithmic HBM bytes of one bucket-major attention call over a chunk
+    of queries, without the window part (added by selected_bytes' local term):
+    per pass, the K and V rows of every distinct bucket any of its queries
+    listed, once; per (query, KV head, bucket) pair, the G query rows and
+    the partial row (G x (2 d + 16) bytes) written once and read once; the
+    long-range lists read once."""
+    info = cache.info()
+    nb = info.n_blocks
+    eleaf = cache.entry_leaf()[0].long()                     # [H_kv, nb, 512]
+    size = (cache.meta()[0].long() & 0xFF)                   # [H_kv, n_leaves]
+    H, k, d, G = cfg.H_kv, cfg.k, cfg.d, cfg.G
+    nq = lr.shape[1]
+    pairs, kv_rows = 0, 0
+    gidx = torch.arange(H, device=lr.device).view(1, H, 1)
+    for p0 in range(0, nq, n_pass):
+        seen = []
+        for s0 in range(p0, min(nq, p0 + n_pass), sub):
+            s1 = min(nq, p0 + n_pass, s0 + sub)
+            L = lr[0, s0:s1].long()                           # [n, H, k]
+            valid = torch.arange(k, device=L.device).view(1, 1, k) < cnt[0, s0:s1].unsqueeze(-1)
+            tok = torch.where(valid, L, torch.zeros_like(L))
+            blk = torch.clamp(tok // 2048, max=max(nb - 1, 0))
+            rank = eleaf[gidx, blk, (tok // 4) % 512]
+            key = torch.where(valid, gidx * (nb * 64) + blk * 64 + rank, torch.full_like(L, -1))
+            srt = key.sort(dim=-1).values
+            new = (srt[..., 1:] != srt[..., :-1]) & (srt[..., 1:] >= 0)
+            pairs += int(new.sum()) + int((srt[..., 0] >= 0).sum())
+            seen.append(torch.unique(srt[srt >= 0]))
+        if seen:
+            u = torch.unique(torch.cat(seen))
+            kv_rows += int((size.view(-1)[u] * 4).sum())
+    row = d * 2
+    return (kv_rows * 2 * row + pairs * G * row + 2 * pairs * G * (2 * d + 16)
+            + int(cnt.clamp_min(0).sum()) * 4)
 
 
 _CPU_CTX = {}
@@ -182,9 +221,10 @@ def cpu_baseline(cfg, inp_cpu, n_units=1500):
                         f"blocks*H_kv*t_block + T*H_kv*t_unit*(mean visible buckets / sampled)"))
 
 
-def traffic_for(kernel_src: str, key: str):
+def traffic_for(kernel_src, key: str):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE, if
-    they were taken on the current kernel source."""
+    they were taken on the current kernel source (one file, or a list whose
+    contents are hashed in order)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -194,7 +234,11 @@ def traffic_for(kernel_src: str, key: str):
         return None
     if not rec:
         return None
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    srcs = [kernel_src] if isinstance(kernel_src, str) else list(kernel_src)
+    hs = hashlib.sha256()
+    for f in srcs:
+        hs.update(open(f, "rb").read())
+    h = hs.hexdigest()
     return rec.get("bytes_per_launch") if rec.get("source_sha256") == h else None
 
 
@@ -223,19 +267,29 @@ def run_prefill(args, cid):
                                         min(CHUNK, n_q), cfg.H_q)
     ws["sel"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws["cache"] = cache0.buf
-    if args.attend == "bucket":
+    attend = args.attend
+    if attend != "gather":
         # passes of up to --bm-pass queries, fewer if free memory is short (workspace <= 40% of it)
         free = torch.cuda.mem_get_info(dev)[0]
         n_pass = args.bm_pass
         while n_pass > 1024 and lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass) > 0.4 * free:
             n_pass //= 2
-        ws["bm"] = torch.empty(lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass),
-                               dtype=torch.uint8, device=dev)
-        log(f"bucket-major attention, passes of {n_pass} queries, workspace {ws['bm'].numel() / 2**30:.1f} GiB")
+        # auto: bucket-major when a bucket is expected in >= 8 pairs per pass (n_pass * k / T)
+        if attend == "auto":
+            attend = "bucket" if n_pass * cfg.k >= 8 * cfg.T else "gather"
+        if attend == "bucket":
+            ws["bm"] = torch.empty(lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass),
+                                   dtype=torch.uint8, device=dev)
+            ws["bm_pass"] = n_pass
+            log(f"bucket-major attention, passes of {n_pass} queries, workspace {ws['bm'].numel() / 2**30:.1f} GiB")
+    if attend == "gather":
+        log("gather attention")
     ws["cnt_sum"] = 0
+    ws["bm_bytes"] = 0
     log("warmup")
     for _ in range(args.warmup):
         ws["cnt_sum"] = 0
+        ws["bm_bytes"] = 0
         prefill_step(cfg, G, ws, O=O)
     lr_total = ws.pop("cnt_sum") if args.warmup > 0 else None
     torch.cuda.synchronize()
@@ -249,16 +303,25 @@ def run_prefill(args, cid):
     wall = time.perf_counter() - t0
     if lr_total is None:
         ws["cnt_sum"] = 0
+        ws["bm_bytes"] = 0
         prefill_step(cfg, G, ws, O=O)
         lr_total = ws.pop("cnt_sum")
     ms_step = wall * 1000 / args.steps
     att_ms = timers["attend"].total_ms() / args.steps
     n_att = timers["attend"].count() // args.steps
-    alg_bytes = selected_bytes(cfg, n_q, lr_total, G["q_pos"][0].cpu())
+    csrc = os.path.join(ROOT, "sparse_attention_indexing_latent_amd", "csrc")
+    if attend == "bucket":
+        # the window part as in the gather accounting, with no long-range rows
+        alg_bytes = selected_bytes(cfg, n_q, 0, G["q_pos"][0].cpu()) + ws["bm_bytes"]
+        kernel = "bucket-major attention call (pairs, scan, scatter, bm_leaf_kernel<128>, bm_local_kernel<128>)"
+        traffic = traffic_for([os.path.join(csrc, "lsa_bucket.hip"), os.path.join(csrc, "lsa_attend.hip")],
+                              f"attend_bucket_{cfg.name}")
+    else:
+        alg_bytes = selected_bytes(cfg, n_q, lr_total, G["q_pos"][0].cpu())
+        kernel = "attend_bf16_kernel<128>"
+        traffic = traffic_for(os.path.join(csrc, "lsa_attend.hip"), f"attend_{cfg.name}")
     achieved = alg_bytes / (att_ms / 1e3) / 1e9
     per_launch = alg_bytes / n_att
-    traffic = traffic_for(os.path.join(ROOT, "sparse_attention_indexing_latent_amd", "csrc", "lsa_attend.hip"),
-                          f"attend_{cfg.name}")
     res = dict(
         metric="1-layer LSA prefill tokens/s at 1M & 10M ctx; decode queries/s at 1M (1 GPU)",
         value=cfg.T / (ms_step / 1e3), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -266,10 +329,11 @@ def run_prefill(args, cid):
         data="synthetic (seeded topic-mixture keys, random-init projection)",
         config={"workload": cfg.name, "T": cfg.T, "H_kv": cfg.H_kv, "H_q": cfg.H_q, "head_dim": cfg.d,
                 "k": cfg.k, "n_sinks": cfg.n_sinks, "window": cfg.window, "search": cfg.search,
-                "beam": cfg.beam, "query_chunk": CHUNK, "attention": args.attend},
+                "beam": cfg.beam, "query_chunk": CHUNK, "attention": attend,
+                "bucket_pass": ws.get("bm_pass")},
         breakdown_ms={"build_buckets": timers["build"].total_ms() / args.steps,
                       "select": timers["select"].total_ms() / args.steps, "sparse_attend": att_ms},
-        roofline={"kernel": "attend_bf16_kernel<128>", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        roofline={"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                   "traffic": traffic, "alg_bytes_per_launch": per_launch,
                   "avg_launch_ms": att_ms / n_att, "launches_per_step": n_att},
@@ -415,8 +479,9 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=4, choices=[2, 4, 5])
-    ap.add_argument("--attend", default="gather", choices=["gather", "bucket"],
-                    help="prefill attention: per-query gather, or bucket-major (each bucket's K/V read once per pass)")
+    ap.add_argument("--attend", default="auto", choices=["auto", "gather", "bucket"],
+                    help="prefill attention: per-query gather, bucket-major (each bucket's K/V read once per pass), "
+                         "or auto (bucket-major when a bucket is expected in >= 8 pairs per pass)")
     ap.add_argument("--bm-pass", type=int, default=32768,
                     help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
     ap.add_argument("--no-decode", action="store_true")

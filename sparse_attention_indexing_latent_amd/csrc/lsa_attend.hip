@@ -443,33 +443,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Rows [RPI i, RPI i + RPI) of a tile, for the NI / 4 load instructions i
+// of wave `wid` (the four waves of a workgroup stage one tile together); the
+// tile holds keys k0 .. k0 + 31, a key past `kend` reads row 0 (weight 0).
+template <int D>
+__device__ __forceinline__ void load_tile_part(const uint16_t* Kbg, const uint16_t* Vbg, int64_t k0, int64_t kend,
+                                               int wid, u32x4 (&kr)[TileLds<D>::NI / 4],
+                                               u32x4 (&vr)[TileLds<D>::NI / 4]) {
+    using TL = TileLds<D>;
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < TL::NI / 4; ++i) {
+        const int row = TL::RPI * (wid * (TL::NI / 4) + i) + l / TL::CPR;
+        const int64_t key = k0 + row < kend ? k0 + row : 0;
+        kr[i] = *reinterpret_cast<const u32x4*>(Kbg + key * D + 8 * (l % TL::CPR));
+        vr[i] = *reinterpret_cast<const u32x4*>(Vbg + key * D + 8 * (l % TL::CPR));
+    }
+}
+template <int D>
+__device__ __forceinline__ void store_tile_part(const u32x4 (&kr)[TileLds<D>::NI / 4],
+                                                const u32x4 (&vr)[TileLds<D>::NI / 4], int wid, uint8_t* buf) {
+    using TL = TileLds<D>;
+    const int l = lane_id();
+#pragma unroll
+    for (int i = 0; i < TL::NI / 4; ++i) {
+        const int o = TL::off(TL::RPI * (wid * (TL::NI / 4) + i) + l / TL::CPR, l % TL::CPR);
+        *reinterpret_cast<u32x4*>(buf + o) = kr[i];
+        *reinterpret_cast<u32x4*>(buf + TL::ARR + o) = vr[i];
+    }
+}
+
 // Sinks + local window of the bucket-major path, then the merge of the
-// unit's bucket partials.  One wave per QW = 16 / G consecutive queries of a
-// KV head: column n of the MFMAs is query n / G, head n % G, so the window
-// keys the queries share are read once per wave instead of once per query.
-// The wave walks the keys in 32-key tiles aligned to multiples of 32 —
-// those covering [0, S1), S1 the largest sink end, then those covering the
-// rest of [kmin, kmax], the union of the windows — and a key counts for a
-// column when it is one of that query's sinks or inside its window, so no
-// key is counted twice.  A unit
-// whose list the bucket pass could not take (np = -1) has that list gathered
-// here, for its own columns only.
+// unit's bucket partials.  One workgroup per 4 QW consecutive queries of a
+// KV head (QW = 16 / G per wave): column n of a wave's MFMAs is query n / G,
+// head n % G, and the four waves share every 32-key tile, staged once in LDS
+// (double-buffered), so the window keys the queries have in common are read
+// once per workgroup.  The keys are walked in 32-key tiles aligned to
+// multiples of 32 — those covering [0, S1), S1 the largest sink end, then
+// those covering the rest of [kmin, kmax], the union of the windows — and a
+// key counts for a column when it is one of that query's sinks or inside its
+// window, so no key is counted twice; a column's keys fall in the same tiles
+// whichever queries share the workgroup, and a tile holding none of them
+// leaves its state exactly as it was.  A unit whose list the bucket pass
+// could not take (np = -1) has that list gathered afterwards by its wave,
+// for its own columns only.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bm_local_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ lr_idx, const int32_t* __restrict__ lr_cnt,
     AttArgs aa, uint16_t* __restrict__ O, int64_t nwg_padded) {
-    __shared__ __align__(16) uint8_t tile_lds[4 * TileLds<D>::BYTES];
-    constexpr int KS = D / 32, NC = 2 * KS, NI = TileLds<D>::NI;
+    using TL = TileLds<D>;
+    // window: two shared tiles; afterwards one private tile per wave
+    __shared__ __align__(16) uint8_t tile_lds[4 * TL::BYTES];
+    __shared__ int64_t red[3][4];
+    constexpr int KS = D / 32, NC = 2 * KS, NI = TL::NI, NIW = NI / 4;
     const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4, n = r;
-    const int G = aa.G, QW = 16 / G;
-    const int64_t ntrip = (aa.nqp + QW - 1) / QW;
-    const int64_t per_g = (int64_t)aa.B * ntrip;
-    const int64_t w_id = xcd_logical(blockIdx.x, nwg_padded) * 4 + wid;
-    if (w_id >= (int64_t)aa.H_kv * per_g) return;
-    const int64_t g = w_id / per_g, rem = w_id % per_g, b = rem / ntrip, tr = rem % ntrip;
+    const int G = aa.G, QW = 16 / G, TQ = 4 * QW;
+    const int64_t ntq = (aa.nqp + TQ - 1) / TQ;
+    const int64_t per_g = (int64_t)aa.B * ntq;
+    const int64_t wg = xcd_logical(blockIdx.x, nwg_padded);
+    if (wg >= (int64_t)aa.H_kv * per_g) return;   // whole workgroup
+    const int64_t g = wg / per_g, rem = wg % per_g, b = rem / ntq, tq = rem % ntq;
     const int qi = n / G, hh = n % G;
-    const int64_t il = tr * QW + qi;
+    const int64_t il = tq * TQ + wid * QW + qi;
     const bool colq = qi < QW && il < aa.nqp;
     const int64_t i = aa.q0 + (colq ? il : 0);
     const int64_t t = colq ? q_pos[b * aa.n_q + i] : -1;
@@ -506,72 +542,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         kmin = min(kmin, (int64_t)__shfl_xor(kmin, o));
         kmax = max(kmax, (int64_t)__shfl_xor(kmax, o));
     }
+    if (l == 0) {
+        red[0][wid] = S1;
+        red[1][wid] = kmin;
+        red[2][wid] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        S1 = max(S1, red[0][w]);
+        kmin = min(kmin, red[1][w]);
+        kmax = max(kmax, red[2][w]);
+    }
     const int64_t bg = b * aa.H_kv + g;
     const uint16_t* Kbg = K + bg * aa.t_cap * D;
     const uint16_t* Vbg = V + bg * aa.t_cap * D;
-    uint8_t* buf = tile_lds + wid * TileLds<D>::BYTES;
-    u32x4 kR[NI], vR[NI];
-    // 32-key tiles at multiples of 32: nt1 tiles from key 0 (the sinks), then
-    // from a2 = max(32 nt1, kmin rounded down) to kmax; a column's keys fall in
-    // the same tiles whichever queries share the wave, and a tile holding
-    // none of them leaves its state exactly as it was
     const int64_t nt1 = (S1 + 31) / 32;
     const int64_t kmin_al = kmin == INT64_MAX ? kmin : (kmin / 32) * 32;
     const int64_t a2 = 32 * nt1 > kmin_al ? 32 * nt1 : kmin_al;
     const int64_t nt2 = kmax >= a2 ? (kmax - a2 + 32) / 32 : 0;
     const int64_t ntiles = nt1 + nt2;
-    auto tile_start = [&](int64_t x) { return x < nt1 ? 32 * x : a2 + 32 * (x - nt1); };
-    auto tile_end = [&](int64_t) { return kmax + 1; };   // no row past the last window is read
+    const int64_t kend = kmax + 1;   // no row past the last window is read
     if (ntiles > 0) {
-        int64_t k0 = tile_start(0), ke = tile_end(0);
-        int32_t tok = k0 + (l & 31) < ke ? (int32_t)(k0 + (l & 31)) : -1;
-        load_tile<D>(Kbg, Vbg, tok, kR, vR);
+        u32x4 kr[NIW], vr[NIW];
+        int64_t k0 = 0 < nt1 ? 0 : a2;
+        load_tile_part<D>(Kbg, Vbg, k0, kend, wid, kr, vr);
         for (int64_t x = 0; x < ntiles; ++x) {
-            const int64_t n0 = x + 1 < ntiles ? tile_start(x + 1) : 0, ne = x + 1 < ntiles ? tile_end(x + 1) : 0;
-            const int32_t nxt = n0 + (l & 31) < ne ? (int32_t)(n0 + (l & 31)) : -1;
-            store_tile<D>(kR, vR, buf);
-            load_tile<D>(Kbg, Vbg, nxt, kR, vR);
+            uint8_t* buf = tile_lds + (x & 1) * TL::BYTES;
+            store_tile_part<D>(kr, vr, wid, buf);
+            __syncthreads();
+            const int64_t kn = x + 1 < nt1 ? 32 * (x + 1) : a2 + 32 * (x + 1 - nt1);
+            if (x + 1 < ntiles) load_tile_part<D>(Kbg, Vbg, kn, kend, wid, kr, vr);
             uint32_t va4 = 0, vb4 = 0;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t ka = k0 + 4 * h + v, kb = k0 + 16 + 4 * h + v;
-                va4 |= (ka < ke && (ka < se || (ka >= l0 && ka <= te))) ? (1u << v) : 0u;
-                vb4 |= (kb < ke && (kb < se || (kb >= l0 && kb <= te))) ? (1u << v) : 0u;
+                va4 |= (ka < se || (ka >= l0 && ka <= te)) ? (1u << v) : 0u;
+                vb4 |= (kb < se || (kb >= l0 && kb <= te)) ? (1u << v) : 0u;
             }
             if (__ballot((va4 | vb4) != 0u) != 0ull)
                 attend_tile<D>(va4, vb4, buf, r, qf, ident, h, aa.scale, m_run, l_run, acc);
-            k0 = n0;
-            ke = ne;
+            k0 = kn;
         }
     }
+    __syncthreads();   // the shared tiles are read no more: the LDS becomes one private tile per wave
     // long-range lists of the units the bucket pass left to the gather
     const uint64_t fb = __ballot(npl < 0);
-    for (int q2 = 0; q2 < QW; ++q2) {
-        if (((fb >> (q2 * G)) & 1ull) == 0ull) continue;   // column q2 * G stands for its query
-        const int lane0 = q2 * G;
-        const int64_t u2 = __shfl(u, lane0);
-        const int64_t t2 = __shfl(t, lane0);
-        const int32_t c2 = __shfl(cnt, lane0);
-        const int32_t* lr = lr_idx + u2 * aa.k;
-        auto tok_at = [&](int64_t j) -> int32_t {
-            if (j >= c2) return -1;
-            const int32_t tk = lr[j];
-            return (tk >= 0 && tk <= t2) ? tk : -1;
-        };
-        int32_t tok = tok_at(l & 31);
-        load_tile<D>(Kbg, Vbg, tok, kR, vR);
-        for (int64_t j = 0; j < c2; j += 32) {
-            const int32_t nxt = tok_at(j + 32 + (l & 31));
-            const uint64_t vm = __ballot(tok >= 0);
-            store_tile<D>(kR, vR, buf);
-            load_tile<D>(Kbg, Vbg, nxt, kR, vR);
-            if ((vm & 0xFFFFFFFFull) != 0ull) {
-                const bool mine = qi == q2;
-                attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
-                               mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h, aa.scale,
-                               m_run, l_run, acc);
+    if (fb != 0ull) {
+        uint8_t* buf = tile_lds + wid * TL::BYTES;
+        u32x4 kR[NI], vR[NI];
+        for (int q2 = 0; q2 < QW; ++q2) {
+            if (((fb >> (q2 * G)) & 1ull) == 0ull) continue;   // column q2 * G stands for its query
+            const int lane0 = q2 * G;
+            const int64_t u2 = __shfl(u, lane0);
+            const int64_t t2 = __shfl(t, lane0);
+            const int32_t c2 = __shfl(cnt, lane0);
+            const int32_t* lr = lr_idx + u2 * aa.k;
+            auto tok_at = [&](int64_t j) -> int32_t {
+                if (j >= c2) return -1;
+                const int32_t tk = lr[j];
+                return (tk >= 0 && tk <= t2) ? tk : -1;
+            };
+            int32_t tok = tok_at(l & 31);
+            load_tile<D>(Kbg, Vbg, tok, kR, vR);
+            for (int64_t j = 0; j < c2; j += 32) {
+                const int32_t nxt = tok_at(j + 32 + (l & 31));
+                const uint64_t vm = __ballot(tok >= 0);
+                store_tile<D>(kR, vR, buf);
+                load_tile<D>(Kbg, Vbg, nxt, kR, vR);
+                if ((vm & 0xFFFFFFFFull) != 0ull) {
+                    const bool mine = qi == q2;
+                    attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
+                                   mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h, aa.scale,
+                                   m_run, l_run, acc);
+                }
+                tok = nxt;
             }
-            tok = nxt;
         }
     }
     l_run += __shfl_xor(l_run, 16);
@@ -709,9 +755,8 @@ int attend_splits(int64_t n_units, int window, int k) {
 hipError_t launch_attend_local(const void* Q, const void* K, const void* V, const int64_t* q_pos,
                                const int32_t* lr_idx, const int32_t* lr_cnt, const AttArgs& aa, int D, void* O,
                                hipStream_t st) {
-    const int QW = 16 / aa.G;
-    const int64_t waves = (int64_t)aa.H_kv * aa.B * ((aa.nqp + QW - 1) / QW);
-    int64_t nwg = (waves + 3) / 4;
+    const int TQ = 4 * (16 / aa.G);
+    int64_t nwg = (int64_t)aa.H_kv * aa.B * ((aa.nqp + TQ - 1) / TQ);
     nwg = (nwg + 7) & ~(int64_t)7;
     if (D == 128)
         hipLaunchKernelGGL(bm_local_kernel<128>, dim3((unsigned)nwg), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
