@@ -198,7 +198,8 @@ constexpr int64_t kBmPoolPerUnit = 80;
 struct BmWs {
     int64_t units, leaves_max, nbins, nbins_pad;
     uint32_t pool_cap;
-    size_t off_lcnt, off_loff, off_ctot, off_csum, off_uoff, off_unp, off_rec, off_srec, off_po, off_pml, total;
+    size_t off_lcnt, off_loff, off_ctot, off_csum, off_gpre, off_uoff, off_unp, off_rec, off_srec, off_work, off_po, off_pml,
+        total;
 };
 
 void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) {
@@ -213,14 +214,16 @@ void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) 
     if (pool > ((int64_t)1 << 31)) pool = (int64_t)1 << 31;
     w.pool_cap = (uint32_t)pool;
     size_t o = 0;
-    w.off_lcnt = o;   o = align256(o + (size_t)(w.nbins_pad + 1) * 4);
+    w.off_lcnt = o;   o = align256(o + (size_t)(w.nbins_pad + 2) * 4);
     w.off_loff = o;   o = align256(o + (size_t)w.nbins_pad * 4);
-    w.off_ctot = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 4);
-    w.off_csum = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 4);
+    w.off_ctot = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 8);
+    w.off_csum = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 8);
+    w.off_gpre = o;   o = align256(o + (size_t)(w.nbins_pad / 64) * 4);
     w.off_uoff = o;   o = align256(o + (size_t)w.units * 4);
     w.off_unp = o;    o = align256(o + (size_t)w.units * 4);
     w.off_rec = o;    o = align256(o + (size_t)pool * 16);
     w.off_srec = o;   o = align256(o + (size_t)pool * 16);
+    w.off_work = o;   o = align256(o + (size_t)w.nbins * 17 * 16);
     w.off_po = o;     o = align256(o + (size_t)pool * G * D * 2);
     w.off_pml = o;    o = align256(o + (size_t)pool * G * 16);
     w.total = o;
@@ -566,10 +569,12 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         bm.loff = reinterpret_cast<uint32_t*>(wb + w.off_loff);
         bm.ctot = reinterpret_cast<uint32_t*>(wb + w.off_ctot);
         bm.csum = reinterpret_cast<uint32_t*>(wb + w.off_csum);
+        bm.gpre = reinterpret_cast<uint32_t*>(wb + w.off_gpre);
         bm.unit_off = reinterpret_cast<uint32_t*>(wb + w.off_uoff);
         bm.unit_np = reinterpret_cast<int32_t*>(wb + w.off_unp);
         bm.rec = reinterpret_cast<lsa::u32x4*>(wb + w.off_rec);
         bm.srec = reinterpret_cast<lsa::u32x4*>(wb + w.off_srec);
+        bm.work = reinterpret_cast<lsa::u32x4*>(wb + w.off_work);
         bm.po = reinterpret_cast<uint16_t*>(wb + w.off_po);
         bm.pml = reinterpret_cast<float*>(wb + w.off_pml);
         lsa::AttArgs aa;

@@ -33,6 +33,10 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -43,34 +47,47 @@ __global__ __launch_bounds__(256) void bm_clear_kernel(uint32_t* __restrict__ p,
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
 
-// Pairs of the current block: lane r turns the mask gathered for bucket
-// rank r into one pair (if any key of it was listed) and clears it.
-__device__ __forceinline__ int bm_flush(unsigned long long* mk, uint32_t* pl, unsigned long long* pm, int blk,
-                                        int np) {
+constexpr int kBmTableBlocks = 8;   // blocks whose bucket masks a pairs wave holds at once
+
+// Pairs of the blocks in the wave's table: for slot s (block tb[s]), lane r
+// turns the mask gathered for bucket rank r into one pair (if any key of it
+// was listed) and clears it.
+__device__ __forceinline__ int bm_flush(unsigned long long (*tab)[64], const int* tb, int used, uint32_t* pl,
+                                        unsigned long long* pm, int np) {
     const int l = lane_id();
     wave_lds_sync();
-    const unsigned long long m = mk[l];
-    const uint64_t nz = __ballot(m != 0ull);
-    const int idx = np + __popcll(nz & ((1ull << l) - 1ull));
-    if (m != 0ull && idx < kBmUnitCap) {
-        pl[idx] = (uint32_t)(blk * kLeavesPerBlock + l);
-        pm[idx] = m;
+    for (int s = 0; s < used; ++s) {
+        const unsigned long long m = tab[s][l];
+        const uint64_t nz = __ballot(m != 0ull);
+        const int idx = np + __popcll(nz & ((1ull << l) - 1ull));
+        if (m != 0ull) {
+            if (idx < kBmUnitCap) {
+                pl[idx] = (uint32_t)(tb[s] * kLeavesPerBlock + l);
+                pm[idx] = m;
+            }
+            tab[s][l] = 0ull;
+        }
+        np += __popcll(nz);
     }
-    mk[l] = 0ull;
     wave_lds_sync();
-    return np + __popcll(nz);
+    return np;
 }
 
 // One wave per local unit ul = (b * nqp + i - q0) * H_kv + g.  A listed
 // token tk lies in block tk / 2048, entry e = (tk / 4) % 512 of it, bucket
 // rank entry_leaf[e] and key number 4 entry_pos[e] + tk % 4 of that bucket.
-// The list is ascending, so the tokens of one block are consecutive: their
-// keys are OR-ed into 64 per-rank masks in LDS and flushed when the block
-// changes.
+// The list is ascending, so the tokens of one block are consecutive: the
+// wave gives each new block the next slot of a table of kBmTableBlocks
+// blocks x 64 bucket masks in LDS, ORs every token's key bit into its slot
+// (one LDS atomic per token, a whole group of 64 tokens at once) and turns
+// the table into pairs when it is full and at the end.  A bucket whose
+// tokens straddle a flush gives two pairs with disjoint key masks, each
+// merged as its own partial: the same attention.
 __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
                                                        const int32_t* __restrict__ lr_idx,
                                                        const int32_t* __restrict__ lr_cnt, AttArgs aa, BmBuffers bm) {
-    __shared__ unsigned long long mk[4][64];
+    __shared__ unsigned long long tab[4][kBmTableBlocks][64];
+    __shared__ int tbl[4][kBmTableBlocks];
     __shared__ uint32_t pl[4][kBmUnitCap];
     __shared__ unsigned long long pm[4][kBmUnitCap];
     const int l = lane_id(), wid = threadIdx.x >> 6;
@@ -83,7 +100,8 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
     const int64_t t = q_pos[b * aa.n_q + i];
     int32_t cnt = lr_cnt[u];
     cnt = cnt < aa.k ? cnt : aa.k;
-    mk[wid][l] = 0ull;
+#pragma unroll
+    for (int x = 0; x < kBmTableBlocks; ++x) tab[wid][x][l] = 0ull;
     wave_lds_sync();
     int np = 0;
     bool bad = false;
@@ -94,7 +112,7 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
         const uint8_t* el = cv.eleaf + bg * cv.s_eleaf;
         const uint8_t* ep = cv.epos + bg * cv.s_epos;
         int32_t prev = -1;
-        int cur = -1;
+        int used = 0, lastb = -1;   // table slots in use; block of the last one
         // rounds of 16 groups of 64 listed tokens: every load of a round is
         // issued before the groups are walked in order
         constexpr int RG = 16;
@@ -133,20 +151,33 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
                 prev = __shfl(tk, 63);   // read only when lane 63 was valid (a further group exists)
                 const int blk = tk / kBlockTokens;
                 const int rank = (int)(inf[m] & 0xFFu), bit = (int)(inf[m] >> 8);
+                // pending lanes are a contiguous run; each takes slot used - 1 + (new blocks up to it)
                 uint64_t pending = __ballot(valid);
                 while (pending != 0ull) {
-                    const int cb = __shfl(blk, __builtin_ctzll(pending));
-                    if (cb != cur) {
-                        if (cur >= 0) np = bm_flush(mk[wid], pl[wid], pm[wid], cur, np);
-                        cur = cb;
+                    const bool pend = (pending >> l) & 1ull;
+                    int pb = __shfl_up(blk, 1);
+                    if (l == __builtin_ctzll(pending)) pb = lastb;
+                    const uint64_t newm = __ballot(pend && blk != pb);
+                    const int slot = used - 1 + __popcll(newm & ((2ull << l) - 1ull));
+                    const uint64_t take = __ballot(pend && slot < kBmTableBlocks);
+                    if (take == 0ull) {   // table full: turn it into pairs
+                        np = bm_flush(tab[wid], tbl[wid], used, pl[wid], pm[wid], np);
+                        used = 0;
+                        lastb = -1;
+                        continue;
                     }
-                    const uint64_t mine = __ballot(valid && blk == cb) & pending;
-                    if ((mine >> l) & 1ull) atomicOr(&mk[wid][rank], 1ull << bit);
-                    pending &= ~mine;
+                    if ((take >> l) & 1ull) {
+                        if ((newm >> l) & 1ull) tbl[wid][slot] = blk;
+                        atomicOr(&tab[wid][slot][rank], 1ull << bit);
+                    }
+                    const int last = 63 - __builtin_clzll(take);
+                    used = __shfl(slot, last) + 1;
+                    lastb = __shfl(blk, last);
+                    pending &= ~take;
                 }
             }
         }
-        if (!bad && cur >= 0) np = bm_flush(mk[wid], pl[wid], pm[wid], cur, np);
+        if (!bad && used > 0) np = bm_flush(tab[wid], tbl[wid], used, pl[wid], pm[wid], np);
     }
     if (bad || np > kBmUnitCap) np = -1;
     uint32_t base = 0;
@@ -171,24 +202,34 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
 }
 
 // Exclusive scan of the pair counts inside each chunk of kBmScanChunk bins
-// (16 per thread), and the chunk's total.
+// (16 per thread), and the chunk's total; likewise for the number of bins
+// that have pairs (per 64-bin group, for the work records in bin order).
 __global__ __launch_bounds__(256) void bm_scan_kernel(BmBuffers bm) {
-    __shared__ uint32_t ws[4];
+    __shared__ uint32_t ws[4], wz[4];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
     const int64_t b0 = (int64_t)blockIdx.x * kBmScanChunk + tid * 16;
     const u32x4* src = reinterpret_cast<const u32x4*>(bm.lcnt + b0);
     u32x4 v[4];
-    uint32_t s = 0;
+    uint32_t s = 0, z = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         v[j] = src[j];
         s += v[j][0] + v[j][1] + v[j][2] + v[j][3];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) z += v[j][x] != 0u ? 1u : 0u;
     }
+    const uint32_t zincl = (uint32_t)wave_incl_scan((int)z);
+    if (l == 63) wz[wid] = zincl;
     const uint32_t incl = (uint32_t)wave_incl_scan((int)s);
     if (l == 63) ws[wid] = incl;
     __syncthreads();
-    uint32_t wpre = 0;
-    for (int w = 0; w < wid; ++w) wpre += ws[w];
+    uint32_t wpre = 0, zpre = 0;
+    for (int w = 0; w < wid; ++w) {
+        wpre += ws[w];
+        zpre += wz[w];
+    }
+    if ((tid & 3) == 0) bm.gpre[b0 / 64] = zpre + zincl - z;
+    if (tid == 255) bm.ctot[gridDim.x + blockIdx.x] = zpre + zincl;
     uint32_t run = wpre + incl - s;
     u32x4* dst = reinterpret_cast<u32x4*>(bm.loff + b0);
 #pragma unroll
@@ -204,25 +245,32 @@ __global__ __launch_bounds__(256) void bm_scan_kernel(BmBuffers bm) {
     if (tid == 255) bm.ctot[blockIdx.x] = wpre + incl;
 }
 
-// Exclusive scan of the chunk totals: one workgroup, 1024 chunks per step.
+// Exclusive scans of the chunk totals (pairs, then bins with pairs): one
+// workgroup, 1024 chunks per step; the number of bins with pairs (work
+// records) goes to lcnt[nbins_pad + 1].
 __global__ __launch_bounds__(1024) void bm_scan_top_kernel(BmBuffers bm, int64_t nch) {
     __shared__ uint32_t ws[16];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
-    uint32_t carry = 0;
-    for (int64_t c0 = 0; c0 < nch; c0 += 1024) {
-        const int64_t c = c0 + tid;
-        const uint32_t v = c < nch ? bm.ctot[c] : 0u;
-        const uint32_t incl = (uint32_t)wave_incl_scan((int)v);
-        if (l == 63) ws[wid] = incl;
-        __syncthreads();
-        uint32_t wpre = 0, tot = 0;
-        for (int w = 0; w < 16; ++w) {
-            wpre += w < wid ? ws[w] : 0u;
-            tot += ws[w];
+    for (int half = 0; half < 2; ++half) {
+        const uint32_t* in = bm.ctot + half * nch;
+        uint32_t* out = bm.csum + half * nch;
+        uint32_t carry = 0;
+        for (int64_t c0 = 0; c0 < nch; c0 += 1024) {
+            const int64_t c = c0 + tid;
+            const uint32_t v = c < nch ? in[c] : 0u;
+            const uint32_t incl = (uint32_t)wave_incl_scan((int)v);
+            if (l == 63) ws[wid] = incl;
+            __syncthreads();
+            uint32_t wpre = 0, tot = 0;
+            for (int w = 0; w < 16; ++w) {
+                wpre += w < wid ? ws[w] : 0u;
+                tot += ws[w];
+            }
+            if (c < nch) out[c] = carry + wpre + incl - v;
+            carry += tot;
+            __syncthreads();
         }
-        if (c < nch) bm.csum[c] = carry + wpre + incl - v;
-        carry += tot;
-        __syncthreads();
+        if (half == 1 && tid == 0) bm.lcnt[bm.nbins_pad + 1] = carry;
     }
 }
 
@@ -243,6 +291,53 @@ __global__ __launch_bounds__(256) void bm_scatter_kernel(AttArgs aa, BmBuffers b
         const uint32_t p = base + (uint32_t)idx;
         const u32x4 r = bm.rec[p];
         bm.srec[bm_bin_start(bm, r[0]) + r[1]] = u32x4{(uint32_t)ul, p, r[2], r[3]};
+    }
+}
+
+// Work records of the bins that received pairs: one wave per 64 bins; for
+// each such bin the wave writes (pair start, pairs, keys, b * H_kv + g) and
+// the bucket's key tokens in member order (key j = token 4 members[j / 4] +
+// j % 4 of its block; keys past the bucket repeat its first).  Records are
+// in bin order, so workgroups running together take neighbouring buckets,
+// which share many of their queries (rows then found in the caches).
+__global__ __launch_bounds__(256) void bm_prep_kernel(CacheView cv, BmBuffers bm) {
+    __shared__ uint16_t memb[4][64][16];
+    const int l = lane_id(), wid = threadIdx.x >> 6;
+    const int64_t b0 = ((int64_t)blockIdx.x * 4 + wid) * 64;
+    if (b0 >= bm.nbins) return;
+    const int64_t bin = b0 + l;
+    const uint32_t np = bin < bm.nbins ? bm.lcnt[bin] : 0u;
+    uint64_t nz = __ballot(np > 0u);
+    if (nz == 0ull) return;
+    // every lane with pairs fetches its bucket's meta and members at once
+    const int64_t bg = bin / bm.leaves_max, leaf = bin % bm.leaves_max;
+    const int blk = (int)(leaf / kLeavesPerBlock);
+    uint32_t meta = 0;
+    if (np > 0u) {
+        meta = cv.meta[bg * cv.s_meta + leaf];
+        uint16_t e[16];
+        load_members(cv.members + bg * cv.s_members + (int64_t)blk * kBlockEntries, (int)((meta >> 8) & 0x3FF), e);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) memb[wid][l][j] = e[j];
+    }
+    // records in bin order: bins with pairs before this 64-bin group, then inside it
+    const uint32_t base = bm.csum[bm.nbins_pad / kBmScanChunk + b0 / kBmScanChunk] + bm.gpre[b0 / 64];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (uint32_t idx = 0; nz != 0ull; ++idx) {
+        const int src = __builtin_ctzll(nz);
+        nz &= nz - 1ull;
+        const uint32_t npairs = __shfl(np, src);
+        const uint32_t m = __shfl(meta, src);
+        const int64_t bgs = (b0 + src) / bm.leaves_max;
+        const int blks = (int)(((b0 + src) % bm.leaves_max) / kLeavesPerBlock);
+        const int ntok = kPool * (int)(m & 0xFF);
+        const int j = l < ntok ? l : 0;
+        const int32_t tk = blks * kBlockTokens + kPool * (int)memb[wid][src][j / kPool] + j % kPool;
+        u32x4* rec = bm.work + (int64_t)(base + idx) * 17;
+        if (l == 0) rec[0] = u32x4{bm_bin_start(bm, (uint32_t)(b0 + src)), npairs, (uint32_t)ntok, (uint32_t)bgs};
+        reinterpret_cast<int32_t*>(rec + 1)[l] = tk;
     }
 }
 
@@ -276,7 +371,7 @@ __device__ __forceinline__ int vt_slot(int j) {
     return 32 * kk + 8 * ((r % 16) / 4) + 4 * (r / 16) + r % 4;
 }
 
-// One workgroup per bin (grid-stride): a bucket's keys/values in LDS, then
+// One workgroup per work record (grid-stride): a bucket's keys/values in LDS, then
 // groups of GP = 16 / G pairs (G query heads each) per wave.  Lane (n, h):
 // column n = pair n / G, head n % G; S^T tiles are 16 keys x 16 columns
 // (rows 4h + v), O^T tiles 16 dims x 16 columns.
@@ -287,38 +382,27 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
     using LL = LeafLds<D>;
     constexpr int KS = D / 32, NDT = D / 16, CPR = D / 8;
     __shared__ __align__(16) uint8_t lds[LL::BYTES];
-    __shared__ int32_t toks[64];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
     const int G = aa.G, GP = 16 / G;
     const float sl2 = aa.scale;
-    for (int64_t bin = blockIdx.x; bin < bm.nbins; bin += gridDim.x) {
-        const uint32_t npairs = bm.lcnt[bin];
-        if (npairs == 0u) continue;
-        const uint32_t start = bm_bin_start(bm, (uint32_t)bin);
-        const int64_t bg = bin / bm.leaves_max, leaf = bin % bm.leaves_max;
-        const int blk = (int)(leaf / kLeavesPerBlock);
-        const uint32_t meta = cv.meta[bg * cv.s_meta + leaf];
-        const int ntok = kPool * (int)(meta & 0xFF);
+    const uint32_t n_work = bm.lcnt[bm.nbins_pad + 1];
+    for (uint32_t wk = blockIdx.x; wk < n_work; wk += gridDim.x) {
+        const u32x4* rec = bm.work + (int64_t)wk * 17;
+        const u32x4 hdr = rec[0];
+        const uint32_t start = hdr[0], npairs = hdr[1];
+        const int ntok = (int)hdr[2];
+        const int64_t bg = hdr[3];
+        const int32_t* tokr = reinterpret_cast<const int32_t*>(rec + 1);
         const int nrow = (ntok + 31) & ~31;   // keys staged: whole 32-key k-steps
         __syncthreads();   // the previous bucket's LDS is no longer read
-        if (tid < 64) {
-            int32_t tk = -1;
-            if (tid < ntok) {
-                const int off = (int)((meta >> 8) & 0x3FF);
-                const int e = cv.members[bg * cv.s_members + (int64_t)blk * kBlockEntries + off + tid / kPool];
-                tk = blk * kBlockTokens + kPool * e + tid % kPool;
-            }
-            toks[tid] = tk;
-        }
-        __syncthreads();
         const uint16_t* Kbg = K + bg * aa.t_cap * D;
         const uint16_t* Vbg = V + bg * aa.t_cap * D;
-        // staging: item = (key pair jp, chunk c); keys past the bucket repeat key 0 (finite, weight 0)
+        // staging: item = (key pair jp, chunk c); keys past the bucket repeat its first (finite, weight 0)
         for (int it = tid; it < (nrow / 2) * CPR; it += 256) {
             const int jp = it / CPR, c = it % CPR;
             const int j0 = 2 * jp;
-            const int32_t t0 = toks[j0] >= 0 ? toks[j0] : toks[0];
-            const int32_t t1 = toks[j0 + 1] >= 0 ? toks[j0 + 1] : toks[0];
+            const u32x2 tp = *reinterpret_cast<const u32x2*>(tokr + j0);
+            const int32_t t0 = (int32_t)tp[0], t1 = (int32_t)tp[1];
             const u32x4 k0 = *reinterpret_cast<const u32x4*>(Kbg + (int64_t)t0 * D + 8 * c);
             const u32x4 k1 = *reinterpret_cast<const u32x4*>(Kbg + (int64_t)t1 * D + 8 * c);
             const u32x4 v0 = *reinterpret_cast<const u32x4*>(Vbg + (int64_t)t0 * D + 8 * c);
@@ -438,13 +522,21 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
                 const float inv = amax > 0.f ? 1.0f / amax : 0.f;
                 uint16_t* po = bm.po + slot * D;
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    uint32_t w2[2];
-#pragma unroll
-                    for (int v = 0; v < 4; v += 2)
-                        w2[v / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[dt][v] * inv)) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[dt][v + 1] * inv)) << 16);
-                    *reinterpret_cast<u32x2*>(po + 16 * dt + 4 * h) = u32x2{w2[0], w2[1]};
+                for (int m = 0; m < NDT / 2; ++m) {
+                    // lane h holds dims 32m + 4h + [0,4) (A) and 32m + 16 + 4h + [0,4) (B); lanes h, h^1
+                    // swap one of them so that each writes 8 consecutive dims (16 bytes, 64 contiguous
+                    // bytes per column and store instruction)
+                    const u32x2 A = u32x2{pk_f16(acc[2 * m][0] * inv, acc[2 * m][1] * inv),
+                                          pk_f16(acc[2 * m][2] * inv, acc[2 * m][3] * inv)};
+                    const u32x2 Bv = u32x2{pk_f16(acc[2 * m + 1][0] * inv, acc[2 * m + 1][1] * inv),
+                                           pk_f16(acc[2 * m + 1][2] * inv, acc[2 * m + 1][3] * inv)};
+                    const bool even = (h & 1) == 0;
+                    const u32x2 send = even ? Bv : A;
+                    const u32x2 got = u32x2{(uint32_t)__shfl_xor((int)send[0], 16), (uint32_t)__shfl_xor((int)send[1], 16)};
+                    if (even)
+                        *reinterpret_cast<u32x4*>(po + 32 * m + 4 * h) = u32x4{A[0], A[1], got[0], got[1]};
+                    else
+                        *reinterpret_cast<u32x4*>(po + 32 * m + 16 + 4 * (h - 1)) = u32x4{got[0], got[1], Bv[0], Bv[1]};
                 }
                 if (h == 0) *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx, psum, amax, 0.f};
             }
@@ -463,7 +555,7 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
 hipError_t launch_bucket_partials(const CacheView& cv, const void* Q, const void* K, const void* V,
                                   const int64_t* q_pos, const int32_t* lr_idx, const int32_t* lr_cnt,
                                   const AttArgs& aa, const BmBuffers& bm, int D, hipStream_t st) {
-    const int64_t nclear = bm.nbins_pad + 1;
+    const int64_t nclear = bm.nbins_pad + 2;
     const unsigned cg = (unsigned)((nclear + 2047) / 2048 < 1024 ? (nclear + 2047) / 2048 : 1024);
     hipLaunchKernelGGL(bm_clear_kernel, dim3(cg), dim3(256), 0, st, bm.lcnt, nclear);
     if (aa.n_units == 0) return hipGetLastError();
@@ -473,6 +565,7 @@ hipError_t launch_bucket_partials(const CacheView& cv, const void* Q, const void
     hipLaunchKernelGGL(bm_scan_kernel, dim3((unsigned)nch), dim3(256), 0, st, bm);
     hipLaunchKernelGGL(bm_scan_top_kernel, dim3(1), dim3(1024), 0, st, bm, nch);
     hipLaunchKernelGGL(bm_scatter_kernel, dim3(ug), dim3(256), 0, st, aa, bm);
+    hipLaunchKernelGGL(bm_prep_kernel, dim3((unsigned)((bm.nbins + 255) / 256)), dim3(256), 0, st, cv, bm);
     const unsigned lg = (unsigned)(bm.nbins < 8192 ? bm.nbins : 8192);
     if (D == 128)
         hipLaunchKernelGGL(bm_leaf_kernel<128>, dim3(lg), dim3(256), 0, st, cv, static_cast<const uint16_t*>(Q),

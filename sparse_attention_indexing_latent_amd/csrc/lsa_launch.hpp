@@ -62,15 +62,18 @@ struct BmBuffers {
     int64_t nbins;             // B * H_kv * leaves_max
     int64_t nbins_pad;         // nbins rounded up to the scan chunk
     uint32_t pool_cap;
-    uint32_t* lcnt;            // [nbins_pad + 1] pairs per bin, then the pool cursor
+    uint32_t* lcnt;            // [nbins_pad + 2] pairs per bin, then the pool cursor, then the work count
     uint32_t* loff;            // [nbins_pad] offset of the bin's pairs inside its scan chunk
-    uint32_t* ctot;            // [nbins_pad / chunk] pairs per scan chunk
-    uint32_t* csum;            // [nbins_pad / chunk] exclusive scan of ctot
+    uint32_t* ctot;            // [2 * nbins_pad / chunk] pairs, then bins with pairs, per scan chunk
+    uint32_t* csum;            // [2 * nbins_pad / chunk] exclusive scans of both halves of ctot
+    uint32_t* gpre;            // [nbins_pad / 64] bins with pairs before each 64-bin group, inside its chunk
     uint32_t* unit_off;        // [n_units]
     int32_t* unit_np;          // [n_units]
     u32x4* rec;                // [pool_cap] (bin, arrival rank in the bin, key mask lo, hi); mask bit j:
                                //   key j of the bucket (member order) is listed
     u32x4* srec;               // [pool_cap] grouped by bin: (local unit, pair slot, key mask lo, hi)
+    u32x4* work;               // [nbins, 17] one record per bin with pairs: (pair start, pairs, keys, b * H_kv + g),
+                               //   then the bucket's 64 key tokens (member order; past the bucket: its first)
     uint16_t* po;              // [pool_cap, G, D] fp16 partial outputs, divided by their scale
     float* pml;                // [pool_cap, G, 4] (max, denominator, scale, 0)
 };
