@@ -236,8 +236,9 @@ lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, con
  * lsa_attend_bucket_major_workspace_bytes(.., 1, ..); the call then runs
  * ceil(n_q / P) passes, P the most queries the workspace holds.  A
  * (query, KV head) whose list is not strictly ascending, holds a token outside
- * [sink end, window start), touches more than 256 buckets, or finds the pass's
- * pair pool full is gathered whole instead (same result, slower).  bf16 only
+ * [sink end, window start), touches more than 256 buckets, or finds its
+ * share of the pass's pair pool full is gathered whole instead (same result,
+ * slower).  bf16 only
  * (LSA_ERR_UNSUPPORTED otherwise); lr_idx rows must not be modified while
  * the call's kernels run. */
 lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache,

@@ -214,7 +214,7 @@ void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) 
     if (pool > ((int64_t)1 << 31)) pool = (int64_t)1 << 31;
     w.pool_cap = (uint32_t)pool;
     size_t o = 0;
-    w.off_lcnt = o;   o = align256(o + (size_t)(w.nbins_pad + 2) * 4);
+    w.off_lcnt = o;   o = align256(o + (size_t)(w.nbins_pad + 2 + lsa::kBmCursors) * 4);
     w.off_loff = o;   o = align256(o + (size_t)w.nbins_pad * 4);
     w.off_ctot = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 8);
     w.off_csum = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 8);

@@ -23,7 +23,7 @@
 //            (whole GQA groups of 16 / G pairs) per MFMA column tile
 // A unit whose list the pairs step cannot take (not strictly ascending, a key
 // outside [sink end, window start), more than kBmUnitCap buckets, or a full
-// pool) keeps np = -1 and is gathered whole by the gather kernel instead.
+// pool slice) keeps np = -1 and is gathered whole by the window kernel instead.
 
 #include "lsa_launch.hpp"
 
@@ -180,11 +180,15 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
         if (!bad && used > 0) np = bm_flush(tab[wid], tbl[wid], used, pl[wid], pm[wid], np);
     }
     if (bad || np > kBmUnitCap) np = -1;
+    // pair slots from pool slice ul % kBmCursors (one atomic per unit, spread over the slices' cursors)
     uint32_t base = 0;
     if (np > 0) {
-        if (l == 0) base = atomicAdd(bm.lcnt + bm.nbins_pad, (uint32_t)np);
-        base = __shfl(base, 0);
-        if ((uint64_t)base + (uint64_t)np > (uint64_t)bm.pool_cap) np = -1;
+        const uint32_t slice = bm.pool_cap / kBmCursors, c = (uint32_t)(ul % kBmCursors);
+        uint32_t off = 0;
+        if (l == 0) off = atomicAdd(bm.lcnt + bm.nbins_pad + 2 + c, (uint32_t)np);
+        off = __shfl(off, 0);
+        if ((uint64_t)off + (uint64_t)np > (uint64_t)slice) np = -1;
+        base = c * slice + off;
     }
     if (np > 0) {
         wave_lds_sync();
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
 hipError_t launch_bucket_partials(const CacheView& cv, const void* Q, const void* K, const void* V,
                                   const int64_t* q_pos, const int32_t* lr_idx, const int32_t* lr_cnt,
                                   const AttArgs& aa, const BmBuffers& bm, int D, hipStream_t st) {
-    const int64_t nclear = bm.nbins_pad + 2;
+    const int64_t nclear = bm.nbins_pad + 2 + kBmCursors;
     const unsigned cg = (unsigned)((nclear + 2047) / 2048 < 1024 ? (nclear + 2047) / 2048 : 1024);
     hipLaunchKernelGGL(bm_clear_kernel, dim3(cg), dim3(256), 0, st, bm.lcnt, nclear);
     if (aa.n_units == 0) return hipGetLastError();

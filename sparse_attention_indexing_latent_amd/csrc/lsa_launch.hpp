@@ -62,7 +62,8 @@ struct BmBuffers {
     int64_t nbins;             // B * H_kv * leaves_max
     int64_t nbins_pad;         // nbins rounded up to the scan chunk
     uint32_t pool_cap;
-    uint32_t* lcnt;            // [nbins_pad + 2] pairs per bin, then the pool cursor, then the work count
+    uint32_t* lcnt;            // [nbins_pad + 2 + kBmCursors] pairs per bin, unused, the work count, then
+                               //   the pool cursors (cursor c hands out slots of pool slice c)
     uint32_t* loff;            // [nbins_pad] offset of the bin's pairs inside its scan chunk
     uint32_t* ctot;            // [2 * nbins_pad / chunk] pairs, then bins with pairs, per scan chunk
     uint32_t* csum;            // [2 * nbins_pad / chunk] exclusive scans of both halves of ctot
@@ -79,6 +80,7 @@ struct BmBuffers {
 };
 constexpr int kBmScanChunk = 4096;   // bins per workgroup of the offset scan
 constexpr int kBmUnitCap = 256;      // most buckets one unit may take through the bucket-major path
+constexpr int kBmCursors = 256;      // pool slices, so that the units' slot requests spread over many words
 
 hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
                         const void* W, hipStream_t st);
