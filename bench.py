@@ -269,14 +269,16 @@ def run_prefill(args, cid):
     ws["cache"] = cache0.buf
     attend = args.attend
     if attend != "gather":
-        # passes of up to --bm-pass queries, fewer if free memory is short (workspace <= 40% of it)
+        # passes of up to --bm-pass queries, fewer if free memory is short (workspace <= 60% of it)
+        torch.cuda.empty_cache()
         free = torch.cuda.mem_get_info(dev)[0]
         n_pass = args.bm_pass
-        while n_pass > 1024 and lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass) > 0.4 * free:
+        while n_pass > 1024 and lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass) > 0.6 * free:
             n_pass //= 2
-        # auto: bucket-major when a bucket is expected in >= 8 pairs per pass (n_pass * k / T)
+        # auto: bucket-major when a bucket is expected in >= 2 pairs per pass (n_pass * k / T); measured:
+        # ahead of the gather at 1M (64 per pass) and at 10M (3.2 per pass: 8.7 s vs 14.0 s per layer)
         if attend == "auto":
-            attend = "bucket" if n_pass * cfg.k >= 8 * cfg.T else "gather"
+            attend = "bucket" if n_pass * cfg.k >= 2 * cfg.T else "gather"
         if attend == "bucket":
             ws["bm"] = torch.empty(lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass),
                                    dtype=torch.uint8, device=dev)
@@ -481,7 +483,7 @@ def main():
     ap.add_argument("--config", type=int, default=4, choices=[2, 4, 5])
     ap.add_argument("--attend", default="auto", choices=["auto", "gather", "bucket"],
                     help="prefill attention: per-query gather, bucket-major (each bucket's K/V read once per pass), "
-                         "or auto (bucket-major when a bucket is expected in >= 8 pairs per pass)")
+                         "or auto (bucket-major when a bucket is expected in >= 2 pairs per pass)")
     ap.add_argument("--bm-pass", type=int, default=32768,
                     help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
     ap.add_argument("--no-decode", action="store_true")
