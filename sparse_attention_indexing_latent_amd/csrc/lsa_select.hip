@@ -1697,12 +1697,51 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
         const int P = pow2_at_least(ncand);
         for (int j = ncand + l; j < P; j += 64) keys[wid][j] = 0ull;
         wave_sync();
-        wave_sort_desc(keys[wid], P);
-        int valid = 0;
-        for (int j = l; j < P; j += 64) valid += keys[wid][j] != 0ull ? 1 : 0;
-        valid = (int)wave_sum((float)valid);
-        nf = valid < sa.beam ? valid : sa.beam;
-        for (int j = l; j < nf; j += 64) front[wid][j] = rank_key_id(keys[wid][j]);
+        // the next front is the set of the top `beam` candidates by key (key 0: no candidate),
+        // found exactly by a threshold: the beam-th largest high word (the ordered score) by a
+        // binary search on ballot counts, then among the keys equal to it the low word (the
+        // inverted id) likewise; only the leaves need their rank order, for the walk
+        {
+            const uint64_t ka = l < P ? keys[wid][l] : 0ull, kb = 64 + l < P ? keys[wid][64 + l] : 0ull;
+            const int nvalid = __popcll(__ballot(ka != 0ull)) + __popcll(__ballot(kb != 0ull));
+            bool sel_a = ka != 0ull, sel_b = kb != 0ull;
+            if (nvalid > sa.beam) {
+                const uint32_t ah = (uint32_t)(ka >> 32), bh = (uint32_t)(kb >> 32);
+                const uint32_t al = (uint32_t)ka, bl = (uint32_t)kb;
+                uint32_t xh = 0;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t c = xh | (1u << bit);
+                    if (__popcll(__ballot(ah >= c)) + __popcll(__ballot(bh >= c)) >= sa.beam) xh = c;
+                }
+                const int need = sa.beam - (__popcll(__ballot(ah > xh)) + __popcll(__ballot(bh > xh)));
+                const bool ea = ah == xh, eb = bh == xh;
+                uint32_t yl = 0;
+                if (__popcll(__ballot(ea)) + __popcll(__ballot(eb)) > need) {
+                    for (int bit = 31; bit >= 0; --bit) {
+                        const uint32_t c = yl | (1u << bit);
+                        if (__popcll(__ballot(ea && al >= c)) + __popcll(__ballot(eb && bl >= c)) >= need) yl = c;
+                    }
+                }
+                sel_a = ah > xh || (ea && al >= yl);
+                sel_b = bh > xh || (eb && bl >= yl);
+            }
+            const uint64_t ba = __ballot(sel_a), bb = __ballot(sel_b);
+            const uint64_t lt = (1ull << l) - 1ull;
+            const int pa = __popcll(ba & lt), pb = __popcll(ba) + __popcll(bb & lt);
+            nf = __popcll(ba) + __popcll(bb);   // min(valid candidates, beam)
+            if (lev > 0) {
+                if (sel_a) front[wid][pa] = rank_key_id(ka);
+                if (sel_b) front[wid][pb] = rank_key_id(kb);
+            } else {   // leaves: the nf <= 64 selected keys, sorted descending, for the walk
+                wave_sync();
+                if (sel_a) keys[wid][pa] = ka;
+                if (sel_b) keys[wid][pb] = kb;
+                wave_sync();
+                uint64_t v[1] = {l < nf ? keys[wid][l] : 0ull};
+                reg_sort_desc<1>(v);
+                keys[wid][l] = v[0];
+            }
+        }
         wave_sync();
     }
     const int got = wave_walk_expand(keys[wid], nf, sel[wid], tk[wid], ent[wid], cv, bg, q, sa.k, out);

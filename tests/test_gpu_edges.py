@@ -165,3 +165,37 @@ def test_exact_ties_follow_lowest_id():
             gaps = np.abs(s - sb)
             gaps = gaps[gaps > 0]
             assert gaps.min() < MARGIN, (strategy, t)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tree_exact_ties_follow_lowest_id(dtype):
+    # blocks 2..5 repeat blocks 0..1 exactly, so whole subtrees have bit-identical
+    # centroids and the beam cut meets many exact ties at every level: the
+    # lowest node index must win, as in the oracle
+    kw = dict(T=12288) if dtype == "f32" else dict(T=12288, d=128, H_kv=1, H_q=4, n_topics=16, k=512, window=256)
+    cfg = _cfg(**kw) if dtype == "f32" else get_config(2, **kw)
+    inp = layer_inputs(cfg, seed=30)
+    K = inp["K"]
+    K[:, :, 4096:8192] = K[:, :, 0:4096]
+    K[:, :, 8192:12288] = K[:, :, 0:4096]
+    G = {kk: inp[kk].to(DEV).contiguous() for kk in ("K", "W", "Q", "q_pos")}
+    cache = lsa.build_buckets(G["K"], G["W"], n_q_heads=cfg.H_q, build_tree=True)
+    W = inp["W"].double().numpy()
+    oc = O.build_head_cache(K[0, 0].double().numpy(), W, cfg.dtype, tree=True)
+    for beam in (64, 5):
+        lr, cnt = lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window, search="tree",
+                             beam=beam)
+        torch.cuda.synchronize()
+        lr, cnt = lr.cpu().numpy(), cnt.cpu().numpy()
+        exact = 0
+        for t in range(8192, cfg.T, 5):
+            qh = O.query_latent(inp["Q"][0, t, : cfg.G].double().numpy(), W, cfg.dtype)
+            ref, info = O.select_tree(qh, oc, t, cfg.k, cfg.n_sinks, cfg.window, beam, with_margin=True)
+            row = lr_row(lr[0, t, 0], cnt[0, t, 0])
+            if np.array_equal(ref, row):
+                exact += 1
+                continue
+            # an exact tie (gap 0) must be broken as the oracle does: only a genuine near tie excuses
+            near = [abs(c) for c in info["cuts"] if c != 0.0]
+            assert near and min(near) < MARGIN, (dtype, beam, t, info["cuts"])
+        assert exact >= 0.9 * len(range(8192, cfg.T, 5)), (dtype, beam, exact)
