@@ -397,6 +397,65 @@ def decode_on_cache(cfg, G, inp, cache_buf, tree):
                 beam=cfg.beam, mean_lr=float(cnt.float().mean()))
 
 
+def run_crossover(args):
+    """Flat vs tree decode on one shared cache as the context grows (the
+    pages' claim: the tree pays off only for long contexts with many
+    concurrent decodes).  For each T, one sequence of the 10M-layer recipe
+    (16,384 topics, 8 / 40 heads, d = 128, k = 2048, beam 64) is bucketed
+    with its tree; for each batch B, B decode queries at position T (query
+    recipe of the prefill) run one step — K/V append, select, attend — as a
+    HIP-graph replay, with flat search (every visible bucket scored) and with
+    tree search.  Prints one JSON line per (T, B, search)."""
+    from synth.topics import make_queries
+    dev = torch.device("cuda:0")
+    out = []
+    for T in args.cross_T:
+        cfg = get_config(5, T=T)
+        log(f"crossover: generating T={T}")
+        inp = layer_inputs(cfg, seed=0, device=dev, T_cap=T + 1, queries=False)
+        g = torch.Generator(device=dev)
+        g.manual_seed(12345)
+        kn = torch.randn(cfg.B, cfg.H_kv, cfg.d, generator=g, device=dev)
+        inp["K"][:, :, T] = (kn / kn.norm(dim=-1, keepdim=True)).to(inp["K"].dtype)
+        inp["V"][:, :, T] = torch.randn(cfg.B, cfg.H_kv, cfg.d, generator=g, device=dev).to(inp["V"].dtype)
+        G = {k: inp[k] for k in ("K", "V", "W")}
+        cache = lsa.build_buckets(G["K"], G["W"], T=T, n_q_heads=cfg.H_q, build_tree=True)
+        newK = G["K"][:, :, T].clone()
+        newV = G["V"][:, :, T].clone()
+        rows = kv_rows(G["K"], T)
+        for B in args.cross_B:
+            qp = torch.full((1, B), T, dtype=torch.int64)
+            Q = make_queries(cfg, 7, inp["mu"], inp["topic"], qp, dev).contiguous()
+            qp = qp.to(dev)
+            lr = torch.empty(1, B, cfg.H_kv, cfg.k, dtype=torch.int32, device=dev)
+            cnt = torch.empty(1, B, cfg.H_kv, dtype=torch.int32, device=dev)
+            O = torch.empty_like(Q)
+            wat = torch.empty(max(1, lsa.attend_workspace_bytes(Q, cfg.H_kv, cfg.k, cfg.window)), dtype=torch.uint8,
+                              device=dev)
+            for search in ("flat", "tree"):
+                scfg = lsa.select_cfg(cfg.k, cfg.n_sinks, cfg.window, search, cfg.beam)
+                wsel = torch.empty(lsa.select_workspace_bytes(cache, scfg, B, cfg.H_q), dtype=torch.uint8, device=dev)
+
+                def step():
+                    append_kv(G, rows, newK, newV)
+                    lsa.select(Q, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window, search=search, beam=cfg.beam,
+                               out=(lr, cnt), workspace=wsel)
+                    lsa.sparse_attend(Q, G["K"], G["V"], qp, lr, cnt, T, cfg.k, cfg.n_sinks, cfg.window, O=O,
+                                      workspace=wat)
+
+                for _ in range(3):
+                    step()
+                torch.cuda.synchronize()
+                ms = graph_replay_ms(step, (lr, cnt, O), 20)
+                rec = dict(study="decode crossover", T=T, batch=B, search=search, beam=cfg.beam if search == "tree" else 0,
+                           ms_per_step=ms, queries_per_s=B / (ms / 1e3), mean_lr=float(cnt.float().mean()))
+                out.append(rec)
+                print(json.dumps(rec), flush=True)
+        del inp, G, cache, newK, newV
+        torch.cuda.empty_cache()
+    return out
+
+
 def graph_replay_ms(step, outs, n):
     """Capture one decode step into a HIP graph, check that replays reproduce
     the eager step's outputs exactly (with eager work and synchronisations in
@@ -486,6 +545,10 @@ def main():
                          "or auto (bucket-major when a bucket is expected in >= 2 pairs per pass)")
     ap.add_argument("--bm-pass", type=int, default=32768,
                     help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
+    ap.add_argument("--study", choices=["crossover"], default=None,
+                    help="instead of the benchmark: the flat vs tree decode crossover over --cross-T x --cross-B")
+    ap.add_argument("--cross-T", type=int, nargs="+", default=[1 << 20, 1 << 21, 1 << 22, 1 << 23, 10485760])
+    ap.add_argument("--cross-B", type=int, nargs="+", default=[1, 4, 16, 64])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -498,6 +561,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.study == "crossover":
+        run_crossover(args)
+        return
     if args.calibrate:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
