@@ -17,6 +17,8 @@ Sources (the pages' titles and sections):
         max over heads.
   * diosapp.com.cn LSA tutorial, section 二, pseudocode: the query is projected
     by the same map and the output is softmax(q K[keys]^T / sqrt(d)) V[keys].
+  * zhichai.net explainer, ch.5 (the training-free D-LSA variant): the
+    projection is taken as the leading 64 principal directions of the keys.
 
 Readings taken where the pages are silent (each one is listed in the design doc):
   a block is 512 pooled entries = 2048 tokens; pooling is the plain mean of
@@ -46,7 +48,7 @@ __all__ = [
     "POOL", "BLOCK_ENTRIES", "BLOCK_TOKENS", "MEAN_BUCKET", "MAX_BUCKET", "LEAVES_PER_BLOCK",
     "round_to", "normalise", "key_latents", "pooled_entries", "ward_block", "ward_blocks",
     "build_head_cache", "build_tree", "query_latent", "query_geometry", "leaf_tokens",
-    "eligible_tokens", "select_flat", "select_tree", "attend", "attend_set",
+    "eligible_tokens", "select_flat", "select_tree", "attend", "attend_set", "pca_projection",
 ]
 
 POOL = 4
@@ -414,3 +416,27 @@ def attend(q: np.ndarray, Kg: np.ndarray, Vg: np.ndarray, t: int, lr: np.ndarray
     nvis, sink_end, l0 = query_geometry(t, n_blocks, n_sinks, window)
     S = np.union1d(np.union1d(np.arange(sink_end), np.arange(l0, t + 1)), np.asarray(lr, np.int64))
     return attend_set(q, Kg, Vg, S.astype(np.int64), scale)
+
+
+# --------------------------------------------------------------------------
+# training-free projection (ch.5): principal directions of the keys
+# --------------------------------------------------------------------------
+
+def pca_projection(keys: np.ndarray, n_dir: int = 64):
+    """Leading n_dir principal directions of a set of key rows (ch.5).
+
+    keys: [N, d] (every key of every head and sequence of the layer).  The
+    covariance is C = (1/N) sum (k - mean)(k - mean)^T in float64; its
+    eigenvectors sorted by eigenvalue descending give W = [v_1 .. v_n_dir]
+    ([d, n_dir], orthonormal columns).  Returns (W, all eigenvalues
+    descending).  Only the spanned subspace is defined (signs, and rotations
+    inside repeated eigenvalues, are arbitrary); the LSA path depends on W
+    only through that subspace, since every latent is normalised.
+    """
+    X = np.asarray(keys, np.float64)
+    mu = X.mean(axis=0)
+    C = (X - mu).T @ (X - mu) / X.shape[0]
+    lam, vec = np.linalg.eigh(C)
+    order = np.argsort(-lam, kind="stable")
+    return vec[:, order[:n_dir]], lam[order]
+

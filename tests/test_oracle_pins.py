@@ -354,3 +354,49 @@ def test_needle_is_retrieved():
             qh = O.query_latent(inp["Q"][b, 0, g * cfg.G:(g + 1) * cfg.G].double().numpy(), W, "bf16")
             lr, info = O.select_flat(qh, cache, cfg.T, cfg.k, cfg.n_sinks, cfg.window)
             assert set(range(p, p + 4)) <= set(lr.tolist()), (b, g, p)
+
+
+# ---------------------------------------------------------------- training-free projection (PCA)
+
+def _hadamard(n):
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def test_pca_closed_form_axes():
+    """Keys whose covariance is exactly diagonal (orthogonal zero-mean Hadamard columns scaled by
+    distinct sigmas): the principal directions are the axes of the largest sigmas, in that order."""
+    H = _hadamard(16)[:, 1:9]                 # 16 x 8, zero-mean, orthogonal columns
+    sig = np.array([0.3, 2.0, 0.7, 1.5, 0.1, 1.1, 0.5, 0.9])
+    X = H * sig + 0.25                         # a constant shift must not matter
+    W, lam = O.pca_projection(X, n_dir=3)
+    axes = np.argsort(-sig)[:3]                # 1, 3, 5
+    for j, ax in enumerate(axes):
+        e = np.zeros(8)
+        e[ax] = 1.0
+        assert abs(abs(W[:, j] @ e) - 1.0) < 1e-12
+    assert np.allclose(lam, np.sort(sig ** 2)[::-1], atol=1e-12)
+
+
+def test_pca_rotation_equivariant_and_orthonormal():
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((4000, 12)) * np.linspace(3.0, 0.2, 12)
+    R, _ = np.linalg.qr(rng.standard_normal((12, 12)))
+    W, _ = O.pca_projection(X, n_dir=5)
+    W2, _ = O.pca_projection(X @ R, n_dir=5)
+    assert np.allclose(W.T @ W, np.eye(5), atol=1e-12)
+    assert np.allclose(W2 @ W2.T, R.T @ (W @ W.T) @ R, atol=1e-8)
+
+
+def test_pca_captures_the_most_variance():
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((3000, 10)) @ rng.standard_normal((10, 10))
+    W, lam = O.pca_projection(X, n_dir=4)
+    C = np.cov(X.T, bias=True)
+    best = np.trace(W.T @ C @ W)
+    assert abs(best - lam[:4].sum()) < 1e-9 * lam[0]
+    for _ in range(20):
+        Qr, _ = np.linalg.qr(rng.standard_normal((10, 4)))
+        assert np.trace(Qr.T @ C @ Qr) <= best + 1e-9
