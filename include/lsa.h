@@ -248,6 +248,24 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
                                           float scale, void* O, void* workspace, size_t workspace_bytes,
                                           void* stream);
 
+/* Workspace bytes lsa_pca_projection needs for this layout's head_dim.  Host only. */
+lsa_status lsa_pca_workspace_bytes(const lsa_layout* layout, size_t* bytes);
+
+/* Training-free projection (zhichai.net "卡片柜" ch.5: the D-LSA variant
+ * that needs no training takes the leading principal directions of the
+ * keys).  Over every key K[b, g, t, :] with b < batch, g < H_kv, t < T
+ * (N = batch * H_kv * T rows): C = (1/N) sum (k - mean)(k - mean)^T,
+ * eigen-decomposed; W [d, 64] (row-major, layout->dtype, rounded to nearest
+ * even in bf16) receives the eigenvectors of the 64 largest eigenvalues as
+ * columns, in descending order, each with its largest-magnitude component
+ * positive.  eigvals (optional, fp32 [d]) receives all eigenvalues,
+ * descending.  W serves as both W_k and W_q; the rest of the path depends on
+ * it only through the spanned subspace (every latent is normalised).
+ * Accumulation in fp32 per workgroup and fp64 across workgroups; the
+ * eigen-solver is a cyclic Jacobi in fp32. */
+lsa_status lsa_pca_projection(const lsa_layout* layout, const void* K, int64_t batch, int64_t t_cap, int64_t T,
+                              void* W, float* eigvals, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable status name; detail of the last failed call on this thread. */
 const char* lsa_status_string(lsa_status status);
 const char* lsa_last_error(void);

@@ -26,7 +26,7 @@ from ._lib import (LsaError, Layout, SelectCfg, CacheInfo, LSA_BF16, LSA_F32, LS
 
 __all__ = ["build_buckets", "select", "sparse_attend", "sparse_attend_bucket_major", "LsaCache", "LsaError",
            "make_layout", "select_cfg", "library_path", "select_workspace_bytes", "attend_workspace_bytes",
-           "attend_bucket_major_workspace_bytes"]
+           "attend_bucket_major_workspace_bytes", "pca_projection"]
 
 _STRATEGIES = {"auto": LSA_STRATEGY_AUTO, "fused": LSA_STRATEGY_FUSED, "materialized": LSA_STRATEGY_MATERIALIZED}
 
@@ -259,3 +259,22 @@ def sparse_attend_bucket_major(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
         _ptr(V), t_cap, cache.T, _ptr(q_pos), B, n_q, _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt),
         ctypes.c_float(scale), _ptr(O), _ptr(workspace), workspace.numel(), _stream(Q.device)))
     return O
+
+
+def pca_projection(K: torch.Tensor, T: Optional[int] = None, with_eigvals: bool = False):
+    """Training-free projection: W [d, 64] = the 64 leading principal directions of the keys
+    K [B, H_kv, t_cap, d] (first T positions), in K's dtype; optionally also all eigenvalues (fp32)."""
+    assert K.is_cuda and K.is_contiguous()
+    B, H_kv, t_cap, d = K.shape
+    T = t_cap if T is None else T
+    layout = make_layout(d, H_kv, H_kv, K.dtype)
+    L = _lib.lib()
+    n = ctypes.c_size_t()
+    _lib.check(L.lsa_pca_workspace_bytes(ctypes.byref(layout), ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=K.device)
+    W = torch.empty(d, _lib.LATENT_DIM, dtype=K.dtype, device=K.device)
+    ev = torch.empty(d, dtype=torch.float32, device=K.device) if with_eigvals else None
+    _lib.check(L.lsa_pca_projection(ctypes.byref(layout), _ptr(K), B, t_cap, T, _ptr(W), _ptr(ev), _ptr(ws),
+                                    ws.numel(), _stream(K.device)))
+    return (W, ev) if with_eigvals else W
+

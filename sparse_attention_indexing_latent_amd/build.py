@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblsa.so")
-SOURCES = ["lsa_api.cpp", "lsa_build.hip", "lsa_select.hip", "lsa_attend.hip", "lsa_bucket.hip"]
+SOURCES = ["lsa_api.cpp", "lsa_build.hip", "lsa_select.hip", "lsa_attend.hip", "lsa_bucket.hip", "lsa_pca.hip"]
 ARCH = os.environ.get("LSA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU forms are kept out of the generated code

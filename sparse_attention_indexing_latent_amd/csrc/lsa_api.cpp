@@ -607,4 +607,29 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
     return ok();
 }
 
+lsa_status lsa_pca_workspace_bytes(const lsa_layout* layout, size_t* bytes) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (!bytes) return fail(LSA_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = lsa::pca_workspace_bytes(layout->head_dim);
+    return ok();
+}
+
+lsa_status lsa_pca_projection(const lsa_layout* layout, const void* K, int64_t batch, int64_t t_cap, int64_t T,
+                              void* W, float* eigvals, void* workspace, size_t workspace_bytes, void* stream) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (batch < 1 || T < 1 || t_cap < T) return fail(LSA_ERR_INVALID_ARG, "need batch >= 1 and 1 <= T <= t_cap");
+    if (!K || !W || !workspace) return fail(LSA_ERR_INVALID_ARG, "K, W and workspace must be non-NULL");
+    if (misaligned(K) || misaligned(W) || misaligned(workspace) || (eigvals && misaligned(eigvals)))
+        return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const size_t need = lsa::pca_workspace_bytes(layout->head_dim);
+    if (workspace_bytes < need) return fail(LSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    hipError_t e = lsa::launch_pca(K, layout->dtype == LSA_BF16, layout->head_dim, t_cap, T,
+                                   (int)(batch * layout->n_kv_heads), W, eigvals, workspace,
+                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

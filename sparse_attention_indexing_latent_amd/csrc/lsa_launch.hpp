@@ -98,6 +98,9 @@ int attend_splits(int64_t n_units, int window, int k);
 hipError_t launch_attend(const void* Q, const void* K, const void* V, const int64_t* q_pos, const int32_t* lr_idx,
                          const int32_t* lr_cnt, const AttArgs& aa, int D, bool bf16, void* O, float* part,
                          hipStream_t st);
+size_t pca_workspace_bytes(int D);
+hipError_t launch_pca(const void* K, bool bf16, int D, int64_t t_cap, int64_t T, int BH, void* W, float* eig,
+                      void* workspace, hipStream_t st);
 hipError_t launch_attend_local(const void* Q, const void* K, const void* V, const int64_t* q_pos,
                                const int32_t* lr_idx, const int32_t* lr_cnt, const AttArgs& aa, int D, void* O,
                                hipStream_t st);
