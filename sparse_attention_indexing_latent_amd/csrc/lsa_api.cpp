@@ -248,7 +248,7 @@ void select_ws(const lsa_layout* L, const lsa_select_cfg* C, int64_t B, int64_t 
     w.off_tau = o;      o = align256(o + (size_t)units * 4);
     w.off_cnt = o;      o = align256(o + (size_t)units * 4);
     if (w.strategy == LSA_STRATEGY_FUSED) {
-        w.off_cand = o; o = align256(o + (size_t)units * lsa::kCandCap * 8);
+        w.off_cand = o; o = align256(o + (size_t)units * lsa::kCandStride * 8);
         w.off_fb = o;   o = align256(o + (size_t)units * 4);
         w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
         w.off_scores = o; o = align256(o + (size_t)w.fb_slots * w.score_stride * 4);

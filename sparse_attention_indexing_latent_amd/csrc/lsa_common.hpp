@@ -16,7 +16,8 @@ constexpr int kLeavesPerBlock = LSA_LEAVES_PER_BLOCK;
 constexpr int kMaxBucket = LSA_MAX_BUCKET;
 constexpr int kMaxGroup = LSA_MAX_GROUP;
 constexpr int kMaxLevels = 40;
-constexpr int kCandCap = 512;      // candidates per (query, KV head) in the fused flat search
+constexpr int kCandCap = 512;      // candidates per (query, KV head) the fused flat search sorts
+constexpr int kCandStride = 1024;  // candidate list slots per (query, KV head) in the fused flat search
 constexpr int kFullTake = 0xFFFF;  // "every eligible token of this bucket"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

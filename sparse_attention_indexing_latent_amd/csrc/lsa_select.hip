@@ -11,14 +11,15 @@
 // Exact selection rule: buckets ranked by (score desc, id asc) are taken
 // whole until k eligible tokens, the last giving its lowest-index eligible
 // tokens.  Three ways to reach it:
-//   fused (many queries): a 64-query x bucket-tile bf16 MFMA scan per KV
-//     head.  Pass 1 keeps, per query and cluster block, the best bucket and
-//     its size and builds a 256-bin histogram of those block maxima weighted
-//     by bucket tokens; the bin where the weight reaches k gives a bound tau
-//     that the true boundary score cannot undercut.  Pass 2 rescans and keeps
-//     every bucket scoring >= tau as a candidate (<= 512).  A per-query wave
-//     then sorts the candidates, walks them and expands.  A query with more
-//     candidates falls back to the exact path below.
+//   fused (many queries): an MFMA scan of the centroids per KV head, 128
+//     queries x 16-bucket tiles (bf16; fp32 in two passes of 64 queries).
+//     Each query keeps a histogram of eligible token weight over score bins
+//     and a floor: the bin where that weight, summed from the top, reaches
+//     k.  Buckets at or above the floor are appended to the query's
+//     candidate list and binned; the final crossing bin gives a bound tau
+//     that the true boundary score cannot undercut.  A per-query wave then
+//     keeps the candidates scoring >= tau (<= 512), sorts, walks and expands
+//     them.  A query with more falls back to the exact path below.
 //   materialised (few queries, e.g. decode): all scores are written out,
 //     then one workgroup per query finds the boundary key with a weighted
 //     4 x 8-bit radix select and collects the selected buckets in id order.
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
                     const bool pred = (!edge || (xb + v < NLv)) && qv && vals[v] >= tau_n;
                     if (pred) {
                         const int pos = atomicAdd(&lcnt[wid][n], 1);
-                        if (pos < kCandCap) cand[u * kCandCap + pos] = rank_key(vals[v], (uint32_t)(xb + v));
+                        if (pos < kCandStride) cand[u * kCandStride + pos] = rank_key(vals[v], (uint32_t)(xb + v));
                     }
                 }
             }
@@ -392,46 +393,102 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
     }
 }
 
-// ------------------------------------------------------------------ candidate pass, LDS-staged (bf16)
-// Pass 1 of the fused flat scan with the centroid tiles shared through LDS:
-// a workgroup owns 128 queries of one KV head (32 per wave, as two 16-query
-// MFMA column groups), streams the visible tiles in chunks of 8 (16 KB,
-// double-buffered; each thread copies 64 B of a chunk, a ring one chunk
-// ahead) and every wave reads the operand fragments from LDS.  A fragment
-// read feeds 2 x G x 2 MFMAs, and the L2 traffic is a quarter of per-wave
-// loads.  Output as pass 1: every visible bucket scoring >= tau of its query
-// is appended (rank key) to the query's candidate list (capped at kCandCap,
-// the count is exact).
+// ------------------------------------------------------------------ single-pass scan, LDS-staged (bf16)
+// The fused flat search's scan in one pass over the centroids, tiles shared
+// through LDS: a workgroup owns 128 queries of one KV head (32 per wave, as
+// two 16-query MFMA column groups), streams the visible tiles in chunks of 8
+// (16 KB) with their buckets' meta words, double-buffered, and every wave
+// reads its operand fragments from LDS (one fragment read feeds 2 x G x 2
+// MFMAs).
+//
+// Each query keeps a histogram of certainly eligible token weight (4 x size
+// for buckets of blocks inside [sink_end, l0)) over score bins (8 of width
+// 1/8 below 0, 64 of width 1/64 over [0, 1), the end bins open) and a floor
+// bin fb: the highest bin at which the weight binned so far, summed from the
+// top, reaches k (raised after every chunk).  A visible bucket in a bin >= fb
+// is appended (rank key) to the query's candidate list and its weight binned;
+// one below fb is skipped: fb only rises, so bins below it can never become
+// the final crossing bin b*, and every bin >= b* holds all of its weight.
+// Hence at the end tau = lower edge of b* (minus 2^-16; -inf if the weight
+// never reaches k) is the bound of the two-pass scan, and the list holds
+// every visible bucket scoring >= tau (plus earlier ones below it, dropped
+// by the finalize).  The list is capped at kCandStride, its count exact.
 constexpr int kScanQ = 128;         // queries per workgroup
 constexpr int kScanChunk = 8;       // tiles per staged chunk
+constexpr int kFNeg = 8;
+constexpr int kFBins = kFNeg + 64;
+constexpr int kFStride = kFBins + 1;   // odd: neighbouring queries fall in different banks
+
+// multiplications by powers of two are exact, so bin(s) >= b  <=>  s >= edge(b)
+__device__ __forceinline__ int fscan_bin(float s) {
+    const int bp = min(kFNeg + (int)(s * 64.0f), kFBins - 1);
+    const int bn = max(kFNeg + (int)floorf(s * 8.0f), 0);
+    return s >= 0.f ? bp : bn;
+}
+
+__device__ __forceinline__ float fscan_edge(int bin) {
+    return bin >= kFNeg ? (float)(bin - kFNeg) * (1.0f / 64.0f) : (float)(bin - kFNeg) * (1.0f / 8.0f);
+}
+
+// The highest bin at which one query's histogram, summed from the top,
+// reaches k (-1 if it never does).  The query's 4 lanes (h = 0..3, the same
+// n) each take a quarter of the bins into registers, the top quarter on
+// h = 0; the lane whose quarter holds the crossing walks it down.  All 64
+// lanes call it (it shuffles across the wave); the result is on all 4.
+__device__ __forceinline__ int fscan_cross_bin(const uint32_t* row, int h, uint32_t k) {
+    constexpr int Q4 = kFBins / 4;
+    const int lo = kFBins - Q4 * (h + 1);   // this lane's bins: [lo, lo + Q4)
+    uint32_t w[Q4];
+    uint32_t sq = 0;
+#pragma unroll
+    for (int j = 0; j < Q4; ++j) w[j] = row[lo + j];
+#pragma unroll
+    for (int j = 0; j < Q4; ++j) sq += w[j];
+    const int n = lane_id() & 15;
+    const uint32_t s0 = (uint32_t)__shfl((int)sq, n), s1 = (uint32_t)__shfl((int)sq, n + 16),
+                   s2 = (uint32_t)__shfl((int)sq, n + 32);
+    uint32_t cum = (h > 0 ? s0 : 0u) + (h > 1 ? s1 : 0u) + (h > 2 ? s2 : 0u);
+    int bin = -1;
+    if (cum < k) {
+#pragma unroll
+        for (int j = Q4 - 1; j >= 0; --j) {
+            cum += w[j];
+            bin = (bin < 0 && cum >= k) ? lo + j : bin;
+        }
+    }
+    bin = max(bin, __shfl_xor(bin, 16));
+    bin = max(bin, __shfl_xor(bin, 32));
+    return bin;
+}
 
 template <int G>
-__global__ __launch_bounds__(256) void scan_collect_kernel(CacheView cv, const uint16_t* __restrict__ qhat,
-                                                           const int64_t* __restrict__ q_pos, SelArgs sa,
-                                                           const float* __restrict__ tau, int* __restrict__ cnt,
-                                                           uint64_t* __restrict__ cand) {
+__global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uint16_t* __restrict__ qhat,
+                                                         const int64_t* __restrict__ q_pos, SelArgs sa,
+                                                         float* __restrict__ tau, int* __restrict__ cnt,
+                                                         uint64_t* __restrict__ cand) {
     __shared__ __align__(16) uint4 stage[2][kScanChunk * 128];   // 2 x 16 KB
-    __shared__ int lcnt[4][2][16];
+    __shared__ __align__(16) uint4 smeta[2][kScanChunk * 4];     // 16 meta words per tile
+    __shared__ uint32_t hist[kScanQ * kFStride];
     __shared__ int wmax[4];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
     const int64_t b = blockIdx.z, g = blockIdx.y;
     const int64_t bg = b * sa.H_kv + g;
     // per column group cg: this lane's query (column n)
-    int64_t iq[2], u[2];
+    int64_t u[2], lo_ok[2], hi_ok[2];
     int NLv[2];
     bool qv[2];
-    float tq[2];
     bf16x8 qf[2][G][2];
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg) {
-        iq[cg] = (int64_t)blockIdx.x * kScanQ + wid * 32 + cg * 16 + n;
-        qv[cg] = iq[cg] < sa.n_q;
-        const int64_t t = qv[cg] ? q_pos[b * sa.n_q + iq[cg]] : -1;
+        const int64_t iq = (int64_t)blockIdx.x * kScanQ + wid * 32 + cg * 16 + n;
+        qv[cg] = iq < sa.n_q;
+        const int64_t t = qv[cg] ? q_pos[b * sa.n_q + iq] : -1;
         const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
         NLv[cg] = t < 0 ? 0 : kLeavesPerBlock * q.nvis;
-        u[cg] = (b * sa.n_q + iq[cg]) * sa.H_kv + g;
-        tq[cg] = qv[cg] ? tau[u[cg]] : 0.f;
-        const int64_t qrow = ((b * sa.n_q + (qv[cg] ? iq[cg] : 0)) * sa.H_q + g * sa.G) * kLatent;
+        lo_ok[cg] = q.sink_end;
+        hi_ok[cg] = q.l0;
+        u[cg] = (b * sa.n_q + (qv[cg] ? iq : 0)) * sa.H_kv + g;
+        const int64_t qrow = ((b * sa.n_q + (qv[cg] ? iq : 0)) * sa.H_q + g * sa.G) * kLatent;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
             uint4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
@@ -444,7 +501,8 @@ __global__ __launch_bounds__(256) void scan_collect_kernel(CacheView cv, const u
             qf[cg][hh][1] = as_bf16x8(c);
         }
     }
-    if (l < 32) lcnt[wid][l >> 4][l & 15] = 0;
+    uint32_t* hrow[2] = {hist + (wid * 32 + n) * kFStride, hist + (wid * 32 + 16 + n) * kFStride};
+    for (int j = tid; j < kScanQ * kFStride; j += 256) hist[j] = 0u;
     // tiles visible to any query of the workgroup
     const int wm = wave_max_i(max(NLv[0], NLv[1]));
     if (l == 0) wmax[wid] = wm;
@@ -452,24 +510,30 @@ __global__ __launch_bounds__(256) void scan_collect_kernel(CacheView cv, const u
     const int maxNLv = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
     const int ntl = maxNLv / 16;
     const int nch = (ntl + kScanChunk - 1) / kScanChunk;
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
-    // staging: thread tid copies words tid + 256 j (j < 4) of a chunk; words past the last tile repeat it
-    u32x4 r0, r1, r2, r3;
-#define LSA_LOAD_CHUNK(c)                                                                                    \
-    {                                                                                                        \
-        const u32x4* s4 = reinterpret_cast<const u32x4*>(src);                                               \
-        r0 = s4[(int64_t)min((c) * kScanChunk + (tid) / 128, ntl - 1) * 128 + (tid & 127)];                  \
-        r1 = s4[(int64_t)min((c) * kScanChunk + (tid + 256) / 128, ntl - 1) * 128 + (tid & 127)];            \
-        r2 = s4[(int64_t)min((c) * kScanChunk + (tid + 512) / 128, ntl - 1) * 128 + (tid & 127)];            \
-        r3 = s4[(int64_t)min((c) * kScanChunk + (tid + 768) / 128, ntl - 1) * 128 + (tid & 127)];            \
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
+    const u32x4* msrc = reinterpret_cast<const u32x4*>(cv.meta + bg * cv.s_meta);
+    int fb[2] = {0, 0};
+    float fe[2] = {kNegInf, kNegInf};
+    int base[2] = {0, 0};   // the query's list length (the same on its 4 lanes)
+    // staging: thread tid copies words tid + 256 j (j < 4) of a chunk and, if tid < 32, meta word tid;
+    // tiles past the last one repeat it
+    u32x4 r0, r1, r2, r3, rmt;
+#define LSA_LOAD_CHUNK(c)                                                                               \
+    {                                                                                                   \
+        r0 = src[(int64_t)min((c) * kScanChunk + (tid) / 128, ntl - 1) * 128 + (tid & 127)];            \
+        r1 = src[(int64_t)min((c) * kScanChunk + (tid + 256) / 128, ntl - 1) * 128 + (tid & 127)];      \
+        r2 = src[(int64_t)min((c) * kScanChunk + (tid + 512) / 128, ntl - 1) * 128 + (tid & 127)];      \
+        r3 = src[(int64_t)min((c) * kScanChunk + (tid + 768) / 128, ntl - 1) * 128 + (tid & 127)];      \
+        if (tid < kScanChunk * 4) rmt = msrc[(int64_t)min((c) * kScanChunk + tid / 4, ntl - 1) * 4 + (tid & 3)]; \
     }
-#define LSA_STORE_CHUNK(bf)                                                                                  \
-    {                                                                                                        \
-        u32x4* d4 = reinterpret_cast<u32x4*>(stage[bf]);                                                     \
-        d4[tid] = r0;                                                                                        \
-        d4[tid + 256] = r1;                                                                                  \
-        d4[tid + 512] = r2;                                                                                  \
-        d4[tid + 768] = r3;                                                                                  \
+#define LSA_STORE_CHUNK(bf)                                                                             \
+    {                                                                                                   \
+        u32x4* d4 = reinterpret_cast<u32x4*>(stage[bf]);                                                \
+        d4[tid] = r0;                                                                                   \
+        d4[tid + 256] = r1;                                                                             \
+        d4[tid + 512] = r2;                                                                             \
+        d4[tid + 768] = r3;                                                                             \
+        if (tid < kScanChunk * 4) reinterpret_cast<u32x4*>(smeta[bf])[tid] = rmt;                       \
     }
     if (nch > 0) {
         LSA_LOAD_CHUNK(0)
@@ -479,52 +543,90 @@ __global__ __launch_bounds__(256) void scan_collect_kernel(CacheView cv, const u
     for (int c = 0; c < nch; ++c) {
         if (c + 1 < nch) LSA_LOAD_CHUNK(c + 1)
         const uint4* sb = stage[c & 1];
+        const uint4* sm = smeta[c & 1];
         const int tend = min(kScanChunk, ntl - c * kScanChunk);
+        bf16x8 a0 = as_bf16x8(sb[l]), a1 = as_bf16x8(sb[64 + l]);
         for (int tt = 0; tt < tend; ++tt) {
             const int x0 = (c * kScanChunk + tt) * 16;
-            const bf16x8 a0 = as_bf16x8(sb[tt * 128 + l]), a1 = as_bf16x8(sb[tt * 128 + 64 + l]);
             const int xb = x0 + 4 * h;
+            f32x4 best[2];
 #pragma unroll
             for (int cg = 0; cg < 2; ++cg) {
-                f32x4 best;
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[cg][hh][0], acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[cg][hh][1], acc, 0, 0, 0);
                     if (hh == 0) {
-                        best = acc;
+                        best[cg] = acc;
                     } else {
-                        best[0] = fmaxf(best[0], acc[0]);
-                        best[1] = fmaxf(best[1], acc[1]);
-                        best[2] = fmaxf(best[2], acc[2]);
-                        best[3] = fmaxf(best[3], acc[3]);
+                        best[cg][0] = fmaxf(best[cg][0], acc[0]);
+                        best[cg][1] = fmaxf(best[cg][1], acc[1]);
+                        best[cg][2] = fmaxf(best[cg][2], acc[2]);
+                        best[cg][3] = fmaxf(best[cg][3], acc[3]);
                     }
                 }
-                // buckets of this lane's query at or above its bound (rare): one branch per group
-                const int lim = qv[cg] ? NLv[cg] - xb : 0;   // buckets xb + v with v < lim are visible
-                const uint32_t m = (best[0] >= tq[cg] && 0 < lim ? 1u : 0u) | (best[1] >= tq[cg] && 1 < lim ? 2u : 0u) |
-                                   (best[2] >= tq[cg] && 2 < lim ? 4u : 0u) | (best[3] >= tq[cg] && 3 < lim ? 8u : 0u);
-                if (m) {
+            }
+            // next tile's fragments (the last tile of a chunk re-reads itself)
+            const int tn = tt + 1 < tend ? tt + 1 : tt;
+            a0 = as_bf16x8(sb[tn * 128 + l]);
+            a1 = as_bf16x8(sb[tn * 128 + 64 + l]);
+            // visible buckets of each query scoring at or above its floor's edge (few once it has risen)
+            uint32_t m[2];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        if (m & (1u << v)) {
-                            const int pos = atomicAdd(&lcnt[wid][cg][n], 1);
-                            if (pos < kCandCap) cand[u[cg] * kCandCap + pos] = rank_key(best[v], (uint32_t)(xb + v));
+            for (int cg = 0; cg < 2; ++cg) {
+                const int lim = qv[cg] ? NLv[cg] - xb : 0;   // buckets xb + v with v < lim are visible
+                m[cg] = (best[cg][0] >= fe[cg] && 0 < lim ? 1u : 0u) | (best[cg][1] >= fe[cg] && 1 < lim ? 2u : 0u) |
+                        (best[cg][2] >= fe[cg] && 2 < lim ? 4u : 0u) | (best[cg][3] >= fe[cg] && 3 < lim ? 8u : 0u);
+            }
+            if (__ballot((m[0] | m[1]) != 0)) {
+                const int64_t lo = (int64_t)(x0 / kLeavesPerBlock) * kBlockTokens;
+                const uint4 m4 = sm[tt * 4 + h];
+                const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+                for (int cg = 0; cg < 2; ++cg) {
+                    // list positions: the query's 4 lanes append in h order after its current length
+                    const int cl = __popc(m[cg]);
+                    const int c0 = __shfl(cl, n), c1 = __shfl(cl, n + 16), c2 = __shfl(cl, n + 32),
+                              c3 = __shfl(cl, n + 48);
+                    int pos = base[cg] + (h > 0 ? c0 : 0) + (h > 1 ? c1 : 0) + (h > 2 ? c2 : 0);
+                    base[cg] += c0 + c1 + c2 + c3;
+                    if (m[cg]) {
+                        const bool elig = lo >= lo_ok[cg] && lo + kBlockTokens <= hi_ok[cg];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            if (m[cg] & (1u << v)) {
+                                if (pos < kCandStride)
+                                    cand[u[cg] * kCandStride + pos] = rank_key(best[cg][v], (uint32_t)(xb + v));
+                                ++pos;
+                                if (elig)
+                                    atomicAdd(&hrow[cg][fscan_bin(best[cg][v])], (uint32_t)kPool * (mm[v] & 0xFFu));
+                            }
                         }
                     }
                 }
             }
         }
         if (c + 1 < nch) LSA_STORE_CHUNK((c + 1) & 1)
+        // raise the floors (the histogram rows are this wave's own)
+        wave_sync();
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            fb[cg] = max(fb[cg], fscan_cross_bin(hrow[cg], h, (uint32_t)sa.k));
+            fe[cg] = fb[cg] >= 1 ? fscan_edge(fb[cg]) : kNegInf;   // bin(s) >= fb  <=>  s >= fe
+        }
         __syncthreads();
     }
 #undef LSA_LOAD_CHUNK
 #undef LSA_STORE_CHUNK
-    if (h == 0) {
+    wave_sync();
 #pragma unroll
-        for (int cg = 0; cg < 2; ++cg)
-            if (qv[cg]) cnt[u[cg]] = lcnt[wid][cg][n];
+    for (int cg = 0; cg < 2; ++cg) {
+        const int bin = fscan_cross_bin(hrow[cg], h, (uint32_t)sa.k);
+        if (h == 0 && qv[cg]) {
+            tau[u[cg]] = bin >= 1 ? fscan_edge(bin) - 1.52587890625e-05f : kNegInf;
+            cnt[u[cg]] = base[cg];
+        }
     }
 }
 
@@ -930,7 +1032,7 @@ __device__ __forceinline__ bool trivial_unit(int64_t t, const Geom& q, int k, in
 
 // ------------------------------------------------------------------ fused finalize
 __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const int64_t* __restrict__ q_pos, SelArgs sa,
-                                                             const int* __restrict__ cnt,
+                                                             const float* __restrict__ tau, const int* __restrict__ cnt,
                                                              const uint64_t* __restrict__ cand, int* fb_list,
                                                              int* counters, int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ __align__(16) uint64_t keys[4][kCandCap];
@@ -944,21 +1046,41 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
     const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
     int32_t* out = lr_idx + u * sa.k;
     if (trivial_unit(t, q, sa.k, out, lr_cnt + u)) return;
+    // the candidates scoring >= tau (the list may also hold buckets below it), compacted in list order
     const int c = cnt[u];
-    if (c > kCandCap) {
+    int f = 0;
+    if (c <= kCandStride) {
+        const uint64_t kmin = (uint64_t)ord_key(tau[u]) << 32;   // key >= kmin  <=>  score >= tau
+        const uint64_t lt = (1ull << l) - 1ull;
+        const uint64_t* cl = cand + u * kCandStride;
+        for (int j0 = 0; j0 < c; j0 += 256) {
+            uint64_t kk[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) kk[r] = j0 + 64 * r + l < c ? cl[j0 + 64 * r + l] : 0ull;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool keep = j0 + 64 * r + l < c && kk[r] >= kmin;
+                const uint64_t bal = __ballot(keep);
+                const int pos = f + __popcll(bal & lt);
+                if (keep && pos < kCandCap) keys[wid][pos] = kk[r];
+                f += __popcll(bal);
+            }
+        }
+    }
+    if (c > kCandStride || f > kCandCap) {
         if (l == 0) {
             const int pos = atomicAdd(&counters[0], 1);
             fb_list[pos] = (int)u;
         }
         return;
     }
-    const int P = pow2_at_least(c);
-    for (int j = l; j < P; j += 64) keys[wid][j] = j < c ? cand[u * kCandCap + j] : 0ull;
+    const int P = pow2_at_least(f);
+    for (int j = f + l; j < P; j += 64) keys[wid][j] = 0ull;
     wave_sync();
     wave_sort_desc(keys[wid], P);
     const int64_t bg = un.b * sa.H_kv + un.g;
     // the rank keys are dead once the walk is done: their space holds the entry keys (<= k / 4)
-    const int got = wave_walk_expand(keys[wid], c, sel[wid], tk[wid], reinterpret_cast<uint32_t*>(keys[wid]), cv, bg,
+    const int got = wave_walk_expand(keys[wid], f, sel[wid], tk[wid], reinterpret_cast<uint32_t*>(keys[wid]), cv, bg,
                                      q, sa.k, out);
     write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
@@ -1783,14 +1905,12 @@ hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_
                                const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, hipStream_t st) {
     dim3 grid((unsigned)((sa.n_q + 63) / 64), (unsigned)sa.H_kv, (unsigned)B);
     if (bf16) {
-        hipLaunchKernelGGL((fused_scan_kernel<true, 0>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, sb.tau, sb.cnt,
-                           sb.cand);
         const dim3 g2((unsigned)((sa.n_q + kScanQ - 1) / kScanQ), (unsigned)sa.H_kv, (unsigned)B);
         const uint16_t* qh = static_cast<const uint16_t*>(sb.qhat);
         switch (sa.G) {
-#define LSA_SCAN_G(GG)                                                                                              \
-    case GG:                                                                                                        \
-        hipLaunchKernelGGL(scan_collect_kernel<GG>, g2, dim3(256), 0, st, cv, qh, q_pos, sa, sb.tau, sb.cnt, sb.cand); \
+#define LSA_SCAN_G(GG)                                                                                           \
+    case GG:                                                                                                     \
+        hipLaunchKernelGGL(scan_fused_kernel<GG>, g2, dim3(256), 0, st, cv, qh, q_pos, sa, sb.tau, sb.cnt, sb.cand); \
         break;
             LSA_SCAN_G(1) LSA_SCAN_G(2) LSA_SCAN_G(3) LSA_SCAN_G(4) LSA_SCAN_G(5) LSA_SCAN_G(6) LSA_SCAN_G(7)
             LSA_SCAN_G(8)
@@ -1806,7 +1926,7 @@ hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fused_finalize_kernel, dim3((unsigned)((sa.n_units + 3) / 4)), dim3(256), 0, st, cv, q_pos, sa,
-                       sb.cnt, sb.cand, sb.fb_list, sb.counters, lr_idx, lr_cnt);
+                       sb.tau, sb.cnt, sb.cand, sb.fb_list, sb.counters, lr_idx, lr_cnt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (bf16)
