@@ -860,11 +860,27 @@ __device__ __forceinline__ int records_tokens(const uint64_t* sel, int a, int b)
 // lies inside [sink_end, l0) and every selected bucket of it is taken whole;
 // the other (special) blocks, at most the two straddling an edge and the one
 // holding the partially taken bucket, go through expand_block_scan.  The
-// member entries of all plain buckets are gathered as (block, entry) keys,
-// sorted once, and entry number p of that order lands at 4 p plus the
-// tokens of the special blocks before its block.
+// member entries of the plain buckets are listed as (block, entry) keys in
+// record order, so grouped by block, each bucket's members ascending (as the
+// build stores them).  An entry's place in (block, entry) order is then the
+// start of its block's group plus the number of smaller entries in that
+// group (its own index when the bucket is alone in the block), so the list
+// is put in order in place, without a sort; entry p of the order lands at
+// 4 p plus the tokens of the special blocks before its block.
 // LDS scratch: ent[] of at least k/4 keys, tk[] of 256 ints (tk[0..64) is
 // expand_block_scan's map, tk[64..) lists the special blocks).
+__device__ __forceinline__ int ent_block_start(const uint32_t* ent, int n, uint32_t blk) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((ent[mid] >> 9) < blk)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const CacheView& cv, int64_t bg,
                                            const Geom& q, int32_t* out, int* tk, uint32_t* ent) {
     const int l = lane_id();
@@ -930,13 +946,59 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
         }
     }
     wave_sync();
-    // plain entries ascending by (block, entry): sort the complements descending
-    const int P = pow2_at_least(nent);
-    for (int j = l; j < P; j += 64) ent[j] = j < nent ? ~ent[j] : 0u;
-    wave_sync();
-    wave_sort_desc_u32(ent, P);
+    // plain entries into (block, entry) order, in place: an entry's place is the start of its block's
+    // group plus the number of smaller entries in the group.  Records go in chunks of whole blocks
+    // (a block has at most 64 buckets), so a group is permuted only after all its reads.
+    int pbase = 0;
+    for (int c0 = 0; c0 < nsel;) {
+        const int i = c0 + l;
+        const bool starts = i < nsel && (i == 0 || sel_block(sel[i - 1]) != sel_block(sel[i]));
+        const uint64_t sb = __ballot(starts) & ~1ull;
+        const bool cut_ok = c0 + 64 >= nsel || sel_block(sel[c0 + 64]) != sel_block(sel[c0 + 63]);
+        const int width = (cut_ok || sb == 0ull) ? 64 : 63 - __builtin_clzll(sb);
+        const bool live = l < width && i < nsel;
+        c0 += width;
+        const uint64_t sv = live ? sel[i] : 0ull;
+        const int blk = (int)sel_block(sv);
+        const int64_t lo = (int64_t)blk * kBlockTokens;
+        const bool special = live && (!(lo >= q.sink_end && lo + kBlockTokens <= q.l0) || blk == part_blk);
+        const int sz = (live && !special) ? sel_size(sv) : 0;
+        const int incl = wave_incl_scan(sz);
+        const int pos = pbase + incl - sz;
+        pbase += __shfl(incl, 63);
+        uint32_t e[16];
+        int rank[16];
+        int ga = 0;
+        if (sz > 0) {
+            ga = ent_block_start(ent, nent, (uint32_t)blk);
+            const int gz = ent_block_start(ent, nent, (uint32_t)blk + 1u);
+#pragma unroll
+            for (int jm = 0; jm < 16; ++jm) {
+                e[jm] = jm < sz ? ent[pos + jm] : 0u;
+                rank[jm] = 0;
+            }
+            if (gz - ga == sz) {
+#pragma unroll
+                for (int jm = 0; jm < 16; ++jm) rank[jm] = jm;   // alone in its block: already ascending
+            } else {
+                for (int qq = ga; qq < gz; ++qq) {
+                    const uint32_t v = ent[qq];
+#pragma unroll
+                    for (int jm = 0; jm < 16; ++jm) rank[jm] += v < e[jm] ? 1 : 0;
+                }
+            }
+        }
+        wave_sync();
+        if (sz > 0) {
+#pragma unroll
+            for (int jm = 0; jm < 16; ++jm)
+                if (jm < sz) ent[ga + rank[jm]] = e[jm];
+        }
+        wave_sync();
+    }
+    // entry p of that order lands at 4 p plus the tokens of the special blocks before its block
     for (int p = l; p < nent; p += 64) {
-        const uint32_t key = ~ent[p];
+        const uint32_t key = ent[p];
         const int blk = (int)(key >> 9);
         int before = 0;
         for (int sidx = 0; sidx < nspec; ++sidx) before += spec_blk[sidx] < blk ? spec_tok[sidx] : 0;
