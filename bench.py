@@ -292,7 +292,7 @@ def run_prefill(args, cid):
     for _ in range(args.warmup):
         ws["cnt_sum"] = 0
         ws["bm_bytes"] = 0
-        prefill_step(cfg, G, ws, O=O)
+        prefill_step(cfg, G, ws, tree=tree, O=O)
     lr_total = ws.pop("cnt_sum") if args.warmup > 0 else None
     torch.cuda.synchronize()
     timers = {k: Timer() for k in ("build", "select", "attend")}
@@ -306,7 +306,7 @@ def run_prefill(args, cid):
     if lr_total is None:
         ws["cnt_sum"] = 0
         ws["bm_bytes"] = 0
-        prefill_step(cfg, G, ws, O=O)
+        prefill_step(cfg, G, ws, tree=tree, O=O)
         lr_total = ws.pop("cnt_sum")
     ms_step = wall * 1000 / args.steps
     att_ms = timers["attend"].total_ms() / args.steps

@@ -869,18 +869,6 @@ __device__ __forceinline__ int records_tokens(const uint64_t* sel, int a, int b)
 // 4 p plus the tokens of the special blocks before its block.
 // LDS scratch: ent[] of at least k/4 keys, tk[] of 256 ints (tk[0..64) is
 // expand_block_scan's map, tk[64..) lists the special blocks).
-__device__ __forceinline__ int ent_block_start(const uint32_t* ent, int n, uint32_t blk) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((ent[mid] >> 9) < blk)
-            lo = mid + 1;
-        else
-            hi = mid;
-    }
-    return lo;
-}
-
 __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const CacheView& cv, int64_t bg,
                                            const Geom& q, int32_t* out, int* tk, uint32_t* ent) {
     const int l = lane_id();
@@ -966,12 +954,18 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
         const int incl = wave_incl_scan(sz);
         const int pos = pbase + incl - sz;
         pbase += __shfl(incl, 63);
+        // the block's group of ent[]: from the place of its first record to that of the next block's
+        // (or the chunk's end); the chunk holds whole blocks
+        const uint64_t bs = __ballot(live && starts);
+        const uint64_t upto = bs & ((2ull << l) - 1ull), after = bs & ~((2ull << l) - 1ull);
+        const int ga_ = __shfl(pos, upto ? 63 - __builtin_clzll(upto) : 0);
+        const int gz_ = __shfl(pos, after ? __builtin_ctzll(after) : 0);
         uint32_t e[16];
         int rank[16];
         int ga = 0;
         if (sz > 0) {
-            ga = ent_block_start(ent, nent, (uint32_t)blk);
-            const int gz = ent_block_start(ent, nent, (uint32_t)blk + 1u);
+            ga = ga_;
+            const int gz = after ? gz_ : pbase;
 #pragma unroll
             for (int jm = 0; jm < 16; ++jm) {
                 e[jm] = jm < sz ? ent[pos + jm] : 0u;
@@ -1826,37 +1820,63 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
         const int64_t span = (int64_t)1 << lev;
         const int ncand = 2 * nf;
         const int ntiles = (ncand + 15) / 16;
-        for (int tt = 0; tt < ntiles; ++tt) {
-            const int c = 16 * tt + n;
-            int64_t node = -1;
-            if (c < ncand) {
-                node = 2 * (int64_t)front[wid][c >> 1] + (c & 1);
-                if (node >= n_lev || node * span >= NLv) node = -1;
-            }
-            float sc = kNegInf;
-            if constexpr (BF16) {
-                uint4 b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+        if constexpr (BF16) {
+            // every candidate tile's centroid fragments are loaded before any is scored, so the
+            // level waits for memory once
+            constexpr int kTiles = 2 * LSA_MAX_BEAM / 16;
+            uint4 b0[kTiles], b1[kTiles];
+            int64_t nodes[kTiles];
+#pragma unroll
+            for (int tt = 0; tt < kTiles; ++tt) {
+                const int c = 16 * tt + n;
+                int64_t node = -1;
+                if (tt < ntiles && c < ncand) {
+                    node = 2 * (int64_t)front[wid][c >> 1] + (c & 1);
+                    if (node >= n_lev || node * span >= NLv) node = -1;
+                }
+                nodes[tt] = node;
+                b0[tt] = b1[tt] = uint4{0, 0, 0, 0};
                 if (node >= 0) {
                     if (lev == 0) {   // leaves: tile-swizzled storage
                         const uint4* p =
                             reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
-                        b0 = p[cent_tile_word(node, h, 0)];
-                        b1 = p[cent_tile_word(node, h, 1)];
+                        b0[tt] = p[cent_tile_word(node, h, 0)];
+                        b1[tt] = p[cent_tile_word(node, h, 1)];
                     } else {
                         const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.tcent) +
                                                                         bg * cv.s_tcent + (lev_off + node) * kLatent +
                                                                         16 * h);
-                        b0 = p[0];
-                        b1 = p[1];
+                        b0[tt] = p[0];
+                        b1[tt] = p[1];
                     }
                 }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, as_bf16x8(b0), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, as_bf16x8(b1), acc, 0, 0, 0);
+            }
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (4 * h + v < G) sc = fmaxf(sc, acc[v]);
-            } else {
+            for (int tt = 0; tt < kTiles; ++tt) {
+                if (tt < ntiles) {
+                    const int c = 16 * tt + n;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, as_bf16x8(b0[tt]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, as_bf16x8(b1[tt]), acc, 0, 0, 0);
+                    float sc = kNegInf;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (4 * h + v < G) sc = fmaxf(sc, acc[v]);
+                    sc = fmaxf(sc, __shfl_xor(sc, 16));
+                    sc = fmaxf(sc, __shfl_xor(sc, 32));
+                    if (h == 0 && c < 2 * LSA_MAX_BEAM)
+                        keys[wid][c] = nodes[tt] >= 0 ? rank_key(sc, (uint32_t)nodes[tt]) : 0ull;
+                }
+            }
+        } else {
+            for (int tt = 0; tt < ntiles; ++tt) {
+                const int c = 16 * tt + n;
+                int64_t node = -1;
+                if (c < ncand) {
+                    node = 2 * (int64_t)front[wid][c >> 1] + (c & 1);
+                    if (node >= n_lev || node * span >= NLv) node = -1;
+                }
+                float sc = kNegInf;
                 if (node >= 0) {
                     const float* base = lev == 0 ? reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent +
                                                        node * kLatent
@@ -1872,10 +1892,10 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
                         }
                     }
                 }
+                sc = fmaxf(sc, __shfl_xor(sc, 16));
+                sc = fmaxf(sc, __shfl_xor(sc, 32));
+                if (h == 0 && c < 2 * LSA_MAX_BEAM) keys[wid][c] = node >= 0 ? rank_key(sc, (uint32_t)node) : 0ull;
             }
-            sc = fmaxf(sc, __shfl_xor(sc, 16));
-            sc = fmaxf(sc, __shfl_xor(sc, 32));
-            if (h == 0 && c < 2 * LSA_MAX_BEAM) keys[wid][c] = node >= 0 ? rank_key(sc, (uint32_t)node) : 0ull;
         }
         wave_sync();
         const int P = pow2_at_least(ncand);
