@@ -246,7 +246,7 @@ void select_ws(const lsa_layout* L, const lsa_select_cfg* C, int64_t B, int64_t 
     w.off_qhat = o;     o = align256(o + (size_t)(B * n_q * L->n_q_heads) * LSA_LATENT_DIM * elt);
     w.off_counters = o; o = align256(o + 64);
     w.off_tau = o;      o = align256(o + (size_t)units * 4);
-    w.off_cnt = o;      o = align256(o + (size_t)units * 4);
+    w.off_cnt = o;      o = align256(o + (size_t)units * 16);   // fused: 4 sub-list counts per unit
     if (w.strategy == LSA_STRATEGY_FUSED) {
         w.off_cand = o; o = align256(o + (size_t)units * lsa::kCandStride * 8);
         w.off_fb = o;   o = align256(o + (size_t)units * 4);

@@ -18,6 +18,7 @@ constexpr int kMaxGroup = LSA_MAX_GROUP;
 constexpr int kMaxLevels = 40;
 constexpr int kCandCap = 512;      // candidates per (query, KV head) the fused flat search sorts
 constexpr int kCandStride = 1024;  // candidate list slots per (query, KV head) in the fused flat search
+constexpr int kSubCap = kCandStride / 4;   // the list is 4 sub-lists of this many slots
 constexpr int kFullTake = 0xFFFF;  // "every eligible token of this bucket"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

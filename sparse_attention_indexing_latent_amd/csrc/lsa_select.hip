@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
                 for (int v = 0; v < 4; ++v) {
                     const bool pred = (!edge || (xb + v < NLv)) && qv && vals[v] >= tau_n;
                     if (pred) {
-                        const int pos = atomicAdd(&lcnt[wid][n], 1);
+                        const int pos = atomicAdd(&lcnt[wid][n], 1);   // slot pos % kSubCap of sub-list pos / kSubCap
                         if (pos < kCandStride) cand[u * kCandStride + pos] = rank_key(vals[v], (uint32_t)(xb + v));
                     }
                 }
@@ -389,7 +389,12 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
             tau[u] = tv;
         }
     } else {
-        if (h == 0 && qv) cnt[u] = lcnt[wid][n];
+        if (h == 0 && qv) {
+            const int c = lcnt[wid][n];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                cnt[4 * u + j] = j < 3 ? min(max(c - kSubCap * j, 0), kSubCap) : max(c - kSubCap * 3, 0);
+        }
     }
 }
 
@@ -412,7 +417,9 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
 // Hence at the end tau = lower edge of b* (minus 2^-16; -inf if the weight
 // never reaches k) is the bound of the two-pass scan, and the list holds
 // every visible bucket scoring >= tau (plus earlier ones below it, dropped
-// by the finalize).  The list is capped at kCandStride, its count exact.
+// by the finalize).  A query's list is 4 sub-lists of kSubCap slots, one per
+// lane of its MFMA column (no cross-lane step per append); their counts are
+// exact even past the cap.
 constexpr int kScanQ = 128;         // queries per workgroup
 constexpr int kScanChunk = 8;       // tiles per staged chunk
 constexpr int kFNeg = 8;
@@ -514,7 +521,7 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
     const u32x4* msrc = reinterpret_cast<const u32x4*>(cv.meta + bg * cv.s_meta);
     int fb[2] = {0, 0};
     float fe[2] = {kNegInf, kNegInf};
-    int base[2] = {0, 0};   // the query's list length (the same on its 4 lanes)
+    int base[2] = {0, 0};   // length of this lane's sub-list (h) of its query's candidate list
     // staging: thread tid copies words tid + 256 j (j < 4) of a chunk and, if tid < 32, meta word tid;
     // tiles past the last one repeat it
     u32x4 r0, r1, r2, r3, rmt;
@@ -579,26 +586,21 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
                 m[cg] = (best[cg][0] >= fe[cg] && 0 < lim ? 1u : 0u) | (best[cg][1] >= fe[cg] && 1 < lim ? 2u : 0u) |
                         (best[cg][2] >= fe[cg] && 2 < lim ? 4u : 0u) | (best[cg][3] >= fe[cg] && 3 < lim ? 8u : 0u);
             }
-            if (__ballot((m[0] | m[1]) != 0)) {
+            if (m[0] | m[1]) {
                 const int64_t lo = (int64_t)(x0 / kLeavesPerBlock) * kBlockTokens;
                 const uint4 m4 = sm[tt * 4 + h];
                 const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
                 for (int cg = 0; cg < 2; ++cg) {
-                    // list positions: the query's 4 lanes append in h order after its current length
-                    const int cl = __popc(m[cg]);
-                    const int c0 = __shfl(cl, n), c1 = __shfl(cl, n + 16), c2 = __shfl(cl, n + 32),
-                              c3 = __shfl(cl, n + 48);
-                    int pos = base[cg] + (h > 0 ? c0 : 0) + (h > 1 ? c1 : 0) + (h > 2 ? c2 : 0);
-                    base[cg] += c0 + c1 + c2 + c3;
                     if (m[cg]) {
+                        // this lane's sub-list h of its query's candidate list
                         const bool elig = lo >= lo_ok[cg] && lo + kBlockTokens <= hi_ok[cg];
+                        uint64_t* sub = cand + u[cg] * kCandStride + h * kSubCap;
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
                             if (m[cg] & (1u << v)) {
-                                if (pos < kCandStride)
-                                    cand[u[cg] * kCandStride + pos] = rank_key(best[cg][v], (uint32_t)(xb + v));
-                                ++pos;
+                                if (base[cg] < kSubCap) sub[base[cg]] = rank_key(best[cg][v], (uint32_t)(xb + v));
+                                ++base[cg];
                                 if (elig)
                                     atomicAdd(&hrow[cg][fscan_bin(best[cg][v])], (uint32_t)kPool * (mm[v] & 0xFFu));
                             }
@@ -623,9 +625,9 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg) {
         const int bin = fscan_cross_bin(hrow[cg], h, (uint32_t)sa.k);
-        if (h == 0 && qv[cg]) {
-            tau[u[cg]] = bin >= 1 ? fscan_edge(bin) - 1.52587890625e-05f : kNegInf;
-            cnt[u[cg]] = base[cg];
+        if (qv[cg]) {
+            if (h == 0) tau[u[cg]] = bin >= 1 ? fscan_edge(bin) - 1.52587890625e-05f : kNegInf;
+            cnt[4 * u[cg] + h] = base[cg];
         }
     }
 }
@@ -1102,20 +1104,25 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
     const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
     int32_t* out = lr_idx + u * sa.k;
     if (trivial_unit(t, q, sa.k, out, lr_cnt + u)) return;
-    // the candidates scoring >= tau (the list may also hold buckets below it), compacted in list order
-    const int c = cnt[u];
+    // the candidates scoring >= tau (the lists may also hold buckets below it), compacted; the
+    // candidate list is 4 sub-lists of kSubCap slots with their own counts
+    const int4 c4 = *reinterpret_cast<const int4*>(cnt + 4 * u);
+    const int cs[4] = {c4.x, c4.y, c4.z, c4.w};
+    const bool over = c4.x > kSubCap || c4.y > kSubCap || c4.z > kSubCap || c4.w > kSubCap;
     int f = 0;
-    if (c <= kCandStride) {
+    if (!over) {
         const uint64_t kmin = (uint64_t)ord_key(tau[u]) << 32;   // key >= kmin  <=>  score >= tau
         const uint64_t lt = (1ull << l) - 1ull;
-        const uint64_t* cl = cand + u * kCandStride;
-        for (int j0 = 0; j0 < c; j0 += 256) {
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            const int c = cs[sl];
+            const uint64_t* cl = cand + u * kCandStride + sl * kSubCap;
             uint64_t kk[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) kk[r] = j0 + 64 * r + l < c ? cl[j0 + 64 * r + l] : 0ull;
+            for (int r = 0; r < 4; ++r) kk[r] = 64 * r + l < c ? cl[64 * r + l] : 0ull;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool keep = j0 + 64 * r + l < c && kk[r] >= kmin;
+                const bool keep = 64 * r + l < c && kk[r] >= kmin;
                 const uint64_t bal = __ballot(keep);
                 const int pos = f + __popcll(bal & lt);
                 if (keep && pos < kCandCap) keys[wid][pos] = kk[r];
@@ -1123,7 +1130,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
             }
         }
     }
-    if (c > kCandStride || f > kCandCap) {
+    if (over || f > kCandCap) {
         if (l == 0) {
             const int pos = atomicAdd(&counters[0], 1);
             fb_list[pos] = (int)u;
