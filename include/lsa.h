@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 2
+#define LSA_ABI_VERSION 3
 
 #define LSA_LATENT_DIM 64         /* latent width (ch.2: 64-d index space) */
 #define LSA_POOL 4                /* keys pooled per entry (ch.2)            */
@@ -123,6 +123,11 @@ typedef struct lsa_select_cfg {
     int32_t search;    /* lsa_search                                                    */
     int32_t beam;      /* tree only: 1..LSA_MAX_BEAM                                    */
     int32_t strategy;  /* lsa_strategy (flat search only)                               */
+    int32_t causal_tree; /* tree only, 0 or 1: score a node that straddles the query's
+                          * visible leaves by the centroid of its visible part (the
+                          * node as a tree built over the visible blocks has it), so a
+                          * prefill query selects what a decode step at its position
+                          * does on a cache grown to that point; 0: stored centroids */
 } lsa_select_cfg;
 
 /* Byte offsets of the cache regions, for inspection (tests, tools).  Per
@@ -134,10 +139,17 @@ typedef struct lsa_select_cfg {
  * [n_blocks_max, 512] uint16 (each block's entry indices grouped by bucket,
  * ascending inside a bucket), entry_leaf [n_blocks_max, 512] uint8 (bucket
  * rank of every entry), tree_cent / tree_sums [nodes_max, 64] for the tree
- * levels above the leaves (level l >= 1 starts at node level_off[l]),
+ * levels above the leaves (level l >= 1 starts at node level_off[l]; each
+ * level has room for ceil(leaves_max / 2^l) nodes, so offsets depend on
+ * t_max only and a node keeps its place as the cache grows),
  * entry_pos [n_blocks_max, 512] uint8 (position of every entry inside its
  * bucket's member list, so token 4e + j of a bucket is its key number
- * 4 * entry_pos[e] + j in member order). */
+ * 4 * entry_pos[e] + j in member order), and with a tree edge_cent
+ * [n_blocks_max + 1, edge_levels, 64] (dtype): row (nb, l) is the centroid
+ * of the level-l node that straddles leaf 64 nb, taken over its leaves
+ * below 64 nb only, i.e. that node as a tree over the first nb blocks has it
+ * (normalised sum of its visible children's sums; rows of levels with no
+ * straddling node are unused). */
 typedef struct lsa_cache_info {
     int64_t n_blocks_max;
     int64_t leaves_max;
@@ -146,13 +158,15 @@ typedef struct lsa_cache_info {
     int64_t n_leaves;
     int32_t n_levels;          /* tree levels including the leaves (1 + ceil(log2 n_leaves)) */
     int32_t elt_bytes;         /* 2 (bf16) or 4 (fp32) */
-    int64_t level_off[40];     /* node offset of tree level l (l >= 1); level_size below */
+    int64_t level_off[40];     /* node offset of tree level l (l >= 1); level_size = nodes in use */
     int64_t level_size[40];
     size_t off_cent, off_sums, off_meta, off_members, off_entry_leaf, off_tree_cent, off_tree_sums;
     size_t stride_cent, stride_sums, stride_meta, stride_members, stride_entry_leaf,
            stride_tree_cent, stride_tree_sums;   /* bytes between consecutive (b, g) */
     size_t total_bytes;
     size_t off_entry_pos, stride_entry_pos;
+    size_t off_edge_cent, stride_edge_cent;   /* tree only: see below */
+    int32_t edge_levels;
 } lsa_cache_info;
 
 /* Bytes of a bucket cache for `batch` sequences of up to t_max tokens.
@@ -176,6 +190,21 @@ lsa_status lsa_cache_describe(const lsa_layout* layout, int64_t batch, int64_t t
 lsa_status lsa_build_buckets(const lsa_layout* layout, const void* K, int64_t batch, int64_t t_cap,
                              int64_t T, const void* W_k, void* cache, size_t cache_bytes,
                              int64_t t_max, void* stream);
+
+/* Cache growth (ch.2: each block of 512 pooled keys is clustered once, as
+ * the keys stream in, and never again).  The cache holds a build (or
+ * extensions) of the first T_old tokens with this layout, batch and t_max;
+ * the full blocks of tokens [T_old, T_new) are clustered and their buckets
+ * appended exactly as lsa_build_buckets would store them, and with
+ * layout->build_tree the tree nodes over the new leaves (the right edge of
+ * every level, and any new levels) are recomputed: the cache then equals,
+ * bit for bit, a build of the first T_new tokens.  Buckets and nodes over
+ * older leaves are not touched, so readers of them may run concurrently on
+ * other streams.  K: [batch, H_kv, t_cap, d], T_old <= T_new <= t_cap,
+ * T_new <= t_max; errors as lsa_build_buckets (nothing is launched). */
+lsa_status lsa_extend_buckets(const lsa_layout* layout, const void* K, int64_t batch, int64_t t_cap,
+                              int64_t T_old, int64_t T_new, const void* W_k, void* cache,
+                              size_t cache_bytes, int64_t t_max, void* stream);
 
 /* Workspace bytes lsa_select needs for this many queries. Host only. */
 lsa_status lsa_select_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg,

@@ -353,15 +353,19 @@ def select_flat(qhat: np.ndarray, cache: Dict, t: int, k: int, n_sinks: int, win
 
 
 def select_tree(qhat: np.ndarray, cache: Dict, t: int, k: int, n_sinks: int, window: int, beam: int,
-                with_margin: bool = False):
+                with_margin: bool = False, causal: bool = False):
     """Tree search (ch.4): beam descent from the root, then expansion.
 
     A node is visible when its first leaf is visible; it is scored with its
-    stored centroid.  At each level the candidates are the visible children
-    of the beam and the best `beam` by (score desc, index asc) are kept; the
-    kept leaves are then expanded exactly as in the flat search.  info['cuts']
-    lists, per level with more candidates than the beam, the gap between the
-    last kept and the first dropped score.
+    stored centroid, or, with causal=True, a node whose leaves are only
+    partly visible is scored with the centroid of its visible leaves
+    (round(normalise(sum of their sums))): the node as the tree over the
+    blocks seen so far has it (ch.2: blocks are clustered as keys stream in).
+    At each level the candidates are the visible children of the beam and the
+    best `beam` by (score desc, index asc) are kept; the kept leaves are then
+    expanded exactly as in the flat search.  info['cuts'] lists, per level
+    with more candidates than the beam, the gap between the last kept and the
+    first dropped score.
     """
     levels = cache["tree"]
     nvis, sink_end, l0 = query_geometry(t, cache["n_blocks"], n_sinks, window)
@@ -378,7 +382,13 @@ def select_tree(qhat: np.ndarray, cache: Dict, t: int, k: int, n_sinks: int, win
         span = levels[lev]["span"]
         ch = np.concatenate([2 * frontier, 2 * frontier + 1])
         ch = np.unique(ch[(ch < n_lev) & (ch * span < NLv)])
-        sc = (levels[lev]["cent"][ch] @ q.T).max(axis=1)
+        cent = levels[lev]["cent"][ch]
+        if causal:
+            for r, j in enumerate(ch):
+                if (j + 1) * span > NLv:   # straddles the visible leaves
+                    part = np.add.reduceat(cache["sums"][j * span: NLv], [0], axis=0)[0]
+                    cent[r] = round_to(normalise(part[None, :]), cache["dtype"])[0]
+        sc = (cent @ q.T).max(axis=1)
         order = np.lexsort((ch, -sc))
         if len(order) > beam:
             info["cuts"].append(float(sc[order[beam - 1]] - sc[order[beam]]))

@@ -49,9 +49,9 @@ def make_layout(head_dim: int, n_kv_heads: int, n_q_heads: int, dtype: torch.dty
 
 
 def select_cfg(k: int, n_sinks: int, window: int, search: str = "flat", beam: int = 0,
-               strategy: str = "auto") -> SelectCfg:
+               strategy: str = "auto", causal_tree: bool = False) -> SelectCfg:
     return SelectCfg(k, n_sinks, window, LSA_SEARCH_TREE if search == "tree" else LSA_SEARCH_FLAT, beam,
-                     _STRATEGIES[strategy])
+                     _STRATEGIES[strategy], int(causal_tree))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -116,6 +116,15 @@ class LsaCache:
         i = self.info()
         return self._region(i.off_entry_pos, i.stride_entry_pos, i.n_blocks * 512, torch.uint8, (i.n_blocks, 512))
 
+    def edge_table(self) -> torch.Tensor:
+        """[B, H_kv, n_blocks_max + 1, levels, 64] tree only: row (nb, l) = centroid of the level-l node
+        straddling leaf 64 nb over its leaves below it (rows of levels with no such node are unused)."""
+        i = self.info()
+        dt = torch.bfloat16 if self.layout.dtype == LSA_BF16 else torch.float32
+        rows = (i.n_blocks_max + 1) * i.edge_levels
+        return self._region(i.off_edge_cent, i.stride_edge_cent, rows * 64, dt,
+                            (i.n_blocks_max + 1, i.edge_levels, 64))
+
     def tree_level(self, lev: int):
         """(centroids, sums) of tree level lev (0 = leaves)."""
         if lev == 0:
@@ -149,6 +158,20 @@ def build_buckets(K: torch.Tensor, W_k: torch.Tensor, T: Optional[int] = None, t
     return LsaCache(cache, layout, B, t_max, T)
 
 
+def extend_buckets(cache: LsaCache, K: torch.Tensor, W_k: torch.Tensor, T_new: int) -> LsaCache:
+    """Cache growth: cluster the full blocks of tokens [cache.T, T_new) of K and append their buckets
+    (and the tree's new right edge) in place; the cache then equals a build of the first T_new tokens.
+
+    K: [B, H_kv, t_cap, d] as for build_buckets, T_new <= t_cap and <= cache.t_max."""
+    assert K.is_cuda and K.is_contiguous() and W_k.is_contiguous()
+    B, H_kv, t_cap, d = K.shape
+    _lib.check(_lib.lib().lsa_extend_buckets(ctypes.byref(cache.layout), _ptr(K), B, t_cap, cache.T, T_new,
+                                             _ptr(W_k), _ptr(cache.buf), cache.buf.numel(), cache.t_max,
+                                             _stream(K.device)))
+    cache.T = T_new
+    return cache
+
+
 def select_workspace_bytes(cache: LsaCache, cfg: SelectCfg, n_q: int, n_q_heads: int) -> int:
     layout = Layout.from_buffer_copy(cache.layout)
     layout.n_q_heads = n_q_heads
@@ -160,17 +183,19 @@ def select_workspace_bytes(cache: LsaCache, cfg: SelectCfg, n_q: int, n_q_heads:
 
 def select(Q: torch.Tensor, cache: LsaCache, q_pos: torch.Tensor, W_q: torch.Tensor, k: int, n_sinks: int,
            window: int, search: str = "flat", beam: int = 0, strategy: str = "auto",
-           workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None):
+           workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None, causal_tree: bool = False):
     """Query side: score buckets, pick the top ones, expand to k tokens.
 
     Q: [B, n_q, H_q, d]; q_pos: int64 [B, n_q] on the GPU.  Returns
     (lr_idx int32 [B, n_q, H_kv, k] ascending, -1 padded; lr_cnt int32 [B, n_q, H_kv]).
+    causal_tree (tree search): nodes straddling a query's visible leaves are scored by their visible
+    part, as a decode step on a cache grown to the query's position would score them.
     """
     assert Q.is_cuda and Q.is_contiguous() and q_pos.dtype == torch.int64 and q_pos.is_contiguous()
     B, n_q, H_q, d = Q.shape
     layout = Layout.from_buffer_copy(cache.layout)
     layout.n_q_heads = H_q
-    cfg = select_cfg(k, n_sinks, window, search, beam, strategy)
+    cfg = select_cfg(k, n_sinks, window, search, beam, strategy, causal_tree)
     L = _lib.lib()
     H_kv = layout.n_kv_heads
     if out is None:

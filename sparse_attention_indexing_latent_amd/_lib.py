@@ -35,7 +35,8 @@ STATUS_NAMES = {
 
 # every symbol include/lsa.h declares
 EXPORTS = [
-    "lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_select_workspace_bytes", "lsa_select",
+    "lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_extend_buckets", "lsa_select_workspace_bytes",
+    "lsa_select",
     "lsa_attend_workspace_bytes", "lsa_sparse_attend", "lsa_attend_bucket_major_workspace_bytes",
     "lsa_sparse_attend_bucket_major", "lsa_pca_workspace_bytes", "lsa_pca_projection", "lsa_status_string",
     "lsa_last_error", "lsa_abi_version",
@@ -49,7 +50,7 @@ class Layout(ctypes.Structure):
 
 
 class SelectCfg(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("k", "n_sinks", "window", "search", "beam", "strategy")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("k", "n_sinks", "window", "search", "beam", "strategy", "causal_tree")]
 
 
 class CacheInfo(ctypes.Structure):
@@ -60,7 +61,8 @@ class CacheInfo(ctypes.Structure):
     ] + [(n, ctypes.c_size_t) for n in (
         "off_cent", "off_sums", "off_meta", "off_members", "off_entry_leaf", "off_tree_cent", "off_tree_sums",
         "stride_cent", "stride_sums", "stride_meta", "stride_members", "stride_entry_leaf", "stride_tree_cent",
-        "stride_tree_sums", "total_bytes", "off_entry_pos", "stride_entry_pos")]
+        "stride_tree_sums", "total_bytes", "off_entry_pos", "stride_entry_pos", "off_edge_cent", "stride_edge_cent")
+    ] + [("edge_levels", ctypes.c_int32)]
 
 
 class LsaError(RuntimeError):
@@ -85,6 +87,7 @@ def lib():
     L.lsa_cache_bytes.argtypes = [P(Layout), i64, i64, P(sz)]
     L.lsa_cache_describe.argtypes = [P(Layout), i64, i64, i64, P(CacheInfo)]
     L.lsa_build_buckets.argtypes = [P(Layout), vp, i64, i64, i64, vp, vp, sz, i64, vp]
+    L.lsa_extend_buckets.argtypes = [P(Layout), vp, i64, i64, i64, i64, vp, vp, sz, i64, vp]
     L.lsa_select_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, i64, P(sz)]
     L.lsa_select.argtypes = [P(Layout), P(SelectCfg), vp, sz, i64, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp]
     L.lsa_attend_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, P(sz)]
@@ -95,7 +98,8 @@ def lib():
                                                  i64, i64, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     L.lsa_pca_workspace_bytes.argtypes = [P(Layout), P(sz)]
     L.lsa_pca_projection.argtypes = [P(Layout), vp, i64, i64, i64, vp, vp, vp, sz, vp]
-    for name in ("lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_select_workspace_bytes",
+    for name in ("lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_extend_buckets",
+                 "lsa_select_workspace_bytes",
                  "lsa_select", "lsa_attend_workspace_bytes", "lsa_sparse_attend",
                  "lsa_attend_bucket_major_workspace_bytes", "lsa_sparse_attend_bucket_major",
                  "lsa_pca_workspace_bytes", "lsa_pca_projection"):

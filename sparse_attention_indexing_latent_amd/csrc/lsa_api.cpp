@@ -61,8 +61,9 @@ struct CacheGeom {
     int32_t elt;
     int64_t level_off[lsa::kMaxLevels];
     int64_t level_size[lsa::kMaxLevels];
-    size_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos;   // bytes per (b, g)
-    size_t off_cent, off_sums, off_meta, off_members, off_eleaf, off_tcent, off_tsums, off_epos, total;
+    int32_t n_lev_cap;   // levels of a tree over leaves_max leaves
+    size_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos, s_edge;   // bytes per (b, g)
+    size_t off_cent, off_sums, off_meta, off_members, off_eleaf, off_tcent, off_tsums, off_epos, off_edge, total;
 };
 
 int64_t tree_nodes_above(int64_t nl) {
@@ -80,19 +81,23 @@ void cache_geom(const lsa_layout* L, int64_t B, int64_t t_max, int64_t T, CacheG
     c.nbm = t_max / LSA_BLOCK_TOKENS;
     c.nlm = c.nbm * LSA_LEAVES_PER_BLOCK;
     c.nnm = L->build_tree ? tree_nodes_above(c.nlm) : 0;
+    c.n_lev_cap = 1;
+    for (int64_t nl = c.nlm; nl > 1; nl = (nl + 1) / 2) ++c.n_lev_cap;
     c.n_blocks = T / LSA_BLOCK_TOKENS;
     c.n_leaves = c.n_blocks * LSA_LEAVES_PER_BLOCK;
     if (c.n_leaves > 0) {
-        int64_t nl = c.n_leaves, off = 0;
+        // sizes from the current leaves, offsets from the capacity (stable as the cache grows)
+        int64_t nl = c.n_leaves, ncap = c.nlm, off = 0;
         int lev = 0;
         c.level_size[0] = nl;
         c.level_off[0] = 0;
         while (nl > 1 && lev + 1 < lsa::kMaxLevels) {
             nl = (nl + 1) / 2;
+            ncap = (ncap + 1) / 2;
             ++lev;
             c.level_off[lev] = off;
             c.level_size[lev] = nl;
-            off += nl;
+            off += ncap;
         }
         c.n_levels = lev + 1;
     }
@@ -105,6 +110,7 @@ void cache_geom(const lsa_layout* L, int64_t B, int64_t t_max, int64_t T, CacheG
     c.s_tcent = align256((size_t)c.nnm * LSA_LATENT_DIM * c.elt);
     c.s_tsums = align256((size_t)c.nnm * LSA_LATENT_DIM * 4);
     c.s_epos = align256((size_t)c.nbm * LSA_BLOCK_ENTRIES);
+    c.s_edge = L->build_tree ? align256((size_t)(c.nbm + 1) * c.n_lev_cap * LSA_LATENT_DIM * c.elt) : 0;
     size_t o = 0;
     c.off_cent = o;    o += c.s_cent * HB;
     c.off_sums = o;    o += c.s_sums * HB;
@@ -114,6 +120,7 @@ void cache_geom(const lsa_layout* L, int64_t B, int64_t t_max, int64_t T, CacheG
     c.off_tcent = o;   o += c.s_tcent * HB;
     c.off_tsums = o;   o += c.s_tsums * HB;
     c.off_epos = o;    o += c.s_epos * HB;
+    c.off_edge = o;    o += c.s_edge * HB;
     c.total = o > 0 ? o : 256;
 }
 
@@ -129,6 +136,7 @@ lsa::CacheView make_view(const CacheGeom& c, void* cache, bool bf16) {
     v.tcent = base + c.off_tcent;
     v.tsums = reinterpret_cast<float*>(base + c.off_tsums);
     v.epos = reinterpret_cast<uint8_t*>(base + c.off_epos);
+    v.edge = base + c.off_edge;
     v.s_cent = (int64_t)(c.s_cent / c.elt);
     v.s_sums = (int64_t)(c.s_sums / 4);
     v.s_meta = (int64_t)(c.s_meta / 4);
@@ -137,9 +145,12 @@ lsa::CacheView make_view(const CacheGeom& c, void* cache, bool bf16) {
     v.s_tcent = (int64_t)(c.s_tcent / c.elt);
     v.s_tsums = (int64_t)(c.s_tsums / 4);
     v.s_epos = (int64_t)c.s_epos;
+    v.s_edge = (int64_t)(c.s_edge / c.elt);
+    v.n_lev_cap = c.n_lev_cap;
     v.n_blocks = (int32_t)c.n_blocks;
     v.n_leaves = (int32_t)c.n_leaves;
     v.n_levels = c.n_levels;
+    v.n_leaves_cap = (int32_t)c.nlm;
     v.bf16 = bf16 ? 1 : 0;
     return v;
 }
@@ -156,6 +167,7 @@ lsa_status check_cfg(const lsa_select_cfg* C, int64_t T) {
                     (long long)T);
     if (C->search == LSA_SEARCH_TREE && (C->beam < 1 || C->beam > LSA_MAX_BEAM))
         return fail(LSA_ERR_CAPACITY, "beam must be in 1..%d", LSA_MAX_BEAM);
+    if (C->causal_tree != 0 && C->causal_tree != 1) return fail(LSA_ERR_INVALID_ARG, "causal_tree must be 0 or 1");
     return LSA_OK;
 }
 
@@ -332,6 +344,9 @@ lsa_status lsa_cache_describe(const lsa_layout* layout, int64_t batch, int64_t t
     info->total_bytes = c.total;
     info->off_entry_pos = c.off_epos;
     info->stride_entry_pos = c.s_epos;
+    info->off_edge_cent = c.off_edge;
+    info->stride_edge_cent = c.s_edge;
+    info->edge_levels = c.n_lev_cap;
     return ok();
 }
 
@@ -355,6 +370,38 @@ lsa_status lsa_build_buckets(const lsa_layout* layout, const void* K, int64_t ba
     hipError_t e = lsa::launch_build(v, K, bf16, t_cap, layout->head_dim, (int)batch, layout->n_kv_heads, W_k, st);
     if (e == hipSuccess && layout->build_tree)
         e = lsa::launch_tree(v, c.level_off, c.level_size, (int)batch, layout->n_kv_heads, st);
+    if (e == hipSuccess && layout->build_tree) e = lsa::launch_edges(v, (int)batch, layout->n_kv_heads, 1, st);
+    if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+lsa_status lsa_extend_buckets(const lsa_layout* layout, const void* K, int64_t batch, int64_t t_cap, int64_t T_old,
+                              int64_t T_new, const void* W_k, void* cache, size_t cache_bytes, int64_t t_max,
+                              void* stream) {
+    lsa_status s = check_layout(layout);
+    if (s) return s;
+    if (batch < 0 || t_cap < 0 || T_old < 0 || t_max < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (T_new < T_old) return fail(LSA_ERR_INVALID_ARG, "T_new=%lld is below T_old=%lld", (long long)T_new, (long long)T_old);
+    if (T_new > t_cap) return fail(LSA_ERR_CAPACITY, "T_new=%lld exceeds t_cap=%lld", (long long)T_new, (long long)t_cap);
+    if (T_new > t_max) return fail(LSA_ERR_CAPACITY, "T_new=%lld exceeds t_max=%lld", (long long)T_new, (long long)t_max);
+    if (!K || !W_k || !cache) return fail(LSA_ERR_INVALID_ARG, "K, W_k and cache must be non-NULL");
+    if (misaligned(K) || misaligned(W_k) || misaligned(cache)) return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
+    CacheGeom c;
+    cache_geom(layout, batch, t_max, T_new, c);
+    if (cache_bytes < c.total)
+        return fail(LSA_ERR_WORKSPACE, "cache has %zu bytes, needs %zu", cache_bytes, c.total);
+    const int64_t b0 = T_old / LSA_BLOCK_TOKENS;
+    if (batch == 0 || c.n_blocks == b0) return ok();
+    const bool bf16 = layout->dtype == LSA_BF16;
+    lsa::CacheView v = make_view(c, cache, bf16);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = lsa::launch_build(v, K, bf16, t_cap, layout->head_dim, (int)batch, layout->n_kv_heads, W_k, st,
+                                     (int)b0);
+    if (e == hipSuccess && layout->build_tree)
+        e = lsa::launch_tree(v, c.level_off, c.level_size, (int)batch, layout->n_kv_heads, st,
+                             b0 * LSA_LEAVES_PER_BLOCK);
+    if (e == hipSuccess && layout->build_tree)
+        e = lsa::launch_edges(v, (int)batch, layout->n_kv_heads, (int)b0 + 1, st);
     if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -417,6 +464,7 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     sa.n_sinks = cfg->n_sinks;
     sa.window = cfg->window;
     sa.beam = cfg->beam;
+    sa.causal_tree = cfg->search == LSA_SEARCH_TREE ? cfg->causal_tree : 0;
     sa.H_q = layout->n_q_heads;
     sa.H_kv = layout->n_kv_heads;
     sa.G = layout->n_q_heads / layout->n_kv_heads;

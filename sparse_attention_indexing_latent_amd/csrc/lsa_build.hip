@@ -33,8 +33,9 @@ __device__ __forceinline__ uint64_t pair_key(float d, int id, int nn) {
 
 template <typename TIN>
 __global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restrict__ K, int64_t t_cap, int d,
-                                                            int H_kv, const TIN* __restrict__ W, CacheView cv) {
-    const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+                                                            int H_kv, const TIN* __restrict__ W, CacheView cv,
+                                                            int blk0) {
+    const int blk = blk0 + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t bg = (int64_t)b * H_kv + g;
 
@@ -289,9 +290,9 @@ __global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restric
 // one), its norm, and the rounded centroid (ch.4: node centroid = mean of
 // every key below it; the normalisation makes mean and sum equivalent).
 __global__ __launch_bounds__(256) void tree_level_kernel(CacheView cv, int lev, int64_t n_child, int64_t n_par,
-                                                         int64_t child_off, int64_t par_off) {
+                                                         int64_t child_off, int64_t par_off, int64_t first) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int64_t node = (int64_t)blockIdx.x * 4 + wid;
+    const int64_t node = first + (int64_t)blockIdx.x * 4 + wid;
     if (node >= n_par) return;
     const int64_t bg = blockIdx.y;
     const float* cs = lev == 1 ? cv.sums + bg * cv.s_sums : cv.tsums + bg * cv.s_tsums + child_off * kLatent;
@@ -308,18 +309,69 @@ __global__ __launch_bounds__(256) void tree_level_kernel(CacheView cv, int lev, 
         reinterpret_cast<float*>(cv.tcent)[bg * cv.s_tcent + o] = v;
 }
 
+// Edge table: one wave per (b, g) and block boundary nb (m = 64 nb leaves).
+// At level l the node straddling leaf m is j = (m - 1) >> l (none when m is
+// a multiple of 2^l); as a node of the tree over the first m leaves its sum
+// is its left child's sum (complete when m >= the children's midpoint) plus
+// its right child's partial sum (the straddling node one level down) when
+// m passes the midpoint, else its left child's partial sum: the additions
+// tree_level_kernel makes for a tree built over m leaves, so the centroid
+// is bit for bit that tree's.  Rows are written for every level of a tree
+// over leaves_max leaves.
+__global__ __launch_bounds__(256) void tree_edge_kernel(CacheView cv, int nb_first) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int64_t nb = nb_first + (int64_t)blockIdx.x * 4 + wid;
+    if (nb > cv.n_blocks) return;
+    const int64_t bg = blockIdx.y;
+    const int64_t m = nb * kLeavesPerBlock;
+    float part = 0.f;   // partial sum of the straddling node one level down
+    // every level of the capacity tree: above the current top, node 0 straddles and only reads
+    // nodes that exist (m <= the midpoint), so the rows do not depend on when they were written
+    for (int lev = 1; lev < cv.n_lev_cap; ++lev) {
+        if ((m & (((int64_t)1 << lev) - 1)) == 0) continue;   // no straddling node at this level
+        const int64_t j = (m - 1) >> lev;
+        const int64_t mid = (2 * j + 1) << (lev - 1);
+        float s;
+        if (m >= mid) {
+            const int64_t c0 = 2 * j;
+            s = lev == 1 ? cv.sums[bg * cv.s_sums + c0 * kLatent + lane]
+                         : cv.tsums[bg * cv.s_tsums + (tree_level_off(cv.n_leaves_cap, lev - 1) + c0) * kLatent + lane];
+            if (m > mid) s += part;
+        } else {
+            s = part;
+        }
+        part = s;
+        const float ss = wave_sum(s * s);
+        const float v = ss > 0.f ? s * (1.0f / sqrtf(ss)) : 0.f;
+        const int64_t o = bg * cv.s_edge + (nb * cv.n_lev_cap + lev) * kLatent + lane;
+        if (cv.bf16)
+            reinterpret_cast<uint16_t*>(cv.edge)[o] = f32_to_bf16(v);
+        else
+            reinterpret_cast<float*>(cv.edge)[o] = v;
+    }
+}
+
 }  // namespace
 
+hipError_t launch_edges(const CacheView& cv, int B, int H_kv, int nb_first, hipStream_t st) {
+    if (nb_first > cv.n_blocks) return hipSuccess;
+    const int64_t n = cv.n_blocks - nb_first + 1;
+    dim3 grid((unsigned)((n + 3) / 4), (unsigned)(B * H_kv));
+    hipLaunchKernelGGL(tree_edge_kernel, grid, dim3(256), 0, st, cv, nb_first);
+    return hipGetLastError();
+}
+
 hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
-                        const void* W, hipStream_t st) {
-    if (cv.n_blocks > 0) {
-        dim3 grid(cv.n_blocks, H_kv, B);
+                        const void* W, hipStream_t st, int blk0) {
+    if (cv.n_blocks > blk0) {
+        dim3 grid(cv.n_blocks - blk0, H_kv, B);
         if (bf16)
             hipLaunchKernelGGL(ward_kernel<uint16_t>, grid, dim3(kWardThreads), 0, st,
-                               static_cast<const uint16_t*>(K), t_cap, d, H_kv, static_cast<const uint16_t*>(W), cv);
+                               static_cast<const uint16_t*>(K), t_cap, d, H_kv, static_cast<const uint16_t*>(W), cv,
+                               blk0);
         else
             hipLaunchKernelGGL(ward_kernel<float>, grid, dim3(kWardThreads), 0, st, static_cast<const float*>(K),
-                               t_cap, d, H_kv, static_cast<const float*>(W), cv);
+                               t_cap, d, H_kv, static_cast<const float*>(W), cv, blk0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -327,12 +379,16 @@ hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t
 }
 
 hipError_t launch_tree(const CacheView& cv, const int64_t* level_off, const int64_t* level_size, int B, int H_kv,
-                       hipStream_t st) {
+                       hipStream_t st, int64_t first_leaf) {
+    // nodes from the one over first_leaf on (all of them for a build; the new right edge when the
+    // cache grows: the nodes over older leaves only are unchanged)
     for (int lev = 1; lev < cv.n_levels; ++lev) {
         const int64_t n_child = level_size[lev - 1], n_par = level_size[lev];
-        dim3 grid((unsigned)((n_par + 3) / 4), (unsigned)(B * H_kv));
+        const int64_t first = first_leaf >> lev;
+        if (first >= n_par) continue;
+        dim3 grid((unsigned)((n_par - first + 3) / 4), (unsigned)(B * H_kv));
         hipLaunchKernelGGL(tree_level_kernel, grid, dim3(256), 0, st, cv, lev, n_child, n_par, level_off[lev - 1],
-                           level_off[lev]);
+                           level_off[lev], first);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

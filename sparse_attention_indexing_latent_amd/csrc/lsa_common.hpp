@@ -39,11 +39,14 @@ struct CacheView {
     void* tcent;           // [B, H_kv, nodes_max, 64]   dtype (tree levels >= 1)
     float* tsums;          // [B, H_kv, nodes_max, 64]
     uint8_t* epos;         // [B, H_kv, n_blocks_max, 512] position of each entry in its bucket's member list
-    int64_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos;
+    void* edge;            // [B, H_kv, n_blocks_max + 1, n_lev_cap, 64] dtype: node straddling 64 nb leaves
+    int64_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos, s_edge;
     int32_t n_blocks;      // full blocks bucketed
     int32_t n_leaves;
     int32_t n_levels;      // tree levels including the leaves
     int32_t bf16;          // centroid storage dtype
+    int32_t n_leaves_cap;  // leaves_max: the tree levels are laid out for it
+    int32_t n_lev_cap;     // levels of a tree over leaves_max leaves (edge table rows)
 };
 
 // bf16 leaf centroids are stored in tiles of 16 buckets (2 KB, 1024
@@ -58,7 +61,9 @@ __device__ __forceinline__ int64_t cent_tile_word(int64_t leaf, int h, int m) {
 }
 
 // Tree level l >= 1 holds ceil(n_leaves / 2^l) nodes (pairing (2j, 2j+1) level
-// by level); levels are stored one after the other from level 1.
+// by level); levels are stored one after the other from level 1, each with
+// room for the nodes over leaves_max leaves, so a node keeps its place as the
+// cache grows (tree_level_off takes leaves_max).
 __device__ __forceinline__ int64_t tree_level_size(int64_t n_leaves, int lev) {
     return (n_leaves + ((int64_t)1 << lev) - 1) >> lev;
 }

@@ -13,6 +13,7 @@ struct SelArgs {
     int32_t n_sinks;
     int32_t window;
     int32_t beam;
+    int32_t causal_tree;   // tree: straddling nodes scored from the cache's edge table
     int32_t H_q;
     int32_t G;
     int32_t H_kv;
@@ -83,9 +84,12 @@ constexpr int kBmUnitCap = 256;      // most buckets one unit may take through t
 constexpr int kBmCursors = 256;      // pool slices, so that the units' slot requests spread over many words
 
 hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
-                        const void* W, hipStream_t st);
+                        const void* W, hipStream_t st, int blk0 = 0);
 hipError_t launch_tree(const CacheView& cv, const int64_t* level_off, const int64_t* level_size, int B, int H_kv,
-                       hipStream_t st);
+                       hipStream_t st, int64_t first_leaf = 0);
+// Edge table of the tree: for every block boundary nb in [nb_first, n_blocks] and
+// level, the centroid of the node straddling leaf 64 nb, over its leaves below it.
+hipError_t launch_edges(const CacheView& cv, int B, int H_kv, int nb_first, hipStream_t st);
 hipError_t launch_qlatent(const void* Q, const void* W, bool bf16, int d, int64_t rows, void* qhat, int* counters,
                           void* zero, size_t zero_bytes, hipStream_t st);
 hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa, int B,

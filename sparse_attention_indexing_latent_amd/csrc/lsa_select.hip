@@ -1823,7 +1823,7 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
     wave_sync();
     for (int lev = top - 1; lev >= 0; --lev) {
         const int64_t n_lev = tree_level_size(cv.n_leaves, lev);
-        const int64_t lev_off = tree_level_off(cv.n_leaves, lev);
+        const int64_t lev_off = tree_level_off(cv.n_leaves_cap, lev);
         const int64_t span = (int64_t)1 << lev;
         const int ncand = 2 * nf;
         const int ntiles = (ncand + 15) / 16;
@@ -1850,9 +1850,13 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
                         b0[tt] = p[cent_tile_word(node, h, 0)];
                         b1[tt] = p[cent_tile_word(node, h, 1)];
                     } else {
-                        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.tcent) +
-                                                                        bg * cv.s_tcent + (lev_off + node) * kLatent +
-                                                                        16 * h);
+                        // a node straddling the visible leaves: its visible part's centroid (causal mode)
+                        const bool edge = sa.causal_tree && (node + 1) * span > NLv;
+                        const uint16_t* src =
+                            edge ? reinterpret_cast<const uint16_t*>(cv.edge) + bg * cv.s_edge +
+                                       ((int64_t)q.nvis * cv.n_lev_cap + lev) * kLatent
+                                 : reinterpret_cast<const uint16_t*>(cv.tcent) + bg * cv.s_tcent + (lev_off + node) * kLatent;
+                        const uint4* p = reinterpret_cast<const uint4*>(src + 16 * h);
                         b0[tt] = p[0];
                         b1[tt] = p[1];
                     }
@@ -1885,10 +1889,13 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
                 }
                 float sc = kNegInf;
                 if (node >= 0) {
+                    const bool edge = lev > 0 && sa.causal_tree && (node + 1) * span > NLv;
                     const float* base = lev == 0 ? reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent +
                                                        node * kLatent
-                                                 : reinterpret_cast<const float*>(cv.tcent) + bg * cv.s_tcent +
-                                                       (lev_off + node) * kLatent;
+                                        : edge ? reinterpret_cast<const float*>(cv.edge) + bg * cv.s_edge +
+                                                     ((int64_t)q.nvis * cv.n_lev_cap + lev) * kLatent
+                                               : reinterpret_cast<const float*>(cv.tcent) + bg * cv.s_tcent +
+                                                     (lev_off + node) * kLatent;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int hh = 4 * h + v;

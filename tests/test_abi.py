@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(decl) == set(_lib.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert L.lsa_abi_version() == 2
+    assert L.lsa_abi_version() == 3
 
 
 def test_status_strings():
@@ -68,11 +68,32 @@ def test_cache_bytes_and_describe():
     # a smaller T inside the same cache
     assert L.lsa_cache_describe(ctypes.byref(lay), 2, 1 << 20, 5000, ctypes.byref(info)) == 0
     assert info.n_blocks == 2 and info.n_leaves == 128 and info.n_levels == 8
-    # level offsets are consecutive
+    # level offsets depend on the capacity only: level l has room for ceil(leaves_max / 2^l) nodes
     offs = [info.level_off[i] for i in range(1, info.n_levels)]
-    sizes = [info.level_size[i] for i in range(1, info.n_levels)]
-    assert all(offs[i + 1] == offs[i] + sizes[i] for i in range(len(offs) - 1))
+    room = [-(-info.leaves_max // (1 << i)) for i in range(1, info.n_levels)]
+    assert all(offs[i + 1] == offs[i] + room[i] for i in range(len(offs) - 1))
+    full = CacheInfo()
+    assert L.lsa_cache_describe(ctypes.byref(lay), 2, 1 << 20, 1 << 20, ctypes.byref(full)) == 0
+    assert all(full.level_off[i] == info.level_off[i] for i in range(1, info.n_levels))
+    assert all(info.level_size[i] == -(-info.n_leaves // (1 << i)) for i in range(info.n_levels))
     assert L.lsa_cache_describe(ctypes.byref(lay), 2, 4096, 5000, ctypes.byref(info)) == 6
+
+
+def test_extend_validation_before_launch():
+    L = _lib.lib()
+    lay = _layout(build_tree=1)
+    fake = ctypes.c_void_p(0x1000)
+    # T_new below T_old, beyond t_cap, beyond t_max
+    assert L.lsa_extend_buckets(ctypes.byref(lay), fake, 1, 8192, 4096, 2048, fake, fake, 1 << 30, 8192, None) == 1
+    assert L.lsa_extend_buckets(ctypes.byref(lay), fake, 1, 4096, 2048, 6144, fake, fake, 1 << 30, 8192, None) == 6
+    assert L.lsa_extend_buckets(ctypes.byref(lay), fake, 1, 8192, 2048, 6144, fake, fake, 1 << 30, 4096, None) == 6
+    # NULL / misaligned pointers, cache too small
+    assert L.lsa_extend_buckets(ctypes.byref(lay), None, 1, 8192, 2048, 6144, fake, fake, 1 << 30, 8192, None) == 1
+    assert L.lsa_extend_buckets(ctypes.byref(lay), ctypes.c_void_p(0x1001), 1, 8192, 2048, 6144, fake, fake,
+                                1 << 30, 8192, None) == 4
+    assert L.lsa_extend_buckets(ctypes.byref(lay), fake, 1, 8192, 2048, 6144, fake, fake, 16, 8192, None) == 5
+    # nothing to do: no new full block
+    assert L.lsa_extend_buckets(ctypes.byref(lay), fake, 1, 8192, 4096, 5000, fake, fake, 1 << 30, 8192, None) == 0
 
 
 def test_build_validation_before_launch():

@@ -289,6 +289,37 @@ def test_tree_hand_checkable_beam_one():
     assert list(info["ranked"]) == [1]
 
 
+def test_causal_tree_equals_the_tree_over_the_visible_blocks():
+    """causal=True at position t is the plain tree search on the cache of the first nvis(t) blocks only
+    (ch.2: blocks are clustered as the keys stream in, so a decode step at t sees exactly that tree):
+    the truncated cache goes through build_tree, not through the partial-node sums."""
+    from synth import get_config, layer_inputs
+    cfg = get_config(1, T=2048 * 11 + 300)
+    inp = layer_inputs(cfg, seed=41)
+    W = inp["W"].double().numpy()
+    Kg = inp["K"][0, 0].double().numpy()
+    full = O.build_head_cache(Kg, W, "f32", tree=True, processes=8)
+    rng = np.random.default_rng(12)
+    changed = 0
+    for nvis in (3, 5, 6, 7, 9, 11):
+        trunc = O.build_head_cache(Kg[: nvis * 2048], W, "f32", tree=True, clusters=full["clusters"][:nvis])
+        for t in (nvis * 2048 + 17, nvis * 2048 + 2000):
+            q = O.round_to(O.normalise(rng.standard_normal((4, 64))), "f32")
+            for beam in (1, 3, 8):
+                a, _ = O.select_tree(q, full, t, 256, 4, 128, beam, causal=True)
+                b, _ = O.select_tree(q, trunc, t, 256, 4, 128, beam)
+                assert np.array_equal(a, b), (nvis, t, beam)
+                c, _ = O.select_tree(q, full, t, 256, 4, 128, beam)
+                changed += not np.array_equal(a, c)
+    print(f"[causal tree] {changed} of 36 selections differ from the stored-centroid search")
+    # the partial nodes do differ from the stored ones (the mode is not a no-op on this cache)
+    m = 64 * 5
+    lev = full["tree"][8]
+    j = (m - 1) // lev["span"]
+    part = O.round_to(O.normalise(full["sums"][j * lev["span"]: m].sum(axis=0)[None, :]), "f32")[0]
+    assert not np.allclose(part, lev["cent"][j])
+
+
 # ---------------------------------------------------------------- attention
 
 def _sdpa(q, K, V, mask, scale):
