@@ -529,9 +529,24 @@ def run_decode(args):
     cent_bytes = cfg.B * cfg.H_kv * nl * 64 * 2
     gather = cfg.B * cfg.H_kv * (int(cnt_c.clamp_min(0).sum()) / (cfg.B * cfg.H_kv) + cfg.window + cfg.n_sinks) * 512
     alg = cent_bytes + gather
+    # streaming growth: a block of 2048 new tokens per sequence clustered into the cache (every 2048 steps):
+    # the last block of each sequence re-added to a cache holding the ones before it
+    grow = lsa.build_buckets(G["K"], G["W"], T=cfg.T - 2048, t_max=cfg.T, n_q_heads=cfg.H_q)
+    grow_ms = []
+    for rep in range(6):
+        grow.T = cfg.T - 2048
+        torch.cuda.synchronize()
+        s.record()
+        lsa.extend_buckets(grow, G["K"], G["W"], cfg.T)
+        e.record()
+        torch.cuda.synchronize()
+        if rep > 0:
+            grow_ms.append(s.elapsed_time(e))
+    grow_block_ms = sum(grow_ms) / len(grow_ms)
     return dict(queries_per_s=cfg.B / (ms / 1e3), ms_per_step=ms, ms_per_step_eager=ms_eager, timing="hip graph replay",
                 needle_found=f"{found}/{cfg.B * cfg.H_kv}",
-                alg_bytes_per_step=alg, hbm_frac=(alg / (ms / 1e3) / 1e9) / HBM_PEAK_GBS)
+                alg_bytes_per_step=alg, hbm_frac=(alg / (ms / 1e3) / 1e9) / HBM_PEAK_GBS,
+                grow_block_ms=grow_block_ms, grow_us_per_step_amortized=grow_block_ms * 1e3 / 2048)
 
 
 def main():

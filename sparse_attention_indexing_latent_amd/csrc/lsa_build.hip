@@ -27,6 +27,30 @@ constexpr int kWardThreads = 512;
 constexpr int kRows = 16;             // broadcast rows per recompute round
 constexpr float kInf = __builtin_huge_valf();
 
+// Wave minimum of a 64-bit key with DPP moves (no LDS round trips): pairs
+// within quads, then halves and rows of 16 (mirrors), then rows 0+1 and
+// 2+3 (row broadcast of lane 15), then all four (broadcast of lane 31); the
+// minimum ends in lane 63 and is read from there by every lane.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const int dlo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false);
+    const int dhi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false);
+    return ((uint64_t)(uint32_t)dhi << 32) | (uint32_t)dlo;
+}
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return b < a ? b : a; }
+__device__ __forceinline__ uint64_t wave_min_u64_dpp(uint64_t v) {
+    v = min_u64(v, dpp_u64<0xB1, 0xF>(v));    // quad_perm [1,0,3,2]
+    v = min_u64(v, dpp_u64<0x4E, 0xF>(v));    // quad_perm [2,3,0,1]
+    v = min_u64(v, dpp_u64<0x141, 0xF>(v));   // row_half_mirror
+    v = min_u64(v, dpp_u64<0x140, 0xF>(v));   // row_mirror
+    v = min_u64(v, dpp_u64<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
+    v = min_u64(v, dpp_u64<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ uint64_t pair_key(float d, int id, int nn) {
     return ((uint64_t)__float_as_uint(d) << 32) | ((uint64_t)id << 16) | (uint64_t)nn;
 }
@@ -128,7 +152,7 @@ __global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restric
     const int n_merge = kBlockEntries - kLeavesPerBlock;
     for (int step = 0; step < n_merge; ++step) {
         uint64_t key = (act && nn >= 0) ? pair_key(nd, tid, nn) : ~0ull;
-        key = wave_min_u64(key);
+        key = wave_min_u64_dpp(key);
         if (lane == 0) red[wid] = key;
         if (tid == 0) nrows = 1;
         __syncthreads();
@@ -208,7 +232,7 @@ __global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restric
                     }
                 }
                 uint64_t k2 = (ok && tid > Kr) ? (((uint64_t)__float_as_uint(dl) << 32) | (uint64_t)tid) : ~0ull;
-                k2 = wave_min_u64(k2);
+                k2 = wave_min_u64_dpp(k2);
                 if (lane == 0) red2[wid][r] = k2;
             }
             __syncthreads();
