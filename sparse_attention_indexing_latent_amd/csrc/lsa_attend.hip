@@ -57,12 +57,13 @@ template <int D>
 __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t ul, int npl, int hh, int h,
                                                       float& m_run, float& l_run, f32x4* acc) {
     constexpr int NC = D / 16;
+    constexpr int MN = 4;   // partials in flight
     const int64_t s0 = aa.bm_off[ul];
-    for (int s = 0; s < npl; s += 4) {
-        f32x4 ml[4];
-        u32x2 o[4][NC];
+    for (int s = 0; s < npl; s += MN) {
+        f32x4 ml[MN];
+        u32x2 o[MN][NC];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < MN; ++j) {
             const int64_t slot = (s0 + (s + j < npl ? s + j : 0)) * aa.G + hh;
             ml[j] = *reinterpret_cast<const f32x4*>(aa.bm_ml + slot * 4);
             const uint16_t* po = aa.bm_po + slot * D;
@@ -71,7 +72,7 @@ __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t
                 o[j][c] = *reinterpret_cast<const u32x2*>(po + 32 * (c / 2) + 8 * h + 4 * (c % 2));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < MN; ++j) {
             const float mj = s + j < npl ? ml[j][0] : kNegInf;
             const float M = fmaxf(m_run, mj);
             const float a = m_run > kNegInf ? __expf(m_run - M) : 0.f;
