@@ -72,8 +72,9 @@ def prefill_step(cfg, G, ws, timers=None, tree=False, O=None):
     if tm:
         e.record()
     n_q = G["Q"].shape[1]
-    for i0 in range(0, n_q, CHUNK):
-        i1 = min(n_q, i0 + CHUNK)
+    chunk = ws.get("chunk", CHUNK)
+    for i0 in range(0, n_q, chunk):
+        i1 = min(n_q, i0 + chunk)
         Qc = G["Q"][:, i0:i1]
         qp = G["q_pos"][:, i0:i1]
         if tm:
@@ -269,12 +270,12 @@ def run_prefill(args, cid):
     ws["cache"] = cache0.buf
     attend = args.attend
     if attend != "gather":
-        # passes of up to --bm-pass queries, fewer if free memory is short (workspace <= 60% of it)
+        # passes of up to --bm-pass queries, fewer (in steps of 4096) if free memory is short (workspace <= --bm-mem of it)
         torch.cuda.empty_cache()
         free = torch.cuda.mem_get_info(dev)[0]
         n_pass = args.bm_pass
-        while n_pass > 1024 and lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass) > 0.6 * free:
-            n_pass //= 2
+        while n_pass > 4096 and lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass) > args.bm_mem * free:
+            n_pass -= 4096
         # auto: bucket-major when a bucket is expected in >= 2 pairs per pass (n_pass * k / T); measured:
         # ahead of the gather at 1M (64 per pass) and at 10M (3.2 per pass: 8.7 s vs 14.0 s per layer)
         if attend == "auto":
@@ -283,7 +284,10 @@ def run_prefill(args, cid):
             ws["bm"] = torch.empty(lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass),
                                    dtype=torch.uint8, device=dev)
             ws["bm_pass"] = n_pass
-            log(f"bucket-major attention, passes of {n_pass} queries, workspace {ws['bm'].numel() / 2**30:.1f} GiB")
+            # query chunks of whole passes (each select call feeds one attention call)
+            ws["chunk"] = n_pass * max(1, CHUNK // n_pass)
+            log(f"bucket-major attention, passes of {n_pass} queries, chunks of {ws['chunk']}, "
+                f"workspace {ws['bm'].numel() / 2**30:.1f} GiB")
     if attend == "gather":
         log("gather attention")
     ws["cnt_sum"] = 0
@@ -331,7 +335,7 @@ def run_prefill(args, cid):
         data="synthetic (seeded topic-mixture keys, random-init projection)",
         config={"workload": cfg.name, "T": cfg.T, "H_kv": cfg.H_kv, "H_q": cfg.H_q, "head_dim": cfg.d,
                 "k": cfg.k, "n_sinks": cfg.n_sinks, "window": cfg.window, "search": cfg.search,
-                "beam": cfg.beam, "query_chunk": CHUNK, "attention": attend,
+                "beam": cfg.beam, "query_chunk": ws.get("chunk", CHUNK), "attention": attend,
                 "bucket_pass": ws.get("bm_pass")},
         breakdown_ms={"build_buckets": timers["build"].total_ms() / args.steps,
                       "select": timers["select"].total_ms() / args.steps, "sparse_attend": att_ms},
@@ -560,6 +564,8 @@ def main():
                          "or auto (bucket-major when a bucket is expected in >= 2 pairs per pass)")
     ap.add_argument("--bm-pass", type=int, default=32768,
                     help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
+    ap.add_argument("--bm-mem", type=float, default=0.6,
+                    help="largest share of the free device memory the bucket-major workspace may take")
     ap.add_argument("--study", choices=["crossover"], default=None,
                     help="instead of the benchmark: the flat vs tree decode crossover over --cross-T x --cross-B")
     ap.add_argument("--cross-T", type=int, nargs="+", default=[1 << 20, 1 << 21, 1 << 22, 1 << 23, 10485760])

@@ -393,15 +393,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         // Software pipeline over 32-key tiles: the rows of the next tile are in
         // flight (registers) while the current one, staged through LDS, is
-        // computed; a tile's indices are fetched one step before its rows.
-        // A key outside [0, t] (malformed list) is never read nor scored.
+        // computed, and the indices of the tile after it are fetched then, so
+        // a row load never waits for its index load.  A key outside [0, t]
+        // (malformed list) is never read nor scored.
         uint8_t* buf = tile_lds + wid * TileLds<D>::BYTES;
         constexpr int NI = TileLds<D>::NI;
         int32_t tok = tok_of(kl, j0 + (l & 31), j1, t);
+        int32_t nxt = tok_of(kl, j0 + 32 + (l & 31), j1, t);
         u32x4 kR[NI], vR[NI];
         load_tile<D>(Kbg, Vbg, tok, kR, vR);
         for (int64_t j = j0; j < j1; j += 32) {
-            const int32_t nxt = tok_of(kl, j + 32 + (l & 31), j1, t);
+            const int32_t nn = tok_of(kl, j + 64 + (l & 31), j1, t);
             const uint64_t vm = __ballot(tok >= 0);   // bit r: tile row r valid (lanes 32..63 repeat 0..31)
             store_tile<D>(kR, vR, buf);
             load_tile<D>(Kbg, Vbg, nxt, kR, vR);   // past the end: masked rows (row 0), never used
@@ -409,6 +411,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 attend_tile<D>((uint32_t)(vm >> (4 * h)) & 0xFu, (uint32_t)(vm >> (16 + 4 * h)) & 0xFu, buf, r, qf,
                                ident, h, aa.scale, m_run, l_run, acc);
             tok = nxt;
+            nxt = nn;
         }
     }
     // acc[c][v] = unnormalised O[head n][32 (c/2) + 8h + 4 (c%2) + v]
