@@ -118,7 +118,7 @@ def selected_bytes(cfg, n_q_total, lr_total, q_pos_all, tile=64):
     return keys * 2 * row + 2 * n_q_total * cfg.H_q * row
 
 
-def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=8192):
+def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=2048):
     """Algorithmic HBM bytes of one bucket-major attention call over a chunk
     of queries, without the window part (added by selected_bytes' local term):
     per pass, the K and V rows of every distinct bucket any of its queries
