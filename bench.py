@@ -564,7 +564,7 @@ def main():
                          "or auto (bucket-major when a bucket is expected in >= 2 pairs per pass)")
     ap.add_argument("--bm-pass", type=int, default=32768,
                     help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
-    ap.add_argument("--bm-mem", type=float, default=0.6,
+    ap.add_argument("--bm-mem", type=float, default=0.72,
                     help="largest share of the free device memory the bucket-major workspace may take")
     ap.add_argument("--study", choices=["crossover"], default=None,
                     help="instead of the benchmark: the flat vs tree decode crossover over --cross-T x --cross-B")
