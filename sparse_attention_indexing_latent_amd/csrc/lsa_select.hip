@@ -1827,7 +1827,14 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
         const int64_t span = (int64_t)1 << lev;
         const int ncand = 2 * nf;
         const int ntiles = (ncand + 15) / 16;
-        if constexpr (BF16) {
+        if (lev > 0 && ncand <= sa.beam) {
+            // every visible child is kept whatever its score (only the leaves are ranked): no scoring
+            for (int c = l; c < ncand; c += 64) {
+                int64_t node = 2 * (int64_t)front[wid][c >> 1] + (c & 1);
+                if (node >= n_lev || node * span >= NLv) node = -1;
+                keys[wid][c] = node >= 0 ? rank_key(0.f, (uint32_t)node) : 0ull;
+            }
+        } else if constexpr (BF16) {
             // every candidate tile's centroid fragments are loaded before any is scored, so the
             // level waits for memory once
             constexpr int kTiles = 2 * LSA_MAX_BEAM / 16;
