@@ -43,6 +43,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A value from another lane of the same quad (DPP quad_perm; every lane of
+// the wave must be active).
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t quad_dpp64(uint64_t v) {
+    return ((uint64_t)quad_dpp<CTRL>((uint32_t)(v >> 32)) << 32) | quad_dpp<CTRL>((uint32_t)v);
+}
+
 __global__ __launch_bounds__(256) void bm_clear_kernel(uint32_t* __restrict__ p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
@@ -166,9 +177,23 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
                         lastb = -1;
                         continue;
                     }
-                    if ((take >> l) & 1ull) {
+                    // the key bits of a run of lanes with the same (slot, bucket) inside a lane quad (an
+                    // entry's 4 tokens, usually) are ORed first: one LDS atomic per run
+                    const bool tl = (take >> l) & 1ull;
+                    const uint32_t key = tl ? ((uint32_t)slot << 8) | (uint32_t)rank : 0xFFFFFFFFu;
+                    const uint64_t bits = tl ? 1ull << bit : 0ull;
+                    const int qi = l & 3;
+                    // (every DPP read runs with the whole wave active: a read from an inactive lane
+                    // would return the reader's own value)
+                    const uint32_t k1 = quad_dpp<0xF9>(key), k2 = quad_dpp<0xFE>(key), k3 = quad_dpp<0xFF>(key),
+                                   k0 = quad_dpp<0x90>(key);   // lanes + 1, + 2, + 3, - 1
+                    const uint64_t b1 = quad_dpp64<0xF9>(bits), b2 = quad_dpp64<0xFE>(bits), b3 = quad_dpp64<0xFF>(bits);
+                    const bool s1 = qi <= 2 && k1 == key, s2 = s1 && qi <= 1 && k2 == key, s3 = s2 && qi == 0 && k3 == key;
+                    const uint64_t comb = bits | (s1 ? b1 : 0ull) | (s2 ? b2 : 0ull) | (s3 ? b3 : 0ull);
+                    const bool head = qi == 0 || k0 != key;   // lane - 1 is another run
+                    if (tl) {
                         if ((newm >> l) & 1ull) tbl[wid][slot] = blk;
-                        atomicOr(&tab[wid][slot][rank], 1ull << bit);
+                        if (head) atomicOr(&tab[wid][slot][rank], comb);
                     }
                     const int last = 63 - __builtin_clzll(take);
                     used = __shfl(slot, last) + 1;
