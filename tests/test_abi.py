@@ -126,6 +126,7 @@ def test_select_validation_before_launch():
     assert call(SelectCfg(2048, 4, 128, 1, 0, 0)) == 6           # tree beam 0
     assert call(SelectCfg(2048, 4, 128, 1, 8, 0)) == 8           # tree on a cache without tree
     assert call(SelectCfg(2048, 4, 128, 0, 0, 9)) == 1           # unknown strategy
+    assert call(SelectCfg(2048, 4, 128, 0, 0, 0, 2)) == 1        # causal_tree not 0 or 1
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), ws=8) == 5     # workspace too small
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), T=9000) == 6   # T > t_max
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), cache_bytes=8) == 5

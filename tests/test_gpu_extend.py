@@ -37,12 +37,12 @@ def _regions(cache, tree):
     return out
 
 
-@pytest.mark.parametrize("dtype,tree", [("bf16", True), ("f32", False), ("f32", True)])
-def test_extend_equals_build(dtype, tree):
+@pytest.mark.parametrize("dtype,tree,B", [("bf16", True, 1), ("f32", False, 1), ("f32", True, 2)])
+def test_extend_equals_build(dtype, tree, B):
     if dtype == "bf16":
-        cfg = get_config(2, T=2048 * 7 + 300, H_kv=2, H_q=10, d=128, n_topics=32)
+        cfg = get_config(2, T=2048 * 7 + 300, H_kv=2, H_q=10, d=128, n_topics=32, B=B)
     else:
-        cfg = get_config(1, T=2048 * 7 + 300, H_kv=2, H_q=4, n_topics=32)
+        cfg = get_config(1, T=2048 * 7 + 300, H_kv=2, H_q=4, n_topics=32, B=B)
     inp = layer_inputs(cfg, seed=51, queries=False)
     K, W = inp["K"].to(DEV).contiguous(), inp["W"].to(DEV).contiguous()
     T = cfg.T
