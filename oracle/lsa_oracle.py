@@ -20,7 +20,7 @@ Sources (the pages' titles and sections):
   * zhichai.net explainer, ch.5 (the training-free D-LSA variant): the
     projection is taken as the leading 64 principal directions of the keys.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
   a block is 512 pooled entries = 2048 tokens; pooling is the plain mean of
   the 4 unit latents (no renormalisation); the Ward stop is ceil(n / 8)
   clusters, a merge is allowed only if the union has <= 16 entries, ties go to

@@ -5,6 +5,6 @@ method itself, so both the CPU oracle and the HIP path can consume what it
 makes without sharing any of the method's arithmetic.
 """
 
-from .topics import CONFIGS, LayerConfig, get_config, layer_inputs, decode_inputs, random_lr_lists
+from .topics import WORKLOADS, LayerConfig, get_config, layer_inputs, decode_inputs, random_lr_lists
 
-__all__ = ["CONFIGS", "LayerConfig", "get_config", "layer_inputs", "decode_inputs", "random_lr_lists"]
+__all__ = ["WORKLOADS", "LayerConfig", "get_config", "layer_inputs", "decode_inputs", "random_lr_lists"]

@@ -72,7 +72,7 @@ class LayerConfig:
 # The five workloads, in order: a tiny fp32 layer; prefill at 131,072 tokens;
 # a 16-sequence decode step at 1M context; prefill at 1M; prefill at 10M with
 # the tree search (beam = k / (4 * 8) leaves) plus an 8-query decode step.
-CONFIGS = {
+WORKLOADS = {
     1: LayerConfig(1, "tiny-f32-8k", 8192, 1, 4, 64, "f32", 32, 256, 4, 128, "flat"),
     2: LayerConfig(2, "prefill-131k", 131072, 8, 40, 128, "bf16", 512, 2048, 4, 1024, "flat"),
     3: LayerConfig(3, "decode-16x1m", 1048576, 8, 40, 128, "bf16", 4096, 2048, 4, 1024, "flat",
@@ -84,7 +84,7 @@ CONFIGS = {
 
 
 def get_config(cid: int, **overrides) -> LayerConfig:
-    cfg = CONFIGS[cid]
+    cfg = WORKLOADS[cid]
     return cfg.scaled(**overrides) if overrides else cfg
 
 
