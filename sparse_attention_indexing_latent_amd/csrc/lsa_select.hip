@@ -420,6 +420,7 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
 // by the finalize).  A query's list is 4 sub-lists of kSubCap slots, one per
 // lane of its MFMA column (no cross-lane step per append); their counts are
 // exact even past the cap.
+constexpr int kSelCap = 256;        // buckets one finalize wave may take (more: the exact path)
 constexpr int kScanQ = 128;         // queries per workgroup
 constexpr int kScanChunk = 8;       // tiles per staged chunk
 constexpr int kFNeg = 8;
@@ -1026,9 +1027,12 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
 }
 
 // Walk keys[0..n) (sorted by rank), pick the buckets until k eligible
-// tokens, sort the picks by id into sel[] and expand.  Returns the count.
-__device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int* tk, uint32_t* ent,
-                                                const CacheView& cv, int64_t bg, const Geom& q, int k, int32_t* out) {
+// tokens, sort the picks by id into sel[] (room for sel_cap) and expand.
+// Returns the count, or -1 with nothing written when more than sel_cap
+// buckets are needed.
+__device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int sel_cap, int* tk,
+                                                uint32_t* ent, const CacheView& cv, int64_t bg, const Geom& q, int k,
+                                                int32_t* out) {
     const int l = lane_id();
     int have = 0, nsel = 0;
     bool done = false;
@@ -1043,11 +1047,12 @@ __device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t*
         const bool take = w > 0 && before < k;
         const uint64_t bal = __ballot(take);
         const int pos = __popcll(bal & ((1ull << l) - 1ull));
-        if (take) sel[nsel + pos] = pack_sel(leaf, lmeta, w, cum <= k, k - before);
+        if (take && nsel + pos < sel_cap) sel[nsel + pos] = pack_sel(leaf, lmeta, w, cum <= k, k - before);
         nsel += __popcll(bal);
         have = __shfl(cum, 63);
         if (have >= k) done = true;
     }
+    if (nsel > sel_cap) return -1;   // more buckets than sel holds: nothing written, the caller falls back
     wave_sync();
     const int P = pow2_at_least(nsel);
     for (int j = nsel + l; j < P; j += 64) sel[j] = ~0ull;   // pads sort after every real entry
@@ -1094,7 +1099,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
                                                              const uint64_t* __restrict__ cand, int* fb_list,
                                                              int* counters, int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ __align__(16) uint64_t keys[4][kCandCap];
-    __shared__ uint64_t sel[4][kCandCap];
+    __shared__ uint64_t sel[4][kSelCap];
     __shared__ int tk[4][256];
     const int l = lane_id(), wid = threadIdx.x >> 6;
     const int64_t u = (int64_t)blockIdx.x * 4 + wid;
@@ -1143,8 +1148,15 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
     wave_sort_desc(keys[wid], P);
     const int64_t bg = un.b * sa.H_kv + un.g;
     // the rank keys are dead once the walk is done: their space holds the entry keys (<= k / 4)
-    const int got = wave_walk_expand(keys[wid], f, sel[wid], tk[wid], reinterpret_cast<uint32_t*>(keys[wid]), cv, bg,
-                                     q, sa.k, out);
+    const int got = wave_walk_expand(keys[wid], f, sel[wid], kSelCap, tk[wid], reinterpret_cast<uint32_t*>(keys[wid]),
+                                     cv, bg, q, sa.k, out);
+    if (got < 0) {   // many small buckets: the exact path takes the unit
+        if (l == 0) {
+            const int pos = atomicAdd(&counters[0], 1);
+            fb_list[pos] = (int)u;
+        }
+        return;
+    }
     write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
 }
@@ -1969,7 +1981,8 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
         }
         wave_sync();
     }
-    const int got = wave_walk_expand(keys[wid], nf, sel[wid], tk[wid], ent[wid], cv, bg, q, sa.k, out);
+    const int got = wave_walk_expand(keys[wid], nf, sel[wid], 2 * LSA_MAX_BEAM, tk[wid], ent[wid], cv, bg, q, sa.k,
+                                     out);   // nf <= beam buckets: never more than sel holds
     write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
 }
