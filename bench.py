@@ -123,8 +123,8 @@ def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=2048):
     of queries, without the window part (added by selected_bytes' local term):
     per pass, the K and V rows of every distinct bucket any of its queries
     listed, once; per (query, KV head, bucket) pair, the G query rows and
-    the partial row (G x (2 d + 16) bytes) written once and read once; the
-    long-range lists read once."""
+    the partial row (G x (3 d / 2 + 16) bytes: 12-bit values) written once
+    and read once; the long-range lists read once."""
     info = cache.info()
     nb = info.n_blocks
     eleaf = cache.entry_leaf()[0].long()                     # [H_kv, nb, 512]
@@ -151,7 +151,7 @@ def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=2048):
             u = torch.unique(torch.cat(seen))
             kv_rows += int((size.view(-1)[u] * 4).sum())
     row = d * 2
-    return (kv_rows * 2 * row + pairs * G * row + 2 * pairs * G * (2 * d + 16)
+    return (kv_rows * 2 * row + pairs * G * row + 2 * pairs * G * (3 * d // 2 + 16)
             + int(cnt.clamp_min(0).sum()) * 4)
 
 

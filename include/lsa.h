@@ -248,8 +248,8 @@ lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg
 /* Workspace bytes lsa_sparse_attend_bucket_major needs to process n_q_pass
  * queries per sequence in one pass (a cache for t_max tokens).  Host only.
  * Dominated by one partial per (query, KV head, bucket) pair (fp32 max,
- * denominator and scale, d fp16 values per head): about
- * 80 * (32 + G * (2 d + 16)) bytes per (query, KV head). */
+ * denominator and scale, d 12-bit values per head): about
+ * 80 * (32 + G * (3 d / 2 + 16)) bytes per (query, KV head). */
 lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg,
                                                    int64_t batch, int64_t n_q_pass, int64_t t_max, size_t* bytes);
 

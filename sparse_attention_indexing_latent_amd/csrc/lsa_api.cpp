@@ -236,7 +236,7 @@ void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) 
     w.off_rec = o;    o = align256(o + (size_t)pool * 16);
     w.off_srec = o;   o = align256(o + (size_t)pool * 16);
     w.off_work = o;   o = align256(o + (size_t)w.nbins * 17 * 16);
-    w.off_po = o;     o = align256(o + (size_t)pool * G * D * 2);
+    w.off_po = o;     o = align256(o + (size_t)pool * G * (3 * D / 2));   // 12-bit packed rows
     w.off_pml = o;    o = align256(o + (size_t)pool * G * 16);
     w.total = o;
 }
@@ -623,7 +623,7 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         bm.rec = reinterpret_cast<lsa::u32x4*>(wb + w.off_rec);
         bm.srec = reinterpret_cast<lsa::u32x4*>(wb + w.off_srec);
         bm.work = reinterpret_cast<lsa::u32x4*>(wb + w.off_work);
-        bm.po = reinterpret_cast<uint16_t*>(wb + w.off_po);
+        bm.po = reinterpret_cast<uint32_t*>(wb + w.off_po);
         bm.pml = reinterpret_cast<float*>(wb + w.off_pml);
         lsa::AttArgs aa;
         memset(&aa, 0, sizeof(aa));

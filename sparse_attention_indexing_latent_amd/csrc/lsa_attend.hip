@@ -57,19 +57,31 @@ template <int D>
 __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t ul, int npl, int hh, int h,
                                                       float& m_run, float& l_run, f32x4* acc) {
     constexpr int NC = D / 16;
+    constexpr int NW = kPartialWords<D>;
     constexpr int MN = 4;   // partials in flight
     const int64_t s0 = aa.bm_off[ul];
     for (int s = 0; s < npl; s += MN) {
         f32x4 ml[MN];
-        u32x2 o[MN][NC];
+        uint32_t w[MN][NW];
 #pragma unroll
         for (int j = 0; j < MN; ++j) {
             const int64_t slot = (s0 + (s + j < npl ? s + j : 0)) * aa.G + hh;
             ml[j] = *reinterpret_cast<const f32x4*>(aa.bm_ml + slot * 4);
-            const uint16_t* po = aa.bm_po + slot * D;
+            // this lane's run: dims 32m + 8h + [0,8), 12-bit values
+            const uint32_t* pw = aa.bm_po + slot * (4 * NW) + h * NW;
+            if constexpr (NW % 4 == 0) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-                o[j][c] = *reinterpret_cast<const u32x2*>(po + 32 * (c / 2) + 8 * h + 4 * (c % 2));
+                for (int x = 0; x < NW; x += 4) {
+                    const u32x4 t = *reinterpret_cast<const u32x4*>(pw + x);
+                    w[j][x] = t[0]; w[j][x + 1] = t[1]; w[j][x + 2] = t[2]; w[j][x + 3] = t[3];
+                }
+            } else {
+#pragma unroll
+                for (int x = 0; x < NW; x += 2) {
+                    const u32x2 t = *reinterpret_cast<const u32x2*>(pw + x);
+                    w[j][x] = t[0]; w[j][x + 1] = t[1];
+                }
+            }
         }
 #pragma unroll
         for (int j = 0; j < MN; ++j) {
@@ -80,10 +92,14 @@ __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t
             const float bs = b * ml[j][2];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const f32x4 oc = {(float)__builtin_bit_cast(_Float16, (uint16_t)(o[j][c][0] & 0xFFFFu)),
-                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(o[j][c][0] >> 16)),
-                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(o[j][c][1] & 0xFFFFu)),
-                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(o[j][c][1] >> 16))};
+                // acc[c][v] is value 4c + v of the run: high byte v of word c, nibble 4 (c % 2) + v of word NC + c / 2
+                const uint32_t hw = w[j][c], nw = w[j][NC + c / 2] >> (16 * (c % 2));
+                f32x4 oc;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int hi = (int)(hw << (24 - 8 * v)) >> 24;
+                    oc[v] = (float)((hi * 16) | (int)((nw >> (4 * v)) & 0xFu));
+                }
                 acc[c] = acc[c] * a + oc * bs;
             }
             l_run = l_run * a + ml[j][1] * b;

@@ -10,9 +10,12 @@
 // the (query, bucket) pairs are grouped by bucket: a workgroup stages one
 // bucket's keys and values in LDS once and runs the MFMAs for every query
 // that picked it, leaving one partial (fp32 max and denominator, the
-// unnormalised output per head as fp16 times an fp32 scale) per pair.  The gather kernel then attends sinks + window
-// and merges the unit's partials with a log-sum-exp combine.  The result is
-// the same attention; only the order of the softmax sums differs.
+// unnormalised output per head as 12-bit integers times an fp32 scale) per
+// pair.  The gather kernel then attends sinks + window and merges the unit's
+// partials with a log-sum-exp combine.  The result is the same attention up
+// to the order of the softmax sums and the rounding of the partials (at most
+// half a step of 1/2047 of the row's largest value, no more than fp16's
+// rounding of that value).
 //
 // Steps of one pass (queries [q0, q0 + nqp) of every sequence):
 //   pairs    one wave per unit: its sorted long-range list -> (bucket, 64-bit
@@ -33,9 +36,13 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+// two rounded integers (|x| < 2^15) as the 16-bit halves of a word
+__device__ __forceinline__ uint32_t pk_i16(float a, float b) {
+    return ((uint32_t)__float2int_rn(a) & 0xFFFFu) | ((uint32_t)__float2int_rn(b) << 16);
 }
+// bits 4..11 of both 16-bit halves, as two bytes; bits 0..3 of both, as two nibbles
+__device__ __forceinline__ uint32_t hi_bytes2(uint32_t p) { return ((p >> 4) & 0xFFu) | ((p >> 12) & 0xFF00u); }
+__device__ __forceinline__ uint32_t lo_nibbles2(uint32_t p) { return (p & 0xFu) | ((p >> 12) & 0xF0u); }
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -548,26 +555,38 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
             amax = fmaxf(amax, __shfl_xor(amax, 32));
             if (col) {
                 const int64_t slot = (int64_t)p * G + hh;
-                const float inv = amax > 0.f ? 1.0f / amax : 0.f;
-                uint16_t* po = bm.po + slot * D;
+                // q = round(o * 2047 / amax): |q| <= 2047
+                const float qs = amax > 0.f ? 2047.f * __builtin_amdgcn_rcpf(amax) : 0.f;
+                constexpr int NW = kPartialWords<D>;
+                uint32_t W[NW];
 #pragma unroll
                 for (int m = 0; m < NDT / 2; ++m) {
                     // lane h holds dims 32m + 4h + [0,4) (A) and 32m + 16 + 4h + [0,4) (B); lanes h, h^1
-                    // swap one of them so that each writes 8 consecutive dims (16 bytes, 64 contiguous
-                    // bytes per column and store instruction)
-                    const u32x2 A = u32x2{pk_f16(acc[2 * m][0] * inv, acc[2 * m][1] * inv),
-                                          pk_f16(acc[2 * m][2] * inv, acc[2 * m][3] * inv)};
-                    const u32x2 Bv = u32x2{pk_f16(acc[2 * m + 1][0] * inv, acc[2 * m + 1][1] * inv),
-                                           pk_f16(acc[2 * m + 1][2] * inv, acc[2 * m + 1][3] * inv)};
+                    // swap one of them so that each holds the 8 dims 32m + 8r + [0,8) of one reading lane r
+                    const u32x2 A = u32x2{pk_i16(acc[2 * m][0] * qs, acc[2 * m][1] * qs),
+                                          pk_i16(acc[2 * m][2] * qs, acc[2 * m][3] * qs)};
+                    const u32x2 Bv = u32x2{pk_i16(acc[2 * m + 1][0] * qs, acc[2 * m + 1][1] * qs),
+                                           pk_i16(acc[2 * m + 1][2] * qs, acc[2 * m + 1][3] * qs)};
                     const bool even = (h & 1) == 0;
                     const u32x2 send = even ? Bv : A;
                     const u32x2 got = u32x2{(uint32_t)__shfl_xor((int)send[0], 16), (uint32_t)__shfl_xor((int)send[1], 16)};
-                    if (even)
-                        *reinterpret_cast<u32x4*>(po + 32 * m + 4 * h) = u32x4{A[0], A[1], got[0], got[1]};
-                    else
-                        *reinterpret_cast<u32x4*>(po + 32 * m + 16 + 4 * (h - 1)) = u32x4{got[0], got[1], Bv[0], Bv[1]};
+                    const u32x4 v8 = even ? u32x4{A[0], A[1], got[0], got[1]} : u32x4{got[0], got[1], Bv[0], Bv[1]};
+                    W[2 * m] = hi_bytes2(v8[0]) | (hi_bytes2(v8[1]) << 16);
+                    W[2 * m + 1] = hi_bytes2(v8[2]) | (hi_bytes2(v8[3]) << 16);
+                    W[NDT + m] = lo_nibbles2(v8[0]) | (lo_nibbles2(v8[1]) << 8) | (lo_nibbles2(v8[2]) << 16) |
+                                 (lo_nibbles2(v8[3]) << 24);
                 }
-                if (h == 0) *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx, psum, amax, 0.f};
+                const int r = (h >> 1) + 2 * (h & 1);   // the reading lane whose dims this lane holds
+                uint32_t* pw = bm.po + slot * (4 * NW) + r * NW;
+                if constexpr (NW % 4 == 0) {
+#pragma unroll
+                    for (int w = 0; w < NW; w += 4)
+                        *reinterpret_cast<u32x4*>(pw + w) = u32x4{W[w], W[w + 1], W[w + 2], W[w + 3]};
+                } else {
+#pragma unroll
+                    for (int w = 0; w < NW; w += 2) *reinterpret_cast<u32x2*>(pw + w) = u32x2{W[w], W[w + 1]};
+                }
+                if (h == 0) *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx, psum, amax * (1.0f / 2047.f), 0.f};
             }
             rc = rn;
             rn = rnn;

@@ -47,8 +47,9 @@ struct AttArgs {
     // bucket-major merge (null bm_np: plain gather of the long-range list)
     const uint32_t* bm_off;       // [n_units] first partial slot of the unit
     const int32_t* bm_np;         // [n_units] partials of the unit; -1: gather its list instead
-    const uint16_t* bm_po;        // [slots, G, D] fp16: unnormalised partial output / its scale
-    const float* bm_ml;           // [slots, G, 4] partial max, denominator, scale (largest |output|), 0
+    const uint32_t* bm_po;        // [slots, G, 3D/8] words: unnormalised partial output / its scale, packed
+                                  //   12-bit integers (kPartialWords layout)
+    const float* bm_ml;           // [slots, G, 4] partial max, denominator, scale (largest |output| / 2047), 0
 };
 
 // Workspace of one bucket-major pass.  A "bin" is one bucket of one (b, g):
@@ -76,9 +77,18 @@ struct BmBuffers {
     u32x4* srec;               // [pool_cap] grouped by bin: (local unit, pair slot, key mask lo, hi)
     u32x4* work;               // [nbins, 17] one record per bin with pairs: (pair start, pairs, keys, b * H_kv + g),
                                //   then the bucket's 64 key tokens (member order; past the bucket: its first)
-    uint16_t* po;              // [pool_cap, G, D] fp16 partial outputs, divided by their scale
+    uint32_t* po;              // [pool_cap, G, 3D/8] packed 12-bit partial outputs (layout below)
     float* pml;                // [pool_cap, G, 4] (max, denominator, scale, 0)
 };
+// A partial output row of D values is stored as integers q = round(o / scale) with
+// scale = max |o| / 2047, so |q| <= 2047 fits 12 bits (worst-case error scale / 2, the
+// same as fp16's for the row's largest values).  The row is 4 runs of 3D/32 words,
+// run r holding the D/4 dims 32m + 8r + i (m < D/32, i < 8, value index 8m + i) of
+// one reading lane: first D/16 words of high bytes (bits 4..11 of q, two's
+// complement; value v in byte v % 4 of word v / 4), then D/32 words of low nibbles
+// (bits 0..3; value v in nibble v % 8 of word D/16 + v / 8).
+template <int D>
+constexpr int kPartialWords = 3 * D / 32;   // words of one run (one reading lane)
 constexpr int kBmScanChunk = 4096;   // bins per workgroup of the offset scan
 constexpr int kBmUnitCap = 256;      // most buckets one unit may take through the bucket-major path
 constexpr int kBmCursors = 256;      // pool slices, so that the units' slot requests spread over many words
