@@ -79,15 +79,19 @@ def prefill_step(cfg, G, ws, timers=None, tree=False, O=None):
         qp = G["q_pos"][:, i0:i1]
         if tm:
             e = tm["select"].span()
-        lr, cnt = lsa.select(Qc, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window,
-                             search="tree" if tree else "flat", beam=cfg.beam, workspace=ws.get("sel"),
-                             out=(ws["lr"][:, : i1 - i0], ws["cnt"][:, : i1 - i0]))
+        recs = "recs" in ws
+        res = lsa.select(Qc, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window,
+                         search="tree" if tree else "flat", beam=cfg.beam, workspace=ws.get("sel"),
+                         out=(ws["lr"][:, : i1 - i0], ws["cnt"][:, : i1 - i0])
+                         + ((ws["recs"][:, : i1 - i0], ws["rcnt"][:, : i1 - i0]) if recs else ()),
+                         bucket_records=recs)
+        lr, cnt = res[0], res[1]
         if tm:
             e.record()
             e = tm["attend"].span()
         if "bm" in ws:
             lsa.sparse_attend_bucket_major(Qc, G["K"], G["V"], qp, lr, cnt, cache, cfg.k, cfg.n_sinks, cfg.window,
-                                           O=O[:, i0:i1], workspace=ws["bm"])
+                                           O=O[:, i0:i1], workspace=ws["bm"], bucket_records=res[2] if recs else None)
         else:
             lsa.sparse_attend(Qc, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window,
                               O=O[:, i0:i1])
@@ -96,7 +100,7 @@ def prefill_step(cfg, G, ws, timers=None, tree=False, O=None):
         if "cnt_sum" in ws:
             ws["cnt_sum"] += int(cnt.clamp_min(0).sum().item())
             if "bm" in ws:
-                ws["bm_bytes"] += bucket_major_bytes(cfg, lr, cnt, cache, ws["bm_pass"])
+                ws["bm_bytes"] += bucket_major_bytes(cfg, lr, cnt, cache, ws["bm_pass"], records="recs" in ws)
     return cache
 
 
@@ -118,13 +122,14 @@ def selected_bytes(cfg, n_q_total, lr_total, q_pos_all, tile=64):
     return keys * 2 * row + 2 * n_q_total * cfg.H_q * row
 
 
-def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=2048):
+def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=2048, records=False):
     """Algorithmic HBM bytes of one bucket-major attention call over a chunk
     of queries, without the window part (added by selected_bytes' local term):
     per pass, the K and V rows of every distinct bucket any of its queries
     listed, once; per (query, KV head, bucket) pair, the G query rows and
     the partial row (G x (3 d / 2 + 16) bytes: 12-bit values) written once
-    and read once; the long-range lists read once."""
+    and read once; the long-range lists read once, or with the selection's
+    bucket records one 16-byte record per pair instead."""
     info = cache.info()
     nb = info.n_blocks
     eleaf = cache.entry_leaf()[0].long()                     # [H_kv, nb, 512]
@@ -151,8 +156,8 @@ def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=2048):
             u = torch.unique(torch.cat(seen))
             kv_rows += int((size.view(-1)[u] * 4).sum())
     row = d * 2
-    return (kv_rows * 2 * row + pairs * G * row + 2 * pairs * G * (3 * d // 2 + 16)
-            + int(cnt.clamp_min(0).sum()) * 4)
+    lists = pairs * 16 if records else int(cnt.clamp_min(0).sum()) * 4
+    return kv_rows * 2 * row + pairs * G * row + 2 * pairs * G * (3 * d // 2 + 16) + lists
 
 
 _CPU_CTX = {}
@@ -269,6 +274,10 @@ def run_prefill(args, cid):
     ws["sel"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws["cache"] = cache0.buf
     attend = args.attend
+    if attend != "gather" and args.bucket_records == "on":
+        # the selection's bucket records for the bucket-major attention (one chunk's worth)
+        ws["recs"] = torch.empty(1, CHUNK, cfg.H_kv, lsa._lib.BUCKET_RECS, 4, dtype=torch.int32, device=dev)
+        ws["rcnt"] = torch.empty(1, CHUNK, cfg.H_kv, dtype=torch.int32, device=dev)
     if attend != "gather":
         # passes of up to --bm-pass queries, fewer (in steps of 4096) if free memory is short (workspace <= --bm-mem of it)
         torch.cuda.empty_cache()
@@ -290,6 +299,8 @@ def run_prefill(args, cid):
                 f"workspace {ws['bm'].numel() / 2**30:.1f} GiB")
     if attend == "gather":
         log("gather attention")
+        ws.pop("recs", None)
+        ws.pop("rcnt", None)
     ws["cnt_sum"] = 0
     ws["bm_bytes"] = 0
     log("warmup")
@@ -336,7 +347,7 @@ def run_prefill(args, cid):
         config={"workload": cfg.name, "T": cfg.T, "H_kv": cfg.H_kv, "H_q": cfg.H_q, "head_dim": cfg.d,
                 "k": cfg.k, "n_sinks": cfg.n_sinks, "window": cfg.window, "search": cfg.search,
                 "beam": cfg.beam, "query_chunk": ws.get("chunk", CHUNK), "attention": attend,
-                "bucket_pass": ws.get("bm_pass")},
+                "bucket_pass": ws.get("bm_pass"), "bucket_records": "recs" in ws},
         breakdown_ms={"build_buckets": timers["build"].total_ms() / args.steps,
                       "select": timers["select"].total_ms() / args.steps, "sparse_attend": att_ms},
         roofline={"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -562,6 +573,9 @@ def main():
     ap.add_argument("--attend", default="auto", choices=["auto", "gather", "bucket"],
                     help="prefill attention: per-query gather, bucket-major (each bucket's K/V read once per pass), "
                          "or auto (bucket-major when a bucket is expected in >= 2 pairs per pass)")
+    ap.add_argument("--bucket-records", choices=["on", "off"], default="on",
+                    help="bucket-major attention takes its pairs from the selection's bucket records (on) or from "
+                         "the token lists (off); the same output")
     ap.add_argument("--bm-pass", type=int, default=32768,
                     help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
     ap.add_argument("--bm-mem", type=float, default=0.72,

@@ -59,7 +59,8 @@
 extern "C" {
 #endif
 
-#define LSA_ABI_VERSION 3
+#define LSA_BUCKET_RECS 256   /* bucket records per (query, KV head) in lsa_select's optional output */
+#define LSA_ABI_VERSION 4
 
 #define LSA_LATENT_DIM 64         /* latent width (ch.2: 64-d index space) */
 #define LSA_POOL 4                /* keys pooled per entry (ch.2)            */
@@ -220,12 +221,22 @@ lsa_status lsa_select_workspace_bytes(const lsa_layout* layout, const lsa_select
  * lr_cnt[b,i,g] = min(k, eligible tokens of the visible buckets).  A query
  * position outside [0, t_cap) of the K/V it will attend is not checked here;
  * positions < 0 give lr_cnt = -1.  T is the number of bucketed tokens the
- * cache was built with. */
+ * cache was built with.
+ * Optional (both NULL, or both set and 16-byte aligned): bucket_recs
+ * [batch, n_q, H_kv, LSA_BUCKET_RECS] records of four uint32 and bucket_cnt
+ * [batch, n_q, H_kv] int32, the same selection one record per selected
+ * bucket: {leaf id, key mask bits 0..31, bits 32..63, 0}, ascending in leaf
+ * id, where key j of a bucket is token 4 members[j / 4] + j % 4 of its block
+ * and is in lr_idx's row exactly when bit j is set.  bucket_cnt holds the
+ * number of records; it is -1 where the row came from the exact fallback, the
+ * materialized strategy or a trivial case (no ranking needed, or position
+ * < 0).  lsa_sparse_attend_bucket_major takes them in place of the token
+ * rows' bucket lookups. */
 lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache,
                       size_t cache_bytes, int64_t t_max, int64_t T, const void* Q,
                       const int64_t* q_pos, int64_t batch, int64_t n_q, const void* W_q,
-                      int32_t* lr_idx, int32_t* lr_cnt, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      int32_t* lr_idx, int32_t* lr_cnt, void* bucket_recs, int32_t* bucket_cnt,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes lsa_sparse_attend needs (split-key partial results). */
 lsa_status lsa_attend_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg,
@@ -261,7 +272,9 @@ lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, con
  * them, and the per-pair softmax partials are merged with the sinks + window
  * part by a log-sum-exp combine.  Outputs equal lsa_sparse_attend's up to
  * the order of the fp32 sums.  Arguments as for lsa_sparse_attend plus the
- * cache (built with T tokens for t_max) and a workspace of at least
+ * cache (built with T tokens for t_max; layout must be the one it was built
+ * with, build_tree included, since the cache's regions are found from it)
+ * and a workspace of at least
  * lsa_attend_bucket_major_workspace_bytes(.., 1, ..); the call then runs
  * ceil(n_q / P) passes, P the most queries the workspace holds.  A
  * (query, KV head) whose list is not strictly ascending, holds a token outside
@@ -269,13 +282,20 @@ lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, con
  * share of the pass's pair pool full is gathered whole instead (same result,
  * slower).  bf16 only
  * (LSA_ERR_UNSUPPORTED otherwise); lr_idx rows must not be modified while
- * the call's kernels run. */
+ * the call's kernels run.
+ * Optional bucket_recs / bucket_cnt (both NULL, or both set): the records
+ * lsa_select wrote with these rows.  A (query, KV head) with bucket_cnt >= 0
+ * takes its (query, bucket) pairs from its records instead of looking up
+ * every listed token: the same pairs in the same order, so the same output
+ * bit for bit.  If a record's bucket lies outside the blocks the query's
+ * long-range keys come from, or the masks' bits do not add up to the row's
+ * count, the row is used instead. */
 lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache,
                                           size_t cache_bytes, int64_t t_max, const void* Q, const void* K,
                                           const void* V, int64_t t_cap, int64_t T, const int64_t* q_pos,
                                           int64_t batch, int64_t n_q, const int32_t* lr_idx, const int32_t* lr_cnt,
-                                          float scale, void* O, void* workspace, size_t workspace_bytes,
-                                          void* stream);
+                                          const void* bucket_recs, const int32_t* bucket_cnt, float scale, void* O,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes lsa_pca_projection needs for this layout's head_dim.  Host only. */
 lsa_status lsa_pca_workspace_bytes(const lsa_layout* layout, size_t* bytes);

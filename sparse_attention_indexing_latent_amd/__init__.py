@@ -183,13 +183,17 @@ def select_workspace_bytes(cache: LsaCache, cfg: SelectCfg, n_q: int, n_q_heads:
 
 def select(Q: torch.Tensor, cache: LsaCache, q_pos: torch.Tensor, W_q: torch.Tensor, k: int, n_sinks: int,
            window: int, search: str = "flat", beam: int = 0, strategy: str = "auto",
-           workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None, causal_tree: bool = False):
+           workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None, causal_tree: bool = False,
+           bucket_records: bool = False):
     """Query side: score buckets, pick the top ones, expand to k tokens.
 
     Q: [B, n_q, H_q, d]; q_pos: int64 [B, n_q] on the GPU.  Returns
     (lr_idx int32 [B, n_q, H_kv, k] ascending, -1 padded; lr_cnt int32 [B, n_q, H_kv]).
     causal_tree (tree search): nodes straddling a query's visible leaves are scored by their visible
     part, as a decode step on a cache grown to the query's position would score them.
+    bucket_records: also return the selection as bucket records, (recs int32 [B, n_q, H_kv, 256, 4]:
+    leaf id, key mask low and high words, 0; counts int32 [B, n_q, H_kv], -1 where none), as a third
+    item; out may then hold four tensors.
     """
     assert Q.is_cuda and Q.is_contiguous() and q_pos.dtype == torch.int64 and q_pos.is_contiguous()
     B, n_q, H_q, d = Q.shape
@@ -201,8 +205,13 @@ def select(Q: torch.Tensor, cache: LsaCache, q_pos: torch.Tensor, W_q: torch.Ten
     if out is None:
         lr_idx = torch.empty(B, n_q, H_kv, k, dtype=torch.int32, device=Q.device)
         lr_cnt = torch.empty(B, n_q, H_kv, dtype=torch.int32, device=Q.device)
+        recs = rcnt = None
+        if bucket_records:
+            recs = torch.empty(B, n_q, H_kv, _lib.BUCKET_RECS, 4, dtype=torch.int32, device=Q.device)
+            rcnt = torch.empty(B, n_q, H_kv, dtype=torch.int32, device=Q.device)
     else:
-        lr_idx, lr_cnt = out
+        lr_idx, lr_cnt = out[0], out[1]
+        recs, rcnt = (out[2], out[3]) if bucket_records else (None, None)
     n = ctypes.c_size_t()
     _lib.check(L.lsa_select_workspace_bytes(ctypes.byref(layout), ctypes.byref(cfg), B, n_q, cache.t_max,
                                             ctypes.byref(n)))
@@ -210,8 +219,12 @@ def select(Q: torch.Tensor, cache: LsaCache, q_pos: torch.Tensor, W_q: torch.Ten
         workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=Q.device)
     _lib.check(L.lsa_select(ctypes.byref(layout), ctypes.byref(cfg), _ptr(cache.buf), cache.buf.numel(),
                             cache.t_max, cache.T, _ptr(Q), _ptr(q_pos), B, n_q, _ptr(W_q),
-                            _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt), _ptr(workspace),
+                            _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt),
+                            _ptr(recs) if bucket_records else ctypes.c_void_p(0),
+                            _ptr(rcnt) if bucket_records else ctypes.c_void_p(0), _ptr(workspace),
                             workspace.numel(), _stream(Q.device)))
+    if bucket_records:
+        return lr_idx, lr_cnt, (recs, rcnt)
     return lr_idx, lr_cnt
 
 
@@ -252,7 +265,8 @@ def sparse_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torc
 
 def attend_bucket_major_workspace_bytes(cache: LsaCache, n_q_heads: int, head_dim: int, n_q_pass: int) -> int:
     """Workspace bytes of one bucket-major pass over n_q_pass queries per sequence."""
-    layout = make_layout(head_dim, cache.layout.n_kv_heads, n_q_heads, torch.bfloat16)
+    layout = make_layout(head_dim, cache.layout.n_kv_heads, n_q_heads, torch.bfloat16,
+                         bool(cache.layout.build_tree))
     n = ctypes.c_size_t()
     _lib.check(_lib.lib().lsa_attend_bucket_major_workspace_bytes(ctypes.byref(layout),
                                                                   ctypes.byref(select_cfg(0, 0, 1)), cache.batch,
@@ -263,15 +277,19 @@ def attend_bucket_major_workspace_bytes(cache: LsaCache, n_q_heads: int, head_di
 def sparse_attend_bucket_major(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torch.Tensor,
                                lr_idx: torch.Tensor, lr_cnt: torch.Tensor, cache: LsaCache, k: int, n_sinks: int,
                                window: int, scale: Optional[float] = None, O: Optional[torch.Tensor] = None,
-                               workspace: Optional[torch.Tensor] = None, n_q_pass: int = 16384) -> torch.Tensor:
+                               workspace: Optional[torch.Tensor] = None, n_q_pass: int = 16384,
+                               bucket_records: Optional[tuple] = None) -> torch.Tensor:
     """sparse_attend computed bucket-major (bf16): same outputs, each bucket's K/V read once per pass.
 
-    Without a workspace, one for passes of min(n_q, n_q_pass) queries is allocated.
+    Without a workspace, one for passes of min(n_q, n_q_pass) queries is allocated.  bucket_records:
+    the (recs, counts) select returned with these lists (pairs taken from them; same output).
     """
     assert Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()
     B, n_q, H_q, d = Q.shape
     _, H_kv, t_cap, _ = K.shape
-    layout = make_layout(d, H_kv, H_q, Q.dtype)
+    # the cache's own layout (build_tree included): the call finds the cache's regions from it
+    assert cache.layout.head_dim == d and cache.layout.n_kv_heads == H_kv
+    layout = make_layout(d, H_kv, H_q, Q.dtype, bool(cache.layout.build_tree))
     cfg = select_cfg(k, n_sinks, window)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if O is None:
@@ -282,6 +300,8 @@ def sparse_attend_bucket_major(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
     _lib.check(_lib.lib().lsa_sparse_attend_bucket_major(
         ctypes.byref(layout), ctypes.byref(cfg), _ptr(cache.buf), cache.buf.numel(), cache.t_max, _ptr(Q), _ptr(K),
         _ptr(V), t_cap, cache.T, _ptr(q_pos), B, n_q, _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt),
+        _ptr(bucket_records[0]) if bucket_records is not None else ctypes.c_void_p(0),
+        _ptr(bucket_records[1]) if bucket_records is not None else ctypes.c_void_p(0),
         ctypes.c_float(scale), _ptr(O), _ptr(workspace), workspace.numel(), _stream(Q.device)))
     return O
 

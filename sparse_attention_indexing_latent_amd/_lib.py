@@ -27,6 +27,7 @@ LEAVES_PER_BLOCK = 64
 MAX_GROUP = 8
 MAX_K = 4096
 MAX_BEAM = 64
+BUCKET_RECS = 256
 
 STATUS_NAMES = {
     0: "LSA_OK", 1: "LSA_ERR_INVALID_ARG", 2: "LSA_ERR_SHAPE", 3: "LSA_ERR_DTYPE", 4: "LSA_ERR_ALIGN",
@@ -89,13 +90,14 @@ def lib():
     L.lsa_build_buckets.argtypes = [P(Layout), vp, i64, i64, i64, vp, vp, sz, i64, vp]
     L.lsa_extend_buckets.argtypes = [P(Layout), vp, i64, i64, i64, i64, vp, vp, sz, i64, vp]
     L.lsa_select_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, i64, P(sz)]
-    L.lsa_select.argtypes = [P(Layout), P(SelectCfg), vp, sz, i64, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp]
+    L.lsa_select.argtypes = [P(Layout), P(SelectCfg), vp, sz, i64, i64, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, sz,
+                             vp]
     L.lsa_attend_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, P(sz)]
     L.lsa_sparse_attend.argtypes = [P(Layout), P(SelectCfg), vp, vp, vp, i64, i64, vp, i64, i64, vp, vp,
                                     ctypes.c_float, vp, vp, sz, vp]
     L.lsa_attend_bucket_major_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, i64, P(sz)]
     L.lsa_sparse_attend_bucket_major.argtypes = [P(Layout), P(SelectCfg), vp, sz, i64, vp, vp, vp, i64, i64, vp,
-                                                 i64, i64, vp, vp, ctypes.c_float, vp, vp, sz, vp]
+                                                 i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     L.lsa_pca_workspace_bytes.argtypes = [P(Layout), P(sz)]
     L.lsa_pca_projection.argtypes = [P(Layout), vp, i64, i64, i64, vp, vp, vp, sz, vp]
     for name in ("lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_extend_buckets",

@@ -422,8 +422,8 @@ lsa_status lsa_select_workspace_bytes(const lsa_layout* layout, const lsa_select
 
 lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache, size_t cache_bytes,
                       int64_t t_max, int64_t T, const void* Q, const int64_t* q_pos, int64_t batch, int64_t n_q,
-                      const void* W_q, int32_t* lr_idx, int32_t* lr_cnt, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      const void* W_q, int32_t* lr_idx, int32_t* lr_cnt, void* bucket_recs, int32_t* bucket_cnt,
+                      void* workspace, size_t workspace_bytes, void* stream) {
     lsa_status s = check_layout(layout);
     if (s) return s;
     if (batch < 0 || n_q < 0 || T < 0 || t_max < 0) return fail(LSA_ERR_INVALID_ARG, "sizes must be >= 0");
@@ -436,8 +436,11 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     if (units == 0) return ok();
     if (!cache || !Q || !q_pos || !W_q || !lr_cnt || (!lr_idx && cfg->k > 0) || !workspace)
         return fail(LSA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if ((bucket_recs == nullptr) != (bucket_cnt == nullptr))
+        return fail(LSA_ERR_INVALID_ARG, "bucket_recs and bucket_cnt must both be NULL or both be set");
     if (misaligned(cache) || misaligned(Q) || misaligned(q_pos) || misaligned(W_q) || misaligned(lr_cnt) ||
-        (lr_idx && misaligned(lr_idx)) || misaligned(workspace))
+        (lr_idx && misaligned(lr_idx)) || misaligned(workspace) || (bucket_recs && misaligned(bucket_recs)) ||
+        (bucket_cnt && misaligned(bucket_cnt)))
         return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
     CacheGeom c;
     cache_geom(layout, batch, t_max, T, c);
@@ -470,9 +473,13 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     sa.G = layout->n_q_heads / layout->n_kv_heads;
     sa.n_q = n_q;
     sa.n_units = units;
+    sa.brec = static_cast<lsa::u32x4*>(bucket_recs);
+    sa.bcnt = bucket_cnt;
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t* lr = lr_idx ? lr_idx : lr_cnt;  // k == 0: rows are empty, never written
-    hipError_t e = lsa::launch_qlatent(Q, W_q, bf16, layout->head_dim, batch * n_q * layout->n_q_heads, sb.qhat,
+    hipError_t e = bucket_cnt ? lsa::launch_fill_i32(bucket_cnt, units, -1, st) : hipSuccess;
+    if (e == hipSuccess)
+        e = lsa::launch_qlatent(Q, W_q, bf16, layout->head_dim, batch * n_q * layout->n_q_heads, sb.qhat,
                                        sb.counters, wb + w.zero_off, w.zero_bytes, st);
     if (e == hipSuccess) {
         if (cfg->search == LSA_SEARCH_TREE)
@@ -566,8 +573,8 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
                                           size_t cache_bytes, int64_t t_max, const void* Q, const void* K,
                                           const void* V, int64_t t_cap, int64_t T, const int64_t* q_pos,
                                           int64_t batch, int64_t n_q, const int32_t* lr_idx, const int32_t* lr_cnt,
-                                          float scale, void* O, void* workspace, size_t workspace_bytes,
-                                          void* stream) {
+                                          const void* bucket_recs, const int32_t* bucket_cnt, float scale, void* O,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
     lsa_status s = check_layout(layout);
     if (s) return s;
     if (!cfg) return fail(LSA_ERR_INVALID_ARG, "cfg is NULL");
@@ -582,8 +589,11 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
     if (units == 0) return ok();
     if (!cache || !Q || !K || !V || !q_pos || !lr_cnt || (!lr_idx && cfg->k > 0) || !O || !workspace)
         return fail(LSA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if ((bucket_recs == nullptr) != (bucket_cnt == nullptr))
+        return fail(LSA_ERR_INVALID_ARG, "bucket_recs and bucket_cnt must both be NULL or both be set");
     if (misaligned(cache) || misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(q_pos) ||
-        misaligned(lr_cnt) || (lr_idx && misaligned(lr_idx)) || misaligned(O) || misaligned(workspace))
+        misaligned(lr_cnt) || (lr_idx && misaligned(lr_idx)) || misaligned(O) || misaligned(workspace) ||
+        (bucket_recs && misaligned(bucket_recs)) || (bucket_cnt && misaligned(bucket_cnt)))
         return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
     CacheGeom c;
     cache_geom(layout, batch, t_max, T, c);
@@ -646,6 +656,8 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         aa.bm_np = bm.unit_np;
         aa.bm_po = bm.po;
         aa.bm_ml = bm.pml;
+        aa.bm_brec = static_cast<const lsa::u32x4*>(bucket_recs);
+        aa.bm_bcnt = bucket_cnt;
         const int32_t* lr = lr_idx ? lr_idx : lr_cnt;
         hipError_t e = lsa::launch_bucket_partials(v, Q, K, V, q_pos, lr, lr_cnt, aa, bm, layout->head_dim, st);
         if (e == hipSuccess)

@@ -124,7 +124,34 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
     int np = 0;
     bool bad = false;
     const int64_t bg = b * aa.H_kv + g;
-    if (t >= 0 && cnt > 0) {
+    const int32_t nrec = (aa.bm_bcnt != nullptr && t >= 0 && cnt > 0) ? aa.bm_bcnt[u] : -1;
+    if (nrec >= 0) {
+        // the selection's bucket records: one pair per record, in the order the list gives them
+        // (ascending leaf), checked against the query's long-range blocks and the row's count
+        const Geom q = query_geom(t, aa.n_blocks, aa.n_sinks, aa.window);
+        const u32x4* rr = aa.bm_brec + u * LSA_BUCKET_RECS;
+        int keys = 0;
+        bool fine = nrec <= kBmUnitCap;   // wave-uniform, as every quantity below
+        for (int c0 = 0; fine && c0 < nrec; c0 += 64) {
+            const int i = c0 + l;
+            const bool live = i < nrec;
+            const u32x4 r = live ? rr[i] : u32x4{0u, 0u, 0u, 0u};
+            const int blk = (int)(r[0] / kLeavesPerBlock);
+            const unsigned long long m = ((unsigned long long)r[2] << 32) | r[1];
+            const bool good = blk < aa.n_blocks && (int64_t)blk * kBlockTokens < q.l0 &&
+                              (int64_t)(blk + 1) * kBlockTokens > q.sink_end && m != 0ull;
+            if (live && good) {
+                pl[wid][i] = r[0];
+                pm[wid][i] = m;
+            }
+            keys += live && good ? __popcll(m) : 0;
+            if (__ballot(live && !good) != 0ull) fine = false;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) keys += __shfl_xor(keys, o);
+        bad = !fine || keys != cnt;
+        np = nrec;
+    } else if (t >= 0 && cnt > 0) {
         const Geom q = query_geom(t, aa.n_blocks, aa.n_sinks, aa.window);
         const int32_t* lr = lr_idx + u * aa.k;
         const uint8_t* el = cv.eleaf + bg * cv.s_eleaf;

@@ -19,6 +19,8 @@ struct SelArgs {
     int32_t H_kv;
     int64_t n_q;
     int64_t n_units;   // B * n_q * H_kv
+    u32x4* brec;       // optional: [n_units, LSA_BUCKET_RECS] bucket records of the selection
+    int32_t* bcnt;     // optional: [n_units] their count (-1: none; the caller fills -1 first)
 };
 
 struct SelectBuffers {
@@ -50,6 +52,8 @@ struct AttArgs {
     const uint32_t* bm_po;        // [slots, G, 3D/8] words: unnormalised partial output / its scale, packed
                                   //   12-bit integers (kPartialWords layout)
     const float* bm_ml;           // [slots, G, 4] partial max, denominator, scale (largest |output| / 2047), 0
+    const u32x4* bm_brec;         // optional: [units of the call, LSA_BUCKET_RECS] the selection's bucket records
+    const int32_t* bm_bcnt;       // optional: their counts (-1: derive the pairs from the list)
 };
 
 // Workspace of one bucket-major pass.  A "bin" is one bucket of one (b, g):
@@ -113,6 +117,7 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V, const int6
                          const int32_t* lr_cnt, const AttArgs& aa, int D, bool bf16, void* O, float* part,
                          hipStream_t st);
 size_t pca_workspace_bytes(int D);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 hipError_t launch_pca(const void* K, bool bf16, int D, int64_t t_cap, int64_t T, int BH, void* W, float* eig,
                       void* workspace, hipStream_t st);
 hipError_t launch_attend_local(const void* Q, const void* K, const void* V, const int64_t* q_pos,

@@ -1026,13 +1026,47 @@ __device__ __forceinline__ int wave_expand(const uint64_t* sel, int nsel, const 
     return total;
 }
 
+// The selection as bucket records (sel[0..nsel), ascending leaf id): per
+// bucket {leaf, key mask lo, hi, 0}, key j being token 4 members[j/4] + j%4
+// of its block.  The mask holds the bucket's eligible keys (tokens in
+// [sink_end, l0)); for the partially taken bucket, the lowest `take` of them,
+// the same tokens expand_block_scan emits for it.
+__device__ __forceinline__ void write_bucket_records(const uint64_t* sel, int nsel, const CacheView& cv, int64_t bg,
+                                                     const Geom& q, u32x4* rec, int32_t* rcnt) {
+    const int l = lane_id();
+    for (int i = l; i < nsel; i += 64) {
+        const uint64_t sv = sel[i];
+        const uint32_t leaf = sel_leaf(sv);
+        const int blk = (int)(leaf / kLeavesPerBlock), sz = sel_size(sv);
+        const int64_t lo = (int64_t)blk * kBlockTokens;
+        uint64_t m = 0ull;
+        if (lo >= q.sink_end && lo + kBlockTokens <= q.l0) {
+            m = sz >= 16 ? ~0ull : (1ull << (kPool * sz)) - 1ull;
+        } else {
+            uint16_t e[16];
+            load_members(cv.members + bg * cv.s_members + (int64_t)blk * kBlockEntries, sel_off(sv), e);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t t0 = lo + (int64_t)e[j] * kPool;
+#pragma unroll
+                for (int x = 0; x < kPool; ++x)
+                    if (j < sz && t0 + x >= q.sink_end && t0 + x < q.l0) m |= 1ull << (kPool * j + x);
+            }
+        }
+        if (!sel_full(sv))
+            for (int drop = __popcll(m) - (int)(sv & 0x7F); drop > 0; --drop) m &= ~(1ull << (63 - __builtin_clzll(m)));
+        rec[i] = u32x4{leaf, (uint32_t)m, (uint32_t)(m >> 32), 0u};
+    }
+    if (l == 0) *rcnt = nsel;
+}
+
 // Walk keys[0..n) (sorted by rank), pick the buckets until k eligible
-// tokens, sort the picks by id into sel[] (room for sel_cap) and expand.
-// Returns the count, or -1 with nothing written when more than sel_cap
-// buckets are needed.
+// tokens, sort the picks by id into sel[] (room for sel_cap) and expand;
+// with rec, also write the picks as bucket records.  Returns the count, or
+// -1 with nothing written when more than sel_cap buckets are needed.
 __device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int sel_cap, int* tk,
                                                 uint32_t* ent, const CacheView& cv, int64_t bg, const Geom& q, int k,
-                                                int32_t* out) {
+                                                int32_t* out, u32x4* rec, int32_t* rcnt) {
     const int l = lane_id();
     int have = 0, nsel = 0;
     bool done = false;
@@ -1063,6 +1097,7 @@ __device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t*
     wave_sort_desc(sel, P);
     for (int j = l; j < P; j += 64) sel[j] = ~sel[j];
     wave_sync();
+    if (rec != nullptr) write_bucket_records(sel, nsel, cv, bg, q, rec, rcnt);
     return wave_expand(sel, nsel, cv, bg, q, out, tk, ent);
 }
 
@@ -1149,7 +1184,8 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
     const int64_t bg = un.b * sa.H_kv + un.g;
     // the rank keys are dead once the walk is done: their space holds the entry keys (<= k / 4)
     const int got = wave_walk_expand(keys[wid], f, sel[wid], kSelCap, tk[wid], reinterpret_cast<uint32_t*>(keys[wid]),
-                                     cv, bg, q, sa.k, out);
+                                     cv, bg, q, sa.k, out, sa.brec ? sa.brec + u * LSA_BUCKET_RECS : nullptr,
+                                     sa.bcnt ? sa.bcnt + u : nullptr);
     if (got < 0) {   // many small buckets: the exact path takes the unit
         if (l == 0) {
             const int pos = atomicAdd(&counters[0], 1);
@@ -1985,10 +2021,17 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
         }
         wave_sync();
     }
+    // nf <= beam buckets: never more than sel holds
     const int got = wave_walk_expand(keys[wid], nf, sel[wid], 2 * LSA_MAX_BEAM, tk[wid], ent[wid], cv, bg, q, sa.k,
-                                     out);   // nf <= beam buckets: never more than sel holds
+                                     out, sa.brec ? sa.brec + u * LSA_BUCKET_RECS : nullptr,
+                                     sa.bcnt ? sa.bcnt + u : nullptr);
     write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
+}
+
+// p[0..n) = v (grid-stride)
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
 }  // namespace
@@ -2018,6 +2061,13 @@ hipError_t launch_qlatent(const void* Q, const void* W, bool bf16, int d, int64_
     } else
         hipLaunchKernelGGL(qlatent_kernel<float>, dim3(grid), dim3(256), 0, st, static_cast<const float*>(Q),
                            static_cast<const float*>(W), d, rows, qhat, 0, counters, z, zero_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const unsigned g = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(g), dim3(256), 0, st, p, n, v);
     return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(decl) == set(_lib.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert L.lsa_abi_version() == 3
+    assert L.lsa_abi_version() == 4
 
 
 def test_status_strings():
@@ -116,9 +116,9 @@ def test_select_validation_before_launch():
     lay = _layout()
     fake = ctypes.c_void_p(0x1000)
 
-    def call(cfg, lay=lay, ws=1 << 30, cache_bytes=1 << 30, T=8192):
+    def call(cfg, lay=lay, ws=1 << 30, cache_bytes=1 << 30, T=8192, recs=None, rcnt=None):
         return L.lsa_select(ctypes.byref(lay), ctypes.byref(cfg), fake, cache_bytes, 8192, T, fake, fake, 1, 4,
-                            fake, fake, fake, fake, ws, None)
+                            fake, fake, fake, recs, rcnt, fake, ws, None)
 
     assert call(SelectCfg(2048, 4, 0, 0, 0, 0)) == 1             # window 0
     assert call(SelectCfg(-1, 4, 128, 0, 0, 0)) == 1             # negative k
@@ -130,6 +130,8 @@ def test_select_validation_before_launch():
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), ws=8) == 5     # workspace too small
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), T=9000) == 6   # T > t_max
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), cache_bytes=8) == 5
+    assert call(SelectCfg(2048, 4, 128, 0, 0, 0), recs=fake) == 1                           # records without counts
+    assert call(SelectCfg(2048, 4, 128, 0, 0, 0), recs=fake, rcnt=ctypes.c_void_p(0x1004)) == 4   # misaligned
     # k >= T is allowed even above LSA_MAX_K (every eligible token)
     n = ctypes.c_size_t()
     assert L.lsa_select_workspace_bytes(ctypes.byref(lay), ctypes.byref(SelectCfg(8192, 4, 128, 0, 0, 0)), 1, 4,
@@ -142,7 +144,7 @@ def test_empty_calls_are_no_ops():
     cfg = SelectCfg(2048, 4, 1024, 0, 0, 0)
     # zero queries: nothing to do, no pointer is touched
     assert L.lsa_select(ctypes.byref(lay), ctypes.byref(cfg), None, 0, 0, 0, None, None, 1, 0, None, None, None,
-                        None, 0, None) == 0
+                        None, None, None, 0, None) == 0
     assert L.lsa_sparse_attend(ctypes.byref(lay), ctypes.byref(cfg), None, None, None, 0, 0, None, 0, 5, None, None,
                                ctypes.c_float(0.1), None, None, 0, None) == 0
 

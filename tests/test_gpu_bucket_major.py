@@ -86,6 +86,18 @@ def test_bucket_major_on_selection(bm):
     assert err <= tol_for("bf16")
 
 
+def test_bucket_major_on_a_cache_with_tree(bm):
+    """A cache built with the tree holds the same buckets at other offsets: the same output, bit for bit (the
+    call must locate the entry maps from the cache's own layout)."""
+    cfg, G = bm["cfg"], bm["G"]
+    tcache = lsa.build_buckets(G["K"], G["W"], n_q_heads=cfg.H_q, build_tree=True)
+    args = (G["Q"], G["K"], G["V"], G["q_pos"], bm["lr"], bm["cnt"])
+    plain = lsa.sparse_attend_bucket_major(*args, bm["cache"], cfg.k, cfg.n_sinks, cfg.window)
+    tree = lsa.sparse_attend_bucket_major(*args, tcache, cfg.k, cfg.n_sinks, cfg.window)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, tree)
+
+
 def test_bucket_major_passes_bit_identical(bm):
     """Splitting the queries into passes changes nothing: each pair's partial and each unit's merge order
     are independent of the pass."""
