@@ -80,11 +80,13 @@ def prefill_step(cfg, G, ws, timers=None, tree=False, O=None):
         if tm:
             e = tm["select"].span()
         recs = "recs" in ws
+        # rows with records need no token list, except in the step that counts the algorithmic bytes
+        skip = recs and ws.get("skip_lists", False) and "cnt_sum" not in ws
         res = lsa.select(Qc, cache, qp, G["W"], cfg.k, cfg.n_sinks, cfg.window,
                          search="tree" if tree else "flat", beam=cfg.beam, workspace=ws.get("sel"),
                          out=(ws["lr"][:, : i1 - i0], ws["cnt"][:, : i1 - i0])
                          + ((ws["recs"][:, : i1 - i0], ws["rcnt"][:, : i1 - i0]) if recs else ()),
-                         bucket_records=recs)
+                         bucket_records=recs, skip_recorded_lists=skip)
         lr, cnt = res[0], res[1]
         if tm:
             e.record()
@@ -274,7 +276,8 @@ def run_prefill(args, cid):
     ws["sel"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws["cache"] = cache0.buf
     attend = args.attend
-    if attend != "gather" and args.bucket_records == "on":
+    if attend != "gather" and args.bucket_records != "off":
+        ws["skip_lists"] = args.bucket_records == "only"
         # the selection's bucket records for the bucket-major attention (one chunk's worth)
         ws["recs"] = torch.empty(1, CHUNK, cfg.H_kv, lsa._lib.BUCKET_RECS, 4, dtype=torch.int32, device=dev)
         ws["rcnt"] = torch.empty(1, CHUNK, cfg.H_kv, dtype=torch.int32, device=dev)
@@ -301,6 +304,7 @@ def run_prefill(args, cid):
         log("gather attention")
         ws.pop("recs", None)
         ws.pop("rcnt", None)
+        ws.pop("skip_lists", None)
     ws["cnt_sum"] = 0
     ws["bm_bytes"] = 0
     log("warmup")
@@ -347,7 +351,8 @@ def run_prefill(args, cid):
         config={"workload": cfg.name, "T": cfg.T, "H_kv": cfg.H_kv, "H_q": cfg.H_q, "head_dim": cfg.d,
                 "k": cfg.k, "n_sinks": cfg.n_sinks, "window": cfg.window, "search": cfg.search,
                 "beam": cfg.beam, "query_chunk": ws.get("chunk", CHUNK), "attention": attend,
-                "bucket_pass": ws.get("bm_pass"), "bucket_records": "recs" in ws},
+                "bucket_pass": ws.get("bm_pass"),
+                "bucket_records": ("only" if ws.get("skip_lists") else "on") if "recs" in ws else "off"},
         breakdown_ms={"build_buckets": timers["build"].total_ms() / args.steps,
                       "select": timers["select"].total_ms() / args.steps, "sparse_attend": att_ms},
         roofline={"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -573,9 +578,10 @@ def main():
     ap.add_argument("--attend", default="auto", choices=["auto", "gather", "bucket"],
                     help="prefill attention: per-query gather, bucket-major (each bucket's K/V read once per pass), "
                          "or auto (bucket-major when a bucket is expected in >= 2 pairs per pass)")
-    ap.add_argument("--bucket-records", choices=["on", "off"], default="on",
-                    help="bucket-major attention takes its pairs from the selection's bucket records (on) or from "
-                         "the token lists (off); the same output")
+    ap.add_argument("--bucket-records", choices=["only", "on", "off"], default="only",
+                    help="bucket-major attention takes its pairs from the selection's bucket records, the rows "
+                         "with records then getting no token list (only) or getting one too (on), or takes them "
+                         "from the token lists (off); the same output")
     ap.add_argument("--bm-pass", type=int, default=32768,
                     help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
     ap.add_argument("--bm-mem", type=float, default=0.72,

@@ -60,7 +60,7 @@ extern "C" {
 #endif
 
 #define LSA_BUCKET_RECS 256   /* bucket records per (query, KV head) in lsa_select's optional output */
-#define LSA_ABI_VERSION 4
+#define LSA_ABI_VERSION 5
 
 #define LSA_LATENT_DIM 64         /* latent width (ch.2: 64-d index space) */
 #define LSA_POOL 4                /* keys pooled per entry (ch.2)            */
@@ -129,6 +129,11 @@ typedef struct lsa_select_cfg {
                           * node as a tree built over the visible blocks has it), so a
                           * prefill query selects what a decode step at its position
                           * does on a cache grown to that point; 0: stored centroids */
+    int32_t skip_recorded_lists; /* 0 or 1; with bucket records requested, 1 leaves the
+                          * lr_idx row of every (query, KV head) that gets records
+                          * unwritten (its lr_cnt is written): for callers that
+                          * pass the records to lsa_sparse_attend_bucket_major,
+                          * which then reads only the other rows' lists */
 } lsa_select_cfg;
 
 /* Byte offsets of the cache regions, for inspection (tests, tools).  Per

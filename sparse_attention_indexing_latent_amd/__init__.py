@@ -49,9 +49,9 @@ def make_layout(head_dim: int, n_kv_heads: int, n_q_heads: int, dtype: torch.dty
 
 
 def select_cfg(k: int, n_sinks: int, window: int, search: str = "flat", beam: int = 0,
-               strategy: str = "auto", causal_tree: bool = False) -> SelectCfg:
+               strategy: str = "auto", causal_tree: bool = False, skip_recorded_lists: bool = False) -> SelectCfg:
     return SelectCfg(k, n_sinks, window, LSA_SEARCH_TREE if search == "tree" else LSA_SEARCH_FLAT, beam,
-                     _STRATEGIES[strategy], int(causal_tree))
+                     _STRATEGIES[strategy], int(causal_tree), int(skip_recorded_lists))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -184,7 +184,7 @@ def select_workspace_bytes(cache: LsaCache, cfg: SelectCfg, n_q: int, n_q_heads:
 def select(Q: torch.Tensor, cache: LsaCache, q_pos: torch.Tensor, W_q: torch.Tensor, k: int, n_sinks: int,
            window: int, search: str = "flat", beam: int = 0, strategy: str = "auto",
            workspace: Optional[torch.Tensor] = None, out: Optional[tuple] = None, causal_tree: bool = False,
-           bucket_records: bool = False):
+           bucket_records: bool = False, skip_recorded_lists: bool = False):
     """Query side: score buckets, pick the top ones, expand to k tokens.
 
     Q: [B, n_q, H_q, d]; q_pos: int64 [B, n_q] on the GPU.  Returns
@@ -193,13 +193,14 @@ def select(Q: torch.Tensor, cache: LsaCache, q_pos: torch.Tensor, W_q: torch.Ten
     part, as a decode step on a cache grown to the query's position would score them.
     bucket_records: also return the selection as bucket records, (recs int32 [B, n_q, H_kv, 256, 4]:
     leaf id, key mask low and high words, 0; counts int32 [B, n_q, H_kv], -1 where none), as a third
-    item; out may then hold four tensors.
+    item; out may then hold four tensors.  skip_recorded_lists (with bucket_records): rows that get
+    records have no token list written (only for sparse_attend_bucket_major with those records).
     """
     assert Q.is_cuda and Q.is_contiguous() and q_pos.dtype == torch.int64 and q_pos.is_contiguous()
     B, n_q, H_q, d = Q.shape
     layout = Layout.from_buffer_copy(cache.layout)
     layout.n_q_heads = H_q
-    cfg = select_cfg(k, n_sinks, window, search, beam, strategy, causal_tree)
+    cfg = select_cfg(k, n_sinks, window, search, beam, strategy, causal_tree, skip_recorded_lists)
     L = _lib.lib()
     H_kv = layout.n_kv_heads
     if out is None:

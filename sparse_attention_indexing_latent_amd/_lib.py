@@ -51,7 +51,8 @@ class Layout(ctypes.Structure):
 
 
 class SelectCfg(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("k", "n_sinks", "window", "search", "beam", "strategy", "causal_tree")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("k", "n_sinks", "window", "search", "beam", "strategy", "causal_tree",
+                                              "skip_recorded_lists")]
 
 
 class CacheInfo(ctypes.Structure):

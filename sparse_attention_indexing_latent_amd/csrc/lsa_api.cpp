@@ -168,6 +168,8 @@ lsa_status check_cfg(const lsa_select_cfg* C, int64_t T) {
     if (C->search == LSA_SEARCH_TREE && (C->beam < 1 || C->beam > LSA_MAX_BEAM))
         return fail(LSA_ERR_CAPACITY, "beam must be in 1..%d", LSA_MAX_BEAM);
     if (C->causal_tree != 0 && C->causal_tree != 1) return fail(LSA_ERR_INVALID_ARG, "causal_tree must be 0 or 1");
+    if (C->skip_recorded_lists != 0 && C->skip_recorded_lists != 1)
+        return fail(LSA_ERR_INVALID_ARG, "skip_recorded_lists must be 0 or 1");
     return LSA_OK;
 }
 
@@ -475,6 +477,7 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     sa.n_units = units;
     sa.brec = static_cast<lsa::u32x4*>(bucket_recs);
     sa.bcnt = bucket_cnt;
+    sa.skip_lists = bucket_recs != nullptr ? cfg->skip_recorded_lists : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t* lr = lr_idx ? lr_idx : lr_cnt;  // k == 0: rows are empty, never written
     hipError_t e = bucket_cnt ? lsa::launch_fill_i32(bucket_cnt, units, -1, st) : hipSuccess;

@@ -21,6 +21,7 @@ struct SelArgs {
     int64_t n_units;   // B * n_q * H_kv
     u32x4* brec;       // optional: [n_units, LSA_BUCKET_RECS] bucket records of the selection
     int32_t* bcnt;     // optional: [n_units] their count (-1: none; the caller fills -1 first)
+    int32_t skip_lists;   // rows that get records: no token list written
 };
 
 struct SelectBuffers {

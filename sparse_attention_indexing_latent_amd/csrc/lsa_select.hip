@@ -1062,11 +1062,12 @@ __device__ __forceinline__ void write_bucket_records(const uint64_t* sel, int ns
 
 // Walk keys[0..n) (sorted by rank), pick the buckets until k eligible
 // tokens, sort the picks by id into sel[] (room for sel_cap) and expand;
-// with rec, also write the picks as bucket records.  Returns the count, or
-// -1 with nothing written when more than sel_cap buckets are needed.
+// with rec, also write the picks as bucket records (and with rec_only, no
+// tokens).  Returns the count, or -1 with nothing written when more than
+// sel_cap buckets are needed.
 __device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t* sel, int sel_cap, int* tk,
                                                 uint32_t* ent, const CacheView& cv, int64_t bg, const Geom& q, int k,
-                                                int32_t* out, u32x4* rec, int32_t* rcnt) {
+                                                int32_t* out, u32x4* rec, int32_t* rcnt, bool rec_only) {
     const int l = lane_id();
     int have = 0, nsel = 0;
     bool done = false;
@@ -1097,7 +1098,10 @@ __device__ __forceinline__ int wave_walk_expand(uint64_t* keys, int n, uint64_t*
     wave_sort_desc(sel, P);
     for (int j = l; j < P; j += 64) sel[j] = ~sel[j];
     wave_sync();
-    if (rec != nullptr) write_bucket_records(sel, nsel, cv, bg, q, rec, rcnt);
+    if (rec != nullptr) {
+        write_bucket_records(sel, nsel, cv, bg, q, rec, rcnt);
+        if (rec_only) return records_tokens(sel, 0, nsel);
+    }
     return wave_expand(sel, nsel, cv, bg, q, out, tk, ent);
 }
 
@@ -1185,7 +1189,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
     // the rank keys are dead once the walk is done: their space holds the entry keys (<= k / 4)
     const int got = wave_walk_expand(keys[wid], f, sel[wid], kSelCap, tk[wid], reinterpret_cast<uint32_t*>(keys[wid]),
                                      cv, bg, q, sa.k, out, sa.brec ? sa.brec + u * LSA_BUCKET_RECS : nullptr,
-                                     sa.bcnt ? sa.bcnt + u : nullptr);
+                                     sa.bcnt ? sa.bcnt + u : nullptr, sa.skip_lists != 0);
     if (got < 0) {   // many small buckets: the exact path takes the unit
         if (l == 0) {
             const int pos = atomicAdd(&counters[0], 1);
@@ -1193,7 +1197,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
         }
         return;
     }
-    write_pad(out, got, sa.k);
+    if (!(sa.brec && sa.skip_lists)) write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
 }
 
@@ -2024,8 +2028,8 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
     // nf <= beam buckets: never more than sel holds
     const int got = wave_walk_expand(keys[wid], nf, sel[wid], 2 * LSA_MAX_BEAM, tk[wid], ent[wid], cv, bg, q, sa.k,
                                      out, sa.brec ? sa.brec + u * LSA_BUCKET_RECS : nullptr,
-                                     sa.bcnt ? sa.bcnt + u : nullptr);
-    write_pad(out, got, sa.k);
+                                     sa.bcnt ? sa.bcnt + u : nullptr, sa.skip_lists != 0);
+    if (!(sa.brec && sa.skip_lists)) write_pad(out, got, sa.k);
     if (l == 0) lr_cnt[u] = got;
 }
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(decl) == set(_lib.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert L.lsa_abi_version() == 4
+    assert L.lsa_abi_version() == 5
 
 
 def test_status_strings():
@@ -127,6 +127,7 @@ def test_select_validation_before_launch():
     assert call(SelectCfg(2048, 4, 128, 1, 8, 0)) == 8           # tree on a cache without tree
     assert call(SelectCfg(2048, 4, 128, 0, 0, 9)) == 1           # unknown strategy
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0, 2)) == 1        # causal_tree not 0 or 1
+    assert call(SelectCfg(2048, 4, 128, 0, 0, 0, 0, 3)) == 1     # skip_recorded_lists not 0 or 1
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), ws=8) == 5     # workspace too small
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), T=9000) == 6   # T > t_max
     assert call(SelectCfg(2048, 4, 128, 0, 0, 0), cache_bytes=8) == 5

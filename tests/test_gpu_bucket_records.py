@@ -117,3 +117,25 @@ def test_records_that_do_not_match_their_row_use_the_row(layer):
     assert torch.equal(out[0][~touched.to(DEV)], ref[0][~touched.to(DEV)])
     print(f"[rec] rows sent to the list path: max diff {float(d.max()):.3e}", flush=True)
     assert float(d.max()) <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("search", ["flat", "tree"])
+def test_skipped_lists_leave_recorded_rows_unwritten_and_the_attention_unchanged(layer, search):
+    cfg, G = layer["cfg"], layer["G"]
+    lr, cnt, rec = _select(layer, search, bucket_records=True)
+    B, n_q, H_kv, k = lr.shape
+    lr_s = torch.full_like(lr, -7)
+    cnt_s = torch.empty_like(cnt)
+    recs_s, rcnt_s = torch.empty_like(rec[0]), torch.empty_like(rec[1])
+    _select(layer, search, bucket_records=True, skip_recorded_lists=True, out=(lr_s, cnt_s, recs_s, rcnt_s))
+    torch.cuda.synchronize()
+    assert torch.equal(cnt_s, cnt) and torch.equal(rcnt_s, rec[1])
+    has = rec[1] >= 0
+    assert bool((lr_s[has] == -7).all())                     # recorded rows: no list written
+    assert torch.equal(lr_s[~has], lr[~has])                # the other rows: their lists
+    args = (G["Q"], G["K"], G["V"], G["q_pos"])
+    tail = (layer["cache"], cfg.k, cfg.n_sinks, cfg.window)
+    a = lsa.sparse_attend_bucket_major(*args, lr, cnt, *tail)
+    b = lsa.sparse_attend_bucket_major(*args, lr_s, cnt_s, *tail, bucket_records=(recs_s, rcnt_s))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
