@@ -285,7 +285,10 @@ def run_prefill(args, cid):
         # passes of up to --bm-pass queries, fewer (in steps of 4096) if free memory is short (workspace <= --bm-mem of it)
         torch.cuda.empty_cache()
         free = torch.cuda.mem_get_info(dev)[0]
-        n_pass = args.bm_pass
+        # default start: 32768 queries when such a pass gives each listed bucket >= 8 pairs on average (its
+        # K/V reads already shared: measured equal or better than larger passes at 1M), else 65536 (at 10M a
+        # bucket gets ~6 pairs per 32768 queries; 40960-query passes, the most that fit, were 7% faster)
+        n_pass = args.bm_pass or (32768 if 32768 * cfg.k >= 8 * cfg.T else 65536)
         while n_pass > 4096 and lsa.attend_bucket_major_workspace_bytes(cache0, cfg.H_q, cfg.d, n_pass) > args.bm_mem * free:
             n_pass -= 4096
         # auto: bucket-major when a bucket is expected in >= 2 pairs per pass (n_pass * k / T); measured:
@@ -582,8 +585,9 @@ def main():
                     help="bucket-major attention takes its pairs from the selection's bucket records, the rows "
                          "with records then getting no token list (only) or getting one too (on), or takes them "
                          "from the token lists (off); the same output")
-    ap.add_argument("--bm-pass", type=int, default=32768,
-                    help="queries per bucket-major pass (the workspace grows with it; more queries share each bucket)")
+    ap.add_argument("--bm-pass", type=int, default=0,
+                    help="most queries per bucket-major pass, lowered in steps of 4096 until the workspace fits "
+                         "(0: 32768 where such a pass gives a bucket >= 8 pairs, else 65536)")
     ap.add_argument("--bm-mem", type=float, default=0.72,
                     help="largest share of the free device memory the bucket-major workspace may take")
     ap.add_argument("--study", choices=["crossover"], default=None,
