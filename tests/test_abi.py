@@ -139,6 +139,26 @@ def test_select_validation_before_launch():
                                         8192, ctypes.byref(n)) == 0
 
 
+def test_bucket_major_validation_before_launch():
+    """Argument checks of lsa_sparse_attend_bucket_major, all before anything is launched."""
+    L = _lib.lib()
+    lay = _layout()
+    cfg = SelectCfg(2048, 4, 1024, 0, 0, 0)
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(recs=None, rcnt=None, lay=lay, ws=1 << 40, cache_bytes=1 << 40):
+        return L.lsa_sparse_attend_bucket_major(ctypes.byref(lay), ctypes.byref(cfg), fake, cache_bytes, 8192,
+                                                fake, fake, fake, 8192, 8192, fake, 1, 4, fake, fake, recs, rcnt,
+                                                ctypes.c_float(0.1), fake, fake, ws, None)
+
+    assert call(recs=fake) == 1                                     # records without counts
+    assert call(rcnt=fake) == 1                                     # counts without records
+    assert call(recs=fake, rcnt=ctypes.c_void_p(0x1004)) == 4       # misaligned counts
+    assert call(lay=_layout(dtype=_lib.LSA_F32)) == 8               # bf16 only
+    assert call(cache_bytes=16) == 5                                # cache too small
+    assert call(ws=16) == 5                                         # workspace too small
+
+
 def test_empty_calls_are_no_ops():
     L = _lib.lib()
     lay = _layout()
