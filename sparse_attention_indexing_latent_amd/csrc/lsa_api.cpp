@@ -225,6 +225,11 @@ void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) 
     const int64_t nch = (w.nbins + lsa::kBmScanChunk - 1) / lsa::kBmScanChunk;
     w.nbins_pad = (nch > 0 ? nch : 1) * lsa::kBmScanChunk;
     int64_t pool = w.units * kBmPoolPerUnit;
+    // at least two full units per pool slice: a small pass (few units per slice) then never runs a slice
+    // out of slots, and which unit an overfull slice sends to the gather path never depends on the order
+    // of the slot requests
+    const int64_t pool_min = (int64_t)lsa::kBmCursors * 2 * lsa::kBmUnitCap;
+    if (pool < pool_min) pool = pool_min;
     if (pool > ((int64_t)1 << 31)) pool = (int64_t)1 << 31;
     w.pool_cap = (uint32_t)pool;
     size_t o = 0;

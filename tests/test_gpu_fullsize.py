@@ -183,6 +183,30 @@ def test_prefill_1m_sampled():
                                 t_of=lambda b, i: i0 + i)
         print(f"[1m] chunk {i0} select {res}", flush=True)
         assert res["unexcused"] == 0 and res["exact"] >= 36
+    # the late chunk as the prefill bench times it: bucket records, no lists for the rows that have them,
+    # bucket-major passes of 32768 queries; equal to the same call on the lists, and to the gather call
+    Qc, qpc = G["Q"][:, sl].contiguous(), G["q_pos"][:, sl].contiguous()
+    lr_r = torch.empty_like(lr)
+    cnt_r = torch.empty_like(cnt)
+    recs = torch.empty(1, CHUNK, cfg.H_kv, 256, 4, dtype=torch.int32, device=DEV)
+    rcnt = torch.empty(1, CHUNK, cfg.H_kv, dtype=torch.int32, device=DEV)
+    lsa.select(Qc, cache, qpc, G["W"], cfg.k, cfg.n_sinks, cfg.window, strategy="fused", bucket_records=True,
+               skip_recorded_lists=True, out=(lr_r, cnt_r, recs, rcnt))
+    ws = torch.empty(lsa.attend_bucket_major_workspace_bytes(cache, cfg.H_q, cfg.d, 32768), dtype=torch.uint8,
+                     device=DEV)
+    tail = (cache, cfg.k, cfg.n_sinks, cfg.window)
+    Ob = lsa.sparse_attend_bucket_major(Qc, G["K"], G["V"], qpc, lr_r, cnt_r, *tail, workspace=ws,
+                                        bucket_records=(recs, rcnt))
+    Ol = lsa.sparse_attend_bucket_major(Qc, G["K"], G["V"], qpc, lr, cnt, *tail, workspace=ws)
+    del ws
+    Og = lsa.sparse_attend(Qc, G["K"], G["V"], qpc, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt_r, cnt) and bool((rcnt >= 0).float().mean() > 0.99)
+    assert torch.equal(Ob, Ol)
+    d_gather = float((Ob.float() - Og.float()).abs().max())
+    print(f"[1m] bench path (records, bucket-major) vs gather max abs diff {d_gather:.3e}", flush=True)
+    assert d_gather <= tol_for("bf16")
+    del Ob, Ol, Og, lr_r, recs
     # attention on synthetic lists for sampled late queries
     qs = torch.tensor(sorted(rng.integers(cfg.T - 4096, cfg.T, 64).tolist()), dtype=torch.int64)
     Qs = G["Q"][:, qs.to(DEV)].contiguous()
@@ -277,3 +301,20 @@ def test_prefill_10m_tree_sampled():
                             t_of=lambda b, i: int(qs[0, i]))
     print(f"[10m] tree select {res}", flush=True)
     assert res["unexcused"] == 0
+    # bucket-major with the tree cache and the selection's records (lists skipped), as the bench times it:
+    # equal to the same call on the lists, and to the gather call
+    lr_r, cnt_r = torch.empty_like(lr), torch.empty_like(cnt)
+    recs = torch.empty(*cnt.shape, 256, 4, dtype=torch.int32, device=DEV)
+    rcnt = torch.empty_like(cnt)
+    lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window, search="tree", beam=cfg.beam,
+               bucket_records=True, skip_recorded_lists=True, out=(lr_r, cnt_r, recs, rcnt))
+    tail = (cache, cfg.k, cfg.n_sinks, cfg.window)
+    Ob = lsa.sparse_attend_bucket_major(G["Q"], G["K"], G["V"], G["q_pos"], lr_r, cnt_r, *tail,
+                                        bucket_records=(recs, rcnt))
+    Ol = lsa.sparse_attend_bucket_major(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, *tail)
+    Og = lsa.sparse_attend(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt_r, cnt) and torch.equal(Ob, Ol)
+    d_gather = float((Ob.float() - Og.float()).abs().max())
+    print(f"[10m] bucket-major (records) vs gather max abs diff {d_gather:.3e}", flush=True)
+    assert d_gather <= tol_for("bf16")
