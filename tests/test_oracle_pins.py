@@ -60,6 +60,57 @@ def test_zero_key_gives_zero_latent():
     assert np.all(u == 0)
 
 
+# ---------------------------------------------------------------- query latent
+
+def _exact_unit_rows():
+    """Integer query rows whose squared norm is exactly 1024^2, so q / ||q|| is
+    exact in float64; with the identity projection the latent is q / 1024.
+    Row 0: 514/1024 = 0.5 + 2^-9 sits half way between the bf16 values 0.5 and
+    0.50390625 (spacing 2^-8 in [0.5, 1)); ties go to the even 0.5.  Row 1:
+    518/1024 sits half way between 0.50390625 (odd last bit) and 0.5078125
+    (even): it rounds up.  885/1024 and 883/1024 lie 1/4 and 3/4 of a step
+    above 0.86328125 = 884/1024 and round to it.  The small components are
+    exact in bf16."""
+    q = np.zeros((2, 64))
+    q[0, :6] = [514, 885, 33, 8, 1, 1]
+    q[1, :5] = [518, 883, 23, 5, 3]
+    assert np.all((q * q).sum(axis=1) == 1024 ** 2)
+    want = np.zeros((2, 64))
+    want[0, :6] = [0.5, 0.86328125, 33 / 1024, 8 / 1024, 1 / 1024, 1 / 1024]
+    want[1, :5] = [0.5078125, 0.86328125, 23 / 1024, 5 / 1024, 3 / 1024]
+    return q, want
+
+
+def test_query_latent_normalises_then_rounds_half_even():
+    q, want = _exact_unit_rows()
+    got = O.query_latent(q, np.eye(64), "bf16")
+    assert np.array_equal(got, want)
+    # without the rounding the half-way components would be kept exactly
+    exact = O.query_latent(q, np.eye(64), "f64")
+    assert exact[0, 0] == 514 / 1024 and exact[1, 0] == 518 / 1024
+    # fp32 storage keeps all of them (every component is a multiple of 2^-10)
+    assert np.array_equal(O.query_latent(q, np.eye(64), "f32"), q / 1024)
+
+
+def test_query_latent_scale_invariant_and_projected():
+    q, want = _exact_unit_rows()
+    for c in (7.5, 2.0 ** -20, 3.0e5):
+        assert np.array_equal(O.query_latent(c * q, np.eye(64), "bf16"), want)
+    # a projection that permutes and scales the axes: q W = 4 * (q permuted)
+    perm = np.random.default_rng(3).permutation(64)
+    W = np.zeros((64, 64))
+    W[np.arange(64), perm] = 4.0
+    got = O.query_latent(q, W, "bf16")
+    assert np.array_equal(got[:, perm], want)
+    # a head dimension larger than the latent: W [128, 64] reading only the first 64 dims
+    q2 = np.concatenate([q, np.full((2, 64), 0.0)], axis=1)
+    W2 = np.concatenate([np.eye(64), np.full((64, 64), 9.0)], axis=0)
+    assert np.array_equal(O.query_latent(q2, W2, "bf16"), want)
+    # the unit norm holds before rounding, and a zero query stays zero
+    assert np.allclose(np.linalg.norm(O.query_latent(q, np.eye(64), "f64"), axis=1), 1.0, atol=0)
+    assert np.all(O.query_latent(np.zeros((1, 64)), np.eye(64), "bf16") == 0)
+
+
 def test_pooling_is_mean_of_four():
     rng = np.random.default_rng(2)
     u = rng.standard_normal((4 * 5 + 3, 64))
