@@ -60,7 +60,7 @@ extern "C" {
 #endif
 
 #define LSA_BUCKET_RECS 256   /* bucket records per (query, KV head) in lsa_select's optional output */
-#define LSA_ABI_VERSION 5
+#define LSA_ABI_VERSION 6
 
 #define LSA_LATENT_DIM 64         /* latent width (ch.2: 64-d index space) */
 #define LSA_POOL 4                /* keys pooled per entry (ch.2)            */
@@ -93,8 +93,10 @@ typedef enum lsa_search { LSA_SEARCH_FLAT = 0, LSA_SEARCH_TREE = 1 } lsa_search;
  * returns identical results; they differ only in speed. */
 typedef enum lsa_strategy {
     LSA_STRATEGY_AUTO = 0,         /* fused for many queries, materialised for few       */
-    LSA_STRATEGY_FUSED = 1,        /* two MFMA scoring passes: a per-query bound from
-                                      per-block maxima, then candidates above the bound  */
+    LSA_STRATEGY_FUSED = 1,        /* one MFMA scoring pass per query tile that keeps the
+                                      buckets above a rising per-query bound, then an exact
+                                      finish over those (fp32: a bound pass, then a
+                                      candidate pass)                                     */
     LSA_STRATEGY_MATERIALIZED = 2  /* every score written to the workspace, then an exact
                                       radix select (decode: few queries, many buckets)   */
 } lsa_strategy;
@@ -263,9 +265,11 @@ lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg
 
 /* Workspace bytes lsa_sparse_attend_bucket_major needs to process n_q_pass
  * queries per sequence in one pass (a cache for t_max tokens).  Host only.
- * Dominated by one partial per (query, KV head, bucket) pair (fp32 max,
- * denominator and scale, d 12-bit values per head): about
- * 80 * (32 + G * (3 d / 2 + 16)) bytes per (query, KV head). */
+ * Dominated by the pool of partials, 80 slots per (query, KV head) on
+ * average, one per (query, KV head, bucket) pair (fp32 max, denominator and
+ * scale, d fp16 values per head), and a staging row of 256 pair records per
+ * (query, KV head): about 80 * (16 + G * (2 d + 16)) + 4104 bytes per
+ * (query, KV head). */
 lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, const lsa_select_cfg* cfg,
                                                    int64_t batch, int64_t n_q_pass, int64_t t_max, size_t* bytes);
 
@@ -275,17 +279,24 @@ lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, con
  * are grouped by bucket through the cache's entry_leaf / entry_pos maps, each
  * bucket's keys and values are read once for every query that listed any of
  * them, and the per-pair softmax partials are merged with the sinks + window
- * part by a log-sum-exp combine.  Outputs equal lsa_sparse_attend's up to
- * the order of the fp32 sums.  Arguments as for lsa_sparse_attend plus the
+ * part by a log-sum-exp combine.  Arguments as for lsa_sparse_attend plus the
  * cache (built with T tokens for t_max; layout must be the one it was built
  * with, build_tree included, since the cache's regions are found from it)
  * and a workspace of at least
  * lsa_attend_bucket_major_workspace_bytes(.., 1, ..); the call then runs
- * ceil(n_q / P) passes, P the most queries the workspace holds.  A
- * (query, KV head) whose list is not strictly ascending, holds a token outside
- * [sink end, window start), touches more than 256 buckets, or finds its
- * share of the pass's pair pool full is gathered whole instead (same result,
- * slower).  bf16 only
+ * ceil(n_q / P) passes, P the most queries the workspace holds.
+ * Precision: each partial's unnormalised output is stored as fp16 values
+ * times an exact power-of-two scale per (pair, head), so a value differs
+ * from lsa_sparse_attend's by the order of the fp32 sums plus the fp16
+ * rounding of each partial value (relative 2^-11 of that value, weighted by
+ * the partial's share of the softmax).
+ * Rows gathered whole instead (same result, slower): a (query, KV head)
+ * whose list is not strictly ascending, holds a token outside
+ * [sink end, window start), or touches more than 256 buckets (its list is
+ * gathered); and one whose pairs do not fit in the pass's pool of partial
+ * slots, which are handed out in query order (its list is gathered, or, for
+ * a row with bucket records, the keys its records name, so a row whose list
+ * the selection skipped is still attended exactly).  bf16 only
  * (LSA_ERR_UNSUPPORTED otherwise); lr_idx rows must not be modified while
  * the call's kernels run.
  * Optional bucket_recs / bucket_cnt (both NULL, or both set): the records
@@ -294,13 +305,17 @@ lsa_status lsa_attend_bucket_major_workspace_bytes(const lsa_layout* layout, con
  * every listed token: the same pairs in the same order, so the same output
  * bit for bit.  If a record's bucket lies outside the blocks the query's
  * long-range keys come from, or the masks' bits do not add up to the row's
- * count, the row is used instead. */
+ * count, the row's list is used instead.
+ * Optional fallback_counts (device, two uint32, NULL for none): the call
+ * adds the number of rows it gathered whole to [0], and of those the rows
+ * whose pairs did not fit in the pool to [1] (the caller zeroes them). */
 lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache,
                                           size_t cache_bytes, int64_t t_max, const void* Q, const void* K,
                                           const void* V, int64_t t_cap, int64_t T, const int64_t* q_pos,
                                           int64_t batch, int64_t n_q, const int32_t* lr_idx, const int32_t* lr_cnt,
                                           const void* bucket_recs, const int32_t* bucket_cnt, float scale, void* O,
-                                          void* workspace, size_t workspace_bytes, void* stream);
+                                          void* workspace, size_t workspace_bytes, uint32_t* fallback_counts,
+                                          void* stream);
 
 /* Workspace bytes lsa_pca_projection needs for this layout's head_dim.  Host only. */
 lsa_status lsa_pca_workspace_bytes(const lsa_layout* layout, size_t* bytes);

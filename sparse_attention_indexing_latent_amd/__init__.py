@@ -279,11 +279,14 @@ def sparse_attend_bucket_major(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
                                lr_idx: torch.Tensor, lr_cnt: torch.Tensor, cache: LsaCache, k: int, n_sinks: int,
                                window: int, scale: Optional[float] = None, O: Optional[torch.Tensor] = None,
                                workspace: Optional[torch.Tensor] = None, n_q_pass: int = 16384,
-                               bucket_records: Optional[tuple] = None) -> torch.Tensor:
+                               bucket_records: Optional[tuple] = None,
+                               fallback_counts: Optional[torch.Tensor] = None) -> torch.Tensor:
     """sparse_attend computed bucket-major (bf16): same outputs, each bucket's K/V read once per pass.
 
     Without a workspace, one for passes of min(n_q, n_q_pass) queries is allocated.  bucket_records:
     the (recs, counts) select returned with these lists (pairs taken from them; same output).
+    fallback_counts: optional int32 [2] device tensor the call adds to: rows gathered whole instead,
+    and of those the rows whose pairs did not fit in the pass's pool.
     """
     assert Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()
     B, n_q, H_q, d = Q.shape
@@ -303,7 +306,8 @@ def sparse_attend_bucket_major(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor
         _ptr(V), t_cap, cache.T, _ptr(q_pos), B, n_q, _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt),
         _ptr(bucket_records[0]) if bucket_records is not None else ctypes.c_void_p(0),
         _ptr(bucket_records[1]) if bucket_records is not None else ctypes.c_void_p(0),
-        ctypes.c_float(scale), _ptr(O), _ptr(workspace), workspace.numel(), _stream(Q.device)))
+        ctypes.c_float(scale), _ptr(O), _ptr(workspace), workspace.numel(), _ptr(fallback_counts),
+        _stream(Q.device)))
     return O
 
 

@@ -98,7 +98,7 @@ def lib():
                                     ctypes.c_float, vp, vp, sz, vp]
     L.lsa_attend_bucket_major_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, i64, P(sz)]
     L.lsa_sparse_attend_bucket_major.argtypes = [P(Layout), P(SelectCfg), vp, sz, i64, vp, vp, vp, i64, i64, vp,
-                                                 i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
+                                                 i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp, vp]
     L.lsa_pca_workspace_bytes.argtypes = [P(Layout), P(sz)]
     L.lsa_pca_projection.argtypes = [P(Layout), vp, i64, i64, i64, vp, vp, vp, sz, vp]
     for name in ("lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_extend_buckets",

@@ -202,18 +202,23 @@ uint32_t next_call_tag() {
 }
 
 // Workspace of one bucket-major pass over nqp queries per sequence: the
-// per-bin counts and offsets, the per-unit slot ranges, the pair records and
-// the partials (fp32 max, denominator and scale; D fp16 values) of every
-// pair slot.  The
-// pool holds kBmPoolPerUnit slots per unit on average (a unit takes one per
-// bucket it reads from, about k / 32 with buckets of 8 entries).
+// per-bin counts and offsets, the per-unit pair counts, slot offsets and
+// staging rows (kBmUnitCap pair records each), the pair records grouped by
+// bin, the work records, and the partials (fp32 max, denominator and scale,
+// D fp16 values) of every pool slot.  The pool holds
+// kBmPoolPerUnit slots per unit on average (a unit takes one per bucket it
+// reads from, about k / 32 with buckets of 8 entries, 64 at k = 2048) and at
+// least one full unit; pool slots are handed out in unit order, so a pass
+// whose units need more runs its last units through the gather path.
 constexpr int64_t kBmPoolPerUnit = 80;
+// most units per pass: keeps every pair and slot index inside 32 bits
+constexpr int64_t kBmMaxUnits = (int64_t)1 << 23;
 
 struct BmWs {
-    int64_t units, leaves_max, nbins, nbins_pad;
+    int64_t units, leaves_max, nbins, nbins_pad, nuch;
     uint32_t pool_cap;
-    size_t off_lcnt, off_loff, off_ctot, off_csum, off_gpre, off_uoff, off_unp, off_rec, off_srec, off_work, off_po, off_pml,
-        total;
+    size_t off_lcnt, off_loff, off_ctot, off_csum, off_gpre, off_uoff, off_unp, off_utot, off_ucsum, off_stage,
+        off_srec, off_work, off_po, off_pml, total;
 };
 
 void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) {
@@ -224,26 +229,26 @@ void bm_ws(const lsa_layout* L, int64_t B, int64_t nqp, int64_t t_max, BmWs& w) 
     w.nbins = B * H_kv * w.leaves_max;
     const int64_t nch = (w.nbins + lsa::kBmScanChunk - 1) / lsa::kBmScanChunk;
     w.nbins_pad = (nch > 0 ? nch : 1) * lsa::kBmScanChunk;
+    w.nuch = (w.units + lsa::kBmScanChunk - 1) / lsa::kBmScanChunk;
+    if (w.nuch < 1) w.nuch = 1;
     int64_t pool = w.units * kBmPoolPerUnit;
-    // at least two full units per pool slice: a small pass (few units per slice) then never runs a slice
-    // out of slots, and which unit an overfull slice sends to the gather path never depends on the order
-    // of the slot requests
-    const int64_t pool_min = (int64_t)lsa::kBmCursors * 2 * lsa::kBmUnitCap;
-    if (pool < pool_min) pool = pool_min;
+    if (pool < lsa::kBmUnitCap) pool = lsa::kBmUnitCap;
     if (pool > ((int64_t)1 << 31)) pool = (int64_t)1 << 31;
     w.pool_cap = (uint32_t)pool;
     size_t o = 0;
-    w.off_lcnt = o;   o = align256(o + (size_t)(w.nbins_pad + 2 + lsa::kBmCursors) * 4);
+    w.off_lcnt = o;   o = align256(o + (size_t)(w.nbins_pad + 4) * 4);
     w.off_loff = o;   o = align256(o + (size_t)w.nbins_pad * 4);
     w.off_ctot = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 8);
     w.off_csum = o;   o = align256(o + (size_t)(w.nbins_pad / lsa::kBmScanChunk) * 8);
     w.off_gpre = o;   o = align256(o + (size_t)(w.nbins_pad / 64) * 4);
     w.off_uoff = o;   o = align256(o + (size_t)w.units * 4);
     w.off_unp = o;    o = align256(o + (size_t)w.units * 4);
-    w.off_rec = o;    o = align256(o + (size_t)pool * 16);
+    w.off_utot = o;   o = align256(o + (size_t)w.nuch * 4);
+    w.off_ucsum = o;  o = align256(o + (size_t)w.nuch * 4);
+    w.off_stage = o;  o = align256(o + (size_t)w.units * lsa::kBmUnitCap * 16);
     w.off_srec = o;   o = align256(o + (size_t)pool * 16);
     w.off_work = o;   o = align256(o + (size_t)w.nbins * 17 * 16);
-    w.off_po = o;     o = align256(o + (size_t)pool * G * (3 * D / 2));   // 12-bit packed rows
+    w.off_po = o;     o = align256(o + (size_t)pool * G * (2 * D));   // fp16 rows
     w.off_pml = o;    o = align256(o + (size_t)pool * G * 16);
     w.total = o;
 }
@@ -582,7 +587,8 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
                                           const void* V, int64_t t_cap, int64_t T, const int64_t* q_pos,
                                           int64_t batch, int64_t n_q, const int32_t* lr_idx, const int32_t* lr_cnt,
                                           const void* bucket_recs, const int32_t* bucket_cnt, float scale, void* O,
-                                          void* workspace, size_t workspace_bytes, void* stream) {
+                                          void* workspace, size_t workspace_bytes, uint32_t* fallback_counts,
+                                          void* stream) {
     lsa_status s = check_layout(layout);
     if (s) return s;
     if (!cfg) return fail(LSA_ERR_INVALID_ARG, "cfg is NULL");
@@ -601,17 +607,22 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         return fail(LSA_ERR_INVALID_ARG, "bucket_recs and bucket_cnt must both be NULL or both be set");
     if (misaligned(cache) || misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(q_pos) ||
         misaligned(lr_cnt) || (lr_idx && misaligned(lr_idx)) || misaligned(O) || misaligned(workspace) ||
-        (bucket_recs && misaligned(bucket_recs)) || (bucket_cnt && misaligned(bucket_cnt)))
+        (bucket_recs && misaligned(bucket_recs)) || (bucket_cnt && misaligned(bucket_cnt)) ||
+        (fallback_counts && misaligned(fallback_counts)))
         return fail(LSA_ERR_ALIGN, "pointers must be 16-byte aligned");
     CacheGeom c;
     cache_geom(layout, batch, t_max, T, c);
     if (cache_bytes < c.total) return fail(LSA_ERR_WORKSPACE, "cache has %zu bytes, needs %zu", cache_bytes, c.total);
-    // queries per pass: the most the workspace holds (the size is increasing in the pass length)
+    if (batch * layout->n_kv_heads > kBmMaxUnits)
+        return fail(LSA_ERR_CAPACITY, "more than %lld (sequence, KV head) slices", (long long)kBmMaxUnits);
+    // queries per pass: the most the workspace holds (the size is increasing in the pass length), and at
+    // most kBmMaxUnits units
     BmWs w;
     bm_ws(layout, batch, 1, t_max, w);
     if (workspace_bytes < w.total)
         return fail(LSA_ERR_WORKSPACE, "workspace has %zu bytes, needs at least %zu", workspace_bytes, w.total);
     int64_t lo = 1, hi = n_q;
+    if (hi > kBmMaxUnits / (batch * layout->n_kv_heads)) hi = kBmMaxUnits / (batch * layout->n_kv_heads);
     while (lo < hi) {
         const int64_t mid = lo + (hi - lo + 1) / 2;
         bm_ws(layout, batch, mid, t_max, w);
@@ -630,6 +641,7 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         bm.leaves_max = w.leaves_max;
         bm.nbins = w.nbins;
         bm.nbins_pad = w.nbins_pad;
+        bm.nuch = w.nuch;
         bm.pool_cap = w.pool_cap;
         bm.lcnt = reinterpret_cast<uint32_t*>(wb + w.off_lcnt);
         bm.loff = reinterpret_cast<uint32_t*>(wb + w.off_loff);
@@ -638,8 +650,11 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         bm.gpre = reinterpret_cast<uint32_t*>(wb + w.off_gpre);
         bm.unit_off = reinterpret_cast<uint32_t*>(wb + w.off_uoff);
         bm.unit_np = reinterpret_cast<int32_t*>(wb + w.off_unp);
-        bm.rec = reinterpret_cast<lsa::u32x4*>(wb + w.off_rec);
+        bm.utot = reinterpret_cast<uint32_t*>(wb + w.off_utot);
+        bm.ucsum = reinterpret_cast<uint32_t*>(wb + w.off_ucsum);
+        bm.stage = reinterpret_cast<lsa::u32x4*>(wb + w.off_stage);
         bm.srec = reinterpret_cast<lsa::u32x4*>(wb + w.off_srec);
+        bm.fallback = fallback_counts;
         bm.work = reinterpret_cast<lsa::u32x4*>(wb + w.off_work);
         bm.po = reinterpret_cast<uint32_t*>(wb + w.off_po);
         bm.pml = reinterpret_cast<float*>(wb + w.off_pml);
@@ -669,7 +684,7 @@ lsa_status lsa_sparse_attend_bucket_major(const lsa_layout* layout, const lsa_se
         const int32_t* lr = lr_idx ? lr_idx : lr_cnt;
         hipError_t e = lsa::launch_bucket_partials(v, Q, K, V, q_pos, lr, lr_cnt, aa, bm, layout->head_dim, st);
         if (e == hipSuccess)
-            e = lsa::launch_attend_local(Q, K, V, q_pos, lr, lr_cnt, aa, layout->head_dim, O, st);
+            e = lsa::launch_attend_local(v, Q, K, V, q_pos, lr, lr_cnt, aa, layout->head_dim, O, st);
         if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     }
     return ok();

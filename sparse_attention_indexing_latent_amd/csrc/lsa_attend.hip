@@ -62,26 +62,15 @@ __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t
     const int64_t s0 = aa.bm_off[ul];
     for (int s = 0; s < npl; s += MN) {
         f32x4 ml[MN];
-        uint32_t w[MN][NW];
+        u32x4 w[MN][NW / 4];
 #pragma unroll
         for (int j = 0; j < MN; ++j) {
             const int64_t slot = (s0 + (s + j < npl ? s + j : 0)) * aa.G + hh;
             ml[j] = *reinterpret_cast<const f32x4*>(aa.bm_ml + slot * 4);
-            // this lane's run: dims 32m + 8h + [0,8), 12-bit values
-            const uint32_t* pw = aa.bm_po + slot * (4 * NW) + h * NW;
-            if constexpr (NW % 4 == 0) {
+            // this lane's run: dims 32m + 8h + [0,8) for every m, fp16
+            const u32x4* pw = reinterpret_cast<const u32x4*>(aa.bm_po + slot * (4 * NW) + h * NW);
 #pragma unroll
-                for (int x = 0; x < NW; x += 4) {
-                    const u32x4 t = *reinterpret_cast<const u32x4*>(pw + x);
-                    w[j][x] = t[0]; w[j][x + 1] = t[1]; w[j][x + 2] = t[2]; w[j][x + 3] = t[3];
-                }
-            } else {
-#pragma unroll
-                for (int x = 0; x < NW; x += 2) {
-                    const u32x2 t = *reinterpret_cast<const u32x2*>(pw + x);
-                    w[j][x] = t[0]; w[j][x + 1] = t[1];
-                }
-            }
+            for (int x = 0; x < NW / 4; ++x) w[j][x] = pw[x];
         }
 #pragma unroll
         for (int j = 0; j < MN; ++j) {
@@ -92,14 +81,12 @@ __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t
             const float bs = b * ml[j][2];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                // acc[c][v] is value 4c + v of the run: high byte v of word c, nibble 4 (c % 2) + v of word NC + c / 2
-                const uint32_t hw = w[j][c], nw = w[j][NC + c / 2] >> (16 * (c % 2));
-                f32x4 oc;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int hi = (int)(hw << (24 - 8 * v)) >> 24;
-                    oc[v] = (float)((hi * 16) | (int)((nw >> (4 * v)) & 0xFu));
-                }
+                // acc[c] holds dims 32 (c/2) + 8h + 4 (c%2) + [0,4): words 2 (c%2), +1 of chunk c/2
+                const uint32_t w0 = w[j][c / 2][2 * (c % 2)], w1 = w[j][c / 2][2 * (c % 2) + 1];
+                const f32x4 oc = {(float)__builtin_bit_cast(_Float16, (uint16_t)(w0 & 0xFFFFu)),
+                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16)),
+                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 & 0xFFFFu)),
+                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16))};
                 acc[c] = acc[c] * a + oc * bs;
             }
             l_run = l_run * a + ml[j][1] * b;
@@ -370,12 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const AUnit un = aunit_of(uu, aa);
     const int64_t t = q_pos[un.b * aa.n_q + un.i];
     // a count above k (never written by the selection) is clamped: the list row holds k entries
-    int32_t cnt = min(lr_cnt[un.u], aa.k);
-    int32_t npl = 0;
-    if (aa.bm_np != nullptr) {
-        npl = aa.bm_np[un.l];
-        if (npl >= 0 && cnt > 0) cnt = 0;   // the long-range keys arrive as bucket partials
-    }
+    const int32_t cnt = min(lr_cnt[un.u], aa.k);
     const int n = r;  // head column of the C layouts
     const int64_t orow = ((un.b * aa.n_q + un.i) * aa.H_q + un.g * aa.G + n) * D;
 
@@ -433,7 +415,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // acc[c][v] = unnormalised O[head n][32 (c/2) + 8h + 4 (c%2) + v]
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    if (npl > 0 && n < aa.G) merge_bucket_partials<D>(aa, un.l, npl, n, h, m_run, l_run, acc);
     if (aa.splits == 1) {
         if (n < aa.G) {
             const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
@@ -509,7 +490,7 @@ __device__ __forceinline__ void store_tile_part(const u32x4 (&kr)[TileLds<D>::NI
 // for its own columns only.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bm_local_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    CacheView cv, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ lr_idx, const int32_t* __restrict__ lr_cnt,
     AttArgs aa, uint16_t* __restrict__ O, int64_t nwg_padded) {
     using TL = TileLds<D>;
@@ -606,7 +587,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
     __syncthreads();   // the shared tiles are read no more: the LDS becomes one private tile per wave
-    // long-range lists of the units the bucket pass left to the gather
+    // long-range keys of the units the bucket pass left to the gather: their token lists (np = -1), or
+    // the keys their bucket records name (np = -2: records rows whose pairs did not fit in the pool; such
+    // rows may have no token list)
     const uint64_t fb = __ballot(npl < 0);
     if (fb != 0ull) {
         uint8_t* buf = tile_lds + wid * TL::BYTES;
@@ -617,6 +600,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int64_t u2 = __shfl(u, lane0);
             const int64_t t2 = __shfl(t, lane0);
             const int32_t c2 = __shfl(cnt, lane0);
+            const int32_t np2 = __shfl(npl, lane0);
+            const bool mine = qi == q2;
+            if (np2 == -2) {
+                // bucket by bucket: key j = 32 half + (l % 32) of the record's bucket, if its mask bit is set
+                const Geom q = query_geom(t2, aa.n_blocks, aa.n_sinks, aa.window);
+                const int32_t nr = aa.bm_bcnt[u2];
+                const u32x4* recs = aa.bm_brec + u2 * LSA_BUCKET_RECS;
+                for (int x = 0; x < nr; ++x) {
+                    const u32x4 rec = recs[x];
+                    const int64_t leaf = rec[0], blk = leaf / kLeavesPerBlock;
+                    const unsigned long long mask = ((unsigned long long)rec[2] << 32) | rec[1];
+                    const uint32_t meta = cv.meta[bg * cv.s_meta + leaf];
+                    const int sz = (int)(meta & 0xFF), off = (int)((meta >> 8) & 0x3FF);
+                    const uint16_t* mem = cv.members + bg * cv.s_members + blk * kBlockEntries + off;
+                    for (int half = 0; half < 2; ++half) {
+                        const int j = 32 * half + (l & 31);
+                        int32_t tok = -1;
+                        if (((mask >> j) & 1ull) && j < kPool * sz) {
+                            const int64_t tk = blk * kBlockTokens + kPool * (int64_t)mem[j / kPool] + j % kPool;
+                            if (tk >= q.sink_end && tk < q.l0 && tk <= t2) tok = (int32_t)tk;
+                        }
+                        const uint64_t vm = __ballot(tok >= 0);
+                        if ((vm & 0xFFFFFFFFull) == 0ull) continue;
+                        load_tile<D>(Kbg, Vbg, tok, kR, vR);
+                        store_tile<D>(kR, vR, buf);
+                        attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
+                                       mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h,
+                                       aa.scale, m_run, l_run, acc);
+                    }
+                }
+                continue;
+            }
             const int32_t* lr = lr_idx + u2 * aa.k;
             auto tok_at = [&](int64_t j) -> int32_t {
                 if (j >= c2) return -1;
@@ -631,7 +646,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 store_tile<D>(kR, vR, buf);
                 load_tile<D>(Kbg, Vbg, nxt, kR, vR);
                 if ((vm & 0xFFFFFFFFull) != 0ull) {
-                    const bool mine = qi == q2;
                     attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
                                    mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h, aa.scale,
                                    m_run, l_run, acc);
@@ -772,20 +786,20 @@ int attend_splits(int64_t n_units, int window, int k) {
     return (int)want;
 }
 
-hipError_t launch_attend_local(const void* Q, const void* K, const void* V, const int64_t* q_pos,
-                               const int32_t* lr_idx, const int32_t* lr_cnt, const AttArgs& aa, int D, void* O,
-                               hipStream_t st) {
+hipError_t launch_attend_local(const CacheView& cv, const void* Q, const void* K, const void* V,
+                               const int64_t* q_pos, const int32_t* lr_idx, const int32_t* lr_cnt, const AttArgs& aa,
+                               int D, void* O, hipStream_t st) {
     const int TQ = 4 * (16 / aa.G);
     int64_t nwg = (int64_t)aa.H_kv * aa.B * ((aa.nqp + TQ - 1) / TQ);
     nwg = (nwg + 7) & ~(int64_t)7;
     if (D == 128)
-        hipLaunchKernelGGL(bm_local_kernel<128>, dim3((unsigned)nwg), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
-                           static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), q_pos, lr_idx, lr_cnt,
-                           aa, static_cast<uint16_t*>(O), nwg);
+        hipLaunchKernelGGL(bm_local_kernel<128>, dim3((unsigned)nwg), dim3(256), 0, st, cv,
+                           static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                           static_cast<const uint16_t*>(V), q_pos, lr_idx, lr_cnt, aa, static_cast<uint16_t*>(O), nwg);
     else
-        hipLaunchKernelGGL(bm_local_kernel<64>, dim3((unsigned)nwg), dim3(256), 0, st, static_cast<const uint16_t*>(Q),
-                           static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), q_pos, lr_idx, lr_cnt,
-                           aa, static_cast<uint16_t*>(O), nwg);
+        hipLaunchKernelGGL(bm_local_kernel<64>, dim3((unsigned)nwg), dim3(256), 0, st, cv,
+                           static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                           static_cast<const uint16_t*>(V), q_pos, lr_idx, lr_cnt, aa, static_cast<uint16_t*>(O), nwg);
     return hipGetLastError();
 }
 

@@ -10,23 +10,27 @@
 // the (query, bucket) pairs are grouped by bucket: a workgroup stages one
 // bucket's keys and values in LDS once and runs the MFMAs for every query
 // that picked it, leaving one partial (fp32 max and denominator, the
-// unnormalised output per head as 12-bit integers times an fp32 scale) per
-// pair.  The gather kernel then attends sinks + window and merges the unit's
-// partials with a log-sum-exp combine.  The result is the same attention up
-// to the order of the softmax sums and the rounding of the partials (at most
-// half a step of 1/2047 of the row's largest value, no more than fp16's
-// rounding of that value).
+// unnormalised output per head as fp16 values times a power-of-two scale)
+// per pair.  The gather kernel then attends sinks + window and merges the
+// unit's partials with a log-sum-exp combine.  The result is the same
+// attention up to the order of the softmax sums and the fp16 rounding of each
+// partial value (relative 2^-11 of that value; the scale is exact).
 //
 // Steps of one pass (queries [q0, q0 + nqp) of every sequence):
-//   pairs    one wave per unit: its sorted long-range list -> (bucket, 64-bit
-//            key mask) pairs, a slot range from the pool, a rank per bin
+//   pairs    one wave per unit: its bucket records, or its sorted long-range
+//            list, -> (bucket, 64-bit key mask) pairs in the unit's staging row
+//   uscan    exclusive scan of the units' pair counts, in unit order: each
+//            unit's range of partial slots in the pool
+//   rank     a rank per pair in its bin (units past the pool: gathered whole)
 //   scan     exclusive scan of the per-bin pair counts
 //   scatter  pair slots grouped by bin
 //   leaf     one workgroup per bucket: keys and values in LDS, 16 query heads
 //            (whole GQA groups of 16 / G pairs) per MFMA column tile
 // A unit whose list the pairs step cannot take (not strictly ascending, a key
-// outside [sink end, window start), more than kBmUnitCap buckets, or a full
-// pool slice) keeps np = -1 and is gathered whole by the window kernel instead.
+// outside [sink end, window start), more than kBmUnitCap buckets) keeps
+// np = -1 and its list is gathered whole by the window kernel instead; so is
+// a unit whose pairs do not fit in the pool, from its list (np = -1) or from
+// the keys its bucket records name (np = -2).
 
 #include "lsa_launch.hpp"
 
@@ -36,13 +40,10 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// two rounded integers (|x| < 2^15) as the 16-bit halves of a word
-__device__ __forceinline__ uint32_t pk_i16(float a, float b) {
-    return ((uint32_t)__float2int_rn(a) & 0xFFFFu) | ((uint32_t)__float2int_rn(b) << 16);
+// two values rounded to nearest-even fp16, as the halves of a word
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
-// bits 4..11 of both 16-bit halves, as two bytes; bits 0..3 of both, as two nibbles
-__device__ __forceinline__ uint32_t hi_bytes2(uint32_t p) { return ((p >> 4) & 0xFFu) | ((p >> 12) & 0xFF00u); }
-__device__ __forceinline__ uint32_t lo_nibbles2(uint32_t p) { return (p & 0xFu) | ((p >> 12) & 0xF0u); }
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -239,28 +240,105 @@ __global__ __launch_bounds__(256) void bm_pairs_kernel(CacheView cv, const int64
         if (!bad && used > 0) np = bm_flush(tab[wid], tbl[wid], used, pl[wid], pm[wid], np);
     }
     if (bad || np > kBmUnitCap) np = -1;
-    // pair slots from pool slice ul % kBmCursors (one atomic per unit, spread over the slices' cursors)
-    uint32_t base = 0;
-    if (np > 0) {
-        const uint32_t slice = bm.pool_cap / kBmCursors, c = (uint32_t)(ul % kBmCursors);
-        uint32_t off = 0;
-        if (l == 0) off = atomicAdd(bm.lcnt + bm.nbins_pad + 2 + c, (uint32_t)np);
-        off = __shfl(off, 0);
-        if ((uint64_t)off + (uint64_t)np > (uint64_t)slice) np = -1;
-        base = c * slice + off;
-    }
+    // the unit's pairs go to its own staging row; pool slots and bin ranks come later (bm_rank_kernel)
     if (np > 0) {
         wave_lds_sync();
+        u32x4* st = bm.stage + ul * kBmUnitCap;
         for (int idx = l; idx < np; idx += 64) {
-            const uint32_t bin = (uint32_t)(bg * bm.leaves_max + pl[wid][idx]);
-            const uint32_t rk = atomicAdd(bm.lcnt + bin, 1u);
             const unsigned long long m = pm[wid][idx];
-            bm.rec[base + (uint32_t)idx] = u32x4{bin, rk, (uint32_t)m, (uint32_t)(m >> 32)};
+            st[idx] = u32x4{(uint32_t)(bg * bm.leaves_max + pl[wid][idx]), 0u, (uint32_t)m, (uint32_t)(m >> 32)};
+        }
+    }
+    if (l == 0) bm.unit_np[ul] = np;
+}
+
+// Exclusive scan of the units' pair counts (negative counts as 0) inside each
+// chunk of kBmScanChunk units, 16 per thread, and the chunk's total.
+__global__ __launch_bounds__(256) void bm_uscan_kernel(int64_t n_units, BmBuffers bm) {
+    __shared__ uint32_t ws[4];
+    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
+    const int64_t u0 = (int64_t)blockIdx.x * kBmScanChunk + tid * 16;
+    uint32_t v[16], s = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int np = u0 + j < n_units ? bm.unit_np[u0 + j] : 0;
+        v[j] = np > 0 ? (uint32_t)np : 0u;
+        s += v[j];
+    }
+    const uint32_t incl = (uint32_t)wave_incl_scan((int)s);
+    if (l == 63) ws[wid] = incl;
+    __syncthreads();
+    uint32_t wpre = 0;
+    for (int w = 0; w < wid; ++w) wpre += ws[w];
+    uint32_t run = wpre + incl - s;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (u0 + j < n_units) bm.unit_off[u0 + j] = run;
+        run += v[j];
+    }
+    if (tid == 255) bm.utot[blockIdx.x] = wpre + incl;
+}
+
+// Exclusive scan of n words by one 1024-thread workgroup, 1024 per step;
+// returns the total to every thread.
+__device__ uint32_t wg_exclusive_scan(const uint32_t* in, uint32_t* out, int64_t n, uint32_t* ws) {
+    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
+    uint32_t carry = 0;
+    for (int64_t c0 = 0; c0 < n; c0 += 1024) {
+        const int64_t c = c0 + tid;
+        const uint32_t v = c < n ? in[c] : 0u;
+        const uint32_t incl = (uint32_t)wave_incl_scan((int)v);
+        if (l == 63) ws[wid] = incl;
+        __syncthreads();
+        uint32_t wpre = 0, tot = 0;
+        for (int w = 0; w < 16; ++w) {
+            wpre += w < wid ? ws[w] : 0u;
+            tot += ws[w];
+        }
+        if (c < n) out[c] = carry + wpre + incl - v;
+        carry += tot;
+        __syncthreads();
+    }
+    return carry;
+}
+
+__global__ __launch_bounds__(1024) void bm_uscan_top_kernel(BmBuffers bm) {
+    __shared__ uint32_t ws[16];
+    wg_exclusive_scan(bm.utot, bm.ucsum, bm.nuch, ws);
+}
+
+// One wave per local unit: its first pool slot is the scan of the pair counts
+// before it; a unit whose pairs would run past the pool is gathered whole
+// instead (its token list, or, for a records row, the keys its records name),
+// and counted.  Every other unit takes a rank in each of its pairs' bins.
+__global__ __launch_bounds__(256) void bm_rank_kernel(AttArgs aa, BmBuffers bm) {
+    const int l = lane_id(), wid = threadIdx.x >> 6;
+    const int64_t ul = (int64_t)blockIdx.x * 4 + wid;
+    if (ul >= aa.n_units) return;
+    int np = bm.unit_np[ul];
+    const uint32_t off = bm.ucsum[ul / kBmScanChunk] + bm.unit_off[ul];
+    bool full = false;
+    if (np > 0 && (uint64_t)off + (uint64_t)np > (uint64_t)bm.pool_cap) {
+        full = true;
+        const int64_t rr = ul / aa.H_kv, b = rr / aa.nqp, i = aa.q0 + rr % aa.nqp;
+        const int64_t u = (b * aa.n_q + i) * aa.H_kv + ul % aa.H_kv;
+        // np > 0 with records means they passed the checks (else np would be -1)
+        np = (aa.bm_bcnt != nullptr && aa.bm_bcnt[u] >= 0) ? -2 : -1;
+    }
+    if (np > 0) {
+        u32x4* st = bm.stage + ul * kBmUnitCap;
+        for (int idx = l; idx < np; idx += 64) {
+            uint32_t* w = reinterpret_cast<uint32_t*>(st + idx);
+            w[1] = atomicAdd(bm.lcnt + w[0], 1u);
         }
     }
     if (l == 0) {
-        bm.unit_off[ul] = base;
+        bm.unit_off[ul] = off;
         bm.unit_np[ul] = np;
+        if (bm.fallback != nullptr && np < 0) {
+            atomicAdd(bm.fallback, 1u);
+            if (full) atomicAdd(bm.fallback + 1, 1u);
+        }
     }
 }
 
@@ -309,39 +387,20 @@ __global__ __launch_bounds__(256) void bm_scan_kernel(BmBuffers bm) {
 }
 
 // Exclusive scans of the chunk totals (pairs, then bins with pairs): one
-// workgroup, 1024 chunks per step; the number of bins with pairs (work
-// records) goes to lcnt[nbins_pad + 1].
+// workgroup; the number of bins with pairs (work records) goes to
+// lcnt[nbins_pad + 1].
 __global__ __launch_bounds__(1024) void bm_scan_top_kernel(BmBuffers bm, int64_t nch) {
     __shared__ uint32_t ws[16];
-    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
-    for (int half = 0; half < 2; ++half) {
-        const uint32_t* in = bm.ctot + half * nch;
-        uint32_t* out = bm.csum + half * nch;
-        uint32_t carry = 0;
-        for (int64_t c0 = 0; c0 < nch; c0 += 1024) {
-            const int64_t c = c0 + tid;
-            const uint32_t v = c < nch ? in[c] : 0u;
-            const uint32_t incl = (uint32_t)wave_incl_scan((int)v);
-            if (l == 63) ws[wid] = incl;
-            __syncthreads();
-            uint32_t wpre = 0, tot = 0;
-            for (int w = 0; w < 16; ++w) {
-                wpre += w < wid ? ws[w] : 0u;
-                tot += ws[w];
-            }
-            if (c < nch) out[c] = carry + wpre + incl - v;
-            carry += tot;
-            __syncthreads();
-        }
-        if (half == 1 && tid == 0) bm.lcnt[bm.nbins_pad + 1] = carry;
-    }
+    wg_exclusive_scan(bm.ctot, bm.csum, nch, ws);
+    const uint32_t nwork = wg_exclusive_scan(bm.ctot + nch, bm.csum + nch, nch, ws);
+    if (threadIdx.x == 0) bm.lcnt[bm.nbins_pad + 1] = nwork;
 }
 
 __device__ __forceinline__ uint32_t bm_bin_start(const BmBuffers& bm, uint32_t bin) {
     return bm.csum[bin / kBmScanChunk] + bm.loff[bin];
 }
 
-// One wave per local unit: its pair records go to their bin's place as
+// One wave per local unit: its staged pairs go to their bin's place as
 // (unit, pair slot, key mask).
 __global__ __launch_bounds__(256) void bm_scatter_kernel(AttArgs aa, BmBuffers bm) {
     const int l = lane_id(), wid = threadIdx.x >> 6;
@@ -350,10 +409,10 @@ __global__ __launch_bounds__(256) void bm_scatter_kernel(AttArgs aa, BmBuffers b
     const int np = bm.unit_np[ul];
     if (np <= 0) return;
     const uint32_t base = bm.unit_off[ul];
+    const u32x4* st = bm.stage + ul * kBmUnitCap;
     for (int idx = l; idx < np; idx += 64) {
-        const uint32_t p = base + (uint32_t)idx;
-        const u32x4 r = bm.rec[p];
-        bm.srec[bm_bin_start(bm, r[0]) + r[1]] = u32x4{(uint32_t)ul, p, r[2], r[3]};
+        const u32x4 r = st[idx];
+        bm.srec[bm_bin_start(bm, r[0]) + r[1]] = u32x4{(uint32_t)ul, base + (uint32_t)idx, r[2], r[3]};
     }
 }
 
@@ -572,7 +631,8 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
                     }
                 }
             }
-            // the row's scale: its largest magnitude over the D dims (4 lanes of the column)
+            // the row's power-of-two scale 2^e: its largest magnitude (over the column's 4 lanes) times 2^-e
+            // lies in [2^14, 2^15), so every value is an fp16 normal or a tiny subnormal and none overflows
             float amax = 0.f;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
@@ -580,40 +640,29 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
                 for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(acc[dt][v]));
             amax = fmaxf(amax, __shfl_xor(amax, 16));
             amax = fmaxf(amax, __shfl_xor(amax, 32));
+            int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 15 : 0;
+            e = e > -100 ? e : -100;
             if (col) {
                 const int64_t slot = (int64_t)p * G + hh;
-                // q = round(o * 2047 / amax): |q| <= 2047
-                const float qs = amax > 0.f ? 2047.f * __builtin_amdgcn_rcpf(amax) : 0.f;
+                const float q = ldexpf(1.0f, -e);
                 constexpr int NW = kPartialWords<D>;
-                uint32_t W[NW];
+                uint32_t* pw = bm.po + slot * (4 * NW);
 #pragma unroll
                 for (int m = 0; m < NDT / 2; ++m) {
                     // lane h holds dims 32m + 4h + [0,4) (A) and 32m + 16 + 4h + [0,4) (B); lanes h, h^1
                     // swap one of them so that each holds the 8 dims 32m + 8r + [0,8) of one reading lane r
-                    const u32x2 A = u32x2{pk_i16(acc[2 * m][0] * qs, acc[2 * m][1] * qs),
-                                          pk_i16(acc[2 * m][2] * qs, acc[2 * m][3] * qs)};
-                    const u32x2 Bv = u32x2{pk_i16(acc[2 * m + 1][0] * qs, acc[2 * m + 1][1] * qs),
-                                           pk_i16(acc[2 * m + 1][2] * qs, acc[2 * m + 1][3] * qs)};
+                    const u32x2 A = u32x2{pk_f16(acc[2 * m][0] * q, acc[2 * m][1] * q),
+                                          pk_f16(acc[2 * m][2] * q, acc[2 * m][3] * q)};
+                    const u32x2 Bv = u32x2{pk_f16(acc[2 * m + 1][0] * q, acc[2 * m + 1][1] * q),
+                                           pk_f16(acc[2 * m + 1][2] * q, acc[2 * m + 1][3] * q)};
                     const bool even = (h & 1) == 0;
                     const u32x2 send = even ? Bv : A;
                     const u32x2 got = u32x2{(uint32_t)__shfl_xor((int)send[0], 16), (uint32_t)__shfl_xor((int)send[1], 16)};
                     const u32x4 v8 = even ? u32x4{A[0], A[1], got[0], got[1]} : u32x4{got[0], got[1], Bv[0], Bv[1]};
-                    W[2 * m] = hi_bytes2(v8[0]) | (hi_bytes2(v8[1]) << 16);
-                    W[2 * m + 1] = hi_bytes2(v8[2]) | (hi_bytes2(v8[3]) << 16);
-                    W[NDT + m] = lo_nibbles2(v8[0]) | (lo_nibbles2(v8[1]) << 8) | (lo_nibbles2(v8[2]) << 16) |
-                                 (lo_nibbles2(v8[3]) << 24);
+                    const int r = (h >> 1) + 2 * (h & 1);   // the reading lane whose dims this lane holds
+                    *reinterpret_cast<u32x4*>(pw + r * NW + 4 * m) = v8;
                 }
-                const int r = (h >> 1) + 2 * (h & 1);   // the reading lane whose dims this lane holds
-                uint32_t* pw = bm.po + slot * (4 * NW) + r * NW;
-                if constexpr (NW % 4 == 0) {
-#pragma unroll
-                    for (int w = 0; w < NW; w += 4)
-                        *reinterpret_cast<u32x4*>(pw + w) = u32x4{W[w], W[w + 1], W[w + 2], W[w + 3]};
-                } else {
-#pragma unroll
-                    for (int w = 0; w < NW; w += 2) *reinterpret_cast<u32x2*>(pw + w) = u32x2{W[w], W[w + 1]};
-                }
-                if (h == 0) *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx, psum, amax * (1.0f / 2047.f), 0.f};
+                if (h == 0) *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx, psum, ldexpf(1.0f, e), 0.f};
             }
             rc = rn;
             rn = rnn;
@@ -630,12 +679,15 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
 hipError_t launch_bucket_partials(const CacheView& cv, const void* Q, const void* K, const void* V,
                                   const int64_t* q_pos, const int32_t* lr_idx, const int32_t* lr_cnt,
                                   const AttArgs& aa, const BmBuffers& bm, int D, hipStream_t st) {
-    const int64_t nclear = bm.nbins_pad + 2 + kBmCursors;
+    const int64_t nclear = bm.nbins_pad + 4;
     const unsigned cg = (unsigned)((nclear + 2047) / 2048 < 1024 ? (nclear + 2047) / 2048 : 1024);
     hipLaunchKernelGGL(bm_clear_kernel, dim3(cg), dim3(256), 0, st, bm.lcnt, nclear);
     if (aa.n_units == 0) return hipGetLastError();
     const unsigned ug = (unsigned)((aa.n_units + 3) / 4);
     hipLaunchKernelGGL(bm_pairs_kernel, dim3(ug), dim3(256), 0, st, cv, q_pos, lr_idx, lr_cnt, aa, bm);
+    hipLaunchKernelGGL(bm_uscan_kernel, dim3((unsigned)bm.nuch), dim3(256), 0, st, aa.n_units, bm);
+    hipLaunchKernelGGL(bm_uscan_top_kernel, dim3(1), dim3(1024), 0, st, bm);
+    hipLaunchKernelGGL(bm_rank_kernel, dim3(ug), dim3(256), 0, st, aa, bm);
     const int64_t nch = bm.nbins_pad / kBmScanChunk;
     hipLaunchKernelGGL(bm_scan_kernel, dim3((unsigned)nch), dim3(256), 0, st, bm);
     hipLaunchKernelGGL(bm_scan_top_kernel, dim3(1), dim3(1024), 0, st, bm, nch);

@@ -49,54 +49,58 @@ struct AttArgs {
     uint32_t tag;                 // distinct per call
     // bucket-major merge (null bm_np: plain gather of the long-range list)
     const uint32_t* bm_off;       // [n_units] first partial slot of the unit
-    const int32_t* bm_np;         // [n_units] partials of the unit; -1: gather its list instead
-    const uint32_t* bm_po;        // [slots, G, 3D/8] words: unnormalised partial output / its scale, packed
-                                  //   12-bit integers (kPartialWords layout)
-    const float* bm_ml;           // [slots, G, 4] partial max, denominator, scale (largest |output| / 2047), 0
+    const int32_t* bm_np;         // [n_units] partials of the unit; -1: gather its list; -2: gather its records' keys
+    const uint32_t* bm_po;        // [slots, G, D/2] words: unnormalised partial output / its scale, fp16
+                                  //   (kPartialWords layout)
+    const float* bm_ml;           // [slots, G, 4] partial max, denominator, scale (a power of two), 0
     const u32x4* bm_brec;         // optional: [units of the call, LSA_BUCKET_RECS] the selection's bucket records
     const int32_t* bm_bcnt;       // optional: their counts (-1: derive the pairs from the list)
 };
 
 // Workspace of one bucket-major pass.  A "bin" is one bucket of one (b, g):
-// (a pair's partial output row is kept as fp16 values in [-1, 1] times an
-// fp32 scale, the row's largest magnitude: half the bytes of fp32 with an
-// absolute rounding error of at most 2^-12 of that scale)
 // bin = (b * H_kv + g) * leaves_max + bucket id.  A pair is one (query, KV
-// head) unit together with one bucket it selected tokens from; pair slots
-// are handed out per unit from a pool of pool_cap.
+// head) unit together with one bucket it selected keys from.  The pairs of a
+// unit are staged in its own row of kBmUnitCap records; an exclusive scan of
+// the units' pair counts (in unit order) then gives every unit its range of
+// partial slots in the pool, so which slots a unit gets, and which units do
+// not fit the pool, never depend on the order in which waves run.
 struct BmBuffers {
     int64_t leaves_max;
     int64_t nbins;             // B * H_kv * leaves_max
     int64_t nbins_pad;         // nbins rounded up to the scan chunk
+    int64_t nuch;              // unit scan chunks: ceil(units / kBmScanChunk)
     uint32_t pool_cap;
-    uint32_t* lcnt;            // [nbins_pad + 2 + kBmCursors] pairs per bin, unused, the work count, then
-                               //   the pool cursors (cursor c hands out slots of pool slice c)
+    uint32_t* lcnt;            // [nbins_pad + 4] pairs per bin, then: unused, the work count, two unused
     uint32_t* loff;            // [nbins_pad] offset of the bin's pairs inside its scan chunk
     uint32_t* ctot;            // [2 * nbins_pad / chunk] pairs, then bins with pairs, per scan chunk
     uint32_t* csum;            // [2 * nbins_pad / chunk] exclusive scans of both halves of ctot
     uint32_t* gpre;            // [nbins_pad / 64] bins with pairs before each 64-bin group, inside its chunk
-    uint32_t* unit_off;        // [n_units]
-    int32_t* unit_np;          // [n_units]
-    u32x4* rec;                // [pool_cap] (bin, arrival rank in the bin, key mask lo, hi); mask bit j:
-                               //   key j of the bucket (member order) is listed
+    uint32_t* unit_off;        // [n_units] first pool slot of the unit (after the rank step; before it: the
+                               //   offset inside its scan chunk)
+    int32_t* unit_np;          // [n_units] pairs of the unit; -1: gather its token list instead; -2: gather the
+                               //   keys its bucket records name (records row whose pairs do not fit the pool)
+    uint32_t* utot;            // [nuch] pairs per unit scan chunk
+    uint32_t* ucsum;           // [nuch] their exclusive scan
+    u32x4* stage;              // [n_units, kBmUnitCap] the unit's pairs: (bin, rank in the bin, key mask lo, hi);
+                               //   mask bit j: key j of the bucket (member order) is listed
     u32x4* srec;               // [pool_cap] grouped by bin: (local unit, pair slot, key mask lo, hi)
     u32x4* work;               // [nbins, 17] one record per bin with pairs: (pair start, pairs, keys, b * H_kv + g),
                                //   then the bucket's 64 key tokens (member order; past the bucket: its first)
-    uint32_t* po;              // [pool_cap, G, 3D/8] packed 12-bit partial outputs (layout below)
+    uint32_t* po;              // [pool_cap, G, D/2] fp16 partial outputs (layout below)
     float* pml;                // [pool_cap, G, 4] (max, denominator, scale, 0)
+    uint32_t* fallback;        // optional, [2]: rows gathered whole are added to [0], those sent there because
+                               //   the pool was full also to [1]
 };
-// A partial output row of D values is stored as integers q = round(o / scale) with
-// scale = max |o| / 2047, so |q| <= 2047 fits 12 bits (worst-case error scale / 2, the
-// same as fp16's for the row's largest values).  The row is 4 runs of 3D/32 words,
-// run r holding the D/4 dims 32m + 8r + i (m < D/32, i < 8, value index 8m + i) of
-// one reading lane: first D/16 words of high bytes (bits 4..11 of q, two's
-// complement; value v in byte v % 4 of word v / 4), then D/32 words of low nibbles
-// (bits 0..3; value v in nibble v % 8 of word D/16 + v / 8).
+// A partial output row of D values o is stored as fp16 values o * 2^-e, the
+// power of two chosen so that the row's largest magnitude times 2^-e lies in
+// [2^14, 2^15) (no overflow, fp16's relative precision for every value down
+// to 2^-10 of the largest), and 2^e as the fp32 scale.  The row is 4 runs of
+// D/8 words, run r holding the D/4 dims 32m + 8r + i (m < D/32, i < 8) of one
+// reading lane, 8 dims (16 bytes) per m.
 template <int D>
-constexpr int kPartialWords = 3 * D / 32;   // words of one run (one reading lane)
-constexpr int kBmScanChunk = 4096;   // bins per workgroup of the offset scan
+constexpr int kPartialWords = D / 8;   // words of one run (one reading lane)
+constexpr int kBmScanChunk = 4096;   // bins (or units) per workgroup of an offset scan
 constexpr int kBmUnitCap = 256;      // most buckets one unit may take through the bucket-major path
-constexpr int kBmCursors = 256;      // pool slices, so that the units' slot requests spread over many words
 
 hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
                         const void* W, hipStream_t st, int blk0 = 0);
@@ -121,9 +125,9 @@ size_t pca_workspace_bytes(int D);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 hipError_t launch_pca(const void* K, bool bf16, int D, int64_t t_cap, int64_t T, int BH, void* W, float* eig,
                       void* workspace, hipStream_t st);
-hipError_t launch_attend_local(const void* Q, const void* K, const void* V, const int64_t* q_pos,
-                               const int32_t* lr_idx, const int32_t* lr_cnt, const AttArgs& aa, int D, void* O,
-                               hipStream_t st);
+hipError_t launch_attend_local(const CacheView& cv, const void* Q, const void* K, const void* V,
+                               const int64_t* q_pos, const int32_t* lr_idx, const int32_t* lr_cnt, const AttArgs& aa,
+                               int D, void* O, hipStream_t st);
 hipError_t launch_bucket_partials(const CacheView& cv, const void* Q, const void* K, const void* V,
                                   const int64_t* q_pos, const int32_t* lr_idx, const int32_t* lr_cnt,
                                   const AttArgs& aa, const BmBuffers& bm, int D, hipStream_t st);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(decl) == set(_lib.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert L.lsa_abi_version() == 5
+    assert L.lsa_abi_version() == 6
 
 
 def test_status_strings():
@@ -146,10 +146,10 @@ def test_bucket_major_validation_before_launch():
     cfg = SelectCfg(2048, 4, 1024, 0, 0, 0)
     fake = ctypes.c_void_p(0x1000)
 
-    def call(recs=None, rcnt=None, lay=lay, ws=1 << 40, cache_bytes=1 << 40):
+    def call(recs=None, rcnt=None, lay=lay, ws=1 << 40, cache_bytes=1 << 40, fallback=None, batch=1):
         return L.lsa_sparse_attend_bucket_major(ctypes.byref(lay), ctypes.byref(cfg), fake, cache_bytes, 8192,
-                                                fake, fake, fake, 8192, 8192, fake, 1, 4, fake, fake, recs, rcnt,
-                                                ctypes.c_float(0.1), fake, fake, ws, None)
+                                                fake, fake, fake, 8192, 8192, fake, batch, 4, fake, fake, recs, rcnt,
+                                                ctypes.c_float(0.1), fake, fake, ws, fallback, None)
 
     assert call(recs=fake) == 1                                     # records without counts
     assert call(rcnt=fake) == 1                                     # counts without records
@@ -157,6 +157,26 @@ def test_bucket_major_validation_before_launch():
     assert call(lay=_layout(dtype=_lib.LSA_F32)) == 8               # bf16 only
     assert call(cache_bytes=16) == 5                                # cache too small
     assert call(ws=16) == 5                                         # workspace too small
+    assert call(fallback=ctypes.c_void_p(0x1008)) == 4              # misaligned fallback counters
+    assert call(batch=1 << 21, cache_bytes=1 << 50) == 6                               # more (sequence, KV head) slices than a pass takes
+
+
+def test_bucket_major_workspace_grows_per_query():
+    """The workspace of a pass: fixed per-bin parts, plus per (query, KV head) a staging row of 256
+    16-byte pair records and 80 pool slots (16 B of pair record, G rows of fp16 values and 16 B of
+    max, denominator and scale)."""
+    L = _lib.lib()
+    lay = _layout()
+    cfg = SelectCfg(2048, 4, 1024, 0, 0, 0)
+    n1, n2 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.lsa_attend_bucket_major_workspace_bytes(ctypes.byref(lay), ctypes.byref(cfg), 1, 4096, 1 << 20,
+                                                     ctypes.byref(n1)) == 0
+    assert L.lsa_attend_bucket_major_workspace_bytes(ctypes.byref(lay), ctypes.byref(cfg), 1, 8192, 1 << 20,
+                                                     ctypes.byref(n2)) == 0
+    G, d = lay.n_q_heads // lay.n_kv_heads, lay.head_dim
+    per_unit = 4 + 4 + 256 * 16 + 80 * (16 + G * (2 * d) + G * 16)
+    units = 4096 * lay.n_kv_heads
+    assert abs((n2.value - n1.value) - units * per_unit) <= 8 * 256 + 4 * units // 4096 * 2 + 16
 
 
 def test_empty_calls_are_no_ops():

@@ -236,3 +236,122 @@ def test_bucket_major_rejects_fp32_and_small_workspace():
         lsa.sparse_attend_bucket_major(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cache, cfg.k, cfg.n_sinks,
                                        cfg.window)
     assert e.value.status == 8
+
+
+def _single_key_records(bm, q_pos, n_rec, seed):
+    """Per (query, KV head): n_rec distinct visible buckets, one eligible key of each, as bucket records
+    (leaf, mask low, mask high, 0; ascending leaf) and as the equivalent sorted token list."""
+    cfg, cache = bm["cfg"], bm["cache"]
+    meta = cache.meta()[0].cpu().numpy().astype(np.int64)
+    mem = cache.members()[0].cpu().numpy().astype(np.int64) & 0xFFFF
+    rng = np.random.default_rng(seed)
+    n_q = len(q_pos)
+    recs = np.zeros((1, n_q, cfg.H_kv, 256, 4), np.int64)
+    rcnt = np.zeros((1, n_q, cfg.H_kv), np.int32)
+    toks = np.full((1, n_q, cfg.H_kv, cfg.k), -1, np.int32)
+    for i, t in enumerate(q_pos):
+        nvis, sink_end, l0 = O.query_geometry(int(t), cfg.T // 2048, cfg.n_sinks, cfg.window)
+        for g in range(cfg.H_kv):
+            rows = []
+            for x in rng.permutation(64 * nvis):
+                blk = x // 64
+                size, off = meta[g, x] & 0xFF, (meta[g, x] >> 8) & 0x3FF
+                keys = blk * 2048 + 4 * mem[g, blk, off + np.arange(4 * size) // 4] + np.arange(4 * size) % 4
+                ok = np.flatnonzero((keys >= sink_end) & (keys < l0))
+                if ok.size == 0:
+                    continue
+                j = int(rng.choice(ok))
+                rows.append((int(x), j, int(keys[j])))
+                if len(rows) == n_rec:
+                    break
+            rows.sort()
+            for r, (x, j, tk) in enumerate(rows):
+                m = 1 << j
+                recs[0, i, g, r] = (x, m & 0xFFFFFFFF, m >> 32, 0)
+            rcnt[0, i, g] = len(rows)
+            tl = np.sort([tk for _, _, tk in rows])
+            toks[0, i, g, :len(tl)] = tl
+    recs_i32 = torch.from_numpy(recs.astype(np.uint32).view(np.int32))
+    return recs_i32, torch.from_numpy(rcnt), torch.from_numpy(toks)
+
+
+def test_pool_overflow_of_records_rows_without_lists(bm):
+    """Records rows of 200 single-key buckets each overflow a pass's pool of 80 slots per unit: the rows
+    past the pool (in unit order) are gathered from their records, never from their token rows (filled
+    with -7 here, as a selection that skips recorded rows leaves them unwritten); counted; and the output
+    repeats bit for bit and matches the oracle on the true token sets."""
+    cfg, G = bm["cfg"], bm["G"]
+    pos = np.array([cfg.T - 1 - 37 * i for i in range(16)])
+    recs, rcnt, toks = _single_key_records(bm, pos, 200, seed=17)
+    assert int(rcnt.min()) == 200
+    sel = torch.from_numpy(pos).to(DEV)
+    Qs = G["Q"][:, sel].contiguous()
+    qp = G["q_pos"][:, sel].contiguous()
+    cnt = rcnt.clone().to(DEV)
+    junk = torch.full((1, len(pos), cfg.H_kv, cfg.k), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(lsa.attend_bucket_major_workspace_bytes(bm["cache"], cfg.H_q, cfg.d, len(pos)),
+                     dtype=torch.uint8, device=DEV)
+    fc = torch.zeros(2, dtype=torch.int32, device=DEV)
+    args = (Qs, G["K"], G["V"], qp, junk, cnt, bm["cache"], cfg.k, cfg.n_sinks, cfg.window)
+    Ob = lsa.sparse_attend_bucket_major(*args, workspace=ws, bucket_records=(recs.to(DEV), rcnt.to(DEV)),
+                                        fallback_counts=fc)
+    Ob2 = lsa.sparse_attend_bucket_major(*args, workspace=ws, bucket_records=(recs.to(DEV), rcnt.to(DEV)))
+    Og = lsa.sparse_attend(Qs, G["K"], G["V"], qp, toks.to(DEV), cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window)
+    torch.cuda.synchronize()
+    units = len(pos) * cfg.H_kv
+    fit = (units * 80) // 200          # pool slots in unit order: the first `fit` units keep their pairs
+    print(f"[bm] overflow: fallback counts {fc.tolist()} (expected {units - fit})", flush=True)
+    assert fc.tolist() == [units - fit, units - fit]
+    assert torch.equal(Ob, Ob2)
+    d = float((Og.float() - Ob.float()).abs().max())
+    assert d <= 4e-3, d
+    err = _oracle_err(bm, Ob.double().cpu().numpy(), toks.numpy(), rcnt.numpy(),
+                      [(i, g) for i in range(len(pos)) for g in range(cfg.H_kv)], positions=pos)
+    print(f"[bm] overflow rows vs gather {d:.3e}, vs oracle {err:.3e}", flush=True)
+    assert err <= tol_for("bf16")
+
+
+def test_selection_path_has_no_fallbacks_and_repeats(bm):
+    """On the selection's own records (lists skipped), every row takes the bucket pass: no fallback, and
+    two calls give the same output bit for bit."""
+    cfg, G = bm["cfg"], bm["G"]
+    lr, cnt, (recs, rcnt) = lsa.select(G["Q"], bm["cache"], G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window,
+                                       strategy="fused", bucket_records=True, skip_recorded_lists=True)
+    fc = torch.zeros(2, dtype=torch.int32, device=DEV)
+    args = (G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, bm["cache"], cfg.k, cfg.n_sinks, cfg.window)
+    O1 = lsa.sparse_attend_bucket_major(*args, bucket_records=(recs, rcnt), fallback_counts=fc)
+    O2 = lsa.sparse_attend_bucket_major(*args, bucket_records=(recs, rcnt))
+    torch.cuda.synchronize()
+    assert fc.tolist() == [0, 0]
+    assert torch.equal(O1, O2)
+
+
+def test_outlier_value_channel(bm):
+    """Values with one channel 80 times larger (and one -64 times): every output still within the bf16
+    bound of the oracle, the bound widened by the output's own bf16 rounding (2^-8 of its magnitude);
+    the fp16 partials carry no error from one channel into another."""
+    cfg, G = bm["cfg"], bm["G"]
+    V = G["V"].clone()
+    V[..., 5] = (V[..., 5].float() * 80).to(V.dtype)
+    V[..., 70] = (V[..., 70].float() * -64).to(V.dtype)
+    Ob = lsa.sparse_attend_bucket_major(G["Q"], G["K"], V, G["q_pos"], bm["lr"], bm["cnt"], bm["cache"], cfg.k,
+                                        cfg.n_sinks, cfg.window)
+    torch.cuda.synchronize()
+    Vs = [V[0, g].double().cpu().numpy() for g in range(cfg.H_kv)]
+    rng = np.random.default_rng(23)
+    lr_c, cnt_c, Ob_c = bm["lr"].cpu().numpy(), bm["cnt"].cpu().numpy(), Ob.double().cpu().numpy()
+    scale = 1 / math.sqrt(cfg.d)
+    worst, worst_other = 0.0, 0.0
+    for _ in range(300):
+        i, g = int(rng.integers(2048, cfg.T)), int(rng.integers(0, cfg.H_kv))
+        ref = O.attend(bm["Q"][i, g * cfg.G:(g + 1) * cfg.G], bm["Ks"][g], Vs[g], i, lr_row(lr_c[0, i, g],
+                       int(cnt_c[0, i, g])), cfg.n_sinks, cfg.window, cfg.T // 2048, scale)
+        got = Ob_c[0, i, g * cfg.G:(g + 1) * cfg.G]
+        excess = np.abs(got - ref) / (tol_for("bf16") + 2.0 ** -8 * np.abs(ref))
+        worst = max(worst, float(excess.max()))
+        others = np.delete(np.abs(got - ref), [5, 70], axis=1)
+        worst_other = max(worst_other, float(others.max()))
+    print(f"[bm] outlier channels: worst error / bound {worst:.3f}, other channels max abs err {worst_other:.3e}",
+          flush=True)
+    assert worst <= 1.0
+    assert worst_other <= tol_for("bf16")
