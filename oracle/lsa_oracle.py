@@ -314,13 +314,35 @@ def _walk(ranked: Sequence[int], scores: np.ndarray, members, t, sink_end, l0, k
 
 
 def _boundary_margin(boundary, scores, weights_positive):
+    """Least nonzero |score(x) - score(boundary)| over the other leaves that hold
+    eligible tokens.  An exact tie (gap 0) is not a margin: it is decided by the
+    lowest-id rule, and both sides compute equal scores for equal centroids."""
     if boundary is None:
         return math.inf
     others = np.flatnonzero(weights_positive)
     others = others[others != boundary]
     if len(others) == 0:
         return math.inf
-    return float(np.abs(scores[others] - scores[boundary]).min())
+    gaps = np.abs(scores[others] - scores[boundary])
+    gaps = gaps[gaps > 0]
+    return float(gaps.min()) if len(gaps) else math.inf
+
+
+def _cut_margin(kept_scores, dropped_scores):
+    """Least nonzero gap between a kept and a dropped score at a beam cut.
+    Without a tie at the cut it is the lowest kept minus the highest dropped
+    score; with an exact tie there (broken by index) the nearest distinct
+    scores on either side of the tied value decide."""
+    kept = np.asarray(kept_scores, np.float64)
+    dropped = np.asarray(dropped_scores, np.float64)
+    if len(kept) == 0 or len(dropped) == 0:
+        return math.inf
+    kmin, dmax = float(kept.min()), float(dropped.max())
+    if kmin > dmax:
+        return kmin - dmax
+    above, below = kept[kept > kmin], dropped[dropped < kmin]
+    gaps = ([float(above.min()) - kmin] if len(above) else []) + ([kmin - float(below.max())] if len(below) else [])
+    return min(gaps) if gaps else math.inf
 
 
 def _weights_positive(cache, NLv, t, sink_end, l0):
@@ -335,7 +357,8 @@ def select_flat(qhat: np.ndarray, cache: Dict, t: int, k: int, n_sinks: int, win
     score(x) = max over the group's query heads of <q_hat_h, c_x> (ch.5 takes
     the max over heads).  Returns (LR int64 ascending, info dict with
     'boundary', 'scores', 'ranked' and, if asked, 'margin' = the least
-    |score(x) - score(boundary)| over other visible leaves with eligible tokens).
+    nonzero |score(x) - score(boundary)| over other visible leaves with eligible
+    tokens; exact ties are decided by the lowest-id rule).
     """
     nvis, sink_end, l0 = query_geometry(t, cache["n_blocks"], n_sinks, window)
     NLv = LEAVES_PER_BLOCK * nvis
@@ -364,8 +387,8 @@ def select_tree(qhat: np.ndarray, cache: Dict, t: int, k: int, n_sinks: int, win
     At each level the candidates are the visible children of the beam and the
     best `beam` by (score desc, index asc) are kept; the kept leaves are then
     expanded exactly as in the flat search.  info['cuts'] lists, per level
-    with more candidates than the beam, the gap between the last kept and the
-    first dropped score.
+    with more candidates than the beam, the least nonzero gap between a kept
+    and a dropped score (exact ties are decided by the index rule).
     """
     levels = cache["tree"]
     nvis, sink_end, l0 = query_geometry(t, cache["n_blocks"], n_sinks, window)
@@ -391,7 +414,7 @@ def select_tree(qhat: np.ndarray, cache: Dict, t: int, k: int, n_sinks: int, win
         sc = (cent @ q.T).max(axis=1)
         order = np.lexsort((ch, -sc))
         if len(order) > beam:
-            info["cuts"].append(float(sc[order[beam - 1]] - sc[order[beam]]))
+            info["cuts"].append(_cut_margin(sc[order[:beam]], sc[order[beam:]]))
         keep = order[:beam]
         frontier, fscore = ch[keep], sc[keep]
     # frontier is ranked by (score desc, id asc) already

@@ -26,15 +26,55 @@ def gpu_partitions(cache, b: int, g: int) -> List[List[List[int]]]:
     meta = cache.meta()[b, g].cpu().numpy().astype(np.int64)
     mem = cache.members()[b, g].cpu().numpy().astype(np.int64) & 0xFFFF
     nb = mem.shape[0]
+    sizes = (meta & 0xFF).reshape(nb, O.LEAVES_PER_BLOCK)
+    offs = ((meta >> 8) & 0x3FF).reshape(nb, O.LEAVES_PER_BLOCK)
     out = []
     for blk in range(nb):
-        leaves = []
-        for r in range(O.LEAVES_PER_BLOCK):
-            m = int(meta[blk * O.LEAVES_PER_BLOCK + r])
-            size, off = m & 0xFF, (m >> 8) & 0x3FF
-            leaves.append(sorted(mem[blk, off: off + size].tolist()))
-        out.append(leaves)
+        row = mem[blk]
+        out.append([sorted(row[o: o + z].tolist()) for o, z in zip(offs[blk], sizes[blk])])
     return out
+
+
+def check_partitions(clusters: List[List[List[int]]]) -> None:
+    """Every block: 64 buckets of 1..16 entries that cover its 512 entries once, numbered by smallest
+    member (the properties a Ward partition of a full block has, whatever the merges)."""
+    for blk, cl in enumerate(clusters):
+        assert len(cl) == O.LEAVES_PER_BLOCK, blk
+        sizes = [len(c) for c in cl]
+        assert min(sizes) >= 1 and max(sizes) <= O.MAX_BUCKET, (blk, sizes)
+        allm = sorted(i for c in cl for i in c)
+        assert allm == list(range(O.BLOCK_ENTRIES)), blk
+        firsts = [c[0] for c in cl]
+        assert firsts == sorted(firsts), blk
+
+
+CENT_ABS = 2.0 ** -16
+
+
+def centroid_excess(gpu_bf16: torch.Tensor, ref: np.ndarray) -> np.ndarray:
+    """Per component, |GPU - oracle| over what is allowed: one bf16 step of the oracle's (bf16-rounded)
+    value, or 2^-16 where that step is smaller (components below 2^-9).  The GPU sums unit latents in
+    fp32, whose absolute error on a component is ~1e-7 however small the component, so a near-zero
+    component may round to a neighbouring bf16 value a few (tiny) steps away; 2^-16 moves a score
+    of unit vectors by less than 2^-16, far inside the 1e-3 selection margin.  <= 1 everywhere passes."""
+    a = gpu_bf16.double().cpu().numpy()
+    b = np.asarray(ref, np.float64)
+    mag = np.abs(b)
+    step = np.where(mag > 0, np.ldexp(1.0, np.frexp(np.maximum(mag, 1e-300))[1] - 8), 0.0)
+    return np.abs(a - b) / np.maximum(step, CENT_ABS)
+
+
+def expand_records(recs: np.ndarray, n: int, members) -> np.ndarray:
+    """Tokens named by n bucket records (leaf, mask low, mask high, _): key j of a bucket is token
+    4 m + j % 4 of its (ascending) member entry m = members[leaf][j // 4]."""
+    out = []
+    for leaf, lo, hi, _ in recs[:n].astype(np.int64) & 0xFFFFFFFF:
+        mask = int(lo) | (int(hi) << 32)
+        mem = np.asarray(members[int(leaf)], np.int64)
+        for j in range(4 * len(mem)):
+            if (mask >> j) & 1:
+                out.append(4 * int(mem[j // 4]) + j % 4)
+    return np.sort(np.asarray(out, np.int64))
 
 
 def ward_first_divergence_margin(E: np.ndarray, gpu_clusters: List[List[int]]) -> float:

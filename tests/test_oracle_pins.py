@@ -482,3 +482,31 @@ def test_pca_captures_the_most_variance():
     for _ in range(20):
         Qr, _ = np.linalg.qr(rng.standard_normal((10, 4)))
         assert np.trace(Qr.T @ C @ Qr) <= best + 1e-9
+
+
+# ---------------------------------------------------------------- margins of the protocol
+
+def test_boundary_margin_ignores_exact_ties():
+    """Two leaves with the same centroid as the boundary leaf tie exactly (decided by id on both sides);
+    the margin is the least nonzero gap, here to a leaf 3e-4 below."""
+    cache = _hand_cache()
+    cache["cent"][7] = cache["cent"][3]
+    cache["cent"][9] = O.normalise(cache["cent"][3] - np.eye(64)[1] * 1e-3)   # slightly below in score
+    q = cache["cent"][3][None, :].copy()
+    # k = 32 tokens: leaf 3 (entries 24..31 = tokens 96..127) is the first and the boundary leaf
+    lr, info = O.select_flat(q, cache, 4096, k=32, n_sinks=0, window=1, with_margin=True)
+    assert info["boundary"] == 3 and list(lr) == list(range(96, 128))
+    s = info["scores"]
+    assert s[7] == s[3]
+    others = np.delete(np.abs(s - s[3]), [3, 7])
+    assert info["margin"] == pytest.approx(others.min()) and info["margin"] > 0
+
+
+def test_cut_margin_around_exact_ties():
+    # no tie at the cut: lowest kept minus highest dropped
+    assert O.lsa_oracle._cut_margin([0.9, 0.5], [0.4, 0.1]) == pytest.approx(0.1)
+    # a tie at the cut (0.5 kept and dropped, broken by index): the nearest distinct scores decide
+    assert O.lsa_oracle._cut_margin([0.9, 0.5003, 0.5], [0.5, 0.45]) == pytest.approx(3e-4)
+    assert O.lsa_oracle._cut_margin([0.9, 0.5], [0.5, 0.4999]) == pytest.approx(1e-4)
+    # only tied values on both sides: nothing can reorder them
+    assert O.lsa_oracle._cut_margin([0.5, 0.5], [0.5]) == math.inf
