@@ -4,14 +4,16 @@
 Default workload: one bf16 prefill layer at T = 1,048,576 (8 KV / 40 query
 heads, head_dim 128, 4096-topic mixture, k = 2048, 4 sinks, window 1024,
 flat search).  One step = build_buckets over all keys + select and
-sparse_attend for every query (in chunks of 65,536 queries), with K, V, Q
-and W already resident in HBM.  Also measured: the decode step at 1M context
-(16 sequences, one query each) and, with --config 5, the 10M-token tree
-prefill.
+sparse_attend for every query (in chunks of whole bucket-major passes), with
+K, V, Q and W already resident in HBM.  The same run then measures the
+decode step at 1M context (16 sequences, one query each, as HIP-graph
+replays), and the 10M-token tree layer (16,384 topics, beam 64; a fixed
+--steps-10m timed steps after --warmup-10m) with its 8-query decode step on
+the shared cache, each under its own key of the one JSON line.
 
-Prints one JSON line (metric, value in tokens/s, roofline of the dominant
-kernel measured with HIP events on the launch stream, and the CPU oracle
-baseline timed on a bounded sample).
+Prints one JSON line (metric, value = the 1M layer's tokens/s, roofline of
+the dominant call measured with HIP events on the launch stream, and the CPU
+oracle baseline timed on a bounded sample).
 """
 
 from __future__ import annotations
@@ -93,7 +95,8 @@ def prefill_step(cfg, G, ws, timers=None, tree=False, O=None):
             e = tm["attend"].span()
         if "bm" in ws:
             lsa.sparse_attend_bucket_major(Qc, G["K"], G["V"], qp, lr, cnt, cache, cfg.k, cfg.n_sinks, cfg.window,
-                                           O=O[:, i0:i1], workspace=ws["bm"], bucket_records=res[2] if recs else None)
+                                           O=O[:, i0:i1], workspace=ws["bm"], bucket_records=res[2] if recs else None,
+                                           fallback_counts=ws.get("fallback"))
         else:
             lsa.sparse_attend(Qc, G["K"], G["V"], qp, lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window,
                               O=O[:, i0:i1])
@@ -129,9 +132,10 @@ def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=2048, records=False):
     of queries, without the window part (added by selected_bytes' local term):
     per pass, the K and V rows of every distinct bucket any of its queries
     listed, once; per (query, KV head, bucket) pair, the G query rows and
-    the partial row (G x (3 d / 2 + 16) bytes: 12-bit values) written once
-    and read once; the long-range lists read once, or with the selection's
-    bucket records one 16-byte record per pair instead."""
+    the partial row (G x (2 d + 16) bytes: fp16 values, max, denominator,
+    scale) written once and read once; the long-range lists read once, or
+    with the selection's bucket records one 16-byte record per pair
+    instead."""
     info = cache.info()
     nb = info.n_blocks
     eleaf = cache.entry_leaf()[0].long()                     # [H_kv, nb, 512]
@@ -159,7 +163,7 @@ def bucket_major_bytes(cfg, lr, cnt, cache, n_pass, sub=2048, records=False):
             kv_rows += int((size.view(-1)[u] * 4).sum())
     row = d * 2
     lists = pairs * 16 if records else int(cnt.clamp_min(0).sum()) * 4
-    return kv_rows * 2 * row + pairs * G * row + 2 * pairs * G * (3 * d // 2 + 16) + lists
+    return kv_rows * 2 * row + pairs * G * row + 2 * pairs * G * (2 * d + 16) + lists
 
 
 _CPU_CTX = {}
@@ -221,7 +225,7 @@ def cpu_baseline(cfg, inp_cpu, n_units=1500):
     wall_per_unit = t_units / n_units
     full_s = (cfg.T // 2048) * cfg.H_kv * wall_per_block + \
         cfg.T * cfg.H_kv * wall_per_unit * max(1.0, mean_leaves / leaves_sample)
-    return dict(value=cfg.T / full_s, unit="tokens/s", cores=procs, kind="oracle",
+    return dict(value=cfg.T / full_s, unit="tokens/s", cores=cores, processes=procs, kind="oracle",
                 sample=(f"the same topic-mixture recipe generated on the CPU at T={nb * 2048}: oracle Ward on its {nb} "
                         f"blocks of KV head 0 ({t_ward:.1f}s wall) and select+attend for {n_units} (query, KV head) "
                         f"units at {(nb - 1) * 64} visible buckets ({t_units:.1f}s wall), each spread over {procs} "
@@ -250,7 +254,7 @@ def traffic_for(kernel_src, key: str):
     return rec.get("bytes_per_launch") if rec.get("source_sha256") == h else None
 
 
-def run_prefill(args, cid):
+def run_prefill(args, cid, steps, warmup):
     cfg = get_config(cid)
     dev = torch.device("cuda:0")
     log(f"generating {cfg.name} on the GPU")
@@ -275,7 +279,8 @@ def run_prefill(args, cid):
                                         min(CHUNK, n_q), cfg.H_q)
     ws["sel"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws["cache"] = cache0.buf
-    attend = args.attend
+    attend = args.attend if cfg.dtype == "bf16" else "gather"   # the bucket-major call is bf16 only
+    ws["fallback"] = torch.zeros(2, dtype=torch.int32, device=dev)
     if attend != "gather" and args.bucket_records != "off":
         ws["skip_lists"] = args.bucket_records == "only"
         # the selection's bucket records for the bucket-major attention (one chunk's worth)
@@ -310,18 +315,18 @@ def run_prefill(args, cid):
         ws.pop("skip_lists", None)
     ws["cnt_sum"] = 0
     ws["bm_bytes"] = 0
-    log("warmup")
-    for _ in range(args.warmup):
+    log(f"warmup ({warmup} steps)")
+    for _ in range(warmup):
         ws["cnt_sum"] = 0
         ws["bm_bytes"] = 0
         prefill_step(cfg, G, ws, tree=tree, O=O)
-    lr_total = ws.pop("cnt_sum") if args.warmup > 0 else None
+    lr_total = ws.pop("cnt_sum") if warmup > 0 else None
     torch.cuda.synchronize()
     timers = {k: Timer() for k in ("build", "select", "attend")}
-    log(f"timing {args.steps} steps")
+    log(f"timing {steps} steps")
     t0 = time.perf_counter()
     torch.cuda.synchronize()
-    for _ in range(args.steps):
+    for _ in range(steps):
         prefill_step(cfg, G, ws, timers, tree=tree, O=O)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -330,9 +335,11 @@ def run_prefill(args, cid):
         ws["bm_bytes"] = 0
         prefill_step(cfg, G, ws, tree=tree, O=O)
         lr_total = ws.pop("cnt_sum")
-    ms_step = wall * 1000 / args.steps
-    att_ms = timers["attend"].total_ms() / args.steps
-    n_att = timers["attend"].count() // args.steps
+    fallbacks = ws["fallback"].tolist()
+    n_runs = steps + (warmup if warmup > 0 else 1)   # warm-up steps, or the one step that counts the bytes
+    ms_step = wall * 1000 / steps
+    att_ms = timers["attend"].total_ms() / steps
+    n_att = timers["attend"].count() // steps
     csrc = os.path.join(ROOT, "sparse_attention_indexing_latent_amd", "csrc")
     if attend == "bucket":
         # the window part as in the gather accounting, with no long-range rows
@@ -348,8 +355,9 @@ def run_prefill(args, cid):
     per_launch = alg_bytes / n_att
     res = dict(
         metric="1-layer LSA prefill tokens/s at 1M & 10M ctx; decode queries/s at 1M (1 GPU)",
-        value=cfg.T / (ms_step / 1e3), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-        ms_per_step=ms_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        value=cfg.T / (ms_step / 1e3), unit="tokens/s", n_gpus=1, steps=steps, warmup=warmup,
+        ms_per_step=ms_step, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16" if cfg.dtype == "bf16" else "f32",
         data="synthetic (seeded topic-mixture keys, random-init projection)",
         config={"workload": cfg.name, "T": cfg.T, "H_kv": cfg.H_kv, "H_q": cfg.H_q, "head_dim": cfg.d,
                 "k": cfg.k, "n_sinks": cfg.n_sinks, "window": cfg.window, "search": cfg.search,
@@ -363,6 +371,10 @@ def run_prefill(args, cid):
                   "traffic": traffic, "alg_bytes_per_launch": per_launch,
                   "avg_launch_ms": att_ms / n_att, "launches_per_step": n_att},
     )
+    if attend == "bucket":
+        # (query, KV head) rows the bucket-major call gathered whole, over every step run (warm-up included),
+        # and of those the rows whose pairs did not fit in a pass's pool
+        res["bucket_major_fallbacks"] = {"rows": fallbacks[0], "pool_full": fallbacks[1], "steps_run": n_runs}
     if cfg.decode_batch:
         res["decode_shared"] = decode_on_cache(cfg, G, inp, ws["cache"], tree)
     return res, cfg, inp
@@ -416,8 +428,21 @@ def decode_on_cache(cfg, G, inp, cache_buf, tree):
         step()
     torch.cuda.synchronize()
     ms = graph_replay_ms(step, (lr, cnt, O), 20)
+    # algorithmic bytes of a step: per (query, KV head), the centroids of every scored tree level (the
+    # children of the beam, where they outnumber it) and the gathered key and value rows
+    units = nq * cfg.H_kv
+    info = cache.info()
+    node_reads = 0
+    if tree:
+        sizes = [info.level_size[lev] for lev in range(info.n_levels)]
+        for lev in range(info.n_levels - 1):
+            cand = min(2 * cfg.beam, sizes[lev])
+            node_reads += cand if cand > cfg.beam else 0
+    rows = float(cnt.clamp_min(0).float().mean()) + cfg.window + cfg.n_sinks
+    alg = units * (node_reads * 64 * 2 + rows * 2 * cfg.d * 2)
     return dict(queries_per_s=nq / (ms / 1e3), ms_per_step=ms, timing="hip graph replay", batch=nq, search=search,
-                beam=cfg.beam, mean_lr=float(cnt.float().mean()))
+                beam=cfg.beam, mean_lr=float(cnt.float().mean()), alg_bytes_per_step=alg,
+                hbm_frac=(alg / (ms / 1e3) / 1e9) / HBM_PEAK_GBS)
 
 
 def run_crossover(args):
@@ -577,7 +602,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", type=int, default=4, choices=[2, 4, 5])
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 4, 5],
+                    help="prefill workload: 4 (1M, the default, followed by the 1M decode and the 10M layer), "
+                         "5 (10M tree layer alone), or the parity configs 1 (8K fp32) and 2 (131K)")
     ap.add_argument("--attend", default="auto", choices=["auto", "gather", "bucket"],
                     help="prefill attention: per-query gather, bucket-major (each bucket's K/V read once per pass), "
                          "or auto (bucket-major when a bucket is expected in >= 2 pairs per pass)")
@@ -595,6 +622,9 @@ def main():
     ap.add_argument("--cross-T", type=int, nargs="+", default=[1 << 20, 1 << 21, 1 << 22, 1 << 23, 10485760])
     ap.add_argument("--cross-B", type=int, nargs="+", default=[1, 4, 16, 64])
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-10m", action="store_true", help="skip the 10M-token tree layer of the default run")
+    ap.add_argument("--steps-10m", type=int, default=2, help="timed steps of the 10M layer (about 8 s each)")
+    ap.add_argument("--warmup-10m", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run one plain 1 GiB device copy (a known-size kernel for scaling HBM counters)")
@@ -616,21 +646,30 @@ def main():
         dst.copy_(src)            # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
-    res, cfg, inp = run_prefill(args, args.config)
+    res, cfg, inp = run_prefill(args, args.config, args.steps, args.warmup)
     log(f"prefill {res['value']:.0f} tokens/s, {res['ms_per_step']:.1f} ms/step")
     del inp
     torch.cuda.empty_cache()
-    if not args.no_decode:
+    if not args.no_decode and args.config == 4:
         try:
             res["decode_1m"] = run_decode(args)
             log(f"decode {res['decode_1m']}")
         except torch.cuda.OutOfMemoryError as exc:  # pragma: no cover
             res["decode_1m"] = {"error": str(exc)[:200]}
         torch.cuda.empty_cache()
+    if not args.no_10m and args.config == 4:
+        # the metric's second prefill context: the 10M-token tree layer, with a fixed small step count
+        r10, _, inp10 = run_prefill(args, 5, args.steps_10m, args.warmup_10m)
+        del inp10
+        torch.cuda.empty_cache()
+        res["prefill_10m"] = {k: r10[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step", "config",
+                                                   "breakdown_ms", "roofline", "bucket_major_fallbacks",
+                                                   "decode_shared") if k in r10}
+        log(f"prefill 10M {r10['value']:.0f} tokens/s, {r10['ms_per_step']:.1f} ms/step")
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         cfg_cpu = get_config(args.config)
-        small = cfg_cpu.scaled(T=64 * 2048)
+        small = cfg_cpu.scaled(T=min(cfg_cpu.T, 64 * 2048))
         inp_cpu = layer_inputs(small, seed=0)
         res["cpu_baseline"] = cpu_baseline(cfg_cpu, inp_cpu)
     else:
