@@ -426,6 +426,9 @@ constexpr int kScanChunk = 8;       // tiles per staged chunk
 constexpr int kFNeg = 8;
 constexpr int kFBins = kFNeg + 64;
 constexpr int kFStride = kFBins + 1;   // odd: neighbouring queries fall in different banks
+constexpr int kMaxLeavesI = 0x7FFFFFFF;
+constexpr float kFltMax = 3.402823466e38f;
+constexpr float kPosInf = __builtin_huge_valf();
 
 // multiplications by powers of two are exact, so bin(s) >= b  <=>  s >= edge(b)
 __device__ __forceinline__ int fscan_bin(float s) {
@@ -477,7 +480,7 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
     __shared__ __align__(16) uint4 stage[2][kScanChunk * 128];   // 2 x 16 KB
     __shared__ __align__(16) uint4 smeta[2][kScanChunk * 4];     // 16 meta words per tile
     __shared__ uint32_t hist[kScanQ * kFStride];
-    __shared__ int wmax[4];
+    __shared__ int wmax[4], wmin[4];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
     const int64_t b = blockIdx.z, g = blockIdx.y;
     const int64_t bg = b * sa.H_kv + g;
@@ -510,18 +513,27 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
         }
     }
     uint32_t* hrow[2] = {hist + (wid * 32 + n) * kFStride, hist + (wid * 32 + 16 + n) * kFStride};
+    uint64_t* sub0 = cand + u[0] * kCandStride + h * kSubCap;
+    uint64_t* sub1 = cand + u[1] * kCandStride + h * kSubCap;
     for (int j = tid; j < kScanQ * kFStride; j += 256) hist[j] = 0u;
-    // tiles visible to any query of the workgroup
+    // tiles visible to any query of the workgroup, and to all of them
     const int wm = wave_max_i(max(NLv[0], NLv[1]));
-    if (l == 0) wmax[wid] = wm;
+    const int wn = wave_min_i(min(qv[0] ? NLv[0] : kMaxLeavesI, qv[1] ? NLv[1] : kMaxLeavesI));
+    if (l == 0) {
+        wmax[wid] = wm;
+        wmin[wid] = wn;
+    }
     __syncthreads();
     const int maxNLv = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const int minNLv = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
     const int ntl = maxNLv / 16;
     const int nch = (ntl + kScanChunk - 1) / kScanChunk;
     const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
     const u32x4* msrc = reinterpret_cast<const u32x4*>(cv.meta + bg * cv.s_meta);
     int fb[2] = {0, 0};
-    float fe[2] = {kNegInf, kNegInf};
+    // floor edges: every score is a candidate before the floor rises (-FLT_MAX: a masked -inf is not);
+    // a column without a query never has one
+    float fe[2] = {qv[0] ? -kFltMax : kPosInf, qv[1] ? -kFltMax : kPosInf};
     int base[2] = {0, 0};   // length of this lane's sub-list (h) of its query's candidate list
     // staging: thread tid copies words tid + 256 j (j < 4) of a chunk and, if tid < 32, meta word tid;
     // tiles past the last one repeat it
@@ -579,35 +591,46 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
             const int tn = tt + 1 < tend ? tt + 1 : tt;
             a0 = as_bf16x8(sb[tn * 128 + l]);
             a1 = as_bf16x8(sb[tn * 128 + 64 + l]);
-            // visible buckets of each query scoring at or above its floor's edge (few once it has risen)
-            uint32_t m[2];
+            // buckets past a query's visible leaves never become candidates (only the last tiles hold such)
+            if (x0 + 16 > minNLv) {
 #pragma unroll
-            for (int cg = 0; cg < 2; ++cg) {
-                const int lim = qv[cg] ? NLv[cg] - xb : 0;   // buckets xb + v with v < lim are visible
-                m[cg] = (best[cg][0] >= fe[cg] && 0 < lim ? 1u : 0u) | (best[cg][1] >= fe[cg] && 1 < lim ? 2u : 0u) |
-                        (best[cg][2] >= fe[cg] && 2 < lim ? 4u : 0u) | (best[cg][3] >= fe[cg] && 3 < lim ? 8u : 0u);
+                for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        best[cg][v] = (qv[cg] && xb + v < NLv[cg]) ? best[cg][v] : kNegInf;
             }
-            if (m[0] | m[1]) {
+            // a bucket scoring at or above its query's floor edge is a candidate (few once the floor has
+            // risen): a lane's 8 values are tested through their maximum first, and a lane holding any
+            // candidate walks its set bits one at a time (the wave runs as many rounds as its busiest lane)
+            const float lm0 = fmaxf(fmaxf(best[0][0], best[0][1]), fmaxf(best[0][2], best[0][3]));
+            const float lm1 = fmaxf(fmaxf(best[1][0], best[1][1]), fmaxf(best[1][2], best[1][3]));
+            if (lm0 >= fe[0] || lm1 >= fe[1]) {
+                uint32_t bits = 0;
+#pragma unroll
+                for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) bits |= best[cg][v] >= fe[cg] ? 1u << (4 * cg + v) : 0u;
                 const int64_t lo = (int64_t)(x0 / kLeavesPerBlock) * kBlockTokens;
                 const uint4 m4 = sm[tt * 4 + h];
-                const uint32_t mm[4] = {m4.x, m4.y, m4.z, m4.w};
-#pragma unroll
-                for (int cg = 0; cg < 2; ++cg) {
-                    if (m[cg]) {
-                        // this lane's sub-list h of its query's candidate list
-                        const bool elig = lo >= lo_ok[cg] && lo + kBlockTokens <= hi_ok[cg];
-                        uint64_t* sub = cand + u[cg] * kCandStride + h * kSubCap;
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            if (m[cg] & (1u << v)) {
-                                if (base[cg] < kSubCap) sub[base[cg]] = rank_key(best[cg][v], (uint32_t)(xb + v));
-                                ++base[cg];
-                                if (elig)
-                                    atomicAdd(&hrow[cg][fscan_bin(best[cg][v])], (uint32_t)kPool * (mm[v] & 0xFFu));
-                            }
-                        }
-                    }
-                }
+                const bool el0 = lo >= lo_ok[0] && lo + kBlockTokens <= hi_ok[0];
+                const bool el1 = lo >= lo_ok[1] && lo + kBlockTokens <= hi_ok[1];
+                do {
+                    const int j = __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    const bool c1 = j >= 4;
+                    const int v = j & 3;
+                    const float s0 = c1 ? best[1][0] : best[0][0], s1 = c1 ? best[1][1] : best[0][1];
+                    const float s2 = c1 ? best[1][2] : best[0][2], s3 = c1 ? best[1][3] : best[0][3];
+                    const float sc = v == 0 ? s0 : (v == 1 ? s1 : (v == 2 ? s2 : s3));
+                    const uint32_t mv = v == 0 ? m4.x : (v == 1 ? m4.y : (v == 2 ? m4.z : m4.w));
+                    // this lane's sub-list h of the query's candidate list
+                    const int bs = c1 ? base[1] : base[0];
+                    uint64_t* sub = c1 ? sub1 : sub0;
+                    if (bs < kSubCap) sub[bs] = rank_key(sc, (uint32_t)(xb + v));
+                    base[0] += c1 ? 0 : 1;
+                    base[1] += c1 ? 1 : 0;
+                    if (c1 ? el1 : el0) atomicAdd((c1 ? hrow[1] : hrow[0]) + fscan_bin(sc), (uint32_t)kPool * (mv & 0xFFu));
+                } while (bits != 0u);
             }
         }
         if (c + 1 < nch) LSA_STORE_CHUNK((c + 1) & 1)
@@ -616,7 +639,7 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
 #pragma unroll
         for (int cg = 0; cg < 2; ++cg) {
             fb[cg] = max(fb[cg], fscan_cross_bin(hrow[cg], h, (uint32_t)sa.k));
-            fe[cg] = fb[cg] >= 1 ? fscan_edge(fb[cg]) : kNegInf;   // bin(s) >= fb  <=>  s >= fe
+            if (qv[cg]) fe[cg] = fb[cg] >= 1 ? fscan_edge(fb[cg]) : -kFltMax;   // bin(s) >= fb  <=>  s >= fe
         }
         __syncthreads();
     }
