@@ -57,20 +57,20 @@ template <int D>
 __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t ul, int npl, int hh, int h,
                                                       float& m_run, float& l_run, f32x4* acc) {
     constexpr int NC = D / 16;
-    constexpr int NW = kPartialWords<D>;
+    constexpr int MW = D / 32;
     constexpr int MN = 4;   // partials in flight
     const int64_t s0 = aa.bm_off[ul];
     for (int s = 0; s < npl; s += MN) {
         f32x4 ml[MN];
-        u32x4 w[MN][NW / 4];
+        u32x4 w[MN][MW];
 #pragma unroll
         for (int j = 0; j < MN; ++j) {
-            const int64_t slot = (s0 + (s + j < npl ? s + j : 0)) * aa.G + hh;
-            ml[j] = *reinterpret_cast<const f32x4*>(aa.bm_ml + slot * 4);
-            // this lane's run: dims 32m + 8h + [0,8) for every m, fp16
-            const u32x4* pw = reinterpret_cast<const u32x4*>(aa.bm_po + slot * (4 * NW) + h * NW);
+            const int64_t pp = s0 + (s + j < npl ? s + j : 0);
+            ml[j] = *reinterpret_cast<const f32x4*>(aa.bm_ml + (pp * aa.G + hh) * 4);
+            // this lane's dims 32m + 8h + [0,8) for every m, fp16 (layout [pair][m][head][lane])
+            const u32x4* pw = reinterpret_cast<const u32x4*>(aa.bm_po + (pp * MW * aa.G + hh) * 16 + h * 4);
 #pragma unroll
-            for (int x = 0; x < NW / 4; ++x) w[j][x] = pw[x];
+            for (int m = 0; m < MW; ++m) w[j][m] = pw[(int64_t)m * aa.G * 4];
         }
 #pragma unroll
         for (int j = 0; j < MN; ++j) {

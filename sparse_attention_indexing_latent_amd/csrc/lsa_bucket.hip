@@ -40,9 +40,25 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// two values rounded to nearest-even fp16, as the halves of a word
-__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kSwap16 = 0x401F;   // ds_swizzle pattern: lane ^ 16 inside each half-wave
+
+// two values rounded to nearest-even fp16 / bf16 (one gfx950 conversion each), as the halves of a word
+__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// acc + both bf16 halves of a word (exact products by 1.0, fp32 sum)
+__device__ __forceinline__ float sum2_bf16(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), acc,
+                                           false);
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -401,7 +417,7 @@ __device__ __forceinline__ uint32_t bm_bin_start(const BmBuffers& bm, uint32_t b
 }
 
 // One wave per local unit: its staged pairs go to their bin's place as
-// (unit, pair slot, key mask).
+// (query row of the unit's first head, pair slot, key mask).
 __global__ __launch_bounds__(256) void bm_scatter_kernel(AttArgs aa, BmBuffers bm) {
     const int l = lane_id(), wid = threadIdx.x >> 6;
     const int64_t ul = (int64_t)blockIdx.x * 4 + wid;
@@ -409,10 +425,13 @@ __global__ __launch_bounds__(256) void bm_scatter_kernel(AttArgs aa, BmBuffers b
     const int np = bm.unit_np[ul];
     if (np <= 0) return;
     const uint32_t base = bm.unit_off[ul];
+    // the row of the group's first query head in Q [B, n_q, H_q, d] (fits 32 bits: checked on the host)
+    const int64_t rr = ul / aa.H_kv, b = rr / aa.nqp, i = aa.q0 + rr % aa.nqp;
+    const uint32_t qrow = (uint32_t)((b * aa.n_q + i) * aa.H_q + (ul % aa.H_kv) * aa.G);
     const u32x4* st = bm.stage + ul * kBmUnitCap;
     for (int idx = l; idx < np; idx += 64) {
         const u32x4 r = st[idx];
-        bm.srec[bm_bin_start(bm, r[0]) + r[1]] = u32x4{(uint32_t)ul, base + (uint32_t)idx, r[2], r[3]};
+        bm.srec[bm_bin_start(bm, r[0]) + r[1]] = u32x4{qrow, base + (uint32_t)idx, r[2], r[3]};
     }
 }
 
@@ -498,7 +517,7 @@ __device__ __forceinline__ int vt_slot(int j) {
 // column n = pair n / G, head n % G; S^T tiles are 16 keys x 16 columns
 // (rows 4h + v), O^T tiles 16 dims x 16 columns.
 template <int D>
-__global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void bm_leaf_kernel(CacheView cv, const uint16_t* __restrict__ Q,
                                                       const uint16_t* __restrict__ K,
                                                       const uint16_t* __restrict__ V, AttArgs aa, BmBuffers bm) {
     using LL = LeafLds<D>;
@@ -506,7 +525,7 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
     __shared__ __align__(16) uint8_t lds[LL::BYTES];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
     const int G = aa.G, GP = 16 / G;
-    const float sl2 = aa.scale;
+    const float sl2 = aa.scale * kLog2e;   // scores in log2 units
     const uint32_t n_work = bm.lcnt[bm.nbins_pad + 1];
     for (uint32_t wk = blockIdx.x; wk < n_work; wk += gridDim.x) {
         const u32x4* rec = bm.work + (int64_t)wk * 17;
@@ -545,7 +564,7 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
         const int pi = n / G, hh = n % G;
         // software pipeline over this wave's groups: the records two groups
         // ahead and the Q rows one group ahead are in flight while a group
-        // is computed (a record with unit ~0: no pair in this column)
+        // is computed (a record with query row ~0: no pair in this column)
 #define LSA_BM_REC(GRP, R)                                                                  \
     {                                                                                        \
         const uint32_t pidx_ = (GRP) * GP + pi;                                              \
@@ -554,15 +573,10 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
     }
 #define LSA_BM_Q(R, QV)                                                                     \
     {                                                                                        \
-        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) QV[ks] = u32x4{0u, 0u, 0u, 0u};    \
-        if (R[0] != ~0u) {                                                                   \
-            const int64_t ul_ = R[0];                                                        \
-            const int64_t gq_ = ul_ % aa.H_kv, rq_ = ul_ / aa.H_kv;                          \
-            const int64_t bq_ = rq_ / aa.nqp, iq_ = aa.q0 + rq_ % aa.nqp;                    \
-            const uint16_t* qrow_ = Q + ((bq_ * aa.n_q + iq_) * aa.H_q + gq_ * G + hh) * D;  \
-            _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) QV[ks] =                       \
-                *reinterpret_cast<const u32x4*>(qrow_ + 32 * ks + 8 * h);                    \
-        }                                                                                    \
+        /* a column without a pair reads Q row 0 (always present; its results are dropped) */ \
+        const uint16_t* qrow_ = Q + ((int64_t)(R[0] != ~0u ? R[0] : 0u) + hh) * D;          \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) QV[ks] =                           \
+            *reinterpret_cast<const u32x4*>(qrow_ + 32 * ks + 8 * h);                        \
     }
         u32x4 rc, rn, qf[KS], qn[KS];
         LSA_BM_REC(wid, rc)
@@ -574,8 +588,11 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
             LSA_BM_REC(grp + 8, rnn)
             const bool col = rc[0] != ~0u;
             const uint32_t p = rc[1];
-            const unsigned long long mask = col ? ((unsigned long long)rc[3] << 32) | rc[2] : 0ull;
-            // S^T = K Q^T over the bucket's keys
+            // this lane's 16 mask bits: key 16 tt + 4 h + v of the bucket is bit 4 tt + v of mk
+            const uint32_t mlo = col ? rc[2] : 0u, mhi = col ? rc[3] : 0u;
+            const uint32_t mk = ((mlo >> (4 * h)) & 0xFu) | (((mlo >> (16 + 4 * h)) & 0xFu) << 4) |
+                                (((mhi >> (4 * h)) & 0xFu) << 8) | (((mhi >> (16 + 4 * h)) & 0xFu) << 12);
+            // S^T = K Q^T over the bucket's keys, in log2 units (scale * log2 e): p = 2^(s - max)
             f32x4 s[4];
             float mx = kNegInf;
 #pragma unroll
@@ -591,29 +608,25 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
                 }
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int j = 16 * tt + 4 * h + v;
-                    s[tt][v] = ((mask >> j) & 1ull) ? s[tt][v] * sl2 : kNegInf;
-                    mx = fmaxf(mx, s[tt][v]);
+                    // a key the pair does not list: min with -inf (with +inf it stays)
+                    const float bias = __uint_as_float((((~mk >> (4 * tt + v)) & 1u) << 31) | 0x7F800000u);
+                    s[tt][v] = __builtin_elementwise_minimum(s[tt][v] * sl2, bias);
                 }
+                mx = fmax_nc(mx, fmax_nc(fmax_nc(s[tt][0], s[tt][1]), fmax_nc(s[tt][2], s[tt][3])));
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // P (bf16, as the PV MFMA uses it) and its sum
+            mx = fmax_nc(mx, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), kSwap16)));
+            mx = fmax_nc(mx, __shfl_xor(mx, 32));
+            // P (bf16, as the PV MFMA uses it) and its sum over the same rounded values
             uint32_t pk[4][2];
             float psum = 0.f;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                uint16_t q4[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float e = mx > kNegInf && s[tt][v] > kNegInf ? __expf(s[tt][v] - mx) : 0.f;
-                    q4[v] = f32_to_bf16(e);
-                    psum += bf16_to_f32(q4[v]);
-                }
-                pk[tt][0] = (uint32_t)q4[0] | ((uint32_t)q4[1] << 16);
-                pk[tt][1] = (uint32_t)q4[2] | ((uint32_t)q4[3] << 16);
+                pk[tt][0] = cvt_pk_bf16(exp2_hw(s[tt][0] - mx), exp2_hw(s[tt][1] - mx));
+                pk[tt][1] = cvt_pk_bf16(exp2_hw(s[tt][2] - mx), exp2_hw(s[tt][3] - mx));
+                psum = sum2_bf16(pk[tt][0], psum);
+                psum = sum2_bf16(pk[tt][1], psum);
             }
-            psum += __shfl_xor(psum, 16);
+            psum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(psum), kSwap16));
             psum += __shfl_xor(psum, 32);
             // O^T = V^T P^T
             f32x4 acc[NDT];
@@ -631,38 +644,51 @@ __global__ __launch_bounds__(256) void bm_leaf_kernel(CacheView cv, const uint16
                     }
                 }
             }
-            // the row's power-of-two scale 2^e: its largest magnitude (over the column's 4 lanes) times 2^-e
-            // lies in [2^14, 2^15), so every value is an fp16 normal or a tiny subnormal and none overflows
-            float amax = 0.f;
+            // the fp16 row is stored unscaled when every value of the wave's pairs fits (a lane's largest
+            // magnitude below 2^15 and, unless zero, at least 2^-8); otherwise each row gets a power-of-two
+            // scale 2^e with its largest magnitude times 2^-e in [2^14, 2^15): no value overflows, and every
+            // value down to 2^-10 of the largest keeps fp16's relative precision
+            float lmax = 0.f;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
+                lmax = fmax_nc(lmax, fmax_nc(fmax_nc(fabsf(acc[dt][0]), fabsf(acc[dt][1])),
+                                             fmax_nc(fabsf(acc[dt][2]), fabsf(acc[dt][3]))));
+            const bool plain = lmax < 32768.f && (lmax >= 0.00390625f || lmax == 0.f);
+            float osc = 1.f;
+            if (__ballot(col && !plain) != 0ull) {
+                float amax = fmax_nc(lmax, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lmax), kSwap16)));
+                amax = fmax_nc(amax, __shfl_xor(amax, 32));
+                int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 15 : 0;
+                e = e > -100 ? e : -100;
+                const float q = ldexpf(1.0f, -e);
+                osc = ldexpf(1.0f, e);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(acc[dt][v]));
-            amax = fmaxf(amax, __shfl_xor(amax, 16));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
-            int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 15 : 0;
-            e = e > -100 ? e : -100;
+                for (int dt = 0; dt < NDT; ++dt) acc[dt] *= q;
+            }
             if (col) {
                 const int64_t slot = (int64_t)p * G + hh;
-                const float q = ldexpf(1.0f, -e);
-                constexpr int NW = kPartialWords<D>;
-                uint32_t* pw = bm.po + slot * (4 * NW);
+                constexpr int MW = D / 32;
+                // partial layout [pair][m][head][reading lane], 16 bytes each: one store instruction writes
+                // every head of a pair's group m as one contiguous run (G x 64 bytes)
+                uint32_t* pw = bm.po + ((int64_t)p * MW * G + hh) * 16;
 #pragma unroll
                 for (int m = 0; m < NDT / 2; ++m) {
                     // lane h holds dims 32m + 4h + [0,4) (A) and 32m + 16 + 4h + [0,4) (B); lanes h, h^1
                     // swap one of them so that each holds the 8 dims 32m + 8r + [0,8) of one reading lane r
-                    const u32x2 A = u32x2{pk_f16(acc[2 * m][0] * q, acc[2 * m][1] * q),
-                                          pk_f16(acc[2 * m][2] * q, acc[2 * m][3] * q)};
-                    const u32x2 Bv = u32x2{pk_f16(acc[2 * m + 1][0] * q, acc[2 * m + 1][1] * q),
-                                           pk_f16(acc[2 * m + 1][2] * q, acc[2 * m + 1][3] * q)};
+                    const u32x2 A = u32x2{cvt_pk_f16(acc[2 * m][0], acc[2 * m][1]), cvt_pk_f16(acc[2 * m][2], acc[2 * m][3])};
+                    const u32x2 Bv = u32x2{cvt_pk_f16(acc[2 * m + 1][0], acc[2 * m + 1][1]),
+                                           cvt_pk_f16(acc[2 * m + 1][2], acc[2 * m + 1][3])};
                     const bool even = (h & 1) == 0;
                     const u32x2 send = even ? Bv : A;
-                    const u32x2 got = u32x2{(uint32_t)__shfl_xor((int)send[0], 16), (uint32_t)__shfl_xor((int)send[1], 16)};
+                    const u32x2 got = u32x2{(uint32_t)__builtin_amdgcn_ds_swizzle((int)send[0], kSwap16),
+                                            (uint32_t)__builtin_amdgcn_ds_swizzle((int)send[1], kSwap16)};
                     const u32x4 v8 = even ? u32x4{A[0], A[1], got[0], got[1]} : u32x4{got[0], got[1], Bv[0], Bv[1]};
                     const int r = (h >> 1) + 2 * (h & 1);   // the reading lane whose dims this lane holds
-                    *reinterpret_cast<u32x4*>(pw + r * NW + 4 * m) = v8;
+                    *reinterpret_cast<u32x4*>(pw + (int64_t)m * G * 16 + r * 4) = v8;
                 }
-                if (h == 0) *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx, psum, ldexpf(1.0f, e), 0.f};
+                // the max back in natural units (the merge and the window part use e^x)
+                if (h == 0)
+                    *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx * kLn2, psum, osc, 0.f};
             }
             rc = rn;
             rn = rnn;

@@ -83,6 +83,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Maximum without the canonicalisation fmaxf needs (v_maximum3_f32 on gfx950; a NaN operand gives NaN,
+// which the scores and outputs here never hold), and 2^x as the bare hardware instruction (results
+// below 2^-126 flush to 0: softmax weights that small never matter).
+__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <typename T> __device__ __forceinline__ float load_f32(const T* p);
 template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }

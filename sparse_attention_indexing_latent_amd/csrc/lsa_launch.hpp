@@ -51,7 +51,7 @@ struct AttArgs {
     const uint32_t* bm_off;       // [n_units] first partial slot of the unit
     const int32_t* bm_np;         // [n_units] partials of the unit; -1: gather its list; -2: gather its records' keys
     const uint32_t* bm_po;        // [slots, G, D/2] words: unnormalised partial output / its scale, fp16
-                                  //   (kPartialWords layout)
+                                  //   (layout: see BmBuffers)
     const float* bm_ml;           // [slots, G, 4] partial max, denominator, scale (a power of two), 0
     const u32x4* bm_brec;         // optional: [units of the call, LSA_BUCKET_RECS] the selection's bucket records
     const int32_t* bm_bcnt;       // optional: their counts (-1: derive the pairs from the list)
@@ -83,7 +83,8 @@ struct BmBuffers {
     uint32_t* ucsum;           // [nuch] their exclusive scan
     u32x4* stage;              // [n_units, kBmUnitCap] the unit's pairs: (bin, rank in the bin, key mask lo, hi);
                                //   mask bit j: key j of the bucket (member order) is listed
-    u32x4* srec;               // [pool_cap] grouped by bin: (local unit, pair slot, key mask lo, hi)
+    u32x4* srec;               // [pool_cap] grouped by bin: (Q row of the unit's first head, pair slot, key mask
+                               //   lo, hi)
     u32x4* work;               // [nbins, 17] one record per bin with pairs: (pair start, pairs, keys, b * H_kv + g),
                                //   then the bucket's 64 key tokens (member order; past the bucket: its first)
     uint32_t* po;              // [pool_cap, G, D/2] fp16 partial outputs (layout below)
@@ -91,14 +92,15 @@ struct BmBuffers {
     uint32_t* fallback;        // optional, [2]: rows gathered whole are added to [0], those sent there because
                                //   the pool was full also to [1]
 };
-// A partial output row of D values o is stored as fp16 values o * 2^-e, the
-// power of two chosen so that the row's largest magnitude times 2^-e lies in
-// [2^14, 2^15) (no overflow, fp16's relative precision for every value down
-// to 2^-10 of the largest), and 2^e as the fp32 scale.  The row is 4 runs of
-// D/8 words, run r holding the D/4 dims 32m + 8r + i (m < D/32, i < 8) of one
-// reading lane, 8 dims (16 bytes) per m.
-template <int D>
-constexpr int kPartialWords = D / 8;   // words of one run (one reading lane)
+// A partial output row of D values o is stored as fp16 values o * 2^-e and
+// 2^e as the fp32 scale: e = 0 when every value fits fp16 with its relative
+// precision (largest magnitude below 2^15 and, unless zero, at least 2^-8),
+// else the power of two with the largest magnitude times 2^-e in [2^14, 2^15)
+// (no overflow, fp16's relative precision for every value down to 2^-10 of
+// the largest).  Layout [pair][m < D/32][head][reading lane r < 4], 16 bytes
+// each: the 8 dims 32m + 8r + [0,8) of (pair, head); a pair's heads of one m
+// are contiguous, so the writes of a group m and the merge's reads are whole
+// G x 64-byte runs.
 constexpr int kBmScanChunk = 4096;   // bins (or units) per workgroup of an offset scan
 constexpr int kBmUnitCap = 256;      // most buckets one unit may take through the bucket-major path
 
