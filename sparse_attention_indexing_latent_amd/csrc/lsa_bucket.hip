@@ -684,11 +684,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                                             (uint32_t)__builtin_amdgcn_ds_swizzle((int)send[1], kSwap16)};
                     const u32x4 v8 = even ? u32x4{A[0], A[1], got[0], got[1]} : u32x4{got[0], got[1], Bv[0], Bv[1]};
                     const int r = (h >> 1) + 2 * (h & 1);   // the reading lane whose dims this lane holds
-                    *reinterpret_cast<u32x4*>(pw + (int64_t)m * G * 16 + r * 4) = v8;
+                    // streaming stores: the pass's partials (tens of GB) never stay in the caches, and
+                    // bypassing them keeps the Q rows and K/V there
+                    __builtin_nontemporal_store(v8, reinterpret_cast<u32x4*>(pw + (int64_t)m * G * 16 + r * 4));
                 }
                 // the max back in natural units (the merge and the window part use e^x)
                 if (h == 0)
-                    *reinterpret_cast<f32x4*>(bm.pml + slot * 4) = f32x4{mx * kLn2, psum, osc, 0.f};
+                    __builtin_nontemporal_store(f32x4{mx * kLn2, psum, osc, 0.f},
+                                                reinterpret_cast<f32x4*>(bm.pml + slot * 4));
             }
             rc = rn;
             rn = rnn;
