@@ -263,6 +263,26 @@ lsa_status lsa_sparse_attend(const lsa_layout* layout, const lsa_select_cfg* cfg
                              const int32_t* lr_idx, const int32_t* lr_cnt, float scale, void* O,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* lsa_sparse_attend for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call with the same arguments and result, except that
+ * the split-key partials (needed when few (query, KV head) units are split
+ * over their key lists, as in decode) live in a fixed 4 MiB device array of
+ * the library instead of a caller workspace.  The call allocates nothing;
+ * its first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress, with the device current; no stream work), so a
+ * caller that captures graphs makes one call before capturing.  A call that
+ * would need more than 4 MiB (lsa_attend_workspace_bytes; only for G = 8
+ * with d = 128 and fewer than 1024 units) fails with LSA_ERR_WORKSPACE
+ * before anything is queued.  All calls on one device share its array:
+ * calls that overlap in time on one device race and must be ordered (one
+ * stream, or events).  Nothing in the array needs clearing between calls. */
+lsa_status lsa_sparse_attend_noalloc(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* Q,
+                                     const void* K, const void* V, int64_t t_cap, int64_t T,
+                                     const int64_t* q_pos, int64_t batch, int64_t n_q,
+                                     const int32_t* lr_idx, const int32_t* lr_cnt, float scale, void* O,
+                                     void* stream);
+
 /* Workspace bytes lsa_sparse_attend_bucket_major needs to process n_q_pass
  * queries per sequence in one pass (a cache for t_max tokens).  Host only.
  * Dominated by the pool of partials, 80 slots per (query, KV head) on

@@ -24,7 +24,8 @@ from . import _lib
 from ._lib import (LsaError, Layout, SelectCfg, CacheInfo, LSA_BF16, LSA_F32, LSA_SEARCH_FLAT, LSA_SEARCH_TREE,
                    LSA_STRATEGY_AUTO, LSA_STRATEGY_FUSED, LSA_STRATEGY_MATERIALIZED)
 
-__all__ = ["build_buckets", "select", "sparse_attend", "sparse_attend_bucket_major", "LsaCache", "LsaError",
+__all__ = ["build_buckets", "select", "sparse_attend", "sparse_attend_noalloc", "sparse_attend_bucket_major",
+           "LsaCache", "LsaError",
            "make_layout", "select_cfg", "library_path", "select_workspace_bytes", "attend_workspace_bytes",
            "attend_bucket_major_workspace_bytes", "pca_projection"]
 
@@ -261,6 +262,26 @@ def sparse_attend(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torc
                                    ctypes.c_float(scale), _ptr(O), _ptr(workspace) if n.value > 0 else ctypes.c_void_p(0),
                                    workspace.numel() if (workspace is not None and n.value > 0) else 0,
                                    _stream(Q.device)))
+    return O
+
+
+def sparse_attend_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, q_pos: torch.Tensor,
+                          lr_idx: torch.Tensor, lr_cnt: torch.Tensor, T: int, k: int, n_sinks: int, window: int,
+                          scale: Optional[float] = None, O: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sparse_attend with the library's own fixed device scratch instead of a workspace (the C call
+    allocates nothing; pass O to keep this wrapper allocation-free too)."""
+    assert Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()
+    B, n_q, H_q, d = Q.shape
+    _, H_kv, t_cap, _ = K.shape
+    layout = make_layout(d, H_kv, H_q, Q.dtype)
+    cfg = select_cfg(k, n_sinks, window)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if O is None:
+        O = torch.empty_like(Q)
+    _lib.check(_lib.lib().lsa_sparse_attend_noalloc(ctypes.byref(layout), ctypes.byref(cfg), _ptr(Q), _ptr(K), _ptr(V),
+                                                    t_cap, T, _ptr(q_pos), B, n_q,
+                                                    _ptr(lr_idx) if k > 0 else ctypes.c_void_p(0), _ptr(lr_cnt),
+                                                    ctypes.c_float(scale), _ptr(O), _stream(Q.device)))
     return O
 
 

@@ -38,7 +38,8 @@ STATUS_NAMES = {
 EXPORTS = [
     "lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_extend_buckets", "lsa_select_workspace_bytes",
     "lsa_select",
-    "lsa_attend_workspace_bytes", "lsa_sparse_attend", "lsa_attend_bucket_major_workspace_bytes",
+    "lsa_attend_workspace_bytes", "lsa_sparse_attend", "lsa_sparse_attend_noalloc",
+    "lsa_attend_bucket_major_workspace_bytes",
     "lsa_sparse_attend_bucket_major", "lsa_pca_workspace_bytes", "lsa_pca_projection", "lsa_status_string",
     "lsa_last_error", "lsa_abi_version",
 ]
@@ -96,6 +97,8 @@ def lib():
     L.lsa_attend_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, P(sz)]
     L.lsa_sparse_attend.argtypes = [P(Layout), P(SelectCfg), vp, vp, vp, i64, i64, vp, i64, i64, vp, vp,
                                     ctypes.c_float, vp, vp, sz, vp]
+    L.lsa_sparse_attend_noalloc.argtypes = [P(Layout), P(SelectCfg), vp, vp, vp, i64, i64, vp, i64, i64, vp, vp,
+                                            ctypes.c_float, vp, vp]
     L.lsa_attend_bucket_major_workspace_bytes.argtypes = [P(Layout), P(SelectCfg), i64, i64, i64, P(sz)]
     L.lsa_sparse_attend_bucket_major.argtypes = [P(Layout), P(SelectCfg), vp, sz, i64, vp, vp, vp, i64, i64, vp,
                                                  i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp, vp]
@@ -103,7 +106,7 @@ def lib():
     L.lsa_pca_projection.argtypes = [P(Layout), vp, i64, i64, i64, vp, vp, vp, sz, vp]
     for name in ("lsa_cache_bytes", "lsa_cache_describe", "lsa_build_buckets", "lsa_extend_buckets",
                  "lsa_select_workspace_bytes",
-                 "lsa_select", "lsa_attend_workspace_bytes", "lsa_sparse_attend",
+                 "lsa_select", "lsa_attend_workspace_bytes", "lsa_sparse_attend", "lsa_sparse_attend_noalloc",
                  "lsa_attend_bucket_major_workspace_bytes", "lsa_sparse_attend_bucket_major",
                  "lsa_pca_workspace_bytes", "lsa_pca_projection"):
         getattr(L, name).restype = ctypes.c_int

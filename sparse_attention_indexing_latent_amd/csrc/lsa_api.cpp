@@ -286,6 +286,11 @@ void select_ws(const lsa_layout* L, const lsa_select_cfg* C, int64_t B, int64_t 
 
 }  // namespace
 
+namespace lsa {
+// Records a failure for lsa_last_error() from another translation unit of the library.
+lsa_status set_error(lsa_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace lsa
+
 extern "C" {
 
 int32_t lsa_abi_version(void) { return LSA_ABI_VERSION; }

@@ -104,6 +104,9 @@ struct BmBuffers {
 constexpr int kBmScanChunk = 4096;   // bins (or units) per workgroup of an offset scan
 constexpr int kBmUnitCap = 256;      // most buckets one unit may take through the bucket-major path
 
+// Sets lsa_last_error()'s message (and returns s) for a failure found outside lsa_api.cpp.
+lsa_status set_error(lsa_status s, const char* msg);
+
 hipError_t launch_build(const CacheView& cv, const void* K, bool bf16, int64_t t_cap, int d, int B, int H_kv,
                         const void* W, hipStream_t st, int blk0 = 0);
 hipError_t launch_tree(const CacheView& cv, const int64_t* level_off, const int64_t* level_size, int B, int H_kv,
