@@ -97,8 +97,11 @@ typedef enum lsa_strategy {
                                       buckets above a rising per-query bound, then an exact
                                       finish over those (fp32: a bound pass, then a
                                       candidate pass)                                     */
-    LSA_STRATEGY_MATERIALIZED = 2  /* every score written to the workspace, then an exact
-                                      radix select (decode: few queries, many buckets)   */
+    LSA_STRATEGY_MATERIALIZED = 2  /* every score and every 16-bucket tile maximum written
+                                      to the workspace; the tile maxima bound a small
+                                      candidate set that is ranked exactly (an exact radix
+                                      select when it is not small); decode: few queries,
+                                      many buckets                                        */
 } lsa_strategy;
 
 /* Shape of the layer.  latent_dim, pool, block_entries, mean_bucket and
@@ -235,8 +238,8 @@ lsa_status lsa_select_workspace_bytes(const lsa_layout* layout, const lsa_select
  * bucket: {leaf id, key mask bits 0..31, bits 32..63, 0}, ascending in leaf
  * id, where key j of a bucket is token 4 members[j / 4] + j % 4 of its block
  * and is in lr_idx's row exactly when bit j is set.  bucket_cnt holds the
- * number of records; it is -1 where the row came from the exact fallback, the
- * materialized strategy or a trivial case (no ranking needed, or position
+ * number of records; it is -1 where the row came from the exact fallback or
+ * a trivial case (no ranking needed, or position
  * < 0).  lsa_sparse_attend_bucket_major takes them in place of the token
  * rows' bucket lookups. */
 lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const void* cache,

@@ -174,8 +174,8 @@ lsa_status check_cfg(const lsa_select_cfg* C, int64_t T) {
 }
 
 struct SelectWs {
-    size_t off_qhat, off_tau, off_cnt, off_counters, off_cand, off_fb, off_scores, zero_off, zero_bytes, total;
-    int64_t score_stride;
+    size_t off_qhat, off_tau, off_cnt, off_counters, off_cand, off_fb, off_scores, off_tmax, zero_off, zero_bytes, total;
+    int64_t score_stride, tmax_stride;
     int fb_slots;
     int strategy;
 };
@@ -280,6 +280,8 @@ void select_ws(const lsa_layout* L, const lsa_select_cfg* C, int64_t B, int64_t 
         w.off_fb = o;   o = align256(o + (size_t)units * 4);
         w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
         w.off_scores = o; o = align256(o + (size_t)units * w.score_stride * 4);
+        w.tmax_stride = w.score_stride / 16;
+        w.off_tmax = o; o = align256(o + (size_t)units * w.tmax_stride * 4);
     }
     w.total = o;
 }
@@ -478,6 +480,8 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     sb.fb_list = reinterpret_cast<int*>(wb + w.off_fb);
     sb.scores = reinterpret_cast<float*>(wb + w.off_scores);
     sb.score_stride = w.score_stride;
+    sb.tmax = reinterpret_cast<float*>(wb + w.off_tmax);
+    sb.tmax_stride = w.tmax_stride;
     sb.fb_slots = w.fb_slots;
     lsa::SelArgs sa;
     sa.k = cfg->k;

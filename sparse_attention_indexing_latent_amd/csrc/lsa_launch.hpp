@@ -33,6 +33,8 @@ struct SelectBuffers {
     int* counters;
     float* scores;
     int64_t score_stride;
+    float* tmax;           // materialized: the largest score of each 16-bucket tile
+    int64_t tmax_stride;
     int fb_slots;
 };
 

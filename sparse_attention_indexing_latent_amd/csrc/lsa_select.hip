@@ -1228,59 +1228,14 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
 // Few queries against many buckets (decode).  Two kernels:
 //
 // score_all_kernel, grid (units x splits), unit-major: every visible bucket
-// score of a (query, KV head), written to the workspace (fp32).  A pure
-// stream over the tile-swizzled centroids, up to 128 tiles per workgroup.
+// score of a (query, KV head) and the largest score of every 16-bucket tile,
+// written to the workspace (fp32).  A pure stream over the tile-swizzled
+// centroids, kScoreTiles tiles per workgroup.
 //
-// score_select_kernel, one 1024-thread workgroup per unit, records held in
-// registers: packed record = offset key << 7 | eligible tokens per bucket
-// (the key is monotone in the score).  Finds a key bound L such that the
-// buckets keyed >= L hold at least k eligible tokens while those above L's
-// bin hold fewer, with at most kCandCap buckets at or above L (weighted
-// histograms of 3072, 2048 and 4 bins, each refining the boundary bin of the
-// one before), collects those buckets, and wave 0 ranks them by (score
-// desc, id asc), walks them to k tokens and expands.  Every bucket keyed
-// below L ranks after every collected one, so the walk ends exactly where a
-// walk over all buckets would.  Too many ties at L send the unit to the
-// exact radix path.
+// decode_finish_kernel, one workgroup per unit: bounds the candidates with
+// the tile maxima, ranks and walks them, and writes the tokens in order
+// (below).
 constexpr int kScoreTiles = 16;   // tiles (16 buckets each) per scoring workgroup: small workgroups overlap best
-constexpr int kThrThreads = 1024;
-constexpr int kThrBins = 3072;    // level 0: key >> 13
-constexpr int kThrGoal = 128;     // refine the bound while more buckets than this sit at or above it
-constexpr int kThrRegs = 32;      // records per thread (one chunk = 32768 buckets)
-constexpr int kMaxBlockWords = 1024;   // blocks a unit may see: 64 x 1024 (2^27 tokens)
-constexpr int kMaskSlots = 384;        // distinct blocks among the taken buckets
-
-// Workgroup-wide exclusive scan over 1024 threads; tot = the sum.  scratch: 16 ints.
-__device__ __forceinline__ int wg1024_excl_scan(int v, int* scratch, int& tot) {
-    const int l = lane_id(), wid = threadIdx.x >> 6;
-    const int inc = wave_incl_scan(v);
-    if (l == 63) scratch[wid] = inc;
-    __syncthreads();
-    int base = 0;
-    tot = 0;
-    for (int w = 0; w < 16; ++w) {
-        const int s = scratch[w];
-        base += w < wid ? s : 0;
-        tot += s;
-    }
-    __syncthreads();
-    return base + inc - v;
-}
-
-// Offset key of a score: monotone non-decreasing in the score and in
-// [0, 3 * 2^23) (s + 2 clamped to [0.5, 4)).  Equal keys need not mean equal
-// scores, so the key only bounds the candidate set; ranking uses the score.
-__device__ __forceinline__ uint32_t thr_key(float s) {
-    const float v = fminf(fmaxf(s + 2.0f, 0.5f), 3.99999976f);
-    return __float_as_uint(v) - 0x3F000000u;
-}
-
-__device__ __forceinline__ unsigned long long shfl_down_u64(unsigned long long v, int o) {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_down(lo, o);
-    hi = __shfl_down(hi, o);
-    return ((unsigned long long)hi << 32) | lo;
-}
 
 // Eligible tokens of a bucket whose block lies inside or outside [sink_end,
 // l0); a block straddling an edge (at most two) needs its member lists.
@@ -1302,10 +1257,19 @@ __device__ __forceinline__ bool unit_is_trivial(int64_t t, const Geom& q, int k)
     return t < 0 || k == 0 || (int64_t)k >= total;
 }
 
+// Largest of the 16 scores of a tile held as 4 values in each of the lanes 0, 16, 32, 48 (in every
+// lane on return).  Exact: the maximum does not depend on the order it is taken in.
+__device__ __forceinline__ float tile_max(const f32x4& v) {
+    float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    return fmaxf(m, __shfl_xor(m, 32));
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void* __restrict__ qhat,
                                                         const int64_t* __restrict__ q_pos, SelArgs sa, int splits,
-                                                        float* __restrict__ scores, int64_t score_stride) {
+                                                        float* __restrict__ scores, int64_t score_stride,
+                                                        float* __restrict__ tmax, int64_t tmax_stride) {
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
     const int64_t u = (int64_t)blockIdx.x / splits;
     const int split = (int)((int64_t)blockIdx.x % splits);
@@ -1320,6 +1284,7 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
     const int64_t bg = un.b * sa.H_kv + un.g;
     const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
     float* sc = scores + u * score_stride;
+    float* tmx = tmax + u * tmax_stride;
     if constexpr (BF16) {
         // B operand: query head n of the group in column n (zero columns past G);
         // the group max is taken across the 16 lanes of each row group
@@ -1364,6 +1329,8 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
                             vals[v] = x;
                         }
                         if (n == 0) *reinterpret_cast<f32x4*>(sc + (int64_t)(tb + j) * 16 + 4 * h) = vals;
+                        const float m = tile_max(vals);   // every lane takes part in the shuffles
+                        if (l == 0) tmx[tb + j] = m;
                     }
                 }
             }
@@ -1375,340 +1342,10 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
             const f32x4 vals =
                 score_tile_f32(reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent, x0, qf32, n == 0, sa.G);
             if (n == 0) *reinterpret_cast<f32x4*>(sc + x0 + 4 * h) = vals;
+            const float m = tile_max(vals);   // lanes past column 0 hold -inf
+            if (l == 0) tmx[tt] = m;
         }
     }
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(kThrThreads) void score_select_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
-                                                                    SelArgs sa, const float* __restrict__ scores,
-                                                                    int64_t score_stride, int* fb_list, int* counters,
-                                                                    int32_t* lr_idx, int32_t* lr_cnt) {
-    // LDS (153 KB): the packed records of up to 32768 buckets, the histogram
-    // (count << 32 | weight), and small scratch.  Once the candidates are
-    // collected, the record space holds the ranking scratch and the tokens.
-    __shared__ __align__(16) uint32_t rec[kThrRegs * kThrThreads];
-    __shared__ unsigned long long hist[kThrBins];
-    __shared__ unsigned long long wtot[kThrThreads / 64];
-    __shared__ int wtot32[kThrThreads / 64];
-    __shared__ uint32_t bc[4];
-    __shared__ int ncand, fin[3];
-    __shared__ int tk[2 * kLeavesPerBlock];   // eligible tokens of the straddling blocks' buckets
-    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
-    const int64_t u = blockIdx.x;
-    const Unit un = unit_of(u, sa);
-    const int64_t t = q_pos[un.b * sa.n_q + un.i];
-    const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
-    int32_t* out = lr_idx + u * sa.k;
-    if (unit_is_trivial(t, q, sa.k)) {
-        if (wid == 0) trivial_unit(t, q, sa.k, out, lr_cnt + u);
-        return;
-    }
-    const int64_t bg = un.b * sa.H_kv + un.g;
-    const float* sc = scores + u * score_stride;
-    const uint32_t* meta = cv.meta + bg * cv.s_meta;
-    const int NLv = kLeavesPerBlock * q.nvis;
-    constexpr int kChunk = kThrRegs * kThrThreads;
-    const int nchunks = (NLv + kChunk - 1) / kChunk;
-    // Eligible tokens of the buckets of the (at most two) blocks straddling an
-    // edge of [sink_end, l0), from their member lists, once.
-    int sb0, sb1;
-    straddling_blocks(q, sb0, sb1);
-    if (tid < 2 * kLeavesPerBlock) {
-        const int blk = tid < kLeavesPerBlock ? sb0 : sb1;
-        const int64_t x = (int64_t)blk * kLeavesPerBlock + tid % kLeavesPerBlock;
-        tk[tid] = (blk >= 0 && x < NLv) ? leaf_weight(cv, bg, (uint32_t)x, q) : 0;
-    }
-    __syncthreads();
-    // Records of one chunk into LDS, 16 at a time per thread with their
-    // score and meta loads in flight together (unconditional, clamped index).
-    auto load_chunk = [&](int c0) {
-        for (int j0 = 0; j0 < kThrRegs; j0 += 16) {
-            float s8[16];
-            uint32_t m8[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int x = c0 + (j0 + j) * kThrThreads + tid;
-                const int xc = x < NLv ? x : NLv - 1;
-                s8[j] = sc[xc];
-                m8[j] = meta[xc];
-            }
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int x = c0 + (j0 + j) * kThrThreads + tid;
-                const int blk = x / kLeavesPerBlock;
-                const int w = blk == sb0   ? tk[x % kLeavesPerBlock]
-                              : blk == sb1 ? tk[kLeavesPerBlock + x % kLeavesPerBlock]
-                                           : leaf_weight_whole((uint32_t)x, m8[j], q);
-                rec[(j0 + j) * kThrThreads + tid] = x < NLv ? (thr_key(s8[j]) << 7) | (uint32_t)w : 0u;
-            }
-        }
-        __syncthreads();
-    };
-    const bool resident = nchunks == 1;
-    if (resident) load_chunk(0);
-    uint32_t lo = 0, target = (uint32_t)sa.k, cabove = 0, lower = 0, flo = 0;
-    int shift = 13, nb = kThrBins;
-    bool overflow = false;
-    // Level -1 histograms only each thread's best bucket.  Those are a subset
-    // of all buckets, so if the ones at or above bin F hold >= k tokens then so
-    // do all buckets at or above F, and the boundary bin is >= F: level 0 may
-    // skip every bucket below F (far fewer LDS atomics).
-    for (int level = -1; level < 3; ++level) {
-        for (int j = tid; j < nb; j += kThrThreads) hist[j] = 0ull;
-        __syncthreads();
-        const uint32_t hi = lo + ((uint32_t)nb << shift);
-        uint32_t best = 0;   // best record with a nonzero weight (records compare by key first)
-        for (int c = 0; c < nchunks; ++c) {
-            if (!resident) load_chunk(c * kChunk);
-            for (int j = 0; j < kThrRegs; ++j) {
-                const uint32_t r = rec[j * kThrThreads + tid];
-                const uint32_t key = r >> 7, w = r & 0x7Fu;
-                if (level < 0) {
-                    if (w > 0 && r > best) best = r;
-                } else if (w > 0 && key >= lo && key < hi && key >= flo) {
-                    atomicAdd(&hist[(key - lo) >> shift], (1ull << 32) | (unsigned long long)w);
-                }
-            }
-            if (!resident) __syncthreads();   // the chunk's records are overwritten next
-        }
-        if (level < 0 && best != 0u)
-            atomicAdd(&hist[(best >> 7) >> shift], (1ull << 32) | (unsigned long long)(best & 0x7Fu));
-        if (level < 0 && tid == 0) bc[0] = 0xFFFFFFFFu;   // stays so if the best buckets hold < k tokens
-        __syncthreads();
-        // thread tid owns bins [per * tid, per * tid + per); suffix sums run from the top bin down
-        const int per = (nb + kThrThreads - 1) / kThrThreads;
-        const int b0 = per * tid;
-        unsigned long long mine = 0ull;
-        for (int j = 0; j < per; ++j)
-            if (b0 + j < nb) mine += hist[b0 + j];
-        unsigned long long suf = mine;   // inclusive suffix within the wave (lanes >= l)
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const unsigned long long v = shfl_down_u64(suf, o);
-            if (l + o < 64) suf += v;
-        }
-        if (l == 0) wtot[wid] = suf;
-        __syncthreads();
-        unsigned long long above = suf - mine;   // bins of higher threads in this wave
-        for (int w2 = wid + 1; w2 < kThrThreads / 64; ++w2) above += wtot[w2];
-        // the boundary bin: weight above it < target <= weight above it + its own
-        for (int j = per - 1; j >= 0; --j) {
-            const int bin = b0 + j;
-            if (bin >= nb) continue;
-            const unsigned long long hv = hist[bin];
-            const uint32_t wa = (uint32_t)above, wb = (uint32_t)hv;
-            if (wa < target && target <= wa + wb) {
-                bc[0] = (uint32_t)bin;
-                bc[1] = target - wa;
-                bc[2] = (uint32_t)(above >> 32);
-                bc[3] = (uint32_t)(hv >> 32);
-            }
-            above += hv;
-        }
-        __syncthreads();
-        const uint32_t B = bc[0], rem = bc[1], cab = cabove + bc[2], cB = bc[3];
-        __syncthreads();
-        if (level < 0) {
-            flo = B == 0xFFFFFFFFu ? 0u : (B << shift);
-            continue;
-        }
-        if (B == 0xFFFFFFFFu) {   // cannot happen: the visible buckets hold every eligible token (> k)
-            overflow = true;
-            break;
-        }
-        if (cab + cB <= (uint32_t)(level == 2 ? kCandCap : kThrGoal)) {
-            lower = lo + (B << shift);
-            break;
-        }
-        if (level == 2) {
-            overflow = true;
-            break;
-        }
-        lo += B << shift;
-        target = rem;
-        cabove = cab;
-        shift = level == 0 ? 2 : 0;
-        nb = level == 0 ? 2048 : 4;
-    }
-    if (overflow) {   // too many buckets tie at the boundary key: the exact radix path takes the unit
-        if (tid == 0) {
-            const int pos = atomicAdd(&counters[0], 1);
-            fb_list[pos] = (int)u;
-        }
-        return;
-    }
-    uint32_t* cid = reinterpret_cast<uint32_t*>(hist);   // [kCandCap] candidate ids (the histogram is dead)
-    if (tid == 0) ncand = 0;
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        if (!resident) load_chunk(c * kChunk);
-        for (int j = 0; j < kThrRegs; ++j) {
-            const int x = c * kChunk + j * kThrThreads + tid;
-            const uint32_t r = rec[j * kThrThreads + tid];
-            const bool take = (r & 0x7Fu) != 0u && (r >> 7) >= lower;
-            const uint64_t bal = __ballot(take);
-            int base = 0;
-            if (l == 0 && bal) base = atomicAdd(&ncand, __popcll(bal));
-            base = __shfl(base, 0);
-            if (take) {
-                const int pos = base + __popcll(bal & ((1ull << l) - 1ull));
-                if (pos < kCandCap) cid[pos] = (uint32_t)x;
-            }
-        }
-        if (!resident) __syncthreads();
-    }
-    __syncthreads();
-    // the record space is dead: ranking scratch and the tokens
-    uint64_t* keys = reinterpret_cast<uint64_t*>(rec);         // [kCandCap]
-    uint64_t* used = keys + kCandCap;                           // [kMaxBlockWords] blocks holding taken buckets
-    uint64_t* mask = used + kMaxBlockWords;                     // [kMaskSlots][32] token masks
-    uint32_t* cmeta = reinterpret_cast<uint32_t*>(mask + kMaskSlots * 32);   // [kCandCap]
-    int* cw = reinterpret_cast<int*>(cmeta + kCandCap);         // [kCandCap]
-    int* coff = cw + kCandCap;                                  // [kCandCap]
-    int* upre = coff + kCandCap;                                // [kMaxBlockWords]
-    int* slot_blk = upre + kMaxBlockWords;                      // [kMaskSlots]
-    static_assert(kCandCap * (8 + 12) + kMaxBlockWords * 12 + kMaskSlots * (256 + 4) <= kThrRegs * kThrThreads * 4,
-                  "ranking scratch fits the records' space");
-    // ---- rank the candidates (score desc, id asc)
-    const int nc = ncand < kCandCap ? ncand : kCandCap;
-    const int P = pow2_at_least(nc);
-    for (int j = tid; j < P; j += kThrThreads) keys[j] = j < nc ? rank_key(sc[cid[j]], cid[j]) : 0ull;
-    __syncthreads();
-    if (wid == 0) wave_sort_desc(keys, P);
-    __syncthreads();
-    // ---- eligible tokens of each ranked candidate, then the buckets taken until k tokens
-    if (tid < nc) {
-        const uint32_t x = rank_key_id(keys[tid]);
-        const uint32_t m = meta[x];
-        const int blk = (int)(x / kLeavesPerBlock);
-        cmeta[tid] = m;
-        cw[tid] = blk == sb0 ? tk[x % kLeavesPerBlock]
-                  : blk == sb1 ? tk[kLeavesPerBlock + x % kLeavesPerBlock]
-                               : leaf_weight_whole(x, m, q);
-    }
-    __syncthreads();
-    if (wid == 0) {
-        int run = 0, ntake = nc, last = 0;
-        for (int c0 = 0; c0 < nc; c0 += 64) {
-            const int j = c0 + l;
-            const int w = j < nc ? cw[j] : 0;
-            const int incl = wave_incl_scan(w) + run;
-            if (j < nc) coff[j] = incl - w;
-            const uint64_t hit = __ballot(j < nc && w > 0 && incl >= sa.k && incl - w < sa.k);
-            if (hit) {
-                const int hl = __builtin_ctzll(hit);
-                ntake = c0 + hl + 1;
-                last = sa.k - __shfl(incl - w, hl);   // tokens the boundary bucket gives
-                break;
-            }
-            run = __shfl(incl, 63);
-        }
-        if (l == 0) {
-            fin[0] = ntake;
-            // total: k when the boundary was reached (always, the candidates hold >= k tokens)
-            fin[1] = ntake < nc || last > 0 ? sa.k : run;
-            fin[2] = last;
-        }
-    }
-    __syncthreads();
-    const int ntake = fin[0], total = fin[1], last = fin[2];
-    // ---- tokens in ascending order through per-block token masks: the blocks of the taken buckets
-    // get slots in block order (a bitmap of used blocks and its prefix counts), every emitted token
-    // sets its bit in its block's 2048-bit mask, and a prefix count over the mask words places it.
-    const int nbw = (cv.n_blocks + 63) / 64;
-    if (nbw > kMaxBlockWords) {   // beyond the masks' reach: the exact radix path takes the unit
-        if (tid == 0) fb_list[atomicAdd(&counters[0], 1)] = (int)u;
-        return;
-    }
-    for (int w = tid; w < nbw; w += kThrThreads) used[w] = 0ull;
-    __syncthreads();
-    for (int j = tid; j < ntake; j += kThrThreads) {
-        const uint32_t blk = rank_key_id(keys[j]) / kLeavesPerBlock;
-        atomicOr(&used[blk / 64], 1ull << (blk % 64));
-    }
-    __syncthreads();
-    {
-        const int pc = tid < nbw ? __popcll(used[tid]) : 0;   // nbw <= kThrThreads
-        int tot;
-        const int ex = wg1024_excl_scan(pc, wtot32, tot);
-        if (tid < nbw) {
-            upre[tid] = ex;
-            uint64_t m = used[tid];
-            int r = ex;
-            while (m) {   // slot -> block
-                const int b = __builtin_ctzll(m);
-                m &= m - 1;
-                if (r < kMaskSlots) slot_blk[r] = tid * 64 + b;
-                ++r;
-            }
-        }
-        if (tid == 0) fin[0] = tot;
-    }
-    __syncthreads();
-    const int nslots = fin[0];
-    if (nslots > kMaskSlots) {
-        if (tid == 0) fb_list[atomicAdd(&counters[0], 1)] = (int)u;
-        return;
-    }
-    for (int w = tid; w < nslots * 32; w += kThrThreads) mask[w] = 0ull;
-    __syncthreads();
-    // emit: bucket j by wave j % 16, lane l = member l / 4, token l % 4 (members ascending, so the
-    // lanes' eligible tokens are in ascending order and the boundary bucket keeps its lowest ones)
-    {
-        constexpr int NW = kThrThreads / 64, GB = 4;   // waves; buckets per wave whose member loads fly together
-        const uint16_t* mem_bg = cv.members + bg * cv.s_members;
-        const int e = l >> 2, jj = l & 3;
-        for (int j0 = wid; j0 < ntake; j0 += NW * GB) {
-            uint16_t mv[GB];
-#pragma unroll
-            for (int g = 0; g < GB; ++g) {
-                const int j = min(j0 + g * NW, ntake - 1);
-                const uint32_t m = cmeta[j];
-                const int sz = (int)(m & 0xFFu), off = (int)((m >> 8) & 0x3FFu);
-                const int64_t blk = rank_key_id(keys[j]) / kLeavesPerBlock;
-                mv[g] = mem_bg[blk * kBlockEntries + off + (e < sz ? e : 0)];
-            }
-#pragma unroll
-            for (int g = 0; g < GB; ++g) {
-                const int j = j0 + g * NW;
-                if (j >= ntake) break;
-                const uint32_t m = cmeta[j];
-                const int sz = (int)(m & 0xFFu);
-                const int blk = (int)(rank_key_id(keys[j]) / kLeavesPerBlock);
-                const int tb = kPool * mv[g] + jj;   // token offset in the block
-                const int64_t t0 = (int64_t)blk * kBlockTokens + tb;
-                const bool el = e < sz && t0 >= q.sink_end && t0 < q.l0;
-                const uint64_t bal = __ballot(el);
-                const int pos = __popcll(bal & ((1ull << l) - 1ull));
-                const int quota = (j == ntake - 1 && last > 0) ? last : 64;
-                if (el && pos < quota) {
-                    const int slot = upre[blk / 64] + __popcll(used[blk / 64] & ((1ull << (blk % 64)) - 1ull));
-                    atomicOr(&mask[slot * 32 + tb / 64], 1ull << (tb % 64));
-                }
-            }
-        }
-    }
-    __syncthreads();
-    // thread tid owns mask words [per * tid, per * tid + per): its tokens follow those of lower words
-    {
-        const int nw = nslots * 32, per = (nw + kThrThreads - 1) / kThrThreads, w0 = per * tid;
-        int pc = 0;
-        for (int w = w0; w < w0 + per && w < nw; ++w) pc += __popcll(mask[w]);
-        int tot;
-        int pos = wg1024_excl_scan(pc, wtot32, tot);
-        for (int w = w0; w < w0 + per && w < nw; ++w) {
-            uint64_t m = mask[w];
-            const int32_t base = slot_blk[w / 32] * kBlockTokens + (w % 32) * 64;
-            while (m) {
-                const int b = __builtin_ctzll(m);
-                m &= m - 1;
-                out[pos++] = base + b;
-            }
-        }
-    }
-    for (int j = total + tid; j < sa.k; j += kThrThreads) out[j] = -1;
-    if (tid == 0) lr_cnt[u] = total;
 }
 
 // Workgroup-wide exclusive scan over 256 threads (4 waves).
@@ -1727,6 +1364,445 @@ __device__ __forceinline__ int wg_excl_scan(int v, int* sh4, int& total) {
     __syncthreads();
     return base + inc - v;
 }
+
+// Bin of a score for the decode finish: 4096 bins of width 2^-11 over [-1, 1), monotone
+// non-decreasing in the score (scores outside the range land in the end bins).
+constexpr int kFinBins = 4096;
+constexpr int kFinTiles = 512;     // tiles whose scores one finish reads (more: the exact path)
+constexpr int kFinMinTiles = 16;
+__device__ __forceinline__ int fin_bin(float s) {
+    return (int)fminf(fmaxf((s + 1.0f) * 2048.0f, 0.0f), 4095.0f);
+}
+
+// The bin where a histogram's count from the top first reaches `target`
+// (thread tid holding bins [16 tid, 16 tid + 16) in hb, `above` the count
+// of the higher threads' bins): written to *out by the one thread holding
+// it; nothing is written when the whole histogram holds less than target.
+__device__ __forceinline__ void crossing_bin(const uint32_t (&hb)[16], int above, int target, int* out) {
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+        const int hv = (int)hb[j];
+        if (above < target && target <= above + hv) *out = 16 * (int)threadIdx.x + j;
+        above += hv;
+    }
+}
+
+// This thread's 16 bins of an LDS histogram of kFinBins, their sum, and the
+// sum over the bins of higher threads (256 threads).
+__device__ __forceinline__ int load_bins(const uint32_t* hist, uint32_t (&hb)[16], int* sh4) {
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 v = h4[4 * threadIdx.x + j];
+        hb[4 * j] = v.x;
+        hb[4 * j + 1] = v.y;
+        hb[4 * j + 2] = v.z;
+        hb[4 * j + 3] = v.w;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mine += (int)hb[j];
+    int tot;
+    const int pre = wg_excl_scan(mine, sh4, tot);
+    return tot - pre - mine;
+}
+
+__device__ __forceinline__ void clear_bins(uint32_t* hist) {
+    uint4* h4 = reinterpret_cast<uint4*>(hist);
+#pragma unroll
+    for (int j = 0; j < kFinBins / 1024; ++j) h4[threadIdx.x + 256 * j] = uint4{0u, 0u, 0u, 0u};
+}
+
+// Candidate keys of the decode finish: ordered like rank_key (score desc,
+// bucket id asc), carrying the candidate's slot in the finish's candidate
+// arrays (< kCandCap) in the low 9 bits; bucket ids below 2^23.
+constexpr uint32_t kFinIdMax = (1u << 23) - 1u;
+static_assert(kCandCap <= 512, "candidate slots fit 9 bits");
+__device__ __forceinline__ uint64_t fin_key(float s, uint32_t id, int slot) {
+    return ((uint64_t)ord_key(s) << 32) | ((uint64_t)(kFinIdMax - id) << 9) | (uint64_t)slot;
+}
+__device__ __forceinline__ uint32_t fin_key_id(uint64_t k) { return kFinIdMax - ((uint32_t)k >> 9); }
+__device__ __forceinline__ int fin_key_slot(uint64_t k) { return (int)(k & 0x1FFu); }
+
+// Position of the j-th (from 0) set bit of x, which has more than j set bits.
+__device__ __forceinline__ int nth_set_bit(uint64_t x, int j) {
+    int b = 0;
+    uint32_t v = (uint32_t)x;
+    int c = __popc(v);
+    if (j >= c) {
+        j -= c;
+        b = 32;
+        v = (uint32_t)(x >> 32);
+    }
+#pragma unroll
+    for (int w = 16; w >= 1; w >>= 1) {
+        c = __popc(v & ((1u << w) - 1u));
+        if (j >= c) {
+            j -= c;
+            b += w;
+            v >>= w;
+        }
+    }
+    return b;
+}
+
+constexpr int kFinTmRegs = 8;    // tile maxima a thread holds (2048 tiles; more are read again)
+constexpr int kFinSlots = 128;   // blocks among the taken buckets (more: the exact path)
+
+// One workgroup per (query, KV head) after score_all_kernel.  Any bucket
+// whose score bin is >= b lies in a tile whose maximum's bin is >= b, so a
+// histogram of the tile maxima names a bin b0 with at least M tiles at or
+// above it (M = max(16, k / 16), grown while too few tokens turn up; M = all
+// tiles means b0 = 0); the buckets of those tiles with a bin >= b0 hold every
+// bucket that scores at least as high as any of them.  A weighted histogram
+// of those buckets (eligible tokens per bucket) names the bin b1 where the
+// tokens from the top first reach k: the buckets with a bin >= b1 form the
+// candidate set S, and every other bucket scores below every bucket in S, so
+// the walk over all buckets in rank order (score desc, id asc) ends inside S.
+// S is ranked (each candidate counts the candidates above it), walked to k
+// tokens (the last bucket giving its lowest eligible tokens), and the taken
+// buckets are put in id order; their blocks get slots in block order, each
+// taken token sets its bit in its slot's 2048-bit mask, and prefix counts
+// over the mask words place every output position's token.  More than
+// kFinTiles tiles, S larger than kCandCap, more than kSelCap taken buckets or
+// kFinSlots blocks send the unit to the exact radix path.
+__global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
+                                                            SelArgs sa, const float* __restrict__ scores,
+                                                            int64_t score_stride, const float* __restrict__ tmax,
+                                                            int64_t tmax_stride, int* fb_list, int* counters,
+                                                            int32_t* lr_idx, int32_t* lr_cnt) {
+    __shared__ __align__(16) uint32_t hist[kFinBins];   // histograms, then the mask words' prefix counts
+    __shared__ __align__(16) uint64_t keys[kCandCap];
+    __shared__ __align__(16) uint64_t mask[kFinSlots * 32];
+    __shared__ uint32_t cmeta[kCandCap];   // per candidate slot: bucket meta, eligible tokens
+    __shared__ int cw[kCandCap];
+    __shared__ int rk[kCandCap];           // rank -> candidate slot
+    __shared__ uint64_t rmask[kSelCap];
+    __shared__ uint32_t sleaf[kSelCap], smeta[kSelCap];
+    __shared__ int stake[kSelCap], sw[kSelCap], sslot[kSelCap];
+    __shared__ int tiles[kFinTiles];
+    __shared__ int slot_blk[kFinSlots];
+    __shared__ int stk[2 * kLeavesPerBlock];   // eligible tokens of the straddling blocks' buckets
+    __shared__ int sh4[4];
+    __shared__ int ntl, nk, wsum, bsel, need_stk, fin[3];
+    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
+    const uint64_t lt = (1ull << l) - 1ull;
+    const int64_t u = blockIdx.x;
+    const Unit un = unit_of(u, sa);
+    const int64_t t = q_pos[un.b * sa.n_q + un.i];
+    const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
+    int32_t* out = lr_idx + u * sa.k;
+    if (unit_is_trivial(t, q, sa.k)) {
+        if (wid == 0) trivial_unit(t, q, sa.k, out, lr_cnt + u);
+        return;
+    }
+    const int NT = kLeavesPerBlock * q.nvis / 16;
+    auto to_exact = [&]() {
+        if (tid == 0) fb_list[atomicAdd(&counters[0], 1)] = (int)u;
+    };
+    if ((int64_t)NT * 16 > (int64_t)kFinIdMax + 1) {
+        to_exact();
+        return;
+    }
+    const int64_t bg = un.b * sa.H_kv + un.g;
+    const float* sc = scores + u * score_stride;
+    const float* tm = tmax + u * tmax_stride;
+    const uint32_t* meta = cv.meta + bg * cv.s_meta;
+    int sb0, sb1;
+    straddling_blocks(q, sb0, sb1);
+    float tmr[kFinTmRegs];
+#pragma unroll
+    for (int r = 0; r < kFinTmRegs; ++r) tmr[r] = tid + 256 * r < NT ? tm[tid + 256 * r] : 0.f;
+    clear_bins(hist);
+    if (tid == 0) need_stk = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kFinTmRegs; ++r)
+        if (tid + 256 * r < NT) atomicAdd(&hist[fin_bin(tmr[r])], 1u);
+    for (int x = tid + 256 * kFinTmRegs; x < NT; x += 256) atomicAdd(&hist[fin_bin(tm[x])], 1u);
+    __syncthreads();
+    uint32_t tb[16];   // this thread's bins of the tile-maximum histogram
+    const int tabove = load_bins(hist, tb, sh4);
+    // scores, metas and eligible tokens of the 16 buckets of tile x (0 tokens: not eligible)
+    auto tile_buckets = [&](int x, float (&s16)[16], uint32_t (&m16)[16], int (&w16)[16]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float4 sv = reinterpret_cast<const float4*>(sc + (int64_t)x * 16)[c];
+            const uint4 mv = reinterpret_cast<const uint4*>(meta + (int64_t)x * 16)[c];
+            s16[4 * c] = sv.x;
+            s16[4 * c + 1] = sv.y;
+            s16[4 * c + 2] = sv.z;
+            s16[4 * c + 3] = sv.w;
+            m16[4 * c] = mv.x;
+            m16[4 * c + 1] = mv.y;
+            m16[4 * c + 2] = mv.z;
+            m16[4 * c + 3] = mv.w;
+        }
+        const int blk = x / (kLeavesPerBlock / 16);   // a tile lies in one block
+        const int so = blk == sb0 ? 0 : (blk == sb1 ? kLeavesPerBlock : -1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t leaf = (uint32_t)(16 * x + i);
+            w16[i] = so >= 0 ? stk[so + leaf % kLeavesPerBlock] : leaf_weight_whole(leaf, m16[i], q);
+        }
+    };
+    int M = min(NT, max(kFinMinTiles, sa.k / 16));
+    int b1 = 0, nt = 0;
+    bool have_stk = false;
+    float s16[16];   // tile `tid`'s buckets while at most 256 tiles are listed
+    uint32_t m16[16];
+    int w16[16];
+    for (;;) {
+        if (tid == 0) {
+            bsel = 0;
+            ntl = 0;
+            wsum = 0;
+        }
+        clear_bins(hist);   // the tile histogram is in tb[]
+        __syncthreads();
+        crossing_bin(tb, tabove, M, &bsel);
+        __syncthreads();
+        const int b0 = M < NT ? bsel : 0;   // M = NT: every bucket of every tile
+        auto list = [&](int x, float v) {
+            const bool qual = x < NT && fin_bin(v) >= b0;
+            const uint64_t bal = __ballot(qual);
+            int base = 0;
+            if (l == 0 && bal) base = atomicAdd(&ntl, __popcll(bal));
+            base = __shfl(base, 0);
+            const int pos = base + __popcll(bal & lt);
+            if (qual && pos < kFinTiles) tiles[pos] = x;
+            const int blk = x / (kLeavesPerBlock / 16);
+            if (qual && (blk == sb0 || blk == sb1)) need_stk = 1;
+        };
+#pragma unroll
+        for (int r = 0; r < kFinTmRegs; ++r) list(tid + 256 * r, tmr[r]);
+        for (int x0 = 256 * kFinTmRegs; x0 < NT; x0 += 256) list(x0 + tid, x0 + tid < NT ? tm[x0 + tid] : 0.f);
+        __syncthreads();
+        nt = ntl;
+        if (nt > kFinTiles) break;   // the exact path (b1 = 0 marks it)
+        if (need_stk && !have_stk) {   // a listed tile lies in a block straddling an edge
+            if (tid < 2 * kLeavesPerBlock) {
+                const int blk = tid < kLeavesPerBlock ? sb0 : sb1;
+                const int64_t x = (int64_t)blk * kLeavesPerBlock + tid % kLeavesPerBlock;
+                stk[tid] = (blk >= 0 && x < 16 * (int64_t)NT) ? leaf_weight(cv, bg, (uint32_t)x, q) : 0;
+            }
+            have_stk = true;
+            __syncthreads();
+        }
+        // weighted histogram of the buckets of the listed tiles with a bin >= b0
+        int wl = 0;
+        for (int j = tid; j < nt; j += 256) {
+            tile_buckets(tiles[j], s16, m16, w16);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int bin = fin_bin(s16[i]);
+                if (w16[i] > 0 && bin >= b0) {
+                    atomicAdd(&hist[bin], (uint32_t)w16[i]);
+                    wl += w16[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) wl += __shfl_xor(wl, o);
+        if (l == 0 && wl) atomicAdd(&wsum, wl);
+        __syncthreads();
+        if (wsum >= sa.k) {
+            uint32_t wb[16];
+            const int wabove = load_bins(hist, wb, sh4);
+            if (tid == 0) bsel = -1;
+            __syncthreads();
+            crossing_bin(wb, wabove, sa.k, &bsel);
+            __syncthreads();
+            b1 = bsel;   // >= b0: the buckets below b0 were not counted
+            break;
+        }
+        if (M >= NT) break;   // cannot happen: the visible buckets hold more than k eligible tokens (b1 = 0)
+        M = min(NT, 4 * M);
+        __syncthreads();   // every thread has read wsum before it is reset
+    }
+    if (b1 <= 0) {   // b1 = 0 would take every bucket: leave the unit to the exact path
+        to_exact();
+        return;
+    }
+    // S: the buckets of the listed tiles with a bin >= b1 (and eligible tokens)
+    if (tid == 0) {
+        nk = 0;
+        fin[0] = 0;
+        fin[2] = -1;
+    }
+    __syncthreads();
+    for (int j = tid; j < nt; j += 256) {
+        if (nt > 256) tile_buckets(tiles[j], s16, m16, w16);   // else the registers hold tile j = tid
+        const int x = tiles[j];
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c += (w16[i] > 0 && fin_bin(s16[i]) >= b1) ? 1 : 0;
+        int pos = c > 0 ? atomicAdd(&nk, c) : 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (w16[i] > 0 && fin_bin(s16[i]) >= b1) {
+                if (pos < kCandCap) {
+                    keys[pos] = fin_key(s16[i], (uint32_t)(16 * x + i), pos);
+                    cmeta[pos] = m16[i];
+                    cw[pos] = w16[i];
+                }
+                ++pos;
+            }
+        }
+    }
+    __syncthreads();
+    const int f = nk;
+    if (f > kCandCap) {
+        to_exact();
+        return;
+    }
+    // rank of each candidate: the number of candidates above it (keys are distinct)
+    for (int j = tid; j < f; j += 256) {
+        const uint64_t kj = keys[j];
+        int r = 0;
+        for (int i = 0; i < f; ++i) r += keys[i] > kj ? 1 : 0;
+        rk[r] = j;
+    }
+    __syncthreads();
+    // the walk: thread tid holds ranks 2 tid and 2 tid + 1; the rank where the tokens reach k
+    {
+        const int j0 = 2 * tid, j1 = j0 + 1;
+        const int w0 = j0 < f ? cw[rk[j0]] : 0, w1 = j1 < f ? cw[rk[j1]] : 0;
+        int tot;
+        const int ex = wg_excl_scan(w0 + w1, sh4, tot);
+        if (w0 > 0 && ex < sa.k && sa.k <= ex + w0) {
+            fin[0] = j0 + 1;
+            fin[1] = sa.k - ex;
+        }
+        if (w1 > 0 && ex + w0 < sa.k && sa.k <= ex + w0 + w1) {
+            fin[0] = j1 + 1;
+            fin[1] = sa.k - ex - w0;
+        }
+    }
+    __syncthreads();
+    const int ntake = fin[0], last = fin[1];
+    if (ntake == 0 || ntake > kSelCap) {   // more buckets than one record row holds
+        to_exact();
+        return;
+    }
+    // the taken buckets in id order (ids are distinct: a bucket's place is the count of smaller ids)
+    if (tid < ntake) {
+        const int j = rk[tid];
+        const uint32_t leaf = fin_key_id(keys[j]);
+        int r = 0;
+        for (int i = 0; i < ntake; ++i) r += fin_key_id(keys[rk[i]]) < leaf ? 1 : 0;
+        const int w = cw[j], take = tid == ntake - 1 ? last : w;
+        sleaf[r] = leaf;
+        smeta[r] = cmeta[j];
+        stake[r] = take;
+        sw[r] = w;
+        rmask[r] = 0ull;
+    }
+    __syncthreads();
+    // block slots in block order
+    {
+        int first = 0, blk = 0;
+        if (tid < ntake) {
+            blk = (int)(sleaf[tid] / kLeavesPerBlock);
+            first = (tid == 0 || (int)(sleaf[tid - 1] / kLeavesPerBlock) != blk) ? 1 : 0;
+            if (stake[tid] < sw[tid]) fin[2] = tid;   // the partially taken bucket
+        }
+        int ns;
+        const int ex = wg_excl_scan(first, sh4, ns);
+        if (tid < ntake) {
+            sslot[tid] = ex + first - 1;
+            if (first && ex < kFinSlots) slot_blk[ex] = blk;
+        }
+        if (tid == 0) fin[1] = ns;
+    }
+    __syncthreads();
+    const int ns = fin[1], rp = fin[2];
+    if (ns > kFinSlots) {
+        to_exact();
+        return;
+    }
+    for (int w = tid; w < ns * 32; w += 256) mask[w] = 0ull;
+    __syncthreads();
+    // entry e of taken bucket r (in id order) by thread (16 r + e) mod 256; the member loads of four
+    // entries are in flight together
+    const uint16_t* mem_bg = cv.members + bg * cv.s_members;
+    const int nent = ntake * 16;
+    for (int i0 = 0; i0 < nent; i0 += 1024) {
+        uint32_t mv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int idx = i0 + 256 * g + tid, r = idx >> 4, e = idx & 15;
+            mv[g] = 0xFFFFFFFFu;
+            if (idx < nent && r != rp) {
+                const uint32_t m = smeta[r];
+                if (e < (int)(m & 0xFFu))
+                    mv[g] = mem_bg[(int64_t)(sleaf[r] / kLeavesPerBlock) * kBlockEntries + ((m >> 8) & 0x3FFu) + e];
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            if (mv[g] == 0xFFFFFFFFu) continue;
+            const int idx = i0 + 256 * g + tid, r = idx >> 4, e = idx & 15;
+            const int tb0 = kPool * (int)mv[g];   // token offset in the block
+            const int64_t t0 = (int64_t)(sleaf[r] / kLeavesPerBlock) * kBlockTokens + tb0;
+            uint32_t bits = 0;
+#pragma unroll
+            for (int jj = 0; jj < kPool; ++jj) bits |= (t0 + jj >= q.sink_end && t0 + jj < q.l0) ? 1u << jj : 0u;
+            if (bits) {
+                atomicOr(&mask[sslot[r] * 32 + tb0 / 64], (uint64_t)bits << (tb0 % 64));
+                atomicOr(&rmask[r], (uint64_t)bits << (kPool * e));
+            }
+        }
+    }
+    if (wid == 0 && rp >= 0) {   // the partial bucket: its lowest `take` eligible keys (key l = lane l)
+        const uint32_t m = smeta[rp];
+        const int e = l >> 2, jj = l & 3, blk = (int)(sleaf[rp] / kLeavesPerBlock);
+        const bool in = e < (int)(m & 0xFFu);
+        const int tb = in ? kPool * (int)mem_bg[(int64_t)blk * kBlockEntries + ((m >> 8) & 0x3FFu) + e] + jj : 0;
+        const int64_t t0 = (int64_t)blk * kBlockTokens + tb;
+        const bool el = in && t0 >= q.sink_end && t0 < q.l0;
+        const uint64_t bal = __ballot(el);
+        const bool tk = el && __popcll(bal & lt) < stake[rp];
+        const uint64_t bt = __ballot(tk);
+        if (tk) atomicOr(&mask[sslot[rp] * 32 + tb / 64], 1ull << (tb % 64));
+        if (l == 0) rmask[rp] = bt;
+    }
+    __syncthreads();
+    if (sa.brec) {
+        u32x4* rec = sa.brec + u * LSA_BUCKET_RECS;
+        if (tid < ntake) rec[tid] = u32x4{sleaf[tid], (uint32_t)rmask[tid], (uint32_t)(rmask[tid] >> 32), 0u};
+        if (tid == 0) sa.bcnt[u] = ntake;
+    }
+    if (!(sa.brec && sa.skip_lists)) {
+        // prefix counts of the mask words (thread tid owns words [per tid, per tid + per)), then the
+        // token of each output position: its word (the last one whose prefix is <= the position) and
+        // the matching set bit in it
+        const int nw = ns * 32, per = (nw + 255) / 256, w0 = per * tid;
+        int pc = 0;
+        for (int w = w0; w < w0 + per && w < nw; ++w) pc += __popcll(mask[w]);
+        int tot;
+        int run = wg_excl_scan(pc, sh4, tot);
+        for (int w = w0; w < w0 + per && w < nw; ++w) {
+            hist[w] = (uint32_t)run;
+            run += __popcll(mask[w]);
+        }
+        __syncthreads();
+        for (int p = tid; p < tot; p += 256) {
+            int lo = 0, hi = nw - 1;   // hist[lo] <= p
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((int)hist[mid] <= p) lo = mid;
+                else hi = mid - 1;
+            }
+            const int b = nth_set_bit(mask[lo], p - (int)hist[lo]);
+            out[p] = slot_blk[lo / 32] * kBlockTokens + (lo % 32) * 64 + b;
+        }
+        for (int j = tot + tid; j < sa.k; j += 256) out[j] = -1;
+    }
+    if (tid == 0) lr_cnt[u] = sa.k;
+}
+
+
 
 constexpr int kExactSel = LSA_MAX_K + 2 * kLeavesPerBlock;   // selected buckets held per query
 
@@ -2142,18 +2218,14 @@ hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int6
     const dim3 grid((unsigned)(sa.n_units * splits));
     if (bf16)
         hipLaunchKernelGGL(score_all_kernel<true>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits, sb.scores,
-                           sb.score_stride);
+                           sb.score_stride, sb.tmax, sb.tmax_stride);
     else
         hipLaunchKernelGGL(score_all_kernel<false>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits, sb.scores,
-                           sb.score_stride);
+                           sb.score_stride, sb.tmax, sb.tmax_stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (bf16)
-        hipLaunchKernelGGL(score_select_kernel<true>, dim3((unsigned)sa.n_units), dim3(kThrThreads), 0, st, cv, q_pos,
-                           sa, sb.scores, sb.score_stride, sb.fb_list, sb.counters, lr_idx, lr_cnt);
-    else
-        hipLaunchKernelGGL(score_select_kernel<false>, dim3((unsigned)sa.n_units), dim3(kThrThreads), 0, st, cv, q_pos,
-                           sa, sb.scores, sb.score_stride, sb.fb_list, sb.counters, lr_idx, lr_cnt);
+    hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)sa.n_units), dim3(256), 0, st, cv, q_pos, sa, sb.scores,
+                       sb.score_stride, sb.tmax, sb.tmax_stride, sb.fb_list, sb.counters, lr_idx, lr_cnt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // the fallback list is almost always empty: a few workgroups loop over it (cheaper to launch)

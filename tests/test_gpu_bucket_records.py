@@ -50,10 +50,10 @@ def _expand(rec_rows, n, members, meta, g):
     return toks
 
 
-@pytest.mark.parametrize("search", ["flat", "tree"])
-def test_records_expand_to_the_rows(layer, search):
-    lr0, cnt0 = _select(layer, search)
-    lr, cnt, (recs, rcnt) = _select(layer, search, bucket_records=True)
+@pytest.mark.parametrize("search,strategy", [("flat", "auto"), ("flat", "materialized"), ("tree", "auto")])
+def test_records_expand_to_the_rows(layer, search, strategy):
+    lr0, cnt0 = _select(layer, search, strategy=strategy)
+    lr, cnt, (recs, rcnt) = _select(layer, search, strategy=strategy, bucket_records=True)
     torch.cuda.synchronize()
     assert torch.equal(lr, lr0) and torch.equal(cnt, cnt0)
     lr, cnt, recs, rcnt = lr[0].cpu().numpy(), cnt[0].cpu().numpy(), recs[0].cpu().numpy(), rcnt[0].cpu().numpy()
@@ -72,12 +72,6 @@ def test_records_expand_to_the_rows(layer, search):
         toks = _expand(recs[i, g], n, layer["members"], layer["meta"], g)
         row = lr[i, g, :int(cnt[i, g])]
         assert len(toks) == len(row) and np.array_equal(np.sort(toks), row), (search, i, g)
-
-
-def test_materialized_strategy_gives_no_records(layer):
-    lr, cnt, (recs, rcnt) = _select(layer, "flat", strategy="materialized", bucket_records=True)
-    torch.cuda.synchronize()
-    assert bool((rcnt == -1).all())
 
 
 @pytest.mark.parametrize("search", ["flat", "tree"])

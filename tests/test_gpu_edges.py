@@ -127,6 +127,26 @@ def test_bf16_shapes(d, H_kv, H_q):
                          positions=range(0, cfg.T, 17))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_materialized_tile_bound(dtype):
+    # T = 32768: 64 tiles of 16 buckets per query against a first bound of max(16, k / 16) = 16
+    # tiles, so the tile maxima decide which tiles' scores the finish reads
+    cfg = _cfg(T=32768, dtype=dtype, d=128 if dtype == "bf16" else 64)
+    inp = layer_inputs(cfg, seed=31, q_positions=torch.arange(20000, 32768, 397).unsqueeze(0))
+    _run_and_compare(cfg, inp, cfg.T, cfg.k, cfg.n_sinks, cfg.window, strategy="materialized")
+
+
+def test_materialized_bound_widens_past_ineligible_tiles():
+    # the keys of the last 4 blocks (inside the query's 8192-token window, so not eligible) all
+    # repeat head 0's query: their 16 tiles score highest and hold no eligible token, so the
+    # finish must widen its tile bound past them
+    cfg = _cfg(T=32768, window=8192)
+    t = cfg.T - 1
+    inp = layer_inputs(cfg, seed=32, q_positions=torch.tensor([[t]]))
+    inp["K"][0, 0, 24576:32768] = inp["Q"][0, 0, 0]
+    _run_and_compare(cfg, inp, cfg.T, cfg.k, cfg.n_sinks, cfg.window, strategy="materialized")
+
+
 def test_tree_odd_leaf_count():
     cfg = _cfg(T=2048 * 5)     # 320 leaves: levels 320, 160, 80, 40, 20, 10, 5, 3, 2, 1
     inp = layer_inputs(cfg, seed=28)
