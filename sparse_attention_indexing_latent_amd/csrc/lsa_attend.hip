@@ -133,53 +133,71 @@ __device__ __forceinline__ int32_t tok_of(const KeyList& kl, int64_t jr, int64_t
 
 // Log-sum-exp combine of the split partials of one unit (all G heads), by
 // one wave.  Lane s (< splits <= 64) holds split s's max and denominator of
-// every head; lane l then sums dims 2l, 2l + 1 over the splits, the loads of
-// 16 splits in flight at once (the partials come from other waves, so they
-// are read with coherent loads).
+// every head; lane l then sums dims 2l, 2l + 1 over the splits in split
+// order.  The partials come from other waves, so they are read with
+// coherent loads; those of 8 splits of every head are in flight at once,
+// the first 8 together with the maxima.
+constexpr int kCombSplits = 8;
 __device__ __forceinline__ void combine_unit(const float* __restrict__ part, const AttArgs& aa, int D, int out_bf16,
                                              void* O, int64_t u) {
     const int l = lane_id();
     const int G = aa.G, S = aa.splits;
     const int64_t rec = D + 2;   // floats per (split, head): max, denominator, D values
     const float* base = part + u * (int64_t)S * G * rec;
+    const bool active = 2 * l < D;
     uint64_t ml[kMaxGroup];
 #pragma unroll
     for (int hh = 0; hh < kMaxGroup; ++hh)
         ml[hh] = (hh < G && l < S) ? load_coherent_u64(base + ((int64_t)l * G + hh) * rec)
                                    : pack_f32x2(kNegInf, 0.f);
-    const int64_t g = u % aa.H_kv, bi = u / aa.H_kv;
-    const bool active = 2 * l < D;
-    for (int hh = 0; hh < G; ++hh) {
+    uint64_t v[kMaxGroup][kCombSplits];
+    auto load_chunk = [&](int s0) {
+#pragma unroll
+        for (int hh = 0; hh < kMaxGroup; ++hh)
+#pragma unroll
+            for (int j = 0; j < kCombSplits; ++j)
+                v[hh][j] = (hh < G && s0 + j < S && active)
+                               ? load_coherent_u64(base + ((int64_t)(s0 + j) * G + hh) * rec + 2 + 2 * l)
+                               : 0ull;
+    };
+    load_chunk(0);
+    float e[kMaxGroup], inv[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
         const float ms = __uint_as_float((uint32_t)ml[hh]), ls = __uint_as_float((uint32_t)(ml[hh] >> 32));
         const float m = wave_max(ms);
-        const float e = ms > kNegInf ? __expf(ms - m) : 0.f;
-        const float lsum = wave_sum(ls * e);
-        float o0 = 0.f, o1 = 0.f;
-        for (int s0 = 0; s0 < S; s0 += 16) {
-            uint64_t v[16];
+        e[hh] = ms > kNegInf ? __expf(ms - m) : 0.f;
+        const float lsum = wave_sum(ls * e[hh]);
+        inv[hh] = lsum > 0.f ? 1.0f / lsum : 0.f;
+        o0[hh] = 0.f;
+        o1[hh] = 0.f;
+    }
+    for (int s0 = 0; s0 < S; s0 += kCombSplits) {
+        if (s0 > 0) load_chunk(s0);
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                v[j] = (s0 + j < S && active) ? load_coherent_u64(base + ((int64_t)(s0 + j) * G + hh) * rec + 2 + 2 * l)
-                                              : 0ull;
+        for (int hh = 0; hh < kMaxGroup; ++hh) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float es = __shfl(e, (s0 + j) & 63);
-                if (s0 + j < S && es != 0.f) {   // a split that saw no key holds no partial output
-                    o0 += __uint_as_float((uint32_t)v[j]) * es;
-                    o1 += __uint_as_float((uint32_t)(v[j] >> 32)) * es;
+            for (int j = 0; j < kCombSplits; ++j) {
+                const float es = __shfl(e[hh], (s0 + j) & 63);
+                if (hh < G && s0 + j < S && es != 0.f) {   // a split that saw no key holds no partial output
+                    o0[hh] += __uint_as_float((uint32_t)v[hh][j]) * es;
+                    o1[hh] += __uint_as_float((uint32_t)(v[hh][j] >> 32)) * es;
                 }
             }
         }
-        const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    }
+    const int64_t g = u % aa.H_kv, bi = u / aa.H_kv;
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
         const int64_t orow = (bi * aa.H_q + g * G + hh) * D;
-        if (active) {
+        if (hh < G && active) {
             if (out_bf16) {
                 uint16_t* o = reinterpret_cast<uint16_t*>(O);
                 *reinterpret_cast<uint32_t*>(o + orow + 2 * l) =
-                    (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
+                    (uint32_t)f32_to_bf16(o0[hh] * inv[hh]) | ((uint32_t)f32_to_bf16(o1[hh] * inv[hh]) << 16);
             } else {
                 float* o = reinterpret_cast<float*>(O);
-                *reinterpret_cast<uint64_t*>(o + orow + 2 * l) = pack_f32x2(o0 * inv, o1 * inv);
+                *reinterpret_cast<uint64_t*>(o + orow + 2 * l) = pack_f32x2(o0[hh] * inv[hh], o1[hh] * inv[hh]);
             }
         }
     }

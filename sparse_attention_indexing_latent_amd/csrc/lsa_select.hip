@@ -1415,14 +1415,15 @@ __device__ __forceinline__ void clear_bins(uint32_t* hist) {
 
 // Candidate keys of the decode finish: ordered like rank_key (score desc,
 // bucket id asc), carrying the candidate's slot in the finish's candidate
-// arrays (< kCandCap) in the low 9 bits; bucket ids below 2^23.
-constexpr uint32_t kFinIdMax = (1u << 23) - 1u;
-static_assert(kCandCap <= 512, "candidate slots fit 9 bits");
+// arrays (< kFinC) in the low 10 bits; bucket ids below 2^22.
+constexpr int kFinC = 1024;   // buckets at or above the tile bound a finish keeps in LDS
+constexpr uint32_t kFinIdMax = (1u << 22) - 1u;
 __device__ __forceinline__ uint64_t fin_key(float s, uint32_t id, int slot) {
-    return ((uint64_t)ord_key(s) << 32) | ((uint64_t)(kFinIdMax - id) << 9) | (uint64_t)slot;
+    return ((uint64_t)ord_key(s) << 32) | ((uint64_t)(kFinIdMax - id) << 10) | (uint64_t)slot;
 }
-__device__ __forceinline__ uint32_t fin_key_id(uint64_t k) { return kFinIdMax - ((uint32_t)k >> 9); }
-__device__ __forceinline__ int fin_key_slot(uint64_t k) { return (int)(k & 0x1FFu); }
+__device__ __forceinline__ uint32_t fin_key_id(uint64_t k) { return kFinIdMax - ((uint32_t)k >> 10); }
+__device__ __forceinline__ int fin_key_slot(uint64_t k) { return (int)(k & 0x3FFu); }
+__device__ __forceinline__ float fin_key_score(uint64_t k) { return ord_key_inv((uint32_t)(k >> 32)); }
 
 // Position of the j-th (from 0) set bit of x, which has more than j set bits.
 __device__ __forceinline__ int nth_set_bit(uint64_t x, int j) {
@@ -1448,43 +1449,48 @@ __device__ __forceinline__ int nth_set_bit(uint64_t x, int j) {
 
 constexpr int kFinTmRegs = 8;    // tile maxima a thread holds (2048 tiles; more are read again)
 constexpr int kFinSlots = 128;   // blocks among the taken buckets (more: the exact path)
+constexpr int kFinOutPer = 8;    // output positions a thread places together
 
 // One workgroup per (query, KV head) after score_all_kernel.  Any bucket
 // whose score bin is >= b lies in a tile whose maximum's bin is >= b, so a
 // histogram of the tile maxima names a bin b0 with at least M tiles at or
 // above it (M = max(16, k / 16), grown while too few tokens turn up; M = all
-// tiles means b0 = 0); the buckets of those tiles with a bin >= b0 hold every
-// bucket that scores at least as high as any of them.  A weighted histogram
-// of those buckets (eligible tokens per bucket) names the bin b1 where the
-// tokens from the top first reach k: the buckets with a bin >= b1 form the
-// candidate set S, and every other bucket scores below every bucket in S, so
-// the walk over all buckets in rank order (score desc, id asc) ends inside S.
-// S is ranked (each candidate counts the candidates above it), walked to k
-// tokens (the last bucket giving its lowest eligible tokens), and the taken
-// buckets are put in id order; their blocks get slots in block order, each
-// taken token sets its bit in its slot's 2048-bit mask, and prefix counts
-// over the mask words place every output position's token.  More than
-// kFinTiles tiles, S larger than kCandCap, more than kSelCap taken buckets or
-// kFinSlots blocks send the unit to the exact radix path.
+// tiles means b0 = 0); the buckets of those tiles with a bin >= b0 (the set
+// C, kept in LDS) hold every bucket that scores at least as high as any of
+// them.  A weighted histogram of C (eligible tokens per bucket) names the bin
+// b1 where the tokens from the top first reach k: the buckets of C with a bin
+// >= b1 form the candidate set S, and every other bucket scores below every
+// bucket in S, so the walk over all buckets in rank order (score desc, id
+// asc) ends inside S.  S is ranked (each candidate counts the candidates
+// above it), walked to k tokens (the last bucket giving its lowest eligible
+// tokens), and the taken buckets are put in id order; their blocks get slots
+// in block order, each taken token sets its bit in its slot's 2048-bit mask,
+// and prefix counts over the mask words place every output position's token.
+// The member lists of S are fetched as soon as S is known, so their latency
+// hides behind the ranking.  More than kFinTiles tiles, S larger than
+// kCandCap, more than kSelCap taken buckets or kFinSlots blocks send the unit
+// to the exact radix path.
 __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
                                                             SelArgs sa, const float* __restrict__ scores,
                                                             int64_t score_stride, const float* __restrict__ tmax,
                                                             int64_t tmax_stride, int* fb_list, int* counters,
                                                             int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ __align__(16) uint32_t hist[kFinBins];   // histograms, then the mask words' prefix counts
-    __shared__ __align__(16) uint64_t keys[kCandCap];
+    __shared__ __align__(16) uint64_t keys[kCandCap];   // S
     __shared__ __align__(16) uint64_t mask[kFinSlots * 32];
-    __shared__ uint32_t cmeta[kCandCap];   // per candidate slot: bucket meta, eligible tokens
-    __shared__ int cw[kCandCap];
-    __shared__ int rk[kCandCap];           // rank -> candidate slot
+    __shared__ __align__(16) uint64_t ckey[kFinC];      // C (or S's own entries when C overflows)
+    __shared__ uint32_t cmeta[kFinC];
+    __shared__ int cw[kFinC];
+    __shared__ __align__(16) uint4 cmem[kCandCap * 3];  // per S position: 24 member entries from off & ~7
+    __shared__ int rk[kCandCap];                         // rank -> S position
     __shared__ uint64_t rmask[kSelCap];
-    __shared__ uint32_t sleaf[kSelCap], smeta[kSelCap];
-    __shared__ int stake[kSelCap], sw[kSelCap], sslot[kSelCap];
+    __shared__ uint32_t tleaf[kSelCap], sleaf[kSelCap], smeta[kSelCap];
+    __shared__ int stake[kSelCap], sw[kSelCap], sslot[kSelCap], spos[kSelCap];
     __shared__ int tiles[kFinTiles];
     __shared__ int slot_blk[kFinSlots];
     __shared__ int stk[2 * kLeavesPerBlock];   // eligible tokens of the straddling blocks' buckets
     __shared__ int sh4[4];
-    __shared__ int ntl, nk, wsum, bsel, need_stk, fin[3];
+    __shared__ int ntl, nc, nk, wsum, bsel, need_stk, fin[3];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
     const uint64_t lt = (1ull << l) - 1ull;
     const int64_t u = blockIdx.x;
@@ -1508,6 +1514,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     const float* sc = scores + u * score_stride;
     const float* tm = tmax + u * tmax_stride;
     const uint32_t* meta = cv.meta + bg * cv.s_meta;
+    const uint16_t* mem_bg = cv.members + bg * cv.s_members;
     int sb0, sb1;
     straddling_blocks(q, sb0, sb1);
     float tmr[kFinTmRegs];
@@ -1523,39 +1530,34 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     __syncthreads();
     uint32_t tb[16];   // this thread's bins of the tile-maximum histogram
     const int tabove = load_bins(hist, tb, sh4);
-    // scores, metas and eligible tokens of the 16 buckets of tile x (0 tokens: not eligible)
-    auto tile_buckets = [&](int x, float (&s16)[16], uint32_t (&m16)[16], int (&w16)[16]) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float4 sv = reinterpret_cast<const float4*>(sc + (int64_t)x * 16)[c];
-            const uint4 mv = reinterpret_cast<const uint4*>(meta + (int64_t)x * 16)[c];
-            s16[4 * c] = sv.x;
-            s16[4 * c + 1] = sv.y;
-            s16[4 * c + 2] = sv.z;
-            s16[4 * c + 3] = sv.w;
-            m16[4 * c] = mv.x;
-            m16[4 * c + 1] = mv.y;
-            m16[4 * c + 2] = mv.z;
-            m16[4 * c + 3] = mv.w;
-        }
+    // scores, metas and eligible tokens of buckets 4 c .. 4 c + 3 of tile x (0 tokens: not eligible)
+    auto quad_buckets = [&](int x, int c, float (&s4)[4], uint32_t (&m4)[4], int (&w4)[4]) {
+        const float4 sv = reinterpret_cast<const float4*>(sc + (int64_t)x * 16)[c];
+        const uint4 mv = reinterpret_cast<const uint4*>(meta + (int64_t)x * 16)[c];
+        s4[0] = sv.x;
+        s4[1] = sv.y;
+        s4[2] = sv.z;
+        s4[3] = sv.w;
+        m4[0] = mv.x;
+        m4[1] = mv.y;
+        m4[2] = mv.z;
+        m4[3] = mv.w;
         const int blk = x / (kLeavesPerBlock / 16);   // a tile lies in one block
         const int so = blk == sb0 ? 0 : (blk == sb1 ? kLeavesPerBlock : -1);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t leaf = (uint32_t)(16 * x + i);
-            w16[i] = so >= 0 ? stk[so + leaf % kLeavesPerBlock] : leaf_weight_whole(leaf, m16[i], q);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t leaf = (uint32_t)(16 * x + 4 * c + i);
+            w4[i] = so >= 0 ? stk[so + leaf % kLeavesPerBlock] : leaf_weight_whole(leaf, m4[i], q);
         }
     };
     int M = min(NT, max(kFinMinTiles, sa.k / 16));
     int b1 = 0, nt = 0;
     bool have_stk = false;
-    float s16[16];   // tile `tid`'s buckets while at most 256 tiles are listed
-    uint32_t m16[16];
-    int w16[16];
     for (;;) {
         if (tid == 0) {
             bsel = 0;
             ntl = 0;
+            nc = 0;
             wsum = 0;
         }
         clear_bins(hist);   // the tile histogram is in tb[]
@@ -1589,16 +1591,37 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
             have_stk = true;
             __syncthreads();
         }
-        // weighted histogram of the buckets of the listed tiles with a bin >= b0
+        // C and its weighted histogram: the buckets of the listed tiles with a bin >= b0 (a quarter
+        // tile per thread)
         int wl = 0;
-        for (int j = tid; j < nt; j += 256) {
-            tile_buckets(tiles[j], s16, m16, w16);
+        for (int idx = tid; idx < 4 * nt; idx += 256) {
+            const int x = tiles[idx >> 2], c4 = idx & 3;
+            float s4[4];
+            uint32_t m4[4];
+            int w4[4];
+            quad_buckets(x, c4, s4, m4, w4);
+            bool in[4];
+            int c = 0;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int bin = fin_bin(s16[i]);
-                if (w16[i] > 0 && bin >= b0) {
-                    atomicAdd(&hist[bin], (uint32_t)w16[i]);
-                    wl += w16[i];
+            for (int i = 0; i < 4; ++i) {
+                const int bin = fin_bin(s4[i]);
+                in[i] = w4[i] > 0 && bin >= b0;
+                if (in[i]) {
+                    atomicAdd(&hist[bin], (uint32_t)w4[i]);
+                    wl += w4[i];
+                    ++c;
+                }
+            }
+            int pos = c > 0 ? atomicAdd(&nc, c) : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (in[i]) {
+                    if (pos < kFinC) {
+                        ckey[pos] = fin_key(s4[i], (uint32_t)(16 * x + 4 * c4 + i), pos);
+                        cmeta[pos] = m4[i];
+                        cw[pos] = w4[i];
+                    }
+                    ++pos;
                 }
             }
         }
@@ -1624,29 +1647,51 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
         to_exact();
         return;
     }
-    // S: the buckets of the listed tiles with a bin >= b1 (and eligible tokens)
+    // S: the buckets of C with a bin >= b1
     if (tid == 0) {
         nk = 0;
         fin[0] = 0;
         fin[2] = -1;
     }
     __syncthreads();
-    for (int j = tid; j < nt; j += 256) {
-        if (nt > 256) tile_buckets(tiles[j], s16, m16, w16);   // else the registers hold tile j = tid
-        const int x = tiles[j];
-        int c = 0;
+    const int ncc = nc;
+    if (ncc <= kFinC) {
+        for (int j0 = 0; j0 < ncc; j0 += 256) {
+            const int j = j0 + tid;
+            const uint64_t kc = j < ncc ? ckey[j] : 0ull;
+            const bool in = j < ncc && fin_bin(fin_key_score(kc)) >= b1;
+            const uint64_t bal = __ballot(in);
+            int base = 0;
+            if (l == 0 && bal) base = atomicAdd(&nk, __popcll(bal));
+            base = __shfl(base, 0);
+            const int pos = base + __popcll(bal & lt);
+            if (in && pos < kCandCap) keys[pos] = kc;
+        }
+    } else {   // C overflowed: S from the listed tiles again, its own entries in the C arrays
+        for (int idx = tid; idx < 4 * nt; idx += 256) {
+            const int x = tiles[idx >> 2], c4 = idx & 3;
+            float s4[4];
+            uint32_t m4[4];
+            int w4[4];
+            quad_buckets(x, c4, s4, m4, w4);
+            bool in[4];
+            int c = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c += (w16[i] > 0 && fin_bin(s16[i]) >= b1) ? 1 : 0;
-        int pos = c > 0 ? atomicAdd(&nk, c) : 0;
+            for (int i = 0; i < 4; ++i) {
+                in[i] = w4[i] > 0 && fin_bin(s4[i]) >= b1;
+                c += in[i] ? 1 : 0;
+            }
+            int pos = c > 0 ? atomicAdd(&nk, c) : 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (w16[i] > 0 && fin_bin(s16[i]) >= b1) {
-                if (pos < kCandCap) {
-                    keys[pos] = fin_key(s16[i], (uint32_t)(16 * x + i), pos);
-                    cmeta[pos] = m16[i];
-                    cw[pos] = w16[i];
+            for (int i = 0; i < 4; ++i) {
+                if (in[i]) {
+                    if (pos < kCandCap) {
+                        keys[pos] = fin_key(s4[i], (uint32_t)(16 * x + 4 * c4 + i), pos);
+                        cmeta[pos] = m4[i];
+                        cw[pos] = w4[i];
+                    }
+                    ++pos;
                 }
-                ++pos;
             }
         }
     }
@@ -1655,6 +1700,23 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     if (f > kCandCap) {
         to_exact();
         return;
+    }
+    // the member lists of S: 24 entries from off & ~7 per candidate, in flight during the ranking
+    uint4 pmv[2][3];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int j = tid + 256 * h2;
+        pmv[h2][0] = pmv[h2][1] = pmv[h2][2] = uint4{0u, 0u, 0u, 0u};
+        if (j < f) {
+            const uint64_t kj = keys[j];
+            const uint32_t m = cmeta[fin_key_slot(kj)];
+            const int a = (int)((m >> 8) & 0x3F8u);
+            const uint4* p = reinterpret_cast<const uint4*>(mem_bg + (int64_t)(fin_key_id(kj) / kLeavesPerBlock) *
+                                                                         kBlockEntries + a);
+            pmv[h2][0] = p[0];
+            if (a + 8 < kBlockEntries) pmv[h2][1] = p[1];
+            if (a + 16 < kBlockEntries) pmv[h2][2] = p[2];
+        }
     }
     // rank of each candidate: the number of candidates above it (keys are distinct)
     for (int j = tid; j < f; j += 256) {
@@ -1667,7 +1729,8 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     // the walk: thread tid holds ranks 2 tid and 2 tid + 1; the rank where the tokens reach k
     {
         const int j0 = 2 * tid, j1 = j0 + 1;
-        const int w0 = j0 < f ? cw[rk[j0]] : 0, w1 = j1 < f ? cw[rk[j1]] : 0;
+        const int w0 = j0 < f ? cw[fin_key_slot(keys[rk[j0]])] : 0;
+        const int w1 = j1 < f ? cw[fin_key_slot(keys[rk[j1]])] : 0;
         int tot;
         const int ex = wg_excl_scan(w0 + w1, sh4, tot);
         if (w0 > 0 && ex < sa.k && sa.k <= ex + w0) {
@@ -1685,17 +1748,21 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
         to_exact();
         return;
     }
+    if (tid < ntake) tleaf[tid] = fin_key_id(keys[rk[tid]]);
+    __syncthreads();
     // the taken buckets in id order (ids are distinct: a bucket's place is the count of smaller ids)
     if (tid < ntake) {
         const int j = rk[tid];
-        const uint32_t leaf = fin_key_id(keys[j]);
+        const uint32_t leaf = tleaf[tid];
         int r = 0;
-        for (int i = 0; i < ntake; ++i) r += fin_key_id(keys[rk[i]]) < leaf ? 1 : 0;
-        const int w = cw[j], take = tid == ntake - 1 ? last : w;
+        for (int i = 0; i < ntake; ++i) r += tleaf[i] < leaf ? 1 : 0;
+        const int slot = fin_key_slot(keys[j]);
+        const int w = cw[slot], take = tid == ntake - 1 ? last : w;
         sleaf[r] = leaf;
-        smeta[r] = cmeta[j];
+        smeta[r] = cmeta[slot];
         stake[r] = take;
         sw[r] = w;
+        spos[r] = j;
         rmask[r] = 0ull;
     }
     __syncthreads();
@@ -1715,6 +1782,15 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
         }
         if (tid == 0) fin[1] = ns;
     }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int j = tid + 256 * h2;
+        if (j < f) {
+            cmem[3 * j] = pmv[h2][0];
+            cmem[3 * j + 1] = pmv[h2][1];
+            cmem[3 * j + 2] = pmv[h2][2];
+        }
+    }
     __syncthreads();
     const int ns = fin[1], rp = fin[2];
     if (ns > kFinSlots) {
@@ -1723,42 +1799,28 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     }
     for (int w = tid; w < ns * 32; w += 256) mask[w] = 0ull;
     __syncthreads();
-    // entry e of taken bucket r (in id order) by thread (16 r + e) mod 256; the member loads of four
-    // entries are in flight together
-    const uint16_t* mem_bg = cv.members + bg * cv.s_members;
-    const int nent = ntake * 16;
-    for (int i0 = 0; i0 < nent; i0 += 1024) {
-        uint32_t mv[4];
+    const uint16_t* cm16 = reinterpret_cast<const uint16_t*>(cmem);
+    // entry e of taken bucket r (in id order) by thread (16 r + e) mod 256
+    for (int idx = tid; idx < ntake * 16; idx += 256) {
+        const int r = idx >> 4, e = idx & 15;
+        const uint32_t m = smeta[r];
+        if (r == rp || e >= (int)(m & 0xFFu)) continue;
+        const int mbr = cm16[24 * spos[r] + ((m >> 8) & 7u) + e];
+        const int tb0 = kPool * mbr;   // token offset in the block
+        const int64_t t0 = (int64_t)(sleaf[r] / kLeavesPerBlock) * kBlockTokens + tb0;
+        uint32_t bits = 0;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int idx = i0 + 256 * g + tid, r = idx >> 4, e = idx & 15;
-            mv[g] = 0xFFFFFFFFu;
-            if (idx < nent && r != rp) {
-                const uint32_t m = smeta[r];
-                if (e < (int)(m & 0xFFu))
-                    mv[g] = mem_bg[(int64_t)(sleaf[r] / kLeavesPerBlock) * kBlockEntries + ((m >> 8) & 0x3FFu) + e];
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            if (mv[g] == 0xFFFFFFFFu) continue;
-            const int idx = i0 + 256 * g + tid, r = idx >> 4, e = idx & 15;
-            const int tb0 = kPool * (int)mv[g];   // token offset in the block
-            const int64_t t0 = (int64_t)(sleaf[r] / kLeavesPerBlock) * kBlockTokens + tb0;
-            uint32_t bits = 0;
-#pragma unroll
-            for (int jj = 0; jj < kPool; ++jj) bits |= (t0 + jj >= q.sink_end && t0 + jj < q.l0) ? 1u << jj : 0u;
-            if (bits) {
-                atomicOr(&mask[sslot[r] * 32 + tb0 / 64], (uint64_t)bits << (tb0 % 64));
-                atomicOr(&rmask[r], (uint64_t)bits << (kPool * e));
-            }
+        for (int jj = 0; jj < kPool; ++jj) bits |= (t0 + jj >= q.sink_end && t0 + jj < q.l0) ? 1u << jj : 0u;
+        if (bits) {
+            atomicOr(&mask[sslot[r] * 32 + tb0 / 64], (uint64_t)bits << (tb0 % 64));
+            atomicOr(&rmask[r], (uint64_t)bits << (kPool * e));
         }
     }
     if (wid == 0 && rp >= 0) {   // the partial bucket: its lowest `take` eligible keys (key l = lane l)
         const uint32_t m = smeta[rp];
         const int e = l >> 2, jj = l & 3, blk = (int)(sleaf[rp] / kLeavesPerBlock);
         const bool in = e < (int)(m & 0xFFu);
-        const int tb = in ? kPool * (int)mem_bg[(int64_t)blk * kBlockEntries + ((m >> 8) & 0x3FFu) + e] + jj : 0;
+        const int tb = in ? kPool * (int)cm16[24 * spos[rp] + ((m >> 8) & 7u) + e] + jj : 0;
         const int64_t t0 = (int64_t)blk * kBlockTokens + tb;
         const bool el = in && t0 >= q.sink_end && t0 < q.l0;
         const uint64_t bal = __ballot(el);
@@ -1775,8 +1837,8 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     }
     if (!(sa.brec && sa.skip_lists)) {
         // prefix counts of the mask words (thread tid owns words [per tid, per tid + per)), then the
-        // token of each output position: its word (the last one whose prefix is <= the position) and
-        // the matching set bit in it
+        // token of each output position: its word (the last one whose prefix is <= the position, found
+        // by kFinOutPer interleaved binary searches) and the matching set bit in it
         const int nw = ns * 32, per = (nw + 255) / 256, w0 = per * tid;
         int pc = 0;
         for (int w = w0; w < w0 + per && w < nw; ++w) pc += __popcll(mask[w]);
@@ -1786,16 +1848,27 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
             hist[w] = (uint32_t)run;
             run += __popcll(mask[w]);
         }
+        for (int w = nw + tid; w < kFinBins; w += 256) hist[w] = 0x7FFFFFFFu;   // past the last word
         __syncthreads();
-        for (int p = tid; p < tot; p += 256) {
-            int lo = 0, hi = nw - 1;   // hist[lo] <= p
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if ((int)hist[mid] <= p) lo = mid;
-                else hi = mid - 1;
+        for (int p0 = 0; p0 < tot; p0 += 256 * kFinOutPer) {
+            int lo[kFinOutPer];
+#pragma unroll
+            for (int i = 0; i < kFinOutPer; ++i) lo[i] = 0;
+#pragma unroll
+            for (int step = kFinBins / 2; step >= 1; step >>= 1) {
+#pragma unroll
+                for (int i = 0; i < kFinOutPer; ++i) {   // lo + step < kFinBins: the read is in bounds
+                    const int c = lo[i] + step, p = p0 + 256 * i + tid;
+                    lo[i] = (int)hist[c] <= p ? c : lo[i];
+                }
             }
-            const int b = nth_set_bit(mask[lo], p - (int)hist[lo]);
-            out[p] = slot_blk[lo / 32] * kBlockTokens + (lo % 32) * 64 + b;
+#pragma unroll
+            for (int i = 0; i < kFinOutPer; ++i) {
+                const int p = p0 + 256 * i + tid;
+                if (p < tot)
+                    out[p] = slot_blk[lo[i] / 32] * kBlockTokens + (lo[i] % 32) * 64 +
+                             nth_set_bit(mask[lo[i]], p - (int)hist[lo[i]]);
+            }
         }
         for (int j = tot + tid; j < sa.k; j += 256) out[j] = -1;
     }
