@@ -276,9 +276,7 @@ void select_ws(const lsa_layout* L, const lsa_select_cfg* C, int64_t B, int64_t 
         w.off_fb = o;   o = align256(o + (size_t)units * 4);
         w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
         w.off_scores = o; o = align256(o + (size_t)w.fb_slots * w.score_stride * 4);
-    } else if (w.strategy == LSA_STRATEGY_MATERIALIZED) {
-        w.off_fb = o;   o = align256(o + (size_t)units * 4);
-        w.fb_slots = (int)(units < kFallbackSlots ? (units > 0 ? units : 1) : kFallbackSlots);
+    } else if (w.strategy == LSA_STRATEGY_MATERIALIZED) {   // the finish runs its exact fallback in place
         w.off_scores = o; o = align256(o + (size_t)units * w.score_stride * 4);
         w.tmax_stride = w.score_stride / 16;
         w.off_tmax = o; o = align256(o + (size_t)units * w.tmax_stride * 4);

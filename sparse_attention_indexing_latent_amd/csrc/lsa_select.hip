@@ -1365,6 +1365,129 @@ __device__ __forceinline__ int wg_excl_scan(int v, int* sh4, int& total) {
     return base + inc - v;
 }
 
+constexpr int kExactSel = LSA_MAX_K + 2 * kLeavesPerBlock;   // selected buckets held per query
+
+// LDS the exact path of one unit works in: hist[256], sel[kExactSel],
+// ebase[kExactSel] (entry keys of the expansion, >= k / 4), tk[256], sh4[4], bc[4].
+struct ExactLds {
+    uint32_t* hist;
+    uint64_t* sel;
+    uint32_t* ebase;
+    int* tk;
+    int* sh4;
+    uint32_t* bc;
+};
+
+// The exact path for unit u by one 256-thread workgroup: a weighted radix
+// select over the unit's scores sc (computed here first when rescore), then
+// the selected buckets in id order and their expansion.
+template <bool BF16>
+__device__ void exact_select_unit(const CacheView& cv, const void* __restrict__ qhat, const int64_t* __restrict__ q_pos,
+                                  const SelArgs& sa, int64_t u, float* sc, bool rescore, int32_t* lr_idx,
+                                  int32_t* lr_cnt, const ExactLds& m) {
+    uint32_t* hist = m.hist;
+    uint64_t* sel = m.sel;
+    uint32_t* ebase = m.ebase;
+    int* tk = m.tk;
+    int* sh4 = m.sh4;
+    uint32_t* bc = m.bc;
+    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
+    const Unit un = unit_of(u, sa);
+    const int64_t t = q_pos[un.b * sa.n_q + un.i];
+    const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
+    int32_t* out = lr_idx + u * sa.k;
+    if (wid == 0) trivial_unit(t, q, sa.k, out, lr_cnt + u);
+    const int64_t total = q.l0 > q.sink_end ? q.l0 - q.sink_end : 0;
+    if (t < 0 || sa.k == 0 || (int64_t)sa.k >= total) {
+        __syncthreads();
+        return;
+    }
+    const int NLv = kLeavesPerBlock * q.nvis;
+    const int64_t bg = un.b * sa.H_kv + un.g;
+    if (rescore) {
+        const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
+        QFragBF16 qf;
+        if constexpr (BF16) load_qfrag_bf16(qf, reinterpret_cast<const uint16_t*>(qhat) + qrow, n == 0, sa.G);
+        const float* qf32 = reinterpret_cast<const float*>(qhat) + qrow;
+        for (int tt = wid; tt < NLv / 16; tt += 4) {
+            const int64_t x0 = (int64_t)tt * 16;
+            f32x4 vals;
+            if constexpr (BF16)
+                vals = score_tile_bf16(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent, x0, qf, sa.G);
+            else
+                vals = score_tile_f32(reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent, x0, qf32, n == 0,
+                                      sa.G);
+            if (n == 0) *reinterpret_cast<f32x4*>(sc + x0 + 4 * h) = vals;
+        }
+        __threadfence_block();
+        __syncthreads();
+    }
+    // weighted radix select: the key K* where the weight of keys >= K* first reaches k
+    uint32_t prefix = 0;
+    uint32_t target = (uint32_t)sa.k;
+    for (int pass = 0; pass < 4; ++pass) {
+        hist[tid] = 0u;
+        __syncthreads();
+        const int shift = 24 - 8 * pass;
+        for (int x = tid; x < NLv; x += 256) {
+            const uint32_t key = ord_key(sc[x]);
+            if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
+            const int w = leaf_weight(cv, bg, (uint32_t)x, q);
+            if (w > 0) atomicAdd(&hist[(key >> shift) & 0xFFu], (uint32_t)w);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t cum = 0;
+            int dsel = 0;
+            for (int dg = 255; dg >= 0; --dg) {
+                const uint32_t hv = hist[dg];
+                if (cum + hv >= target) {
+                    dsel = dg;
+                    break;
+                }
+                cum += hv;
+            }
+            bc[0] = (prefix << 8) | (uint32_t)dsel;
+            bc[1] = target - cum;
+        }
+        __syncthreads();
+        prefix = bc[0];
+        target = bc[1];
+        __syncthreads();
+    }
+    const uint32_t kstar = prefix;   // boundary key; `target` tokens still needed among keys == K*
+    // selected buckets in id order
+    int nsel = 0, eq_have = 0;
+    for (int x0 = 0; x0 < NLv; x0 += 256) {
+        const int x = x0 + tid;
+        uint32_t key = 0;
+        int w = 0;
+        if (x < NLv) {
+            key = ord_key(sc[x]);
+            if (key >= kstar) w = leaf_weight(cv, bg, (uint32_t)x, q);
+        }
+        const bool gt = w > 0 && key > kstar, eq = w > 0 && key == kstar;
+        int eq_tot;
+        const int eb = wg_excl_scan(eq ? w : 0, sh4, eq_tot) + eq_have;
+        const bool take_all = gt || (eq && eb + w <= (int)target);
+        const bool take_part = !take_all && eq && eb < (int)target;
+        int s_tot;
+        const int pos = wg_excl_scan((take_all || take_part) ? 1 : 0, sh4, s_tot);
+        if ((take_all || take_part) && nsel + pos < kExactSel)
+            sel[nsel + pos] = pack_sel((uint32_t)x, cv.meta[bg * cv.s_meta + x], w, take_all, (int)target - eb);
+        nsel += s_tot;
+        eq_have += eq_tot;
+    }
+    __syncthreads();
+    if (wid == 0) {
+        const int ns = nsel < kExactSel ? nsel : kExactSel;
+        const int got = wave_expand(sel, ns, cv, bg, q, out, tk, ebase);
+        write_pad(out, got, sa.k);
+        if (l == 0) lr_cnt[u] = got;
+    }
+    __syncthreads();
+}
+
 // Bin of a score for the decode finish: 4096 bins of width 2^-11 over [-1, 1), monotone
 // non-decreasing in the score (scores outside the range land in the end bins).
 constexpr int kFinBins = 4096;
@@ -1468,16 +1591,15 @@ constexpr int kFinOutPer = 8;    // output positions a thread places together
 // and prefix counts over the mask words place every output position's token.
 // The member lists of S are fetched as soon as S is known, so their latency
 // hides behind the ranking.  More than kFinTiles tiles, S larger than
-// kCandCap, more than kSelCap taken buckets or kFinSlots blocks send the unit
-// to the exact radix path.
+// kCandCap, more than kSelCap taken buckets or kFinSlots blocks: the workgroup
+// runs the exact radix path for the unit instead.
 __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
                                                             SelArgs sa, const float* __restrict__ scores,
                                                             int64_t score_stride, const float* __restrict__ tmax,
-                                                            int64_t tmax_stride, int* fb_list, int* counters,
-                                                            int32_t* lr_idx, int32_t* lr_cnt) {
+                                                            int64_t tmax_stride, int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ __align__(16) uint32_t hist[kFinBins];   // histograms, then the mask words' prefix counts
     __shared__ __align__(16) uint64_t keys[kCandCap];   // S
-    __shared__ __align__(16) uint64_t mask[kFinSlots * 32];
+    __shared__ __align__(16) uint64_t mask[kFinSlots * 32 > kExactSel ? kFinSlots * 32 : kExactSel];
     __shared__ __align__(16) uint64_t ckey[kFinC];      // C (or S's own entries when C overflows)
     __shared__ uint32_t cmeta[kFinC];
     __shared__ int cw[kFinC];
@@ -1491,6 +1613,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     __shared__ int stk[2 * kLeavesPerBlock];   // eligible tokens of the straddling blocks' buckets
     __shared__ int sh4[4];
     __shared__ int ntl, nc, nk, wsum, bsel, need_stk, fin[3];
+    __shared__ uint32_t ebc[4];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6;
     const uint64_t lt = (1ull << l) - 1ull;
     const int64_t u = blockIdx.x;
@@ -1503,9 +1626,14 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
         return;
     }
     const int NT = kLeavesPerBlock * q.nvis / 16;
+    // the exact radix path, in this workgroup, over the unit's scores (its LDS in arrays that are
+    // free whenever it runs)
     auto to_exact = [&]() {
-        if (tid == 0) fb_list[atomicAdd(&counters[0], 1)] = (int)u;
+        const ExactLds m{hist, mask, reinterpret_cast<uint32_t*>(cmem), rk, sh4, ebc};
+        exact_select_unit<true>(cv, nullptr, q_pos, sa, u, const_cast<float*>(scores + u * score_stride), false,
+                                lr_idx, lr_cnt, m);
     };
+    static_assert(kCandCap * 3 * 4 >= kExactSel && kCandCap >= 256, "the exact path's LDS fits the finish's arrays");
     if ((int64_t)NT * 16 > (int64_t)kFinIdMax + 1) {
         to_exact();
         return;
@@ -1877,8 +2005,6 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
 
 
 
-constexpr int kExactSel = LSA_MAX_K + 2 * kLeavesPerBlock;   // selected buckets held per query
-
 // One workgroup per (query, KV head): weighted radix select of the boundary
 // key over materialised scores, then the selected buckets in id order.
 // With unit_list, loops over the fallback list; with rescore, it scores each
@@ -1891,109 +2017,16 @@ __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const v
                                                            int32_t* lr_idx, int32_t* lr_cnt) {
     __shared__ uint32_t hist[256];
     __shared__ uint64_t sel[kExactSel];
-    __shared__ uint32_t ebase[kExactSel];   // entry keys of the expansion (>= k / 4)
+    __shared__ uint32_t ebase[kExactSel];
     __shared__ int tk[256];
     __shared__ int sh4[4];
     __shared__ uint32_t bc[4];
-    const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
+    const ExactLds m{hist, sel, ebase, tk, sh4, bc};
     const int n_items = unit_list ? counters[0] : (int)sa.n_units;
     for (int slot = blockIdx.x; slot < n_items; slot += gridDim.x) {
         const int64_t u = unit_list ? unit_list[slot] : slot;
-        const Unit un = unit_of(u, sa);
-        const int64_t t = q_pos[un.b * sa.n_q + un.i];
-        const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
-        int32_t* out = lr_idx + u * sa.k;
-        if (wid == 0) trivial_unit(t, q, sa.k, out, lr_cnt + u);
-        const int64_t total = q.l0 > q.sink_end ? q.l0 - q.sink_end : 0;
-        if (t < 0 || sa.k == 0 || (int64_t)sa.k >= total) {
-            __syncthreads();
-            continue;
-        }
-        const int NLv = kLeavesPerBlock * q.nvis;
-        const int64_t bg = un.b * sa.H_kv + un.g;
-        float* sc = scores + (rescore ? (int64_t)blockIdx.x : u) * score_stride;
-        if (rescore) {
-            const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
-            QFragBF16 qf;
-            if constexpr (BF16) load_qfrag_bf16(qf, reinterpret_cast<const uint16_t*>(qhat) + qrow, n == 0, sa.G);
-            const float* qf32 = reinterpret_cast<const float*>(qhat) + qrow;
-            for (int tt = wid; tt < NLv / 16; tt += 4) {
-                const int64_t x0 = (int64_t)tt * 16;
-                f32x4 vals;
-                if constexpr (BF16)
-                    vals = score_tile_bf16(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent, x0, qf, sa.G);
-                else
-                    vals = score_tile_f32(reinterpret_cast<const float*>(cv.cent) + bg * cv.s_cent, x0, qf32, n == 0,
-                                          sa.G);
-                if (n == 0) *reinterpret_cast<f32x4*>(sc + x0 + 4 * h) = vals;
-            }
-            __threadfence_block();
-            __syncthreads();
-        }
-        // weighted radix select: the key K* where the weight of keys >= K* first reaches k
-        uint32_t prefix = 0;
-        uint32_t target = (uint32_t)sa.k;
-        for (int pass = 0; pass < 4; ++pass) {
-            hist[tid] = 0u;
-            __syncthreads();
-            const int shift = 24 - 8 * pass;
-            for (int x = tid; x < NLv; x += 256) {
-                const uint32_t key = ord_key(sc[x]);
-                if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
-                const int w = leaf_weight(cv, bg, (uint32_t)x, q);
-                if (w > 0) atomicAdd(&hist[(key >> shift) & 0xFFu], (uint32_t)w);
-            }
-            __syncthreads();
-            if (tid == 0) {
-                uint32_t cum = 0;
-                int dsel = 0;
-                for (int dg = 255; dg >= 0; --dg) {
-                    const uint32_t hv = hist[dg];
-                    if (cum + hv >= target) {
-                        dsel = dg;
-                        break;
-                    }
-                    cum += hv;
-                }
-                bc[0] = (prefix << 8) | (uint32_t)dsel;
-                bc[1] = target - cum;
-            }
-            __syncthreads();
-            prefix = bc[0];
-            target = bc[1];
-            __syncthreads();
-        }
-        const uint32_t kstar = prefix;   // boundary key; `target` tokens still needed among keys == K*
-        // selected buckets in id order
-        int nsel = 0, eq_have = 0;
-        for (int x0 = 0; x0 < NLv; x0 += 256) {
-            const int x = x0 + tid;
-            uint32_t key = 0;
-            int w = 0;
-            if (x < NLv) {
-                key = ord_key(sc[x]);
-                if (key >= kstar) w = leaf_weight(cv, bg, (uint32_t)x, q);
-            }
-            const bool gt = w > 0 && key > kstar, eq = w > 0 && key == kstar;
-            int eq_tot;
-            const int eb = wg_excl_scan(eq ? w : 0, sh4, eq_tot) + eq_have;
-            const bool take_all = gt || (eq && eb + w <= (int)target);
-            const bool take_part = !take_all && eq && eb < (int)target;
-            int s_tot;
-            const int pos = wg_excl_scan((take_all || take_part) ? 1 : 0, sh4, s_tot);
-            if ((take_all || take_part) && nsel + pos < kExactSel)
-                sel[nsel + pos] = pack_sel((uint32_t)x, cv.meta[bg * cv.s_meta + x], w, take_all, (int)target - eb);
-            nsel += s_tot;
-            eq_have += eq_tot;
-        }
-        __syncthreads();
-        if (wid == 0) {
-            const int ns = nsel < kExactSel ? nsel : kExactSel;
-            const int got = wave_expand(sel, ns, cv, bg, q, out, tk, ebase);
-            write_pad(out, got, sa.k);
-            if (l == 0) lr_cnt[u] = got;
-        }
-        __syncthreads();
+        exact_select_unit<BF16>(cv, qhat, q_pos, sa, u, scores + (rescore ? (int64_t)blockIdx.x : u) * score_stride,
+                                rescore != 0, lr_idx, lr_cnt, m);
     }
 }
 
@@ -2298,17 +2331,7 @@ hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int6
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)sa.n_units), dim3(256), 0, st, cv, q_pos, sa, sb.scores,
-                       sb.score_stride, sb.tmax, sb.tmax_stride, sb.fb_list, sb.counters, lr_idx, lr_cnt);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // the fallback list is almost always empty: a few workgroups loop over it (cheaper to launch)
-    const unsigned fb_grid = (unsigned)(sb.fb_slots < 8 ? sb.fb_slots : 8);
-    if (bf16)
-        hipLaunchKernelGGL(exact_select_kernel<true>, dim3(fb_grid), dim3(256), 0, st, cv, sb.qhat, q_pos, sa,
-                           sb.fb_list, sb.counters, sb.scores, sb.score_stride, 0, lr_idx, lr_cnt);
-    else
-        hipLaunchKernelGGL(exact_select_kernel<false>, dim3(fb_grid), dim3(256), 0, st, cv, sb.qhat, q_pos, sa,
-                           sb.fb_list, sb.counters, sb.scores, sb.score_stride, 0, lr_idx, lr_cnt);
+                       sb.score_stride, sb.tmax, sb.tmax_stride, lr_idx, lr_cnt);
     return hipGetLastError();
 }
 

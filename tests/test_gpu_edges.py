@@ -147,6 +147,19 @@ def test_materialized_bound_widens_past_ineligible_tiles():
     _run_and_compare(cfg, inp, cfg.T, cfg.k, cfg.n_sinks, cfg.window, strategy="materialized")
 
 
+def test_materialized_exact_path_when_every_score_is_near_minus_one():
+    # every key points against the (shared) query direction, so every bucket scores within 2^-11 of
+    # -1: all sit in the finish's lowest histogram bin and the workgroup runs the exact radix path
+    cfg = _cfg(T=8192)
+    qp = torch.tensor([[3000, 5000, 8191]], dtype=torch.int64)
+    inp = layer_inputs(cfg, seed=33, q_positions=qp)
+    q0 = inp["Q"][0, 0, 0].clone()
+    inp["Q"][0, :, :] = q0   # every head and query aims the same way
+    g = torch.Generator().manual_seed(33)
+    inp["K"][0, 0, :cfg.T] = -4.0 * q0 + 0.08 * torch.randn(cfg.T, cfg.d, generator=g)
+    _run_and_compare(cfg, inp, cfg.T, cfg.k, cfg.n_sinks, cfg.window, strategy="materialized")
+
+
 def test_tree_odd_leaf_count():
     cfg = _cfg(T=2048 * 5)     # 320 leaves: levels 320, 160, 80, 40, 20, 10, 5, 3, 2, 1
     inp = layer_inputs(cfg, seed=28)
