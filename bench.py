@@ -386,6 +386,22 @@ def kv_rows(K, T):
     return torch.arange(B * H, device=K.device) * t_cap + T
 
 
+def pair_kv(G):
+    """Move K and V into one allocation [2, B, H_kv, t_cap, d] (K = [0], V = [1]) so that a decode
+    step appends both rows with one index_copy_; returns that tensor."""
+    KV = torch.empty((2,) + tuple(G["K"].shape), dtype=G["K"].dtype, device=G["K"].device)
+    KV[0].copy_(G["K"])
+    KV[1].copy_(G["V"])
+    G["K"], G["V"] = KV[0], KV[1]
+    return KV
+
+
+def append_kv_pair(KV, rows2, newKV):
+    """Both rows of the new token into the paired K/V tensor with one index_copy_ (rows2: the K rows,
+    then the same rows of V)."""
+    KV.view(-1, KV.shape[-1]).index_copy_(0, rows2, newKV)
+
+
 def append_kv(G, rows, newK, newV):
     """Write one new token's key/value rows: one index_copy_ per tensor (a
     slice assignment into a >2^31-element tensor splits into one copy per
@@ -537,10 +553,12 @@ def run_decode(args):
     log("generating decode-16x1m on the GPU")
     inp = decode_inputs(cfg, seed=0, device=dev)
     G = {k: inp[k].contiguous() for k in ("K", "V", "W", "Q", "q_pos")}
+    del inp["K"], inp["V"]
+    KV = pair_kv(G)
     cache = lsa.build_buckets(G["K"], G["W"], T=cfg.T, n_q_heads=cfg.H_q)
-    newK = G["K"][:, :, cfg.T].clone()
-    newV = G["V"][:, :, cfg.T].clone()
     rows = kv_rows(G["K"], cfg.T)
+    rows2 = torch.cat([rows, rows + G["K"].numel() // G["K"].shape[-1]])
+    newKV = torch.cat([G["K"][:, :, cfg.T].reshape(-1, cfg.d), G["V"][:, :, cfg.T].reshape(-1, cfg.d)])
     ws = lsa.select_workspace_bytes(cache, lsa.select_cfg(cfg.k, cfg.n_sinks, cfg.window), 1, cfg.H_q)
     wsel = torch.empty(ws, dtype=torch.uint8, device=dev)
     lr = torch.empty(cfg.B, 1, cfg.H_kv, cfg.k, dtype=torch.int32, device=dev)
@@ -550,7 +568,7 @@ def run_decode(args):
                       device=dev)
 
     def step():
-        append_kv(G, rows, newK, newV)      # append the new token's key/value at row T
+        append_kv_pair(KV, rows2, newKV)    # append the new token's key and value at row T
         lsa.select(G["Q"], cache, G["q_pos"], G["W"], cfg.k, cfg.n_sinks, cfg.window, workspace=wsel,
                    out=(lr, cnt))
         lsa.sparse_attend(G["Q"], G["K"], G["V"], G["q_pos"], lr, cnt, cfg.T, cfg.k, cfg.n_sinks, cfg.window, O=O,
