@@ -60,7 +60,7 @@ extern "C" {
 #endif
 
 #define LSA_BUCKET_RECS 256   /* bucket records per (query, KV head) in lsa_select's optional output */
-#define LSA_ABI_VERSION 6
+#define LSA_ABI_VERSION 7
 
 #define LSA_LATENT_DIM 64         /* latent width (ch.2: 64-d index space) */
 #define LSA_POOL 4                /* keys pooled per entry (ch.2)            */
@@ -178,6 +178,12 @@ typedef struct lsa_cache_info {
     size_t off_entry_pos, stride_entry_pos;
     size_t off_edge_cent, stride_edge_cent;   /* tree only: see below */
     int32_t edge_levels;
+    /* bf16 only (else 0): each leaf centroid also as int8 codes with one fp32
+     * scale per leaf, code = round(centroid / scale), scale = max |component|
+     * / 127 (0 for a zero centroid), the codes in tiles of 16 leaves (1 KB:
+     * leaf r's 16 codes of dims [16 h, 16 h + 16) at byte 16 (r + 16 h));
+     * the flat decode scan bounds the bf16 scores with them */
+    size_t off_cent_i8, stride_cent_i8, off_cent_scale, stride_cent_scale;
 } lsa_cache_info;
 
 /* Bytes of a bucket cache for `batch` sequences of up to t_max tokens.

@@ -65,7 +65,8 @@ class CacheInfo(ctypes.Structure):
         "off_cent", "off_sums", "off_meta", "off_members", "off_entry_leaf", "off_tree_cent", "off_tree_sums",
         "stride_cent", "stride_sums", "stride_meta", "stride_members", "stride_entry_leaf", "stride_tree_cent",
         "stride_tree_sums", "total_bytes", "off_entry_pos", "stride_entry_pos", "off_edge_cent", "stride_edge_cent")
-    ] + [("edge_levels", ctypes.c_int32)]
+    ] + [("edge_levels", ctypes.c_int32)] + [(n, ctypes.c_size_t) for n in (
+        "off_cent_i8", "stride_cent_i8", "off_cent_scale", "stride_cent_scale")]
 
 
 class LsaError(RuntimeError):

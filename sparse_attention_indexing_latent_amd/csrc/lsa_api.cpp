@@ -62,8 +62,9 @@ struct CacheGeom {
     int64_t level_off[lsa::kMaxLevels];
     int64_t level_size[lsa::kMaxLevels];
     int32_t n_lev_cap;   // levels of a tree over leaves_max leaves
-    size_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos, s_edge;   // bytes per (b, g)
-    size_t off_cent, off_sums, off_meta, off_members, off_eleaf, off_tcent, off_tsums, off_epos, off_edge, total;
+    size_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos, s_edge, s_cq, s_csc;   // per (b, g)
+    size_t off_cent, off_sums, off_meta, off_members, off_eleaf, off_tcent, off_tsums, off_epos, off_edge, off_cq,
+        off_csc, total;
 };
 
 int64_t tree_nodes_above(int64_t nl) {
@@ -111,6 +112,8 @@ void cache_geom(const lsa_layout* L, int64_t B, int64_t t_max, int64_t T, CacheG
     c.s_tsums = align256((size_t)c.nnm * LSA_LATENT_DIM * 4);
     c.s_epos = align256((size_t)c.nbm * LSA_BLOCK_ENTRIES);
     c.s_edge = L->build_tree ? align256((size_t)(c.nbm + 1) * c.n_lev_cap * LSA_LATENT_DIM * c.elt) : 0;
+    c.s_cq = L->dtype == LSA_BF16 ? align256((size_t)c.nlm * LSA_LATENT_DIM) : 0;   // int8 codes
+    c.s_csc = L->dtype == LSA_BF16 ? align256((size_t)c.nlm * 4) : 0;              // fp32 scales
     size_t o = 0;
     c.off_cent = o;    o += c.s_cent * HB;
     c.off_sums = o;    o += c.s_sums * HB;
@@ -121,6 +124,8 @@ void cache_geom(const lsa_layout* L, int64_t B, int64_t t_max, int64_t T, CacheG
     c.off_tsums = o;   o += c.s_tsums * HB;
     c.off_epos = o;    o += c.s_epos * HB;
     c.off_edge = o;    o += c.s_edge * HB;
+    c.off_cq = o;      o += c.s_cq * HB;
+    c.off_csc = o;     o += c.s_csc * HB;
     c.total = o > 0 ? o : 256;
 }
 
@@ -137,6 +142,10 @@ lsa::CacheView make_view(const CacheGeom& c, void* cache, bool bf16) {
     v.tsums = reinterpret_cast<float*>(base + c.off_tsums);
     v.epos = reinterpret_cast<uint8_t*>(base + c.off_epos);
     v.edge = base + c.off_edge;
+    v.cq = reinterpret_cast<int8_t*>(base + c.off_cq);
+    v.csc = reinterpret_cast<float*>(base + c.off_csc);
+    v.s_cq = (int64_t)c.s_cq;
+    v.s_csc = (int64_t)(c.s_csc / 4);
     v.s_cent = (int64_t)(c.s_cent / c.elt);
     v.s_sums = (int64_t)(c.s_sums / 4);
     v.s_meta = (int64_t)(c.s_meta / 4);
@@ -364,6 +373,10 @@ lsa_status lsa_cache_describe(const lsa_layout* layout, int64_t batch, int64_t t
     info->off_edge_cent = c.off_edge;
     info->stride_edge_cent = c.s_edge;
     info->edge_levels = c.n_lev_cap;
+    info->off_cent_i8 = c.off_cq;
+    info->stride_cent_i8 = c.s_cq;
+    info->off_cent_scale = c.off_csc;
+    info->stride_cent_scale = c.s_csc;
     return ok();
 }
 

@@ -293,6 +293,29 @@ __global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restric
                                ((uint32_t)f32_to_bf16(mu[c + 2 * e + 1] * inv) << 16);
                     cw[cent_tile_word(leaf, h, m)] = uint4{w[0], w[1], w[2], w[3]};
                 }
+            // int8 codes of the rounded centroid: scale = max |c| / 127, code = round(c / scale)
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < kLatent; ++c) amax = fmaxf(amax, fabsf(bf16_to_f32(f32_to_bf16(mu[c] * inv))));
+            const float sc = amax / 127.0f;
+            uint4* qw = reinterpret_cast<uint4*>(cv.cq + bg * cv.s_cq);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const float c = bf16_to_f32(f32_to_bf16(mu[16 * h + 4 * e + b] * inv));
+                        const int code = sc > 0.f ? (int)fminf(fmaxf(rintf(c / sc), -127.f), 127.f) : 0;
+                        word |= (uint32_t)(uint8_t)(int8_t)code << (8 * b);
+                    }
+                    w[e] = word;
+                }
+                qw[(leaf >> 4) * 64 + (leaf & 15) + 16 * h] = uint4{w[0], w[1], w[2], w[3]};
+            }
+            cv.csc[bg * cv.s_csc + leaf] = sc;
         } else {
             float* crow = reinterpret_cast<float*>(cv.cent) + bg * cv.s_cent + leaf * kLatent;
 #pragma unroll

@@ -25,6 +25,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- cache view
@@ -40,7 +41,9 @@ struct CacheView {
     float* tsums;          // [B, H_kv, nodes_max, 64]
     uint8_t* epos;         // [B, H_kv, n_blocks_max, 512] position of each entry in its bucket's member list
     void* edge;            // [B, H_kv, n_blocks_max + 1, n_lev_cap, 64] dtype: node straddling 64 nb leaves
-    int64_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos, s_edge;
+    int8_t* cq;            // bf16 only: [B, H_kv, leaves_max / 16 tiles, 1 KB] int8 codes of the centroids
+    float* csc;            // bf16 only: [B, H_kv, leaves_max] their scales
+    int64_t s_cent, s_sums, s_meta, s_members, s_eleaf, s_tcent, s_tsums, s_epos, s_edge, s_cq, s_csc;
     int32_t n_blocks;      // full blocks bucketed
     int32_t n_leaves;
     int32_t n_levels;      // tree levels including the leaves

@@ -1235,7 +1235,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
 // decode_finish_kernel, one workgroup per unit: bounds the candidates with
 // the tile maxima, ranks and walks them, and writes the tokens in order
 // (below).
-constexpr int kScoreTiles = 16;   // tiles (16 buckets each) per scoring workgroup: small workgroups overlap best
+constexpr int kScoreTiles = 128;   // tiles (16 buckets each) per scoring workgroup
 
 // Eligible tokens of a bucket whose block lies inside or outside [sink_end,
 // l0); a block straddling an edge (at most two) needs its member lists.
@@ -1255,6 +1255,73 @@ __device__ __forceinline__ void straddling_blocks(const Geom& q, int& b0, int& b
 __device__ __forceinline__ bool unit_is_trivial(int64_t t, const Geom& q, int k) {
     const int64_t total = q.l0 > q.sink_end ? q.l0 - q.sink_end : 0;
     return t < 0 || k == 0 || (int64_t)k >= total;
+}
+
+// int8 stage of the bf16 decode scan.  Lane (n, kg) of a wave holds query
+// head n's latent dims [16 kg, 16 kg + 16) (zero past the group) as int8
+// codes q = round(qhat / sq_n), sq_n = max |qhat_n| / 127.  With the leaf
+// codes c = round(cent / sc_x) (the cache's int8 copy), the stage-1 score of
+// leaf x is s~ = max_n D_nx sq_n sc_x (D the exact int32 code dot product),
+// and |s~ - s| <= sc_x Qa + Qb for the bf16 score s of the same leaf:
+//   Qa = 0.5001 max_n ||qhat_n||_1      (the leaf's rounding, |cent - sc c| <= 0.5001 sc),
+//   Qb = 0.5001 * 8.3 max_n sq_n + 1e-5 (the query's rounding against ||sc c||_1 <= 8.3 for a
+//        centroid of norm <= 1.002, plus fp32 rounding of both scores).
+struct QCodes {
+    i32x4 codes;     // this lane's 16 codes (B operand of the int8 MFMA)
+    float sq;        // sq of this lane's head column (0 past the group)
+    float qa, qb;    // the unit's bound constants
+};
+__device__ __forceinline__ QCodes query_codes(const uint16_t* qrow_h0, int G) {
+    const int l = lane_id(), n = l & 15, kg = l >> 4;
+    float v[16];
+    if (n < G) {
+        const uint4* p = reinterpret_cast<const uint4*>(qrow_h0 + n * kLatent + 16 * kg);
+        const uint4 a = p[0], b = p[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = 0.f;
+    }
+    float amax = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        amax = fmaxf(amax, fabsf(v[i]));
+        l1 += fabsf(v[i]);
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    l1 += __shfl_xor(l1, 16);
+    l1 += __shfl_xor(l1, 32);
+    QCodes r;
+    r.sq = amax / 127.0f;
+    const float rq = r.sq > 0.f ? __builtin_amdgcn_rcpf(r.sq) : 0.f;   // 1 ulp: |code - q / sq| <= 0.50003
+    uint32_t w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float x = v[4 * e + b];
+            const int c = (int)fminf(fmaxf(rintf(x * rq), -127.f), 127.f);
+            word |= (uint32_t)(uint8_t)(int8_t)c << (8 * b);
+        }
+        w4[e] = word;
+    }
+    r.codes = i32x4{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]};
+    float qa = l1 * 1.0001f, qs = r.sq;   // l1 of head n (every kg lane), its sq
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        qa = fmaxf(qa, __shfl_xor(qa, o));
+        qs = fmaxf(qs, __shfl_xor(qs, o));
+    }
+    r.qa = 0.5001f * qa;
+    r.qb = 0.5001f * 8.3f * qs + 1e-5f;
+    return r;
 }
 
 // Largest of the 16 scores of a tile held as 4 values in each of the lanes 0, 16, 32, 48 (in every
@@ -1286,50 +1353,53 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
     float* sc = scores + u * score_stride;
     float* tmx = tmax + u * tmax_stride;
     if constexpr (BF16) {
-        // B operand: query head n of the group in column n (zero columns past G);
-        // the group max is taken across the 16 lanes of each row group
-        uint4 qa = {0, 0, 0, 0}, qc = {0, 0, 0, 0};
-        if (n < sa.G) {
-            const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(qhat) + qrow +
-                                                            n * kLatent + 16 * h);
-            qa = p[0];
-            qc = p[1];
-        }
-        const bf16x8 q0 = as_bf16x8(qa), q1 = as_bf16x8(qc);
-        const uint16_t* cb = reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent;
+        // stage-1 scores from the int8 codes (query head n in column n); the tile maximum taken of the
+        // upper bounds s~ + sc Qa + Qb
+        const QCodes qc = query_codes(reinterpret_cast<const uint16_t*>(qhat) + qrow, sa.G);
+        const float sqn = n < sa.G ? qc.sq : -1.0f;   // a negative factor marks the columns past the group
+        const uint4* cq = reinterpret_cast<const uint4*>(cv.cq + bg * cv.s_cq);
+        const float* csc = cv.csc + bg * cv.s_csc;
         // batches of TPI tiles; the next batch's loads are in flight while one is scored
         // (loads are unconditional, past the last tile they repeat it, so they stay in flight together)
         constexpr int TPI = 4;
-        uint4 a[2][TPI][2];
+        uint4 a[2][TPI];
+        float4 scl[2][TPI];
+        auto issue = [&](int buf, int tb) {
 #pragma unroll
-        for (int j = 0; j < TPI; ++j)
-            load_cent_bf16(cb, (int64_t)min(w0 + j, w1 - 1) * 16, a[0][j][0], a[0][j][1]);
+            for (int j = 0; j < TPI; ++j) {
+                const int64_t tt = min(tb + j, w1 - 1);
+                a[buf][j] = cq[tt * 64 + l];
+                scl[buf][j] = *reinterpret_cast<const float4*>(csc + tt * 16 + 4 * h);
+            }
+        };
+        issue(0, w0);
         for (int tt0 = w0; tt0 < w1; tt0 += 2 * TPI) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int tb = tt0 + half * TPI;
                 if (tb >= w1) break;
-#pragma unroll
-                for (int j = 0; j < TPI; ++j)
-                    load_cent_bf16(cb, (int64_t)min(tb + TPI + j, w1 - 1) * 16, a[half ^ 1][j][0], a[half ^ 1][j][1]);
+                issue(half ^ 1, tb + TPI);
 #pragma unroll
                 for (int j = 0; j < TPI; ++j) {
                     if (tb + j < w1) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[half][j][0]), q0, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[half][j][1]), q1, acc, 0, 0, 0);
-                        f32x4 vals;
+                        const uint4 av = a[half][j];
+                        i32x4 acc = {0, 0, 0, 0};
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{(int)av.x, (int)av.y, (int)av.z, (int)av.w},
+                                                                    qc.codes, acc, 0, 0, 0);
+                        const float scv[4] = {scl[half][j].x, scl[half][j].y, scl[half][j].z, scl[half][j].w};
+                        f32x4 vals, ub;
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            float x = n < sa.G ? acc[v] : kNegInf;
+                            float x = sqn >= 0.f ? (float)acc[v] * sqn : kNegInf;
                             x = fmaxf(x, __shfl_xor(x, 1));
                             x = fmaxf(x, __shfl_xor(x, 2));
                             x = fmaxf(x, __shfl_xor(x, 4));
                             x = fmaxf(x, __shfl_xor(x, 8));
-                            vals[v] = x;
+                            vals[v] = x * scv[v];
+                            ub[v] = vals[v] + (scv[v] * qc.qa + qc.qb);
                         }
                         if (n == 0) *reinterpret_cast<f32x4*>(sc + (int64_t)(tb + j) * 16 + 4 * h) = vals;
-                        const float m = tile_max(vals);   // every lane takes part in the shuffles
+                        const float m = tile_max(ub);   // every lane takes part in the shuffles
                         if (l == 0) tmx[tb + j] = m;
                     }
                 }
@@ -1593,7 +1663,8 @@ constexpr int kFinOutPer = 8;    // output positions a thread places together
 // hides behind the ranking.  More than kFinTiles tiles, S larger than
 // kCandCap, more than kSelCap taken buckets or kFinSlots blocks: the workgroup
 // runs the exact radix path for the unit instead.
-__global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const int64_t* __restrict__ q_pos,
+__global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const void* __restrict__ qhat,
+                                                            const int64_t* __restrict__ q_pos,
                                                             SelArgs sa, const float* __restrict__ scores,
                                                             int64_t score_stride, const float* __restrict__ tmax,
                                                             int64_t tmax_stride, int32_t* lr_idx, int32_t* lr_cnt) {
@@ -1603,6 +1674,8 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     __shared__ __align__(16) uint64_t ckey[kFinC];      // C (or S's own entries when C overflows)
     __shared__ uint32_t cmeta[kFinC];
     __shared__ int cw[kFinC];
+    __shared__ int cp[kFinC];      // bounded scores: the candidates of C whose upper bound reaches the bound
+    __shared__ float cex[kFinC];   // their bf16 scores
     __shared__ __align__(16) uint4 cmem[kCandCap * 3];  // per S position: 24 member entries from off & ~7
     __shared__ int rk[kCandCap];                         // rank -> S position
     __shared__ uint64_t rmask[kSelCap];
@@ -1628,9 +1701,10 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     const int NT = kLeavesPerBlock * q.nvis / 16;
     // the exact radix path, in this workgroup, over the unit's scores (its LDS in arrays that are
     // free whenever it runs)
+    const bool filter = cv.bf16 != 0;   // scores are the int8 stage's s~, bounded by +-(sc Qa + Qb)
     auto to_exact = [&]() {
         const ExactLds m{hist, mask, reinterpret_cast<uint32_t*>(cmem), rk, sh4, ebc};
-        exact_select_unit<true>(cv, nullptr, q_pos, sa, u, const_cast<float*>(scores + u * score_stride), false,
+        exact_select_unit<true>(cv, qhat, q_pos, sa, u, const_cast<float*>(scores + u * score_stride), filter,
                                 lr_idx, lr_cnt, m);
     };
     static_assert(kCandCap * 3 * 4 >= kExactSel && kCandCap >= 256, "the exact path's LDS fits the finish's arrays");
@@ -1643,11 +1717,19 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     const float* tm = tmax + u * tmax_stride;
     const uint32_t* meta = cv.meta + bg * cv.s_meta;
     const uint16_t* mem_bg = cv.members + bg * cv.s_members;
-    int sb0, sb1;
-    straddling_blocks(q, sb0, sb1);
+    const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
     float tmr[kFinTmRegs];
 #pragma unroll
     for (int r = 0; r < kFinTmRegs; ++r) tmr[r] = tid + 256 * r < NT ? tm[tid + 256 * r] : 0.f;
+    float Qa = 0.f, Qb = 0.f;
+    if (filter) {   // the bound constants of the scan (the same arithmetic on the same query)
+        const QCodes qc = query_codes(reinterpret_cast<const uint16_t*>(qhat) + qrow, sa.G);
+        Qa = qc.qa;
+        Qb = qc.qb;
+    }
+    const float* csc = filter ? cv.csc + bg * cv.s_csc : nullptr;
+    int sb0, sb1;
+    straddling_blocks(q, sb0, sb1);
     clear_bins(hist);
     if (tid == 0) need_stk = 0;
     __syncthreads();
@@ -1659,17 +1741,34 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     uint32_t tb[16];   // this thread's bins of the tile-maximum histogram
     const int tabove = load_bins(hist, tb, sh4);
     // scores, metas and eligible tokens of buckets 4 c .. 4 c + 3 of tile x (0 tokens: not eligible)
-    auto quad_buckets = [&](int x, int c, float (&s4)[4], uint32_t (&m4)[4], int (&w4)[4]) {
-        const float4 sv = reinterpret_cast<const float4*>(sc + (int64_t)x * 16)[c];
-        const uint4 mv = reinterpret_cast<const uint4*>(meta + (int64_t)x * 16)[c];
-        s4[0] = sv.x;
-        s4[1] = sv.y;
-        s4[2] = sv.z;
-        s4[3] = sv.w;
-        m4[0] = mv.x;
-        m4[1] = mv.y;
-        m4[2] = mv.z;
-        m4[3] = mv.w;
+    // quarter tile c of tile x: the raw loads (scores, metas, scales), then the per-bucket values:
+    // scores, half-widths of their bounds (0 for exact scores), metas and eligible tokens
+    struct QuadRaw {
+        float4 sv;
+        uint4 mv;
+        float4 cs;
+    };
+    auto quad_load = [&](int x, int c) {
+        QuadRaw r;
+        r.sv = reinterpret_cast<const float4*>(sc + (int64_t)x * 16)[c];
+        r.mv = reinterpret_cast<const uint4*>(meta + (int64_t)x * 16)[c];
+        r.cs = filter ? reinterpret_cast<const float4*>(csc + (int64_t)x * 16)[c] : float4{0.f, 0.f, 0.f, 0.f};
+        return r;
+    };
+    auto quad_eval = [&](const QuadRaw& r, int x, int c, float (&s4)[4], float (&e4)[4], uint32_t (&m4)[4],
+                         int (&w4)[4]) {
+        s4[0] = r.sv.x;
+        s4[1] = r.sv.y;
+        s4[2] = r.sv.z;
+        s4[3] = r.sv.w;
+        e4[0] = filter ? r.cs.x * Qa + Qb : 0.f;
+        e4[1] = filter ? r.cs.y * Qa + Qb : 0.f;
+        e4[2] = filter ? r.cs.z * Qa + Qb : 0.f;
+        e4[3] = filter ? r.cs.w * Qa + Qb : 0.f;
+        m4[0] = r.mv.x;
+        m4[1] = r.mv.y;
+        m4[2] = r.mv.z;
+        m4[3] = r.mv.w;
         const int blk = x / (kLeavesPerBlock / 16);   // a tile lies in one block
         const int so = blk == sb0 ? 0 : (blk == sb1 ? kLeavesPerBlock : -1);
 #pragma unroll
@@ -1678,7 +1777,10 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
             w4[i] = so >= 0 ? stk[so + leaf % kLeavesPerBlock] : leaf_weight_whole(leaf, m4[i], q);
         }
     };
-    int M = min(NT, max(kFinMinTiles, sa.k / 16));
+    auto quad_buckets = [&](int x, int c, float (&s4)[4], float (&e4)[4], uint32_t (&m4)[4], int (&w4)[4]) {
+        quad_eval(quad_load(x, c), x, c, s4, e4, m4, w4);
+    };
+    int M = min(NT, filter ? max(4 * kFinMinTiles, sa.k / 8) : max(kFinMinTiles, sa.k / 16));
     int b1 = 0, nt = 0;
     bool have_stk = false;
     for (;;) {
@@ -1719,37 +1821,51 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
             have_stk = true;
             __syncthreads();
         }
-        // C and its weighted histogram: the buckets of the listed tiles with a bin >= b0 (a quarter
-        // tile per thread)
+        // The weighted histogram of the lower bounds s~ - e (bins >= b0) and C: the buckets of the listed
+        // tiles whose upper bound s~ + e has a bin >= b0 (e = 0 for exact scores; a quarter tile per thread)
         int wl = 0;
-        for (int idx = tid; idx < 4 * nt; idx += 256) {
-            const int x = tiles[idx >> 2], c4 = idx & 3;
-            float s4[4];
-            uint32_t m4[4];
-            int w4[4];
-            quad_buckets(x, c4, s4, m4, w4);
-            bool in[4];
-            int c = 0;
+        constexpr int QPT = 4;   // quarter tiles per thread whose loads are in flight together
+        for (int i0 = 0; i0 < 4 * nt; i0 += 256 * QPT) {
+            QuadRaw raw[QPT];   // every load first, then the evaluation
+            int xq[QPT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int bin = fin_bin(s4[i]);
-                in[i] = w4[i] > 0 && bin >= b0;
-                if (in[i]) {
-                    atomicAdd(&hist[bin], (uint32_t)w4[i]);
-                    wl += w4[i];
-                    ++c;
-                }
+            for (int qq = 0; qq < QPT; ++qq) {
+                const int idx = min(i0 + 256 * qq + tid, 4 * nt - 1);
+                xq[qq] = tiles[idx >> 2];
+                raw[qq] = quad_load(xq[qq], idx & 3);
             }
-            int pos = c > 0 ? atomicAdd(&nc, c) : 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (in[i]) {
-                    if (pos < kFinC) {
-                        ckey[pos] = fin_key(s4[i], (uint32_t)(16 * x + 4 * c4 + i), pos);
-                        cmeta[pos] = m4[i];
-                        cw[pos] = w4[i];
+            for (int qq = 0; qq < QPT; ++qq) {
+                const int idx = i0 + 256 * qq + tid;
+                if (idx >= 4 * nt) break;
+                const int x = xq[qq], c4 = idx & 3;
+                float s4[QPT][4], e4[QPT][4];
+                uint32_t m4[QPT][4];
+                int w4[QPT][4];
+                quad_eval(raw[qq], x, c4, s4[qq], e4[qq], m4[qq], w4[qq]);
+                bool inc[4];
+                int c = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int bin = fin_bin(s4[qq][i] - e4[qq][i]);
+                    if (w4[qq][i] > 0 && bin >= b0) {
+                        atomicAdd(&hist[bin], (uint32_t)w4[qq][i]);
+                        wl += w4[qq][i];
                     }
-                    ++pos;
+                    inc[i] = w4[qq][i] > 0 && fin_bin(s4[qq][i] + e4[qq][i]) >= b0;
+                    c += inc[i] ? 1 : 0;
+                }
+                int pos = c > 0 ? atomicAdd(&nc, c) : 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (inc[i]) {
+                        if (pos < kFinC) {
+                            ckey[pos] = fin_key(s4[qq][i] + e4[qq][i], (uint32_t)(16 * x + 4 * c4 + i), pos);
+                            cmeta[pos] = m4[qq][i];
+                            cw[pos] = w4[qq][i];
+                        }
+                        ++pos;
+                    }
                 }
             }
         }
@@ -1775,7 +1891,11 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
         to_exact();
         return;
     }
-    // S: the buckets of C with a bin >= b1
+    // b1: the bin where the lower bounds' tokens reach k, so at least k tokens score >= its edge and
+    // every bucket scoring that high has its upper bound in a bin >= b1.  Exact scores (e = 0): S = the
+    // buckets of C with a bin >= b1.  Bounded scores: C' = the buckets of C whose upper bound has a
+    // bin >= b1, their bf16 scores computed here (the same MFMA as the exact scan), and S = those of C'
+    // at or above the bin b where their tokens reach k.
     if (tid == 0) {
         nk = 0;
         fin[0] = 0;
@@ -1783,7 +1903,84 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     }
     __syncthreads();
     const int ncc = nc;
-    if (ncc <= kFinC) {
+    if (filter && ncc > kFinC) {
+        to_exact();
+        return;
+    }
+    if (filter) {
+        if (tid == 0) ntl = 0;
+        clear_bins(hist);
+        __syncthreads();
+        for (int j0 = 0; j0 < ncc; j0 += 256) {   // C'
+            const int j = j0 + tid;
+            const bool in = j < ncc && fin_bin(fin_key_score(ckey[j])) >= b1;
+            const uint64_t bal = __ballot(in);
+            int base = 0;
+            if (l == 0 && bal) base = atomicAdd(&ntl, __popcll(bal));
+            base = __shfl(base, 0);
+            if (in) cp[base + __popcll(bal & lt)] = j;
+        }
+        __syncthreads();
+        const int ncp = ntl;
+        {   // bf16 scores of C': groups of 16 candidates (MFMA rows), two groups per wave in flight
+            const int n = l & 15, h = l >> 4;
+            uint4 qa4 = {0, 0, 0, 0}, qc4 = {0, 0, 0, 0};
+            if (n < sa.G) {
+                const uint4* pq = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(qhat) + qrow +
+                                                                 n * kLatent + 16 * h);
+                qa4 = pq[0];
+                qc4 = pq[1];
+            }
+            const bf16x8 q0 = as_bf16x8(qa4), q1 = as_bf16x8(qc4);
+            const uint4* cw4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
+            for (int g0 = 32 * wid; g0 < ncp; g0 += 128) {
+                uint4 a[2][2];
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    const int e = min(g0 + 16 * gg + n, ncp - 1);
+                    const uint32_t leaf = fin_key_id(ckey[cp[e]]);
+                    a[gg][0] = cw4[cent_tile_word(leaf, h, 0)];
+                    a[gg][1] = cw4[cent_tile_word(leaf, h, 1)];
+                }
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[gg][0]), q0, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[gg][1]), q1, acc, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = n < sa.G ? acc[v] : kNegInf;
+                        x = fmaxf(x, __shfl_xor(x, 1));
+                        x = fmaxf(x, __shfl_xor(x, 2));
+                        x = fmaxf(x, __shfl_xor(x, 4));
+                        x = fmaxf(x, __shfl_xor(x, 8));
+                        const int idx = g0 + 16 * gg + 4 * h + v;
+                        if (n == 0 && idx < ncp) cex[idx] = x;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        for (int j = tid; j < ncp; j += 256) atomicAdd(&hist[fin_bin(cex[j])], (uint32_t)cw[cp[j]]);
+        __syncthreads();
+        uint32_t eb[16];
+        const int eabove = load_bins(hist, eb, sh4);
+        if (tid == 0) bsel = -1;
+        __syncthreads();
+        crossing_bin(eb, eabove, sa.k, &bsel);
+        __syncthreads();
+        const int be = bsel;   // >= b1: C' holds every bucket scoring >= the edge of b1
+        for (int j0 = 0; j0 < ncp; j0 += 256) {   // S
+            const int j = j0 + tid;
+            const bool in = j < ncp && be >= 0 && fin_bin(cex[j]) >= be;
+            const uint64_t bal = __ballot(in);
+            int base = 0;
+            if (l == 0 && bal) base = atomicAdd(&nk, __popcll(bal));
+            base = __shfl(base, 0);
+            const int pos = base + __popcll(bal & lt);
+            if (in && pos < kCandCap) keys[pos] = fin_key(cex[j], fin_key_id(ckey[cp[j]]), cp[j]);
+        }
+    } else if (ncc <= kFinC) {
         for (int j0 = 0; j0 < ncc; j0 += 256) {
             const int j = j0 + tid;
             const uint64_t kc = j < ncc ? ckey[j] : 0ull;
@@ -1798,10 +1995,10 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     } else {   // C overflowed: S from the listed tiles again, its own entries in the C arrays
         for (int idx = tid; idx < 4 * nt; idx += 256) {
             const int x = tiles[idx >> 2], c4 = idx & 3;
-            float s4[4];
+            float s4[4], e4[4];
             uint32_t m4[4];
             int w4[4];
-            quad_buckets(x, c4, s4, m4, w4);
+            quad_buckets(x, c4, s4, e4, m4, w4);
             bool in[4];
             int c = 0;
 #pragma unroll
@@ -2330,7 +2527,8 @@ hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int6
                            sb.score_stride, sb.tmax, sb.tmax_stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)sa.n_units), dim3(256), 0, st, cv, q_pos, sa, sb.scores,
+    hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)sa.n_units), dim3(256), 0, st, cv, sb.qhat, q_pos, sa,
+                       sb.scores,
                        sb.score_stride, sb.tmax, sb.tmax_stride, lr_idx, lr_cnt);
     return hipGetLastError();
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(decl) == set(_lib.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert L.lsa_abi_version() == 6
+    assert L.lsa_abi_version() == 7
 
 
 def test_status_strings():
