@@ -1691,7 +1691,26 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     const uint64_t lt = (1ull << l) - 1ull;
     const int64_t u = blockIdx.x;
     const Unit un = unit_of(u, sa);
+    const bool filter = cv.bf16 != 0;   // scores are the int8 stage's s~, bounded by +-(sc Qa + Qb)
+    const int64_t bg = un.b * sa.H_kv + un.g;
+    const float* sc = scores + u * score_stride;
+    const float* tm = tmax + u * tmax_stride;
+    const uint32_t* meta = cv.meta + bg * cv.s_meta;
+    const uint16_t* mem_bg = cv.members + bg * cv.s_members;
+    const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
+    // the tile maxima of every bucketed tile and the query rows are loaded before the position (and so
+    // the visible tile count NT <= NTmax) is known: their loads are in flight together
+    const int NTmax = (int)min((int64_t)kLeavesPerBlock * cv.n_blocks / 16, tmax_stride);
+    float tmr[kFinTmRegs];
+#pragma unroll
+    for (int r = 0; r < kFinTmRegs; ++r) tmr[r] = tid + 256 * r < NTmax ? tm[tid + 256 * r] : 0.f;
     const int64_t t = q_pos[un.b * sa.n_q + un.i];
+    float Qa = 0.f, Qb = 0.f;
+    if (filter) {   // the bound constants of the scan (the same arithmetic on the same query)
+        const QCodes qc = query_codes(reinterpret_cast<const uint16_t*>(qhat) + qrow, sa.G);
+        Qa = qc.qa;
+        Qb = qc.qb;
+    }
     const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
     int32_t* out = lr_idx + u * sa.k;
     if (unit_is_trivial(t, q, sa.k)) {
@@ -1701,7 +1720,6 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     const int NT = kLeavesPerBlock * q.nvis / 16;
     // the exact radix path, in this workgroup, over the unit's scores (its LDS in arrays that are
     // free whenever it runs)
-    const bool filter = cv.bf16 != 0;   // scores are the int8 stage's s~, bounded by +-(sc Qa + Qb)
     auto to_exact = [&]() {
         const ExactLds m{hist, mask, reinterpret_cast<uint32_t*>(cmem), rk, sh4, ebc};
         exact_select_unit<true>(cv, qhat, q_pos, sa, u, const_cast<float*>(scores + u * score_stride), filter,
@@ -1711,21 +1729,6 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     if ((int64_t)NT * 16 > (int64_t)kFinIdMax + 1) {
         to_exact();
         return;
-    }
-    const int64_t bg = un.b * sa.H_kv + un.g;
-    const float* sc = scores + u * score_stride;
-    const float* tm = tmax + u * tmax_stride;
-    const uint32_t* meta = cv.meta + bg * cv.s_meta;
-    const uint16_t* mem_bg = cv.members + bg * cv.s_members;
-    const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
-    float tmr[kFinTmRegs];
-#pragma unroll
-    for (int r = 0; r < kFinTmRegs; ++r) tmr[r] = tid + 256 * r < NT ? tm[tid + 256 * r] : 0.f;
-    float Qa = 0.f, Qb = 0.f;
-    if (filter) {   // the bound constants of the scan (the same arithmetic on the same query)
-        const QCodes qc = query_codes(reinterpret_cast<const uint16_t*>(qhat) + qrow, sa.G);
-        Qa = qc.qa;
-        Qb = qc.qb;
     }
     const float* csc = filter ? cv.csc + bg * cv.s_csc : nullptr;
     int sb0, sb1;
@@ -1780,6 +1783,8 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     auto quad_buckets = [&](int x, int c, float (&s4)[4], float (&e4)[4], uint32_t (&m4)[4], int (&w4)[4]) {
         quad_eval(quad_load(x, c), x, c, s4, e4, m4, w4);
     };
+    // bounded scores need more tiles: the lower bounds of the top buckets must clear the bin of the
+    // M-th tile maximum of the upper bounds
     int M = min(NT, filter ? max(4 * kFinMinTiles, sa.k / 8) : max(kFinMinTiles, sa.k / 16));
     int b1 = 0, nt = 0;
     bool have_stk = false;
