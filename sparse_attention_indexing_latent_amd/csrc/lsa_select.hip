@@ -402,74 +402,79 @@ __global__ __launch_bounds__(256) void fused_scan_kernel(CacheView cv, const voi
 // The fused flat search's scan in one pass over the centroids, tiles shared
 // through LDS: a workgroup owns 128 queries of one KV head (32 per wave, as
 // two 16-query MFMA column groups), streams the visible tiles in chunks of 8
-// (16 KB) with their buckets' meta words, double-buffered, and every wave
-// reads its operand fragments from LDS (one fragment read feeds 2 x G x 2
-// MFMAs).
+// (24 KB) with their buckets' meta words (the next chunk in registers while
+// one is scored), and every wave reads its operand fragments from LDS (one
+// fragment read feeds 2 x G x 2 MFMAs).
 //
 // Each query keeps a histogram of certainly eligible token weight (4 x size
-// for buckets of blocks inside [sink_end, l0)) over score bins (8 of width
-// 1/8 below 0, 64 of width 1/64 over [0, 1), the end bins open) and a floor
-// bin fb: the highest bin at which the weight binned so far, summed from the
-// top, reaches k (raised after every chunk).  A visible bucket in a bin >= fb
-// is appended (rank key) to the query's candidate list and its weight binned;
+// for buckets of blocks inside [sink_end, l0)) over score bins (one below 0,
+// 64 of width 1/64 over [0, 1), the last open) and a floor bin fb: the
+// highest bin at which the weight binned so far, summed from the top,
+// reaches k (raised after every chunk).  A visible bucket in a bin >= fb is
+// appended (rank key) to the query's candidate list and its weight binned;
 // one below fb is skipped: fb only rises, so bins below it can never become
 // the final crossing bin b*, and every bin >= b* holds all of its weight.
 // Hence at the end tau = lower edge of b* (minus 2^-16; -inf if the weight
-// never reaches k) is the bound of the two-pass scan, and the list holds
-// every visible bucket scoring >= tau (plus earlier ones below it, dropped
-// by the finalize).  A query's list is 4 sub-lists of kSubCap slots, one per
-// lane of its MFMA column (no cross-lane step per append); their counts are
-// exact even past the cap.
+// never reaches k) bounds the k-th token's bucket score from below, and the
+// list holds every visible bucket scoring >= tau (plus earlier ones below
+// it, dropped by the finalize).  A query's list is 4 sub-lists of kSubCap
+// slots filled in order (one running count per query; the counts are exact
+// past the cap).  The floor rises by walking up from fb while the weight
+// above the next bin still reaches k, with the weight at or above fb kept
+// as a running sum (every binned bucket lies at or above the floor).
+//
+// Candidates are rare per lane (a query appends ~k(1 + ln(N/k)) of N
+// buckets, mostly early) but present in nearly every tile of a wave, so
+// appending them where they arise would run the wave's append code for one
+// or two lanes per tile.  Instead a lane whose 4 scores of a column group
+// reach the floor pushes them, as one group, into a per-wave LDS queue
+// (compacted by a ballot; the other lanes write just past the compacted
+// ones, which keeps the push free of branches), and the wave takes 64 groups
+// at a time, one per lane: each score still at or above the floor gets a
+// list slot from an LDS counter, its rank key stored, its weight binned.
+// The queue is emptied before the floors rise, so the histogram is complete
+// when they do.
+//
+// The tile loop is software-pipelined: the MFMAs of tile i + 1 are issued
+// before tile i's scores are tested and pushed, so the matrix core runs
+// while the same wave does the vector work of the previous tile.
 constexpr int kSelCap = 256;        // buckets one finalize wave may take (more: the exact path)
 constexpr int kScanQ = 128;         // queries per workgroup
-constexpr int kScanChunk = 8;       // tiles per staged chunk
-constexpr int kFNeg = 8;
-constexpr int kFBins = kFNeg + 64;
-constexpr int kFStride = kFBins + 1;   // odd: neighbouring queries fall in different banks
+constexpr int kScanChunk = 12;      // tiles per staged chunk (even)
+constexpr int kQueueCap = 192;      // queued groups per wave: < 64 left + 2 column groups x 64
+constexpr int kHBins = 65;          // score bins: s < 0, then 64 of width 1/64 over [0, 1) (the last open)
+constexpr int kHStride = kHBins;    // odd: neighbouring queries' rows fall in different banks
 constexpr int kMaxLeavesI = 0x7FFFFFFF;
 constexpr float kFltMax = 3.402823466e38f;
 constexpr float kPosInf = __builtin_huge_valf();
 
-// multiplications by powers of two are exact, so bin(s) >= b  <=>  s >= edge(b)
-__device__ __forceinline__ int fscan_bin(float s) {
-    const int bp = min(kFNeg + (int)(s * 64.0f), kFBins - 1);
-    const int bn = max(kFNeg + (int)floorf(s * 8.0f), 0);
-    return s >= 0.f ? bp : bn;
-}
+// multiplications by powers of two are exact, so for b >= 1: bin(s) >= b  <=>  s >= edge(b)
+__device__ __forceinline__ int hbin(float s) { return s < 0.f ? 0 : min(1 + (int)(s * 64.0f), kHBins - 1); }
+__device__ __forceinline__ float hedge(int b) { return (float)(b - 1) * (1.0f / 64.0f); }
 
-__device__ __forceinline__ float fscan_edge(int bin) {
-    return bin >= kFNeg ? (float)(bin - kFNeg) * (1.0f / 64.0f) : (float)(bin - kFNeg) * (1.0f / 8.0f);
-}
-
-// The highest bin at which one query's histogram, summed from the top,
-// reaches k (-1 if it never does).  The query's 4 lanes (h = 0..3, the same
-// n) each take a quarter of the bins into registers, the top quarter on
-// h = 0; the lane whose quarter holds the crossing walks it down.  All 64
-// lanes call it (it shuffles across the wave); the result is on all 4.
-__device__ __forceinline__ int fscan_cross_bin(const uint32_t* row, int h, uint32_t k) {
-    constexpr int Q4 = kFBins / 4;
-    const int lo = kFBins - Q4 * (h + 1);   // this lane's bins: [lo, lo + Q4)
-    uint32_t w[Q4];
-    uint32_t sq = 0;
+// The 2 x G x 2 MFMAs of one tile (fragments a0, a1) for both column groups, and the max over heads.
+template <int G>
+__device__ __forceinline__ void scan_mfma(f32x4 (&acc)[2][G], const bf16x8& a0, const bf16x8& a1,
+                                          const bf16x8 (&qf)[2][G][2]) {
 #pragma unroll
-    for (int j = 0; j < Q4; ++j) w[j] = row[lo + j];
+    for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
-    for (int j = 0; j < Q4; ++j) sq += w[j];
-    const int n = lane_id() & 15;
-    const uint32_t s0 = (uint32_t)__shfl((int)sq, n), s1 = (uint32_t)__shfl((int)sq, n + 16),
-                   s2 = (uint32_t)__shfl((int)sq, n + 32);
-    uint32_t cum = (h > 0 ? s0 : 0u) + (h > 1 ? s1 : 0u) + (h > 2 ? s2 : 0u);
-    int bin = -1;
-    if (cum < k) {
-#pragma unroll
-        for (int j = Q4 - 1; j >= 0; --j) {
-            cum += w[j];
-            bin = (bin < 0 && cum >= k) ? lo + j : bin;
+        for (int hh = 0; hh < G; ++hh) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[cg][hh][0], c, 0, 0, 0);
+            acc[cg][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[cg][hh][1], c, 0, 0, 0);
         }
+}
+template <int G>
+__device__ __forceinline__ void head_max(const f32x4 (&acc)[2][G], f32x4 (&best)[2]) {
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+        best[cg] = acc[cg][0];
+#pragma unroll
+        for (int hh = 1; hh < G; ++hh)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) best[cg][v] = fmax_nc(best[cg][v], acc[cg][hh][v]);
     }
-    bin = max(bin, __shfl_xor(bin, 16));
-    bin = max(bin, __shfl_xor(bin, 32));
-    return bin;
 }
 
 template <int G>
@@ -477,28 +482,45 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
                                                          const int64_t* __restrict__ q_pos, SelArgs sa,
                                                          float* __restrict__ tau, int* __restrict__ cnt,
                                                          uint64_t* __restrict__ cand) {
-    __shared__ __align__(16) uint4 stage[2][kScanChunk * 128];   // 2 x 16 KB
-    __shared__ __align__(16) uint4 smeta[2][kScanChunk * 4];     // 16 meta words per tile
-    __shared__ uint32_t hist[kScanQ * kFStride];
+    __shared__ __align__(16) uint4 stage[kScanChunk * 128];     // 24 KB
+    __shared__ __align__(16) uint32_t smeta[kScanChunk * 16];   // meta word of every bucket of the chunk
+    __shared__ uint32_t hist[kScanQ * kHStride];
+    __shared__ __align__(16) f32x4 qsc[4][kQueueCap];           // per wave: queued groups' 4 scores
+    __shared__ uint16_t qhd[4][kQueueCap];                      //   and (tile << 7 | h << 5 | query slot)
+    __shared__ int lcnt[kScanQ];                                // candidate list lengths
+    __shared__ uint32_t wsum[kScanQ];                           // binned weight at or above the floor bin
+    __shared__ int fbin[kScanQ];                                // floor bins
+    __shared__ float fedge[kScanQ];                             // floor edges (+inf: no query)
+    __shared__ int2 erng[kScanQ];                               // blocks [x, y) certainly eligible
     __shared__ int wmax[4], wmin[4];
     const int tid = threadIdx.x, l = lane_id(), wid = tid >> 6, n = l & 15, h = l >> 4;
     const int64_t b = blockIdx.z, g = blockIdx.y;
     const int64_t bg = b * sa.H_kv + g;
-    // per column group cg: this lane's query (column n)
-    int64_t u[2], lo_ok[2], hi_ok[2];
+    // unit of the wave's query slot qs (0..31) = ubase + qs * H_kv
+    const int64_t q0 = (int64_t)blockIdx.x * kScanQ + wid * 32;   // the wave's first query
+    const int64_t ubase = (b * sa.n_q + q0) * sa.H_kv + g;
+    // per column group cg: this lane's query (column n), query slot 16 cg + n
     int NLv[2];
     bool qv[2];
     bf16x8 qf[2][G][2];
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg) {
-        const int64_t iq = (int64_t)blockIdx.x * kScanQ + wid * 32 + cg * 16 + n;
+        const int64_t iq = q0 + cg * 16 + n;
         qv[cg] = iq < sa.n_q;
         const int64_t t = qv[cg] ? q_pos[b * sa.n_q + iq] : -1;
         const Geom q = query_geom(t < 0 ? 0 : t, cv.n_blocks, sa.n_sinks, sa.window);
         NLv[cg] = t < 0 ? 0 : kLeavesPerBlock * q.nvis;
-        lo_ok[cg] = q.sink_end;
-        hi_ok[cg] = q.l0;
-        u[cg] = (b * sa.n_q + (qv[cg] ? iq : 0)) * sa.H_kv + g;
+        if (h == 0) {
+            const int qw = wid * 32 + cg * 16 + n;
+            lcnt[qw] = 0;
+            wsum[qw] = 0u;
+            fbin[qw] = 0;
+            // every score is a candidate before the floor rises (-FLT_MAX: a masked -inf is not); a
+            // column without a query never has one
+            fedge[qw] = qv[cg] ? -kFltMax : kPosInf;
+            // block j is eligible iff sink_end <= 2048 j and 2048 (j + 1) <= l0
+            erng[qw] = int2{(int)((q.sink_end + kBlockTokens - 1) / kBlockTokens), (int)(q.l0 / kBlockTokens)};
+        }
         const int64_t qrow = ((b * sa.n_q + (qv[cg] ? iq : 0)) * sa.H_q + g * sa.G) * kLatent;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
@@ -512,10 +534,13 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
             qf[cg][hh][1] = as_bf16x8(c);
         }
     }
-    uint32_t* hrow[2] = {hist + (wid * 32 + n) * kFStride, hist + (wid * 32 + 16 + n) * kFStride};
-    uint64_t* sub0 = cand + u[0] * kCandStride + h * kSubCap;
-    uint64_t* sub1 = cand + u[1] * kCandStride + h * kSubCap;
-    for (int j = tid; j < kScanQ * kFStride; j += 256) hist[j] = 0u;
+    // wait for the query fragments here: with them still in flight the compiler would wait for every
+    // outstanding load before each chunk's tile loop (a loop holding stores and no loads), the chunk
+    // prefetch included
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    // queue header of this lane's group of column group cg in tile tt: (tt << 7) | (h << 5) | slot
+    const uint32_t hb[2] = {((uint32_t)h << 5) | (uint32_t)n, ((uint32_t)h << 5) | (uint32_t)(16 + n)};
+    for (int j = tid; j < kScanQ * kHStride; j += 256) hist[j] = 0u;
     // tiles visible to any query of the workgroup, and to all of them
     const int wm = wave_max_i(max(NLv[0], NLv[1]));
     const int wn = wave_min_i(min(qv[0] ? NLv[0] : kMaxLeavesI, qv[1] ? NLv[1] : kMaxLeavesI));
@@ -527,131 +552,185 @@ __global__ __launch_bounds__(256) void scan_fused_kernel(CacheView cv, const uin
     const int maxNLv = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
     const int minNLv = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
     const int ntl = maxNLv / 16;
+    const int ntlm = minNLv / 16;   // tiles visible to every query: no masking
     const int nch = (ntl + kScanChunk - 1) / kScanChunk;
     const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
     const u32x4* msrc = reinterpret_cast<const u32x4*>(cv.meta + bg * cv.s_meta);
-    int fb[2] = {0, 0};
-    // floor edges: every score is a candidate before the floor rises (-FLT_MAX: a masked -inf is not);
-    // a column without a query never has one
     float fe[2] = {qv[0] ? -kFltMax : kPosInf, qv[1] ? -kFltMax : kPosInf};
-    int base[2] = {0, 0};   // length of this lane's sub-list (h) of its query's candidate list
-    // staging: thread tid copies words tid + 256 j (j < 4) of a chunk and, if tid < 32, meta word tid;
-    // tiles past the last one repeat it
-    u32x4 r0, r1, r2, r3, rmt;
-#define LSA_LOAD_CHUNK(c)                                                                               \
-    {                                                                                                   \
-        r0 = src[(int64_t)min((c) * kScanChunk + (tid) / 128, ntl - 1) * 128 + (tid & 127)];            \
-        r1 = src[(int64_t)min((c) * kScanChunk + (tid + 256) / 128, ntl - 1) * 128 + (tid & 127)];      \
-        r2 = src[(int64_t)min((c) * kScanChunk + (tid + 512) / 128, ntl - 1) * 128 + (tid & 127)];      \
-        r3 = src[(int64_t)min((c) * kScanChunk + (tid + 768) / 128, ntl - 1) * 128 + (tid & 127)];      \
-        if (tid < kScanChunk * 4) rmt = msrc[(int64_t)min((c) * kScanChunk + tid / 4, ntl - 1) * 4 + (tid & 3)]; \
-    }
-#define LSA_STORE_CHUNK(bf)                                                                             \
-    {                                                                                                   \
-        u32x4* d4 = reinterpret_cast<u32x4*>(stage[bf]);                                                \
-        d4[tid] = r0;                                                                                   \
-        d4[tid + 256] = r1;                                                                             \
-        d4[tid + 512] = r2;                                                                             \
-        d4[tid + 768] = r3;                                                                             \
-        if (tid < kScanChunk * 4) reinterpret_cast<u32x4*>(smeta[bf])[tid] = rmt;                       \
-    }
-    if (nch > 0) {
-        LSA_LOAD_CHUNK(0)
-        LSA_STORE_CHUNK(0)
-    }
-    __syncthreads();
+    f32x4* qs_w = qsc[wid];
+    uint16_t* qh_w = qhd[wid];
+    int qn = 0;   // queued groups of this wave (uniform)
+    // One queued group per lane (slot e, chunk c): each of its scores at or above its query's floor edge
+    // is appended to the query's list and, if its block is certainly eligible, binned.
+    auto take = [&](int e, int c) {
+        const f32x4 sv = qs_w[e];
+        const uint32_t hd = qh_w[e];
+        const int qs = (int)(hd & 31u);
+        const int xl0 = (int)(hd >> 5) * 4;   // bucket of value 0 within the chunk: 16 tile + 4 h
+        const int qw = wid * 32 + qs;
+        const float fq = fedge[qw];
+        const int x0 = c * kScanChunk * 16 + xl0;
+        const int2 er = erng[qw];
+        const int blk = x0 / kLeavesPerBlock;
+        const bool el = (blk >= er.x) & (blk < er.y);
+        bool p[4];
+        int np = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            p[v] = sv[v] >= fq;
+            np += p[v] ? 1 : 0;
+        }
+        int pos = atomicAdd(&lcnt[qw], np);   // slot pos % kSubCap of sub-list pos / kSubCap
+        uint64_t* dst = cand + (ubase + (int64_t)qs * sa.H_kv) * kCandStride;
+        uint32_t wadd = 0;
+        uint32_t* hr = hist + qw * kHStride;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            if (p[v]) {
+                if (pos < kCandStride) dst[pos] = rank_key(sv[v], (uint32_t)(x0 + v));
+                ++pos;
+                if (el) {
+                    const uint32_t w = (uint32_t)kPool * (smeta[xl0 + v] & 0xFFu);
+                    atomicAdd(&hr[hbin(sv[v])], w);
+                    wadd += w;
+                }
+            }
+        }
+        if (wadd) atomicAdd(&wsum[qw], wadd);
+    };
+    // A lane whose scores of column group cg reach the floor pushes them as a group (tile tt).  Compacted
+    // slots from the ballot; the other lanes write the slots right after them, which later pushes
+    // overwrite (every lane writes, so the push has no branch).
+    auto push = [&](const f32x4 (&best)[2], int tt) {
+        const uint32_t tb = (uint32_t)tt << 7;
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+            const float lm = fmax_nc(fmax_nc(best[cg][0], best[cg][1]), fmax_nc(best[cg][2], best[cg][3]));
+            const bool p = lm >= fe[cg];
+            const uint64_t m = __ballot(p);
+            const int cm = (int)__popcll(m);
+            const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)qn));
+            const uint32_t post = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(~m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)~m, (uint32_t)(qn + cm)));
+            const int slot = (int)(p ? pre : post);
+            qs_w[slot] = best[cg];
+            qh_w[slot] = (uint16_t)(hb[cg] + tb);
+            qn += cm;
+        }
+    };
+    auto drain = [&](int c) {
+        if (qn >= 64) {
+            wave_sync();
+            do {
+                qn -= 64;
+                take(qn + l, c);
+            } while (qn >= 64);
+            wave_sync();
+        }
+    };
+    // staging: thread tid copies words tid + 256 j (j < kScanChunk / 2) of a chunk and, if tid <
+    // 4 kScanChunk, meta word tid; tiles past the last one repeat it
+    constexpr int kRW = kScanChunk / 2;
+    u32x4 rw[kRW], rmt;
+    auto load_chunk = [&](int c) {
+#pragma unroll
+        for (int j = 0; j < kRW; ++j)
+            rw[j] = src[(int64_t)min(c * kScanChunk + (tid + 256 * j) / 128, ntl - 1) * 128 + (tid & 127)];
+        if (tid < kScanChunk * 4) rmt = msrc[(int64_t)min(c * kScanChunk + tid / 4, ntl - 1) * 4 + (tid & 3)];
+    };
+    if (nch > 0) load_chunk(0);
     for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) LSA_LOAD_CHUNK(c + 1)
-        const uint4* sb = stage[c & 1];
-        const uint4* sm = smeta[c & 1];
+        {
+            u32x4* d4 = reinterpret_cast<u32x4*>(stage);
+#pragma unroll
+            for (int j = 0; j < kRW; ++j) d4[tid + 256 * j] = rw[j];
+            if (tid < kScanChunk * 4) reinterpret_cast<u32x4*>(smeta)[tid] = rmt;
+        }
+        __syncthreads();
+        if (c + 1 < nch) load_chunk(c + 1);
         const int tend = min(kScanChunk, ntl - c * kScanChunk);
-        bf16x8 a0 = as_bf16x8(sb[l]), a1 = as_bf16x8(sb[64 + l]);
-        for (int tt = 0; tt < tend; ++tt) {
-            const int x0 = (c * kScanChunk + tt) * 16;
-            const int xb = x0 + 4 * h;
-            f32x4 best[2];
+        const int tmain = min(max(ntlm - c * kScanChunk, 0), tend);
+        f32x4 acc[2][G], best[2];
+        if (tmain > 0) {
+            scan_mfma<G>(acc, as_bf16x8(stage[l]), as_bf16x8(stage[64 + l]), qf);
+            for (int tt = 0; tt + 1 < tmain; ++tt) {
+                const bf16x8 a0 = as_bf16x8(stage[(tt + 1) * 128 + l]), a1 = as_bf16x8(stage[(tt + 1) * 128 + 64 + l]);
+                head_max<G>(acc, best);
+                scan_mfma<G>(acc, a0, a1, qf);   // tile tt + 1 runs while tile tt is pushed
+                push(best, tt);
+                // one MFMA, then two vector instructions of the previous tile's work, in turn
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-            for (int cg = 0; cg < 2; ++cg) {
+                for (int i = 0; i < 2 * G * 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                }
+                drain(c);
+            }
+            head_max<G>(acc, best);
+            push(best, tmain - 1);
+            drain(c);
+        }
+        // tiles past some query's visible leaves: those buckets never become candidates
+        for (int tt = tmain; tt < tend; ++tt) {
+            scan_mfma<G>(acc, as_bf16x8(stage[tt * 128 + l]), as_bf16x8(stage[tt * 128 + 64 + l]), qf);
+            head_max<G>(acc, best);
+            const int xb = (c * kScanChunk + tt) * 16 + 4 * h;
 #pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[cg][hh][0], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[cg][hh][1], acc, 0, 0, 0);
-                    if (hh == 0) {
-                        best[cg] = acc;
-                    } else {
-                        best[cg][0] = fmaxf(best[cg][0], acc[0]);
-                        best[cg][1] = fmaxf(best[cg][1], acc[1]);
-                        best[cg][2] = fmaxf(best[cg][2], acc[2]);
-                        best[cg][3] = fmaxf(best[cg][3], acc[3]);
+            for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    best[cg][v] = (qv[cg] && xb + v < NLv[cg]) ? best[cg][v] : kNegInf;
+            push(best, tt);
+            drain(c);
+        }
+        // the chunk's last queued groups, then raise the floors (the rows are this wave's own)
+        wave_sync();
+        if (l < qn) take(l, c);
+        qn = 0;
+        wave_sync();
+        if (l < 32) {
+            // 8 bins read at once, walked in registers (the floor seldom rises further per chunk)
+            const int qw = wid * 32 + l;
+            int f = fbin[qw];
+            uint32_t W = wsum[qw];
+            const uint32_t* hr = hist + qw * kHStride;
+            bool up = true;
+            while (up) {
+                uint32_t hv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) hv[j] = hr[min(f + j, kHBins - 1)];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    up = up && f < kHBins - 1 && W - hv[j] >= (uint32_t)sa.k;
+                    if (up) {
+                        W -= hv[j];
+                        ++f;
                     }
                 }
             }
-            // next tile's fragments (the last tile of a chunk re-reads itself)
-            const int tn = tt + 1 < tend ? tt + 1 : tt;
-            a0 = as_bf16x8(sb[tn * 128 + l]);
-            a1 = as_bf16x8(sb[tn * 128 + 64 + l]);
-            // buckets past a query's visible leaves never become candidates (only the last tiles hold such)
-            if (x0 + 16 > minNLv) {
-#pragma unroll
-                for (int cg = 0; cg < 2; ++cg)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        best[cg][v] = (qv[cg] && xb + v < NLv[cg]) ? best[cg][v] : kNegInf;
-            }
-            // a bucket scoring at or above its query's floor edge is a candidate (few once the floor has
-            // risen): a lane's 8 values are tested through their maximum first, and a lane holding any
-            // candidate walks its set bits one at a time (the wave runs as many rounds as its busiest lane)
-            const float lm0 = fmaxf(fmaxf(best[0][0], best[0][1]), fmaxf(best[0][2], best[0][3]));
-            const float lm1 = fmaxf(fmaxf(best[1][0], best[1][1]), fmaxf(best[1][2], best[1][3]));
-            if (lm0 >= fe[0] || lm1 >= fe[1]) {
-                uint32_t bits = 0;
-#pragma unroll
-                for (int cg = 0; cg < 2; ++cg)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) bits |= best[cg][v] >= fe[cg] ? 1u << (4 * cg + v) : 0u;
-                const int64_t lo = (int64_t)(x0 / kLeavesPerBlock) * kBlockTokens;
-                const uint4 m4 = sm[tt * 4 + h];
-                const bool el0 = lo >= lo_ok[0] && lo + kBlockTokens <= hi_ok[0];
-                const bool el1 = lo >= lo_ok[1] && lo + kBlockTokens <= hi_ok[1];
-                do {
-                    const int j = __builtin_ctz(bits);
-                    bits &= bits - 1u;
-                    const bool c1 = j >= 4;
-                    const int v = j & 3;
-                    const float s0 = c1 ? best[1][0] : best[0][0], s1 = c1 ? best[1][1] : best[0][1];
-                    const float s2 = c1 ? best[1][2] : best[0][2], s3 = c1 ? best[1][3] : best[0][3];
-                    const float sc = v == 0 ? s0 : (v == 1 ? s1 : (v == 2 ? s2 : s3));
-                    const uint32_t mv = v == 0 ? m4.x : (v == 1 ? m4.y : (v == 2 ? m4.z : m4.w));
-                    // this lane's sub-list h of the query's candidate list
-                    const int bs = c1 ? base[1] : base[0];
-                    uint64_t* sub = c1 ? sub1 : sub0;
-                    if (bs < kSubCap) sub[bs] = rank_key(sc, (uint32_t)(xb + v));
-                    base[0] += c1 ? 0 : 1;
-                    base[1] += c1 ? 1 : 0;
-                    if (c1 ? el1 : el0) atomicAdd((c1 ? hrow[1] : hrow[0]) + fscan_bin(sc), (uint32_t)kPool * (mv & 0xFFu));
-                } while (bits != 0u);
-            }
+            fbin[qw] = f;
+            wsum[qw] = W;
+            if (f >= 1 && q0 + l < sa.n_q) fedge[qw] = hedge(f);   // bin(s) >= f  <=>  s >= edge(f)
         }
-        if (c + 1 < nch) LSA_STORE_CHUNK((c + 1) & 1)
-        // raise the floors (the histogram rows are this wave's own)
         wave_sync();
-#pragma unroll
-        for (int cg = 0; cg < 2; ++cg) {
-            fb[cg] = max(fb[cg], fscan_cross_bin(hrow[cg], h, (uint32_t)sa.k));
-            if (qv[cg]) fe[cg] = fb[cg] >= 1 ? fscan_edge(fb[cg]) : -kFltMax;   // bin(s) >= fb  <=>  s >= fe
-        }
-        __syncthreads();
+        fe[0] = fedge[wid * 32 + n];
+        fe[1] = fedge[wid * 32 + 16 + n];
+        __syncthreads();   // the stage is rewritten next
     }
-#undef LSA_LOAD_CHUNK
-#undef LSA_STORE_CHUNK
-    wave_sync();
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg) {
-        const int bin = fscan_cross_bin(hrow[cg], h, (uint32_t)sa.k);
         if (qv[cg]) {
-            if (h == 0) tau[u[cg]] = bin >= 1 ? fscan_edge(bin) - 1.52587890625e-05f : kNegInf;
-            cnt[4 * u[cg] + h] = base[cg];
+            const int qw = wid * 32 + cg * 16 + n;
+            const int64_t u = ubase + (int64_t)(cg * 16 + n) * sa.H_kv;
+            const int c = lcnt[qw];
+            if (h == 0) {
+                const int f = fbin[qw];
+                const bool crossed = wsum[qw] >= (uint32_t)sa.k;   // f is the crossing bin
+                tau[u] = (crossed && f >= 1) ? hedge(f) - 1.52587890625e-05f : kNegInf;
+            }
+            cnt[4 * u + h] = h < 3 ? min(max(c - kSubCap * h, 0), kSubCap) : max(c - kSubCap * 3, 0);
         }
     }
 }
