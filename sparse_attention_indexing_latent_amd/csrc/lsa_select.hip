@@ -1403,6 +1403,20 @@ __device__ __forceinline__ QCodes query_codes(const uint16_t* qrow_h0, int G) {
     return r;
 }
 
+// Maximum over the 16 lanes of each row of the wave (in every lane of the row), by DPP moves: swaps
+// inside quads (xor 1, xor 2), then the mirrored half row and the mirrored row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+static_assert(kMaxGroup <= 8, "the decode scan folds heads 4..7 in with one exchange");
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1, 0, 3, 2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2, 3, 0, 1]
+    x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
+    return fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
+}
+
 // Largest of the 16 scores of a tile held as 4 values in each of the lanes 0, 16, 32, 48 (in every
 // lane on return).  Exact: the maximum does not depend on the order it is taken in.
 __device__ __forceinline__ float tile_max(const f32x4& v) {
@@ -1435,20 +1449,29 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
         // stage-1 scores from the int8 codes (query head n in column n); the tile maximum taken of the
         // upper bounds s~ + sc Qa + Qb
         const QCodes qc = query_codes(reinterpret_cast<const uint16_t*>(qhat) + qrow, sa.G);
-        const float sqn = n < sa.G ? qc.sq : -1.0f;   // a negative factor marks the columns past the group
+        // the MFMA takes the query heads as rows and the tile's buckets as columns (the operand layouts are
+        // alike), so lane (bucket c, h) holds heads 4h..4h+3 of bucket c: the max over heads is 3 maxima in
+        // the lane and 2 across its 4 lanes; sq of those heads, a negative factor past the group
+        float sqh[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float sj = __shfl(qc.sq, 4 * h + j);   // lane 4h + j holds head 4h + j's sq
+            sqh[j] = 4 * h + j < sa.G ? sj : -1.0f;
+        }
+        const float qa = qc.qa, qb = qc.qb;
         const uint4* cq = reinterpret_cast<const uint4*>(cv.cq + bg * cv.s_cq);
         const float* csc = cv.csc + bg * cv.s_csc;
         // batches of TPI tiles; the next batch's loads are in flight while one is scored
         // (loads are unconditional, past the last tile they repeat it, so they stay in flight together)
         constexpr int TPI = 4;
         uint4 a[2][TPI];
-        float4 scl[2][TPI];
+        float scl[2][TPI];
         auto issue = [&](int buf, int tb) {
 #pragma unroll
             for (int j = 0; j < TPI; ++j) {
                 const int64_t tt = min(tb + j, w1 - 1);
                 a[buf][j] = cq[tt * 64 + l];
-                scl[buf][j] = *reinterpret_cast<const float4*>(csc + tt * 16 + 4 * h);
+                scl[buf][j] = csc[tt * 16 + n];   // this lane's bucket
             }
         };
         issue(0, w0);
@@ -1463,22 +1486,17 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
                     if (tb + j < w1) {
                         const uint4 av = a[half][j];
                         i32x4 acc = {0, 0, 0, 0};
-                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{(int)av.x, (int)av.y, (int)av.z, (int)av.w},
-                                                                    qc.codes, acc, 0, 0, 0);
-                        const float scv[4] = {scl[half][j].x, scl[half][j].y, scl[half][j].z, scl[half][j].w};
-                        f32x4 vals, ub;
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qc.codes, i32x4{(int)av.x, (int)av.y, (int)av.z,
+                                                                                    (int)av.w}, acc, 0, 0, 0);
+                        float x = kNegInf;
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            float x = sqn >= 0.f ? (float)acc[v] * sqn : kNegInf;
-                            x = fmaxf(x, __shfl_xor(x, 1));
-                            x = fmaxf(x, __shfl_xor(x, 2));
-                            x = fmaxf(x, __shfl_xor(x, 4));
-                            x = fmaxf(x, __shfl_xor(x, 8));
-                            vals[v] = x * scv[v];
-                            ub[v] = vals[v] + (scv[v] * qc.qa + qc.qb);
-                        }
-                        if (n == 0) *reinterpret_cast<f32x4*>(sc + (int64_t)(tb + j) * 16 + 4 * h) = vals;
-                        const float m = tile_max(ub);   // every lane takes part in the shuffles
+                        for (int v = 0; v < 4; ++v) x = fmaxf(x, sqh[v] >= 0.f ? (float)acc[v] * sqh[v] : kNegInf);
+                        x = fmaxf(x, __shfl_xor(x, 16));   // heads 4..7 (a group has at most 8)
+                        const float sv = scl[half][j];
+                        const float val = x * sv;
+                        const float ub = val + (sv * qa + qb);
+                        if (h == 0) sc[(int64_t)(tb + j) * 16 + n] = val;
+                        const float m = row_max16(ub);   // tile maximum over the 16 buckets (rows 0 and 1)
                         if (l == 0) tmx[tb + j] = m;
                     }
                 }
