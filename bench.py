@@ -344,12 +344,12 @@ def run_prefill(args, cid, steps, warmup):
     if attend == "bucket":
         # the window part as in the gather accounting, with no long-range rows
         alg_bytes = selected_bytes(cfg, n_q, 0, G["q_pos"][0].cpu()) + ws["bm_bytes"]
-        kernel = "bucket-major attention call (pairs, scan, scatter, bm_leaf_kernel<128>, bm_local_kernel<128>)"
+        kernel = f"bucket-major attention call (pairs, scan, scatter, bm_leaf_kernel<{cfg.d}>, bm_local_kernel<{cfg.d}>)"
         traffic = traffic_for([os.path.join(csrc, "lsa_bucket.hip"), os.path.join(csrc, "lsa_attend.hip")],
                               f"attend_bucket_{cfg.name}")
     else:
         alg_bytes = selected_bytes(cfg, n_q, lr_total, G["q_pos"][0].cpu())
-        kernel = "attend_bf16_kernel<128>"
+        kernel = f"attend_bf16_kernel<{cfg.d}>" if cfg.dtype == "bf16" else "attend_f32_kernel"
         traffic = traffic_for(os.path.join(csrc, "lsa_attend.hip"), f"attend_{cfg.name}")
     achieved = alg_bytes / (att_ms / 1e3) / 1e9
     per_launch = alg_bytes / n_att
