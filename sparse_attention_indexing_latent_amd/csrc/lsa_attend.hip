@@ -51,15 +51,36 @@ __device__ __forceinline__ AUnit aunit_of(int64_t uu, const AttArgs& aa) {
 
 // Log-sum-exp merge of a unit's bucket partials of head hh (of its group)
 // into this lane's running state (lane (n, h) holds dims 32 (c/2) + 8h +
-// 4 (c%2) + [0, 4) of acc[c]); partials are read four at a time, a missing
-// one (past the unit's count) reads the first slot again with weight 0.
+// 4 (c%2) + [0, 4) of acc[c]), in two passes: the largest partial maximum M
+// first (the running state is rescaled to it once), then every partial's
+// values weighted by exp(m_j - M) times its scale, one fp16-source FMA per
+// value (v_fma_mix) with no rescaling of the accumulator per partial.
+// Partials are read four at a time, a missing one (past the unit's count)
+// reads the first slot again with weight 0.
 template <int D>
 __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t ul, int npl, int hh, int h,
                                                       float& m_run, float& l_run, f32x4* acc) {
     constexpr int NC = D / 16;
     constexpr int MW = D / 32;
     constexpr int MN = 4;   // partials in flight
+    constexpr int MX = 8;   // maxima in flight
     const int64_t s0 = aa.bm_off[ul];
+    float M = m_run;
+    for (int s = 0; s < npl; s += MX) {
+        float mx[MX];
+#pragma unroll
+        for (int j = 0; j < MX; ++j) {
+            const int64_t pp = s0 + (s + j < npl ? s + j : 0);
+            mx[j] = aa.bm_ml[(pp * aa.G + hh) * 4];
+        }
+#pragma unroll
+        for (int j = 0; j < MX; ++j) M = fmaxf(M, mx[j]);   // the repeated first slot changes nothing
+    }
+    const float a = m_run > kNegInf ? __expf(m_run - M) : 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] *= a;
+    l_run *= a;
+    m_run = M;
     for (int s = 0; s < npl; s += MN) {
         f32x4 ml[MN];
         u32x4 w[MN][MW];
@@ -74,23 +95,18 @@ __device__ __forceinline__ void merge_bucket_partials(const AttArgs& aa, int64_t
         }
 #pragma unroll
         for (int j = 0; j < MN; ++j) {
-            const float mj = s + j < npl ? ml[j][0] : kNegInf;
-            const float M = fmaxf(m_run, mj);
-            const float a = m_run > kNegInf ? __expf(m_run - M) : 0.f;
-            const float b = mj > kNegInf ? __expf(mj - M) : 0.f;
+            const float b = s + j < npl ? __expf(ml[j][0] - M) : 0.f;
             const float bs = b * ml[j][2];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 // acc[c] holds dims 32 (c/2) + 8h + 4 (c%2) + [0,4): words 2 (c%2), +1 of chunk c/2
                 const uint32_t w0 = w[j][c / 2][2 * (c % 2)], w1 = w[j][c / 2][2 * (c % 2) + 1];
-                const f32x4 oc = {(float)__builtin_bit_cast(_Float16, (uint16_t)(w0 & 0xFFFFu)),
-                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16)),
-                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 & 0xFFFFu)),
-                                  (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16))};
-                acc[c] = acc[c] * a + oc * bs;
+                acc[c][0] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(w0 & 0xFFFFu)), bs, acc[c][0]);
+                acc[c][1] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16)), bs, acc[c][1]);
+                acc[c][2] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(w1 & 0xFFFFu)), bs, acc[c][2]);
+                acc[c][3] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16)), bs, acc[c][3]);
             }
-            l_run = l_run * a + ml[j][1] * b;
-            m_run = M;
+            l_run = fmaf(ml[j][1], b, l_run);
         }
     }
 }
