@@ -1715,6 +1715,20 @@ __device__ __forceinline__ uint32_t fin_key_id(uint64_t k) { return kFinIdMax - 
 __device__ __forceinline__ int fin_key_slot(uint64_t k) { return (int)(k & 0x3FFu); }
 __device__ __forceinline__ float fin_key_score(uint64_t k) { return ord_key_inv((uint32_t)(k >> 32)); }
 
+// Exclusive prefix over the wave's lanes of c (0 <= c < 16), and the wave's total, by four ballots.
+__device__ __forceinline__ int wave_excl_count16(int c, int& tot) {
+    const uint64_t lt = (1ull << lane_id()) - 1ull;
+    int pre = 0;
+    tot = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint64_t m = __ballot((c >> b) & 1);
+        pre += __popcll(m & lt) << b;
+        tot += __popcll(m) << b;
+    }
+    return pre;
+}
+
 // Position of the j-th (from 0) set bit of x, which has more than j set bits.
 __device__ __forceinline__ int nth_set_bit(uint64_t x, int j) {
     int b = 0;
@@ -1823,483 +1837,543 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
                                 lr_idx, lr_cnt, m);
     };
     static_assert(kCandCap * 3 * 4 >= kExactSel && kCandCap >= 256, "the exact path's LDS fits the finish's arrays");
-    if ((int64_t)NT * 16 > (int64_t)kFinIdMax + 1) {
-        to_exact();
-        return;
-    }
-    const float* csc = filter ? cv.csc + bg * cv.s_csc : nullptr;
-    int sb0, sb1;
-    straddling_blocks(q, sb0, sb1);
-    clear_bins(hist);
-    if (tid == 0) need_stk = 0;
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kFinTmRegs; ++r)
-        if (tid + 256 * r < NT) atomicAdd(&hist[fin_bin(tmr[r])], 1u);
-    for (int x = tid + 256 * kFinTmRegs; x < NT; x += 256) atomicAdd(&hist[fin_bin(tm[x])], 1u);
-    __syncthreads();
-    uint32_t tb[16];   // this thread's bins of the tile-maximum histogram
-    const int tabove = load_bins(hist, tb, sh4);
-    // scores, metas and eligible tokens of buckets 4 c .. 4 c + 3 of tile x (0 tokens: not eligible)
-    // quarter tile c of tile x: the raw loads (scores, metas, scales), then the per-bucket values:
-    // scores, half-widths of their bounds (0 for exact scores), metas and eligible tokens
-    struct QuadRaw {
-        float4 sv;
-        uint4 mv;
-        float4 cs;
-    };
-    auto quad_load = [&](int x, int c) {
-        QuadRaw r;
-        r.sv = reinterpret_cast<const float4*>(sc + (int64_t)x * 16)[c];
-        r.mv = reinterpret_cast<const uint4*>(meta + (int64_t)x * 16)[c];
-        r.cs = filter ? reinterpret_cast<const float4*>(csc + (int64_t)x * 16)[c] : float4{0.f, 0.f, 0.f, 0.f};
-        return r;
-    };
-    auto quad_eval = [&](const QuadRaw& r, int x, int c, float (&s4)[4], float (&e4)[4], uint32_t (&m4)[4],
-                         int (&w4)[4]) {
-        s4[0] = r.sv.x;
-        s4[1] = r.sv.y;
-        s4[2] = r.sv.z;
-        s4[3] = r.sv.w;
-        e4[0] = filter ? r.cs.x * Qa + Qb : 0.f;
-        e4[1] = filter ? r.cs.y * Qa + Qb : 0.f;
-        e4[2] = filter ? r.cs.z * Qa + Qb : 0.f;
-        e4[3] = filter ? r.cs.w * Qa + Qb : 0.f;
-        m4[0] = r.mv.x;
-        m4[1] = r.mv.y;
-        m4[2] = r.mv.z;
-        m4[3] = r.mv.w;
-        const int blk = x / (kLeavesPerBlock / 16);   // a tile lies in one block
-        const int so = blk == sb0 ? 0 : (blk == sb1 ? kLeavesPerBlock : -1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t leaf = (uint32_t)(16 * x + 4 * c + i);
-            w4[i] = so >= 0 ? stk[so + leaf % kLeavesPerBlock] : leaf_weight_whole(leaf, m4[i], q);
+    // the bounded path; true: the unit needs the exact path instead (one copy of its code, below: the
+    // kernel runs once per CU, so its instruction fetch is part of its latency)
+    const bool exact = [&]() -> bool {
+        if ((int64_t)NT * 16 > (int64_t)kFinIdMax + 1) {
+            return true;
         }
-    };
-    auto quad_buckets = [&](int x, int c, float (&s4)[4], float (&e4)[4], uint32_t (&m4)[4], int (&w4)[4]) {
-        quad_eval(quad_load(x, c), x, c, s4, e4, m4, w4);
-    };
-    // bounded scores need more tiles: the lower bounds of the top buckets must clear the bin of the
-    // M-th tile maximum of the upper bounds
-    int M = min(NT, filter ? max(4 * kFinMinTiles, sa.k / 8) : max(kFinMinTiles, sa.k / 16));
-    int b1 = 0, nt = 0;
-    bool have_stk = false;
-    for (;;) {
-        if (tid == 0) {
-            bsel = 0;
-            ntl = 0;
-            nc = 0;
-            wsum = 0;
-        }
-        clear_bins(hist);   // the tile histogram is in tb[]
+        const float* csc = filter ? cv.csc + bg * cv.s_csc : nullptr;
+        int sb0, sb1;
+        straddling_blocks(q, sb0, sb1);
+        // the entry -> bucket map of the straddling blocks (threads 0..127: sb0, 128..255: sb1; 4 entries
+        // each), loaded now and turned into eligible tokens per bucket when a listed tile needs them
+        const int eblk = tid < 128 ? sb0 : sb1;
+        const bool ehave = eblk >= 0 && eblk < q.nvis;
+        const uint32_t ecodes =
+            ehave ? reinterpret_cast<const uint32_t*>(cv.eleaf + bg * cv.s_eleaf + (int64_t)eblk * kBlockEntries)[tid & 127]
+                  : 0u;
+        clear_bins(hist);
+        if (tid == 0) need_stk = 0;
         __syncthreads();
-        crossing_bin(tb, tabove, M, &bsel);
+    #pragma unroll
+        for (int r = 0; r < kFinTmRegs; ++r)
+            if (tid + 256 * r < NT) atomicAdd(&hist[fin_bin(tmr[r])], 1u);
+        for (int x = tid + 256 * kFinTmRegs; x < NT; x += 256) atomicAdd(&hist[fin_bin(tm[x])], 1u);
         __syncthreads();
-        const int b0 = M < NT ? bsel : 0;   // M = NT: every bucket of every tile
-        auto list = [&](int x, float v) {
-            const bool qual = x < NT && fin_bin(v) >= b0;
-            const uint64_t bal = __ballot(qual);
-            int base = 0;
-            if (l == 0 && bal) base = atomicAdd(&ntl, __popcll(bal));
-            base = __shfl(base, 0);
-            const int pos = base + __popcll(bal & lt);
-            if (qual && pos < kFinTiles) tiles[pos] = x;
-            const int blk = x / (kLeavesPerBlock / 16);
-            if (qual && (blk == sb0 || blk == sb1)) need_stk = 1;
+        uint32_t tb[16];   // this thread's bins of the tile-maximum histogram
+        const int tabove = load_bins(hist, tb, sh4);
+        // scores, metas and eligible tokens of buckets 4 c .. 4 c + 3 of tile x (0 tokens: not eligible)
+        // quarter tile c of tile x: the raw loads (scores, metas, scales), then the per-bucket values:
+        // scores, half-widths of their bounds (0 for exact scores), metas and eligible tokens
+        struct QuadRaw {
+            float4 sv;
+            uint4 mv;
+            float4 cs;
         };
-#pragma unroll
-        for (int r = 0; r < kFinTmRegs; ++r) list(tid + 256 * r, tmr[r]);
-        for (int x0 = 256 * kFinTmRegs; x0 < NT; x0 += 256) list(x0 + tid, x0 + tid < NT ? tm[x0 + tid] : 0.f);
-        __syncthreads();
-        nt = ntl;
-        if (nt > kFinTiles) break;   // the exact path (b1 = 0 marks it)
-        if (need_stk && !have_stk) {   // a listed tile lies in a block straddling an edge
-            if (tid < 2 * kLeavesPerBlock) {
-                const int blk = tid < kLeavesPerBlock ? sb0 : sb1;
-                const int64_t x = (int64_t)blk * kLeavesPerBlock + tid % kLeavesPerBlock;
-                stk[tid] = (blk >= 0 && x < 16 * (int64_t)NT) ? leaf_weight(cv, bg, (uint32_t)x, q) : 0;
+        auto quad_load = [&](int x, int c) {
+            QuadRaw r;
+            r.sv = reinterpret_cast<const float4*>(sc + (int64_t)x * 16)[c];
+            r.mv = reinterpret_cast<const uint4*>(meta + (int64_t)x * 16)[c];
+            r.cs = filter ? reinterpret_cast<const float4*>(csc + (int64_t)x * 16)[c] : float4{0.f, 0.f, 0.f, 0.f};
+            return r;
+        };
+        auto quad_eval = [&](const QuadRaw& r, int x, int c, float (&s4)[4], float (&e4)[4], uint32_t (&m4)[4],
+                             int (&w4)[4]) {
+            s4[0] = r.sv.x;
+            s4[1] = r.sv.y;
+            s4[2] = r.sv.z;
+            s4[3] = r.sv.w;
+            e4[0] = filter ? r.cs.x * Qa + Qb : 0.f;
+            e4[1] = filter ? r.cs.y * Qa + Qb : 0.f;
+            e4[2] = filter ? r.cs.z * Qa + Qb : 0.f;
+            e4[3] = filter ? r.cs.w * Qa + Qb : 0.f;
+            m4[0] = r.mv.x;
+            m4[1] = r.mv.y;
+            m4[2] = r.mv.z;
+            m4[3] = r.mv.w;
+            const int blk = x / (kLeavesPerBlock / 16);   // a tile lies in one block
+            const int so = blk == sb0 ? 0 : (blk == sb1 ? kLeavesPerBlock : -1);
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t leaf = (uint32_t)(16 * x + 4 * c + i);
+                w4[i] = so >= 0 ? stk[so + leaf % kLeavesPerBlock] : leaf_weight_whole(leaf, m4[i], q);
             }
-            have_stk = true;
+        };
+        auto quad_buckets = [&](int x, int c, float (&s4)[4], float (&e4)[4], uint32_t (&m4)[4], int (&w4)[4]) {
+            quad_eval(quad_load(x, c), x, c, s4, e4, m4, w4);
+        };
+        // bounded scores need more tiles: the lower bounds of the top buckets must clear the bin of the
+        // M-th tile maximum of the upper bounds
+        int M = min(NT, filter ? max(4 * kFinMinTiles, sa.k / 8) : max(kFinMinTiles, sa.k / 16));
+        int b1 = 0, nt = 0;
+        bool have_stk = false;
+        for (;;) {
+            if (tid == 0) {
+                bsel = 0;
+                ntl = 0;
+                nc = 0;
+                wsum = 0;
+            }
+            clear_bins(hist);   // the tile histogram is in tb[]
             __syncthreads();
-        }
-        // The weighted histogram of the lower bounds s~ - e (bins >= b0) and C: the buckets of the listed
-        // tiles whose upper bound s~ + e has a bin >= b0 (e = 0 for exact scores; a quarter tile per thread)
-        int wl = 0;
-        constexpr int QPT = 4;   // quarter tiles per thread whose loads are in flight together
-        for (int i0 = 0; i0 < 4 * nt; i0 += 256 * QPT) {
-            QuadRaw raw[QPT];   // every load first, then the evaluation
-            int xq[QPT];
-#pragma unroll
-            for (int qq = 0; qq < QPT; ++qq) {
-                const int idx = min(i0 + 256 * qq + tid, 4 * nt - 1);
-                xq[qq] = tiles[idx >> 2];
-                raw[qq] = quad_load(xq[qq], idx & 3);
-            }
-#pragma unroll
-            for (int qq = 0; qq < QPT; ++qq) {
-                const int idx = i0 + 256 * qq + tid;
-                if (idx >= 4 * nt) break;
-                const int x = xq[qq], c4 = idx & 3;
-                float s4[QPT][4], e4[QPT][4];
-                uint32_t m4[QPT][4];
-                int w4[QPT][4];
-                quad_eval(raw[qq], x, c4, s4[qq], e4[qq], m4[qq], w4[qq]);
-                bool inc[4];
-                int c = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int bin = fin_bin(s4[qq][i] - e4[qq][i]);
-                    if (w4[qq][i] > 0 && bin >= b0) {
-                        atomicAdd(&hist[bin], (uint32_t)w4[qq][i]);
-                        wl += w4[qq][i];
+            crossing_bin(tb, tabove, M, &bsel);
+            __syncthreads();
+            const int b0 = M < NT ? bsel : 0;   // M = NT: every bucket of every tile
+            auto list = [&](int x, float v) {
+                const bool qual = x < NT && fin_bin(v) >= b0;
+                const uint64_t bal = __ballot(qual);
+                int base = 0;
+                if (l == 0 && bal) base = atomicAdd(&ntl, __popcll(bal));
+                base = __shfl(base, 0);
+                const int pos = base + __popcll(bal & lt);
+                if (qual && pos < kFinTiles) tiles[pos] = x;
+                const int blk = x / (kLeavesPerBlock / 16);
+                if (qual && (blk == sb0 || blk == sb1)) need_stk = 1;
+            };
+            {   // the tiles held in registers: one slot reservation per wave
+                uint32_t qm = 0;
+                bool stk_hit = false;
+    #pragma unroll
+                for (int r = 0; r < kFinTmRegs; ++r) {
+                    const int x = tid + 256 * r;
+                    if (x < NT && fin_bin(tmr[r]) >= b0) {
+                        qm |= 1u << r;
+                        const int blk = x / (kLeavesPerBlock / 16);
+                        stk_hit = stk_hit || blk == sb0 || blk == sb1;
                     }
-                    inc[i] = w4[qq][i] > 0 && fin_bin(s4[qq][i] + e4[qq][i]) >= b0;
-                    c += inc[i] ? 1 : 0;
                 }
-                int pos = c > 0 ? atomicAdd(&nc, c) : 0;
-#pragma unroll
+                const int c = __popc(qm);
+                int tot;
+                const int pre = wave_excl_count16(c, tot);
+                int base = 0;
+                if (l == 0 && tot) base = atomicAdd(&ntl, tot);
+                int pos = __shfl(base, 0) + pre;
+    #pragma unroll
+                for (int r = 0; r < kFinTmRegs; ++r) {
+                    if ((qm >> r) & 1u) {
+                        if (pos < kFinTiles) tiles[pos] = tid + 256 * r;
+                        ++pos;
+                    }
+                }
+                if (stk_hit) need_stk = 1;
+            }
+            for (int x0 = 256 * kFinTmRegs; x0 < NT; x0 += 256) list(x0 + tid, x0 + tid < NT ? tm[x0 + tid] : 0.f);
+            __syncthreads();
+            nt = ntl;
+            if (nt > kFinTiles) break;   // the exact path (b1 = 0 marks it)
+            if (need_stk && !have_stk) {   // a listed tile lies in a block straddling an edge
+                // eligible tokens of each bucket of the block: the sum over its entries (entry e holds
+                // tokens [4 e, 4 e + 4) of the block) of their tokens inside [sink_end, l0)
+                if (tid < 2 * kLeavesPerBlock) stk[tid] = 0;
+                __syncthreads();
+                if (ehave) {
+                    const int so = tid < 128 ? 0 : kLeavesPerBlock;
+                    const int64_t tb = (int64_t)eblk * kBlockTokens + (int64_t)kPool * 4 * (tid & 127);
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t lf = (ecodes >> (8 * i)) & 0xFFu;
+                        int w = 0;
+    #pragma unroll
+                        for (int jj = 0; jj < kPool; ++jj) {
+                            const int64_t tk = tb + kPool * i + jj;
+                            w += (tk >= q.sink_end && tk < q.l0) ? 1 : 0;
+                        }
+                        if (w > 0 && lf < (uint32_t)kLeavesPerBlock) atomicAdd(&stk[so + lf], w);
+                    }
+                }
+                have_stk = true;
+                __syncthreads();
+            }
+            // The weighted histogram of the lower bounds s~ - e (bins >= b0) and C: the buckets of the listed
+            // tiles whose upper bound s~ + e has a bin >= b0 (e = 0 for exact scores; a quarter tile per thread)
+            int wl = 0;
+            constexpr int QPT = 6;   // quarter tiles per thread whose loads are in flight together (384 tiles)
+            for (int i0 = 0; i0 < 4 * nt; i0 += 256 * QPT) {
+                QuadRaw raw[QPT];   // every load first, then the evaluation
+                int xq[QPT];
+    #pragma unroll
+                for (int qq = 0; qq < QPT; ++qq) {
+                    const int idx = min(i0 + 256 * qq + tid, 4 * nt - 1);
+                    xq[qq] = tiles[idx >> 2];
+                    if (i0 + 256 * qq < 4 * nt) raw[qq] = quad_load(xq[qq], idx & 3);   // uniform
+                }
+    #pragma unroll
+                for (int qq = 0; qq < QPT; ++qq) {
+                    if (i0 + 256 * qq >= 4 * nt) break;   // uniform: the wave goes on while any lane has a quarter
+                    const int idx = i0 + 256 * qq + tid;
+                    const bool valid = idx < 4 * nt;
+                    const int x = xq[qq], c4 = idx & 3;
+                    float s4[QPT][4], e4[QPT][4];
+                    uint32_t m4[QPT][4];
+                    int w4[QPT][4];
+                    quad_eval(raw[qq], x, c4, s4[qq], e4[qq], m4[qq], w4[qq]);
+                    if (!valid) {
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) w4[qq][i] = 0;
+                    }
+                    bool inc[4];
+                    int c = 0;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int bin = fin_bin(s4[qq][i] - e4[qq][i]);
+                        if (w4[qq][i] > 0 && bin >= b0) {
+                            atomicAdd(&hist[bin], (uint32_t)w4[qq][i]);
+                            wl += w4[qq][i];
+                        }
+                        inc[i] = w4[qq][i] > 0 && fin_bin(s4[qq][i] + e4[qq][i]) >= b0;
+                        c += inc[i] ? 1 : 0;
+                    }
+                    int tot;
+                    const int pre = wave_excl_count16(c, tot);   // one slot reservation per wave
+                    int base = 0;
+                    if (l == 0 && tot) base = atomicAdd(&nc, tot);
+                    int pos = __shfl(base, 0) + pre;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (inc[i]) {
+                            if (pos < kFinC) {
+                                ckey[pos] = fin_key(s4[qq][i] + e4[qq][i], (uint32_t)(16 * x + 4 * c4 + i), pos);
+                                cmeta[pos] = m4[qq][i];
+                                cw[pos] = w4[qq][i];
+                            }
+                            ++pos;
+                        }
+                    }
+                }
+            }
+    #pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) wl += __shfl_xor(wl, o);
+            if (l == 0 && wl) atomicAdd(&wsum, wl);
+            __syncthreads();
+            if (wsum >= sa.k) {
+                uint32_t wb[16];
+                const int wabove = load_bins(hist, wb, sh4);
+                if (tid == 0) bsel = -1;
+                __syncthreads();
+                crossing_bin(wb, wabove, sa.k, &bsel);
+                __syncthreads();
+                b1 = bsel;   // >= b0: the buckets below b0 were not counted
+                break;
+            }
+            if (M >= NT) break;   // cannot happen: the visible buckets hold more than k eligible tokens (b1 = 0)
+            M = min(NT, 4 * M);
+            __syncthreads();   // every thread has read wsum before it is reset
+        }
+        if (b1 <= 0) {   // b1 = 0 would take every bucket: leave the unit to the exact path
+            return true;
+        }
+        // b1: the bin where the lower bounds' tokens reach k, so at least k tokens score >= its edge and
+        // every bucket scoring that high has its upper bound in a bin >= b1.  Exact scores (e = 0): S = the
+        // buckets of C with a bin >= b1.  Bounded scores: C' = the buckets of C whose upper bound has a
+        // bin >= b1, their bf16 scores computed here (the same MFMA as the exact scan), and S = those of C'
+        // at or above the bin b where their tokens reach k.
+        if (tid == 0) {
+            nk = 0;
+            fin[0] = 0;
+            fin[2] = -1;
+        }
+        __syncthreads();
+        const int ncc = nc;
+        if (filter && ncc > kFinC) {
+            return true;
+        }
+        if (filter) {
+            if (tid == 0) ntl = 0;
+            clear_bins(hist);
+            __syncthreads();
+            for (int j0 = 0; j0 < ncc; j0 += 256) {   // C'
+                const int j = j0 + tid;
+                const bool in = j < ncc && fin_bin(fin_key_score(ckey[j])) >= b1;
+                const uint64_t bal = __ballot(in);
+                int base = 0;
+                if (l == 0 && bal) base = atomicAdd(&ntl, __popcll(bal));
+                base = __shfl(base, 0);
+                if (in) cp[base + __popcll(bal & lt)] = j;
+            }
+            __syncthreads();
+            const int ncp = ntl;
+            {   // bf16 scores of C': groups of 16 candidates (MFMA rows), kGrp consecutive groups per wave with
+                // their loads in flight together (128 candidates per round)
+                constexpr int kGrp = 2;
+                const int n = l & 15, h = l >> 4;
+                uint4 qa4 = {0, 0, 0, 0}, qc4 = {0, 0, 0, 0};
+                if (n < sa.G) {
+                    const uint4* pq = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(qhat) + qrow +
+                                                                     n * kLatent + 16 * h);
+                    qa4 = pq[0];
+                    qc4 = pq[1];
+                }
+                const bf16x8 q0 = as_bf16x8(qa4), q1 = as_bf16x8(qc4);
+                const uint4* cw4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
+                for (int g0 = 16 * kGrp * wid; g0 < ncp; g0 += 64 * kGrp) {
+                    uint4 a[kGrp][2];
+    #pragma unroll
+                    for (int gg = 0; gg < kGrp; ++gg) {
+                        if (g0 + 16 * gg < ncp) {   // uniform
+                            const int e = min(g0 + 16 * gg + n, ncp - 1);
+                            const uint32_t leaf = fin_key_id(ckey[cp[e]]);
+                            a[gg][0] = cw4[cent_tile_word(leaf, h, 0)];
+                            a[gg][1] = cw4[cent_tile_word(leaf, h, 1)];
+                        }
+                    }
+    #pragma unroll
+                    for (int gg = 0; gg < kGrp; ++gg) {
+                        if (g0 + 16 * gg >= ncp) break;   // uniform
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[gg][0]), q0, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[gg][1]), q1, acc, 0, 0, 0);
+    #pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            float x = n < sa.G ? acc[v] : kNegInf;
+                            x = fmaxf(x, __shfl_xor(x, 1));
+                            x = fmaxf(x, __shfl_xor(x, 2));
+                            x = fmaxf(x, __shfl_xor(x, 4));
+                            x = fmaxf(x, __shfl_xor(x, 8));
+                            const int idx = g0 + 16 * gg + 4 * h + v;
+                            if (n == 0 && idx < ncp) cex[idx] = x;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            for (int j = tid; j < ncp; j += 256) atomicAdd(&hist[fin_bin(cex[j])], (uint32_t)cw[cp[j]]);
+            __syncthreads();
+            uint32_t eb[16];
+            const int eabove = load_bins(hist, eb, sh4);
+            if (tid == 0) bsel = -1;
+            __syncthreads();
+            crossing_bin(eb, eabove, sa.k, &bsel);
+            __syncthreads();
+            const int be = bsel;   // >= b1: C' holds every bucket scoring >= the edge of b1
+            for (int j0 = 0; j0 < ncp; j0 += 256) {   // S
+                const int j = j0 + tid;
+                const bool in = j < ncp && be >= 0 && fin_bin(cex[j]) >= be;
+                const uint64_t bal = __ballot(in);
+                int base = 0;
+                if (l == 0 && bal) base = atomicAdd(&nk, __popcll(bal));
+                base = __shfl(base, 0);
+                const int pos = base + __popcll(bal & lt);
+                if (in && pos < kCandCap) keys[pos] = fin_key(cex[j], fin_key_id(ckey[cp[j]]), cp[j]);
+            }
+        } else if (ncc <= kFinC) {
+            for (int j0 = 0; j0 < ncc; j0 += 256) {
+                const int j = j0 + tid;
+                const uint64_t kc = j < ncc ? ckey[j] : 0ull;
+                const bool in = j < ncc && fin_bin(fin_key_score(kc)) >= b1;
+                const uint64_t bal = __ballot(in);
+                int base = 0;
+                if (l == 0 && bal) base = atomicAdd(&nk, __popcll(bal));
+                base = __shfl(base, 0);
+                const int pos = base + __popcll(bal & lt);
+                if (in && pos < kCandCap) keys[pos] = kc;
+            }
+        } else {   // C overflowed: S from the listed tiles again, its own entries in the C arrays
+            for (int idx = tid; idx < 4 * nt; idx += 256) {
+                const int x = tiles[idx >> 2], c4 = idx & 3;
+                float s4[4], e4[4];
+                uint32_t m4[4];
+                int w4[4];
+                quad_buckets(x, c4, s4, e4, m4, w4);
+                bool in[4];
+                int c = 0;
+    #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (inc[i]) {
-                        if (pos < kFinC) {
-                            ckey[pos] = fin_key(s4[qq][i] + e4[qq][i], (uint32_t)(16 * x + 4 * c4 + i), pos);
-                            cmeta[pos] = m4[qq][i];
-                            cw[pos] = w4[qq][i];
+                    in[i] = w4[i] > 0 && fin_bin(s4[i]) >= b1;
+                    c += in[i] ? 1 : 0;
+                }
+                int pos = c > 0 ? atomicAdd(&nk, c) : 0;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (in[i]) {
+                        if (pos < kCandCap) {
+                            keys[pos] = fin_key(s4[i], (uint32_t)(16 * x + 4 * c4 + i), pos);
+                            cmeta[pos] = m4[i];
+                            cw[pos] = w4[i];
                         }
                         ++pos;
                     }
                 }
             }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) wl += __shfl_xor(wl, o);
-        if (l == 0 && wl) atomicAdd(&wsum, wl);
         __syncthreads();
-        if (wsum >= sa.k) {
-            uint32_t wb[16];
-            const int wabove = load_bins(hist, wb, sh4);
-            if (tid == 0) bsel = -1;
-            __syncthreads();
-            crossing_bin(wb, wabove, sa.k, &bsel);
-            __syncthreads();
-            b1 = bsel;   // >= b0: the buckets below b0 were not counted
-            break;
+        const int f = nk;
+        if (f > kCandCap) {
+            return true;
         }
-        if (M >= NT) break;   // cannot happen: the visible buckets hold more than k eligible tokens (b1 = 0)
-        M = min(NT, 4 * M);
-        __syncthreads();   // every thread has read wsum before it is reset
-    }
-    if (b1 <= 0) {   // b1 = 0 would take every bucket: leave the unit to the exact path
-        to_exact();
-        return;
-    }
-    // b1: the bin where the lower bounds' tokens reach k, so at least k tokens score >= its edge and
-    // every bucket scoring that high has its upper bound in a bin >= b1.  Exact scores (e = 0): S = the
-    // buckets of C with a bin >= b1.  Bounded scores: C' = the buckets of C whose upper bound has a
-    // bin >= b1, their bf16 scores computed here (the same MFMA as the exact scan), and S = those of C'
-    // at or above the bin b where their tokens reach k.
-    if (tid == 0) {
-        nk = 0;
-        fin[0] = 0;
-        fin[2] = -1;
-    }
-    __syncthreads();
-    const int ncc = nc;
-    if (filter && ncc > kFinC) {
-        to_exact();
-        return;
-    }
-    if (filter) {
-        if (tid == 0) ntl = 0;
-        clear_bins(hist);
-        __syncthreads();
-        for (int j0 = 0; j0 < ncc; j0 += 256) {   // C'
-            const int j = j0 + tid;
-            const bool in = j < ncc && fin_bin(fin_key_score(ckey[j])) >= b1;
-            const uint64_t bal = __ballot(in);
-            int base = 0;
-            if (l == 0 && bal) base = atomicAdd(&ntl, __popcll(bal));
-            base = __shfl(base, 0);
-            if (in) cp[base + __popcll(bal & lt)] = j;
-        }
-        __syncthreads();
-        const int ncp = ntl;
-        {   // bf16 scores of C': groups of 16 candidates (MFMA rows), two groups per wave in flight
-            const int n = l & 15, h = l >> 4;
-            uint4 qa4 = {0, 0, 0, 0}, qc4 = {0, 0, 0, 0};
-            if (n < sa.G) {
-                const uint4* pq = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(qhat) + qrow +
-                                                                 n * kLatent + 16 * h);
-                qa4 = pq[0];
-                qc4 = pq[1];
-            }
-            const bf16x8 q0 = as_bf16x8(qa4), q1 = as_bf16x8(qc4);
-            const uint4* cw4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent);
-            for (int g0 = 32 * wid; g0 < ncp; g0 += 128) {
-                uint4 a[2][2];
-#pragma unroll
-                for (int gg = 0; gg < 2; ++gg) {
-                    const int e = min(g0 + 16 * gg + n, ncp - 1);
-                    const uint32_t leaf = fin_key_id(ckey[cp[e]]);
-                    a[gg][0] = cw4[cent_tile_word(leaf, h, 0)];
-                    a[gg][1] = cw4[cent_tile_word(leaf, h, 1)];
-                }
-#pragma unroll
-                for (int gg = 0; gg < 2; ++gg) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[gg][0]), q0, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[gg][1]), q1, acc, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float x = n < sa.G ? acc[v] : kNegInf;
-                        x = fmaxf(x, __shfl_xor(x, 1));
-                        x = fmaxf(x, __shfl_xor(x, 2));
-                        x = fmaxf(x, __shfl_xor(x, 4));
-                        x = fmaxf(x, __shfl_xor(x, 8));
-                        const int idx = g0 + 16 * gg + 4 * h + v;
-                        if (n == 0 && idx < ncp) cex[idx] = x;
-                    }
-                }
+        // the member lists of S: 24 entries from off & ~7 per candidate, in flight during the ranking
+        uint4 pmv[2][3];
+    #pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int j = tid + 256 * h2;
+            pmv[h2][0] = pmv[h2][1] = pmv[h2][2] = uint4{0u, 0u, 0u, 0u};
+            if (j < f) {
+                const uint64_t kj = keys[j];
+                const uint32_t m = cmeta[fin_key_slot(kj)];
+                const int a = (int)((m >> 8) & 0x3F8u);
+                const uint4* p = reinterpret_cast<const uint4*>(mem_bg + (int64_t)(fin_key_id(kj) / kLeavesPerBlock) *
+                                                                             kBlockEntries + a);
+                pmv[h2][0] = p[0];
+                if (a + 8 < kBlockEntries) pmv[h2][1] = p[1];
+                if (a + 16 < kBlockEntries) pmv[h2][2] = p[2];
             }
         }
-        __syncthreads();
-        for (int j = tid; j < ncp; j += 256) atomicAdd(&hist[fin_bin(cex[j])], (uint32_t)cw[cp[j]]);
-        __syncthreads();
-        uint32_t eb[16];
-        const int eabove = load_bins(hist, eb, sh4);
-        if (tid == 0) bsel = -1;
-        __syncthreads();
-        crossing_bin(eb, eabove, sa.k, &bsel);
-        __syncthreads();
-        const int be = bsel;   // >= b1: C' holds every bucket scoring >= the edge of b1
-        for (int j0 = 0; j0 < ncp; j0 += 256) {   // S
-            const int j = j0 + tid;
-            const bool in = j < ncp && be >= 0 && fin_bin(cex[j]) >= be;
-            const uint64_t bal = __ballot(in);
-            int base = 0;
-            if (l == 0 && bal) base = atomicAdd(&nk, __popcll(bal));
-            base = __shfl(base, 0);
-            const int pos = base + __popcll(bal & lt);
-            if (in && pos < kCandCap) keys[pos] = fin_key(cex[j], fin_key_id(ckey[cp[j]]), cp[j]);
-        }
-    } else if (ncc <= kFinC) {
-        for (int j0 = 0; j0 < ncc; j0 += 256) {
-            const int j = j0 + tid;
-            const uint64_t kc = j < ncc ? ckey[j] : 0ull;
-            const bool in = j < ncc && fin_bin(fin_key_score(kc)) >= b1;
-            const uint64_t bal = __ballot(in);
-            int base = 0;
-            if (l == 0 && bal) base = atomicAdd(&nk, __popcll(bal));
-            base = __shfl(base, 0);
-            const int pos = base + __popcll(bal & lt);
-            if (in && pos < kCandCap) keys[pos] = kc;
-        }
-    } else {   // C overflowed: S from the listed tiles again, its own entries in the C arrays
-        for (int idx = tid; idx < 4 * nt; idx += 256) {
-            const int x = tiles[idx >> 2], c4 = idx & 3;
-            float s4[4], e4[4];
-            uint32_t m4[4];
-            int w4[4];
-            quad_buckets(x, c4, s4, e4, m4, w4);
-            bool in[4];
-            int c = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                in[i] = w4[i] > 0 && fin_bin(s4[i]) >= b1;
-                c += in[i] ? 1 : 0;
-            }
-            int pos = c > 0 ? atomicAdd(&nk, c) : 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (in[i]) {
-                    if (pos < kCandCap) {
-                        keys[pos] = fin_key(s4[i], (uint32_t)(16 * x + 4 * c4 + i), pos);
-                        cmeta[pos] = m4[i];
-                        cw[pos] = w4[i];
-                    }
-                    ++pos;
-                }
-            }
-        }
-    }
-    __syncthreads();
-    const int f = nk;
-    if (f > kCandCap) {
-        to_exact();
-        return;
-    }
-    // the member lists of S: 24 entries from off & ~7 per candidate, in flight during the ranking
-    uint4 pmv[2][3];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        const int j = tid + 256 * h2;
-        pmv[h2][0] = pmv[h2][1] = pmv[h2][2] = uint4{0u, 0u, 0u, 0u};
-        if (j < f) {
+        // rank of each candidate: the number of candidates above it (keys are distinct)
+        for (int j = tid; j < f; j += 256) {
             const uint64_t kj = keys[j];
-            const uint32_t m = cmeta[fin_key_slot(kj)];
-            const int a = (int)((m >> 8) & 0x3F8u);
-            const uint4* p = reinterpret_cast<const uint4*>(mem_bg + (int64_t)(fin_key_id(kj) / kLeavesPerBlock) *
-                                                                         kBlockEntries + a);
-            pmv[h2][0] = p[0];
-            if (a + 8 < kBlockEntries) pmv[h2][1] = p[1];
-            if (a + 16 < kBlockEntries) pmv[h2][2] = p[2];
+            int r = 0;
+            for (int i = 0; i < f; ++i) r += keys[i] > kj ? 1 : 0;
+            rk[r] = j;
         }
-    }
-    // rank of each candidate: the number of candidates above it (keys are distinct)
-    for (int j = tid; j < f; j += 256) {
-        const uint64_t kj = keys[j];
-        int r = 0;
-        for (int i = 0; i < f; ++i) r += keys[i] > kj ? 1 : 0;
-        rk[r] = j;
-    }
-    __syncthreads();
-    // the walk: thread tid holds ranks 2 tid and 2 tid + 1; the rank where the tokens reach k
-    {
-        const int j0 = 2 * tid, j1 = j0 + 1;
-        const int w0 = j0 < f ? cw[fin_key_slot(keys[rk[j0]])] : 0;
-        const int w1 = j1 < f ? cw[fin_key_slot(keys[rk[j1]])] : 0;
-        int tot;
-        const int ex = wg_excl_scan(w0 + w1, sh4, tot);
-        if (w0 > 0 && ex < sa.k && sa.k <= ex + w0) {
-            fin[0] = j0 + 1;
-            fin[1] = sa.k - ex;
-        }
-        if (w1 > 0 && ex + w0 < sa.k && sa.k <= ex + w0 + w1) {
-            fin[0] = j1 + 1;
-            fin[1] = sa.k - ex - w0;
-        }
-    }
-    __syncthreads();
-    const int ntake = fin[0], last = fin[1];
-    if (ntake == 0 || ntake > kSelCap) {   // more buckets than one record row holds
-        to_exact();
-        return;
-    }
-    if (tid < ntake) tleaf[tid] = fin_key_id(keys[rk[tid]]);
-    __syncthreads();
-    // the taken buckets in id order (ids are distinct: a bucket's place is the count of smaller ids)
-    if (tid < ntake) {
-        const int j = rk[tid];
-        const uint32_t leaf = tleaf[tid];
-        int r = 0;
-        for (int i = 0; i < ntake; ++i) r += tleaf[i] < leaf ? 1 : 0;
-        const int slot = fin_key_slot(keys[j]);
-        const int w = cw[slot], take = tid == ntake - 1 ? last : w;
-        sleaf[r] = leaf;
-        smeta[r] = cmeta[slot];
-        stake[r] = take;
-        sw[r] = w;
-        spos[r] = j;
-        rmask[r] = 0ull;
-    }
-    __syncthreads();
-    // block slots in block order
-    {
-        int first = 0, blk = 0;
-        if (tid < ntake) {
-            blk = (int)(sleaf[tid] / kLeavesPerBlock);
-            first = (tid == 0 || (int)(sleaf[tid - 1] / kLeavesPerBlock) != blk) ? 1 : 0;
-            if (stake[tid] < sw[tid]) fin[2] = tid;   // the partially taken bucket
-        }
-        int ns;
-        const int ex = wg_excl_scan(first, sh4, ns);
-        if (tid < ntake) {
-            sslot[tid] = ex + first - 1;
-            if (first && ex < kFinSlots) slot_blk[ex] = blk;
-        }
-        if (tid == 0) fin[1] = ns;
-    }
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        const int j = tid + 256 * h2;
-        if (j < f) {
-            cmem[3 * j] = pmv[h2][0];
-            cmem[3 * j + 1] = pmv[h2][1];
-            cmem[3 * j + 2] = pmv[h2][2];
-        }
-    }
-    __syncthreads();
-    const int ns = fin[1], rp = fin[2];
-    if (ns > kFinSlots) {
-        to_exact();
-        return;
-    }
-    for (int w = tid; w < ns * 32; w += 256) mask[w] = 0ull;
-    __syncthreads();
-    const uint16_t* cm16 = reinterpret_cast<const uint16_t*>(cmem);
-    // entry e of taken bucket r (in id order) by thread (16 r + e) mod 256
-    for (int idx = tid; idx < ntake * 16; idx += 256) {
-        const int r = idx >> 4, e = idx & 15;
-        const uint32_t m = smeta[r];
-        if (r == rp || e >= (int)(m & 0xFFu)) continue;
-        const int mbr = cm16[24 * spos[r] + ((m >> 8) & 7u) + e];
-        const int tb0 = kPool * mbr;   // token offset in the block
-        const int64_t t0 = (int64_t)(sleaf[r] / kLeavesPerBlock) * kBlockTokens + tb0;
-        uint32_t bits = 0;
-#pragma unroll
-        for (int jj = 0; jj < kPool; ++jj) bits |= (t0 + jj >= q.sink_end && t0 + jj < q.l0) ? 1u << jj : 0u;
-        if (bits) {
-            atomicOr(&mask[sslot[r] * 32 + tb0 / 64], (uint64_t)bits << (tb0 % 64));
-            atomicOr(&rmask[r], (uint64_t)bits << (kPool * e));
-        }
-    }
-    if (wid == 0 && rp >= 0) {   // the partial bucket: its lowest `take` eligible keys (key l = lane l)
-        const uint32_t m = smeta[rp];
-        const int e = l >> 2, jj = l & 3, blk = (int)(sleaf[rp] / kLeavesPerBlock);
-        const bool in = e < (int)(m & 0xFFu);
-        const int tb = in ? kPool * (int)cm16[24 * spos[rp] + ((m >> 8) & 7u) + e] + jj : 0;
-        const int64_t t0 = (int64_t)blk * kBlockTokens + tb;
-        const bool el = in && t0 >= q.sink_end && t0 < q.l0;
-        const uint64_t bal = __ballot(el);
-        const bool tk = el && __popcll(bal & lt) < stake[rp];
-        const uint64_t bt = __ballot(tk);
-        if (tk) atomicOr(&mask[sslot[rp] * 32 + tb / 64], 1ull << (tb % 64));
-        if (l == 0) rmask[rp] = bt;
-    }
-    __syncthreads();
-    if (sa.brec) {
-        u32x4* rec = sa.brec + u * LSA_BUCKET_RECS;
-        if (tid < ntake) rec[tid] = u32x4{sleaf[tid], (uint32_t)rmask[tid], (uint32_t)(rmask[tid] >> 32), 0u};
-        if (tid == 0) sa.bcnt[u] = ntake;
-    }
-    if (!(sa.brec && sa.skip_lists)) {
-        // prefix counts of the mask words (thread tid owns words [per tid, per tid + per)), then the
-        // token of each output position: its word (the last one whose prefix is <= the position, found
-        // by kFinOutPer interleaved binary searches) and the matching set bit in it
-        const int nw = ns * 32, per = (nw + 255) / 256, w0 = per * tid;
-        int pc = 0;
-        for (int w = w0; w < w0 + per && w < nw; ++w) pc += __popcll(mask[w]);
-        int tot;
-        int run = wg_excl_scan(pc, sh4, tot);
-        for (int w = w0; w < w0 + per && w < nw; ++w) {
-            hist[w] = (uint32_t)run;
-            run += __popcll(mask[w]);
-        }
-        for (int w = nw + tid; w < kFinBins; w += 256) hist[w] = 0x7FFFFFFFu;   // past the last word
         __syncthreads();
-        for (int p0 = 0; p0 < tot; p0 += 256 * kFinOutPer) {
-            int lo[kFinOutPer];
-#pragma unroll
-            for (int i = 0; i < kFinOutPer; ++i) lo[i] = 0;
-#pragma unroll
-            for (int step = kFinBins / 2; step >= 1; step >>= 1) {
-#pragma unroll
-                for (int i = 0; i < kFinOutPer; ++i) {   // lo + step < kFinBins: the read is in bounds
-                    const int c = lo[i] + step, p = p0 + 256 * i + tid;
-                    lo[i] = (int)hist[c] <= p ? c : lo[i];
+        // the walk: thread tid holds ranks 2 tid and 2 tid + 1; the rank where the tokens reach k
+        {
+            const int j0 = 2 * tid, j1 = j0 + 1;
+            const int w0 = j0 < f ? cw[fin_key_slot(keys[rk[j0]])] : 0;
+            const int w1 = j1 < f ? cw[fin_key_slot(keys[rk[j1]])] : 0;
+            int tot;
+            const int ex = wg_excl_scan(w0 + w1, sh4, tot);
+            if (w0 > 0 && ex < sa.k && sa.k <= ex + w0) {
+                fin[0] = j0 + 1;
+                fin[1] = sa.k - ex;
+            }
+            if (w1 > 0 && ex + w0 < sa.k && sa.k <= ex + w0 + w1) {
+                fin[0] = j1 + 1;
+                fin[1] = sa.k - ex - w0;
+            }
+        }
+        __syncthreads();
+        const int ntake = fin[0], last = fin[1];
+        if (ntake == 0 || ntake > kSelCap) {   // more buckets than one record row holds
+            return true;
+        }
+        if (tid < ntake) tleaf[tid] = fin_key_id(keys[rk[tid]]);
+        __syncthreads();
+        // the taken buckets in id order (ids are distinct: a bucket's place is the count of smaller ids)
+        if (tid < ntake) {
+            const int j = rk[tid];
+            const uint32_t leaf = tleaf[tid];
+            int r = 0;
+            for (int i = 0; i < ntake; ++i) r += tleaf[i] < leaf ? 1 : 0;
+            const int slot = fin_key_slot(keys[j]);
+            const int w = cw[slot], take = tid == ntake - 1 ? last : w;
+            sleaf[r] = leaf;
+            smeta[r] = cmeta[slot];
+            stake[r] = take;
+            sw[r] = w;
+            spos[r] = j;
+            rmask[r] = 0ull;
+        }
+        __syncthreads();
+        // block slots in block order
+        {
+            int first = 0, blk = 0;
+            if (tid < ntake) {
+                blk = (int)(sleaf[tid] / kLeavesPerBlock);
+                first = (tid == 0 || (int)(sleaf[tid - 1] / kLeavesPerBlock) != blk) ? 1 : 0;
+                if (stake[tid] < sw[tid]) fin[2] = tid;   // the partially taken bucket
+            }
+            int ns;
+            const int ex = wg_excl_scan(first, sh4, ns);
+            if (tid < ntake) {
+                sslot[tid] = ex + first - 1;
+                if (first && ex < kFinSlots) slot_blk[ex] = blk;
+            }
+            if (tid == 0) fin[1] = ns;
+        }
+    #pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int j = tid + 256 * h2;
+            if (j < f) {
+                cmem[3 * j] = pmv[h2][0];
+                cmem[3 * j + 1] = pmv[h2][1];
+                cmem[3 * j + 2] = pmv[h2][2];
+            }
+        }
+        __syncthreads();
+        const int ns = fin[1], rp = fin[2];
+        if (ns > kFinSlots) {
+            return true;
+        }
+        for (int w = tid; w < ns * 32; w += 256) mask[w] = 0ull;
+        __syncthreads();
+        const uint16_t* cm16 = reinterpret_cast<const uint16_t*>(cmem);
+        // entry e of taken bucket r (in id order) by thread (16 r + e) mod 256
+        for (int idx = tid; idx < ntake * 16; idx += 256) {
+            const int r = idx >> 4, e = idx & 15;
+            const uint32_t m = smeta[r];
+            if (r == rp || e >= (int)(m & 0xFFu)) continue;
+            const int mbr = cm16[24 * spos[r] + ((m >> 8) & 7u) + e];
+            const int tb0 = kPool * mbr;   // token offset in the block
+            const int64_t t0 = (int64_t)(sleaf[r] / kLeavesPerBlock) * kBlockTokens + tb0;
+            uint32_t bits = 0;
+    #pragma unroll
+            for (int jj = 0; jj < kPool; ++jj) bits |= (t0 + jj >= q.sink_end && t0 + jj < q.l0) ? 1u << jj : 0u;
+            if (bits) {
+                atomicOr(&mask[sslot[r] * 32 + tb0 / 64], (uint64_t)bits << (tb0 % 64));
+                atomicOr(&rmask[r], (uint64_t)bits << (kPool * e));
+            }
+        }
+        if (wid == 0 && rp >= 0) {   // the partial bucket: its lowest `take` eligible keys (key l = lane l)
+            const uint32_t m = smeta[rp];
+            const int e = l >> 2, jj = l & 3, blk = (int)(sleaf[rp] / kLeavesPerBlock);
+            const bool in = e < (int)(m & 0xFFu);
+            const int tb = in ? kPool * (int)cm16[24 * spos[rp] + ((m >> 8) & 7u) + e] + jj : 0;
+            const int64_t t0 = (int64_t)blk * kBlockTokens + tb;
+            const bool el = in && t0 >= q.sink_end && t0 < q.l0;
+            const uint64_t bal = __ballot(el);
+            const bool tk = el && __popcll(bal & lt) < stake[rp];
+            const uint64_t bt = __ballot(tk);
+            if (tk) atomicOr(&mask[sslot[rp] * 32 + tb / 64], 1ull << (tb % 64));
+            if (l == 0) rmask[rp] = bt;
+        }
+        __syncthreads();
+        if (sa.brec) {
+            u32x4* rec = sa.brec + u * LSA_BUCKET_RECS;
+            if (tid < ntake) rec[tid] = u32x4{sleaf[tid], (uint32_t)rmask[tid], (uint32_t)(rmask[tid] >> 32), 0u};
+            if (tid == 0) sa.bcnt[u] = ntake;
+        }
+        if (!(sa.brec && sa.skip_lists)) {
+            // prefix counts of the mask words (thread tid owns words [per tid, per tid + per)), then the
+            // token of each output position: its word (the last one whose prefix is <= the position, found
+            // by kFinOutPer interleaved binary searches) and the matching set bit in it
+            const int nw = ns * 32, per = (nw + 255) / 256, w0 = per * tid;
+            int pc = 0;
+            for (int w = w0; w < w0 + per && w < nw; ++w) pc += __popcll(mask[w]);
+            int tot;
+            int run = wg_excl_scan(pc, sh4, tot);
+            for (int w = w0; w < w0 + per && w < nw; ++w) {
+                hist[w] = (uint32_t)run;
+                run += __popcll(mask[w]);
+            }
+            for (int w = nw + tid; w < kFinBins; w += 256) hist[w] = 0x7FFFFFFFu;   // past the last word
+            __syncthreads();
+            for (int p0 = 0; p0 < tot; p0 += 256 * kFinOutPer) {
+                int lo[kFinOutPer];
+    #pragma unroll
+                for (int i = 0; i < kFinOutPer; ++i) lo[i] = 0;
+    #pragma unroll
+                for (int step = kFinBins / 2; step >= 1; step >>= 1) {
+    #pragma unroll
+                    for (int i = 0; i < kFinOutPer; ++i) {   // lo + step < kFinBins: the read is in bounds
+                        const int c = lo[i] + step, p = p0 + 256 * i + tid;
+                        lo[i] = (int)hist[c] <= p ? c : lo[i];
+                    }
+                }
+    #pragma unroll
+                for (int i = 0; i < kFinOutPer; ++i) {
+                    const int p = p0 + 256 * i + tid;
+                    if (p < tot)
+                        out[p] = slot_blk[lo[i] / 32] * kBlockTokens + (lo[i] % 32) * 64 +
+                                 nth_set_bit(mask[lo[i]], p - (int)hist[lo[i]]);
                 }
             }
-#pragma unroll
-            for (int i = 0; i < kFinOutPer; ++i) {
-                const int p = p0 + 256 * i + tid;
-                if (p < tot)
-                    out[p] = slot_blk[lo[i] / 32] * kBlockTokens + (lo[i] % 32) * 64 +
-                             nth_set_bit(mask[lo[i]], p - (int)hist[lo[i]]);
-            }
+            for (int j = tot + tid; j < sa.k; j += 256) out[j] = -1;
         }
-        for (int j = tot + tid; j < sa.k; j += 256) out[j] = -1;
-    }
-    if (tid == 0) lr_cnt[u] = sa.k;
+        if (tid == 0) lr_cnt[u] = sa.k;
+        return false;
+    }();
+    if (exact) to_exact();
 }
 
 
