@@ -220,21 +220,24 @@ __device__ __forceinline__ void combine_unit(const float* __restrict__ part, con
 }
 
 // Arrival of one split of a unit: returns true for the split that arrives
-// last.  The word holds (call tag << 32 | splits arrived so far); a word
-// carrying another call's tag counts as zero arrivals, and the last arrival
-// leaves (tag, 0), so every call leaves the words ready for the next one.
-// The CAS loop retries only while other splits update the word at the same
-// moment, so it ends after at most `splits` attempts.
+// last.  The word holds (call tag << 32 | splits arrived so far).  A word
+// that carries another call's tag (an earlier call, or junk in fresh memory)
+// is claimed by this call's first arrival with one compare-and-swap to
+// (tag, 1); every other arrival adds 1 with one fetch-add, so the last
+// arrival waits for at most two device-scope atomics however many splits
+// arrive together (a compare-and-swap loop for every arrival serialises the
+// splits' round trips: 8 splits per unit cost 49.6 instead of 41.9 us per
+// 16 x 1M decode step).  The only writers of the word during a call are that
+// call's splits, so the claim loop ends as soon as one claim succeeds.
 __device__ __forceinline__ bool split_arrive(unsigned long long* word, uint32_t tag, int splits) {
     unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while (true) {
-        const uint32_t seen = (uint32_t)(cur >> 32) == tag ? (uint32_t)cur : 0u;
-        const uint32_t now = seen + 1u;
-        const unsigned long long nv = ((unsigned long long)tag << 32) | (now == (uint32_t)splits ? 0u : now);
-        if (__hip_atomic_compare_exchange_strong(word, &cur, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-            return now == (uint32_t)splits;
+    while ((uint32_t)(cur >> 32) != tag) {
+        if (__hip_atomic_compare_exchange_strong(word, &cur, ((unsigned long long)tag << 32) | 1ull,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return splits == 1;
     }
+    const unsigned long long old = __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)old + 1u == (uint32_t)splits;
 }
 
 // After a split wave has written its partials (coherent stores): the last

@@ -9,7 +9,7 @@
 // calls that overlap in time on one device race (run them on one stream, or
 // order them).  Nothing in it needs clearing: the partials are written
 // before they are read, and an arrival word left by an earlier call carries
-// that call's tag, which counts as no arrivals.
+// that call's tag, so the next call's first arrival claims it afresh.
 
 #include <hip/hip_runtime.h>
 
