@@ -511,7 +511,9 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t* lr = lr_idx ? lr_idx : lr_cnt;  // k == 0: rows are empty, never written
     hipError_t e = bucket_cnt ? lsa::launch_fill_i32(bucket_cnt, units, -1, st) : hipSuccess;
-    if (e == hipSuccess)
+    // the bf16 materialized scan computes its own query latents
+    const bool own_qhat = cfg->search == LSA_SEARCH_FLAT && w.strategy == LSA_STRATEGY_MATERIALIZED && bf16;
+    if (e == hipSuccess && !own_qhat)
         e = lsa::launch_qlatent(Q, W_q, bf16, layout->head_dim, batch * n_q * layout->n_q_heads, sb.qhat,
                                        sb.counters, wb + w.zero_off, w.zero_bytes, st);
     if (e == hipSuccess) {
@@ -520,7 +522,8 @@ lsa_status lsa_select(const lsa_layout* layout, const lsa_select_cfg* cfg, const
         else if (w.strategy == LSA_STRATEGY_FUSED)
             e = lsa::launch_select_fused(v, bf16, q_pos, sa, (int)batch, sb, lr, lr_cnt, st);
         else
-            e = lsa::launch_select_materialized(v, bf16, q_pos, sa, sb, lr, lr_cnt, st);
+            e = lsa::launch_select_materialized(v, bf16, q_pos, sa, sb, lr, lr_cnt, Q, W_q, layout->head_dim,
+                                                batch * n_q * layout->n_q_heads, st);
     }
     if (e != hipSuccess) return fail(LSA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -120,8 +120,10 @@ hipError_t launch_qlatent(const void* Q, const void* W, bool bf16, int d, int64_
                           void* zero, size_t zero_bytes, hipStream_t st);
 hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa, int B,
                                const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, hipStream_t st);
+// bf16: the scan computes the q_hat rows from Q and W itself (no latent launch before it)
 hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa,
-                                      const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, hipStream_t st);
+                                      const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, const void* Q,
+                                      const void* W, int d, int64_t q_rows, hipStream_t st);
 hipError_t launch_select_tree(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa,
                               const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, hipStream_t st);
 int attend_splits(int64_t n_units, int window, int k);

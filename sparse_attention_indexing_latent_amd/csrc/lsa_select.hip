@@ -102,37 +102,68 @@ __global__ __launch_bounds__(256) void qlatent_kernel(const TIN* __restrict__ Q,
 
 // bf16: 16 query rows per MFMA tile, Q [16 x d] . W [d x 64] as 4 column
 // tiles; lane (r, h) feeds head dims [d/4 h, d/4 h + d/4) of row r, the W
-// fragments use the same dim order and stay in registers for the whole
-// (persistent) workgroup.  The C layout gives lane (n, h) rows 4h..4h+3 of
-// latent column n of each tile; row norms are reduced over the 16 lanes of
-// a row group.
+// fragments use the same dim order.  The C layout gives lane (n, h) rows
+// 4h..4h+3 of latent column n of each tile; row norms are reduced over the
+// 16 lanes of a row group.  One code path for the latent kernel and for the
+// decode scan (which computes its unit's rows itself), so both give the
+// same q_hat bit for bit.
+template <int D>
+__device__ __forceinline__ void qlatent_w_frag(const uint16_t* __restrict__ W, int nt, bf16x8 (&wf)[D / 32]) {
+    constexpr int DPL = D / 4, KS = DPL / 8;
+    const int l = lane_id(), r = l & 15, h = l >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint16_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = W[(DPL * h + 8 * ks + j) * kLatent + 16 * nt + r];
+        wf[ks] = as_bf16x8(uint4{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16),
+                                 (uint32_t)e[4] | ((uint32_t)e[5] << 16), (uint32_t)e[6] | ((uint32_t)e[7] << 16)});
+    }
+}
+
+// Query rows row0 .. row0 + 15 (rows >= `rows` read as zero) as A fragments.
+template <int D>
+__device__ __forceinline__ void qlatent_q_frag(const uint16_t* __restrict__ Q, int64_t row0, int64_t rows,
+                                               uint4 (&qa)[D / 32]) {
+    constexpr int DPL = D / 4, KS = DPL / 8;
+    const int l = lane_id(), r = l & 15, h = l >> 4;
+    const int64_t row = row0 + r;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qa[ks] = row < rows ? *reinterpret_cast<const uint4*>(Q + row * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
+}
+
+// The rounded unit rows: out[nt][v] = q_hat[row0 + 4h + v][16 nt + n] for lane (n, h).
+__device__ __forceinline__ void qlatent_normalise(const f32x4 (&c)[4], uint16_t (&out)[4][4]) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        float ss = c[0][v] * c[0][v] + c[1][v] * c[1][v] + c[2][v] * c[2][v] + c[3][v] * c[3][v];
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        ss += __shfl_xor(ss, 8);
+        const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) out[nt][v] = f32_to_bf16(c[nt][v] * inv);
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void qlatent_bf16_kernel(const uint16_t* __restrict__ Q,
                                                            const uint16_t* __restrict__ W, int64_t rows,
                                                            uint16_t* __restrict__ qhat, int* counters,
                                                            uint4* zero, int64_t zero_n) {
-    constexpr int DPL = D / 4, KS = DPL / 8;
+    constexpr int KS = D / 32;
     if (blockIdx.x == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0;
     clear_words(zero, zero_n);
     const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4;
-    bf16x8 wf[4][KS];
+    bf16x8 wf[4][KS];   // in registers for the whole (persistent) workgroup
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint16_t e[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) e[j] = W[(DPL * h + 8 * ks + j) * kLatent + 16 * nt + r];
-            wf[nt][ks] = as_bf16x8(uint4{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16),
-                                         (uint32_t)e[4] | ((uint32_t)e[5] << 16), (uint32_t)e[6] | ((uint32_t)e[7] << 16)});
-        }
+    for (int nt = 0; nt < 4; ++nt) qlatent_w_frag<D>(W, nt, wf[nt]);
     const int64_t ntile = (rows + 15) / 16;
     for (int64_t tile = (int64_t)blockIdx.x * 4 + wid; tile < ntile; tile += (int64_t)gridDim.x * 4) {
-        const int64_t row = tile * 16 + r;
         uint4 qa[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qa[ks] = row < rows ? *reinterpret_cast<const uint4*>(Q + row * D + DPL * h + 8 * ks) : uint4{0, 0, 0, 0};
+        qlatent_q_frag<D>(Q, tile * 16, rows, qa);
         f32x4 c[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -141,21 +172,53 @@ __global__ __launch_bounds__(256) void qlatent_bf16_kernel(const uint16_t* __res
             for (int ks = 0; ks < KS; ++ks)
                 c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), wf[nt][ks], c[nt], 0, 0, 0);
         }
+        uint16_t o[4][4];
+        qlatent_normalise(c, o);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            float ss = c[0][v] * c[0][v] + c[1][v] * c[1][v] + c[2][v] * c[2][v] + c[3][v] * c[3][v];
-            ss += __shfl_xor(ss, 1);
-            ss += __shfl_xor(ss, 2);
-            ss += __shfl_xor(ss, 4);
-            ss += __shfl_xor(ss, 8);
-            const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
             const int64_t orow = tile * 16 + 4 * h + v;
             if (orow < rows) {
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) qhat[orow * kLatent + 16 * nt + r] = f32_to_bf16(c[nt][v] * inv);
+                for (int nt = 0; nt < 4; ++nt) qhat[orow * kLatent + 16 * nt + r] = o[nt][v];
             }
         }
     }
+}
+
+// The decode scan's own q_hat rows of one unit (rows row0 .. row0 + G - 1): one
+// MFMA tile per wave, the W fragments loaded one column tile at a time (few
+// registers), the rows put in the wave's LDS area (16 x 64 bf16) for the
+// query codes; with `out` set, the unit's G rows are also written there.
+template <int D>
+__device__ __forceinline__ void qlatent_unit_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ W,
+                                                  int64_t row0, int64_t rows, int G, uint16_t* lds_rows,
+                                                  uint16_t* __restrict__ out) {
+    constexpr int KS = D / 32;
+    const int l = lane_id(), r = l & 15, h = l >> 4;
+    uint4 qa[KS];
+    qlatent_q_frag<D>(Q, row0, rows, qa);
+    f32x4 c[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        bf16x8 wf[KS];
+        qlatent_w_frag<D>(W, nt, wf);
+        c[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            c[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[ks]), wf[ks], c[nt], 0, 0, 0);
+    }
+    uint16_t o[4][4];
+    qlatent_normalise(c, o);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int rr = 4 * h + v;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            lds_rows[rr * kLatent + 16 * nt + r] = o[nt][v];
+            if (out != nullptr && rr < G) out[(row0 + rr) * kLatent + 16 * nt + r] = o[nt][v];
+        }
+    }
+    wave_sync();
 }
 
 // ------------------------------------------------------------------ scoring tiles
@@ -1425,11 +1488,18 @@ __device__ __forceinline__ float tile_max(const f32x4& v) {
     return fmaxf(m, __shfl_xor(m, 32));
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void* __restrict__ qhat,
+// bf16 (D > 0): the scan computes its unit's q_hat rows from Q and W itself
+// (no separate latent kernel ahead of it in decode), and the workgroup of
+// split 0 writes them to qhat for the finish.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, void* __restrict__ qhat,
                                                         const int64_t* __restrict__ q_pos, SelArgs sa, int splits,
                                                         float* __restrict__ scores, int64_t score_stride,
-                                                        float* __restrict__ tmax, int64_t tmax_stride) {
+                                                        float* __restrict__ tmax, int64_t tmax_stride,
+                                                        const uint16_t* __restrict__ Qin, const uint16_t* __restrict__ Win,
+                                                        int64_t q_rows) {
+    __shared__ __align__(16) uint16_t qrows_lds[BF16 ? 4 * 16 * kLatent : 1];
+    __shared__ __align__(16) uint16_t w_lds[BF16 ? (D > 0 ? D : 1) * kLatent : 1];
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
     const int64_t u = (int64_t)blockIdx.x / splits;
     const int split = (int)((int64_t)blockIdx.x % splits);
@@ -1440,25 +1510,11 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
     const int ntiles = kLeavesPerBlock * q.nvis / 16;
     const int t0 = split * kScoreTiles, t1 = min(ntiles, t0 + kScoreTiles);
     const int w0 = t0 + (kScoreTiles / 4) * wid, w1 = min(t1, w0 + kScoreTiles / 4);   // this wave's tiles
-    if (w0 >= w1) return;
     const int64_t bg = un.b * sa.H_kv + un.g;
     const int64_t qrow = ((un.b * sa.n_q + un.i) * sa.H_q + un.g * sa.G) * kLatent;
     float* sc = scores + u * score_stride;
     float* tmx = tmax + u * tmax_stride;
     if constexpr (BF16) {
-        // stage-1 scores from the int8 codes (query head n in column n); the tile maximum taken of the
-        // upper bounds s~ + sc Qa + Qb
-        const QCodes qc = query_codes(reinterpret_cast<const uint16_t*>(qhat) + qrow, sa.G);
-        // the MFMA takes the query heads as rows and the tile's buckets as columns (the operand layouts are
-        // alike), so lane (bucket c, h) holds heads 4h..4h+3 of bucket c: the max over heads is 3 maxima in
-        // the lane and 2 across its 4 lanes; sq of those heads, a negative factor past the group
-        float sqh[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float sj = __shfl(qc.sq, 4 * h + j);   // lane 4h + j holds head 4h + j's sq
-            sqh[j] = 4 * h + j < sa.G ? sj : -1.0f;
-        }
-        const float qa = qc.qa, qb = qc.qb;
         const uint4* cq = reinterpret_cast<const uint4*>(cv.cq + bg * cv.s_cq);
         const float* csc = cv.csc + bg * cv.s_csc;
         // batches of TPI tiles; the next batch's loads are in flight while one is scored
@@ -1474,7 +1530,29 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
                 scl[buf][j] = csc[tt * 16 + n];   // this lane's bucket
             }
         };
-        issue(0, w0);
+        // the first codes are in flight while W is staged in LDS (whole workgroup) and this unit's q_hat
+        // rows are computed (the wave of split 0 that scores the first tiles also stores them for the finish)
+        if (w0 < w1) issue(0, w0);
+        for (int x = threadIdx.x; x < D * kLatent / 8; x += 256)
+            reinterpret_cast<uint4*>(w_lds)[x] = reinterpret_cast<const uint4*>(Win)[x];
+        __syncthreads();
+        if (w0 >= w1) return;
+        uint16_t* myrows = qrows_lds + wid * 16 * kLatent;
+        qlatent_unit_bf16<D>(Qin, w_lds, qrow / kLatent, q_rows, sa.G, myrows,
+                             (split == 0 && wid == 0) ? reinterpret_cast<uint16_t*>(qhat) : nullptr);
+        // stage-1 scores from the int8 codes (query head n in column n); the tile maximum taken of the
+        // upper bounds s~ + sc Qa + Qb
+        const QCodes qc = query_codes(myrows, sa.G);
+        // the MFMA takes the query heads as rows and the tile's buckets as columns (the operand layouts are
+        // alike), so lane (bucket c, h) holds heads 4h..4h+3 of bucket c: the max over heads is 3 maxima in
+        // the lane and 2 across its 4 lanes; sq of those heads, a negative factor past the group
+        float sqh[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float sj = __shfl(qc.sq, 4 * h + j);   // lane 4h + j holds head 4h + j's sq
+            sqh[j] = 4 * h + j < sa.G ? sj : -1.0f;
+        }
+        const float qa = qc.qa, qb = qc.qb;
         for (int tt0 = w0; tt0 < w1; tt0 += 2 * TPI) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -1503,6 +1581,7 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, const void
             }
         }
     } else {
+        if (w0 >= w1) return;
         const float* qf32 = reinterpret_cast<const float*>(qhat) + qrow;
         for (int tt = w0; tt < w1; ++tt) {
             const int64_t x0 = (int64_t)tt * 16;
@@ -2691,16 +2770,22 @@ hipError_t launch_select_fused(const CacheView& cv, bool bf16, const int64_t* q_
 }
 
 hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa,
-                                      const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, hipStream_t st) {
+                                      const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, const void* Q,
+                                      const void* W, int d, int64_t q_rows, hipStream_t st) {
     const int64_t ntiles_max = (int64_t)cv.n_blocks * kLeavesPerBlock / 16;
     const int splits = (int)((ntiles_max + kScoreTiles - 1) / kScoreTiles > 0 ? (ntiles_max + kScoreTiles - 1) / kScoreTiles : 1);
     const dim3 grid((unsigned)(sa.n_units * splits));
-    if (bf16)
-        hipLaunchKernelGGL(score_all_kernel<true>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits, sb.scores,
-                           sb.score_stride, sb.tmax, sb.tmax_stride);
+    const uint16_t* Qb = static_cast<const uint16_t*>(Q);
+    const uint16_t* Wb = static_cast<const uint16_t*>(W);
+    if (bf16 && d == 128)
+        hipLaunchKernelGGL((score_all_kernel<true, 128>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits,
+                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows);
+    else if (bf16)
+        hipLaunchKernelGGL((score_all_kernel<true, 64>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits,
+                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows);
     else
-        hipLaunchKernelGGL(score_all_kernel<false>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits, sb.scores,
-                           sb.score_stride, sb.tmax, sb.tmax_stride);
+        hipLaunchKernelGGL((score_all_kernel<false, 0>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits,
+                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)sa.n_units), dim3(256), 0, st, cv, sb.qhat, q_pos, sa,
