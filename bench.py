@@ -364,8 +364,8 @@ def run_prefill(args, cid, steps, warmup):
                 "beam": cfg.beam, "query_chunk": ws.get("chunk", CHUNK), "attention": attend,
                 "bucket_pass": ws.get("bm_pass"),
                 "bucket_records": ("only" if ws.get("skip_lists") else "on") if "recs" in ws else "off"},
-        breakdown_ms={"build_buckets": timers["build"].total_ms() / args.steps,
-                      "select": timers["select"].total_ms() / args.steps, "sparse_attend": att_ms},
+        breakdown_ms={"build_buckets": timers["build"].total_ms() / steps,
+                      "select": timers["select"].total_ms() / steps, "sparse_attend": att_ms},
         roofline={"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                   "traffic": traffic, "alg_bytes_per_launch": per_launch,
