@@ -55,8 +55,15 @@ __device__ __forceinline__ uint64_t pair_key(float d, int id, int nn) {
     return ((uint64_t)__float_as_uint(d) << 32) | ((uint64_t)id << 16) | (uint64_t)nn;
 }
 
+// Register budget: 128 VGPRs (4 waves per SIMD), so two 512-thread workgroups
+// share a CU.  A block's 448 merges are a chain of barriers and workgroup
+// reductions, so a second block on the CU fills the first one's waits; the
+// values that do not fit (88 VGPRs, mostly the cluster mean's components
+// between recomputes) spill to scratch.  Measured on the 1M layer (4096 x 8
+// blocks): 53.7 ms with one workgroup per CU (156 VGPRs, no spills), 32.2 ms
+// with two, 44.1 and 133 ms with three and four (more spills).
 template <typename TIN>
-__global__ __launch_bounds__(kWardThreads) void ward_kernel(const TIN* __restrict__ K, int64_t t_cap, int d,
+__global__ __launch_bounds__(kWardThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void ward_kernel(const TIN* __restrict__ K, int64_t t_cap, int d,
                                                             int H_kv, const TIN* __restrict__ W, CacheView cv,
                                                             int blk0) {
     const int blk = blk0 + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
