@@ -526,13 +526,15 @@ __device__ __forceinline__ void store_tile_part(const u32x4 (&kr)[TileLds<D>::NI
 // could not take (np = -1) has that list gathered afterwards by its wave,
 // for its own columns only.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bm_local_kernel(
+// 3 waves per SIMD (168 VGPRs, some spilled; 33 KB of LDS): three workgroups per CU keep more partial
+// reads in flight than two without spills (1M layer: the attention call 3-4% faster)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void bm_local_kernel(
     CacheView cv, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int64_t* __restrict__ q_pos, const int32_t* __restrict__ lr_idx, const int32_t* __restrict__ lr_cnt,
     AttArgs aa, uint16_t* __restrict__ O, int64_t nwg_padded) {
     using TL = TileLds<D>;
-    // window: two shared tiles; afterwards one private tile per wave
-    __shared__ __align__(16) uint8_t tile_lds[4 * TL::BYTES];
+    // window: two shared tiles; afterwards the private tiles of two waves at a time
+    __shared__ __align__(16) uint8_t tile_lds[2 * TL::BYTES];
     __shared__ int64_t red[3][4];
     constexpr int KS = D / 32, NC = 2 * KS, NI = TL::NI, NIW = NI / 4;
     const int l = lane_id(), wid = threadIdx.x >> 6, r = l & 15, h = l >> 4, n = r;
@@ -623,73 +625,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             k0 = kn;
         }
     }
-    __syncthreads();   // the shared tiles are read no more: the LDS becomes one private tile per wave
+    __syncthreads();   // the shared tiles are read no more: they become private tiles, one per wave of a pair
     // long-range keys of the units the bucket pass left to the gather: their token lists (np = -1), or
     // the keys their bucket records name (np = -2: records rows whose pairs did not fit in the pool; such
-    // rows may have no token list)
+    // rows may have no token list).  Waves 0 and 1 gather first, then waves 2 and 3 in the same two tiles
+    // (the LDS holds two tiles, not four: three workgroups then share a CU)
     const uint64_t fb = __ballot(npl < 0);
-    if (fb != 0ull) {
-        uint8_t* buf = tile_lds + wid * TL::BYTES;
-        u32x4 kR[NI], vR[NI];
-        for (int q2 = 0; q2 < QW; ++q2) {
-            if (((fb >> (q2 * G)) & 1ull) == 0ull) continue;   // column q2 * G stands for its query
-            const int lane0 = q2 * G;
-            const int64_t u2 = __shfl(u, lane0);
-            const int64_t t2 = __shfl(t, lane0);
-            const int32_t c2 = __shfl(cnt, lane0);
-            const int32_t np2 = __shfl(npl, lane0);
-            const bool mine = qi == q2;
-            if (np2 == -2) {
-                // bucket by bucket: key j = 32 half + (l % 32) of the record's bucket, if its mask bit is set
-                const Geom q = query_geom(t2, aa.n_blocks, aa.n_sinks, aa.window);
-                const int32_t nr = aa.bm_bcnt[u2];
-                const u32x4* recs = aa.bm_brec + u2 * LSA_BUCKET_RECS;
-                for (int x = 0; x < nr; ++x) {
-                    const u32x4 rec = recs[x];
-                    const int64_t leaf = rec[0], blk = leaf / kLeavesPerBlock;
-                    const unsigned long long mask = ((unsigned long long)rec[2] << 32) | rec[1];
-                    const uint32_t meta = cv.meta[bg * cv.s_meta + leaf];
-                    const int sz = (int)(meta & 0xFF), off = (int)((meta >> 8) & 0x3FF);
-                    const uint16_t* mem = cv.members + bg * cv.s_members + blk * kBlockEntries + off;
-                    for (int half = 0; half < 2; ++half) {
-                        const int j = 32 * half + (l & 31);
-                        int32_t tok = -1;
-                        if (((mask >> j) & 1ull) && j < kPool * sz) {
-                            const int64_t tk = blk * kBlockTokens + kPool * (int64_t)mem[j / kPool] + j % kPool;
-                            if (tk >= q.sink_end && tk < q.l0 && tk <= t2) tok = (int32_t)tk;
+    for (int rnd = 0; rnd < 2; ++rnd) {
+        if ((wid >> 1) == rnd && fb != 0ull) {
+            uint8_t* buf = tile_lds + (wid & 1) * TL::BYTES;
+            u32x4 kR[NI], vR[NI];
+            for (int q2 = 0; q2 < QW; ++q2) {
+                if (((fb >> (q2 * G)) & 1ull) == 0ull) continue;   // column q2 * G stands for its query
+                const int lane0 = q2 * G;
+                const int64_t u2 = __shfl(u, lane0);
+                const int64_t t2 = __shfl(t, lane0);
+                const int32_t c2 = __shfl(cnt, lane0);
+                const int32_t np2 = __shfl(npl, lane0);
+                const bool mine = qi == q2;
+                if (np2 == -2) {
+                    // bucket by bucket: key j = 32 half + (l % 32) of the record's bucket, if its mask bit is set
+                    const Geom q = query_geom(t2, aa.n_blocks, aa.n_sinks, aa.window);
+                    const int32_t nr = aa.bm_bcnt[u2];
+                    const u32x4* recs = aa.bm_brec + u2 * LSA_BUCKET_RECS;
+                    for (int x = 0; x < nr; ++x) {
+                        const u32x4 rec = recs[x];
+                        const int64_t leaf = rec[0], blk = leaf / kLeavesPerBlock;
+                        const unsigned long long mask = ((unsigned long long)rec[2] << 32) | rec[1];
+                        const uint32_t meta = cv.meta[bg * cv.s_meta + leaf];
+                        const int sz = (int)(meta & 0xFF), off = (int)((meta >> 8) & 0x3FF);
+                        const uint16_t* mem = cv.members + bg * cv.s_members + blk * kBlockEntries + off;
+                        for (int half = 0; half < 2; ++half) {
+                            const int j = 32 * half + (l & 31);
+                            int32_t tok = -1;
+                            if (((mask >> j) & 1ull) && j < kPool * sz) {
+                                const int64_t tk = blk * kBlockTokens + kPool * (int64_t)mem[j / kPool] + j % kPool;
+                                if (tk >= q.sink_end && tk < q.l0 && tk <= t2) tok = (int32_t)tk;
+                            }
+                            const uint64_t vm = __ballot(tok >= 0);
+                            if ((vm & 0xFFFFFFFFull) == 0ull) continue;
+                            load_tile<D>(Kbg, Vbg, tok, kR, vR);
+                            store_tile<D>(kR, vR, buf);
+                            attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
+                                           mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h,
+                                           aa.scale, m_run, l_run, acc);
                         }
-                        const uint64_t vm = __ballot(tok >= 0);
-                        if ((vm & 0xFFFFFFFFull) == 0ull) continue;
-                        load_tile<D>(Kbg, Vbg, tok, kR, vR);
-                        store_tile<D>(kR, vR, buf);
-                        attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
-                                       mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h,
-                                       aa.scale, m_run, l_run, acc);
                     }
+                    continue;
                 }
-                continue;
-            }
-            const int32_t* lr = lr_idx + u2 * aa.k;
-            auto tok_at = [&](int64_t j) -> int32_t {
-                if (j >= c2) return -1;
-                const int32_t tk = lr[j];
-                return (tk >= 0 && tk <= t2) ? tk : -1;
-            };
-            int32_t tok = tok_at(l & 31);
-            load_tile<D>(Kbg, Vbg, tok, kR, vR);
-            for (int64_t j = 0; j < c2; j += 32) {
-                const int32_t nxt = tok_at(j + 32 + (l & 31));
-                const uint64_t vm = __ballot(tok >= 0);
-                store_tile<D>(kR, vR, buf);
-                load_tile<D>(Kbg, Vbg, nxt, kR, vR);
-                if ((vm & 0xFFFFFFFFull) != 0ull) {
-                    attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
-                                   mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h, aa.scale,
-                                   m_run, l_run, acc);
+                const int32_t* lr = lr_idx + u2 * aa.k;
+                auto tok_at = [&](int64_t j) -> int32_t {
+                    if (j >= c2) return -1;
+                    const int32_t tk = lr[j];
+                    return (tk >= 0 && tk <= t2) ? tk : -1;
+                };
+                int32_t tok = tok_at(l & 31);
+                load_tile<D>(Kbg, Vbg, tok, kR, vR);
+                for (int64_t j = 0; j < c2; j += 32) {
+                    const int32_t nxt = tok_at(j + 32 + (l & 31));
+                    const uint64_t vm = __ballot(tok >= 0);
+                    store_tile<D>(kR, vR, buf);
+                    load_tile<D>(Kbg, Vbg, nxt, kR, vR);
+                    if ((vm & 0xFFFFFFFFull) != 0ull) {
+                        attend_tile<D>(mine ? (uint32_t)(vm >> (4 * h)) & 0xFu : 0u,
+                                       mine ? (uint32_t)(vm >> (16 + 4 * h)) & 0xFu : 0u, buf, r, qf, ident, h, aa.scale,
+                                       m_run, l_run, acc);
+                    }
+                    tok = nxt;
                 }
-                tok = nxt;
             }
         }
+        if (rnd == 0) __syncthreads();   // the second pair reuses the first pair's tiles
     }
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
