@@ -2486,15 +2486,21 @@ __global__ __launch_bounds__(256) void exact_select_kernel(CacheView cv, const v
 // One wave per (query, KV head).  A = the group's query latents (heads as
 // rows), B = 16 candidate node centroids per MFMA, so lane l ends with the
 // scores of heads 4*(l/16)..+3 for candidate l % 16.
+// Occupancy: the expansion's entry scratch is dynamic LDS sized by k (ent_cap
+// = ceil(k / 4) keys per wave, 8.4 KB per workgroup at k = 2048 instead of
+// 16 KB for the largest k), and the register budget is 85 VGPRs, so six
+// workgroups share a CU at k = 2048 (a level waits on its centroid loads;
+// more waves fill those waits: 8.70 -> 8.35 ms per 65,536-query chunk of the
+// 1M layer with its tree).
 template <bool BF16>
-__global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __restrict__ qhat,
-                                                   const int64_t* __restrict__ q_pos, SelArgs sa, int32_t* lr_idx,
-                                                   int32_t* lr_cnt) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 6))) void tree_kernel(
+    CacheView cv, const void* __restrict__ qhat, const int64_t* __restrict__ q_pos, SelArgs sa, int32_t* lr_idx,
+    int32_t* lr_cnt, int ent_cap) {
     __shared__ uint64_t keys[4][2 * LSA_MAX_BEAM];
     __shared__ uint32_t front[4][LSA_MAX_BEAM];
     __shared__ uint64_t sel[4][2 * LSA_MAX_BEAM];
     __shared__ int tk[4][256];
-    __shared__ uint32_t ent[4][LSA_MAX_K / kPool];
+    extern __shared__ __align__(16) uint32_t tree_ent[];   // [4][ent_cap]
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
     const int64_t u = (int64_t)blockIdx.x * 4 + wid;
     if (u >= sa.n_units) return;
@@ -2683,7 +2689,8 @@ __global__ __launch_bounds__(256) void tree_kernel(CacheView cv, const void* __r
         wave_sync();
     }
     // nf <= beam buckets: never more than sel holds
-    const int got = wave_walk_expand(keys[wid], nf, sel[wid], 2 * LSA_MAX_BEAM, tk[wid], ent[wid], cv, bg, q, sa.k,
+    const int got = wave_walk_expand(keys[wid], nf, sel[wid], 2 * LSA_MAX_BEAM, tk[wid], tree_ent + wid * ent_cap, cv,
+                                     bg, q, sa.k,
                                      out, sa.brec ? sa.brec + u * LSA_BUCKET_RECS : nullptr,
                                      sa.bcnt ? sa.bcnt + u : nullptr, sa.skip_lists != 0);
     if (!(sa.brec && sa.skip_lists)) write_pad(out, got, sa.k);
@@ -2797,10 +2804,17 @@ hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int6
 hipError_t launch_select_tree(const CacheView& cv, bool bf16, const int64_t* q_pos, const SelArgs& sa,
                               const SelectBuffers& sb, int32_t* lr_idx, int32_t* lr_cnt, hipStream_t st) {
     dim3 grid((unsigned)((sa.n_units + 3) / 4));
+    // the expansion scratch: at least k / 4 entry keys per wave, rounded to 16 bytes (a k above LSA_MAX_K is
+    // only accepted when it covers every bucketed token, and then every unit is trivial: no expansion)
+    const int k_exp = sa.k < LSA_MAX_K ? sa.k : LSA_MAX_K;
+    const int ent_cap = ((k_exp + kPool - 1) / kPool + 3) & ~3;
+    const size_t dyn = (size_t)4 * ent_cap * sizeof(uint32_t);
     if (bf16)
-        hipLaunchKernelGGL(tree_kernel<true>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, lr_idx, lr_cnt);
+        hipLaunchKernelGGL(tree_kernel<true>, grid, dim3(256), dyn, st, cv, sb.qhat, q_pos, sa, lr_idx, lr_cnt,
+                           ent_cap);
     else
-        hipLaunchKernelGGL(tree_kernel<false>, grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, lr_idx, lr_cnt);
+        hipLaunchKernelGGL(tree_kernel<false>, grid, dim3(256), dyn, st, cv, sb.qhat, q_pos, sa, lr_idx, lr_cnt,
+                           ent_cap);
     return hipGetLastError();
 }
 
