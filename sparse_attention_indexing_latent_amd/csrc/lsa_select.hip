@@ -1381,6 +1381,7 @@ __global__ __launch_bounds__(256) void fused_finalize_kernel(CacheView cv, const
 // step, all resident at once, and half as many copies of each unit's query-latent setup as 128 (the decode
 // step 2-4 us faster)
 constexpr int kScoreTiles = 256;
+constexpr int64_t kExactScanAbove = 2048;   // tiles per unit above which the bf16 decode scan writes exact scores
 
 // Eligible tokens of a bucket whose block lies inside or outside [sink_end,
 // l0); a block straddling an edge (at most two) needs its member lists.
@@ -1500,7 +1501,7 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, void* __re
                                                         float* __restrict__ scores, int64_t score_stride,
                                                         float* __restrict__ tmax, int64_t tmax_stride,
                                                         const uint16_t* __restrict__ Qin, const uint16_t* __restrict__ Win,
-                                                        int64_t q_rows) {
+                                                        int64_t q_rows, int exact) {
     __shared__ __align__(16) uint16_t qrows_lds[BF16 ? 4 * 16 * kLatent : 1];
     __shared__ __align__(16) uint16_t w_lds[BF16 ? (D > 0 ? D : 1) * kLatent : 1];
     const int l = lane_id(), wid = threadIdx.x >> 6, n = l & 15, h = l >> 4;
@@ -1535,7 +1536,7 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, void* __re
         };
         // the first codes are in flight while W is staged in LDS (whole workgroup) and this unit's q_hat
         // rows are computed (the wave of split 0 that scores the first tiles also stores them for the finish)
-        if (w0 < w1) issue(0, w0);
+        if (w0 < w1 && !exact) issue(0, w0);
         for (int x = threadIdx.x; x < D * kLatent / 8; x += 256)
             reinterpret_cast<uint4*>(w_lds)[x] = reinterpret_cast<const uint4*>(Win)[x];
         __syncthreads();
@@ -1543,6 +1544,21 @@ __global__ __launch_bounds__(256) void score_all_kernel(CacheView cv, void* __re
         uint16_t* myrows = qrows_lds + wid * 16 * kLatent;
         qlatent_unit_bf16<D>(Qin, w_lds, qrow / kLatent, q_rows, sa.G, myrows,
                              (split == 0 && wid == 0) ? reinterpret_cast<uint16_t*>(qhat) : nullptr);
+        if (exact) {
+            // exact bf16 scores and tile maxima (the exact path's own MFMA, so the same scores as the fused
+            // strategy): the finish's first tile bound then holds without widening however many tiles
+            QFragBF16 qf;
+            load_qfrag_bf16(qf, myrows, n == 0, sa.G);
+            const uint16_t* cent_bg = reinterpret_cast<const uint16_t*>(cv.cent) + bg * cv.s_cent;
+            for (int tt = w0; tt < w1; ++tt) {
+                const int64_t x0 = (int64_t)tt * 16;
+                const f32x4 vals = score_tile_bf16(cent_bg, x0, qf, sa.G);
+                if (n == 0) *reinterpret_cast<f32x4*>(sc + x0 + 4 * h) = vals;
+                const float m = tile_max(vals);   // lanes 0, 16, 32, 48: query slot 0
+                if (l == 0) tmx[tt] = m;
+            }
+            return;
+        }
         // stage-1 scores from the int8 codes (query head n in column n); the tile maximum taken of the
         // upper bounds s~ + sc Qa + Qb
         const QCodes qc = query_codes(myrows, sa.G);
@@ -1860,7 +1876,8 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
                                                             const int64_t* __restrict__ q_pos,
                                                             SelArgs sa, const float* __restrict__ scores,
                                                             int64_t score_stride, const float* __restrict__ tmax,
-                                                            int64_t tmax_stride, int32_t* lr_idx, int32_t* lr_cnt) {
+                                                            int64_t tmax_stride, int32_t* lr_idx, int32_t* lr_cnt,
+                                                            int int8_scores) {
     __shared__ __align__(16) uint32_t hist[kFinBins];   // histograms, then the mask words' prefix counts
     __shared__ __align__(16) uint64_t keys[kCandCap];   // S
     __shared__ __align__(16) uint64_t mask[kFinSlots * 32 > kExactSel ? kFinSlots * 32 : kExactSel];
@@ -1884,7 +1901,8 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(CacheView cv, const 
     const uint64_t lt = (1ull << l) - 1ull;
     const int64_t u = blockIdx.x;
     const Unit un = unit_of(u, sa);
-    const bool filter = cv.bf16 != 0;   // scores are the int8 stage's s~, bounded by +-(sc Qa + Qb)
+    // scores are the int8 stage's s~, bounded by +-(sc Qa + Qb); else exact
+    const bool filter = cv.bf16 != 0 && int8_scores != 0;
     const int64_t bg = un.b * sa.H_kv + un.g;
     const float* sc = scores + u * score_stride;
     const float* tm = tmax + u * tmax_stride;
@@ -2787,20 +2805,25 @@ hipError_t launch_select_materialized(const CacheView& cv, bool bf16, const int6
     const dim3 grid((unsigned)(sa.n_units * splits));
     const uint16_t* Qb = static_cast<const uint16_t*>(Q);
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
+    // bf16 caches of more than 2048 tiles (1M tokens) are scanned with exact bf16 scores: the int8 bounds'
+    // half-width (about 0.016) leaves too few certainly-eligible tokens in the top tiles once there are many
+    // tiles near the top, so the finish would widen past its tile capacity and rescore every bucket on the
+    // exact path (16 x 2M decode 1.2 ms, 10M 6.8 ms per select); exact scores need no widening
+    const int exact = (bf16 && ntiles_max > kExactScanAbove) ? 1 : 0;
     if (bf16 && d == 128)
         hipLaunchKernelGGL((score_all_kernel<true, 128>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits,
-                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows);
+                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows, exact);
     else if (bf16)
         hipLaunchKernelGGL((score_all_kernel<true, 64>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits,
-                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows);
+                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows, exact);
     else
         hipLaunchKernelGGL((score_all_kernel<false, 0>), grid, dim3(256), 0, st, cv, sb.qhat, q_pos, sa, splits,
-                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows);
+                           sb.scores, sb.score_stride, sb.tmax, sb.tmax_stride, Qb, Wb, q_rows, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)sa.n_units), dim3(256), 0, st, cv, sb.qhat, q_pos, sa,
                        sb.scores,
-                       sb.score_stride, sb.tmax, sb.tmax_stride, lr_idx, lr_cnt);
+                       sb.score_stride, sb.tmax, sb.tmax_stride, lr_idx, lr_cnt, exact ? 0 : 1);
     return hipGetLastError();
 }
 
